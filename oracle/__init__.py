@@ -1,0 +1,202 @@
+"""CPU oracle for C[M,N] = A[M,K] · B[N,K]^T with f16 or Q8_0 weights.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The GPU
+library (``gemm_wq_gemv_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``wqref.c`` (plain C, f64 accumulation, built with
+``-O2 -fno-fast-math -ffp-contract=off``); this module only marshals numpy
+arrays.  Every function cites the passage it follows in ``wqref.c``.
+
+Parity status of each function (what pins it, see ``tests/test_oracle.py``):
+  f16_value      exhaustive over all 65536 patterns against ``struct '<e'``
+  f16_bits       against numpy's float16 cast on every exponent/rounding case
+  q8_0_quantize  hand-derived golden blocks, round-trip bounds, tie rounding
+  decode         hand-built blocks, one-hot / identity products
+  matmul         exact rational brute force, identity, one-hot, linearity,
+                 permutation, numpy float64 matmul on the decoded weights
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "wqref.c")
+_LIB = os.path.join(_HERE, "libwqref.so")
+
+FMT_F16 = 0
+FMT_Q8_0 = 1
+QK = 32
+BLOCK_BYTES = 34
+
+CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
+          "-pthread", "-std=c11", "-Wall", "-Wextra"]
+
+
+def build(out: str | None = None, defines: tuple = ()) -> str:
+    """Compile the oracle with gcc (always recompiles)."""
+    out = out or _LIB
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, *[f"-D{d}" for d in defines], "-o", tmp, _SRC, "-lm"],
+                   check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+class Oracle:
+    """ctypes view of one build of ``wqref.c``."""
+
+    def __init__(self, path: str = _LIB):
+        if not os.path.exists(path):
+            if path != _LIB:
+                raise FileNotFoundError(path)
+            build()
+        lib = ctypes.CDLL(path)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.wqref_f16_value.restype = ctypes.c_double
+        lib.wqref_f16_value.argtypes = [ctypes.c_uint16]
+        lib.wqref_f16_bits.restype = ctypes.c_uint16
+        lib.wqref_f16_bits.argtypes = [ctypes.c_float]
+        lib.wqref_f16_bits_array.restype = None
+        lib.wqref_f16_bits_array.argtypes = [P, P, I64]
+        lib.wqref_f16_value_array.restype = None
+        lib.wqref_f16_value_array.argtypes = [P, P, I64]
+        lib.wqref_q8_0_quantize.restype = I
+        lib.wqref_q8_0_quantize.argtypes = [P, P, I64]
+        lib.wqref_decode.restype = I
+        lib.wqref_decode.argtypes = [P, I, I64, I64, P]
+        lib.wqref_matmul.restype = I
+        lib.wqref_matmul.argtypes = [P, P, I, I64, I64, I64, P, P, I]
+        lib.wqref_matmul_entries.restype = I
+        lib.wqref_matmul_entries.argtypes = [P, P, I, I64, I64, I64, P, P, I64, P, P, I]
+        self.lib = lib
+        self.path = path
+
+    # -- f16 (f32_to_f16 / f16_to_f32, lattice-inference 0.1.2 page) --------
+    def f16_bits(self, x) -> np.ndarray:
+        """float32 -> binary16 bit patterns, round to nearest even."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint16)
+        self.lib.wqref_f16_bits_array(x.ctypes.data, out.ctypes.data, x.size)
+        return out
+
+    def f16_value(self, bits) -> np.ndarray:
+        """binary16 bit patterns -> exact float64 values."""
+        bits = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(bits.shape, dtype=np.float64)
+        self.lib.wqref_f16_value_array(bits.ctypes.data, out.ctypes.data, bits.size)
+        return out
+
+    # -- Q8_0 (quantize_row_q8_0, lattice-inference 0.1.2 page) --------------
+    def q8_0_quantize(self, w) -> np.ndarray:
+        """float32 [..., K] (K % 32 == 0) -> uint8 [..., K/32*34] Q8_0 bytes."""
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        k = w.shape[-1]
+        if k % QK:
+            raise ValueError("last dimension must be a multiple of 32")
+        out = np.empty(w.shape[:-1] + (k // QK * BLOCK_BYTES,), dtype=np.uint8)
+        if self.lib.wqref_q8_0_quantize(w.ctypes.data, out.ctypes.data, w.size) != 0:
+            raise ValueError("quantize failed")
+        return out
+
+    # -- decode and product (dispatch_matmul_half / gemm_q8 statements) -----
+    def decode(self, b, fmt: int, n: int, k: int) -> np.ndarray:
+        """Exact weights [n, k] (float64) of an f16 or Q8_0 matrix."""
+        b = np.ascontiguousarray(b)
+        out = np.empty((n, k), dtype=np.float64)
+        if self.lib.wqref_decode(b.ctypes.data, fmt, n, k, out.ctypes.data) != 0:
+            raise ValueError("decode: bad arguments")
+        return out
+
+    def encode(self, w, fmt: int) -> np.ndarray:
+        """Weight bytes of float32 w [n, k] in the given format, by the oracle's own encoders."""
+        if fmt == FMT_F16:
+            return self.f16_bits(w)
+        if fmt == FMT_Q8_0:
+            return self.q8_0_quantize(w)
+        raise ValueError(f"unknown format {fmt}")
+
+    def matmul(self, a, b, fmt: int, m: int, n: int, k: int, threads: int | None = None):
+        """(C, bound): C[m,n] = sum_k a[m,k] w[n,k] in float64 and the per-element
+        tolerance 1e-5 * sum_k |a[m,k] w[n,k]| + 1e-6."""
+        a = np.ascontiguousarray(a, dtype=np.float32)
+        b = np.ascontiguousarray(b)
+        if a.size < m * k:
+            raise ValueError("a too small")
+        c = np.empty((m, n), dtype=np.float64)
+        bound = np.empty((m, n), dtype=np.float64)
+        rc = self.lib.wqref_matmul(a.ctypes.data, b.ctypes.data, fmt, m, n, k, c.ctypes.data,
+                                   bound.ctypes.data, threads or _threads())
+        if rc != 0:
+            raise ValueError("matmul: bad arguments")
+        return c, bound
+
+    def matmul_entries(self, a, b, fmt: int, m: int, n: int, k: int, rows, cols,
+                       threads: int | None = None):
+        """(c, bound) for the selected outputs (rows[i], cols[i]) only."""
+        a = np.ascontiguousarray(a, dtype=np.float32)
+        b = np.ascontiguousarray(b)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        cols = np.ascontiguousarray(cols, dtype=np.int64)
+        if rows.shape != cols.shape:
+            raise ValueError("rows/cols shape mismatch")
+        c = np.empty(rows.shape, dtype=np.float64)
+        bound = np.empty(rows.shape, dtype=np.float64)
+        rc = self.lib.wqref_matmul_entries(a.ctypes.data, b.ctypes.data, fmt, m, n, k,
+                                           rows.ctypes.data, cols.ctypes.data, rows.size,
+                                           c.ctypes.data, bound.ctypes.data,
+                                           threads or _threads())
+        if rc != 0:
+            raise ValueError("matmul_entries: bad arguments")
+        return c, bound
+
+
+_default: Oracle | None = None
+
+
+def get() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def f16_bits(x):
+    return get().f16_bits(x)
+
+
+def f16_value(bits):
+    return get().f16_value(bits)
+
+
+def q8_0_quantize(w):
+    return get().q8_0_quantize(w)
+
+
+def decode(b, fmt, n, k):
+    return get().decode(b, fmt, n, k)
+
+
+def matmul(a, b, fmt, m, n, k, threads=None):
+    return get().matmul(a, b, fmt, m, n, k, threads)
+
+
+def matmul_entries(a, b, fmt, m, n, k, rows, cols, threads=None):
+    return get().matmul_entries(a, b, fmt, m, n, k, rows, cols, threads)
+
+
+def encode(w, fmt: int) -> np.ndarray:
+    """Weight bytes of float32 w [n, k] in the given format, by the oracle's own encoders."""
+    return get().encode(w, fmt)

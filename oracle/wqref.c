@@ -1,0 +1,285 @@
+/*
+ * wqref — CPU oracle for the mixed-precision weight matmul
+ *
+ *     C[M,N] = A[M,K] · B[N,K]^T        (C is overwritten: beta = 0)
+ *
+ * A holds f32 activations, row-major [M,K].  B holds weights, row-major
+ * [N,K], stored either as IEEE-754 binary16 ("f16") or as Q8_0 blocks:
+ * 34 bytes per 32 consecutive weights of a row, a little-endian f16 scale d
+ * followed by 32 two's-complement int8 codes q; the weight is d*q.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously-correct
+ * reference the GPU library is checked against.  Only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg may load it.  It shares
+ * no code, header, table or helper with the GPU library, and neither uses
+ * the other.
+ *
+ * Passages followed (page title; item on the page):
+ *  - lattice-inference 0.9.0, forward/metal_qwen35/inner/dispatch.rs;
+ *    doc comment of dispatch_matmul_half: C[M,N] = A[M,K] @ B_half[N,K]^T,
+ *    A f32, B f16 widened to f32 before accumulation, C f32.
+ *  - same page, dispatch_matmul_q8: Q8_0 weights are [N, K/32 * 34] bytes;
+ *    dispatch_gemm_q8: m == 0 or n == 0 is a no-op, K must be > 0 and a
+ *    multiple of 32.
+ *  - lattice-inference 0.1.2, forward/metal_qwen35.rs; kernel matmul_bt:
+ *    B is stored [N,K] and read transposed; kernels gemv_q8_decode and
+ *    gemm_q8: block = [f16 scale (2 B)][32 x int8 (32 B)], weight = d*q;
+ *    QK8_0 = 32, Q8_0_BLOCK_SIZE = 34 and quantize_row_q8_0 (the quantiser);
+ *    f32_to_f16 (round to nearest even, with subnormals) and f16_to_f32.
+ *  - ferrum-kernels 0.7.7, attention/metal/pipelines.rs; MetalPipelines::gemm:
+ *    the same product as sgemm(RowMajor, NoTrans, Trans, alpha=1, beta=0).
+ *
+ * Arithmetic: every decoded weight is an exact binary value and every product
+ * a[m,k] * w[n,k] is exact in double (at most 24 + 19 significant bits), so
+ * the only rounding is that of the double sum, about K * 2^-53 relative --
+ * far below the f32 tolerance the GPU path is held to.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { WQREF_F16 = 0, WQREF_Q8_0 = 1 };
+enum { WQREF_QK = 32, WQREF_BLOCK_BYTES = 34 };
+
+/* ------------------------------------------------------------------ f16 -- */
+
+/* Exact value of an IEEE-754 binary16 bit pattern (f16_to_f32 on the
+ * lattice-inference 0.1.2 page): sign s, 5-bit biased exponent e, 10-bit
+ * fraction f.  e == 0: f * 2^-24 (zero or subnormal); e == 31: inf or NaN;
+ * otherwise (1024 + f) * 2^(e - 25), i.e. (1 + f/1024) * 2^(e - 15). */
+double wqref_f16_value(uint16_t h) {
+    const int s = (h >> 15) & 1;
+    const int e = (h >> 10) & 0x1f;
+    const int f = h & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -24);
+    else if (e == 31)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + f), e - 25);
+    return s ? -mag : mag;
+}
+
+/* f32 -> binary16 bits, round to nearest, ties to even (f32_to_f16 on the
+ * lattice-inference 0.1.2 page).  Written at the value level: find the
+ * spacing 2^q of half values around |x| (q >= -24, the subnormal spacing),
+ * round |x| / 2^q to the nearest integer r with ties to even, and encode
+ * r * 2^q.  |x| >= 65520 (the midpoint between 65504, the largest finite
+ * half, and 65536) rounds to infinity.  NaN stays NaN with the quiet bit
+ * set and the top fraction bits kept, as on the page. */
+uint16_t wqref_f16_bits(float x) {
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (isnan(x)) {
+        uint16_t payload = (uint16_t)((u >> 13) & 0x3ffu);
+        return (uint16_t)(sign | 0x7c00u | payload | 0x200u);
+    }
+    const double ax = fabs((double)x);
+    if (isinf(x) || ax >= 65520.0) return (uint16_t)(sign | 0x7c00u);
+    if (ax == 0.0) return sign;
+    int e2;
+    frexp(ax, &e2);          /* ax in [2^(e2-1), 2^e2) */
+    int q = (e2 - 1) - 10;   /* spacing of 11-bit significands in that binade */
+    if (q < -24) q = -24;    /* below 2^-14 the spacing is the subnormal one */
+    const double r = nearbyint(ldexp(ax, -q)); /* exact scaling; RNE rounding */
+    if (q == -24) {
+        /* r * 2^-24 with r in [0, 2048]: the bit pattern is r itself
+         * (subnormals f * 2^-24, then (1024 + f) * 2^-24 for exponent 1,
+         * and r = 2048 is 2^-13 = exponent 2, fraction 0). */
+        return (uint16_t)(sign | (uint16_t)r);
+    }
+    int E = q + 10;          /* unbiased exponent of the binade */
+    double rr = r;           /* in [1024, 2048] */
+    if (rr >= 2048.0) {      /* rounding carried into the next binade */
+        rr = 1024.0;
+        E += 1;
+    }
+    if (E > 15) return (uint16_t)(sign | 0x7c00u);
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)((uint32_t)rr - 1024u));
+}
+
+void wqref_f16_bits_array(const float *x, uint16_t *out, int64_t count) {
+    for (int64_t i = 0; i < count; ++i) out[i] = wqref_f16_bits(x[i]);
+}
+
+void wqref_f16_value_array(const uint16_t *h, double *out, int64_t count) {
+    for (int64_t i = 0; i < count; ++i) out[i] = wqref_f16_value(h[i]);
+}
+
+/* ----------------------------------------------------------------- Q8_0 -- */
+
+/* Quantise count f32 values (count % 32 == 0) into count/32 Q8_0 blocks,
+ * following quantize_row_q8_0 on the lattice-inference 0.1.2 page, in f32:
+ *   amax = max |v| over the block (NaN ignored by the max),
+ *   d    = amax / 127,
+ *   id   = 1 / d, or 0 when d == 0,
+ *   bytes 0..1 = f16(d), little-endian,
+ *   q_i  = round(v_i * id) -- round half away from zero -- clamped to
+ *          [-127, 127] and stored as two's-complement int8.
+ * Returns 0, or -1 if count is negative or not a multiple of 32. */
+int wqref_q8_0_quantize(const float *x, uint8_t *out, int64_t count) {
+    if (count < 0 || count % WQREF_QK) return -1;
+    const int64_t nblocks = count / WQREF_QK;
+    for (int64_t b = 0; b < nblocks; ++b) {
+        const float *v = x + b * WQREF_QK;
+        uint8_t *o = out + b * WQREF_BLOCK_BYTES;
+        float amax = 0.0f;
+        for (int i = 0; i < WQREF_QK; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        const float d = amax / 127.0f;
+        const float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+        const uint16_t h = wqref_f16_bits(d);
+        o[0] = (uint8_t)(h & 0xff);
+        o[1] = (uint8_t)(h >> 8);
+        for (int i = 0; i < WQREF_QK; ++i) {
+            float t = roundf(v[i] * id);
+            int qi;
+            if (isnan(t))
+                qi = 0;
+            else if (t < -127.0f)
+                qi = -127;
+            else if (t > 127.0f)
+                qi = 127;
+            else
+                qi = (int)t;
+            o[2 + i] = (uint8_t)(int8_t)qi;
+        }
+    }
+    return 0;
+}
+
+/* Exact weight w[n,k] of a Q8_0 matrix with K columns (K % 32 == 0):
+ * row n starts at byte n*(K/32)*34, block j = k/32 at +34*j, scale d is the
+ * little-endian f16 at block bytes 0..1, q = int8 at block byte 2 + k%32. */
+static double q8_0_weight(const uint8_t *b, int64_t K, int64_t n, int64_t k) {
+    const int64_t nb = K / WQREF_QK;
+    const uint8_t *blk = b + (n * nb + k / WQREF_QK) * WQREF_BLOCK_BYTES;
+    const uint16_t h = (uint16_t)(blk[0] | (blk[1] << 8));
+    const int8_t q = (int8_t)blk[2 + k % WQREF_QK];
+    return wqref_f16_value(h) * (double)q;
+}
+
+static double weight(const void *b, int fmt, int64_t K, int64_t n, int64_t k) {
+    if (fmt == WQREF_F16) return wqref_f16_value(((const uint16_t *)b)[n * K + k]);
+    return q8_0_weight((const uint8_t *)b, K, n, k);
+}
+
+static int check_args(const void *b, int fmt, int64_t N, int64_t K) {
+    if (N < 0 || K < 0) return -1;
+    if (fmt != WQREF_F16 && fmt != WQREF_Q8_0) return -1;
+    if (fmt == WQREF_Q8_0 && (K == 0 || K % WQREF_QK)) return -1;
+    if (!b && N > 0 && K > 0) return -1;
+    return 0;
+}
+
+/* Decode the whole weight matrix into its exact values, w[n*K + k]. */
+int wqref_decode(const void *b, int fmt, int64_t N, int64_t K, double *w) {
+    if (check_args(b, fmt, N, K)) return -1;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) w[n * K + k] = weight(b, fmt, K, n, k);
+    return 0;
+}
+
+/* --------------------------------------------------------------- matmul -- */
+
+typedef struct {
+    const float *a;
+    const void *b;
+    int fmt;
+    int64_t M, N, K;
+    double *c, *bound;
+    /* full matrix: rows n in [n0, n1); entries: pairs [n0, n1) of the lists */
+    int64_t n0, n1;
+    const int64_t *em, *en;
+} job_t;
+
+/* One output: s = sum_k a[m,k] * w[n,k] and the tolerance scale
+ * 1e-5 * sum_k |a[m,k] * w[n,k]| + 1e-6, with w already decoded. */
+static void dot(const float *arow, const double *w, int64_t K, double *s_out, double *bnd_out) {
+    double s = 0.0, sa = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        const double p = (double)arow[k] * w[k];
+        s += p;
+        sa += fabs(p);
+    }
+    *s_out = s;
+    *bnd_out = 1e-5 * sa + 1e-6;
+}
+
+static void *matmul_worker(void *arg) {
+    job_t *j = (job_t *)arg;
+    double *w = (double *)malloc(sizeof(double) * (size_t)(j->K > 0 ? j->K : 1));
+    if (!w) return (void *)1;
+    for (int64_t n = j->n0; n < j->n1; ++n) {
+        for (int64_t k = 0; k < j->K; ++k) w[k] = weight(j->b, j->fmt, j->K, n, k);
+        for (int64_t m = 0; m < j->M; ++m)
+            dot(j->a + m * j->K, w, j->K, &j->c[m * j->N + n], &j->bound[m * j->N + n]);
+    }
+    free(w);
+    return NULL;
+}
+
+static void *entries_worker(void *arg) {
+    job_t *j = (job_t *)arg;
+    double *w = (double *)malloc(sizeof(double) * (size_t)(j->K > 0 ? j->K : 1));
+    if (!w) return (void *)1;
+    for (int64_t i = j->n0; i < j->n1; ++i) {
+        const int64_t m = j->em[i], n = j->en[i];
+        for (int64_t k = 0; k < j->K; ++k) w[k] = weight(j->b, j->fmt, j->K, n, k);
+        dot(j->a + m * j->K, w, j->K, &j->c[i], &j->bound[i]);
+    }
+    free(w);
+    return NULL;
+}
+
+static int run_jobs(job_t *base, int64_t total, int nthreads, void *(*fn)(void *)) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 128) nthreads = 128;
+    if (total < nthreads) nthreads = total > 0 ? (int)total : 1;
+    job_t jobs[128];
+    pthread_t tids[128];
+    int started[128] = {0};
+    int rc = 0;
+    const int64_t per = (total + nthreads - 1) / nthreads;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = *base;
+        jobs[t].n0 = per * t < total ? per * t : total;
+        jobs[t].n1 = per * (t + 1) < total ? per * (t + 1) : total;
+        if (t == nthreads - 1 || pthread_create(&tids[t], NULL, fn, &jobs[t]) != 0) {
+            if (fn(&jobs[t]) != NULL) rc = -1;
+        } else {
+            started[t] = 1;
+        }
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        void *ret = NULL;
+        if (started[t] && (pthread_join(tids[t], &ret) != 0 || ret != NULL)) rc = -1;
+    }
+    return rc;
+}
+
+/* Full product: c[m*N + n] and bound[m*N + n] for every m < M, n < N.
+ * K == 0 (f16 only) gives c = 0.  Returns 0, or -1 on bad arguments. */
+int wqref_matmul(const float *a, const void *b, int fmt, int64_t M, int64_t N, int64_t K,
+                 double *c, double *bound, int nthreads) {
+    if (M < 0 || check_args(b, fmt, N, K)) return -1;
+    if (M == 0 || N == 0) return 0;
+    if (!c || !bound || (!a && K > 0)) return -1;
+    job_t base = {a, b, fmt, M, N, K, c, bound, 0, 0, NULL, NULL};
+    return run_jobs(&base, N, nthreads, matmul_worker);
+}
+
+/* Selected outputs: c[i], bound[i] for the entries (rows[i], cols[i]). */
+int wqref_matmul_entries(const float *a, const void *b, int fmt, int64_t M, int64_t N, int64_t K,
+                         const int64_t *rows, const int64_t *cols, int64_t count, double *c,
+                         double *bound, int nthreads) {
+    if (M < 0 || count < 0 || check_args(b, fmt, N, K)) return -1;
+    for (int64_t i = 0; i < count; ++i)
+        if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N) return -1;
+    if (count == 0) return 0;
+    job_t base = {a, b, fmt, M, N, K, c, bound, 0, 0, rows, cols};
+    return run_jobs(&base, count, nthreads, entries_worker);
+}

@@ -1,0 +1,425 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself or with the GPU library.  Each
+pin checks the oracle against one of:
+  * values derived by hand from the pages (tests/golden/*.txt, cited there),
+  * a library routine (struct's and numpy's binary16 codecs, numpy float64
+    matmul on weights decoded by numpy),
+  * exact rational arithmetic (fractions.Fraction) on small inputs,
+  * invariants of the product (identity, one-hot, linearity, permutation).
+
+``PINS`` is also run against deliberately broken copies of the oracle
+(test_mutants_are_caught) to show that a plausible mistake anywhere in it --
+a dropped term, a wrong sign, index or byte order, a wrong rounding rule --
+fails at least one pin.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import struct
+import subprocess
+import tempfile
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import wqgen
+from oracle import FMT_F16, FMT_Q8_0
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# --------------------------------------------------------------- helpers --
+def _parse_float(tok: str) -> float:
+    if tok in ("inf", "-inf", "nan"):
+        return float(tok)
+    if "0x" in tok:
+        return float.fromhex(tok)
+    return float(tok)
+
+
+def _golden_f16():
+    rows = []
+    with open(os.path.join(GOLDEN, "f16_values.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            tok = line.split()
+            rows.append((_parse_float(tok[0]), int(tok[1], 16)))
+    return rows
+
+
+def _golden_q8():
+    blocks = []
+    with open(os.path.join(GOLDEN, "q8_0_blocks.txt")) as f:
+        lines = [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+    i = 0
+    while i < len(lines):
+        assert lines[i].startswith("block ")
+        vals = [_parse_float(t) for t in lines[i + 1].split()]
+        byts = bytes(int(t, 16) for t in lines[i + 2].split())
+        blocks.append((lines[i][6:], np.array(vals, dtype=np.float32), byts))
+        i += 3
+    return blocks
+
+
+def _golden_matmul():
+    a, f16, q8, c = {}, {}, {}, {}
+    dims = None
+    with open(os.path.join(GOLDEN, "matmul_tiny.txt")) as f:
+        for line in f:
+            tok = line.split()
+            if not tok or tok[0].startswith("#"):
+                continue
+            if tok[0] == "dims":
+                dims = tuple(int(t) for t in tok[1:4])
+            elif tok[0] == "a":
+                a[(int(tok[1]), int(tok[2]))] = float(tok[3])
+            elif tok[0] == "f16":
+                f16[(int(tok[1]), int(tok[2]))] = int(tok[3], 16)
+            elif tok[0] == "q8":
+                q8[int(tok[1])] = bytes(int(t, 16) for t in tok[2:])
+            elif tok[0] == "c":
+                c[(int(tok[1]), int(tok[2]))] = float(tok[3])
+    M, N, K = dims
+    A = np.zeros((M, K), np.float32)
+    for (m, k), v in a.items():
+        A[m, k] = v
+    B16 = np.zeros((N, K), np.uint16)
+    for (n, k), v in f16.items():
+        B16[n, k] = v
+    B8 = np.frombuffer(b"".join(q8[n] for n in range(N)), dtype=np.uint8).reshape(N, -1)
+    C = np.zeros((M, N))
+    for (m, n), v in c.items():
+        C[m, n] = v
+    return M, N, K, A, B16, B8, C
+
+
+def _numpy_decode(b, fmt, n, k):
+    """Weights decoded with numpy's own binary16 codec (independent of the oracle)."""
+    if fmt == FMT_F16:
+        return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float64).reshape(n, k)
+    raw = np.ascontiguousarray(b, dtype=np.uint8).reshape(n, k // 32, 34)
+    d = raw[:, :, 0:2].copy().view("<f2").astype(np.float64)          # [n, nb, 1]
+    q = raw[:, :, 2:34].copy().view(np.int8).astype(np.float64)       # [n, nb, 32]
+    return (d * q).reshape(n, k)
+
+
+def _dyadic_inputs(rng, m, n, k, fmt):
+    a = (rng.integers(-4, 5, size=(m, k)) * 0.5).astype(np.float32)
+    if fmt == FMT_F16:
+        vals = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0, 0.25, -0.25], np.float16)
+        b = vals[rng.integers(0, len(vals), size=(n, k))].view(np.uint16)
+    else:
+        blocks = []
+        for _ in range(n * k // 32):
+            d = [0x3800, 0x3c00, 0x3400][rng.integers(0, 3)]
+            q = rng.integers(-4, 5, size=32).astype(np.int8)
+            blocks.append(struct.pack("<H", d) + q.tobytes())
+        b = np.frombuffer(b"".join(blocks), np.uint8).reshape(n, -1)
+    return a, b
+
+
+# ------------------------------------------------------------------- pins --
+def pin_f16_decode_exhaustive(orc):
+    """All 65536 binary16 patterns against struct's '<e' decoder."""
+    bits = np.arange(65536, dtype=np.uint16)
+    got = orc.f16_value(bits)
+    want = np.array([struct.unpack("<e", int(b).to_bytes(2, "little"))[0] for b in bits])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def pin_f16_encode_golden(orc):
+    """Hand-derived patterns of tests/golden/f16_values.txt."""
+    rows = _golden_f16()
+    x = np.array([r[0] for r in rows], dtype=np.float32)
+    want = np.array([r[1] for r in rows], dtype=np.uint16)
+    got = orc.f16_bits(x)
+    bad = [(float(x[i]).hex(), hex(got[i]), hex(want[i])) for i in range(len(x)) if got[i] != want[i]]
+    assert not bad, bad
+
+
+def pin_f16_encode_vs_numpy(orc):
+    """Every exponent, with the fraction bits at and around each rounding point,
+    against numpy's float32 -> float16 cast (round to nearest even)."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x2001,
+                     0x3000, 0x4000, 0x7FFF, 0x8000, 0x8001, 0xC000, 0xFFFF], dtype=np.uint32)
+    u = (hi[:, None] | lows[None, :]).ravel()
+    rng = np.random.default_rng(1234)
+    u = np.concatenate([u, rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)])
+    x = u.view(np.float32)
+    finite = ~np.isnan(x)
+    got = orc.f16_bits(x)
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got[finite], want[finite])
+    # NaN keeps its sign, sets the quiet bit and stays NaN.
+    g = got[~finite]
+    assert np.all((g & 0x7c00) == 0x7c00) and np.all((g & 0x0200) == 0x0200)
+    assert np.array_equal(g >> 15, (u[~finite] >> 31).astype(np.uint16))
+
+
+def pin_q8_golden(orc):
+    """Hand-derived blocks of tests/golden/q8_0_blocks.txt (ties round away from zero,
+    little-endian scale, zero block, subnormal scale, clamp at +-127)."""
+    for name, vals, byts in _golden_q8():
+        assert vals.size == 32 and len(byts) == 34, name
+        got = orc.q8_0_quantize(vals.reshape(1, 32)).tobytes()
+        assert got == byts, (name, got.hex(" "), byts.hex(" "))
+
+
+def pin_q8_roundtrip(orc):
+    """Round trip of the quantiser on N(0, 0.02) and N(0, 1) weights.  With d the
+    f32 scale the quantiser divides by (amax/127) and h = f16(d) the stored one:
+      |x - d*q| <= d/2 + d*2^-16 (the slack covers the f32 product x * (1/d));
+      the decoded weight is exactly h*q;
+      |x - h*q| <= d/2 + 127*|d - h| + tiny."""
+    for std in (0.02, 1.0):
+        w = wqgen.normal((64, 256), seed=7, stream=9, std=std)
+        b = orc.q8_0_quantize(w)
+        raw = b.reshape(64, 8, 34)
+        q = raw[:, :, 2:].copy().view(np.int8).astype(np.float64).reshape(64, 256)
+        h = orc.f16_value(raw[:, :, 0].astype(np.uint16) | (raw[:, :, 1].astype(np.uint16) << 8))
+        amax = np.abs(w.reshape(64, 8, 32)).max(axis=2)
+        d = (amax.astype(np.float32) / np.float32(127.0)).astype(np.float64)
+        dd = np.repeat(d, 32, axis=1)
+        hh = np.repeat(h, 32, axis=1)
+        x = w.astype(np.float64)
+        assert np.all(np.abs(x - dd * q) <= dd / 2 + dd * 2.0 ** -16)
+        assert np.array_equal(orc.decode(b, FMT_Q8_0, 64, 256), hh * q)
+        assert np.all(np.abs(x - hh * q) <= dd / 2 + 127 * np.abs(dd - hh) + 1e-12)
+        assert np.all(np.abs(q) <= 127)
+        # the largest |x| of every block maps to +-127
+        idx = np.abs(w.reshape(64, 8, 32)).argmax(axis=2)
+        qmax = np.take_along_axis(q.reshape(64, 8, 32), idx[:, :, None], axis=2)[:, :, 0]
+        assert np.all(np.abs(qmax) == 127)
+
+
+def pin_q8_decode_handbuilt(orc):
+    """Blocks built byte by byte: scale 1.0, 0.5 and -2.0, every int8 code -128..127
+    (the decoder accepts -128 though the quantiser never writes it)."""
+    codes = np.arange(-128, 128, dtype=np.int8)
+    for hbits, dval in ((0x3c00, 1.0), (0x3800, 0.5), (0xc000, -2.0)):
+        blocks = b"".join(struct.pack("<H", hbits) + codes[i:i + 32].tobytes()
+                          for i in range(0, 256, 32))
+        b = np.frombuffer(blocks, np.uint8).reshape(1, -1)
+        got = orc.decode(b, FMT_Q8_0, 1, 256)[0]
+        assert np.array_equal(got, dval * codes.astype(np.float64))
+
+
+def pin_matmul_golden(orc):
+    """The hand-worked 2x3x32 example of tests/golden/matmul_tiny.txt, both formats."""
+    M, N, K, A, B16, B8, C = _golden_matmul()
+    for fmt, b in ((FMT_F16, B16), (FMT_Q8_0, B8)):
+        c, _ = orc.matmul(A, b, fmt, M, N, K)
+        assert np.array_equal(c, C), (fmt, c)
+
+
+def pin_bruteforce_fraction(orc):
+    """Tiny dyadic inputs: every product and sum is exact, so the oracle must equal
+    exact rational arithmetic bit for bit; and on N(0,1) activations it must be
+    within K * 2^-52 * sum|p| of the exact sum."""
+    rng = np.random.default_rng(5)
+    for fmt in (FMT_F16, FMT_Q8_0):
+        for m in (1, 2, 3):
+            for n in (1, 2, 3):
+                for k in (32, 64):
+                    a, b = _dyadic_inputs(rng, m, n, k, fmt)
+                    w = _numpy_decode(b, fmt, n, k)
+                    c, _ = orc.matmul(a, b, fmt, m, n, k)
+                    for i in range(m):
+                        for j in range(n):
+                            exact = sum(Fraction(float(a[i, t])) * Fraction(float(w[j, t]))
+                                        for t in range(k))
+                            assert c[i, j] == float(exact)
+        a = wqgen.normal((2, 96), seed=1, stream=0)
+        wf = wqgen.normal((3, 96), seed=1, stream=1, std=0.02)
+        b = orc.encode(wf, fmt)
+        w = _numpy_decode(b, fmt, 3, 96)
+        c, _ = orc.matmul(a, b, fmt, 2, 3, 96)
+        for i in range(2):
+            for j in range(3):
+                terms = [Fraction(float(a[i, t])) * Fraction(float(w[j, t])) for t in range(96)]
+                exact = sum(terms)
+                scale = float(sum(abs(t) for t in terms))
+                assert abs(Fraction(c[i, j]) - exact) <= Fraction(96 * scale) * Fraction(1, 2 ** 52)
+
+
+def pin_identity_and_onehot(orc):
+    """B = I gives C = A exactly; a one-hot B row n (weight v at column j(n)) gives
+    c[m,n] = a[m,j(n)] * v exactly, for f16 (incl. subnormal v) and Q8_0."""
+    K = 64
+    a = wqgen.normal((3, K), seed=2, stream=0)
+    eye16 = np.where(np.eye(K, dtype=bool), 0x3c00, 0).astype(np.uint16)
+    c, _ = orc.matmul(a, eye16, FMT_F16, 3, K, K)
+    assert np.array_equal(c, a.astype(np.float64))
+    blocks = []
+    for n in range(K):
+        for j in range(K // 32):
+            q = np.zeros(32, np.int8)
+            if n // 32 == j:
+                q[n % 32] = 1
+            blocks.append(struct.pack("<H", 0x3c00) + q.tobytes())
+    eye8 = np.frombuffer(b"".join(blocks), np.uint8).reshape(K, -1)
+    c, _ = orc.matmul(a, eye8, FMT_Q8_0, 3, K, K)
+    assert np.array_equal(c, a.astype(np.float64))
+    # one-hot rows
+    N = 40
+    cols = [(7 * n + 3) % K for n in range(N)]
+    vals16 = [0x0001, 0x03ff, 0x0400, 0x3c00, 0xbc00, 0x7bff, 0x3555, 0xc001] * 5
+    b16 = np.zeros((N, K), np.uint16)
+    for n in range(N):
+        b16[n, cols[n]] = vals16[n]
+    c, _ = orc.matmul(a, b16, FMT_F16, 3, N, K)
+    v = np.array([struct.unpack("<e", struct.pack("<H", h))[0] for h in vals16])
+    assert np.array_equal(c, a[:, cols].astype(np.float64) * v[None, :])
+    blocks = []
+    qs = [1, -1, 127, -128, 5, -77, 64, 3] * 5
+    ds = [0x3c00, 0x0001, 0x2e66, 0xc000, 0x7bff, 0x3800, 0x0400, 0x251f] * 5
+    for n in range(N):
+        for j in range(K // 32):
+            q = np.zeros(32, np.int8)
+            if cols[n] // 32 == j:
+                q[cols[n] % 32] = qs[n]
+            blocks.append(struct.pack("<H", ds[n]) + q.tobytes())
+    b8 = np.frombuffer(b"".join(blocks), np.uint8).reshape(N, -1)
+    c, _ = orc.matmul(a, b8, FMT_Q8_0, 3, N, K)
+    dv = np.array([struct.unpack("<e", struct.pack("<H", h))[0] for h in ds])
+    assert np.array_equal(c, a[:, cols].astype(np.float64) * (dv * np.array(qs))[None, :])
+
+
+def pin_invariants(orc):
+    """GEMV(a_m) equals GEMM row m; C(2A) = 2C(A) and C(-A) = -C(A) exactly;
+    permuting the rows of B permutes the columns of C; entries match the full product."""
+    M, N, K = 5, 37, 96
+    a = wqgen.normal((M, K), seed=4, stream=0)
+    wf = wqgen.normal((N, K), seed=4, stream=1, std=0.02)
+    for fmt in (FMT_F16, FMT_Q8_0):
+        b = orc.encode(wf, fmt)
+        c, bound = orc.matmul(a, b, fmt, M, N, K)
+        for m in range(M):
+            cm, _ = orc.matmul(a[m:m + 1], b, fmt, 1, N, K)
+            assert np.array_equal(cm[0], c[m])
+        c2, _ = orc.matmul(2 * a, b, fmt, M, N, K)
+        assert np.array_equal(c2, 2 * c)
+        cn, _ = orc.matmul(-a, b, fmt, M, N, K)
+        assert np.array_equal(cn, -c)
+        perm = np.random.default_rng(0).permutation(N)
+        cp, _ = orc.matmul(a, np.ascontiguousarray(b[perm]), fmt, M, N, K)
+        assert np.array_equal(cp, c[:, perm])
+        rows = np.array([0, 4, 2, 1, 3])
+        cols = np.array([36, 0, 17, 5, 20])
+        ce, be = orc.matmul_entries(a, b, fmt, M, N, K, rows, cols)
+        assert np.array_equal(ce, c[rows, cols]) and np.array_equal(be, bound[rows, cols])
+
+
+def pin_numpy_matmul(orc):
+    """Against numpy float64 A @ W.T with W decoded by numpy (library routines only),
+    including ragged shapes, K = 0 and the tolerance scale 1e-5*sum|a w| + 1e-6."""
+    for (M, N, K) in ((1, 300, 256), (7, 129, 320), (33, 65, 1024)):
+        a = wqgen.normal((M, K), seed=M, stream=0)
+        wf = wqgen.normal((N, K), seed=M, stream=1, std=0.02)
+        for fmt in (FMT_F16, FMT_Q8_0):
+            b = orc.encode(wf, fmt)
+            w = _numpy_decode(b, fmt, N, K)
+            c, bound = orc.matmul(a, b, fmt, M, N, K)
+            a64 = a.astype(np.float64)
+            ref = a64 @ w.T
+            sabs = np.abs(a64) @ np.abs(w).T
+            assert np.all(np.abs(c - ref) <= 1e-12 * sabs + 1e-300)
+            assert np.allclose(bound, 1e-5 * sabs + 1e-6, rtol=1e-12, atol=0)
+    c, bound = orc.matmul(np.zeros((2, 0), np.float32), np.zeros((3, 0), np.uint16), FMT_F16, 2, 3, 0)
+    assert np.array_equal(c, np.zeros((2, 3))) and np.allclose(bound, 1e-6)
+
+
+PINS = [
+    pin_f16_decode_exhaustive,
+    pin_f16_encode_golden,
+    pin_f16_encode_vs_numpy,
+    pin_q8_golden,
+    pin_q8_roundtrip,
+    pin_q8_decode_handbuilt,
+    pin_matmul_golden,
+    pin_bruteforce_fraction,
+    pin_identity_and_onehot,
+    pin_invariants,
+    pin_numpy_matmul,
+]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(orc, pin):
+    pin(orc)
+
+
+def test_argument_errors(orc):
+    a = np.zeros((1, 48), np.float32)
+    with pytest.raises(ValueError):
+        orc.matmul(a, np.zeros((1, 51), np.uint8), FMT_Q8_0, 1, 1, 48)  # K % 32 != 0
+    with pytest.raises(ValueError):
+        orc.matmul(a, np.zeros((1, 0), np.uint8), FMT_Q8_0, 1, 1, 0)    # Q8_0 with K == 0
+    with pytest.raises(ValueError):
+        orc.matmul(a, np.zeros((1, 48), np.uint16), 7, 1, 1, 48)        # unknown format
+    with pytest.raises(ValueError):
+        orc.q8_0_quantize(np.zeros((1, 40), np.float32))
+    c, _ = orc.matmul(a, np.zeros((1, 48), np.uint16), FMT_F16, 0, 1, 48)
+    assert c.shape == (0, 1)
+
+
+# --------------------------------------------------------------- mutants --
+# Each entry plants one plausible mistake in a copy of wqref.c.
+MUTANTS = {
+    "drop_last_k_term": ("for (int64_t k = 0; k < K; ++k) {\n        const double p",
+                         "for (int64_t k = 0; k + 1 < K; ++k) {\n        const double p"),
+    "reversed_k_index": ("((const uint16_t *)b)[n * K + k]", "((const uint16_t *)b)[n * K + (K - 1 - k)]"),
+    "q8_code_sign": ("return wqref_f16_value(h) * (double)q;", "return wqref_f16_value(h) * (double)(-q);"),
+    "q8_scale_big_endian": ("(uint16_t)(blk[0] | (blk[1] << 8))", "(uint16_t)(blk[1] | (blk[0] << 8))"),
+    "q8_block_stride_32": ("(n * nb + k / WQREF_QK) * WQREF_BLOCK_BYTES", "(n * nb + k / WQREF_QK) * 32"),
+    "f16_truncate": ("nearbyint(ldexp(ax, -q))", "floor(ldexp(ax, -q))"),
+    "f16_flush_subnormal": ("if (q < -24) q = -24;", "if (q < -24) q = -24; if (e2 - 1 < -14) return sign;"),
+    "f16_exponent_bias": ("(uint16_t)((E + 15) << 10)", "(uint16_t)((E + 16) << 10)"),
+    "q8_round_ties_even": ("roundf(v[i] * id)", "rintf(v[i] * id)"),
+    "q8_scale_over_128": ("amax / 127.0f", "amax / 128.0f"),
+    "q8_scale_byte_order_write": ("o[0] = (uint8_t)(h & 0xff);\n        o[1] = (uint8_t)(h >> 8);",
+                                  "o[1] = (uint8_t)(h & 0xff);\n        o[0] = (uint8_t)(h >> 8);"),
+    "f32_accumulate": ("s += p;", "s = (double)(float)(s + p);"),
+    "row_zero_only": ("dot(j->a + m * j->K, w", "dot(j->a + 0 * j->K, w"),
+    "abs_sum_dropped": ("sa += fabs(p);", "sa += p;"),
+}
+
+
+@pytest.mark.slow
+def test_mutants_are_caught():
+    src = os.path.join(os.path.dirname(oracle.__file__), "wqref.c")
+    text = open(src).read()
+    tmp = tempfile.mkdtemp(prefix="wqref_mut_")
+    try:
+        survivors = []
+        for name, (old, new) in MUTANTS.items():
+            assert text.count(old) >= 1, f"mutation site missing: {name}"
+            msrc = os.path.join(tmp, f"{name}.c")
+            with open(msrc, "w") as f:
+                f.write(text.replace(old, new))
+            so = os.path.join(tmp, f"{name}.so")
+            subprocess.run(["gcc", *oracle.CFLAGS, "-o", so, msrc, "-lm"], check=True)
+            mut = oracle.Oracle(so)
+            caught = False
+            for pin in PINS:
+                try:
+                    pin(mut)
+                except AssertionError:
+                    caught = True
+                    break
+            if not caught:
+                survivors.append(name)
+        assert not survivors, f"mutants not caught by any pin: {survivors}"
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)

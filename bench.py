@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of libwqmm on one MI355X.
+
+Headline workload (one JSON line on stdout): the f16-weight decode GEMV suite
+at hidden 2048, M = 1, (N, K) = (6144, 2048) gate/up, (2048, 6144) down,
+(2048, 2048) o_proj and (151936, 2048) LM head; A ~ N(0,1) f32, B ~ N(0,0.02)
+cast to f16 on the GPU, seed 0.  One step runs the four GEMVs once through
+wq_matmul.  ``value`` = weight bytes of all timed steps / timed wall time
+(GB/s), inputs resident in HBM.  Every weight matrix is rotated over enough
+distinct copies (>= 1 GiB in total) that each launch reads cold from HBM
+rather than from the 256 MB Infinity Cache.
+
+``roofline`` is for the dominant kernel, the LM-head GEMV: its algorithmic
+bytes (N*K*2 weight bytes) over its average launch duration, measured with
+HIP events around each launch on the stream it runs on, inside the timed
+region.  ``cpu_baseline`` times the CPU oracle (all host cores it uses) on the
+same suite.  ``secondary`` reports the other configurations: the Q8_0 decode
+suite, the f16 prefill GEMM at M = 512, the Q8_0 M sweep, and a plain device
+copy as the achievable-bandwidth reference.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode GEMV weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+ROTATE_BYTES = 1 << 30
+DECODE = [("gate_up", 6144, 2048), ("down", 2048, 6144), ("o_proj", 2048, 2048), ("lm_head", 151936, 2048)]
+PREFILL = [(512, 6144, 2048), (512, 2048, 6144)]
+SWEEP_SHAPES = [(11008, 4096), (4096, 11008)]
+SWEEP_M = [1, 2, 4, 8, 16, 64, 512]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-secondary", action="store_true", help="headline suite only")
+    p.add_argument("--only", choices=["f16", "q8", "prefill", "sweep"], default=None,
+                   help="run one workload only (for profiling); prints no headline line")
+    return p.parse_args()
+
+
+class Suite:
+    """Decode GEMV suite in one format with rotated weight copies."""
+
+    def __init__(self, wq, wqgen, torch, fmt, seed, host_weights):
+        self.fmt = fmt
+        self.items = []
+        for name, n, k in DECODE:
+            w = host_weights[(n, k)]
+            wd = torch.from_numpy(w).cuda()
+            b0 = wq.pack_f16(wd) if fmt == wq.WQ_FMT_F16 else wq.quantize_q8_0(wd)
+            del wd
+            nbytes = wq.weight_bytes(n, k, fmt)
+            copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+            bs = [b0] + [b0.clone() for _ in range(copies - 1)]
+            a = torch.from_numpy(wqgen.activations(1, k, seed)).cuda()
+            c = torch.empty((1, n), dtype=torch.float32, device="cuda")
+            self.items.append(dict(name=name, n=n, k=k, bs=bs, a=a, c=c, bytes=nbytes))
+        self.bytes_per_step = sum(it["bytes"] for it in self.items)
+        torch.cuda.synchronize()
+
+    def step(self, wq, i, events=None):
+        for j, it in enumerate(self.items):
+            b = it["bs"][i % len(it["bs"])]
+            if events is not None:
+                events[j][0].record()
+            wq.wq_matmul(it["a"], b, it["c"], 1, it["n"], it["k"], self.fmt)
+            if events is not None:
+                events[j][1].record()
+
+
+def time_suite(torch, wq, suite, steps, warmup, per_kernel):
+    """Returns (total seconds, per-item mean launch seconds or None)."""
+    for i in range(warmup):
+        suite.step(wq, i)
+    torch.cuda.synchronize()
+    ev = None
+    if per_kernel:
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+              for _ in suite.items]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        suite.step(wq, warmup + i, [e[i] for e in ev] if ev else None)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total = start.elapsed_time(end) / 1e3
+    per = None
+    if ev:
+        per = [sum(e[i][0].elapsed_time(e[i][1]) for i in range(steps)) / steps / 1e3 for e in ev]
+    return total, wall, per
+
+
+def time_launches(torch, fn, iters, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        fn(warmup + i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / 1e3 / iters
+
+
+def cpu_baseline(host_weights, seed, budget_s=12.0):
+    """The CPU oracle on the f16 decode suite: whole suite repeated until the
+    time budget is used (at least one pass)."""
+    import numpy as np
+
+    import oracle
+    import wqgen
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    enc = {(n, k): oracle.encode(host_weights[(n, k)], oracle.FMT_F16) for _, n, k in DECODE}
+    acts = {k: wqgen.activations(1, k, seed) for _, _, k in DECODE}
+    bytes_done, t_total, passes = 0, 0.0, 0
+    while passes == 0 or t_total < budget_s:
+        for _, n, k in DECODE:
+            t0 = time.perf_counter()
+            oracle.matmul(acts[k], enc[(n, k)], oracle.FMT_F16, 1, n, k, threads=threads)
+            t_total += time.perf_counter() - t0
+            bytes_done += 2 * n * k
+        passes += 1
+    del np
+    return {"value": round(bytes_done / t_total / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the f16 decode suite (4 GEMVs, M=1, {bytes_done // passes} "
+                      f"weight bytes per pass), f64 accumulation, {t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path (pass --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import gemm_wq_gemv_amd as wq
+    import wqgen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    F16, Q8 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0
+
+    log("drawing inputs")
+    host_weights = {(n, k): wqgen.weights(n, k, args.seed) for _, n, k in DECODE}
+
+    secondary = {}
+    only = args.only
+    result = None
+
+    if only in (None, "f16"):
+        log("f16 decode suite: encoding + rotation copies")
+        s16 = Suite(wq, wqgen, torch, F16, args.seed, host_weights)
+        log("f16 decode suite: timing")
+        total, wall, per = time_suite(torch, wq, s16, args.steps, args.warmup, per_kernel=True)
+        lm = [i for i, it in enumerate(s16.items) if it["name"] == "lm_head"][0]
+        lm_bytes = s16.items[lm]["bytes"]
+        lm_s = per[lm]
+        achieved = lm_bytes / lm_s / 1e9
+        value = s16.bytes_per_step * args.steps / total / 1e9
+        result = {
+            "metric": METRIC,
+            "value": round(value, 2),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(total / args.steps * 1e3, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f32",
+            "data": "synthetic",
+            "config": {
+                "workload": "f16-weight decode GEMV suite at hidden 2048, M=1: (N,K) = (6144,2048) gate/up, "
+                            "(2048,6144) down, (2048,2048) o_proj, (151936,2048) LM head; A ~ N(0,1) f32, "
+                            "B ~ N(0,0.02) cast to f16; seed 0",
+                "weight_bytes_per_step": s16.bytes_per_step,
+                "rotation": {it["name"]: len(it["bs"]) for it in s16.items},
+                "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                "wall_s": round(wall, 4),
+            },
+            "roofline": {
+                "kernel": "gemv_f16_vec (LM head, N=151936, K=2048)",
+                "bound": "hbm",
+                "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None,
+                "avg_launch_us": round(lm_s * 1e6, 3),
+                "algorithmic_bytes_per_launch": lm_bytes,
+            },
+        }
+        secondary["f16_decode_per_kernel"] = {
+            it["name"]: {"us": round(t * 1e6, 3), "GB/s": round(it["bytes"] / t / 1e9, 1),
+                         "frac_hbm": round(it["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4)}
+            for it, t in zip(s16.items, per)}
+        del s16
+        torch.cuda.empty_cache()
+
+    if not args.no_secondary and only in (None, "q8"):
+        log("Q8_0 decode suite")
+        s8 = Suite(wq, wqgen, torch, Q8, args.seed, host_weights)
+        total, _, per = time_suite(torch, wq, s8, args.steps, args.warmup, per_kernel=True)
+        secondary["q8_decode_suite"] = {
+            "GB/s": round(s8.bytes_per_step * args.steps / total / 1e9, 2),
+            "frac_hbm": round(s8.bytes_per_step * args.steps / total / 1e9 / HBM_PEAK_GBS, 4),
+            "per_kernel": {it["name"]: {"us": round(t * 1e6, 3), "GB/s": round(it["bytes"] / t / 1e9, 1)}
+                           for it, t in zip(s8.items, per)},
+        }
+        del s8
+        torch.cuda.empty_cache()
+
+    if not args.no_secondary and only in (None, "prefill"):
+        log("f16 prefill GEMM, M=512")
+        out = {}
+        for m, n, k in PREFILL:
+            w = wqgen.weights(n, k, args.seed)
+            b = wq.pack_f16(torch.from_numpy(w).cuda())
+            a = torch.from_numpy(wqgen.activations(m, k, args.seed)).cuda()
+            c = torch.empty((m, n), device="cuda")
+            t = time_launches(torch, lambda i: wq.wq_matmul(a, b, c, m, n, k, F16), max(10, args.steps // 2),
+                              args.warmup)
+            tf = 2.0 * m * n * k / t / 1e12
+            out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(tf, 2),
+                                   "frac_mfma_fp32": round(tf / FP32_MFMA_PEAK_TFLOPS, 4)}
+        secondary["f16_prefill_m512"] = out
+
+    if not args.no_secondary and only in (None, "sweep"):
+        log("Q8_0 M sweep")
+        out = {}
+        for n, k in SWEEP_SHAPES:
+            w = wqgen.weights(n, k, args.seed)
+            b0 = wq.quantize_q8_0(torch.from_numpy(w).cuda())
+            nbytes = wq.weight_bytes(n, k, Q8)
+            bs = [b0] + [b0.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / nbytes)) - 1)]
+            a_all = torch.from_numpy(wqgen.activations(max(SWEEP_M), k, args.seed)).cuda()
+            for m in SWEEP_M:
+                a = a_all[:m].contiguous()
+                c = torch.empty((m, n), device="cuda")
+                t = time_launches(torch, lambda i: wq.wq_matmul(a, bs[i % len(bs)], c, m, n, k, Q8),
+                                  max(10, args.steps // 2), args.warmup)
+                out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(nbytes / t / 1e9, 1),
+                                       "TFLOP/s": round(2.0 * m * n * k / t / 1e12, 2),
+                                       "route": "gemv" if wq.wq_route_for(m, n, k, Q8) == wq.WQ_ROUTE_GEMV
+                                       else "gemm"}
+            del bs, b0
+            torch.cuda.empty_cache()
+        secondary["q8_sweep"] = out
+
+    if not args.no_secondary and only is None:
+        log("device copy reference")
+        nb = 1 << 30
+        src = torch.empty(nb // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        t = time_launches(torch, lambda i: dst.copy_(src), 10, 3)
+        secondary["device_copy_1GiB"] = {"us": round(t * 1e6, 1), "GB/s_read_plus_write": round(2 * nb / t / 1e9, 1)}
+        del src, dst
+
+    if result is None:
+        log(json.dumps(secondary))
+        return
+    if not args.no_cpu:
+        log("CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(host_weights, args.seed)
+    else:
+        result["cpu_baseline"] = None
+    result["secondary"] = secondary
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

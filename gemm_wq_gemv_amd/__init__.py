@@ -1,0 +1,233 @@
+"""Python binding of libwqmm (argument marshalling only).
+
+Each function has the name and argument order of the C entry point declared in
+``include/wqmm.h`` and forwards to it through ctypes: tensors become device
+pointers, the stream becomes a ``hipStream_t``.  All computation happens in
+the library's HIP kernels; there is no fallback of any kind, and importing
+this module fails loudly if ``libwqmm.so`` is missing and cannot be built.
+
+PyTorch supplies device memory and streams.  ``torch`` is imported before the
+library is loaded so that libwqmm binds to the HIP runtime torch already
+loaded (both carry the soname ``libamdhip64.so.7``): one runtime per process,
+so torch's stream handles and device pointers are valid in the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must precede loading libwqmm, see above)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwqmm.so")
+
+WQ_FMT_F16 = 0
+WQ_FMT_Q8_0 = 1
+
+WQ_OK = 0
+WQ_ERR_NULL = 1
+WQ_ERR_SHAPE = 2
+WQ_ERR_K = 3
+WQ_ERR_FORMAT = 4
+WQ_ERR_ALIGN = 5
+WQ_ERR_LAUNCH = 6
+WQ_ERR_ALIAS = 7
+WQ_ERR_ROUTE = 8
+
+WQ_ROUTE_AUTO = 0
+WQ_ROUTE_GEMV = 1
+WQ_ROUTE_GEMM = 2
+
+Q8_0_BLOCK_BYTES = 34
+Q8_0_BLOCK_WEIGHTS = 32
+
+
+class WQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sigs = {
+        "wq_gemv_f16": (I, [P, P, P, I64, I64, P]),
+        "wq_gemv_q8_0": (I, [P, P, P, I64, I64, P]),
+        "wq_gemm_f16": (I, [P, P, P, I64, I64, I64, P]),
+        "wq_gemm_q8_0": (I, [P, P, P, I64, I64, I64, P]),
+        "wq_matmul": (I, [P, P, P, I64, I64, I64, I, P]),
+        "wq_pack_f16": (I, [P, P, I64, P]),
+        "wq_quantize_q8_0": (I, [P, P, I64, P]),
+        "wq_route_for": (I, [I64, I64, I64, I]),
+        "wq_set_forced_route": (I, [I]),
+        "wq_route_count": (ctypes.c_uint64, [I]),
+        "wq_reset_route_counts": (None, []),
+        "wq_status_str": (ctypes.c_char_p, [I]),
+        "wq_abi_version": (I, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+# ----------------------------------------------------------------- helpers --
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream))
+
+
+def _need(t, nbytes: int, what: str):
+    if t is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+
+
+def _dtype(t, dtypes, what):
+    if t is not None and t.dtype not in dtypes:
+        raise TypeError(f"{what} must be one of {dtypes}, got {t.dtype}")
+
+
+_F32 = (torch.float32,)
+_H = (torch.uint16, torch.int16, torch.float16)
+_U8 = (torch.uint8, torch.int8)
+
+
+def weight_bytes(n: int, k: int, fmt: int) -> int:
+    """Bytes of an [n, k] weight matrix in the given format."""
+    if fmt == WQ_FMT_F16:
+        return 2 * n * k
+    return n * (k // Q8_0_BLOCK_WEIGHTS) * Q8_0_BLOCK_BYTES
+
+
+def _check(status: int, what: str):
+    if status != WQ_OK:
+        raise WQError(status, what)
+
+
+def _sizes(a, b, c, m, n, k, fmt):
+    if m > 0 and n > 0:
+        _dtype(a, _F32, "a")
+        _dtype(c, _F32, "c")
+        _dtype(b, _H if fmt == WQ_FMT_F16 else _U8, "b")
+        _need(a, 4 * m * k, "a")
+        _need(c, 4 * m * n, "c")
+        if k >= 0 and (fmt != WQ_FMT_Q8_0 or k % 32 == 0):
+            _need(b, weight_bytes(n, k, fmt), "b")
+
+
+# ------------------------------------------------------------ entry points --
+def wq_gemv_f16(a, b, c, n: int, k: int, stream=None) -> None:
+    _sizes(a, b, c, 1, n, k, WQ_FMT_F16)
+    _check(_lib.wq_gemv_f16(_ptr(a), _ptr(b), _ptr(c), n, k, _stream(stream)), "wq_gemv_f16")
+
+
+def wq_gemv_q8_0(a, b, c, n: int, k: int, stream=None) -> None:
+    _sizes(a, b, c, 1, n, k, WQ_FMT_Q8_0)
+    _check(_lib.wq_gemv_q8_0(_ptr(a), _ptr(b), _ptr(c), n, k, _stream(stream)), "wq_gemv_q8_0")
+
+
+def wq_gemm_f16(a, b, c, m: int, n: int, k: int, stream=None) -> None:
+    _sizes(a, b, c, m, n, k, WQ_FMT_F16)
+    _check(_lib.wq_gemm_f16(_ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(stream)), "wq_gemm_f16")
+
+
+def wq_gemm_q8_0(a, b, c, m: int, n: int, k: int, stream=None) -> None:
+    _sizes(a, b, c, m, n, k, WQ_FMT_Q8_0)
+    _check(_lib.wq_gemm_q8_0(_ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(stream)), "wq_gemm_q8_0")
+
+
+def wq_matmul(a, b, c, m: int, n: int, k: int, fmt: int, stream=None) -> None:
+    if fmt in (WQ_FMT_F16, WQ_FMT_Q8_0):
+        _sizes(a, b, c, m, n, k, fmt)
+    _check(_lib.wq_matmul(_ptr(a), _ptr(b), _ptr(c), m, n, k, fmt, _stream(stream)), "wq_matmul")
+
+
+def wq_pack_f16(w, out, count: int, stream=None) -> None:
+    if count > 0:
+        _dtype(w, _F32, "w")
+        _dtype(out, _H, "out")
+        _need(w, 4 * count, "w")
+        _need(out, 2 * count, "out")
+    _check(_lib.wq_pack_f16(_ptr(w), _ptr(out), count, _stream(stream)), "wq_pack_f16")
+
+
+def wq_quantize_q8_0(w, out, count: int, stream=None) -> None:
+    if count > 0 and count % 32 == 0:
+        _dtype(w, _F32, "w")
+        _dtype(out, _U8, "out")
+        _need(w, 4 * count, "w")
+        _need(out, count // 32 * Q8_0_BLOCK_BYTES, "out")
+    _check(_lib.wq_quantize_q8_0(_ptr(w), _ptr(out), count, _stream(stream)), "wq_quantize_q8_0")
+
+
+def wq_route_for(m: int, n: int, k: int, fmt: int) -> int:
+    return int(_lib.wq_route_for(m, n, k, fmt))
+
+
+def wq_set_forced_route(route: int) -> int:
+    return int(_lib.wq_set_forced_route(route))
+
+
+def wq_route_count(route: int) -> int:
+    return int(_lib.wq_route_count(route))
+
+
+def wq_reset_route_counts() -> None:
+    _lib.wq_reset_route_counts()
+
+
+def status_str(status: int) -> str:
+    return _lib.wq_status_str(status).decode()
+
+
+wq_status_str = status_str
+
+
+def wq_abi_version() -> int:
+    return int(_lib.wq_abi_version())
+
+
+# ------------------------------------------------------- tensor conveniences --
+def pack_f16(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """f32 [n, k] device tensor -> binary16 bits (uint16 [n, k]) via wq_pack_f16."""
+    out = torch.empty(w.shape, dtype=torch.uint16, device=w.device)
+    wq_pack_f16(w, out, w.numel(), stream)
+    return out
+
+
+def quantize_q8_0(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """f32 [n, k] device tensor (k % 32 == 0) -> Q8_0 bytes (uint8 [n, k/32*34])."""
+    n, k = w.shape
+    out = torch.empty((n, k // 32 * Q8_0_BLOCK_BYTES), dtype=torch.uint8, device=w.device)
+    wq_quantize_q8_0(w, out, w.numel(), stream)
+    return out
+
+
+def matmul(a: torch.Tensor, b: torch.Tensor, n: int, k: int, fmt: int, out=None, stream=None) -> torch.Tensor:
+    """C = A . B^T for f32 a [m, k] and encoded weights b (via wq_matmul)."""
+    m = a.numel() // k if k else a.shape[0]
+    c = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=a.device)
+    wq_matmul(a, b, c, m, n, k, fmt, stream)
+    return c

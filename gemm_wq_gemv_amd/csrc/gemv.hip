@@ -1,0 +1,347 @@
+// Decode GEMV (M = 1): c[n] = sum_k a[k] * w[n, k] for f16 and Q8_0 weights.
+//
+// The operation is the M = 1 case of dispatch_matmul_half / dispatch_matmul_q8
+// (lattice-inference 0.9.0, dispatch.rs) and of the kernels gemv_decode_m1 and
+// gemv_q8_decode (lattice-inference 0.1.2, metal_qwen35.rs).  Those kernels
+// were written for 32-lane Apple SIMD groups (one threadgroup per output row
+// for f16, two rows per threadgroup for Q8_0).  On CDNA4 the work is bound by
+// HBM bandwidth, so the design here is about the byte stream:
+//
+//  * A wave (64 lanes) owns whole weight rows.  The activation vector is held
+//    in VGPRs for the wave's lifetime (each lane keeps the slice of `a` that
+//    matches the weight bytes it reads), so `a` is read from L2 once per wave
+//    instead of once per row.
+//  * f16: each lane reads 16-byte chunks (8 weights) of R rows at once with
+//    128-bit non-temporal loads; a row of K = 2048 is four such loads per lane,
+//    fully coalesced.  f16 -> f32 widening happens in registers.
+//  * Q8_0: a 34-byte block is only 2-byte aligned, so the wave first copies S
+//    whole rows (a contiguous, 16-byte aligned byte range when K % 256 == 0)
+//    into its LDS slice with coalesced 128-bit loads, then each lane decodes
+//    whole blocks from LDS (scale, 32 int8 codes) against its register slice of
+//    `a`: sum_q = sum_i q_i a_i, acc += d * sum_q, as the pages apply d after
+//    the block's int8 dot product.
+//  * Reductions: DPP within 16-lane rows, lane-xor across rows (64 lanes).
+//  * Persistent waves: the grid is sized to fill the chip once and every wave
+//    walks row groups with a stride, balanced so all waves do equal work.
+#include "wq_internal.h"
+
+#include <algorithm>
+
+namespace wq {
+namespace {
+
+// ------------------------------------------------------------------ f16 ----
+
+__device__ __forceinline__ float dot8_f16(uint4 w, float4 lo, float4 hi, float acc) {
+    acc = fmaf(half_bits_to_float(w.x & 0xffffu), lo.x, acc);
+    acc = fmaf(half_bits_to_float(w.x >> 16), lo.y, acc);
+    acc = fmaf(half_bits_to_float(w.y & 0xffffu), lo.z, acc);
+    acc = fmaf(half_bits_to_float(w.y >> 16), lo.w, acc);
+    acc = fmaf(half_bits_to_float(w.z & 0xffffu), hi.x, acc);
+    acc = fmaf(half_bits_to_float(w.z >> 16), hi.y, acc);
+    acc = fmaf(half_bits_to_float(w.w & 0xffffu), hi.z, acc);
+    acc = fmaf(half_bits_to_float(w.w >> 16), hi.w, acc);
+    return acc;
+}
+
+// T 16-byte chunk slots per lane cover K = 512*T weights; R rows per step.
+// FULL: K == 512*T exactly, so no slot needs a bounds check.
+// Requires K % 8 == 0 and 16-byte aligned a and b.
+template <int T, int R, bool FULL>
+__global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
+                                                    const uint16_t *__restrict__ b,
+                                                    float *__restrict__ c, int64_t n, int64_t k,
+                                                    int64_t groups) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+    const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) / kWave;
+    const int nch = static_cast<int>(k >> 3);
+
+    float4 alo[T], ahi[T];
+    const float4 *a4 = reinterpret_cast<const float4 *>(a);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int idx = t * kWave + lane;
+        if (FULL || idx < nch) {
+            alo[t] = a4[2 * idx];
+            ahi[t] = a4[2 * idx + 1];
+        } else {
+            alo[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+            ahi[t] = alo[t];
+        }
+    }
+
+    for (int64_t g = wave; g < groups; g += nwaves) {
+        const int64_t r0 = g * R;
+        uint4 w[R][T];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = r0 + r;
+            const uint4 *brow = reinterpret_cast<const uint4 *>(b + row * k);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const int idx = t * kWave + lane;
+                if ((FULL || idx < nch) && row < n)
+                    w[r][t] = load_nt16(brow + idx);
+                else
+                    w[r][t] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            acc[r] = 0.f;
+#pragma unroll
+            for (int t = 0; t < T; ++t) acc[r] = dot8_f16(w[r][t], alo[t], ahi[t], acc[r]);
+        }
+        float mine = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float s = wave_sum(acc[r]);
+            if (lane == r) mine = s;
+        }
+        if (lane < R && r0 + lane < n) c[r0 + lane] = mine;
+    }
+}
+
+// Any K, any 2-byte alignment of b: one wave per row, lanes stride over K.
+__global__ __launch_bounds__(256) void gemv_f16_any(const float *__restrict__ a,
+                                                    const uint16_t *__restrict__ b,
+                                                    float *__restrict__ c, int64_t n, int64_t k) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+    const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) / kWave;
+    for (int64_t row = wave; row < n; row += nwaves) {
+        const uint16_t *brow = b + row * k;
+        float acc = 0.f;
+        for (int64_t kk = lane; kk < k; kk += kWave) acc = fmaf(half_bits_to_float(brow[kk]), a[kk], acc);
+        acc = wave_sum(acc);
+        if (lane == 0) c[row] = acc;
+    }
+}
+
+// ----------------------------------------------------------------- Q8_0 ----
+
+constexpr int kQ8BlockBytes = 34;
+constexpr int kQ8StageTarget = 17408;  // bytes staged per pass (8 rows at K = 2048)
+
+// Dot product of one Q8_0 block held in LDS at byte offset pb with the 32
+// activations av[0..31]: returns d * sum_i q_i * av[i].
+__device__ __forceinline__ float q8_block_dot(const uint8_t *stage, int pb, const float *av) {
+    const int qa = pb + 2;          // first code byte
+    const int sh = qa & 3;          // 0 or 2: codes start mid-dword for half the blocks
+    const uint32_t *s32 = reinterpret_cast<const uint32_t *>(stage + (qa - sh));
+    uint32_t wd[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) wd[i] = s32[i];
+    const uint32_t hb = *reinterpret_cast<const uint16_t *>(stage + pb);
+    float sumq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t q = __builtin_amdgcn_alignbyte(wd[i + 1], wd[i], sh);
+        sumq = fmaf(static_cast<float>(static_cast<int8_t>(q & 0xffu)), av[4 * i + 0], sumq);
+        sumq = fmaf(static_cast<float>(static_cast<int8_t>((q >> 8) & 0xffu)), av[4 * i + 1], sumq);
+        sumq = fmaf(static_cast<float>(static_cast<int8_t>((q >> 16) & 0xffu)), av[4 * i + 2], sumq);
+        sumq = fmaf(static_cast<float>(static_cast<int8_t>(q >> 24)), av[4 * i + 3], sumq);
+    }
+    return half_bits_to_float(hb) * sumq;
+}
+
+// One wave per workgroup.  LPR lanes share a row; lane l covers blocks
+// j = l % LPR + LPR * t (t < J) of that row and keeps a[32 j .. 32 j + 32) in
+// VGPRs.  Each pass stages S consecutive rows (S * row_bytes bytes) in LDS.
+// Requires K % 256 == 0 (rows are whole 16-byte chunks), 16-byte aligned a, b.
+template <int J, int LPR>
+__global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a,
+                                                     const uint8_t *__restrict__ b,
+                                                     float *__restrict__ c, int64_t n, int64_t k,
+                                                     int S, int64_t passes) {
+    extern __shared__ uint4 stage4[];
+    constexpr int RPL = kWave / LPR;
+    const int lane = threadIdx.x;
+    const int nb = static_cast<int>(k >> 5);
+    const int row_bytes = nb * kQ8BlockBytes;
+    const int jl = lane % LPR;
+    const int rsub = lane / LPR;
+
+    float av[J][32];
+#pragma unroll
+    for (int t = 0; t < J; ++t) {
+        const int j = jl + LPR * t;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < nb) v = reinterpret_cast<const float4 *>(a + 32 * j)[i];
+            av[t][4 * i + 0] = v.x;
+            av[t][4 * i + 1] = v.y;
+            av[t][4 * i + 2] = v.z;
+            av[t][4 * i + 3] = v.w;
+        }
+    }
+
+    const uint8_t *stage = reinterpret_cast<const uint8_t *>(stage4);
+    for (int64_t p = blockIdx.x; p < passes; p += gridDim.x) {
+        const int64_t row0 = p * S;
+        const int rows = static_cast<int>(min<int64_t>(S, n - row0));
+        const int nchunks = rows * row_bytes / 16;
+        const uint4 *src = reinterpret_cast<const uint4 *>(b + row0 * row_bytes);
+        for (int ci = lane; ci < nchunks; ci += kWave) stage4[ci] = load_nt16(src + ci);
+        __syncthreads();
+        for (int sb = 0; sb < rows; sb += RPL) {
+            const int s = sb + rsub;
+            float acc = 0.f;
+            if (s < rows) {
+#pragma unroll
+                for (int t = 0; t < J; ++t) {
+                    const int j = jl + LPR * t;
+                    if (j < nb) acc += q8_block_dot(stage, s * row_bytes + kQ8BlockBytes * j, av[t]);
+                }
+            }
+            acc = group_sum<LPR>(acc);
+            if (jl == 0 && s < rows) c[row0 + s] = acc;
+        }
+        __syncthreads();
+    }
+}
+
+// Any K % 32 == 0 and 2-byte aligned b: one wave per row, lanes stride over
+// blocks, reading each block with 2-byte loads.
+__global__ __launch_bounds__(256) void gemv_q8_any(const float *__restrict__ a,
+                                                   const uint8_t *__restrict__ b,
+                                                   float *__restrict__ c, int64_t n, int64_t k) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+    const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) / kWave;
+    const int64_t nb = k >> 5;
+    for (int64_t row = wave; row < n; row += nwaves) {
+        const uint8_t *brow = b + row * nb * kQ8BlockBytes;
+        float acc = 0.f;
+        for (int64_t j = lane; j < nb; j += kWave) {
+            const uint16_t *blk = reinterpret_cast<const uint16_t *>(brow + j * kQ8BlockBytes);
+            const float *aj = a + 32 * j;
+            float sumq = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t two = blk[1 + i];
+                sumq = fmaf(static_cast<float>(static_cast<int8_t>(two & 0xffu)), aj[2 * i], sumq);
+                sumq = fmaf(static_cast<float>(static_cast<int8_t>(two >> 8)), aj[2 * i + 1], sumq);
+            }
+            acc = fmaf(half_bits_to_float(blk[0]), sumq, acc);
+        }
+        acc = wave_sum(acc);
+        if (lane == 0) c[row] = acc;
+    }
+}
+
+// ---------------------------------------------------------------- helpers --
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Number of workers for `items` work items when at most `cap` fit at once:
+// the fewest that still finish in the same number of rounds, so that every
+// worker gets the same count (within one).
+inline int64_t balanced_workers(int64_t items, int64_t cap) {
+    if (items <= cap) return items;
+    const int64_t rounds = (items + cap - 1) / cap;
+    return (items + rounds - 1) / rounds;
+}
+
+template <int T, int R>
+hipError_t run_f16_vec(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
+                       hipStream_t s, int cus) {
+    const int64_t groups = (n + R - 1) / R;
+    const int64_t waves = balanced_workers(groups, static_cast<int64_t>(cus) * 16);
+    const int64_t blocks = (waves + 3) / 4;
+    const bool full = (k == 512LL * T);
+    if (trace_enabled())
+        fprintf(stderr, "[wqmm] gemv_f16_vec<T=%d,R=%d,full=%d> n=%lld k=%lld grid=%lld block=256\n", T, R,
+                full ? 1 : 0, (long long)n, (long long)k, (long long)blocks);
+    if (full)
+        hipLaunchKernelGGL((gemv_f16_vec<T, R, true>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups);
+    else
+        hipLaunchKernelGGL((gemv_f16_vec<T, R, false>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups);
+    return hipGetLastError();
+}
+
+template <int J, int LPR>
+hipError_t run_q8_staged(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
+                         hipStream_t s, int cus) {
+    const int row_bytes = static_cast<int>((k >> 5) * kQ8BlockBytes);
+    const int S = std::max(1, kQ8StageTarget / row_bytes);
+    const int64_t passes = (n + S - 1) / S;
+    const int64_t blocks = balanced_workers(passes, static_cast<int64_t>(cus) * 8);
+    const size_t lds = static_cast<size_t>(S) * row_bytes + 16;  // +16: 9-dword window slack
+    if (trace_enabled())
+        fprintf(stderr, "[wqmm] gemv_q8_staged<J=%d,LPR=%d> n=%lld k=%lld S=%d grid=%lld block=64 lds=%zu\n", J,
+                LPR, (long long)n, (long long)k, S, (long long)blocks, lds);
+    hipLaunchKernelGGL((gemv_q8_staged<J, LPR>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k, S, passes);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
+                           hipStream_t s) {
+    DeviceInfo di;
+    hipError_t e = device_info(&di);
+    if (e != hipSuccess) return e;
+    const int64_t nch = k / 8;
+    const int64_t T = (nch + 63) / 64;
+    if (k % 8 == 0 && aligned16(a) && aligned16(b) && T >= 1 && T <= 32) {
+        if (T <= 1) return run_f16_vec<1, 8>(a, b, c, n, k, s, di.cus);
+        if (T <= 2) return run_f16_vec<2, 8>(a, b, c, n, k, s, di.cus);
+        if (T <= 4) return run_f16_vec<4, 4>(a, b, c, n, k, s, di.cus);
+        if (T <= 8) return run_f16_vec<8, 2>(a, b, c, n, k, s, di.cus);
+        if (T <= 12) return run_f16_vec<12, 1>(a, b, c, n, k, s, di.cus);
+        if (T <= 16) return run_f16_vec<16, 1>(a, b, c, n, k, s, di.cus);
+        if (T <= 24) return run_f16_vec<24, 1>(a, b, c, n, k, s, di.cus);
+        return run_f16_vec<32, 1>(a, b, c, n, k, s, di.cus);
+    }
+    const int64_t waves = balanced_workers(n, static_cast<int64_t>(di.cus) * 16);
+    const int64_t blocks = (waves + 3) / 4;
+    if (trace_enabled())
+        fprintf(stderr, "[wqmm] gemv_f16_any n=%lld k=%lld grid=%lld block=256\n", (long long)n, (long long)k,
+                (long long)blocks);
+    hipLaunchKernelGGL(gemv_f16_any, dim3(blocks), dim3(256), 0, s, a, b, c, n, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
+                            hipStream_t s) {
+    DeviceInfo di;
+    hipError_t e = device_info(&di);
+    if (e != hipSuccess) return e;
+    const int64_t nb = k / 32;
+    const int64_t row_bytes = nb * kQ8BlockBytes;
+    if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= 32768) {
+        if (nb >= 64) {
+            const int64_t J = (nb + 63) / 64;
+            switch (J) {
+                case 1: return run_q8_staged<1, 64>(a, b, c, n, k, s, di.cus);
+                case 2: return run_q8_staged<2, 64>(a, b, c, n, k, s, di.cus);
+                case 3: return run_q8_staged<3, 64>(a, b, c, n, k, s, di.cus);
+                case 4: return run_q8_staged<4, 64>(a, b, c, n, k, s, di.cus);
+                case 5: return run_q8_staged<5, 64>(a, b, c, n, k, s, di.cus);
+                case 6: return run_q8_staged<6, 64>(a, b, c, n, k, s, di.cus);
+                case 7: return run_q8_staged<7, 64>(a, b, c, n, k, s, di.cus);
+                case 8: return run_q8_staged<8, 64>(a, b, c, n, k, s, di.cus);
+                default: break;
+            }
+        } else if (nb >= 32) {
+            if (nb == 32) return run_q8_staged<1, 32>(a, b, c, n, k, s, di.cus);
+            return run_q8_staged<2, 32>(a, b, c, n, k, s, di.cus);
+        } else {
+            if (nb <= 16) return run_q8_staged<1, 16>(a, b, c, n, k, s, di.cus);
+            return run_q8_staged<2, 16>(a, b, c, n, k, s, di.cus);
+        }
+    }
+    const int64_t waves = balanced_workers(n, static_cast<int64_t>(di.cus) * 16);
+    const int64_t blocks = (waves + 3) / 4;
+    if (trace_enabled())
+        fprintf(stderr, "[wqmm] gemv_q8_any n=%lld k=%lld grid=%lld block=256\n", (long long)n, (long long)k,
+                (long long)blocks);
+    hipLaunchKernelGGL(gemv_q8_any, dim3(blocks), dim3(256), 0, s, a, b, c, n, k);
+    return hipGetLastError();
+}
+
+}  // namespace wq

@@ -1,0 +1,71 @@
+// Internal declarations shared by the libwqmm translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+// ----------------------------------------------------------------- device --
+// Wavefront size on CDNA4.
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 128-bit non-temporal (streaming) global load: weights are read exactly once.
+__device__ __forceinline__ uint4 load_nt16(const uint4 *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// binary16 bits -> f32, exact (the hardware conversion keeps subnormals).
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of G lanes (G in {16, 32, 64}); every lane of a group
+// receives the group's sum.  Within a 16-lane DPP row: quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror, row_mirror; across rows: lane xor.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(G == 16 || G == 32 || G == 64, "group size");
+    v += dpp_f32<0xb1>(v);
+    v += dpp_f32<0x4e>(v);
+    v += dpp_f32<0x141>(v);
+    v += dpp_f32<0x140>(v);
+    if constexpr (G >= 32) v += __shfl_xor(v, 16, kWave);
+    if constexpr (G >= 64) v += __shfl_xor(v, 32, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+
+// ------------------------------------------------------------------- host --
+struct DeviceInfo {
+    int cus;  // compute units of the current device
+};
+// Properties of the current HIP device, queried once per device.
+hipError_t device_info(DeviceInfo *out);
+
+// Launchers.  Arguments are already validated by the C-ABI layer; these only
+// pick a kernel variant and grid and enqueue it on `s`.
+hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
+                           hipStream_t s);
+hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
+                            hipStream_t s);
+hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,
+                       int64_t k, hipStream_t s);
+hipError_t launch_fill_zero(float *c, int64_t count, hipStream_t s);
+hipError_t launch_pack_f16(const float *w, uint16_t *out, int64_t count, hipStream_t s);
+hipError_t launch_quantize_q8_0(const float *w, uint8_t *out, int64_t count, hipStream_t s);
+
+// Set by WQ_TRACE=1: one line per launch on stderr.
+bool trace_enabled();
+
+}  // namespace wq

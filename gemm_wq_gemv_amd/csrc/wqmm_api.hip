@@ -1,0 +1,228 @@
+// C ABI of libwqmm: argument validation, M routing, route counters, launches.
+// The contract (layouts, ownership, errors) is documented in include/wqmm.h.
+#include "../../include/wqmm.h"
+#include "wq_internal.h"
+
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+namespace wq {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+DeviceInfo g_dev[kMaxDevices];
+hipError_t g_dev_err[kMaxDevices];
+
+std::atomic<int> g_forced_route{WQ_ROUTE_AUTO};
+std::atomic<uint64_t> g_route_count[3];
+
+int trace_flag() {
+    static const int v = [] {
+        const char *e = std::getenv("WQ_TRACE");
+        return (e && e[0] && std::strcmp(e, "0") != 0) ? 1 : 0;
+    }();
+    return v;
+}
+}  // namespace
+
+bool trace_enabled() { return trace_flag() != 0; }
+
+hipError_t device_info(DeviceInfo *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_dev_once[dev], [dev] {
+        int cus = 0;
+        g_dev_err[dev] = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        g_dev[dev].cus = cus > 0 ? cus : 1;
+    });
+    *out = g_dev[dev];
+    return g_dev_err[dev];
+}
+
+}  // namespace wq
+
+namespace {
+
+bool mul_ok(int64_t x, int64_t y, int64_t *out) { return !__builtin_mul_overflow(x, y, out); }
+
+bool overlaps(const void *p, int64_t pbytes, const void *q, int64_t qbytes) {
+    if (!p || !q || pbytes <= 0 || qbytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+    return a0 < b0 + static_cast<uintptr_t>(qbytes) && b0 < a0 + static_cast<uintptr_t>(pbytes);
+}
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+
+// Validates a product call.  Returns WQ_OK with *noop = true when nothing is
+// to be done (m == 0 or n == 0), WQ_OK with *noop = false when a launch
+// follows, or an error status.
+int validate(const float *a, const void *b, const float *c, int64_t m, int64_t n, int64_t k, int fmt,
+             bool *noop) {
+    *noop = false;
+    if (fmt != WQ_FMT_F16 && fmt != WQ_FMT_Q8_0) return WQ_ERR_FORMAT;
+    if (m < 0 || n < 0 || k < 0) return WQ_ERR_SHAPE;
+    if (m == 0 || n == 0) {
+        *noop = true;
+        return WQ_OK;
+    }
+    if (fmt == WQ_FMT_Q8_0 && (k == 0 || k % 32 != 0)) return WQ_ERR_K;
+    int64_t a_elems, c_elems, b_bytes, a_bytes, c_bytes;
+    if (!mul_ok(m, k, &a_elems) || !mul_ok(a_elems, 4, &a_bytes)) return WQ_ERR_SHAPE;
+    if (!mul_ok(m, n, &c_elems) || !mul_ok(c_elems, 4, &c_bytes)) return WQ_ERR_SHAPE;
+    if (fmt == WQ_FMT_F16) {
+        int64_t nk;
+        if (!mul_ok(n, k, &nk) || !mul_ok(nk, 2, &b_bytes)) return WQ_ERR_SHAPE;
+    } else {
+        if (!mul_ok(n, (k / 32) * 34, &b_bytes)) return WQ_ERR_SHAPE;
+    }
+    if (!c) return WQ_ERR_NULL;
+    if (k > 0 && (!a || !b)) return WQ_ERR_NULL;
+    if (!aligned(c, 4) || (a && !aligned(a, 4)) || (b && !aligned(b, 2))) return WQ_ERR_ALIGN;
+    if (k > 0 && (overlaps(c, c_bytes, a, a_bytes) || overlaps(c, c_bytes, b, b_bytes))) return WQ_ERR_ALIAS;
+    return WQ_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_LAUNCH; }
+
+int auto_route(int64_t m) { return m == 1 ? WQ_ROUTE_GEMV : WQ_ROUTE_GEMM; }
+
+int run_gemv(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s) {
+    // One GEMV launch per row of A (the route for M == 1; forced otherwise).
+    for (int64_t i = 0; i < m; ++i) {
+        const float *ai = a + i * k;
+        float *ci = c + i * n;
+        hipError_t e = (fmt == WQ_FMT_F16)
+                           ? wq::launch_gemv_f16(ai, static_cast<const uint16_t *>(b), ci, n, k, s)
+                           : wq::launch_gemv_q8_0(ai, static_cast<const uint8_t *>(b), ci, n, k, s);
+        if (e != hipSuccess) return WQ_ERR_LAUNCH;
+        wq::g_route_count[WQ_ROUTE_GEMV].fetch_add(1, std::memory_order_relaxed);
+    }
+    return WQ_OK;
+}
+
+int run_gemm(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s) {
+    hipError_t e = wq::launch_gemm(a, b, fmt, c, m, n, k, s);
+    if (e != hipSuccess) return WQ_ERR_LAUNCH;
+    wq::g_route_count[WQ_ROUTE_GEMM].fetch_add(1, std::memory_order_relaxed);
+    return WQ_OK;
+}
+
+// K == 0 (f16 only): the empty sum, c = 0.
+int run_zero(float *c, int64_t m, int64_t n, hipStream_t s) {
+    return status_of(wq::launch_fill_zero(c, m * n, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int wq_abi_version(void) { return 100; }
+
+const char *wq_status_str(int status) {
+    switch (status) {
+        case WQ_OK: return "ok";
+        case WQ_ERR_NULL: return "a required pointer is NULL";
+        case WQ_ERR_SHAPE: return "negative dimension or byte count overflow";
+        case WQ_ERR_K: return "Q8_0 needs K > 0 and K % 32 == 0";
+        case WQ_ERR_FORMAT: return "unknown weight format";
+        case WQ_ERR_ALIGN: return "misaligned pointer (a, c need 4 bytes; b needs 2)";
+        case WQ_ERR_LAUNCH: return "HIP kernel launch failed";
+        case WQ_ERR_ALIAS: return "output overlaps an input";
+        case WQ_ERR_ROUTE: return "unknown route";
+        default: return "unknown status";
+    }
+}
+
+int wq_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k, void *stream) {
+    bool noop;
+    int st = validate(a, b, c, 1, n, k, WQ_FMT_F16, &noop);
+    if (st != WQ_OK || noop) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (k == 0) return run_zero(c, 1, n, s);
+    return run_gemv(a, b, c, 1, n, k, WQ_FMT_F16, s);
+}
+
+int wq_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, void *stream) {
+    bool noop;
+    int st = validate(a, b, c, 1, n, k, WQ_FMT_Q8_0, &noop);
+    if (st != WQ_OK || noop) return st;
+    return run_gemv(a, b, c, 1, n, k, WQ_FMT_Q8_0, static_cast<hipStream_t>(stream));
+}
+
+int wq_gemm_f16(const float *a, const uint16_t *b, float *c, int64_t m, int64_t n, int64_t k, void *stream) {
+    bool noop;
+    int st = validate(a, b, c, m, n, k, WQ_FMT_F16, &noop);
+    if (st != WQ_OK || noop) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (k == 0) return run_zero(c, m, n, s);
+    return run_gemm(a, b, c, m, n, k, WQ_FMT_F16, s);
+}
+
+int wq_gemm_q8_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t n, int64_t k, void *stream) {
+    bool noop;
+    int st = validate(a, b, c, m, n, k, WQ_FMT_Q8_0, &noop);
+    if (st != WQ_OK || noop) return st;
+    return run_gemm(a, b, c, m, n, k, WQ_FMT_Q8_0, static_cast<hipStream_t>(stream));
+}
+
+int wq_matmul(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, void *stream) {
+    bool noop;
+    int st = validate(a, b, c, m, n, k, fmt, &noop);
+    if (st != WQ_OK || noop) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (k == 0) return run_zero(c, m, n, s);
+    int route = wq::g_forced_route.load(std::memory_order_relaxed);
+    if (route == WQ_ROUTE_AUTO) route = auto_route(m);
+    if (route == WQ_ROUTE_GEMV) return run_gemv(a, b, c, m, n, k, fmt, s);
+    return run_gemm(a, b, c, m, n, k, fmt, s);
+}
+
+int wq_pack_f16(const float *w, uint16_t *out, int64_t count, void *stream) {
+    if (count < 0) return WQ_ERR_SHAPE;
+    if (count == 0) return WQ_OK;
+    if (count > INT64_MAX / 4) return WQ_ERR_SHAPE;
+    if (!w || !out) return WQ_ERR_NULL;
+    if (!aligned(w, 4) || !aligned(out, 2)) return WQ_ERR_ALIGN;
+    if (overlaps(w, count * 4, out, count * 2)) return WQ_ERR_ALIAS;
+    return status_of(wq::launch_pack_f16(w, out, count, static_cast<hipStream_t>(stream)));
+}
+
+int wq_quantize_q8_0(const float *w, uint8_t *out, int64_t count, void *stream) {
+    if (count < 0) return WQ_ERR_SHAPE;
+    if (count % 32 != 0) return WQ_ERR_K;
+    if (count == 0) return WQ_OK;
+    if (count > INT64_MAX / 4) return WQ_ERR_SHAPE;
+    if (!w || !out) return WQ_ERR_NULL;
+    if (!aligned(w, 4) || !aligned(out, 2)) return WQ_ERR_ALIGN;
+    if (overlaps(w, count * 4, out, count / 32 * 34)) return WQ_ERR_ALIAS;
+    return status_of(wq::launch_quantize_q8_0(w, out, count, static_cast<hipStream_t>(stream)));
+}
+
+int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt) {
+    if (fmt != WQ_FMT_F16 && fmt != WQ_FMT_Q8_0) return -WQ_ERR_FORMAT;
+    if (m < 0 || n < 0 || k < 0) return -WQ_ERR_SHAPE;
+    if (fmt == WQ_FMT_Q8_0 && m > 0 && n > 0 && (k == 0 || k % 32 != 0)) return -WQ_ERR_K;
+    return auto_route(m);
+}
+
+int wq_set_forced_route(int route) {
+    if (route != WQ_ROUTE_AUTO && route != WQ_ROUTE_GEMV && route != WQ_ROUTE_GEMM) return -WQ_ERR_ROUTE;
+    return wq::g_forced_route.exchange(route);
+}
+
+uint64_t wq_route_count(int route) {
+    if (route != WQ_ROUTE_GEMV && route != WQ_ROUTE_GEMM) return 0;
+    return wq::g_route_count[route].load(std::memory_order_relaxed);
+}
+
+void wq_reset_route_counts(void) {
+    for (auto &x : wq::g_route_count) x.store(0, std::memory_order_relaxed);
+}
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+/*
+ * wqmm.h -- C ABI of libwqmm, the mixed-precision weight matmul for AMD
+ * Instinct MI355X (gfx950):
+ *
+ *     C[M,N] = A[M,K] . B[N,K]^T          (C is overwritten, beta = 0)
+ *
+ * Source of the operation: lattice-inference 0.9.0,
+ * forward/metal_qwen35/inner/dispatch.rs -- dispatch_matmul_half (doc
+ * comment: C[M,N] = A[M,K] @ B_half[N,K]^T, A f32 activations, B f16 weights
+ * widened to f32 before accumulation, C f32), dispatch_matmul_q8 (Q8_0
+ * weights [N, K/32 * 34]) and dispatch_gemm_q8 (M == 1 takes the decode
+ * GEMV, M > 1 the tiled GEMM; m == 0 or n == 0 is a no-op; K must be a
+ * non-zero multiple of 32).  Formats: lattice-inference 0.1.2,
+ * forward/metal_qwen35.rs -- kernel gemv_q8_decode (block = f16 scale, then
+ * 32 int8), quantize_row_q8_0, f32_to_f16.  The same product as
+ * sgemm(RowMajor, NoTrans, Trans, alpha = 1, beta = 0): ferrum-kernels
+ * 0.7.7, attention/metal/pipelines.rs, MetalPipelines::gemm.
+ *
+ * Layouts (all row-major, tightly packed, no stride arguments):
+ *   a  f32 [M, K]                         lda = K
+ *   b  f16 bit patterns [N, K]            2*N*K bytes
+ *      or Q8_0 bytes [N, K/32 * 34]       row n starts at byte n*(K/32)*34;
+ *         block j of the row at +34*j: bytes 0..1 a little-endian f16 scale d,
+ *         bytes 2..33 int8 codes q; weight (n, 32*j + i) = d * q[i]
+ *   c  f32 [M, N]                         ldc = N
+ * Accumulation is in f32; the summation order is unspecified, so results may
+ * differ from a serial f32 sum by rounding only.  The weight decode itself is
+ * exact (f16 -> f32 widening, d * q is exact in f32).
+ *
+ * Pointers: a, b, c (and w, out of the packing calls) are DEVICE pointers on
+ * the current HIP device.  The caller owns all memory; the library never
+ * allocates, frees or keeps caller buffers.  Buffers must stay alive until the
+ * enqueued work has run.
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream).  Every call only enqueues work and returns without synchronising;
+ * c is written when the stream runs.  Calls are reentrant and thread-safe.
+ *
+ * Errors: every call validates all arguments before it enqueues anything.
+ * On any error nothing is launched and c is not touched.  Alignment: a and c
+ * must be 4-byte aligned, b 2-byte aligned.  c must not overlap a or b.
+ * m == 0 or n == 0 returns WQ_OK without touching any pointer.  For f16,
+ * K == 0 is allowed and writes zeros to c (the empty sum); a and b may then be
+ * NULL.  Q8_0 needs K > 0 and K % 32 == 0.
+ */
+#ifndef WQMM_H
+#define WQMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight storage formats (the pages' QuantFormat plus their f16 weights). */
+typedef enum wq_format {
+    WQ_FMT_F16 = 0,  /* IEEE-754 binary16 bit patterns */
+    WQ_FMT_Q8_0 = 1  /* 34-byte Q8_0 blocks of 32 weights */
+} wq_format;
+
+/* Status codes returned by every entry point. */
+typedef enum wq_status {
+    WQ_OK = 0,
+    WQ_ERR_NULL = 1,    /* a required pointer is NULL */
+    WQ_ERR_SHAPE = 2,   /* negative dimension, or a byte count overflows int64 */
+    WQ_ERR_K = 3,       /* Q8_0 with K == 0 or K % 32 != 0 */
+    WQ_ERR_FORMAT = 4,  /* fmt is not a wq_format */
+    WQ_ERR_ALIGN = 5,   /* a or c not 4-byte aligned, or b not 2-byte aligned */
+    WQ_ERR_LAUNCH = 6,  /* the HIP runtime failed to enqueue a kernel */
+    WQ_ERR_ALIAS = 7,   /* c overlaps a or b */
+    WQ_ERR_ROUTE = 8    /* not a wq_route value */
+} wq_status;
+
+/* Kernel families wq_matmul can route to. */
+typedef enum wq_route {
+    WQ_ROUTE_AUTO = 0,  /* choose by M (wq_route_for) */
+    WQ_ROUTE_GEMV = 1,  /* decode GEMV: one launch per row of A */
+    WQ_ROUTE_GEMM = 2   /* LDS-tiled fp32-MFMA GEMM */
+} wq_route;
+
+/* ---------------------------------------------------------------------- */
+/* Decode GEMV, M = 1: c[n] = sum_k a[k] * w[n, k].  a is f32 [K], c f32 [N].
+ * The weights stream from HBM once; a is held on chip.  Passage: kernel
+ * gemv_decode_m1 (f16) and gemv_q8_decode (Q8_0), lattice-inference 0.1.2
+ * metal_qwen35.rs; dispatch_matmul_half / dispatch_matmul_q8, lattice-inference
+ * 0.9.0 dispatch.rs.  There is no m argument: a GEMV computes one row. */
+int wq_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k, void *stream);
+int wq_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, void *stream);
+
+/* Prefill GEMM, any M >= 1: C = A . B^T through LDS tiles of A and of the
+ * dequantised B, with fp32 matrix-core (MFMA) accumulation.  Passage: kernels
+ * matmul_bt, gemm_q8 and gemm_q4_tiled (tiling prior art), lattice-inference
+ * 0.1.2 metal_qwen35.rs; dispatch_gemm_q8, lattice-inference 0.9.0 dispatch.rs. */
+int wq_gemm_f16(const float *a, const uint16_t *b, float *c, int64_t m, int64_t n, int64_t k,
+                void *stream);
+int wq_gemm_q8_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t n, int64_t k,
+                 void *stream);
+
+/* M-routed product for either format (fmt is a wq_format).  M == 1 takes the
+ * GEMV, M > 1 the GEMM, unless a route is forced (wq_set_forced_route).
+ * Passage: dispatch_gemm_q8 and dispatch_gemm, lattice-inference 0.9.0
+ * dispatch.rs. */
+int wq_matmul(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt,
+              void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Weight preparation (done once, at load time).
+ * wq_pack_f16: out[i] = binary16 bits of w[i], round to nearest even, with
+ *   subnormals; overflow gives infinity.  Passage: f32_to_f16 and
+ *   make_buffer_f16, lattice-inference 0.1.2 metal_qwen35.rs.
+ * wq_quantize_q8_0: count f32 values (count % 32 == 0, else WQ_ERR_K) into
+ *   count/32 Q8_0 blocks written to out (count/32*34 bytes).  Per block:
+ *   amax = max|v|, d = amax/127, id = 1/d (0 if d == 0), scale bytes =
+ *   f16(d) little-endian, q = clamp(round_half_away(v*id), -127, 127), all in
+ *   f32.  A row-major [N, K] matrix with K % 32 == 0 gives the [N, K/32*34]
+ *   layout above.  Passage: quantize_row_q8_0 and make_buffer_q8_0,
+ *   lattice-inference 0.1.2 metal_qwen35.rs.
+ * w and out are device pointers (w 4-byte aligned, out 2-byte aligned for
+ * f16); count == 0 is a no-op; out must not overlap w. */
+int wq_pack_f16(const float *w, uint16_t *out, int64_t count, void *stream);
+int wq_quantize_q8_0(const float *w, uint8_t *out, int64_t count, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Routing and introspection (host only; these never touch the GPU). */
+
+/* The route wq_matmul takes for these arguments when nothing is forced
+ * (WQ_ROUTE_GEMV or WQ_ROUTE_GEMM), or a negative wq_status on bad arguments. */
+int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt);
+
+/* Force every later wq_matmul call in the process onto one route
+ * (WQ_ROUTE_AUTO restores the M rule).  Returns the previous setting, or
+ * -WQ_ERR_ROUTE for an unknown value.  Meant for tests that check that all
+ * routes agree (the pages' test hook forcing the fallback GEMM). */
+int wq_set_forced_route(int route);
+
+/* Kernel launches made so far per route (WQ_ROUTE_GEMV / WQ_ROUTE_GEMM) by
+ * any entry point, and a reset.  The pages keep such "path proof" counters. */
+uint64_t wq_route_count(int route);
+void wq_reset_route_counts(void);
+
+/* Static text for a status code ("unknown status" for others). */
+const char *wq_status_str(int status);
+
+/* ABI version: 100 * major + minor. */
+int wq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQMM_H */

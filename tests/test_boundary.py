@@ -1,0 +1,144 @@
+"""The C-ABI boundary on the CPU: symbols, validation, routing (no kernel runs).
+
+Every call here returns from libwqmm's argument checks before any HIP call,
+so it runs in a container without a GPU.  Pointers are plain integers: the
+library never dereferences them on these paths.
+"""
+import os
+import re
+
+import pytest
+
+import gemm_wq_gemv_amd as wq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wqmm.h")
+L = wq._lib
+
+# Fake, suitably aligned device addresses far apart from each other.
+A, B, C = 0x100000, 0x900000, 0x1100000
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for want in ("wq_gemv_f16", "wq_gemv_q8_0", "wq_gemm_f16", "wq_gemm_q8_0", "wq_matmul",
+                 "wq_pack_f16", "wq_quantize_q8_0"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_binding_has_every_entry_point_by_the_same_name():
+    for name in _declared():
+        assert callable(getattr(wq, name, None)), name
+
+
+def test_single_hip_runtime_in_process():
+    # torch is imported first, so libwqmm reuses torch's libamdhip64.so.7.
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs
+
+
+def test_abi_and_status_strings():
+    assert wq.wq_abi_version() == 100
+    for st in range(0, 9):
+        assert wq.status_str(st)
+    assert wq.status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("fmt", [wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0])
+def test_empty_outputs_are_noops(fmt):
+    # m == 0 or n == 0: nothing to do, pointers are not even looked at.
+    assert L.wq_matmul(None, None, None, 0, 16, 64, fmt, None) == wq.WQ_OK
+    assert L.wq_matmul(None, None, None, 4, 0, 64, fmt, None) == wq.WQ_OK
+    assert L.wq_gemm_f16(None, None, None, 0, 0, 0, None) == wq.WQ_OK
+    assert L.wq_gemv_q8_0(None, None, None, 0, 33, None) == wq.WQ_OK  # n == 0 first, as on the page
+
+
+def test_q8_k_rules():
+    for k in (0, 16, 33, 48, 1000):
+        assert L.wq_gemv_q8_0(A, B, C, 8, k, None) == wq.WQ_ERR_K
+        assert L.wq_gemm_q8_0(A, B, C, 2, 8, k, None) == wq.WQ_ERR_K
+        assert L.wq_matmul(A, B, C, 2, 8, k, wq.WQ_FMT_Q8_0, None) == wq.WQ_ERR_K
+    assert L.wq_quantize_q8_0(A, B, 33, None) == wq.WQ_ERR_K
+
+
+def test_shape_format_null_align_alias():
+    assert L.wq_matmul(A, B, C, -1, 8, 64, 0, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_matmul(A, B, C, 1, -8, 64, 0, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_matmul(A, B, C, 1, 8, -64, 0, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_matmul(A, B, C, 1 << 40, 1 << 40, 64, 0, None) == wq.WQ_ERR_SHAPE  # overflow
+    assert L.wq_matmul(A, B, C, 1, 8, 64, 2, None) == wq.WQ_ERR_FORMAT
+    assert L.wq_matmul(A, B, C, 1, 8, 64, -1, None) == wq.WQ_ERR_FORMAT
+    assert L.wq_gemv_f16(None, B, C, 8, 64, None) == wq.WQ_ERR_NULL
+    assert L.wq_gemv_f16(A, None, C, 8, 64, None) == wq.WQ_ERR_NULL
+    assert L.wq_gemv_f16(A, B, None, 8, 64, None) == wq.WQ_ERR_NULL
+    assert L.wq_gemm_f16(None, None, None, 2, 8, 0, None) == wq.WQ_ERR_NULL  # K == 0 still writes c
+    assert L.wq_gemv_f16(A + 2, B, C, 8, 64, None) == wq.WQ_ERR_ALIGN
+    assert L.wq_gemv_f16(A, B + 1, C, 8, 64, None) == wq.WQ_ERR_ALIGN
+    assert L.wq_gemv_f16(A, B, C + 2, 8, 64, None) == wq.WQ_ERR_ALIGN
+    # c overlapping a or b
+    assert L.wq_gemv_f16(A, B, A + 64, 8, 64, None) == wq.WQ_ERR_ALIAS
+    assert L.wq_gemm_q8_0(A, B, B + 4, 2, 8, 64, None) == wq.WQ_ERR_ALIAS
+    assert L.wq_pack_f16(A, A + 8, 64, None) == wq.WQ_ERR_ALIAS
+    assert L.wq_pack_f16(A, B, -1, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_pack_f16(A, B, 0, None) == wq.WQ_OK
+    assert L.wq_pack_f16(None, B, 5, None) == wq.WQ_ERR_NULL
+    assert L.wq_quantize_q8_0(A, B + 1, 64, None) == wq.WQ_ERR_ALIGN
+
+
+def test_routing_rule():
+    for fmt in (wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0):
+        assert wq.wq_route_for(1, 4096, 4096, fmt) == wq.WQ_ROUTE_GEMV
+        for m in (2, 4, 8, 16, 64, 512):
+            assert wq.wq_route_for(m, 4096, 4096, fmt) == wq.WQ_ROUTE_GEMM
+    assert wq.wq_route_for(2, 8, 33, wq.WQ_FMT_Q8_0) == -wq.WQ_ERR_K
+    assert wq.wq_route_for(2, 8, 32, 5) == -wq.WQ_ERR_FORMAT
+    assert wq.wq_route_for(-2, 8, 32, 0) == -wq.WQ_ERR_SHAPE
+
+
+def test_forced_route_setting():
+    prev = wq.wq_set_forced_route(wq.WQ_ROUTE_GEMM)
+    try:
+        assert prev == wq.WQ_ROUTE_AUTO
+        assert wq.wq_set_forced_route(wq.WQ_ROUTE_GEMV) == wq.WQ_ROUTE_GEMM
+        assert wq.wq_set_forced_route(7) == -wq.WQ_ERR_ROUTE
+    finally:
+        wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
+    wq.wq_reset_route_counts()
+    assert wq.wq_route_count(wq.WQ_ROUTE_GEMV) == 0 and wq.wq_route_count(wq.WQ_ROUTE_GEMM) == 0
+    assert wq.wq_route_count(99) == 0
+
+
+def test_python_binding_rejects_host_and_short_tensors():
+    import torch
+    a = torch.zeros(64)
+    with pytest.raises(ValueError):
+        wq.wq_gemv_f16(a, torch.zeros(64, dtype=torch.uint16), torch.zeros(1), 1, 64)  # host tensors
+    with pytest.raises(ValueError):
+        wq.wq_gemv_f16(a, torch.zeros(10, dtype=torch.uint16), torch.zeros(1), 1, 64)  # b too short
+    with pytest.raises(TypeError):
+        wq.wq_gemv_f16(a.double(), torch.zeros(64, dtype=torch.uint16), torch.zeros(1), 1, 64)
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The library and its binding never import, include or load the oracle or
+    the input generator; the oracle never includes library code."""
+    pkg = os.path.join(ROOT, "gemm_wq_gemv_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b|wqref|wqgen", text), f
+    src = open(os.path.join(ROOT, "oracle", "wqref.c")).read()
+    assert "#include \"" not in src and "wqmm" not in src and "hip" not in src.lower().replace("ship", "")

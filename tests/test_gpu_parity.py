@@ -1,0 +1,367 @@
+"""GPU parity: libwqmm (through its C ABI) against the CPU oracle.
+
+Both sides draw the same seeded f32 inputs from ``wqgen``; each side encodes
+the weights with its own code (the library's wq_pack_f16 / wq_quantize_q8_0 on
+the GPU, the oracle's encoders on the CPU) and the encoded bytes must agree
+bit for bit.  Products must satisfy, per element,
+    |c - c_ref| <= 1e-5 * sum_k |a_k w_k| + 1e-6,
+with c_ref the oracle's float64 result.  Outputs are poisoned with NaN before
+every launch, so an element that is never written fails.
+
+Sizes: the oracle computes every output of the small and ragged cases and of
+the decode configurations; at M = 64 and 512 it computes a sample of outputs
+(first/last rows and columns, tile edges, random picks), and the rest of the
+GPU output is checked to be finite.
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import gemm_wq_gemv_amd as wq
+import oracle
+import wqgen
+
+pytestmark = pytest.mark.gpu
+
+F16, Q8 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0
+DECODE_SHAPES = [(6144, 2048), (2048, 6144), (2048, 2048), (151936, 2048)]
+SWEEP_SHAPES = [(11008, 4096), (4096, 11008)]
+SWEEP_M = [1, 2, 4, 8, 16, 64, 512]
+
+
+def say(msg: str):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
+    yield
+    wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
+
+
+# ------------------------------------------------------------------ inputs --
+@functools.lru_cache(maxsize=6)
+def weights_f32(n, k, seed=0):
+    return wqgen.weights(n, k, seed)
+
+
+@functools.lru_cache(maxsize=6)
+def acts(m, k, seed=0):
+    return wqgen.activations(m, k, seed)
+
+
+@functools.lru_cache(maxsize=6)
+def encoded(n, k, fmt, seed=0):
+    """(oracle bytes, library bytes on the GPU) for the same f32 weights."""
+    w = weights_f32(n, k, seed)
+    ref = oracle.encode(w, fmt)
+    wd = torch.from_numpy(w).cuda()
+    dev = wq.pack_f16(wd) if fmt == F16 else wq.quantize_q8_0(wd)
+    torch.cuda.synchronize()
+    del wd
+    return ref, dev
+
+
+def _entry(name, fmt):
+    if name == "gemv":
+        f = wq.wq_gemv_f16 if fmt == F16 else wq.wq_gemv_q8_0
+        return lambda a, b, c, m, n, k: f(a, b, c, n, k)
+    if name == "gemm":
+        f = wq.wq_gemm_f16 if fmt == F16 else wq.wq_gemm_q8_0
+        return lambda a, b, c, m, n, k: f(a, b, c, m, n, k)
+    return lambda a, b, c, m, n, k: wq.wq_matmul(a, b, c, m, n, k, fmt)
+
+
+def run_gpu(entry, fmt, a_np, b_dev, m, n, k, stream=None):
+    a = torch.from_numpy(np.ascontiguousarray(a_np)).cuda()
+    c = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+    fn = _entry(entry, fmt)
+    if stream is None:
+        fn(a, b_dev, c, m, n, k)
+    else:
+        with torch.cuda.stream(stream):
+            fn(a, b_dev, c, m, n, k)
+    torch.cuda.synchronize()
+    return c.cpu().numpy()
+
+
+def assert_close(c, c_ref, bound, what):
+    err = np.abs(c.astype(np.float64) - c_ref)
+    bad = ~(err <= bound)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        det = [(tuple(i), float(c[tuple(i)]), float(c_ref[tuple(i)]), float(bound[tuple(i)])) for i in idx]
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance, e.g. {det}")
+    return float(np.max(err / bound)) if err.size else 0.0
+
+
+def full_case(entry, fmt, m, n, k, seed=0):
+    say(f"{entry} fmt={fmt} m={m} n={n} k={k} seed={seed}")
+    ref_b, dev_b = encoded(n, k, fmt, seed)
+    a = acts(m, k, seed)
+    c = run_gpu(entry, fmt, a, dev_b, m, n, k)
+    c_ref, bound = oracle.matmul(a, ref_b, fmt, m, n, k)
+    return assert_close(c, c_ref, bound, f"{entry} fmt={fmt} {m}x{n}x{k}")
+
+
+def sample_indices(m, n, rng, count=2048):
+    rows = sorted({0, 1, m - 1, m // 2, min(m - 1, 63), min(m - 1, 64), min(m - 1, 127), min(m - 1, 128)}
+                  | set(rng.integers(0, m, 8).tolist()))
+    cols = sorted({0, 1, n - 1, n // 2, min(n - 1, 95), min(n - 1, 96), min(n - 1, 127), min(n - 1, 128)}
+                  | set(rng.integers(0, n, max(8, count // len(rows) - 8)).tolist()))
+    rr, cc = np.meshgrid(rows, cols, indexing="ij")
+    return rr.ravel(), cc.ravel()
+
+
+def sampled_case(entry, fmt, m, n, k, seed=0):
+    say(f"{entry} fmt={fmt} m={m} n={n} k={k} seed={seed} (sampled)")
+    ref_b, dev_b = encoded(n, k, fmt, seed)
+    a = acts(m, k, seed)
+    c = run_gpu(entry, fmt, a, dev_b, m, n, k)
+    assert np.isfinite(c).all(), "unwritten (NaN) or non-finite outputs"
+    rows, cols = sample_indices(m, n, np.random.default_rng(seed + m))
+    c_ref, bound = oracle.matmul_entries(a, ref_b, fmt, m, n, k, rows, cols)
+    return assert_close(c[rows, cols], c_ref, bound, f"{entry} fmt={fmt} {m}x{n}x{k} sampled")
+
+
+# ------------------------------------------------------- weight encoding --
+@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("nk", [(1024, 1024), (6144, 2048), (2048, 6144), (151936, 2048), (4096, 11008), (3, 96)])
+def test_weight_encoding_bit_exact(fmt, nk):
+    n, k = nk
+    say(f"encode fmt={fmt} n={n} k={k}")
+    ref, dev = encoded(n, k, fmt)
+    got = dev.cpu().numpy()
+    assert got.shape == ref.shape
+    assert np.array_equal(got.view(np.uint8), ref.view(np.uint8))
+
+
+def test_pack_f16_special_values():
+    say("pack_f16 special values")
+    x = np.array([1.0, -2.0, 65504.0, 65519.875, 65520.0, 1e6, -1e6, 2.0 ** -14, 2.0 ** -24, 2.0 ** -25,
+                  1.5 * 2.0 ** -24, 1023.5 * 2.0 ** -24, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 2.0 ** -149,
+                  -2.0 ** -149, -0.0, 0.0, np.inf, -np.inf, 0.1, 0.02], dtype=np.float32)
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 1 << 32, size=1 << 18, dtype=np.uint64).astype(np.uint32)
+    x = np.concatenate([x, bits.view(np.float32)])
+    finite_or_inf = ~np.isnan(x)
+    got = wq.pack_f16(torch.from_numpy(x).cuda()).cpu().numpy()
+    ref = oracle.f16_bits(x)
+    assert np.array_equal(got[finite_or_inf], ref[finite_or_inf])
+    g = got[~finite_or_inf]
+    assert np.all((g & 0x7c00) == 0x7c00) and np.all((g & 0x3ff) != 0)  # NaN stays NaN
+
+
+def test_quantize_q8_0_golden_and_edges():
+    say("quantize_q8_0 ties, zero blocks, tiny and huge scales")
+    rng = np.random.default_rng(11)
+    blocks = [
+        np.array([127, 2.5, -2.5, 0.5, -0.5, 1.5, -1.5, 0.49] + [0] * 24, np.float32),
+        np.zeros(32, np.float32),
+        (rng.standard_normal(32) * 1e-30).astype(np.float32),
+        (rng.standard_normal(32) * 1e4).astype(np.float32),
+        (rng.standard_normal(32) * 2e7).astype(np.float32),    # d beyond the f16 range: scale inf
+        np.full(32, -3.0, np.float32),
+    ]
+    x = np.concatenate(blocks + [rng.standard_normal(32 * 4096).astype(np.float32)])
+    got = wq.quantize_q8_0(torch.from_numpy(x.reshape(1, -1)).cuda()).cpu().numpy()
+    ref = oracle.q8_0_quantize(x.reshape(1, -1))
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------- configurations --
+def test_gemv_f16_1024():
+    """GEMV M=1, K=1024, N=1024, f16 weights, seed 0."""
+    full_case("matmul", F16, 1, 1024, 1024)
+    full_case("gemv", F16, 1, 1024, 1024)
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("nk", DECODE_SHAPES)
+def test_decode_suite(fmt, nk):
+    """Decode GEMV at hidden 2048: gate/up, down, o_proj, LM head."""
+    n, k = nk
+    full_case("matmul", fmt, 1, n, k)
+
+
+@pytest.mark.parametrize("nk", [(6144, 2048), (2048, 6144)])
+def test_prefill_f16_m512(nk):
+    n, k = nk
+    sampled_case("matmul", F16, 512, n, k)
+
+
+@pytest.mark.parametrize("nk", SWEEP_SHAPES)
+@pytest.mark.parametrize("m", SWEEP_M)
+def test_q8_sweep(nk, m):
+    n, k = nk
+    if m <= 16:
+        full_case("matmul", Q8, m, n, k)
+    else:
+        sampled_case("matmul", Q8, m, n, k)
+
+
+# ---------------------------------------------------------- ragged / edges --
+RAGGED = [(1, 1, 32), (1, 7, 96), (1, 129, 1056), (1, 1000, 4128), (1, 33, 256), (1, 65, 8192),
+          (2, 5, 64), (3, 77, 160), (17, 130, 288), (130, 97, 320), (257, 300, 512), (33, 1, 2048),
+          (1, 300, 20480), (5, 4099, 256)]
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("mnk", RAGGED, ids=[f"{m}x{n}x{k}" for m, n, k in RAGGED])
+def test_ragged(fmt, mnk):
+    m, n, k = mnk
+    full_case("matmul", fmt, m, n, k, seed=1)
+    if m == 1:
+        full_case("gemm", fmt, m, n, k, seed=1)
+
+
+@pytest.mark.parametrize("mnk", [(1, 37, 1), (1, 50, 7), (2, 19, 33), (1, 64, 1001), (9, 40, 999), (1, 8, 4100)])
+def test_f16_any_k(mnk):
+    """K not a multiple of 8 (or of 32): the general code paths."""
+    m, n, k = mnk
+    full_case("matmul", F16, m, n, k, seed=2)
+    full_case("gemm", F16, m, n, k, seed=2)
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+def test_misaligned_pointers(fmt, entry):
+    """a offset by 4 bytes and b by 2 bytes from 16-byte alignment."""
+    m, n, k = (1, 300, 2048)
+    say(f"misaligned {entry} fmt={fmt}")
+    ref_b, dev_b = encoded(n, k, fmt, 3)
+    a = acts(m, k, 3)
+    raw = dev_b.view(-1).view(torch.uint8)
+    b_buf = torch.empty(raw.numel() + 2, dtype=torch.uint8, device="cuda")
+    b_buf[2:].copy_(raw)
+    a_buf = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+    a_buf[1:].copy_(torch.from_numpy(a.ravel()))
+    c = torch.full((m, n), float("nan"), device="cuda")
+    # Shifted pointers go through the C ABI directly (the binding takes whole tensors).
+    L = wq._lib
+    s = torch.cuda.current_stream().cuda_stream
+    bp = b_buf.data_ptr() + 2
+    if entry == "gemv":
+        fn = L.wq_gemv_f16 if fmt == F16 else L.wq_gemv_q8_0
+        st = fn(a_buf.data_ptr() + 4, bp, c.data_ptr(), n, k, s)
+    else:
+        fn = L.wq_gemm_f16 if fmt == F16 else L.wq_gemm_q8_0
+        st = fn(a_buf.data_ptr() + 4, bp, c.data_ptr(), m, n, k, s)
+    assert st == wq.WQ_OK
+    torch.cuda.synchronize()
+    c_ref, bound = oracle.matmul(a, ref_b, fmt, m, n, k)
+    assert_close(c.cpu().numpy(), c_ref, bound, "misaligned")
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8])
+def test_onehot_a_dequant_bit_exact(fmt):
+    """a = e_j gives c[n] = w[n, j] exactly: the decode is bit-exact, through the
+    GEMV and through the GEMM."""
+    n, k = 4099, 2048
+    say(f"one-hot a fmt={fmt}")
+    ref_b, dev_b = encoded(n, k, fmt, 4)
+    w = oracle.decode(ref_b, fmt, n, k)
+    js = [0, 1, 31, 32, 33, 1000, 2047]
+    a = np.zeros((len(js), k), np.float32)
+    for i, j in enumerate(js):
+        a[i, j] = 1.0
+    for i, j in enumerate(js):
+        c = run_gpu("gemv", fmt, a[i:i + 1], dev_b, 1, n, k)
+        assert np.array_equal(c[0].astype(np.float64), w[:, j]), f"gemv column {j}"
+    c = run_gpu("gemm", fmt, a, dev_b, len(js), n, k)
+    for i, j in enumerate(js):
+        assert np.array_equal(c[i].astype(np.float64), w[:, j]), f"gemm column {j}"
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8])
+def test_identity_a_gives_transposed_weights(fmt):
+    """A = I (M = K) gives C = W^T exactly: checks the matrix-core lane layout
+    and every tile edge of the GEMM."""
+    for (n, k) in [(96, 256), (300, 160)]:
+        say(f"identity a fmt={fmt} n={n} k={k}")
+        ref_b, dev_b = encoded(n, k, fmt, 5)
+        w = oracle.decode(ref_b, fmt, n, k)
+        c = run_gpu("gemm", fmt, np.eye(k, dtype=np.float32), dev_b, k, n, k)
+        assert np.array_equal(c.astype(np.float64), w.T)
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8])
+def test_empty_and_k0(fmt):
+    say(f"empty outputs fmt={fmt}")
+    c = torch.full((4, 8), float("nan"), device="cuda")
+    a = torch.zeros(4 * 64, device="cuda")
+    b = torch.zeros(8 * 64 * 2, dtype=torch.uint8, device="cuda")
+    wq.wq_matmul(a, b, c, 0, 8, 64, fmt)
+    wq.wq_matmul(a, b, c, 4, 0, 64, fmt)
+    torch.cuda.synchronize()
+    assert torch.isnan(c).all()
+    if fmt == F16:
+        wq.wq_matmul(None, None, c, 4, 8, 0, F16)
+        wq.wq_gemv_f16(None, None, c, 8, 0)
+        torch.cuda.synchronize()
+        assert (c == 0).all()
+    else:
+        with pytest.raises(wq.WQError):
+            wq.wq_matmul(a, b, c, 4, 8, 0, Q8)
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("m", [1, 7, 512])
+def test_deterministic_and_linear(fmt, m):
+    """Repeated calls are bitwise identical; C(2A) = 2 C(A) and C(-A) = -C(A)."""
+    n, k = 2048, 2048
+    say(f"determinism fmt={fmt} m={m}")
+    _, dev_b = encoded(n, k, fmt, 6)
+    a = acts(m, k, 6)
+    c1 = run_gpu("matmul", fmt, a, dev_b, m, n, k)
+    c2 = run_gpu("matmul", fmt, a, dev_b, m, n, k)
+    assert np.array_equal(c1, c2)
+    assert np.array_equal(run_gpu("matmul", fmt, 2 * a, dev_b, m, n, k), 2 * c1)
+    assert np.array_equal(run_gpu("matmul", fmt, -a, dev_b, m, n, k), -c1)
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8])
+def test_routes_agree_and_are_counted(fmt):
+    n, k = 1000, 1024
+    ref_b, dev_b = encoded(n, k, fmt, 7)
+    c_ref = {}
+    for m in (1, 3):
+        a = acts(m, k, 7)
+        c_ref[m] = oracle.matmul(a, ref_b, fmt, m, n, k)
+    try:
+        for route, per_call in ((wq.WQ_ROUTE_GEMV, {1: 1, 3: 3}), (wq.WQ_ROUTE_GEMM, {1: 1, 3: 1}),
+                                (wq.WQ_ROUTE_AUTO, None)):
+            wq.wq_set_forced_route(route)
+            for m in (1, 3):
+                say(f"route={route} fmt={fmt} m={m}")
+                wq.wq_reset_route_counts()
+                c = run_gpu("matmul", fmt, acts(m, k, 7), dev_b, m, n, k)
+                assert_close(c, *c_ref[m], f"route {route} m={m}")
+                gv, gm = wq.wq_route_count(wq.WQ_ROUTE_GEMV), wq.wq_route_count(wq.WQ_ROUTE_GEMM)
+                if route == wq.WQ_ROUTE_GEMV:
+                    assert (gv, gm) == (per_call[m], 0)
+                elif route == wq.WQ_ROUTE_GEMM:
+                    assert (gv, gm) == (0, 1)
+                else:
+                    assert (gv, gm) == ((1, 0) if m == 1 else (0, 1))
+    finally:
+        wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
+
+
+def test_nondefault_stream():
+    n, k = 2048, 2048
+    say("non-default stream")
+    ref_b, dev_b = encoded(n, k, F16, 8)
+    s = torch.cuda.Stream()
+    for m in (1, 64):
+        a = acts(m, k, 8)
+        c = run_gpu("matmul", F16, a, dev_b, m, n, k, stream=s)
+        c_ref, bound = oracle.matmul(a, ref_b, F16, m, n, k)
+        assert_close(c, c_ref, bound, f"stream m={m}")

@@ -123,7 +123,9 @@ __global__ __launch_bounds__(256) void gemv_f16_any(const float *__restrict__ a,
 // ----------------------------------------------------------------- Q8_0 ----
 
 constexpr int kQ8BlockBytes = 34;
-constexpr int kQ8StageTarget = 17408;  // bytes staged per pass (8 rows at K = 2048)
+constexpr int kQ8Chunks = 17;                // 16-byte chunks per lane per pass
+constexpr int kQ8StageTarget = kQ8Chunks * 64 * 16;  // 17408 bytes: 8 rows at K = 2048
+constexpr int kQ8MaxRowsPerPass = kQ8StageTarget / (8 * kQ8BlockBytes);  // 64 rows at K = 256
 
 // Dot product of one Q8_0 block held in LDS at byte offset pb with the 32
 // activations av[0..31]: returns d * sum_i q_i * av[i].
@@ -149,7 +151,11 @@ __device__ __forceinline__ float q8_block_dot(const uint8_t *stage, int pb, cons
 
 // One wave per workgroup.  LPR lanes share a row; lane l covers blocks
 // j = l % LPR + LPR * t (t < J) of that row and keeps a[32 j .. 32 j + 32) in
-// VGPRs.  Each pass stages S consecutive rows (S * row_bytes bytes) in LDS.
+// VGPRs.  Each pass covers S consecutive rows, i.e. S * row_bytes contiguous
+// bytes (at most kQ8Chunks * 64 16-byte chunks).  The chunks of the next pass
+// are loaded into registers (kQ8Chunks independent 128-bit loads per lane, all
+// in flight together) while the current pass is decoded from LDS; they are
+// written to LDS at the top of the next iteration.
 // Requires K % 256 == 0 (rows are whole 16-byte chunks), 16-byte aligned a, b.
 template <int J, int LPR>
 __global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a,
@@ -179,14 +185,41 @@ __global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a
         }
     }
 
+    wait_vmem_all();
+
+    // Chunks of pass p: bytes [p*S*row_bytes, ...) for min(S, n - p*S) rows.
+    auto pass_chunks = [&](int64_t p) -> int {
+        return static_cast<int>(min<int64_t>(S, n - p * S)) * row_bytes / 16;
+    };
+    uint4 next[kQ8Chunks];
+    auto fetch = [&](int64_t p) {
+        const int nch = pass_chunks(p);
+        const uint4 *src = reinterpret_cast<const uint4 *>(b + p * S * row_bytes);
+#pragma unroll
+        for (int u = 0; u < kQ8Chunks; ++u) {
+            const int ci = u * kWave + lane;
+            if (ci < nch) next[u] = load_nt16(src + ci);
+        }
+    };
+
     const uint8_t *stage = reinterpret_cast<const uint8_t *>(stage4);
-    for (int64_t p = blockIdx.x; p < passes; p += gridDim.x) {
+    __shared__ float result[kQ8MaxRowsPerPass];
+    int64_t p = blockIdx.x;
+    if (p < passes) fetch(p);
+    for (; p < passes; p += gridDim.x) {
         const int64_t row0 = p * S;
         const int rows = static_cast<int>(min<int64_t>(S, n - row0));
-        const int nchunks = rows * row_bytes / 16;
-        const uint4 *src = reinterpret_cast<const uint4 *>(b + row0 * row_bytes);
-        for (int ci = lane; ci < nchunks; ci += kWave) stage4[ci] = load_nt16(src + ci);
+        const int nch = rows * row_bytes / 16;
+        __syncthreads();  // the previous pass is fully read from LDS
+#pragma unroll
+        for (int u = 0; u < kQ8Chunks; ++u) {
+            const int ci = u * kWave + lane;
+            if (ci < nch) stage4[ci] = next[u];
+        }
         __syncthreads();
+        if (p + gridDim.x < passes) fetch(p + gridDim.x);  // in flight during the decode below
+        // The decode loop has no global memory access, so nothing in it waits
+        // for the prefetch; row results go to LDS and leave in one store.
         for (int sb = 0; sb < rows; sb += RPL) {
             const int s = sb + rsub;
             float acc = 0.f;
@@ -198,9 +231,10 @@ __global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a
                 }
             }
             acc = group_sum<LPR>(acc);
-            if (jl == 0 && s < rows) c[row0 + s] = acc;
+            if (jl == 0 && s < rows) result[s] = acc;
         }
         __syncthreads();
+        if (lane < rows) c[row0 + lane] = result[lane];
     }
 }
 
@@ -267,7 +301,7 @@ template <int J, int LPR>
 hipError_t run_q8_staged(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
                          hipStream_t s, int cus) {
     const int row_bytes = static_cast<int>((k >> 5) * kQ8BlockBytes);
-    const int S = std::max(1, kQ8StageTarget / row_bytes);
+    const int S = std::max(1, kQ8StageTarget / row_bytes);  // S * row_bytes <= kQ8StageTarget
     const int64_t passes = (n + S - 1) / S;
     const int64_t blocks = balanced_workers(passes, static_cast<int64_t>(cus) * 8);
     const size_t lds = static_cast<size_t>(S) * row_bytes + 16;  // +16: 9-dword window slack
@@ -313,7 +347,7 @@ hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t 
     if (e != hipSuccess) return e;
     const int64_t nb = k / 32;
     const int64_t row_bytes = nb * kQ8BlockBytes;
-    if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= 32768) {
+    if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= kQ8StageTarget) {
         if (nb >= 64) {
             const int64_t J = (nb + 63) / 64;
             switch (J) {

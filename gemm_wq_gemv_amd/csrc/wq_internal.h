@@ -18,6 +18,11 @@ __device__ __forceinline__ uint4 load_nt16(const uint4 *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free).  Used once after loads
+// whose registers stay live across a loop that issues newer loads, so the
+// compiler does not re-wait for them inside the loop.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // binary16 bits -> f32, exact (the hardware conversion keeps subnormals).
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));

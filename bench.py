@@ -284,7 +284,7 @@ def main():
             torch.cuda.empty_cache()
         secondary["q8_sweep"] = out
 
-    if not args.no_secondary and only is None:
+    if (not args.no_secondary and only is None) or only == "f16":
         log("device copy reference")
         nb = 1 << 30
         src = torch.empty(nb // 4, dtype=torch.float32, device="cuda")

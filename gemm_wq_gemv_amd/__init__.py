@@ -63,6 +63,8 @@ def _load() -> ctypes.CDLL:
         "wq_pack_f16": (I, [P, P, I64, P]),
         "wq_quantize_q8_0": (I, [P, P, I64, P]),
         "wq_route_for": (I, [I64, I64, I64, I]),
+        "wq_gemm_plan": (I, [I64, I64, I64, I, I, P, P, P]),
+        "wq_set_gemm_plan": (I, [I, I, I]),
         "wq_set_forced_route": (I, [I]),
         "wq_route_count": (ctypes.c_uint64, [I]),
         "wq_reset_route_counts": (None, []),
@@ -184,6 +186,21 @@ def wq_quantize_q8_0(w, out, count: int, stream=None) -> None:
 
 def wq_route_for(m: int, n: int, k: int, fmt: int) -> int:
     return int(_lib.wq_route_for(m, n, k, fmt))
+
+
+def wq_gemm_plan(m: int, n: int, k: int, fmt: int, cus: int = 256):
+    """(bm, bn, splits) the GEMM uses for this problem on `cus` compute units."""
+    bm, bn, sp = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(_lib.wq_gemm_plan(m, n, k, fmt, cus, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(sp)),
+           "wq_gemm_plan")
+    return bm.value, bn.value, sp.value
+
+
+def wq_set_gemm_plan(bm: int, bn: int, splits: int) -> None:
+    _check(_lib.wq_set_gemm_plan(bm, bn, splits), "wq_set_gemm_plan")
+
+
+GEMM_TILES = [(128, 128), (128, 96), (128, 64), (64, 128), (64, 64), (32, 128), (16, 128), (16, 64)]
 
 
 def wq_set_forced_route(route: int) -> int:

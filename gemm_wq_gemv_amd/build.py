@@ -1,6 +1,7 @@
 """Build libwqmm.so in-tree with hipcc for gfx950.
 
-Usage: ``python -m gemm_wq_gemv_amd.build`` (or ``__graft_entry__.build()``).
+Usage: ``python gemm_wq_gemv_amd/build.py`` (or ``__graft_entry__.build()``); not
+``python -m``, which would first import the package and load the old library.
 Always recompiles.  Objects go to ``gemm_wq_gemv_amd/_build/``; the shared
 library to ``gemm_wq_gemv_amd/libwqmm.so``.
 """

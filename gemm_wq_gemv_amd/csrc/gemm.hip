@@ -10,21 +10,30 @@
 // CDNA4 design:
 //  * A workgroup of 4 waves computes a BM x BN tile of C; waves are arranged
 //    WM x WN and each owns a (BM/WM) x (BN/WN) sub-tile made of 16x16 blocks,
-//    each block accumulated by v_mfma_f32_16x16x4_f32 in four AGPR/VGPRs.
+//    each block accumulated by v_mfma_f32_16x16x4_f32 in four AGPRs.
 //  * The K loop steps by BK = 32, exactly one Q8_0 block per weight row.  Each
 //    step stages the A tile (f32) and the weight tile, widened (f16) or
-//    dequantised (d*q, exact in f32), into LDS, double-buffered: the global
-//    loads of step k+1 are in flight while the matrix cores work on step k,
-//    with one barrier per step.
+//    dequantised (d*q, exact in f32), in LDS.  Three-stage pipeline with one
+//    barrier per step: tile i is read from LDS buffer i&1 by the matrix cores,
+//    tile i+1 (already in registers) is written to the other buffer between
+//    the two halves of step i's MFMAs, and tile i+2 is loading from memory.
 //  * The reduction index inside a 32-wide step is permuted so that every lane
 //    reads 8 consecutive k (two 128-bit LDS reads) per 16-row fragment: in MFMA
 //    step t the lane group g = lane/16 supplies k = 8g + t.  The sum over k is
 //    unchanged; only its order differs.
 //  * Rows of the LDS tiles are padded by 16 bytes to spread LDS banks.
+//  * Split K: when the (M, N) tiles alone cannot fill 256 CUs (small M, long
+//    K), the K range is cut into equal splits whose partial tiles go to a
+//    scratch buffer and are summed in split order by a second pass, so the
+//    result is deterministic.  A cost model picks the tile shape and split
+//    count per call.
 //  * Workgroup -> tile mapping is XCD-aware: workgroups are dealt round-robin
 //    to the 8 XCDs, so consecutive workgroup ids on one XCD are given tiles
 //    that share weight columns (M-fastest tile order) and hit the same L2.
 #include "wq_internal.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace wq {
 namespace {
@@ -64,7 +73,12 @@ struct Gemm {
         uint32_t q8[FMT == FMT_Q8_0 ? B8_ITERS : 1][8];
     };
 
-    // Global -> registers for the k-tile starting at k0.
+    // Global -> registers for the k-tile starting at k0.  On the vector path
+    // every thread issues the same number of loads on every call (addresses
+    // are clamped into the matrices and out-of-range values zeroed after the
+    // load), so the compiler can count outstanding loads across the software
+    // pipeline instead of draining them all.  VEC requires K % 8 == 0 (f16)
+    // or K % 32 == 0 (Q8_0) and 16-byte aligned rows of A (and of f16 B).
     static __device__ __forceinline__ void load(Regs &r, const float *__restrict__ a,
                                                 const void *__restrict__ bw, int64_t M, int64_t N,
                                                 int64_t K, int64_t m0, int64_t n0, int64_t k0,
@@ -75,16 +89,17 @@ struct Gemm {
             const int c4 = tid & 7;
             const int64_t gm = m0 + row, gk = k0 + 4 * c4;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (row < BM && gm < M) {
+            if (VEC) {
+                // Rows past M only feed outputs that are never stored; the
+                // K tail is zeroed when the tile is written to LDS.
+                const int64_t gmc = min<int64_t>(gm, M - 1), gkc = min<int64_t>(gk, K - 4);
+                v = *reinterpret_cast<const float4 *>(a + gmc * K + gkc);
+            } else if (row < BM && gm < M) {
                 const float *p = a + gm * K + gk;
-                if (VEC) {
-                    if (gk + 4 <= K) v = *reinterpret_cast<const float4 *>(p);
-                } else {
-                    if (gk + 0 < K) v.x = p[0];
-                    if (gk + 1 < K) v.y = p[1];
-                    if (gk + 2 < K) v.z = p[2];
-                    if (gk + 3 < K) v.w = p[3];
-                }
+                if (gk + 0 < K) v.x = p[0];
+                if (gk + 1 < K) v.y = p[1];
+                if (gk + 2 < K) v.z = p[2];
+                if (gk + 3 < K) v.w = p[3];
             }
             r.a[i] = v;
         }
@@ -96,17 +111,16 @@ struct Gemm {
                 const int c8 = tid & 3;
                 const int64_t gn = n0 + row, gk = k0 + 8 * c8;
                 uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (row < BN && gn < N) {
+                if (VEC) {
+                    const int64_t gnc = min<int64_t>(gn, N - 1), gkc = min<int64_t>(gk, K - 8);
+                    v = *reinterpret_cast<const uint4 *>(b + gnc * K + gkc);
+                } else if (row < BN && gn < N) {
                     const uint16_t *p = b + gn * K + gk;
-                    if (VEC) {
-                        if (gk + 8 <= K) v = *reinterpret_cast<const uint4 *>(p);
-                    } else {
-                        uint32_t h[8];
+                    uint32_t h[8];
 #pragma unroll
-                        for (int u = 0; u < 8; ++u) h[u] = (gk + u < K) ? p[u] : 0u;
-                        v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                                       h[6] | (h[7] << 16));
-                    }
+                    for (int u = 0; u < 8; ++u) h[u] = (gk + u < K) ? p[u] : 0u;
+                    v = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                   h[6] | (h[7] << 16));
                 }
                 r.b16[i] = v;
             }
@@ -118,35 +132,36 @@ struct Gemm {
             for (int i = 0; i < B8_ITERS; ++i) {
                 const int row = (tid >> 1) + 128 * i;
                 const int h = tid & 1;
-                const int64_t gn = n0 + row;
-                r.d8[i] = 0u;
+                // Rows past N only feed outputs that are never stored.
+                const int64_t gnc = min<int64_t>(n0 + row, N - 1);
+                const uint16_t *blk =
+                    reinterpret_cast<const uint16_t *>(b + gnc * row_bytes + kb * kQ8BlockBytes);
+                r.d8[i] = blk[0];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) r.q8[i][u] = 0u;
-                if (row < BN && gn < N) {
-                    const uint16_t *blk =
-                        reinterpret_cast<const uint16_t *>(b + gn * row_bytes + kb * kQ8BlockBytes);
-                    r.d8[i] = blk[0];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) r.q8[i][u] = blk[1 + 8 * h + u];
-                }
+                for (int u = 0; u < 8; ++u) r.q8[i][u] = blk[1 + 8 * h + u];
             }
         }
     }
 
     // Registers -> LDS (A as is; weights widened or dequantised to f32).
+    // k0/K: the tile's first k and the reduction length; on the vector path the
+    // chunks at or past K (f16 with K % 32 != 0) are written as zeros here.
     static __device__ __forceinline__ void store(const Regs &r, float (*As)[LDP], float (*Bs)[LDP],
-                                                 int tid) {
+                                                 int tid, int64_t k0, int64_t K) {
+        const bool a_in = !VEC || k0 + 4 * (tid & 7) + 4 <= K;
 #pragma unroll
         for (int i = 0; i < A_ITERS; ++i) {
             const int row = (tid >> 3) + 32 * i;
-            if (row < BM) *reinterpret_cast<float4 *>(&As[row][4 * (tid & 7)]) = r.a[i];
+            if (row < BM)
+                *reinterpret_cast<float4 *>(&As[row][4 * (tid & 7)]) = a_in ? r.a[i] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         if constexpr (FMT == FMT_F16) {
+            const bool b_in = !VEC || k0 + 8 * (tid & 3) + 8 <= K;
 #pragma unroll
             for (int i = 0; i < B16_ITERS; ++i) {
                 const int row = (tid >> 2) + 64 * i;
                 if (row < BN) {
-                    const uint4 v = r.b16[i];
+                    const uint4 v = b_in ? r.b16[i] : make_uint4(0u, 0u, 0u, 0u);
                     float4 lo = make_float4(half_bits_to_float(v.x & 0xffffu), half_bits_to_float(v.x >> 16),
                                             half_bits_to_float(v.y & 0xffffu), half_bits_to_float(v.y >> 16));
                     float4 hi = make_float4(half_bits_to_float(v.z & 0xffffu), half_bits_to_float(v.z >> 16),
@@ -177,40 +192,56 @@ struct Gemm {
         }
     }
 
-    static __device__ __forceinline__ void compute(v4f (&acc)[FM][FN], const float (*As)[LDP],
-                                                   const float (*Bs)[LDP], int wm, int wn, int lane) {
+    // Fragments of one k-tile: lane (i = lane % 16, g = lane / 16) holds, for
+    // fragment f, the 8 consecutive k = 8g .. 8g+7 of its row: `lo` covers MFMA
+    // steps t = 0..3 and `hi` steps t = 4..7.
+    struct Frags {
+        float4 a_lo[FM], a_hi[FM], b_lo[FN], b_hi[FN];
+    };
+
+    static __device__ __forceinline__ void read_frags(Frags &fr, const float (*As)[LDP],
+                                                      const float (*Bs)[LDP], int wm, int wn,
+                                                      int lane) {
         const int li = lane & 15, lg = lane >> 4;
-        float af[FM][8], bf[FN][8];
 #pragma unroll
-        for (int f = 0; f < FM; ++f) {
-            const float *src = &As[wm * WTM + 16 * f + li][8 * lg];
-            const float4 x = *reinterpret_cast<const float4 *>(src);
-            const float4 y = *reinterpret_cast<const float4 *>(src + 4);
-            af[f][0] = x.x; af[f][1] = x.y; af[f][2] = x.z; af[f][3] = x.w;
-            af[f][4] = y.x; af[f][5] = y.y; af[f][6] = y.z; af[f][7] = y.w;
-        }
+        for (int f = 0; f < FM; ++f)
+            fr.a_lo[f] = *reinterpret_cast<const float4 *>(&As[wm * WTM + 16 * f + li][8 * lg]);
 #pragma unroll
-        for (int f = 0; f < FN; ++f) {
-            const float *src = &Bs[wn * WTN + 16 * f + li][8 * lg];
-            const float4 x = *reinterpret_cast<const float4 *>(src);
-            const float4 y = *reinterpret_cast<const float4 *>(src + 4);
-            bf[f][0] = x.x; bf[f][1] = x.y; bf[f][2] = x.z; bf[f][3] = x.w;
-            bf[f][4] = y.x; bf[f][5] = y.y; bf[f][6] = y.z; bf[f][7] = y.w;
-        }
+        for (int f = 0; f < FN; ++f)
+            fr.b_lo[f] = *reinterpret_cast<const float4 *>(&Bs[wn * WTN + 16 * f + li][8 * lg]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+        for (int f = 0; f < FM; ++f)
+            fr.a_hi[f] = *reinterpret_cast<const float4 *>(&As[wm * WTM + 16 * f + li][8 * lg + 4]);
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+            fr.b_hi[f] = *reinterpret_cast<const float4 *>(&Bs[wn * WTN + 16 * f + li][8 * lg + 4]);
+    }
+
+    static __device__ __forceinline__ float comp(const float4 &v, int t) {
+        return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w;
+    }
+
+    // Four MFMA steps (k = 8g + t0 .. 8g + t0 + 3) on every 16x16 block.
+    static __device__ __forceinline__ void mfma_half(v4f (&acc)[FM][FN], const float4 (&a)[FM],
+                                                     const float4 (&b)[FN]) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][t], bf[j][t], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(a[i], t), comp(b[j], t), acc[i][j],
+                                                                     0, 0, 0);
     }
 };
 
+// Grid: tiles * splits workgroups.  Split s covers k-tiles [s*kts, min(kt, (s+1)*kts)).
+// With one split the tile goes straight to C; otherwise to out = partial + s*M*N
+// (same layout), summed in split order by reduce_splits.
 template <int BM, int BN, int WM, int WN, int FMT, bool VEC>
 __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, const void *__restrict__ bw,
                                                  float *__restrict__ c, int64_t M, int64_t N, int64_t K,
-                                                 int mtiles, int tiles) {
+                                                 int mtiles, int tiles, int splits, int kts) {
     using G = Gemm<BM, BN, WM, WN, FMT, VEC>;
     __shared__ float As[2][BM][LDP];
     __shared__ float Bs[2][BN][LDP];
@@ -218,9 +249,14 @@ __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, co
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int tile = xcd_tile(blockIdx.x, tiles);
+    const int idx = xcd_tile(blockIdx.x, tiles * splits);
+    const int tile = idx % tiles, split = idx / tiles;
     const int64_t m0 = static_cast<int64_t>(tile % mtiles) * BM;
     const int64_t n0 = static_cast<int64_t>(tile / mtiles) * BN;
+    const int64_t ktiles = (K + BK - 1) / BK;
+    const int64_t kt0 = static_cast<int64_t>(split) * kts;
+    const int64_t nkt = min<int64_t>(ktiles, kt0 + kts) - kt0;  // >= 1 by construction
+    float *out = c + static_cast<int64_t>(split) * M * N;
 
     v4f acc[G::FM][G::FN];
 #pragma unroll
@@ -228,102 +264,220 @@ __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, co
 #pragma unroll
         for (int j = 0; j < G::FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t ktiles = (K + BK - 1) / BK;
-    typename G::Regs r;
-    G::load(r, a, bw, M, N, K, m0, n0, 0, tid);
-    G::store(r, As[0], Bs[0], tid);
+    // Software pipeline: tile i is in LDS buffer i & 1; tile i+1 sits in
+    // registers and is written to the other buffer between the two MFMA
+    // halves of step i; tile i+2 is being loaded from global memory.
+    typename G::Regs r0, r1;
+    G::load(r0, a, bw, M, N, K, m0, n0, kt0 * BK, tid);
+    G::store(r0, As[0], Bs[0], tid, kt0 * BK, K);
+    G::load(r1, a, bw, M, N, K, m0, n0, (kt0 + min<int64_t>(1, nkt - 1)) * BK, tid);
     __syncthreads();
-    for (int64_t kt = 0; kt < ktiles; ++kt) {
-        const int cur = static_cast<int>(kt & 1);
-        const bool more = kt + 1 < ktiles;
-        if (more) G::load(r, a, bw, M, N, K, m0, n0, (kt + 1) * BK, tid);
-        G::compute(acc, As[cur], Bs[cur], wm, wn, lane);
-        if (more) G::store(r, As[cur ^ 1], Bs[cur ^ 1], tid);
+
+    auto step = [&](int64_t i, typename G::Regs &rnext, typename G::Regs &rfut) {
+        // Always load (the last tile again near the end): a fixed load count.
+        G::load(rfut, a, bw, M, N, K, m0, n0, (kt0 + min<int64_t>(i + 2, nkt - 1)) * BK, tid);
+        const int cur = static_cast<int>(i & 1);
+        typename G::Frags fr;
+        G::read_frags(fr, As[cur], Bs[cur], wm, wn, lane);
+        G::mfma_half(acc, fr.a_lo, fr.b_lo);
+        if (i + 1 < nkt) G::store(rnext, As[cur ^ 1], Bs[cur ^ 1], tid, (kt0 + i + 1) * BK, K);
+        G::mfma_half(acc, fr.a_hi, fr.b_hi);
         __syncthreads();
+    };
+    int64_t i = 0;
+    for (; i + 1 < nkt; i += 2) {
+        step(i, r1, r0);
+        step(i + 1, r0, r1);
     }
+    if (i < nkt) step(i, r1, r0);
 
     // D[i][j] of a 16x16 block: lane l, register v holds row 4*(l/16) + v, column l%16.
     const int li = lane & 15, lg = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < G::FM; ++i) {
+    for (int fi = 0; fi < G::FM; ++fi) {
+        const int64_t rbase = m0 + wm * G::WTM + 16 * fi + 4 * lg;
 #pragma unroll
-        for (int j = 0; j < G::FN; ++j) {
-            const int64_t col = n0 + wn * G::WTN + 16 * j + li;
+        for (int fj = 0; fj < G::FN; ++fj) {
+            const int64_t col = n0 + wn * G::WTN + 16 * fj + li;
+            if (col >= N) continue;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t row = m0 + wm * G::WTM + 16 * i + 4 * lg + v;
-                if (row < M && col < N) c[row * N + col] = acc[i][j][v];
-            }
+            for (int v = 0; v < 4; ++v)
+                if (rbase + v < M) out[(rbase + v) * N + col] = acc[fi][fj][v];
         }
+    }
+}
+
+// C[i] = sum over s < splits of partial[s][i], in split order (deterministic).
+__global__ __launch_bounds__(256) void reduce_splits(const float *__restrict__ partial, float *__restrict__ c,
+                                                     int64_t count, int splits) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < count; e += stride) {
+        float v = partial[e];
+        for (int s = 1; s < splits; ++s) v += partial[static_cast<int64_t>(s) * count + e];
+        c[e] = v;
     }
 }
 
 struct TileCfg {
     int bm, bn;
+    int occ;     // workgroups that fit on one CU at once (LDS and VGPR limits)
+    double eff;  // fraction of the fp32 matrix-core rate one CU sustains on
+                 // this tile when enough workgroups are co-resident
+};
+
+struct Plan {
+    TileCfg t;
+    int splits;
+    int kts;  // k-tiles per split
 };
 
 template <int BM, int BN, int WM, int WN, int FMT>
-hipError_t run(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, bool vec,
-               hipStream_t s) {
+hipError_t run(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, bool vec, int splits,
+               int kts, hipStream_t s) {
     const int64_t mt = (m + BM - 1) / BM, nt = (n + BN - 1) / BN;
     const int64_t tiles = mt * nt;
-    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (tiles * splits > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int64_t grid = tiles * splits;
     if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemm_mfma<BM=%d,BN=%d,WM=%d,WN=%d,fmt=%d,vec=%d> m=%lld n=%lld k=%lld grid=%lld\n",
-                BM, BN, WM, WN, FMT, vec ? 1 : 0, (long long)m, (long long)n, (long long)k, (long long)tiles);
+        fprintf(stderr,
+                "[wqmm] gemm_mfma<BM=%d,BN=%d,WM=%d,WN=%d,fmt=%d,vec=%d> m=%lld n=%lld k=%lld splits=%d kts=%d "
+                "grid=%lld\n",
+                BM, BN, WM, WN, FMT, vec ? 1 : 0, (long long)m, (long long)n, (long long)k, splits, kts,
+                (long long)grid);
     if (vec)
-        hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, true>), dim3(tiles), dim3(256), 0, s, a, b, c, m, n,
-                           k, static_cast<int>(mt), static_cast<int>(tiles));
+        hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, true>), dim3(grid), dim3(256), 0, s, a, b, c, m, n, k,
+                           static_cast<int>(mt), static_cast<int>(tiles), splits, kts);
     else
-        hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, false>), dim3(tiles), dim3(256), 0, s, a, b, c, m, n,
-                           k, static_cast<int>(mt), static_cast<int>(tiles));
+        hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, false>), dim3(grid), dim3(256), 0, s, a, b, c, m, n, k,
+                           static_cast<int>(mt), static_cast<int>(tiles), splits, kts);
     return hipGetLastError();
 }
 
-// Candidate tiles: (BM, BN).  The estimate prefers configurations that fill
-// every CU evenly and, among those, larger tiles (fewer re-reads of A and B).
-constexpr TileCfg kCfgs[] = {{128, 128}, {128, 96}, {128, 64}, {64, 128}, {64, 64}, {32, 128}, {16, 256}, {16, 128}};
+// Tile shapes compiled in, with their occupancy and sustained efficiency.
+// The efficiencies and the co-residency factors in choose_plan were fitted
+// to measured run times of every (tile, split) choice on MI355X for the
+// M = 512 prefill shapes and the Q8_0 M sweep (M = 2 .. 64).
+constexpr TileCfg kCfgs[] = {
+    {128, 128, 2, 0.90}, {128, 96, 2, 0.873}, {128, 64, 2, 0.837}, {64, 128, 2, 0.837},
+    {64, 64, 4, 0.80},   {32, 128, 3, 0.70},  {16, 128, 3, 0.35},  {16, 64, 6, 0.30},
+};
 
-double tile_efficiency(const TileCfg &t) {
-    // Relative throughput per CU of one tile shape when every CU is busy
-    // (bigger wave tiles amortise LDS traffic and barriers better).
-    const double area = static_cast<double>(t.bm) * t.bn;
-    return area / (area + 2048.0);
-}
-
-TileCfg choose_tile(int64_t m, int64_t n, int cus) {
-    TileCfg best = kCfgs[0];
+// Cost model over tile shapes and K splits, in CU clock cycles.  The busiest
+// CU runs per_cu workgroups, co = min(per_cu, occ) of them at once; a CU with
+// a single workgroup (one wave per SIMD) loses latency hiding (factor 0.6),
+// two recover most of it (0.92).  Weight streaming bounds the time from
+// below; a split adds the partial-sum pass.
+Plan choose_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus) {
+    const int64_t ktiles = (k + BK - 1) / BK;
+    const double wbytes = fmt == FMT_F16 ? 2.0 * n * k : static_cast<double>(n) * (k / 32) * kQ8BlockBytes;
+    const double hbm_bytes_per_cycle = 6.0e12 / 2.4e9;  // sustained, whole chip
+    Plan best{kCfgs[0], 1, static_cast<int>(ktiles)};
     double best_t = 1e300;
     for (const TileCfg &t : kCfgs) {
-        const int64_t mt = (m + t.bm - 1) / t.bm, nt = (n + t.bn - 1) / t.bn;
-        const int64_t tiles = mt * nt;
-        const int per_cu = 1;
-        const int64_t rounds = (tiles + static_cast<int64_t>(cus) * per_cu - 1) / (static_cast<int64_t>(cus) * per_cu);
-        // time ~ rounds * tile area (padded M included) / efficiency
-        const double est = static_cast<double>(rounds) * t.bm * t.bn / tile_efficiency(t);
-        if (est < best_t * 0.999) {
-            best_t = est;
-            best = t;
+        if (t.bm > 16 && t.bm >= 2 * m) continue;  // mostly padding rows
+        const int64_t tiles = ((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn);
+        for (int sp : {1, 2, 3, 4, 6, 8, 12, 16}) {
+            const int64_t kts = (ktiles + sp - 1) / sp;
+            const int64_t splits = (ktiles + kts - 1) / kts;  // no empty split
+            if (splits != sp && sp != 1) continue;
+            if (sp > 1 && kts < 4) continue;
+            const int64_t wgs = tiles * splits;
+            if (wgs > 0x7fffffffLL) continue;
+            const int64_t per_cu = (wgs + cus - 1) / cus;
+            const int64_t co = std::min<int64_t>(per_cu, t.occ);
+            const double f = co <= 1 ? 0.6 : co == 2 ? 0.92 : 1.0;
+            double est = per_cu * (2.0 * t.bm * t.bn * BK * kts) / (256.0 * t.eff * f) +
+                         2000.0 * static_cast<double>((per_cu + co - 1) / co);
+            const double mt = static_cast<double>((m + t.bm - 1) / t.bm);
+            est = std::max(est, wbytes * std::min(mt, 4.0) / hbm_bytes_per_cycle);
+            if (splits > 1) est += 2.0 * splits * m * n * 4.0 / hbm_bytes_per_cycle + 1000.0;
+            if (est < best_t * 0.98) {
+                best_t = est;
+                best = Plan{t, static_cast<int>(splits), static_cast<int>(kts)};
+            }
         }
     }
     return best;
 }
 
 template <int FMT>
+hipError_t dispatch_tile(const Plan &p, const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k,
+                         bool vec, hipStream_t s) {
+    const int sp = p.splits, kts = p.kts;
+    const TileCfg t = p.t;
+    if (t.bm == 128 && t.bn == 128) return run<128, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
+    if (t.bm == 128 && t.bn == 96) return run<128, 96, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
+    if (t.bm == 128 && t.bn == 64) return run<128, 64, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
+    if (t.bm == 64 && t.bn == 128) return run<64, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
+    if (t.bm == 64 && t.bn == 64) return run<64, 64, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
+    if (t.bm == 32 && t.bn == 128) return run<32, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
+    if (t.bm == 16 && t.bn == 128) return run<16, 128, 1, 4, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
+    return run<16, 64, 1, 4, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
+}
+
+std::atomic<uint64_t> g_plan_override{0};  // bm | bn << 16 | splits << 32; 0 = none
+
+bool known_tile(int bm, int bn) {
+    for (const TileCfg &t : kCfgs)
+        if (t.bm == bm && t.bn == bn) return true;
+    return false;
+}
+
+Plan planned(int64_t m, int64_t n, int64_t k, int fmt, int cus) {
+    const uint64_t o = g_plan_override.load(std::memory_order_relaxed);
+    if (o == 0) return choose_plan(m, n, k, fmt, cus);
+    const int bm = static_cast<int>(o & 0xffff), bn = static_cast<int>((o >> 16) & 0xffff);
+    const int64_t ktiles = (k + BK - 1) / BK;
+    const int64_t want = std::max<int64_t>(1, std::min<int64_t>(static_cast<int64_t>(o >> 32), ktiles));
+    const int64_t kts = (ktiles + want - 1) / want;
+    TileCfg t = kCfgs[0];
+    for (const TileCfg &c : kCfgs)
+        if (c.bm == bm && c.bn == bn) t = c;
+    return Plan{t, static_cast<int>((ktiles + kts - 1) / kts), static_cast<int>(kts)};
+}
+
+template <int FMT>
 hipError_t dispatch(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, bool vec,
                     hipStream_t s, int cus) {
-    const TileCfg t = choose_tile(m, n, cus);
-    if (t.bm == 128 && t.bn == 128) return run<128, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, s);
-    if (t.bm == 128 && t.bn == 96) return run<128, 96, 2, 2, FMT>(a, b, c, m, n, k, vec, s);
-    if (t.bm == 128 && t.bn == 64) return run<128, 64, 2, 2, FMT>(a, b, c, m, n, k, vec, s);
-    if (t.bm == 64 && t.bn == 128) return run<64, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, s);
-    if (t.bm == 64 && t.bn == 64) return run<64, 64, 2, 2, FMT>(a, b, c, m, n, k, vec, s);
-    if (t.bm == 32 && t.bn == 128) return run<32, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, s);
-    if (t.bm == 16 && t.bn == 256) return run<16, 256, 1, 4, FMT>(a, b, c, m, n, k, vec, s);
-    return run<16, 128, 1, 4, FMT>(a, b, c, m, n, k, vec, s);
+    Plan p = planned(m, n, k, FMT, cus);
+    if (p.splits == 1) return dispatch_tile<FMT>(p, a, b, c, m, n, k, vec, s);
+    // Split K: partial tiles go to a stream-ordered scratch buffer from the
+    // device's default memory pool, then one pass sums them in split order.
+    float *partial = nullptr;
+    const size_t bytes = static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(n) * 4;
+    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&partial), bytes, s);
+    if (e != hipSuccess) return e;
+    e = dispatch_tile<FMT>(p, a, b, partial, m, n, k, vec, s);
+    if (e == hipSuccess) {
+        const int64_t count = m * n;
+        const int64_t grid = std::min<int64_t>((count + 255) / 256, 65536);
+        hipLaunchKernelGGL(reduce_splits, dim3(grid), dim3(256), 0, s, partial, c, count, p.splits);
+        e = hipGetLastError();
+    }
+    const hipError_t ef = hipFreeAsync(partial, s);
+    return e != hipSuccess ? e : ef;
 }
 
 }  // namespace
+
+void gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits) {
+    const Plan p = planned(m, n, k, fmt, cus);
+    *bm = p.t.bm;
+    *bn = p.t.bn;
+    *splits = p.splits;
+}
+
+bool set_gemm_plan_override(int bm, int bn, int splits) {
+    if (bm == 0 && bn == 0 && splits == 0) {
+        g_plan_override.store(0, std::memory_order_relaxed);
+        return true;
+    }
+    if (!known_tile(bm, bn) || splits < 1 || splits > 64) return false;
+    g_plan_override.store(static_cast<uint64_t>(bm) | (static_cast<uint64_t>(bn) << 16) |
+                              (static_cast<uint64_t>(splits) << 32),
+                          std::memory_order_relaxed);
+    return true;
+}
 
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
                        hipStream_t s) {

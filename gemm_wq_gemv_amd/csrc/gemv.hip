@@ -301,7 +301,11 @@ template <int J, int LPR>
 hipError_t run_q8_staged(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
                          hipStream_t s, int cus) {
     const int row_bytes = static_cast<int>((k >> 5) * kQ8BlockBytes);
-    const int S = std::max(1, kQ8StageTarget / row_bytes);  // S * row_bytes <= kQ8StageTarget
+    // Rows per pass: as many as fit the stage (S * row_bytes <= kQ8StageTarget),
+    // but few enough that a small matrix still gives every CU about four waves
+    // (a wave decodes its S rows serially after its loads land).
+    const int s_max = std::max(1, kQ8StageTarget / row_bytes);
+    const int S = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s_max, n / (4LL * cus))));
     const int64_t passes = (n + S - 1) / S;
     const int64_t blocks = balanced_workers(passes, static_cast<int64_t>(cus) * 8);
     const size_t lds = static_cast<size_t>(S) * row_bytes + 16;  // +16: 9-dword window slack

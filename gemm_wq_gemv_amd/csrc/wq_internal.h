@@ -66,6 +66,11 @@ hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t 
                             hipStream_t s);
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,
                        int64_t k, hipStream_t s);
+// Tile shape and K-split count the GEMM picks for a problem on `cus` CUs.
+void gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits);
+// Test hook: force the GEMM tiling (bm, bn from the compiled set; splits >= 1,
+// capped at the number of k-tiles); (0, 0, 0) clears it.  False if unknown.
+bool set_gemm_plan_override(int bm, int bn, int splits);
 hipError_t launch_fill_zero(float *c, int64_t count, hipStream_t s);
 hipError_t launch_pack_f16(const float *w, uint16_t *out, int64_t count, hipStream_t s);
 hipError_t launch_quantize_q8_0(const float *w, uint8_t *out, int64_t count, hipStream_t s);

@@ -211,6 +211,19 @@ int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt) {
     return auto_route(m);
 }
 
+int wq_gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits) {
+    if (fmt != WQ_FMT_F16 && fmt != WQ_FMT_Q8_0) return WQ_ERR_FORMAT;
+    if (m <= 0 || n <= 0 || k <= 0 || cus <= 0) return WQ_ERR_SHAPE;
+    if (fmt == WQ_FMT_Q8_0 && k % 32 != 0) return WQ_ERR_K;
+    if (!bm || !bn || !splits) return WQ_ERR_NULL;
+    wq::gemm_plan(m, n, k, fmt, cus, bm, bn, splits);
+    return WQ_OK;
+}
+
+int wq_set_gemm_plan(int bm, int bn, int splits) {
+    return wq::set_gemm_plan_override(bm, bn, splits) ? WQ_OK : WQ_ERR_SHAPE;
+}
+
 int wq_set_forced_route(int route) {
     if (route != WQ_ROUTE_AUTO && route != WQ_ROUTE_GEMV && route != WQ_ROUTE_GEMM) return -WQ_ERR_ROUTE;
     return wq::g_forced_route.exchange(route);

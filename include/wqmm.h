@@ -30,7 +30,9 @@
  * Pointers: a, b, c (and w, out of the packing calls) are DEVICE pointers on
  * the current HIP device.  The caller owns all memory; the library never
  * allocates, frees or keeps caller buffers.  Buffers must stay alive until the
- * enqueued work has run.
+ * enqueued work has run.  A GEMM that splits K takes a scratch buffer of
+ * splits*M*N*4 bytes from the device's default memory pool, stream-ordered on
+ * the call's stream (hipMallocAsync / hipFreeAsync); wq_gemm_plan tells when.
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Every call only enqueues work and returns without synchronising;
@@ -66,7 +68,7 @@ typedef enum wq_status {
     WQ_ERR_K = 3,       /* Q8_0 with K == 0 or K % 32 != 0 */
     WQ_ERR_FORMAT = 4,  /* fmt is not a wq_format */
     WQ_ERR_ALIGN = 5,   /* a or c not 4-byte aligned, or b not 2-byte aligned */
-    WQ_ERR_LAUNCH = 6,  /* the HIP runtime failed to enqueue a kernel */
+    WQ_ERR_LAUNCH = 6,  /* the HIP runtime failed to enqueue a kernel or scratch */
     WQ_ERR_ALIAS = 7,   /* c overlaps a or b */
     WQ_ERR_ROUTE = 8    /* not a wq_route value */
 } wq_status;
@@ -126,6 +128,20 @@ int wq_quantize_q8_0(const float *w, uint8_t *out, int64_t count, void *stream);
 /* The route wq_matmul takes for these arguments when nothing is forced
  * (WQ_ROUTE_GEMV or WQ_ROUTE_GEMM), or a negative wq_status on bad arguments. */
 int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt);
+
+/* The tiling the GEMM uses for (m, n, k, fmt) on a device with `cus` compute
+ * units (256 on MI355X): tile rows *bm, tile columns *bn and the number of K
+ * splits *splits (1 = no split; otherwise partial tiles are summed by a
+ * second, deterministic pass).  Returns a wq_status; all dimensions must be
+ * positive. */
+int wq_gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits);
+
+/* Test and tuning hook: force every later GEMM onto tile (bm, bn) with
+ * `splits` K splits (capped at the number of 32-wide k-steps); (0, 0, 0)
+ * restores the cost model.  Tiles: 128x128, 128x96, 128x64, 64x128, 64x64,
+ * 32x128, 16x128, 16x64.  Returns WQ_ERR_SHAPE for anything else.  Results
+ * do not depend on the tiling beyond f32 rounding. */
+int wq_set_gemm_plan(int bm, int bn, int splits);
 
 /* Force every later wq_matmul call in the process onto one route
  * (WQ_ROUTE_AUTO restores the M rule).  Returns the previous setting, or

@@ -142,3 +142,40 @@ def test_product_path_does_not_touch_the_oracle():
                 assert not re.search(r"\boracle\b|wqref|wqgen", text), f
     src = open(os.path.join(ROOT, "oracle", "wqref.c")).read()
     assert "#include \"" not in src and "wqmm" not in src and "hip" not in src.lower().replace("ship", "")
+
+
+def test_gemm_planner_invariants():
+    """Every plan uses a compiled tile, no split is empty, tiny M uses 16-row
+    tiles, and the M = 512 prefill shapes get the tilings measured fastest."""
+    for m in (1, 2, 7, 16, 33, 64, 130, 512, 4096):
+        for n in (1, 97, 2048, 11008):
+            for k in (32, 1000, 2048, 11008):
+                for fmt in (wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0):
+                    if fmt == wq.WQ_FMT_Q8_0 and k % 32:
+                        continue
+                    bm, bn, sp = wq.wq_gemm_plan(m, n, k, fmt)
+                    assert (bm, bn) in wq.GEMM_TILES
+                    kt = -(-k // 32)
+                    assert 1 <= sp <= kt
+                    kts = -(-kt // sp)
+                    assert (sp - 1) * kts < kt          # the last split is not empty
+                    if m <= 16:
+                        assert bm == 16
+    assert wq.wq_gemm_plan(512, 6144, 2048, wq.WQ_FMT_F16) == (64, 64, 1)
+    assert wq.wq_gemm_plan(512, 4096, 11008, wq.WQ_FMT_Q8_0) == (128, 128, 4)
+    assert wq.wq_gemm_plan(16, 11008, 4096, wq.WQ_FMT_Q8_0) == (16, 128, 8)
+
+
+def test_gemm_plan_override_hook():
+    try:
+        wq.wq_set_gemm_plan(32, 128, 3)
+        assert wq.wq_gemm_plan(512, 6144, 2048, wq.WQ_FMT_F16) == (32, 128, 3)
+        assert wq.wq_gemm_plan(5, 10, 64, wq.WQ_FMT_F16) == (32, 128, 2)   # capped at 2 k-steps
+        with pytest.raises(wq.WQError):
+            wq.wq_set_gemm_plan(48, 64, 1)
+        with pytest.raises(wq.WQError):
+            wq.wq_set_gemm_plan(64, 64, 0)
+    finally:
+        wq.wq_set_gemm_plan(0, 0, 0)
+    assert wq.wq_gemm_plan(512, 6144, 2048, wq.WQ_FMT_F16) == (64, 64, 1)
+    assert L.wq_gemm_plan(0, 1, 1, 0, 256, None, None, None) == wq.WQ_ERR_SHAPE

@@ -365,3 +365,28 @@ def test_nondefault_stream():
         c = run_gpu("matmul", F16, a, dev_b, m, n, k, stream=s)
         c_ref, bound = oracle.matmul(a, ref_b, F16, m, n, k)
         assert_close(c, c_ref, bound, f"stream m={m}")
+
+
+PLAN_CASES = [(F16, 37, 300, 640), (Q8, 37, 300, 640), (F16, 130, 97, 1000), (F16, 5, 77, 1003),
+              (Q8, 300, 129, 2080)]
+
+
+@pytest.mark.parametrize("case", PLAN_CASES, ids=[f"fmt{f}-{m}x{n}x{k}" for f, m, n, k in PLAN_CASES])
+def test_every_gemm_tiling_and_split(case):
+    """Every compiled tile shape with 1, 2, 3 and 5 K splits (forced through the
+    plan hook) matches the oracle, including the K tail (K % 32 != 0) and the
+    unaligned-K general path."""
+    fmt, m, n, k = case
+    ref_b, dev_b = encoded(n, k, fmt, 9)
+    a = acts(m, k, 9)
+    c_ref, bound = oracle.matmul(a, ref_b, fmt, m, n, k)
+    try:
+        for bm, bn in wq.GEMM_TILES:
+            for sp in (1, 2, 3, 5):
+                say(f"plan {bm}x{bn}/{sp} fmt={fmt} {m}x{n}x{k}")
+                wq.wq_set_gemm_plan(bm, bn, sp)
+                assert wq.wq_gemm_plan(m, n, k, fmt)[:2] == (bm, bn)
+                c = run_gpu("gemm", fmt, a, dev_b, m, n, k)
+                assert_close(c, c_ref, bound, f"plan {bm}x{bn}/{sp}")
+    finally:
+        wq.wq_set_gemm_plan(0, 0, 0)

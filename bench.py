@@ -41,6 +41,36 @@ SWEEP_SHAPES = [(11008, 4096), (4096, 11008)]
 SWEEP_M = [1, 2, 4, 8, 16, 64, 512]
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_f16_lm_head_151936x2048.md")
+GEMV_SOURCES = [os.path.join(ROOT, "gemm_wq_gemv_amd", "csrc", f) for f in ("gemv.hip", "wq_internal.h")]
+
+
+def gemv_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for path in GEMV_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per LM-head launch from the committed rocprofv3 PMC summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), if it was taken on the current
+    kernel sources; otherwise None."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
+    if fields.get("source_sha256", "").strip() != gemv_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -214,7 +244,7 @@ def main():
                 "peak": HBM_PEAK_GBS,
                 "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None,
+                "traffic": recorded_traffic(),
                 "avg_launch_us": round(lm_s * 1e6, 3),
                 "algorithmic_bytes_per_launch": lm_bytes,
             },

@@ -307,6 +307,7 @@ hipError_t run_q8_staged(const float *a, const uint8_t *b, float *c, int64_t n, 
     const int s_max = std::max(1, kQ8StageTarget / row_bytes);
     const int S = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s_max, n / (4LL * cus))));
     const int64_t passes = (n + S - 1) / S;
+    // 8 waves per CU: the LDS stages of 9 fill the CU; measured best on MI355X.
     const int64_t blocks = balanced_workers(passes, static_cast<int64_t>(cus) * 8);
     const size_t lds = static_cast<size_t>(S) * row_bytes + 16;  // +16: 9-dword window slack
     if (trace_enabled())

@@ -17,9 +17,12 @@
 //  * Q8_0: a 34-byte block is only 2-byte aligned, so the wave first copies S
 //    whole rows (a contiguous, 16-byte aligned byte range when K % 256 == 0)
 //    into its LDS slice with coalesced 128-bit loads, then each lane decodes
-//    whole blocks from LDS (scale, 32 int8 codes) against its register slice of
-//    `a`: sum_q = sum_i q_i a_i, acc += d * sum_q, as the pages apply d after
-//    the block's int8 dot product.
+//    whole blocks from LDS (scale, 32 int8 codes, read with unaligned 16-byte
+//    LDS loads) against its register slice of `a`: sum_q = sum_i q_i a_i,
+//    acc += d * sum_q, as the pages apply d after the block's int8 dot
+//    product.  The decode of a pass is branch-free so the rows' dependency
+//    chains overlap, and the rows of a pass are reduced together by one
+//    butterfly (each cross-lane step halves the values a lane carries).
 //  * Reductions: DPP within 16-lane rows, lane-xor across rows (64 lanes).
 //  * Persistent waves: the grid is sized to fill the chip once and every wave
 //    walks row groups with a stride, balanced so all waves do equal work.
@@ -125,45 +128,47 @@ __global__ __launch_bounds__(256) void gemv_f16_any(const float *__restrict__ a,
 constexpr int kQ8BlockBytes = 34;
 constexpr int kQ8Chunks = 17;                // 16-byte chunks per lane per pass
 constexpr int kQ8StageTarget = kQ8Chunks * 64 * 16;  // 17408 bytes: 8 rows at K = 2048
-constexpr int kQ8MaxRowsPerPass = kQ8StageTarget / (8 * kQ8BlockBytes);  // 64 rows at K = 256
 
 // Dot product of one Q8_0 block held in LDS at byte offset pb with the 32
-// activations av[0..31]: returns d * sum_i q_i * av[i].
+// activations av[0..31]: returns d * sum_i q_i * av[i].  The codes are read as
+// two 16-byte LDS loads at block bytes 2 and 18, which are only 2-byte aligned
+// for half of the blocks; gfx950 LDS accepts such unaligned reads.
 __device__ __forceinline__ float q8_block_dot(const uint8_t *stage, int pb, const float *av) {
-    const int qa = pb + 2;          // first code byte
-    const int sh = qa & 3;          // 0 or 2: codes start mid-dword for half the blocks
-    const uint32_t *s32 = reinterpret_cast<const uint32_t *>(stage + (qa - sh));
-    uint32_t wd[9];
-#pragma unroll
-    for (int i = 0; i < 9; ++i) wd[i] = s32[i];
     const uint32_t hb = *reinterpret_cast<const uint16_t *>(stage + pb);
-    float sumq = 0.f;
+    u32x4 q0, q1;
+    __builtin_memcpy(&q0, __builtin_assume_aligned(stage + pb + 2, 2), 16);
+    __builtin_memcpy(&q1, __builtin_assume_aligned(stage + pb + 18, 2), 16);
+    const uint32_t wd[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    // Four independent partial sums (one per byte lane) keep four FMA chains
+    // in flight instead of one 32-long dependent chain.
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const uint32_t q = __builtin_amdgcn_alignbyte(wd[i + 1], wd[i], sh);
-        sumq = fmaf(static_cast<float>(static_cast<int8_t>(q & 0xffu)), av[4 * i + 0], sumq);
-        sumq = fmaf(static_cast<float>(static_cast<int8_t>((q >> 8) & 0xffu)), av[4 * i + 1], sumq);
-        sumq = fmaf(static_cast<float>(static_cast<int8_t>((q >> 16) & 0xffu)), av[4 * i + 2], sumq);
-        sumq = fmaf(static_cast<float>(static_cast<int8_t>(q >> 24)), av[4 * i + 3], sumq);
+        const uint32_t q = wd[i];
+        part[0] = fmaf(static_cast<float>(static_cast<int8_t>(q & 0xffu)), av[4 * i + 0], part[0]);
+        part[1] = fmaf(static_cast<float>(static_cast<int8_t>((q >> 8) & 0xffu)), av[4 * i + 1], part[1]);
+        part[2] = fmaf(static_cast<float>(static_cast<int8_t>((q >> 16) & 0xffu)), av[4 * i + 2], part[2]);
+        part[3] = fmaf(static_cast<float>(static_cast<int8_t>(q >> 24)), av[4 * i + 3], part[3]);
     }
-    return half_bits_to_float(hb) * sumq;
+    return half_bits_to_float(hb) * ((part[0] + part[1]) + (part[2] + part[3]));
 }
 
 // One wave per workgroup.  LPR lanes share a row; lane l covers blocks
 // j = l % LPR + LPR * t (t < J) of that row and keeps a[32 j .. 32 j + 32) in
-// VGPRs.  Each pass covers S consecutive rows, i.e. S * row_bytes contiguous
-// bytes (at most kQ8Chunks * 64 16-byte chunks).  The chunks of the next pass
-// are loaded into registers (kQ8Chunks independent 128-bit loads per lane, all
-// in flight together) while the current pass is decoded from LDS; they are
-// written to LDS at the top of the next iteration.
+// VGPRs.  A pass covers S = SL * (64 / LPR) consecutive rows, i.e. S * row_bytes
+// contiguous bytes (at most kQ8Chunks * 64 16-byte chunks).  The next pass is
+// in flight in registers (kQ8Chunks independent 128-bit loads per lane) while
+// the current pass, already copied to LDS, is decoded; the SL rows a lane
+// group decodes are unrolled so their LDS reads and reductions interleave.
 // Requires K % 256 == 0 (rows are whole 16-byte chunks), 16-byte aligned a, b.
-template <int J, int LPR>
+template <int J, int LPR, int SL>
 __global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a,
                                                      const uint8_t *__restrict__ b,
                                                      float *__restrict__ c, int64_t n, int64_t k,
-                                                     int S, int64_t passes) {
+                                                     int64_t passes) {
     extern __shared__ uint4 stage4[];
     constexpr int RPL = kWave / LPR;
+    constexpr int S = SL * RPL;
     const int lane = threadIdx.x;
     const int nb = static_cast<int>(k >> 5);
     const int row_bytes = nb * kQ8BlockBytes;
@@ -184,26 +189,22 @@ __global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a
             av[t][4 * i + 3] = v.w;
         }
     }
-
     wait_vmem_all();
 
-    // Chunks of pass p: bytes [p*S*row_bytes, ...) for min(S, n - p*S) rows.
-    auto pass_chunks = [&](int64_t p) -> int {
-        return static_cast<int>(min<int64_t>(S, n - p * S)) * row_bytes / 16;
-    };
+    // Staging guards are wave-uniform: a whole 1 KiB load (or LDS write) is
+    // skipped when the pass ends before it; inside the last one, lanes past
+    // the end re-read the pass's last chunk (in bounds) and write it to LDS
+    // slots nobody reads.  No per-lane exec masking in the streaming loop.
     uint4 next[kQ8Chunks];
     auto fetch = [&](int64_t p) {
-        const int nch = pass_chunks(p);
+        const int nch = static_cast<int>(min<int64_t>(S, n - p * S)) * row_bytes / 16;
         const uint4 *src = reinterpret_cast<const uint4 *>(b + p * S * row_bytes);
 #pragma unroll
-        for (int u = 0; u < kQ8Chunks; ++u) {
-            const int ci = u * kWave + lane;
-            if (ci < nch) next[u] = load_nt16(src + ci);
-        }
+        for (int u = 0; u < kQ8Chunks; ++u)
+            if (u * kWave < nch) next[u] = load_nt16(src + min(u * kWave + lane, nch - 1));
     };
 
     const uint8_t *stage = reinterpret_cast<const uint8_t *>(stage4);
-    __shared__ float result[kQ8MaxRowsPerPass];
     int64_t p = blockIdx.x;
     if (p < passes) fetch(p);
     for (; p < passes; p += gridDim.x) {
@@ -212,29 +213,34 @@ __global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a
         const int nch = rows * row_bytes / 16;
         __syncthreads();  // the previous pass is fully read from LDS
 #pragma unroll
-        for (int u = 0; u < kQ8Chunks; ++u) {
-            const int ci = u * kWave + lane;
-            if (ci < nch) stage4[ci] = next[u];
-        }
+        for (int u = 0; u < kQ8Chunks; ++u)
+            if (u * kWave < nch) stage4[u * kWave + lane] = next[u];
         __syncthreads();
         if (p + gridDim.x < passes) fetch(p + gridDim.x);  // in flight during the decode below
-        // The decode loop has no global memory access, so nothing in it waits
-        // for the prefetch; row results go to LDS and leave in one store.
-        for (int sb = 0; sb < rows; sb += RPL) {
-            const int s = sb + rsub;
-            float acc = 0.f;
-            if (s < rows) {
+        // Branch-free decode: every (row, slot) reads an in-bounds block of the
+        // stage (rows past `rows` hold stale bytes, slots past the row end use
+        // the row's last block) and the result is masked, so all SL * J block
+        // dot products sit in one basic block and their latencies overlap.
+        float acc[SL];
 #pragma unroll
-                for (int t = 0; t < J; ++t) {
-                    const int j = jl + LPR * t;
-                    if (j < nb) acc += q8_block_dot(stage, s * row_bytes + kQ8BlockBytes * j, av[t]);
-                }
+        for (int sl = 0; sl < SL; ++sl) {
+            const int srow = sl * RPL + rsub;
+            acc[sl] = 0.f;
+#pragma unroll
+            for (int t = 0; t < J; ++t) {
+                const int j = jl + LPR * t;
+                const float d = q8_block_dot(stage, srow * row_bytes + kQ8BlockBytes * min(j, nb - 1), av[t]);
+                acc[sl] += (j < nb) ? d : 0.f;
             }
-            acc = group_sum<LPR>(acc);
-            if (jl == 0 && s < rows) result[s] = acc;
+            if (srow >= rows) acc[sl] = 0.f;
         }
-        __syncthreads();
-        if (lane < rows) c[row0 + lane] = result[lane];
+        // One butterfly reduction for all SL rows of the lane group; lane
+        // jl then holds the sum of row sl = jl / (LPR / SL), stored by the
+        // first lane of each run: one store instruction for the pass.
+        const float sum = rows_sum<SL, LPR>(acc, jl);
+        const int sl_mine = jl / (LPR / SL);
+        const int srow_mine = sl_mine * RPL + rsub;
+        if (jl % (LPR / SL) == 0 && srow_mine < rows) c[row0 + srow_mine] = sum;
     }
 }
 
@@ -297,24 +303,40 @@ hipError_t run_f16_vec(const float *a, const uint16_t *b, float *c, int64_t n, i
     return hipGetLastError();
 }
 
-template <int J, int LPR>
-hipError_t run_q8_staged(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
-                         hipStream_t s, int cus) {
+template <int J, int LPR, int SL>
+hipError_t run_q8_staged_sl(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
+                            int cus) {
+    constexpr int S = SL * (kWave / LPR);
     const int row_bytes = static_cast<int>((k >> 5) * kQ8BlockBytes);
-    // Rows per pass: as many as fit the stage (S * row_bytes <= kQ8StageTarget),
-    // but few enough that a small matrix still gives every CU about four waves
-    // (a wave decodes its S rows serially after its loads land).
-    const int s_max = std::max(1, kQ8StageTarget / row_bytes);
-    const int S = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(s_max, n / (4LL * cus))));
     const int64_t passes = (n + S - 1) / S;
-    // 8 waves per CU: the LDS stages of 9 fill the CU; measured best on MI355X.
+    // 8 waves per CU (LDS stages of 9 fill a CU): measured best on MI355X.
     const int64_t blocks = balanced_workers(passes, static_cast<int64_t>(cus) * 8);
-    const size_t lds = static_cast<size_t>(S) * row_bytes + 16;  // +16: 9-dword window slack
+    const size_t lds = (static_cast<size_t>(S) * row_bytes + 1023) / 1024 * 1024;  // whole 1 KiB writes
     if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_q8_staged<J=%d,LPR=%d> n=%lld k=%lld S=%d grid=%lld block=64 lds=%zu\n", J,
-                LPR, (long long)n, (long long)k, S, (long long)blocks, lds);
-    hipLaunchKernelGGL((gemv_q8_staged<J, LPR>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k, S, passes);
+        fprintf(stderr, "[wqmm] gemv_q8_staged<J=%d,LPR=%d,SL=%d> n=%lld k=%lld S=%d grid=%lld block=64 lds=%zu\n",
+                J, LPR, SL, (long long)n, (long long)k, S, (long long)blocks, lds);
+    hipLaunchKernelGGL((gemv_q8_staged<J, LPR, SL>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k, passes);
     return hipGetLastError();
+}
+
+// Rows per pass: as many as fit the stage (S * row_bytes <= kQ8StageTarget),
+// but few enough that a small matrix still gives every CU about four waves
+// (a wave decodes its rows after its loads land); SL is a power of two.
+template <int J, int LPR>
+hipError_t run_q8_staged(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
+                         int cus) {
+    constexpr int RPL = kWave / LPR;
+    const int row_bytes = static_cast<int>((k >> 5) * kQ8BlockBytes);
+    const int64_t s_fit = kQ8StageTarget / row_bytes;
+    const int64_t s_fill = std::max<int64_t>(1, n / (4LL * cus));
+    const int64_t sl_max = std::max<int64_t>(1, std::min(s_fit, s_fill) / RPL);
+    if constexpr (J <= 1)
+        if (sl_max >= 8 && 8 * RPL <= s_fit) return run_q8_staged_sl<J, LPR, 8>(a, b, c, n, k, s, cus);
+    if constexpr (J <= 2)
+        if (sl_max >= 4 && 4 * RPL <= s_fit) return run_q8_staged_sl<J, LPR, 4>(a, b, c, n, k, s, cus);
+    if constexpr (J <= 4)
+        if (sl_max >= 2 && 2 * RPL <= s_fit) return run_q8_staged_sl<J, LPR, 2>(a, b, c, n, k, s, cus);
+    return run_q8_staged_sl<J, LPR, 1>(a, b, c, n, k, s, cus);
 }
 
 }  // namespace
@@ -352,7 +374,7 @@ hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t 
     if (e != hipSuccess) return e;
     const int64_t nb = k / 32;
     const int64_t row_bytes = nb * kQ8BlockBytes;
-    if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= kQ8StageTarget) {
+    if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= kQ8StageTarget) {  // 17 chunks per lane
         if (nb >= 64) {
             const int64_t J = (nb + 63) / 64;
             switch (J) {

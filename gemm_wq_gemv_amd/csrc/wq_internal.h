@@ -34,19 +34,55 @@ __device__ __forceinline__ float dpp_f32(float v) {
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 
-// Sum over aligned groups of G lanes (G in {16, 32, 64}); every lane of a group
-// receives the group's sum.  Within a 16-lane DPP row: quad_perm [1,0,3,2],
-// quad_perm [2,3,0,1], row_half_mirror, row_mirror; across rows: lane xor.
+// Sum over aligned groups of G lanes (G a power of two up to 64); every lane
+// of a group receives the group's sum.  Within a 16-lane DPP row:
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror;
+// across rows: lane xor 16 and 32.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-    static_assert(G == 16 || G == 32 || G == 64, "group size");
-    v += dpp_f32<0xb1>(v);
-    v += dpp_f32<0x4e>(v);
-    v += dpp_f32<0x141>(v);
-    v += dpp_f32<0x140>(v);
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "group size");
+    if constexpr (G >= 2) v += dpp_f32<0xb1>(v);
+    if constexpr (G >= 4) v += dpp_f32<0x4e>(v);
+    if constexpr (G >= 8) v += dpp_f32<0x141>(v);
+    if constexpr (G >= 16) v += dpp_f32<0x140>(v);
     if constexpr (G >= 32) v += __shfl_xor(v, 16, kWave);
     if constexpr (G >= 64) v += __shfl_xor(v, 32, kWave);
     return v;
+}
+
+// The value of a partner lane that differs from this one in bit log2(H) and is
+// a perfect matching of the lanes with that bit clear to those with it set
+// (lane xor H for H >= 8; the DPP mirrors pair lanes inside a row).
+template <int H>
+__device__ __forceinline__ float bit_partner(float v) {
+    if constexpr (H == 32 || H == 16) return __shfl_xor(v, H, kWave);
+    else if constexpr (H == 8) return dpp_f32<0x128>(v);  // row_ror:8
+    else if constexpr (H == 4) return dpp_f32<0x141>(v);  // row_half_mirror
+    else if constexpr (H == 2) return dpp_f32<0x4e>(v);
+    else return dpp_f32<0xb1>(v);
+}
+
+// N row sums per lane, reduced over aligned groups of G lanes (N <= G, both
+// powers of two).  Each butterfly step pairs lanes across the group's top
+// bit; the lane with the bit set keeps the upper half of the rows, adds its
+// partner's copy of them, and the number of values halves.  Afterwards lane
+// g of a group (g = lane % G) holds the complete sum of row g / (G / N).
+template <int N, int G>
+__device__ __forceinline__ float rows_sum(const float (&v)[N], int g) {
+    if constexpr (N == 1) {
+        return group_sum<G>(v[0]);
+    } else {
+        constexpr int H = G / 2;
+        const bool hi = (g & H) != 0;
+        float w[N / 2];
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const float send = hi ? v[i] : v[N / 2 + i];
+            const float keep = hi ? v[N / 2 + i] : v[i];
+            w[i] = keep + bit_partner<H>(send);
+        }
+        return rows_sum<N / 2, H>(w, g);
+    }
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }

@@ -39,6 +39,7 @@ DECODE = [("gate_up", 6144, 2048), ("down", 2048, 6144), ("o_proj", 2048, 2048),
 PREFILL = [(512, 6144, 2048), (512, 2048, 6144)]
 SWEEP_SHAPES = [(11008, 4096), (4096, 11008)]
 SWEEP_M = [1, 2, 4, 8, 16, 64, 512]
+ROUTE_NAMES = {1: "gemv", 2: "gemm", 3: "small_m"}
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_f16_lm_head_151936x2048.md")
@@ -308,8 +309,7 @@ def main():
                                   max(10, args.steps // 2), args.warmup)
                 out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(nbytes / t / 1e9, 1),
                                        "TFLOP/s": round(2.0 * m * n * k / t / 1e12, 2),
-                                       "route": "gemv" if wq.wq_route_for(m, n, k, Q8) == wq.WQ_ROUTE_GEMV
-                                       else "gemm"}
+                                       "route": ROUTE_NAMES[wq.wq_route_for(m, n, k, Q8)]}
             del bs, b0
             torch.cuda.empty_cache()
         secondary["q8_sweep"] = out

@@ -37,6 +37,7 @@ WQ_ERR_ROUTE = 8
 WQ_ROUTE_AUTO = 0
 WQ_ROUTE_GEMV = 1
 WQ_ROUTE_GEMM = 2
+WQ_ROUTE_SKINNY = 3
 
 Q8_0_BLOCK_BYTES = 34
 Q8_0_BLOCK_WEIGHTS = 32
@@ -88,17 +89,24 @@ def _ptr(t):
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError("expected a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("tensor must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return t.data_ptr() or None
 
 
-def _stream(stream):
+_raw_stream = torch._C._cuda_getCurrentRawStream
+
+
+def _stream(stream, like=None):
+    """hipStream_t for `stream` (a torch.cuda.Stream or a raw handle); None is
+    torch's current stream on the device of tensor `like` (else the current
+    device)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream))
+        dev = like.get_device() if like is not None and like.is_cuda else torch.cuda.current_device()
+        return _raw_stream(dev)
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)
 
 
 def _need(t, nbytes: int, what: str):
@@ -142,28 +150,28 @@ def _sizes(a, b, c, m, n, k, fmt):
 # ------------------------------------------------------------ entry points --
 def wq_gemv_f16(a, b, c, n: int, k: int, stream=None) -> None:
     _sizes(a, b, c, 1, n, k, WQ_FMT_F16)
-    _check(_lib.wq_gemv_f16(_ptr(a), _ptr(b), _ptr(c), n, k, _stream(stream)), "wq_gemv_f16")
+    _check(_lib.wq_gemv_f16(_ptr(a), _ptr(b), _ptr(c), n, k, _stream(stream, c)), "wq_gemv_f16")
 
 
 def wq_gemv_q8_0(a, b, c, n: int, k: int, stream=None) -> None:
     _sizes(a, b, c, 1, n, k, WQ_FMT_Q8_0)
-    _check(_lib.wq_gemv_q8_0(_ptr(a), _ptr(b), _ptr(c), n, k, _stream(stream)), "wq_gemv_q8_0")
+    _check(_lib.wq_gemv_q8_0(_ptr(a), _ptr(b), _ptr(c), n, k, _stream(stream, c)), "wq_gemv_q8_0")
 
 
 def wq_gemm_f16(a, b, c, m: int, n: int, k: int, stream=None) -> None:
     _sizes(a, b, c, m, n, k, WQ_FMT_F16)
-    _check(_lib.wq_gemm_f16(_ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(stream)), "wq_gemm_f16")
+    _check(_lib.wq_gemm_f16(_ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(stream, c)), "wq_gemm_f16")
 
 
 def wq_gemm_q8_0(a, b, c, m: int, n: int, k: int, stream=None) -> None:
     _sizes(a, b, c, m, n, k, WQ_FMT_Q8_0)
-    _check(_lib.wq_gemm_q8_0(_ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(stream)), "wq_gemm_q8_0")
+    _check(_lib.wq_gemm_q8_0(_ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(stream, c)), "wq_gemm_q8_0")
 
 
 def wq_matmul(a, b, c, m: int, n: int, k: int, fmt: int, stream=None) -> None:
     if fmt in (WQ_FMT_F16, WQ_FMT_Q8_0):
         _sizes(a, b, c, m, n, k, fmt)
-    _check(_lib.wq_matmul(_ptr(a), _ptr(b), _ptr(c), m, n, k, fmt, _stream(stream)), "wq_matmul")
+    _check(_lib.wq_matmul(_ptr(a), _ptr(b), _ptr(c), m, n, k, fmt, _stream(stream, c)), "wq_matmul")
 
 
 def wq_pack_f16(w, out, count: int, stream=None) -> None:
@@ -172,7 +180,7 @@ def wq_pack_f16(w, out, count: int, stream=None) -> None:
         _dtype(out, _H, "out")
         _need(w, 4 * count, "w")
         _need(out, 2 * count, "out")
-    _check(_lib.wq_pack_f16(_ptr(w), _ptr(out), count, _stream(stream)), "wq_pack_f16")
+    _check(_lib.wq_pack_f16(_ptr(w), _ptr(out), count, _stream(stream, out)), "wq_pack_f16")
 
 
 def wq_quantize_q8_0(w, out, count: int, stream=None) -> None:
@@ -181,7 +189,7 @@ def wq_quantize_q8_0(w, out, count: int, stream=None) -> None:
         _dtype(out, _U8, "out")
         _need(w, 4 * count, "w")
         _need(out, count // 32 * Q8_0_BLOCK_BYTES, "out")
-    _check(_lib.wq_quantize_q8_0(_ptr(w), _ptr(out), count, _stream(stream)), "wq_quantize_q8_0")
+    _check(_lib.wq_quantize_q8_0(_ptr(w), _ptr(out), count, _stream(stream, out)), "wq_quantize_q8_0")
 
 
 def wq_route_for(m: int, n: int, k: int, fmt: int) -> int:

@@ -441,24 +441,27 @@ hipError_t dispatch(const float *a, const void *b, float *c, int64_t m, int64_t 
                     hipStream_t s, int cus) {
     Plan p = planned(m, n, k, FMT, cus);
     if (p.splits == 1) return dispatch_tile<FMT>(p, a, b, c, m, n, k, vec, s);
-    // Split K: partial tiles go to a stream-ordered scratch buffer from the
-    // device's default memory pool, then one pass sums them in split order.
-    float *partial = nullptr;
+    // Split K: partial tiles go to the device's scratch buffer, then one pass
+    // sums them in split order.
+    ScratchLease lease;
+    void *scratch = nullptr;
     const size_t bytes = static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(n) * 4;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&partial), bytes, s);
+    hipError_t e = lease.acquire(bytes, s, &scratch);
     if (e != hipSuccess) return e;
+    float *partial = static_cast<float *>(scratch);
     e = dispatch_tile<FMT>(p, a, b, partial, m, n, k, vec, s);
-    if (e == hipSuccess) {
-        const int64_t count = m * n;
-        const int64_t grid = std::min<int64_t>((count + 255) / 256, 65536);
-        hipLaunchKernelGGL(reduce_splits, dim3(grid), dim3(256), 0, s, partial, c, count, p.splits);
-        e = hipGetLastError();
-    }
-    const hipError_t ef = hipFreeAsync(partial, s);
-    return e != hipSuccess ? e : ef;
+    if (e == hipSuccess) e = launch_reduce_splits(partial, c, m * n, p.splits, s);
+    const hipError_t er = lease.release();
+    return e != hipSuccess ? e : er;
 }
 
 }  // namespace
+
+hipError_t launch_reduce_splits(const float *partial, float *c, int64_t count, int splits, hipStream_t s) {
+    const int64_t grid = std::min<int64_t>((count + 255) / 256, 65536);
+    hipLaunchKernelGGL(reduce_splits, dim3(grid), dim3(256), 0, s, partial, c, count, splits);
+    return hipGetLastError();
+}
 
 void gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits) {
     const Plan p = planned(m, n, k, fmt, cus);

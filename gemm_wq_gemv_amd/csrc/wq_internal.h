@@ -102,6 +102,11 @@ hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t 
                             hipStream_t s);
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,
                        int64_t k, hipStream_t s);
+// Small-M weight-streaming product (M <= 16 rows of A per launch).
+hipError_t launch_skinny(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
+                         hipStream_t s);
+// C[i] = sum of partial[s * count + i] over s < splits, in split order.
+hipError_t launch_reduce_splits(const float *partial, float *c, int64_t count, int splits, hipStream_t s);
 // Tile shape and K-split count the GEMM picks for a problem on `cus` CUs.
 void gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits);
 // Test hook: force the GEMM tiling (bm, bn from the compiled set; splits >= 1,
@@ -110,6 +115,31 @@ bool set_gemm_plan_override(int bm, int bn, int splits);
 hipError_t launch_fill_zero(float *c, int64_t count, hipStream_t s);
 hipError_t launch_pack_f16(const float *w, uint16_t *out, int64_t count, hipStream_t s);
 hipError_t launch_quantize_q8_0(const float *w, uint8_t *out, int64_t count, hipStream_t s);
+
+// Split-K scratch.  One buffer per device, grown on demand from the device's
+// default memory pool (stream-ordered) and kept for reuse; a lease holds the
+// device's lock from acquire() until the kernels that use the buffer are
+// enqueued, then records an event on the stream, and the next lease waits on
+// that event from its own stream, so uses on different streams never overlap.
+// Requests above kScratchCacheBytes take a private stream-ordered allocation.
+constexpr size_t kScratchCacheBytes = size_t(256) << 20;
+class ScratchLease {
+  public:
+    ScratchLease() = default;
+    ScratchLease(const ScratchLease &) = delete;
+    ScratchLease &operator=(const ScratchLease &) = delete;
+    ~ScratchLease();
+    // Gives *ptr with at least `bytes` bytes usable by work enqueued on `s`.
+    hipError_t acquire(size_t bytes, hipStream_t s, void **ptr);
+    // After the last kernel using the buffer is enqueued on `s`.
+    hipError_t release();
+
+  private:
+    int dev_ = -1;
+    hipStream_t s_ = nullptr;
+    void *priv_ = nullptr;  // private allocation (large requests)
+    bool held_ = false;     // device lock held
+};
 
 // Set by WQ_TRACE=1: one line per launch on stderr.
 bool trace_enabled();

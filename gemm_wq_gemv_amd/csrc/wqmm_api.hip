@@ -18,7 +18,7 @@ DeviceInfo g_dev[kMaxDevices];
 hipError_t g_dev_err[kMaxDevices];
 
 std::atomic<int> g_forced_route{WQ_ROUTE_AUTO};
-std::atomic<uint64_t> g_route_count[3];
+std::atomic<uint64_t> g_route_count[4];
 
 int trace_flag() {
     static const int v = [] {
@@ -44,6 +44,87 @@ hipError_t device_info(DeviceInfo *out) {
     *out = g_dev[dev];
     return g_dev_err[dev];
 }
+
+namespace {
+struct DevScratch {
+    std::mutex mu;
+    void *ptr = nullptr;
+    size_t bytes = 0;
+    hipEvent_t done = nullptr;  // recorded after the last use
+    bool used = false;
+};
+DevScratch g_scratch[kMaxDevices];
+}  // namespace
+
+hipError_t ScratchLease::acquire(size_t bytes, hipStream_t s, void **ptr) {
+    *ptr = nullptr;
+    s_ = s;
+    hipError_t e = hipGetDevice(&dev_);
+    if (e != hipSuccess) return e;
+    if (dev_ < 0 || dev_ >= kMaxDevices) return hipErrorInvalidDevice;
+    if (bytes > kScratchCacheBytes) {
+        e = hipMallocAsync(&priv_, bytes, s);
+        if (e == hipSuccess) *ptr = priv_;
+        return e;
+    }
+    DevScratch &d = g_scratch[dev_];
+    d.mu.lock();
+    held_ = true;
+    if (!d.done) {
+        e = hipEventCreateWithFlags(&d.done, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            d.done = nullptr;
+            return e;
+        }
+    }
+    // Order this use after the previous one, whichever stream it was on.
+    if (d.used) {
+        e = hipStreamWaitEvent(s, d.done, 0);
+        if (e != hipSuccess) return e;
+    }
+    if (bytes > d.bytes) {
+        // Grow (at least double): free the old buffer and allocate the new one
+        // on this stream, both ordered after the wait above.
+        size_t want = d.bytes * 2 > bytes ? d.bytes * 2 : bytes;
+        if (want > kScratchCacheBytes) want = kScratchCacheBytes;
+        want = (want + 4095) & ~size_t(4095);
+        if (d.ptr) {
+            e = hipFreeAsync(d.ptr, s);
+            d.ptr = nullptr;
+            d.bytes = 0;
+            if (e != hipSuccess) return e;
+        }
+        e = hipMallocAsync(&d.ptr, want, s);
+        if (e != hipSuccess) {
+            d.ptr = nullptr;
+            return e;
+        }
+        d.bytes = want;
+    }
+    *ptr = d.ptr;
+    return hipSuccess;
+}
+
+hipError_t ScratchLease::release() {
+    hipError_t e = hipSuccess;
+    if (priv_) {
+        e = hipFreeAsync(priv_, s_);
+        priv_ = nullptr;
+    }
+    if (held_) {
+        DevScratch &d = g_scratch[dev_];
+        if (d.done) {
+            const hipError_t er = hipEventRecord(d.done, s_);
+            d.used = er == hipSuccess;
+            if (e == hipSuccess) e = er;
+        }
+        held_ = false;
+        d.mu.unlock();
+    }
+    return e;
+}
+
+ScratchLease::~ScratchLease() { (void)release(); }
 
 }  // namespace wq
 
@@ -90,7 +171,15 @@ int validate(const float *a, const void *b, const float *c, int64_t m, int64_t n
 
 int status_of(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_LAUNCH; }
 
-int auto_route(int64_t m) { return m == 1 ? WQ_ROUTE_GEMV : WQ_ROUTE_GEMM; }
+// M == 1: the decode GEMV; 2 <= M <= 8 (f16) or 4 (Q8_0): the weight-streaming
+// small-M kernel, which is faster than the tiled GEMM there (measured on
+// MI355X at N, K in {4096, 11008}); larger M: the LDS-tiled GEMM.
+constexpr int64_t kSkinnyRows = 16;  // rows of A per small-M launch
+int auto_route(int64_t m, int fmt) {
+    if (m <= 1) return WQ_ROUTE_GEMV;
+    return m <= (fmt == WQ_FMT_F16 ? 8 : 4) ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;
+}
+bool known_route(int r) { return r == WQ_ROUTE_GEMV || r == WQ_ROUTE_GEMM || r == WQ_ROUTE_SKINNY; }
 
 int run_gemv(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s) {
     // One GEMV launch per row of A (the route for M == 1; forced otherwise).
@@ -110,6 +199,17 @@ int run_gemm(const float *a, const void *b, float *c, int64_t m, int64_t n, int6
     hipError_t e = wq::launch_gemm(a, b, fmt, c, m, n, k, s);
     if (e != hipSuccess) return WQ_ERR_LAUNCH;
     wq::g_route_count[WQ_ROUTE_GEMM].fetch_add(1, std::memory_order_relaxed);
+    return WQ_OK;
+}
+
+// One small-M launch per block of up to kSkinnyRows rows of A.
+int run_skinny(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s) {
+    for (int64_t i = 0; i < m; i += kSkinnyRows) {
+        const int64_t rows = m - i < kSkinnyRows ? m - i : kSkinnyRows;
+        hipError_t e = wq::launch_skinny(a + i * k, b, fmt, c + i * n, rows, n, k, s);
+        if (e != hipSuccess) return WQ_ERR_LAUNCH;
+        wq::g_route_count[WQ_ROUTE_SKINNY].fetch_add(1, std::memory_order_relaxed);
+    }
     return WQ_OK;
 }
 
@@ -178,8 +278,9 @@ int wq_matmul(const float *a, const void *b, float *c, int64_t m, int64_t n, int
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (k == 0) return run_zero(c, m, n, s);
     int route = wq::g_forced_route.load(std::memory_order_relaxed);
-    if (route == WQ_ROUTE_AUTO) route = auto_route(m);
+    if (route == WQ_ROUTE_AUTO) route = auto_route(m, fmt);
     if (route == WQ_ROUTE_GEMV) return run_gemv(a, b, c, m, n, k, fmt, s);
+    if (route == WQ_ROUTE_SKINNY) return run_skinny(a, b, c, m, n, k, fmt, s);
     return run_gemm(a, b, c, m, n, k, fmt, s);
 }
 
@@ -208,7 +309,7 @@ int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt) {
     if (fmt != WQ_FMT_F16 && fmt != WQ_FMT_Q8_0) return -WQ_ERR_FORMAT;
     if (m < 0 || n < 0 || k < 0) return -WQ_ERR_SHAPE;
     if (fmt == WQ_FMT_Q8_0 && m > 0 && n > 0 && (k == 0 || k % 32 != 0)) return -WQ_ERR_K;
-    return auto_route(m);
+    return auto_route(m, fmt);
 }
 
 int wq_gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits) {
@@ -225,12 +326,12 @@ int wq_set_gemm_plan(int bm, int bn, int splits) {
 }
 
 int wq_set_forced_route(int route) {
-    if (route != WQ_ROUTE_AUTO && route != WQ_ROUTE_GEMV && route != WQ_ROUTE_GEMM) return -WQ_ERR_ROUTE;
+    if (route != WQ_ROUTE_AUTO && !known_route(route)) return -WQ_ERR_ROUTE;
     return wq::g_forced_route.exchange(route);
 }
 
 uint64_t wq_route_count(int route) {
-    if (route != WQ_ROUTE_GEMV && route != WQ_ROUTE_GEMM) return 0;
+    if (!known_route(route)) return 0;
     return wq::g_route_count[route].load(std::memory_order_relaxed);
 }
 

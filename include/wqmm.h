@@ -77,7 +77,9 @@ typedef enum wq_status {
 typedef enum wq_route {
     WQ_ROUTE_AUTO = 0,  /* choose by M (wq_route_for) */
     WQ_ROUTE_GEMV = 1,  /* decode GEMV: one launch per row of A */
-    WQ_ROUTE_GEMM = 2   /* LDS-tiled fp32-MFMA GEMM */
+    WQ_ROUTE_GEMM = 2,  /* LDS-tiled fp32-MFMA GEMM */
+    WQ_ROUTE_SKINNY = 3 /* small-M weight-streaming fp32-MFMA product: one
+                           launch per block of up to 16 rows of A */
 } wq_route;
 
 /* ---------------------------------------------------------------------- */
@@ -99,9 +101,13 @@ int wq_gemm_q8_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t 
                  void *stream);
 
 /* M-routed product for either format (fmt is a wq_format).  M == 1 takes the
- * GEMV, M > 1 the GEMM, unless a route is forced (wq_set_forced_route).
- * Passage: dispatch_gemm_q8 and dispatch_gemm, lattice-inference 0.9.0
- * dispatch.rs. */
+ * GEMV; 2 <= M <= 8 (f16) or 2 <= M <= 4 (Q8_0) the small-M weight-streaming
+ * kernel; larger M the tiled GEMM, unless a route is forced
+ * (wq_set_forced_route).  The small-M kernel reads every weight once per 16
+ * rows of A with fp32 matrix-core accumulation; when it splits K it uses the
+ * same scratch as the GEMM (splits*M*N*4 bytes).  Passage: dispatch_gemm_q8
+ * and dispatch_gemm, lattice-inference 0.9.0 dispatch.rs (M == 1 decode,
+ * M > 1 batched product). */
 int wq_matmul(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt,
               void *stream);
 
@@ -126,7 +132,8 @@ int wq_quantize_q8_0(const float *w, uint8_t *out, int64_t count, void *stream);
 /* Routing and introspection (host only; these never touch the GPU). */
 
 /* The route wq_matmul takes for these arguments when nothing is forced
- * (WQ_ROUTE_GEMV or WQ_ROUTE_GEMM), or a negative wq_status on bad arguments. */
+ * (WQ_ROUTE_GEMV, WQ_ROUTE_SKINNY or WQ_ROUTE_GEMM), or a negative wq_status
+ * on bad arguments. */
 int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt);
 
 /* The tiling the GEMM uses for (m, n, k, fmt) on a device with `cus` compute
@@ -149,7 +156,7 @@ int wq_set_gemm_plan(int bm, int bn, int splits);
  * routes agree (the pages' test hook forcing the fallback GEMM). */
 int wq_set_forced_route(int route);
 
-/* Kernel launches made so far per route (WQ_ROUTE_GEMV / WQ_ROUTE_GEMM) by
+/* Kernel launches made so far per route (GEMV, GEMM or SKINNY) by
  * any entry point, and a reset.  The pages keep such "path proof" counters. */
 uint64_t wq_route_count(int route);
 void wq_reset_route_counts(void);

@@ -100,7 +100,10 @@ def test_shape_format_null_align_alias():
 def test_routing_rule():
     for fmt in (wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0):
         assert wq.wq_route_for(1, 4096, 4096, fmt) == wq.WQ_ROUTE_GEMV
-        for m in (2, 4, 8, 16, 64, 512):
+        top = 8 if fmt == wq.WQ_FMT_F16 else 4
+        for m in range(2, top + 1):
+            assert wq.wq_route_for(m, 4096, 4096, fmt) == wq.WQ_ROUTE_SKINNY
+        for m in (top + 1, 16, 17, 64, 512):
             assert wq.wq_route_for(m, 4096, 4096, fmt) == wq.WQ_ROUTE_GEMM
     assert wq.wq_route_for(2, 8, 33, wq.WQ_FMT_Q8_0) == -wq.WQ_ERR_K
     assert wq.wq_route_for(2, 8, 32, 5) == -wq.WQ_ERR_FORMAT
@@ -112,11 +115,14 @@ def test_forced_route_setting():
     try:
         assert prev == wq.WQ_ROUTE_AUTO
         assert wq.wq_set_forced_route(wq.WQ_ROUTE_GEMV) == wq.WQ_ROUTE_GEMM
+        assert wq.wq_set_forced_route(wq.WQ_ROUTE_SKINNY) == wq.WQ_ROUTE_GEMV
         assert wq.wq_set_forced_route(7) == -wq.WQ_ERR_ROUTE
+        assert wq.wq_set_forced_route(-1) == -wq.WQ_ERR_ROUTE
     finally:
         wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
     wq.wq_reset_route_counts()
-    assert wq.wq_route_count(wq.WQ_ROUTE_GEMV) == 0 and wq.wq_route_count(wq.WQ_ROUTE_GEMM) == 0
+    for r in (wq.WQ_ROUTE_GEMV, wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY):
+        assert wq.wq_route_count(r) == 0
     assert wq.wq_route_count(99) == 0
 
 

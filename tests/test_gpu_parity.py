@@ -231,10 +231,11 @@ def test_f16_any_k(mnk):
 
 
 @pytest.mark.parametrize("fmt", [F16, Q8])
-@pytest.mark.parametrize("entry", ["gemv", "gemm"])
+@pytest.mark.parametrize("entry", ["gemv", "gemm", "matmul"])
 def test_misaligned_pointers(fmt, entry):
-    """a offset by 4 bytes and b by 2 bytes from 16-byte alignment."""
-    m, n, k = (1, 300, 2048)
+    """a offset by 4 bytes and b by 2 bytes from 16-byte alignment (wq_matmul
+    at M = 3 takes the small-M kernel's scalar-load variant)."""
+    m, n, k = (3 if entry == "matmul" else 1, 300, 2048)
     say(f"misaligned {entry} fmt={fmt}")
     ref_b, dev_b = encoded(n, k, fmt, 3)
     a = acts(m, k, 3)
@@ -251,6 +252,8 @@ def test_misaligned_pointers(fmt, entry):
     if entry == "gemv":
         fn = L.wq_gemv_f16 if fmt == F16 else L.wq_gemv_q8_0
         st = fn(a_buf.data_ptr() + 4, bp, c.data_ptr(), n, k, s)
+    elif entry == "matmul":
+        st = L.wq_matmul(a_buf.data_ptr() + 4, bp, c.data_ptr(), m, n, k, fmt, s)
     else:
         fn = L.wq_gemm_f16 if fmt == F16 else L.wq_gemm_q8_0
         st = fn(a_buf.data_ptr() + 4, bp, c.data_ptr(), m, n, k, s)
@@ -329,28 +332,29 @@ def test_deterministic_and_linear(fmt, m):
 
 @pytest.mark.parametrize("fmt", [F16, Q8])
 def test_routes_agree_and_are_counted(fmt):
+    """Every route gives the oracle's product for any M, and the path-proof
+    counters show which kernels ran: the GEMV once per row of A, the GEMM once,
+    the small-M kernel once per 16 rows of A."""
     n, k = 1000, 1024
     ref_b, dev_b = encoded(n, k, fmt, 7)
-    c_ref = {}
-    for m in (1, 3):
-        a = acts(m, k, 7)
-        c_ref[m] = oracle.matmul(a, ref_b, fmt, m, n, k)
+    ms = (1, 3, 20)
+    c_ref = {m: oracle.matmul(acts(m, k, 7), ref_b, fmt, m, n, k) for m in ms}
+    routes = (wq.WQ_ROUTE_GEMV, wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY)
+    expect = {
+        wq.WQ_ROUTE_GEMV: {1: (1, 0, 0), 3: (3, 0, 0), 20: (20, 0, 0)},
+        wq.WQ_ROUTE_GEMM: {1: (0, 1, 0), 3: (0, 1, 0), 20: (0, 1, 0)},
+        wq.WQ_ROUTE_SKINNY: {1: (0, 0, 1), 3: (0, 0, 1), 20: (0, 0, 2)},
+        wq.WQ_ROUTE_AUTO: {1: (1, 0, 0), 3: (0, 0, 1), 20: (0, 1, 0)},
+    }
     try:
-        for route, per_call in ((wq.WQ_ROUTE_GEMV, {1: 1, 3: 3}), (wq.WQ_ROUTE_GEMM, {1: 1, 3: 1}),
-                                (wq.WQ_ROUTE_AUTO, None)):
+        for route, per_call in expect.items():
             wq.wq_set_forced_route(route)
-            for m in (1, 3):
+            for m in ms:
                 say(f"route={route} fmt={fmt} m={m}")
                 wq.wq_reset_route_counts()
                 c = run_gpu("matmul", fmt, acts(m, k, 7), dev_b, m, n, k)
                 assert_close(c, *c_ref[m], f"route {route} m={m}")
-                gv, gm = wq.wq_route_count(wq.WQ_ROUTE_GEMV), wq.wq_route_count(wq.WQ_ROUTE_GEMM)
-                if route == wq.WQ_ROUTE_GEMV:
-                    assert (gv, gm) == (per_call[m], 0)
-                elif route == wq.WQ_ROUTE_GEMM:
-                    assert (gv, gm) == (0, 1)
-                else:
-                    assert (gv, gm) == ((1, 0) if m == 1 else (0, 1))
+                assert tuple(wq.wq_route_count(r) for r in routes) == per_call[m]
     finally:
         wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
 
@@ -365,6 +369,24 @@ def test_nondefault_stream():
         c = run_gpu("matmul", F16, a, dev_b, m, n, k, stream=s)
         c_ref, bound = oracle.matmul(a, ref_b, F16, m, n, k)
         assert_close(c, c_ref, bound, f"stream m={m}")
+
+
+SKINNY_SHAPES = {F16: [(1, 8), (37, 1000), (300, 2048), (4099, 136), (19, 33), (64, 1001)],
+                 Q8: [(1, 32), (37, 992), (300, 2080), (4099, 160), (64, 4096)]}
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("m", [1, 2, 4, 5, 8, 9, 12, 13, 16])
+def test_small_m_kernel_every_row_group(fmt, m):
+    """The small-M kernel (forced route) for every group count of A rows
+    (MB = 1..4), ragged N, K with and without a partial step, K split across
+    workgroups (small N), and K % 8 != 0 (f16 scalar-load variant)."""
+    try:
+        wq.wq_set_forced_route(wq.WQ_ROUTE_SKINNY)
+        for n, k in SKINNY_SHAPES[fmt]:
+            full_case("matmul", fmt, m, n, k, seed=10)
+    finally:
+        wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
 
 
 PLAN_CASES = [(F16, 37, 300, 640), (Q8, 37, 300, 640), (F16, 130, 97, 1000), (F16, 5, 77, 1003),

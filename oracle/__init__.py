@@ -30,6 +30,7 @@ _LIB = os.path.join(_HERE, "libwqref.so")
 
 FMT_F16 = 0
 FMT_Q8_0 = 1
+FMT_Q4_0 = 2
 QK = 32
 BLOCK_BYTES = 34
 
@@ -113,7 +114,7 @@ class Oracle:
 
     # -- decode and product (dispatch_matmul_half / gemm_q8 statements) -----
     def decode(self, b, fmt: int, n: int, k: int) -> np.ndarray:
-        """Exact weights [n, k] (float64) of an f16 or Q8_0 matrix."""
+        """Exact weights [n, k] (float64) of an f16, Q8_0 or Q4_0 matrix."""
         b = np.ascontiguousarray(b)
         out = np.empty((n, k), dtype=np.float64)
         if self.lib.wqref_decode(b.ctypes.data, fmt, n, k, out.ctypes.data) != 0:

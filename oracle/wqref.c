@@ -4,9 +4,12 @@
  *     C[M,N] = A[M,K] · B[N,K]^T        (C is overwritten: beta = 0)
  *
  * A holds f32 activations, row-major [M,K].  B holds weights, row-major
- * [N,K], stored either as IEEE-754 binary16 ("f16") or as Q8_0 blocks:
- * 34 bytes per 32 consecutive weights of a row, a little-endian f16 scale d
- * followed by 32 two's-complement int8 codes q; the weight is d*q.
+ * [N,K], stored either as IEEE-754 binary16 ("f16"), as Q8_0 blocks (34
+ * bytes per 32 consecutive weights of a row: a little-endian f16 scale d
+ * followed by 32 two's-complement int8 codes q; the weight is d*q) or as
+ * Q4_0 blocks (18 bytes per 32 weights: the f16 scale d, then 16 bytes
+ * whose low nibble holds weight 2i and high nibble weight 2i+1 as unsigned
+ * codes u; the weight is (u - 8)*d).
  *
  * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously-correct
  * reference the GPU library is checked against.  Only the test suite, the
@@ -26,6 +29,12 @@
  *    gemm_q8: block = [f16 scale (2 B)][32 x int8 (32 B)], weight = d*q;
  *    QK8_0 = 32, Q8_0_BLOCK_SIZE = 34 and quantize_row_q8_0 (the quantiser);
  *    f32_to_f16 (round to nearest even, with subnormals) and f16_to_f32.
+ *  - lattice-inference 0.1.2 page, kernels gemv_q4_decode, gemm_q4 and
+ *    gemm_q4_tiled: Q4_0 block = [f16 scale (2 B)][16 bytes of packed 4-bit
+ *    codes], weight 2i from the low and 2i+1 from the high nibble of byte i,
+ *    value (nibble - 8) * scale; QK4_0 = 32, Q4_0_BLOCK_SIZE = 18.  (One
+ *    dispatch comment on the 0.9.0 page says [N, K/32 * 20] bytes; every
+ *    kernel reads 18-byte blocks, which is the reading taken.)
  *  - ferrum-kernels 0.7.7, attention/metal/pipelines.rs; MetalPipelines::gemm:
  *    the same product as sgemm(RowMajor, NoTrans, Trans, alpha=1, beta=0).
  *
@@ -40,8 +49,8 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { WQREF_F16 = 0, WQREF_Q8_0 = 1 };
-enum { WQREF_QK = 32, WQREF_BLOCK_BYTES = 34 };
+enum { WQREF_F16 = 0, WQREF_Q8_0 = 1, WQREF_Q4_0 = 2 };
+enum { WQREF_QK = 32, WQREF_BLOCK_BYTES = 34, WQREF_Q4_BLOCK_BYTES = 18 };
 
 /* ------------------------------------------------------------------ f16 -- */
 
@@ -162,15 +171,31 @@ static double q8_0_weight(const uint8_t *b, int64_t K, int64_t n, int64_t k) {
     return wqref_f16_value(h) * (double)q;
 }
 
+/* Exact weight w[n,k] of a Q4_0 matrix with K columns (K % 32 == 0):
+ * row n starts at byte n*(K/32)*18, block j = k/32 at +18*j, scale d is the
+ * little-endian f16 at block bytes 0..1; with i = k%32, the code u is the low
+ * nibble of block byte 2 + i/2 when i is even and its high nibble when i is
+ * odd, and the weight is (u - 8) * d. */
+static double q4_0_weight(const uint8_t *b, int64_t K, int64_t n, int64_t k) {
+    const int64_t nb = K / WQREF_QK;
+    const uint8_t *blk = b + (n * nb + k / WQREF_QK) * WQREF_Q4_BLOCK_BYTES;
+    const uint16_t h = (uint16_t)(blk[0] | (blk[1] << 8));
+    const int i = (int)(k % WQREF_QK);
+    const uint8_t byte = blk[2 + i / 2];
+    const int u = (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);
+    return (double)(u - 8) * wqref_f16_value(h);
+}
+
 static double weight(const void *b, int fmt, int64_t K, int64_t n, int64_t k) {
     if (fmt == WQREF_F16) return wqref_f16_value(((const uint16_t *)b)[n * K + k]);
+    if (fmt == WQREF_Q4_0) return q4_0_weight((const uint8_t *)b, K, n, k);
     return q8_0_weight((const uint8_t *)b, K, n, k);
 }
 
 static int check_args(const void *b, int fmt, int64_t N, int64_t K) {
     if (N < 0 || K < 0) return -1;
-    if (fmt != WQREF_F16 && fmt != WQREF_Q8_0) return -1;
-    if (fmt == WQREF_Q8_0 && (K == 0 || K % WQREF_QK)) return -1;
+    if (fmt != WQREF_F16 && fmt != WQREF_Q8_0 && fmt != WQREF_Q4_0) return -1;
+    if (fmt != WQREF_F16 && (K == 0 || K % WQREF_QK)) return -1;
     if (!b && N > 0 && K > 0) return -1;
     return 0;
 }

@@ -27,7 +27,7 @@ import pytest
 
 import oracle
 import wqgen
-from oracle import FMT_F16, FMT_Q8_0
+from oracle import FMT_F16, FMT_Q4_0, FMT_Q8_0
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -67,8 +67,21 @@ def _golden_q8():
     return blocks
 
 
+def _golden_q4():
+    blocks = []
+    with open(os.path.join(GOLDEN, "q4_0_blocks.txt")) as f:
+        lines = [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+    for i in range(0, len(lines), 3):
+        assert lines[i].startswith("block ")
+        byts = bytes(int(t, 16) for t in lines[i + 1].split())
+        vals = [_parse_float(t) for t in lines[i + 2].split()]
+        assert len(byts) == 18 and len(vals) == 32, lines[i]
+        blocks.append((lines[i][6:], byts, np.array(vals, dtype=np.float64)))
+    return blocks
+
+
 def _golden_matmul():
-    a, f16, q8, c = {}, {}, {}, {}
+    a, f16, q8, q4, c = {}, {}, {}, {}, {}
     dims = None
     with open(os.path.join(GOLDEN, "matmul_tiny.txt")) as f:
         for line in f:
@@ -83,6 +96,8 @@ def _golden_matmul():
                 f16[(int(tok[1]), int(tok[2]))] = int(tok[3], 16)
             elif tok[0] == "q8":
                 q8[int(tok[1])] = bytes(int(t, 16) for t in tok[2:])
+            elif tok[0] == "q4":
+                q4[int(tok[1])] = bytes(int(t, 16) for t in tok[2:])
             elif tok[0] == "c":
                 c[(int(tok[1]), int(tok[2]))] = float(tok[3])
     M, N, K = dims
@@ -93,16 +108,24 @@ def _golden_matmul():
     for (n, k), v in f16.items():
         B16[n, k] = v
     B8 = np.frombuffer(b"".join(q8[n] for n in range(N)), dtype=np.uint8).reshape(N, -1)
+    B4 = np.frombuffer(b"".join(q4[n] for n in range(N)), dtype=np.uint8).reshape(N, -1)
     C = np.zeros((M, N))
     for (m, n), v in c.items():
         C[m, n] = v
-    return M, N, K, A, B16, B8, C
+    return M, N, K, A, B16, B8, B4, C
 
 
 def _numpy_decode(b, fmt, n, k):
     """Weights decoded with numpy's own binary16 codec (independent of the oracle)."""
     if fmt == FMT_F16:
         return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float64).reshape(n, k)
+    if fmt == FMT_Q4_0:
+        raw = np.ascontiguousarray(b, dtype=np.uint8).reshape(n, k // 32, 18)
+        d = raw[:, :, 0:2].copy().view("<f2").astype(np.float64)          # [n, nb, 1]
+        codes = np.empty((n, k // 32, 32), np.int64)
+        codes[:, :, 0::2] = raw[:, :, 2:18] & 0x0F
+        codes[:, :, 1::2] = raw[:, :, 2:18] >> 4
+        return (d * (codes - 8)).reshape(n, k)
     raw = np.ascontiguousarray(b, dtype=np.uint8).reshape(n, k // 32, 34)
     d = raw[:, :, 0:2].copy().view("<f2").astype(np.float64)          # [n, nb, 1]
     q = raw[:, :, 2:34].copy().view(np.int8).astype(np.float64)       # [n, nb, 32]
@@ -114,6 +137,12 @@ def _dyadic_inputs(rng, m, n, k, fmt):
     if fmt == FMT_F16:
         vals = np.array([0.0, 0.5, -0.5, 1.0, -1.0, 2.0, -2.0, 0.25, -0.25], np.float16)
         b = vals[rng.integers(0, len(vals), size=(n, k))].view(np.uint16)
+    elif fmt == FMT_Q4_0:
+        blocks = []
+        for _ in range(n * k // 32):
+            d = [0x3800, 0x3c00, 0x3400, 0xb800][rng.integers(0, 4)]
+            blocks.append(struct.pack("<H", d) + rng.integers(0, 256, size=16).astype(np.uint8).tobytes())
+        b = np.frombuffer(b"".join(blocks), np.uint8).reshape(n, -1)
     else:
         blocks = []
         for _ in range(n * k // 32):
@@ -122,6 +151,15 @@ def _dyadic_inputs(rng, m, n, k, fmt):
             blocks.append(struct.pack("<H", d) + q.tobytes())
         b = np.frombuffer(b"".join(blocks), np.uint8).reshape(n, -1)
     return a, b
+
+
+def _weights(orc, fmt, n, k, seed):
+    """Encoded weights for the random-input pins: the oracle's f16 / Q8_0
+    encoders on N(0, 0.02) draws, and wqgen's synthetic bytes for Q4_0 (the
+    pages give no Q4_0 encoder)."""
+    if fmt == FMT_Q4_0:
+        return wqgen.q4_0_bytes(n, k, seed)
+    return orc.encode(wqgen.normal((n, k), seed=seed, stream=1, std=0.02), fmt)
 
 
 # ------------------------------------------------------------------- pins --
@@ -215,10 +253,23 @@ def pin_q8_decode_handbuilt(orc):
         assert np.array_equal(got, dval * codes.astype(np.float64))
 
 
+def pin_q4_golden(orc):
+    """Q4_0 blocks decoded by hand from the pages' Q4_0 kernels (tests/golden/q4_0_blocks.txt):
+    little-endian scale, low nibble = even weight, code offset 8, negative and
+    subnormal scales; a row of all the blocks and each block alone."""
+    blocks = _golden_q4()
+    row = np.frombuffer(b"".join(byts for _, byts, _ in blocks), np.uint8).reshape(1, -1)
+    got = orc.decode(row, FMT_Q4_0, 1, 32 * len(blocks))[0]
+    assert np.array_equal(got, np.concatenate([vals for _, _, vals in blocks]))
+    for name, byts, vals in blocks:
+        got = orc.decode(np.frombuffer(byts, np.uint8).reshape(1, 18), FMT_Q4_0, 1, 32)[0]
+        assert np.array_equal(got, vals), name
+
+
 def pin_matmul_golden(orc):
-    """The hand-worked 2x3x32 example of tests/golden/matmul_tiny.txt, both formats."""
-    M, N, K, A, B16, B8, C = _golden_matmul()
-    for fmt, b in ((FMT_F16, B16), (FMT_Q8_0, B8)):
+    """The hand-worked 2x3x32 example of tests/golden/matmul_tiny.txt, all three formats."""
+    M, N, K, A, B16, B8, B4, C = _golden_matmul()
+    for fmt, b in ((FMT_F16, B16), (FMT_Q8_0, B8), (FMT_Q4_0, B4)):
         c, _ = orc.matmul(A, b, fmt, M, N, K)
         assert np.array_equal(c, C), (fmt, c)
 
@@ -228,7 +279,7 @@ def pin_bruteforce_fraction(orc):
     exact rational arithmetic bit for bit; and on N(0,1) activations it must be
     within K * 2^-52 * sum|p| of the exact sum."""
     rng = np.random.default_rng(5)
-    for fmt in (FMT_F16, FMT_Q8_0):
+    for fmt in (FMT_F16, FMT_Q8_0, FMT_Q4_0):
         for m in (1, 2, 3):
             for n in (1, 2, 3):
                 for k in (32, 64):
@@ -241,8 +292,7 @@ def pin_bruteforce_fraction(orc):
                                         for t in range(k))
                             assert c[i, j] == float(exact)
         a = wqgen.normal((2, 96), seed=1, stream=0)
-        wf = wqgen.normal((3, 96), seed=1, stream=1, std=0.02)
-        b = orc.encode(wf, fmt)
+        b = _weights(orc, fmt, 3, 96, seed=1)
         w = _numpy_decode(b, fmt, 3, 96)
         c, _ = orc.matmul(a, b, fmt, 2, 3, 96)
         for i in range(2):
@@ -294,6 +344,19 @@ def pin_identity_and_onehot(orc):
     c, _ = orc.matmul(a, b8, FMT_Q8_0, 3, N, K)
     dv = np.array([struct.unpack("<e", struct.pack("<H", h))[0] for h in ds])
     assert np.array_equal(c, a[:, cols].astype(np.float64) * (dv * np.array(qs))[None, :])
+    # Q4_0: identity (code 9 = +1 on the diagonal, 8 = 0 elsewhere), then one-hot
+    # rows with codes 0..15 (weights -8..7 times the scale)
+    def q4_row(n_codes, d):
+        nib = np.array(n_codes, np.uint8).reshape(-1, 32)
+        packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+        return b"".join(struct.pack("<H", d) + blk.tobytes() for blk in packed)
+    eye4 = b"".join(q4_row([9 if t == n else 8 for t in range(K)], 0x3c00) for n in range(K))
+    c, _ = orc.matmul(a, np.frombuffer(eye4, np.uint8).reshape(K, -1), FMT_Q4_0, 3, K, K)
+    assert np.array_equal(c, a.astype(np.float64))
+    us = [(3 * n) % 16 for n in range(N)]
+    b4 = b"".join(q4_row([us[n] if t == cols[n] else 8 for t in range(K)], ds[n]) for n in range(N))
+    c, _ = orc.matmul(a, np.frombuffer(b4, np.uint8).reshape(N, -1), FMT_Q4_0, 3, N, K)
+    assert np.array_equal(c, a[:, cols].astype(np.float64) * (dv * (np.array(us) - 8))[None, :])
 
 
 def pin_invariants(orc):
@@ -301,9 +364,8 @@ def pin_invariants(orc):
     permuting the rows of B permutes the columns of C; entries match the full product."""
     M, N, K = 5, 37, 96
     a = wqgen.normal((M, K), seed=4, stream=0)
-    wf = wqgen.normal((N, K), seed=4, stream=1, std=0.02)
-    for fmt in (FMT_F16, FMT_Q8_0):
-        b = orc.encode(wf, fmt)
+    for fmt in (FMT_F16, FMT_Q8_0, FMT_Q4_0):
+        b = _weights(orc, fmt, N, K, seed=4)
         c, bound = orc.matmul(a, b, fmt, M, N, K)
         for m in range(M):
             cm, _ = orc.matmul(a[m:m + 1], b, fmt, 1, N, K)
@@ -326,9 +388,8 @@ def pin_numpy_matmul(orc):
     including ragged shapes, K = 0 and the tolerance scale 1e-5*sum|a w| + 1e-6."""
     for (M, N, K) in ((1, 300, 256), (7, 129, 320), (33, 65, 1024)):
         a = wqgen.normal((M, K), seed=M, stream=0)
-        wf = wqgen.normal((N, K), seed=M, stream=1, std=0.02)
-        for fmt in (FMT_F16, FMT_Q8_0):
-            b = orc.encode(wf, fmt)
+        for fmt in (FMT_F16, FMT_Q8_0, FMT_Q4_0):
+            b = _weights(orc, fmt, N, K, seed=M)
             w = _numpy_decode(b, fmt, N, K)
             c, bound = orc.matmul(a, b, fmt, M, N, K)
             a64 = a.astype(np.float64)
@@ -347,6 +408,7 @@ PINS = [
     pin_q8_golden,
     pin_q8_roundtrip,
     pin_q8_decode_handbuilt,
+    pin_q4_golden,
     pin_matmul_golden,
     pin_bruteforce_fraction,
     pin_identity_and_onehot,
@@ -366,6 +428,8 @@ def test_argument_errors(orc):
         orc.matmul(a, np.zeros((1, 51), np.uint8), FMT_Q8_0, 1, 1, 48)  # K % 32 != 0
     with pytest.raises(ValueError):
         orc.matmul(a, np.zeros((1, 0), np.uint8), FMT_Q8_0, 1, 1, 0)    # Q8_0 with K == 0
+    with pytest.raises(ValueError):
+        orc.matmul(a, np.zeros((1, 27), np.uint8), FMT_Q4_0, 1, 1, 48)  # Q4_0, K % 32 != 0
     with pytest.raises(ValueError):
         orc.matmul(a, np.zeros((1, 48), np.uint16), 7, 1, 1, 48)        # unknown format
     with pytest.raises(ValueError):
@@ -393,6 +457,13 @@ MUTANTS = {
     "f32_accumulate": ("s += p;", "s = (double)(float)(s + p);"),
     "row_zero_only": ("dot(j->a + m * j->K, w", "dot(j->a + 0 * j->K, w"),
     "abs_sum_dropped": ("sa += fabs(p);", "sa += p;"),
+    "q4_nibble_order": ("(i % 2 == 0) ? (byte & 0x0F) : (byte >> 4)", "(i % 2 == 0) ? (byte >> 4) : (byte & 0x0F)"),
+    "q4_no_offset": ("(double)(u - 8)", "(double)(u)"),
+    "q4_offset_7": ("(double)(u - 8)", "(double)(u - 7)"),
+    "q4_block_20_bytes": ("* WQREF_Q4_BLOCK_BYTES;", "* 20;"),
+    "q4_split_halves_layout": ("blk[2 + i / 2];\n    const int u = (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
+                               "blk[2 + i % 16];\n    const int u = (i < 16) ? (byte & 0x0F) : (byte >> 4);"),
+    "q4_signed_nibble": ("(byte & 0x0F) : (byte >> 4);", "((byte & 0x0F) ^ 8) : ((byte >> 4) ^ 8);"),
 }
 
 

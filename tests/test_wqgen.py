@@ -66,3 +66,22 @@ def test_moments():
     assert abs(w.std() - 0.02) < 0.0002
     # tail mass beyond 3 sigma for a normal: 0.0027
     assert abs(np.mean(np.abs(x) > 3.0) - 0.0027) < 0.0004
+
+
+def test_q4_0_bytes_layout_and_determinism():
+    b = wqgen.q4_0_bytes(5, 96, seed=3)
+    assert b.shape == (5, 3 * 18) and b.dtype == np.uint8
+    assert np.array_equal(b, wqgen.q4_0_bytes(5, 96, seed=3))
+    assert np.array_equal(b[2:4], wqgen.q4_0_bytes(2, 96, seed=3, row0=2))
+    assert not np.array_equal(b, wqgen.q4_0_bytes(5, 96, seed=4))
+    blocks = b.reshape(-1, 18)
+    scale = blocks[:, 0:2].copy().view("<u2").ravel()
+    assert np.all((scale & 0x7C00) == 0x1C00)            # |d| in [2^-8, 2^-7)
+    # codes of a big draw: all 16 values, both scale signs
+    big = wqgen.q4_0_bytes(64, 1024, seed=0).reshape(-1, 18)
+    codes = np.concatenate([big[:, 2:] & 0x0F, big[:, 2:] >> 4]).ravel()
+    assert set(np.unique(codes)) == set(range(16))
+    signs = big[:, 1] >> 7
+    assert 0.4 < signs.mean() < 0.6
+    with pytest.raises(ValueError):
+        wqgen.q4_0_bytes(1, 48)

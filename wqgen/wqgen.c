@@ -42,6 +42,14 @@ uint64_t wqgen_u64(uint64_t key, uint64_t i) {
     return mix64(key + (i + 1) * WQGEN_GAMMA);
 }
 
+/* out[i] = output offset + i of stream (seed, stream), for i < count. */
+int wqgen_u64_fill(uint64_t *out, uint64_t count, uint64_t seed, uint64_t stream, uint64_t offset) {
+    if (count && !out) return -1;
+    const uint64_t key = wqgen_stream_key(seed, stream);
+    for (uint64_t i = 0; i < count; ++i) out[i] = wqgen_u64(key, offset + i);
+    return 0;
+}
+
 static inline double unit_open0(uint64_t x) {
     return (double)((x >> 11) + 1) * (1.0 / 9007199254740992.0); /* 2^-53 */
 }

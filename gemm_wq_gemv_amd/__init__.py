@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libwqmm.so")
 
 WQ_FMT_F16 = 0
 WQ_FMT_Q8_0 = 1
+WQ_FMT_Q4_0 = 2
 
 WQ_OK = 0
 WQ_ERR_NULL = 1
@@ -41,6 +42,7 @@ WQ_ROUTE_SKINNY = 3
 
 Q8_0_BLOCK_BYTES = 34
 Q8_0_BLOCK_WEIGHTS = 32
+Q4_0_BLOCK_BYTES = 18
 
 
 class WQError(RuntimeError):
@@ -58,8 +60,10 @@ def _load() -> ctypes.CDLL:
     sigs = {
         "wq_gemv_f16": (I, [P, P, P, I64, I64, P]),
         "wq_gemv_q8_0": (I, [P, P, P, I64, I64, P]),
+        "wq_gemv_q4_0": (I, [P, P, P, I64, I64, P]),
         "wq_gemm_f16": (I, [P, P, P, I64, I64, I64, P]),
         "wq_gemm_q8_0": (I, [P, P, P, I64, I64, I64, P]),
+        "wq_gemm_q4_0": (I, [P, P, P, I64, I64, I64, P]),
         "wq_matmul": (I, [P, P, P, I64, I64, I64, I, P]),
         "wq_pack_f16": (I, [P, P, I64, P]),
         "wq_quantize_q8_0": (I, [P, P, I64, P]),
@@ -128,6 +132,8 @@ def weight_bytes(n: int, k: int, fmt: int) -> int:
     """Bytes of an [n, k] weight matrix in the given format."""
     if fmt == WQ_FMT_F16:
         return 2 * n * k
+    if fmt == WQ_FMT_Q4_0:
+        return n * (k // Q8_0_BLOCK_WEIGHTS) * Q4_0_BLOCK_BYTES
     return n * (k // Q8_0_BLOCK_WEIGHTS) * Q8_0_BLOCK_BYTES
 
 
@@ -143,7 +149,7 @@ def _sizes(a, b, c, m, n, k, fmt):
         _dtype(b, _H if fmt == WQ_FMT_F16 else _U8, "b")
         _need(a, 4 * m * k, "a")
         _need(c, 4 * m * n, "c")
-        if k >= 0 and (fmt != WQ_FMT_Q8_0 or k % 32 == 0):
+        if k >= 0 and (fmt == WQ_FMT_F16 or k % 32 == 0):
             _need(b, weight_bytes(n, k, fmt), "b")
 
 
@@ -158,6 +164,11 @@ def wq_gemv_q8_0(a, b, c, n: int, k: int, stream=None) -> None:
     _check(_lib.wq_gemv_q8_0(_ptr(a), _ptr(b), _ptr(c), n, k, _stream(stream, c)), "wq_gemv_q8_0")
 
 
+def wq_gemv_q4_0(a, b, c, n: int, k: int, stream=None) -> None:
+    _sizes(a, b, c, 1, n, k, WQ_FMT_Q4_0)
+    _check(_lib.wq_gemv_q4_0(_ptr(a), _ptr(b), _ptr(c), n, k, _stream(stream, c)), "wq_gemv_q4_0")
+
+
 def wq_gemm_f16(a, b, c, m: int, n: int, k: int, stream=None) -> None:
     _sizes(a, b, c, m, n, k, WQ_FMT_F16)
     _check(_lib.wq_gemm_f16(_ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(stream, c)), "wq_gemm_f16")
@@ -168,8 +179,13 @@ def wq_gemm_q8_0(a, b, c, m: int, n: int, k: int, stream=None) -> None:
     _check(_lib.wq_gemm_q8_0(_ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(stream, c)), "wq_gemm_q8_0")
 
 
+def wq_gemm_q4_0(a, b, c, m: int, n: int, k: int, stream=None) -> None:
+    _sizes(a, b, c, m, n, k, WQ_FMT_Q4_0)
+    _check(_lib.wq_gemm_q4_0(_ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(stream, c)), "wq_gemm_q4_0")
+
+
 def wq_matmul(a, b, c, m: int, n: int, k: int, fmt: int, stream=None) -> None:
-    if fmt in (WQ_FMT_F16, WQ_FMT_Q8_0):
+    if fmt in (WQ_FMT_F16, WQ_FMT_Q8_0, WQ_FMT_Q4_0):
         _sizes(a, b, c, m, n, k, fmt)
     _check(_lib.wq_matmul(_ptr(a), _ptr(b), _ptr(c), m, n, k, fmt, _stream(stream, c)), "wq_matmul")
 

@@ -1,4 +1,4 @@
-// Prefill GEMM (M > 1): C[M,N] = A[M,K] . B[N,K]^T with f16 or Q8_0 weights,
+// Prefill GEMM (M > 1): C[M,N] = A[M,K] . B[N,K]^T with f16, Q8_0 or Q4_0 weights,
 // fp32 matrix-core accumulation.
 //
 // Operation: dispatch_gemm_q8 / dispatch_gemm (lattice-inference 0.9.0,
@@ -45,8 +45,9 @@ constexpr int PAD = 4;            // floats of padding per LDS row
 constexpr int LDP = BK + PAD;     // LDS row pitch in floats
 constexpr int kXcds = 8;
 constexpr int kQ8BlockBytes = 34;
+constexpr int kQ4BlockBytes = 18;
 
-enum { FMT_F16 = 0, FMT_Q8_0 = 1 };
+enum { FMT_F16 = 0, FMT_Q8_0 = 1, FMT_Q4_0 = 2 };
 
 // Tile id for workgroup `bid` of `tiles`, so that XCD x (= bid % 8) receives a
 // contiguous range of tile ids.
@@ -64,13 +65,16 @@ struct Gemm {
     static_assert(FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
     static constexpr int A_ITERS = (BM * 8 + 255) / 256;    // float4 chunks of A per thread
     static constexpr int B16_ITERS = (BN * 4 + 255) / 256;  // uint4 chunks of f16 B per thread
-    static constexpr int B8_ITERS = (BN * 2 + 255) / 256;   // half blocks of Q8_0 B per thread
+    static constexpr int B8_ITERS = (BN * 2 + 255) / 256;   // half blocks of Q8_0 / Q4_0 B per thread
+    static constexpr bool QUANT = FMT != FMT_F16;
+    static constexpr int QBB = FMT == FMT_Q4_0 ? kQ4BlockBytes : kQ8BlockBytes;  // block bytes
+    static constexpr int QW = FMT == FMT_Q4_0 ? 4 : 8;  // 16-bit code words per half block
 
     struct Regs {
         float4 a[A_ITERS];
         uint4 b16[FMT == FMT_F16 ? B16_ITERS : 1];
-        uint32_t d8[FMT == FMT_Q8_0 ? B8_ITERS : 1];
-        uint32_t q8[FMT == FMT_Q8_0 ? B8_ITERS : 1][8];
+        uint32_t d8[QUANT ? B8_ITERS : 1];
+        uint32_t q8[QUANT ? B8_ITERS : 1][QW];
     };
 
     // Global -> registers for the k-tile starting at k0.  On the vector path
@@ -125,8 +129,10 @@ struct Gemm {
                 r.b16[i] = v;
             }
         } else {
+            // Thread half h of a block row reads the scale and the code bytes
+            // of weights 16h .. 16h+15: 16 bytes (Q8_0) or 8 bytes (Q4_0).
             const uint8_t *b = static_cast<const uint8_t *>(bw);
-            const int64_t row_bytes = (K >> 5) * kQ8BlockBytes;
+            const int64_t row_bytes = (K >> 5) * QBB;
             const int64_t kb = k0 >> 5;
 #pragma unroll
             for (int i = 0; i < B8_ITERS; ++i) {
@@ -134,11 +140,10 @@ struct Gemm {
                 const int h = tid & 1;
                 // Rows past N only feed outputs that are never stored.
                 const int64_t gnc = min<int64_t>(n0 + row, N - 1);
-                const uint16_t *blk =
-                    reinterpret_cast<const uint16_t *>(b + gnc * row_bytes + kb * kQ8BlockBytes);
+                const uint16_t *blk = reinterpret_cast<const uint16_t *>(b + gnc * row_bytes + kb * QBB);
                 r.d8[i] = blk[0];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) r.q8[i][u] = blk[1 + 8 * h + u];
+                for (int u = 0; u < QW; ++u) r.q8[i][u] = blk[1 + QW * h + u];
             }
         }
     }
@@ -169,6 +174,26 @@ struct Gemm {
                     float *dst = &Bs[row][8 * (tid & 3)];
                     *reinterpret_cast<float4 *>(dst) = lo;
                     *reinterpret_cast<float4 *>(dst + 4) = hi;
+                }
+            }
+        } else if constexpr (FMT == FMT_Q4_0) {
+            // Code word u holds weights 4u .. 4u+3 of the half block, one per
+            // nibble from the least significant: (nibble - 8) * d.
+#pragma unroll
+            for (int i = 0; i < B8_ITERS; ++i) {
+                const int row = (tid >> 1) + 128 * i;
+                if (row < BN) {
+                    const float d = half_bits_to_float(r.d8[i]);
+                    float *dst = &Bs[row][16 * (tid & 1)];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t w = r.q8[i][u];
+                        float4 v = make_float4(d * static_cast<float>(static_cast<int>(w & 0xfu) - 8),
+                                               d * static_cast<float>(static_cast<int>((w >> 4) & 0xfu) - 8),
+                                               d * static_cast<float>(static_cast<int>((w >> 8) & 0xfu) - 8),
+                                               d * static_cast<float>(static_cast<int>((w >> 12) & 0xfu) - 8));
+                        *reinterpret_cast<float4 *>(dst + 4 * u) = v;
+                    }
                 }
             }
         } else {
@@ -369,7 +394,8 @@ constexpr TileCfg kCfgs[] = {
 // below; a split adds the partial-sum pass.
 Plan choose_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus) {
     const int64_t ktiles = (k + BK - 1) / BK;
-    const double wbytes = fmt == FMT_F16 ? 2.0 * n * k : static_cast<double>(n) * (k / 32) * kQ8BlockBytes;
+    const double wbytes = fmt == FMT_F16 ? 2.0 * n * k
+                          : static_cast<double>(n) * (k / 32) * (fmt == FMT_Q4_0 ? kQ4BlockBytes : kQ8BlockBytes);
     const double hbm_bytes_per_cycle = 6.0e12 / 2.4e9;  // sustained, whole chip
     Plan best{kCfgs[0], 1, static_cast<int>(ktiles)};
     double best_t = 1e300;
@@ -493,7 +519,8 @@ hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t
         const bool vec = a16 && b16 && (k % 8 == 0);
         return dispatch<FMT_F16>(a, b, c, m, n, k, vec, s, di.cus);
     }
-    const bool vec = a16;  // K % 32 == 0 always holds for Q8_0
+    const bool vec = a16;  // K % 32 == 0 always holds for Q8_0 and Q4_0
+    if (fmt == FMT_Q4_0) return dispatch<FMT_Q4_0>(a, b, c, m, n, k, vec, s, di.cus);
     return dispatch<FMT_Q8_0>(a, b, c, m, n, k, vec, s, di.cus);
 }
 

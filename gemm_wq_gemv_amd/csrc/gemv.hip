@@ -1,8 +1,9 @@
-// Decode GEMV (M = 1): c[n] = sum_k a[k] * w[n, k] for f16 and Q8_0 weights.
+// Decode GEMV (M = 1): c[n] = sum_k a[k] * w[n, k] for f16, Q8_0 and Q4_0 weights.
 //
-// The operation is the M = 1 case of dispatch_matmul_half / dispatch_matmul_q8
-// (lattice-inference 0.9.0, dispatch.rs) and of the kernels gemv_decode_m1 and
-// gemv_q8_decode (lattice-inference 0.1.2, metal_qwen35.rs).  Those kernels
+// The operation is the M = 1 case of dispatch_matmul_half / dispatch_matmul_q8 /
+// dispatch_matmul_q4 (lattice-inference 0.9.0, dispatch.rs) and of the kernels
+// gemv_decode_m1, gemv_q8_decode and gemv_q4_decode (lattice-inference 0.1.2,
+// metal_qwen35.rs).  Those kernels
 // were written for 32-lane Apple SIMD groups (one threadgroup per output row
 // for f16, two rows per threadgroup for Q8_0).  On CDNA4 the work is bound by
 // HBM bandwidth, so the design here is about the byte stream:
@@ -20,7 +21,10 @@
 //    whole blocks from LDS (scale, 32 int8 codes, read with unaligned 16-byte
 //    LDS loads) against its register slice of `a`: sum_q = sum_i q_i a_i,
 //    acc += d * sum_q, as the pages apply d after the block's int8 dot
-//    product.  The decode of a pass is branch-free so the rows' dependency
+//    product.  Q4_0 (18-byte blocks, 4-bit codes) is staged the same way; its
+//    codes are turned into exact f16 values (u - 8) with one packed f16
+//    subtraction per two codes and fed to mixed-precision FMAs.
+//    The decode of a pass is branch-free so the rows' dependency
 //    chains overlap, and the rows of a pass are reduced together by one
 //    butterfly (each cross-lane step halves the values a lane carries).
 //  * Reductions: DPP within 16-lane rows, lane-xor across rows (64 lanes).
@@ -123,11 +127,20 @@ __global__ __launch_bounds__(256) void gemv_f16_any(const float *__restrict__ a,
     }
 }
 
-// ----------------------------------------------------------------- Q8_0 ----
+// ------------------------------------------------------- Q8_0 and Q4_0 ----
 
-constexpr int kQ8BlockBytes = 34;
-constexpr int kQ8Chunks = 17;                // 16-byte chunks per lane per pass
-constexpr int kQ8StageTarget = kQ8Chunks * 64 * 16;  // 17408 bytes: 8 rows at K = 2048
+enum { QFMT_Q8_0 = 1, QFMT_Q4_0 = 2 };
+
+// Block bytes, and 16-byte chunks each lane stages per pass (the stage holds
+// whole rows: 8 rows of Q8_0 at K = 2048, 16 rows of Q4_0 at K = 2048).
+template <int FMT>
+struct QB {
+    static constexpr int kBytes = FMT == QFMT_Q8_0 ? 34 : 18;
+    static constexpr int kChunks = FMT == QFMT_Q8_0 ? 17 : 18;
+    static constexpr int kStage = kChunks * 64 * 16;
+};
+constexpr int kQ8BlockBytes = QB<QFMT_Q8_0>::kBytes;
+constexpr int kQ4BlockBytes = QB<QFMT_Q4_0>::kBytes;
 
 // Dot product of one Q8_0 block held in LDS at byte offset pb with the 32
 // activations av[0..31]: returns d * sum_i q_i * av[i].  The codes are read as
@@ -153,25 +166,81 @@ __device__ __forceinline__ float q8_block_dot(const uint8_t *stage, int pb, cons
     return half_bits_to_float(hb) * ((part[0] + part[1]) + (part[2] + part[3]));
 }
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// (u - 8) for the 4-bit codes in bits 0..3 of both 16-bit halves of x, or
+// 16 * (u - 8) for codes in bits 4..7 (HI): the code is placed in the
+// mantissa of the f16 1024 (0x6400), which reads as 1024 + u (1024 + 16 u),
+// and one packed subtraction removes 1032 (1152).  Every step is exact.
+template <bool HI>
+__device__ __forceinline__ h2 q4_pair(uint32_t x) {
+    const uint32_t m = (x & (HI ? 0x00F000F0u : 0x000F000Fu)) | 0x64006400u;
+    const _Float16 bias = HI ? static_cast<_Float16>(1152.0f) : static_cast<_Float16>(1032.0f);
+    return __builtin_bit_cast(h2, m) - h2{bias, bias};
+}
+
+// Dot product of one Q4_0 block in LDS at byte offset pb with av[0..31]:
+// d * sum_i (u_i - 8) * av[i].  Byte j of the 16 code bytes (one unaligned
+// 16-byte LDS read at block byte 2) holds weight 2j in its low nibble and
+// 2j + 1 in its high nibble.  Codes from high nibbles come out scaled by 16
+// and are summed apart; the exact power-of-two 1/16 is applied at the end.
+// The f16 code values feed mixed-precision FMAs (f32 activation, f32 sum).
+__device__ __forceinline__ float q4_block_dot(const uint8_t *stage, int pb, const float *av) {
+    const uint32_t hb = *reinterpret_cast<const uint16_t *>(stage + pb);
+    u32x4 q;
+    __builtin_memcpy(&q, __builtin_assume_aligned(stage + pb + 2, 2), 16);
+    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    float lo[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // dword i = code bytes 4i .. 4i+3 = weights 8i .. 8i+7
+        const uint32_t w = wd[i], w8 = wd[i] >> 8;
+        const h2 p0 = q4_pair<false>(w);   // weights 8i+0, 8i+4
+        const h2 p1 = q4_pair<true>(w);    // 8i+1, 8i+5 (x16)
+        const h2 p2 = q4_pair<false>(w8);  // 8i+2, 8i+6
+        const h2 p3 = q4_pair<true>(w8);   // 8i+3, 8i+7 (x16)
+        const float *x = av + 8 * i;
+        lo[0] = fmaf(static_cast<float>(p0.x), x[0], lo[0]);
+        lo[1] = fmaf(static_cast<float>(p0.y), x[4], lo[1]);
+        lo[0] = fmaf(static_cast<float>(p2.x), x[2], lo[0]);
+        lo[1] = fmaf(static_cast<float>(p2.y), x[6], lo[1]);
+        hi[0] = fmaf(static_cast<float>(p1.x), x[1], hi[0]);
+        hi[1] = fmaf(static_cast<float>(p1.y), x[5], hi[1]);
+        hi[0] = fmaf(static_cast<float>(p3.x), x[3], hi[0]);
+        hi[1] = fmaf(static_cast<float>(p3.y), x[7], hi[1]);
+    }
+    return half_bits_to_float(hb) * ((lo[0] + lo[1]) + 0.0625f * (hi[0] + hi[1]));
+}
+
+template <int FMT>
+__device__ __forceinline__ float block_dot(const uint8_t *stage, int pb, const float *av) {
+    if constexpr (FMT == QFMT_Q8_0)
+        return q8_block_dot(stage, pb, av);
+    else
+        return q4_block_dot(stage, pb, av);
+}
+
 // One wave per workgroup.  LPR lanes share a row; lane l covers blocks
 // j = l % LPR + LPR * t (t < J) of that row and keeps a[32 j .. 32 j + 32) in
 // VGPRs.  A pass covers S = SL * (64 / LPR) consecutive rows, i.e. S * row_bytes
-// contiguous bytes (at most kQ8Chunks * 64 16-byte chunks).  The next pass is
-// in flight in registers (kQ8Chunks independent 128-bit loads per lane) while
-// the current pass, already copied to LDS, is decoded; the SL rows a lane
-// group decodes are unrolled so their LDS reads and reductions interleave.
+// contiguous bytes (at most kChunks * 64 16-byte chunks).  The next pass is in
+// flight in registers (kChunks independent 128-bit loads per lane) while the
+// current pass, already copied to LDS, is decoded; the SL rows a lane group
+// decodes are unrolled so their LDS reads and reductions interleave.
 // Requires K % 256 == 0 (rows are whole 16-byte chunks), 16-byte aligned a, b.
-template <int J, int LPR, int SL>
-__global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a,
-                                                     const uint8_t *__restrict__ b,
-                                                     float *__restrict__ c, int64_t n, int64_t k,
-                                                     int64_t passes) {
+template <int FMT, int J, int LPR, int SL>
+__global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
+                                                    const uint8_t *__restrict__ b,
+                                                    float *__restrict__ c, int64_t n, int64_t k,
+                                                    int64_t passes) {
     extern __shared__ uint4 stage4[];
+    constexpr int BB = QB<FMT>::kBytes;
+    constexpr int CH = QB<FMT>::kChunks;
     constexpr int RPL = kWave / LPR;
     constexpr int S = SL * RPL;
     const int lane = threadIdx.x;
     const int nb = static_cast<int>(k >> 5);
-    const int row_bytes = nb * kQ8BlockBytes;
+    const int row_bytes = nb * BB;
     const int jl = lane % LPR;
     const int rsub = lane / LPR;
 
@@ -195,12 +264,12 @@ __global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a
     // skipped when the pass ends before it; inside the last one, lanes past
     // the end re-read the pass's last chunk (in bounds) and write it to LDS
     // slots nobody reads.  No per-lane exec masking in the streaming loop.
-    uint4 next[kQ8Chunks];
+    uint4 next[CH];
     auto fetch = [&](int64_t p) {
         const int nch = static_cast<int>(min<int64_t>(S, n - p * S)) * row_bytes / 16;
         const uint4 *src = reinterpret_cast<const uint4 *>(b + p * S * row_bytes);
 #pragma unroll
-        for (int u = 0; u < kQ8Chunks; ++u)
+        for (int u = 0; u < CH; ++u)
             if (u * kWave < nch) next[u] = load_nt16(src + min(u * kWave + lane, nch - 1));
     };
 
@@ -213,7 +282,7 @@ __global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a
         const int nch = rows * row_bytes / 16;
         __syncthreads();  // the previous pass is fully read from LDS
 #pragma unroll
-        for (int u = 0; u < kQ8Chunks; ++u)
+        for (int u = 0; u < CH; ++u)
             if (u * kWave < nch) stage4[u * kWave + lane] = next[u];
         __syncthreads();
         if (p + gridDim.x < passes) fetch(p + gridDim.x);  // in flight during the decode below
@@ -229,7 +298,7 @@ __global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a
 #pragma unroll
             for (int t = 0; t < J; ++t) {
                 const int j = jl + LPR * t;
-                const float d = q8_block_dot(stage, srow * row_bytes + kQ8BlockBytes * min(j, nb - 1), av[t]);
+                const float d = block_dot<FMT>(stage, srow * row_bytes + BB * min(j, nb - 1), av[t]);
                 acc[sl] += (j < nb) ? d : 0.f;
             }
             if (srow >= rows) acc[sl] = 0.f;
@@ -246,25 +315,38 @@ __global__ __launch_bounds__(64) void gemv_q8_staged(const float *__restrict__ a
 
 // Any K % 32 == 0 and 2-byte aligned b: one wave per row, lanes stride over
 // blocks, reading each block with 2-byte loads.
-__global__ __launch_bounds__(256) void gemv_q8_any(const float *__restrict__ a,
-                                                   const uint8_t *__restrict__ b,
-                                                   float *__restrict__ c, int64_t n, int64_t k) {
+template <int FMT>
+__global__ __launch_bounds__(256) void gemv_q_any(const float *__restrict__ a, const uint8_t *__restrict__ b,
+                                                  float *__restrict__ c, int64_t n, int64_t k) {
+    constexpr int BB = QB<FMT>::kBytes;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
     const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) / kWave;
     const int64_t nb = k >> 5;
     for (int64_t row = wave; row < n; row += nwaves) {
-        const uint8_t *brow = b + row * nb * kQ8BlockBytes;
+        const uint8_t *brow = b + row * nb * BB;
         float acc = 0.f;
         for (int64_t j = lane; j < nb; j += kWave) {
-            const uint16_t *blk = reinterpret_cast<const uint16_t *>(brow + j * kQ8BlockBytes);
+            const uint16_t *blk = reinterpret_cast<const uint16_t *>(brow + j * BB);
             const float *aj = a + 32 * j;
             float sumq = 0.f;
+            if constexpr (FMT == QFMT_Q8_0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t two = blk[1 + i];
-                sumq = fmaf(static_cast<float>(static_cast<int8_t>(two & 0xffu)), aj[2 * i], sumq);
-                sumq = fmaf(static_cast<float>(static_cast<int8_t>(two >> 8)), aj[2 * i + 1], sumq);
+                for (int i = 0; i < 16; ++i) {
+                    const uint32_t two = blk[1 + i];
+                    sumq = fmaf(static_cast<float>(static_cast<int8_t>(two & 0xffu)), aj[2 * i], sumq);
+                    sumq = fmaf(static_cast<float>(static_cast<int8_t>(two >> 8)), aj[2 * i + 1], sumq);
+                }
+            } else {
+                // u16 i holds code bytes 2i (weights 4i, 4i+1) and 2i+1 (4i+2, 4i+3)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t two = blk[1 + i];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        sumq = fmaf(static_cast<float>(static_cast<int>((two >> (4 * t)) & 0xfu) - 8), aj[4 * i + t],
+                                    sumq);
+                }
             }
             acc = fmaf(half_bits_to_float(blk[0]), sumq, acc);
         }
@@ -303,40 +385,81 @@ hipError_t run_f16_vec(const float *a, const uint16_t *b, float *c, int64_t n, i
     return hipGetLastError();
 }
 
-template <int J, int LPR, int SL>
-hipError_t run_q8_staged_sl(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
-                            int cus) {
+template <int FMT, int J, int LPR, int SL>
+hipError_t run_q_staged_sl(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
+                           int cus) {
     constexpr int S = SL * (kWave / LPR);
-    const int row_bytes = static_cast<int>((k >> 5) * kQ8BlockBytes);
+    const int row_bytes = static_cast<int>((k >> 5) * QB<FMT>::kBytes);
     const int64_t passes = (n + S - 1) / S;
     // 8 waves per CU (LDS stages of 9 fill a CU): measured best on MI355X.
     const int64_t blocks = balanced_workers(passes, static_cast<int64_t>(cus) * 8);
     const size_t lds = (static_cast<size_t>(S) * row_bytes + 1023) / 1024 * 1024;  // whole 1 KiB writes
     if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_q8_staged<J=%d,LPR=%d,SL=%d> n=%lld k=%lld S=%d grid=%lld block=64 lds=%zu\n",
-                J, LPR, SL, (long long)n, (long long)k, S, (long long)blocks, lds);
-    hipLaunchKernelGGL((gemv_q8_staged<J, LPR, SL>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k, passes);
+        fprintf(stderr,
+                "[wqmm] gemv_q_staged<fmt=%d,J=%d,LPR=%d,SL=%d> n=%lld k=%lld S=%d grid=%lld block=64 lds=%zu\n",
+                FMT, J, LPR, SL, (long long)n, (long long)k, S, (long long)blocks, lds);
+    hipLaunchKernelGGL((gemv_q_staged<FMT, J, LPR, SL>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k, passes);
     return hipGetLastError();
 }
 
-// Rows per pass: as many as fit the stage (S * row_bytes <= kQ8StageTarget),
-// but few enough that a small matrix still gives every CU about four waves
-// (a wave decodes its rows after its loads land); SL is a power of two.
-template <int J, int LPR>
-hipError_t run_q8_staged(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
-                         int cus) {
+// Rows per pass: as many as fit the stage (S * row_bytes <= kStage), but few
+// enough that a small matrix still gives every CU about four waves (a wave
+// decodes its rows after its loads land); SL is a power of two.
+template <int FMT, int J, int LPR>
+hipError_t run_q_staged(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
+                        int cus) {
     constexpr int RPL = kWave / LPR;
-    const int row_bytes = static_cast<int>((k >> 5) * kQ8BlockBytes);
-    const int64_t s_fit = kQ8StageTarget / row_bytes;
+    const int row_bytes = static_cast<int>((k >> 5) * QB<FMT>::kBytes);
+    const int64_t s_fit = QB<FMT>::kStage / row_bytes;
     const int64_t s_fill = std::max<int64_t>(1, n / (4LL * cus));
     const int64_t sl_max = std::max<int64_t>(1, std::min(s_fit, s_fill) / RPL);
+    if constexpr (FMT == QFMT_Q4_0 && J <= 1)
+        if (sl_max >= 16 && 16 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 16>(a, b, c, n, k, s, cus);
     if constexpr (J <= 1)
-        if (sl_max >= 8 && 8 * RPL <= s_fit) return run_q8_staged_sl<J, LPR, 8>(a, b, c, n, k, s, cus);
+        if (sl_max >= 8 && 8 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 8>(a, b, c, n, k, s, cus);
     if constexpr (J <= 2)
-        if (sl_max >= 4 && 4 * RPL <= s_fit) return run_q8_staged_sl<J, LPR, 4>(a, b, c, n, k, s, cus);
+        if (sl_max >= 4 && 4 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 4>(a, b, c, n, k, s, cus);
     if constexpr (J <= 4)
-        if (sl_max >= 2 && 2 * RPL <= s_fit) return run_q8_staged_sl<J, LPR, 2>(a, b, c, n, k, s, cus);
-    return run_q8_staged_sl<J, LPR, 1>(a, b, c, n, k, s, cus);
+        if (sl_max >= 2 && 2 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 2>(a, b, c, n, k, s, cus);
+    return run_q_staged_sl<FMT, J, LPR, 1>(a, b, c, n, k, s, cus);
+}
+
+// Staged kernel when K % 256 == 0, a and b are 16-byte aligned and a row fits
+// the stage with at most 8 blocks per lane; otherwise the plain kernel.
+template <int FMT>
+hipError_t launch_gemv_q(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s) {
+    DeviceInfo di;
+    hipError_t e = device_info(&di);
+    if (e != hipSuccess) return e;
+    const int64_t nb = k / 32;
+    const int64_t row_bytes = nb * QB<FMT>::kBytes;
+    if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= QB<FMT>::kStage && nb <= 512) {
+        if (nb >= 64) {
+            switch ((nb + 63) / 64) {
+                case 1: return run_q_staged<FMT, 1, 64>(a, b, c, n, k, s, di.cus);
+                case 2: return run_q_staged<FMT, 2, 64>(a, b, c, n, k, s, di.cus);
+                case 3: return run_q_staged<FMT, 3, 64>(a, b, c, n, k, s, di.cus);
+                case 4: return run_q_staged<FMT, 4, 64>(a, b, c, n, k, s, di.cus);
+                case 5: return run_q_staged<FMT, 5, 64>(a, b, c, n, k, s, di.cus);
+                case 6: return run_q_staged<FMT, 6, 64>(a, b, c, n, k, s, di.cus);
+                case 7: return run_q_staged<FMT, 7, 64>(a, b, c, n, k, s, di.cus);
+                default: return run_q_staged<FMT, 8, 64>(a, b, c, n, k, s, di.cus);
+            }
+        } else if (nb >= 32) {
+            if (nb == 32) return run_q_staged<FMT, 1, 32>(a, b, c, n, k, s, di.cus);
+            return run_q_staged<FMT, 2, 32>(a, b, c, n, k, s, di.cus);
+        } else {
+            if (nb <= 16) return run_q_staged<FMT, 1, 16>(a, b, c, n, k, s, di.cus);
+            return run_q_staged<FMT, 2, 16>(a, b, c, n, k, s, di.cus);
+        }
+    }
+    const int64_t waves = balanced_workers(n, static_cast<int64_t>(di.cus) * 16);
+    const int64_t blocks = (waves + 3) / 4;
+    if (trace_enabled())
+        fprintf(stderr, "[wqmm] gemv_q_any<fmt=%d> n=%lld k=%lld grid=%lld block=256\n", FMT, (long long)n,
+                (long long)k, (long long)blocks);
+    hipLaunchKernelGGL((gemv_q_any<FMT>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -369,40 +492,12 @@ hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t 
 
 hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
                             hipStream_t s) {
-    DeviceInfo di;
-    hipError_t e = device_info(&di);
-    if (e != hipSuccess) return e;
-    const int64_t nb = k / 32;
-    const int64_t row_bytes = nb * kQ8BlockBytes;
-    if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= kQ8StageTarget) {  // 17 chunks per lane
-        if (nb >= 64) {
-            const int64_t J = (nb + 63) / 64;
-            switch (J) {
-                case 1: return run_q8_staged<1, 64>(a, b, c, n, k, s, di.cus);
-                case 2: return run_q8_staged<2, 64>(a, b, c, n, k, s, di.cus);
-                case 3: return run_q8_staged<3, 64>(a, b, c, n, k, s, di.cus);
-                case 4: return run_q8_staged<4, 64>(a, b, c, n, k, s, di.cus);
-                case 5: return run_q8_staged<5, 64>(a, b, c, n, k, s, di.cus);
-                case 6: return run_q8_staged<6, 64>(a, b, c, n, k, s, di.cus);
-                case 7: return run_q8_staged<7, 64>(a, b, c, n, k, s, di.cus);
-                case 8: return run_q8_staged<8, 64>(a, b, c, n, k, s, di.cus);
-                default: break;
-            }
-        } else if (nb >= 32) {
-            if (nb == 32) return run_q8_staged<1, 32>(a, b, c, n, k, s, di.cus);
-            return run_q8_staged<2, 32>(a, b, c, n, k, s, di.cus);
-        } else {
-            if (nb <= 16) return run_q8_staged<1, 16>(a, b, c, n, k, s, di.cus);
-            return run_q8_staged<2, 16>(a, b, c, n, k, s, di.cus);
-        }
-    }
-    const int64_t waves = balanced_workers(n, static_cast<int64_t>(di.cus) * 16);
-    const int64_t blocks = (waves + 3) / 4;
-    if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_q8_any n=%lld k=%lld grid=%lld block=256\n", (long long)n, (long long)k,
-                (long long)blocks);
-    hipLaunchKernelGGL(gemv_q8_any, dim3(blocks), dim3(256), 0, s, a, b, c, n, k);
-    return hipGetLastError();
+    return launch_gemv_q<QFMT_Q8_0>(a, b, c, n, k, s);
+}
+
+hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
+                            hipStream_t s) {
+    return launch_gemv_q<QFMT_Q4_0>(a, b, c, n, k, s);
 }
 
 }  // namespace wq

@@ -1,5 +1,5 @@
-// Small-M product (2 <= M <= 16): C[M,N] = A[M,K] . B[N,K]^T with f16 or
-// Q8_0 weights, streamed once from HBM through the fp32 matrix cores.
+// Small-M product (2 <= M <= 16): C[M,N] = A[M,K] . B[N,K]^T with f16, Q8_0
+// or Q4_0 weights, streamed once from HBM through the fp32 matrix cores.
 //
 // Operation: the M > 1 branch of dispatch_gemm_q8 (lattice-inference 0.9.0,
 // dispatch.rs); its multi-row GEMV prior art is the kernel gemm_q8 (a few
@@ -50,7 +50,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQ8BlockBytes = 34;
-enum { FMT_F16 = 0, FMT_Q8_0 = 1 };
+constexpr int kQ4BlockBytes = 18;
+enum { FMT_F16 = 0, FMT_Q8_0 = 1, FMT_Q4_0 = 2 };
 
 // Buffer resource over [p, p + bytes) (bytes capped at 4 GiB - 1): raw,
 // untyped (stride 0), third dword as for every gfx9 target.
@@ -66,23 +67,27 @@ __device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ u32x2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, kStream);
 }
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, kStream));
+}
 __device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, kStream));
 }
 
 template <int FMT, int MB, int NT, int E, bool VEC>
 struct Skinny {
-    static constexpr int KS = 16 * E;                          // columns per step
-    static constexpr int WD = FMT == FMT_F16 ? E / 2 : E / 4;  // weight dwords per lane and tile
+    static constexpr int KS = 16 * E;  // columns per step
+    static constexpr int WD = FMT == FMT_F16 ? E / 2 : FMT == FMT_Q8_0 ? E / 4 : E / 8;  // weight dwords
     static_assert(E == 8 || E == 16 || E == 32, "chunk");
+    static constexpr int QBB = FMT == FMT_Q4_0 ? kQ4BlockBytes : kQ8BlockBytes;
     // Bytes one step advances along a weight row / an activation row.
-    static constexpr uint32_t kWStep = FMT == FMT_F16 ? 2 * KS : KS / 32 * kQ8BlockBytes;
+    static constexpr uint32_t kWStep = FMT == FMT_F16 ? 2 * KS : KS / 32 * QBB;
     static constexpr uint32_t kAStep = 4 * KS;
 
     struct Regs {
         float a[MB][E];
         uint32_t w[NT][WD];
-        uint32_t d[FMT == FMT_Q8_0 ? NT : 1];
+        uint32_t d[FMT != FMT_F16 ? NT : 1];
     };
 
     // Per-lane byte offsets, fixed for the whole K loop.  Lane (b, c) reads
@@ -92,7 +97,7 @@ struct Skinny {
     struct Lane {
         uint32_t a[MB];  // into A
         uint32_t w[NT];  // into the tiles: f16 chunk, or Q8_0 codes
-        uint32_t d[NT];  // Q8_0 scale of the lane's block
+        uint32_t d[NT];  // offset of the scale of the lane's block (Q8_0, Q4_0)
         int b, c;
     };
 
@@ -103,7 +108,7 @@ struct Skinny {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
             L.a[mb] = static_cast<uint32_t>((min<int64_t>(4 * mb + L.c, M - 1) * K + E * L.b) * 4);
-        const uint64_t row_bytes = FMT == FMT_F16 ? 2ull * K : static_cast<uint64_t>(K >> 5) * kQ8BlockBytes;
+        const uint64_t row_bytes = FMT == FMT_F16 ? 2ull * K : static_cast<uint64_t>(K >> 5) * QBB;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const uint64_t rb = static_cast<uint64_t>(4 * t + L.c) * row_bytes;
@@ -111,9 +116,11 @@ struct Skinny {
                 L.w[t] = static_cast<uint32_t>(rb + 2 * E * L.b);
                 L.d[t] = 0;
             } else {
+                // The lane's E columns start at code index off of block blk:
+                // byte 2 + off (Q8_0) or 2 + off / 2 (Q4_0, two codes a byte).
                 const int blk = (E * L.b) >> 5, off = (E * L.b) & 31;
-                L.d[t] = static_cast<uint32_t>(rb + blk * kQ8BlockBytes);
-                L.w[t] = L.d[t] + 2 + off;
+                L.d[t] = static_cast<uint32_t>(rb + blk * QBB);
+                L.w[t] = L.d[t] + 2 + (FMT == FMT_Q8_0 ? off : off / 2);
             }
         }
         return L;
@@ -169,15 +176,18 @@ struct Skinny {
                 }
             }
         } else {
+            // WD dwords of codes: 4 (Q8_0) or 8 (Q4_0) weights per dword.
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 r.d[t] = bload2(rw, L.d[t]);
-                if constexpr (E == 8) {
+                if constexpr (WD == 1) {
+                    r.w[t][0] = bload4(rw, L.w[t]);
+                } else if constexpr (WD == 2) {
                     const u32x2 v = bload8(rw, L.w[t]);
                     r.w[t][0] = v[0], r.w[t][1] = v[1];
                 } else {
 #pragma unroll
-                    for (int q = 0; q < E / 16; ++q) {
+                    for (int q = 0; q < WD / 4; ++q) {
                         const u32x4 v = bload16(rw, L.w[t] + 16 * q);
 #pragma unroll
                         for (int u = 0; u < 4; ++u) r.w[t][4 * q + u] = v[u];
@@ -192,10 +202,15 @@ struct Skinny {
         if constexpr (FMT == FMT_F16) {
             const uint32_t w = r.w[t][e / 2];
             return half_bits_to_float((e & 1) ? (w >> 16) : (w & 0xffffu));
-        } else {
+        } else if constexpr (FMT == FMT_Q8_0) {
             const uint32_t w = r.w[t][e / 4];
             const int8_t q = static_cast<int8_t>((w >> (8 * (e & 3))) & 0xffu);
             return half_bits_to_float(r.d[t]) * static_cast<float>(q);
+        } else {
+            // Code byte j holds column 2j (low nibble) and 2j + 1 (high).
+            const uint32_t w = r.w[t][e / 8];
+            const int u = static_cast<int>((w >> (4 * (e & 7))) & 0xfu);
+            return half_bits_to_float(r.d[t]) * static_cast<float>(u - 8);
         }
     }
 
@@ -255,7 +270,7 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const float *__restrict__ 
     const int s0 = sp * sps, s1 = min(nsteps, s0 + sps);
 
     const typename S::Lane L = S::lane_offsets(lane, M, K);
-    const uint64_t row_bytes = FMT == FMT_F16 ? 2ull * K : static_cast<uint64_t>(K >> 5) * kQ8BlockBytes;
+    const uint64_t row_bytes = FMT == FMT_F16 ? 2ull * K : static_cast<uint64_t>(K >> 5) * S::QBB;
     const uint8_t *wbase = static_cast<const uint8_t *>(bw) + n0 * row_bytes;
     const uint64_t wbytes = (N - n0) * row_bytes;  // from the workgroup's first row to the end
     const uint64_t abytes = static_cast<uint64_t>(M) * K * 4;
@@ -342,6 +357,10 @@ template <>
 struct SkCfg<FMT_Q8_0, 1> {
     static constexpr int NT = 2, E = 16, P = 2;
 };
+template <>
+struct SkCfg<FMT_Q4_0, 1> {
+    static constexpr int NT = 2, E = 16, P = 2;
+};
 constexpr int kSkW = 4;
 constexpr int kSkWavesPerCU = 8;
 
@@ -423,6 +442,7 @@ hipError_t launch_skinny(const float *a, const void *b, int fmt, float *c, int64
         const bool vec = a16 && (reinterpret_cast<uintptr_t>(b) & 15) == 0 && k % 8 == 0;
         return run_fmt<FMT_F16>(a, b, c, m, n, k, vec, di.cus, s);
     }
+    if (fmt == FMT_Q4_0) return run_fmt<FMT_Q4_0>(a, b, c, m, n, k, a16, di.cus, s);
     return run_fmt<FMT_Q8_0>(a, b, c, m, n, k, a16, di.cus, s);
 }
 

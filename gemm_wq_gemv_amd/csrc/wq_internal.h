@@ -98,6 +98,8 @@ hipError_t device_info(DeviceInfo *out);
 // pick a kernel variant and grid and enqueue it on `s`.
 hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
                            hipStream_t s);
+hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
+                            hipStream_t s);
 hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
                             hipStream_t s);
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,

@@ -140,19 +140,21 @@ bool overlaps(const void *p, int64_t pbytes, const void *q, int64_t qbytes) {
 
 bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
 
+bool known_format(int fmt) { return fmt == WQ_FMT_F16 || fmt == WQ_FMT_Q8_0 || fmt == WQ_FMT_Q4_0; }
+
 // Validates a product call.  Returns WQ_OK with *noop = true when nothing is
 // to be done (m == 0 or n == 0), WQ_OK with *noop = false when a launch
 // follows, or an error status.
 int validate(const float *a, const void *b, const float *c, int64_t m, int64_t n, int64_t k, int fmt,
              bool *noop) {
     *noop = false;
-    if (fmt != WQ_FMT_F16 && fmt != WQ_FMT_Q8_0) return WQ_ERR_FORMAT;
+    if (!known_format(fmt)) return WQ_ERR_FORMAT;
     if (m < 0 || n < 0 || k < 0) return WQ_ERR_SHAPE;
     if (m == 0 || n == 0) {
         *noop = true;
         return WQ_OK;
     }
-    if (fmt == WQ_FMT_Q8_0 && (k == 0 || k % 32 != 0)) return WQ_ERR_K;
+    if (fmt != WQ_FMT_F16 && (k == 0 || k % 32 != 0)) return WQ_ERR_K;
     int64_t a_elems, c_elems, b_bytes, a_bytes, c_bytes;
     if (!mul_ok(m, k, &a_elems) || !mul_ok(a_elems, 4, &a_bytes)) return WQ_ERR_SHAPE;
     if (!mul_ok(m, n, &c_elems) || !mul_ok(c_elems, 4, &c_bytes)) return WQ_ERR_SHAPE;
@@ -160,7 +162,7 @@ int validate(const float *a, const void *b, const float *c, int64_t m, int64_t n
         int64_t nk;
         if (!mul_ok(n, k, &nk) || !mul_ok(nk, 2, &b_bytes)) return WQ_ERR_SHAPE;
     } else {
-        if (!mul_ok(n, (k / 32) * 34, &b_bytes)) return WQ_ERR_SHAPE;
+        if (!mul_ok(n, (k / 32) * (fmt == WQ_FMT_Q8_0 ? 34 : 18), &b_bytes)) return WQ_ERR_SHAPE;
     }
     if (!c) return WQ_ERR_NULL;
     if (k > 0 && (!a || !b)) return WQ_ERR_NULL;
@@ -177,7 +179,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_LAUNCH; }
 constexpr int64_t kSkinnyRows = 16;  // rows of A per small-M launch
 int auto_route(int64_t m, int fmt) {
     if (m <= 1) return WQ_ROUTE_GEMV;
-    return m <= (fmt == WQ_FMT_F16 ? 8 : 4) ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;
+    return m <= (fmt == WQ_FMT_F16 ? 8 : 4) ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;  // Q4_0 as Q8_0
 }
 bool known_route(int r) { return r == WQ_ROUTE_GEMV || r == WQ_ROUTE_GEMM || r == WQ_ROUTE_SKINNY; }
 
@@ -186,9 +188,9 @@ int run_gemv(const float *a, const void *b, float *c, int64_t m, int64_t n, int6
     for (int64_t i = 0; i < m; ++i) {
         const float *ai = a + i * k;
         float *ci = c + i * n;
-        hipError_t e = (fmt == WQ_FMT_F16)
-                           ? wq::launch_gemv_f16(ai, static_cast<const uint16_t *>(b), ci, n, k, s)
-                           : wq::launch_gemv_q8_0(ai, static_cast<const uint8_t *>(b), ci, n, k, s);
+        hipError_t e = (fmt == WQ_FMT_F16)    ? wq::launch_gemv_f16(ai, static_cast<const uint16_t *>(b), ci, n, k, s)
+                       : (fmt == WQ_FMT_Q8_0) ? wq::launch_gemv_q8_0(ai, static_cast<const uint8_t *>(b), ci, n, k, s)
+                                              : wq::launch_gemv_q4_0(ai, static_cast<const uint8_t *>(b), ci, n, k, s);
         if (e != hipSuccess) return WQ_ERR_LAUNCH;
         wq::g_route_count[WQ_ROUTE_GEMV].fetch_add(1, std::memory_order_relaxed);
     }
@@ -222,7 +224,7 @@ int run_zero(float *c, int64_t m, int64_t n, hipStream_t s) {
 
 extern "C" {
 
-int wq_abi_version(void) { return 100; }
+int wq_abi_version(void) { return 101; }
 
 const char *wq_status_str(int status) {
     switch (status) {
@@ -255,6 +257,13 @@ int wq_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t 
     return run_gemv(a, b, c, 1, n, k, WQ_FMT_Q8_0, static_cast<hipStream_t>(stream));
 }
 
+int wq_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, void *stream) {
+    bool noop;
+    int st = validate(a, b, c, 1, n, k, WQ_FMT_Q4_0, &noop);
+    if (st != WQ_OK || noop) return st;
+    return run_gemv(a, b, c, 1, n, k, WQ_FMT_Q4_0, static_cast<hipStream_t>(stream));
+}
+
 int wq_gemm_f16(const float *a, const uint16_t *b, float *c, int64_t m, int64_t n, int64_t k, void *stream) {
     bool noop;
     int st = validate(a, b, c, m, n, k, WQ_FMT_F16, &noop);
@@ -269,6 +278,13 @@ int wq_gemm_q8_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t 
     int st = validate(a, b, c, m, n, k, WQ_FMT_Q8_0, &noop);
     if (st != WQ_OK || noop) return st;
     return run_gemm(a, b, c, m, n, k, WQ_FMT_Q8_0, static_cast<hipStream_t>(stream));
+}
+
+int wq_gemm_q4_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t n, int64_t k, void *stream) {
+    bool noop;
+    int st = validate(a, b, c, m, n, k, WQ_FMT_Q4_0, &noop);
+    if (st != WQ_OK || noop) return st;
+    return run_gemm(a, b, c, m, n, k, WQ_FMT_Q4_0, static_cast<hipStream_t>(stream));
 }
 
 int wq_matmul(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, void *stream) {
@@ -306,16 +322,16 @@ int wq_quantize_q8_0(const float *w, uint8_t *out, int64_t count, void *stream) 
 }
 
 int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt) {
-    if (fmt != WQ_FMT_F16 && fmt != WQ_FMT_Q8_0) return -WQ_ERR_FORMAT;
+    if (!known_format(fmt)) return -WQ_ERR_FORMAT;
     if (m < 0 || n < 0 || k < 0) return -WQ_ERR_SHAPE;
-    if (fmt == WQ_FMT_Q8_0 && m > 0 && n > 0 && (k == 0 || k % 32 != 0)) return -WQ_ERR_K;
+    if (fmt != WQ_FMT_F16 && m > 0 && n > 0 && (k == 0 || k % 32 != 0)) return -WQ_ERR_K;
     return auto_route(m, fmt);
 }
 
 int wq_gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits) {
-    if (fmt != WQ_FMT_F16 && fmt != WQ_FMT_Q8_0) return WQ_ERR_FORMAT;
+    if (!known_format(fmt)) return WQ_ERR_FORMAT;
     if (m <= 0 || n <= 0 || k <= 0 || cus <= 0) return WQ_ERR_SHAPE;
-    if (fmt == WQ_FMT_Q8_0 && k % 32 != 0) return WQ_ERR_K;
+    if (fmt != WQ_FMT_F16 && k % 32 != 0) return WQ_ERR_K;
     if (!bm || !bn || !splits) return WQ_ERR_NULL;
     wq::gemm_plan(m, n, k, fmt, cus, bm, bn, splits);
     return WQ_OK;

@@ -12,7 +12,9 @@
  * GEMV, M > 1 the tiled GEMM; m == 0 or n == 0 is a no-op; K must be a
  * non-zero multiple of 32).  Formats: lattice-inference 0.1.2,
  * forward/metal_qwen35.rs -- kernel gemv_q8_decode (block = f16 scale, then
- * 32 int8), quantize_row_q8_0, f32_to_f16.  The same product as
+ * 32 int8), quantize_row_q8_0, f32_to_f16; kernels gemv_q4_decode, gemm_q4
+ * and gemm_q4_tiled (Q4_0 block = f16 scale, then 16 bytes of 4-bit codes;
+ * dispatch_gemm_q4 on the 0.9.0 page routes M as for Q8_0).  The same product as
  * sgemm(RowMajor, NoTrans, Trans, alpha = 1, beta = 0): ferrum-kernels
  * 0.7.7, attention/metal/pipelines.rs, MetalPipelines::gemm.
  *
@@ -22,10 +24,14 @@
  *      or Q8_0 bytes [N, K/32 * 34]       row n starts at byte n*(K/32)*34;
  *         block j of the row at +34*j: bytes 0..1 a little-endian f16 scale d,
  *         bytes 2..33 int8 codes q; weight (n, 32*j + i) = d * q[i]
+ *      or Q4_0 bytes [N, K/32 * 18]       row n starts at byte n*(K/32)*18;
+ *         block j at +18*j: bytes 0..1 the little-endian f16 scale d, byte
+ *         2 + i holds code u of weight 2i (low nibble) and of weight 2i + 1
+ *         (high nibble); weight = (u - 8) * d
  *   c  f32 [M, N]                         ldc = N
  * Accumulation is in f32; the summation order is unspecified, so results may
  * differ from a serial f32 sum by rounding only.  The weight decode itself is
- * exact (f16 -> f32 widening, d * q is exact in f32).
+ * exact (f16 -> f32 widening; d * q and (u - 8) * d are exact in f32).
  *
  * Pointers: a, b, c (and w, out of the packing calls) are DEVICE pointers on
  * the current HIP device.  The caller owns all memory; the library never
@@ -43,7 +49,7 @@
  * must be 4-byte aligned, b 2-byte aligned.  c must not overlap a or b.
  * m == 0 or n == 0 returns WQ_OK without touching any pointer.  For f16,
  * K == 0 is allowed and writes zeros to c (the empty sum); a and b may then be
- * NULL.  Q8_0 needs K > 0 and K % 32 == 0.
+ * NULL.  Q8_0 and Q4_0 need K > 0 and K % 32 == 0.
  */
 #ifndef WQMM_H
 #define WQMM_H
@@ -57,7 +63,8 @@ extern "C" {
 /* Weight storage formats (the pages' QuantFormat plus their f16 weights). */
 typedef enum wq_format {
     WQ_FMT_F16 = 0,  /* IEEE-754 binary16 bit patterns */
-    WQ_FMT_Q8_0 = 1  /* 34-byte Q8_0 blocks of 32 weights */
+    WQ_FMT_Q8_0 = 1, /* 34-byte Q8_0 blocks of 32 weights */
+    WQ_FMT_Q4_0 = 2  /* 18-byte Q4_0 blocks of 32 weights */
 } wq_format;
 
 /* Status codes returned by every entry point. */
@@ -65,7 +72,7 @@ typedef enum wq_status {
     WQ_OK = 0,
     WQ_ERR_NULL = 1,    /* a required pointer is NULL */
     WQ_ERR_SHAPE = 2,   /* negative dimension, or a byte count overflows int64 */
-    WQ_ERR_K = 3,       /* Q8_0 with K == 0 or K % 32 != 0 */
+    WQ_ERR_K = 3,       /* Q8_0 / Q4_0 with K == 0 or K % 32 != 0 */
     WQ_ERR_FORMAT = 4,  /* fmt is not a wq_format */
     WQ_ERR_ALIGN = 5,   /* a or c not 4-byte aligned, or b not 2-byte aligned */
     WQ_ERR_LAUNCH = 6,  /* the HIP runtime failed to enqueue a kernel or scratch */
@@ -85,11 +92,13 @@ typedef enum wq_route {
 /* ---------------------------------------------------------------------- */
 /* Decode GEMV, M = 1: c[n] = sum_k a[k] * w[n, k].  a is f32 [K], c f32 [N].
  * The weights stream from HBM once; a is held on chip.  Passage: kernel
- * gemv_decode_m1 (f16) and gemv_q8_decode (Q8_0), lattice-inference 0.1.2
- * metal_qwen35.rs; dispatch_matmul_half / dispatch_matmul_q8, lattice-inference
- * 0.9.0 dispatch.rs.  There is no m argument: a GEMV computes one row. */
+ * gemv_decode_m1 (f16), gemv_q8_decode (Q8_0) and gemv_q4_decode (Q4_0),
+ * lattice-inference 0.1.2 metal_qwen35.rs; dispatch_matmul_half /
+ * dispatch_matmul_q8 / dispatch_matmul_q4, lattice-inference 0.9.0
+ * dispatch.rs.  There is no m argument: a GEMV computes one row. */
 int wq_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k, void *stream);
 int wq_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, void *stream);
+int wq_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, void *stream);
 
 /* Prefill GEMM, any M >= 1: C = A . B^T through LDS tiles of A and of the
  * dequantised B, with fp32 matrix-core (MFMA) accumulation.  Passage: kernels
@@ -99,9 +108,11 @@ int wq_gemm_f16(const float *a, const uint16_t *b, float *c, int64_t m, int64_t 
                 void *stream);
 int wq_gemm_q8_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t n, int64_t k,
                  void *stream);
+int wq_gemm_q4_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t n, int64_t k,
+                 void *stream);
 
 /* M-routed product for either format (fmt is a wq_format).  M == 1 takes the
- * GEMV; 2 <= M <= 8 (f16) or 2 <= M <= 4 (Q8_0) the small-M weight-streaming
+ * GEMV; 2 <= M <= 8 (f16) or 2 <= M <= 4 (Q8_0, Q4_0) the small-M weight-streaming
  * kernel; larger M the tiled GEMM, unless a route is forced
  * (wq_set_forced_route).  The small-M kernel reads every weight once per 16
  * rows of A with fp32 matrix-core accumulation; when it splits K it uses the

@@ -27,8 +27,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for want in ("wq_gemv_f16", "wq_gemv_q8_0", "wq_gemm_f16", "wq_gemm_q8_0", "wq_matmul",
-                 "wq_pack_f16", "wq_quantize_q8_0"):
+    for want in ("wq_gemv_f16", "wq_gemv_q8_0", "wq_gemv_q4_0", "wq_gemm_f16", "wq_gemm_q8_0",
+                 "wq_gemm_q4_0", "wq_matmul", "wq_pack_f16", "wq_quantize_q8_0"):
         assert want in names
 
 
@@ -50,13 +50,13 @@ def test_single_hip_runtime_in_process():
 
 
 def test_abi_and_status_strings():
-    assert wq.wq_abi_version() == 100
+    assert wq.wq_abi_version() == 101
     for st in range(0, 9):
         assert wq.status_str(st)
     assert wq.status_str(99) == "unknown status"
 
 
-@pytest.mark.parametrize("fmt", [wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0])
+@pytest.mark.parametrize("fmt", [wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0])
 def test_empty_outputs_are_noops(fmt):
     # m == 0 or n == 0: nothing to do, pointers are not even looked at.
     assert L.wq_matmul(None, None, None, 0, 16, 64, fmt, None) == wq.WQ_OK
@@ -65,11 +65,14 @@ def test_empty_outputs_are_noops(fmt):
     assert L.wq_gemv_q8_0(None, None, None, 0, 33, None) == wq.WQ_OK  # n == 0 first, as on the page
 
 
-def test_q8_k_rules():
+def test_q8_and_q4_k_rules():
     for k in (0, 16, 33, 48, 1000):
         assert L.wq_gemv_q8_0(A, B, C, 8, k, None) == wq.WQ_ERR_K
         assert L.wq_gemm_q8_0(A, B, C, 2, 8, k, None) == wq.WQ_ERR_K
         assert L.wq_matmul(A, B, C, 2, 8, k, wq.WQ_FMT_Q8_0, None) == wq.WQ_ERR_K
+        assert L.wq_gemv_q4_0(A, B, C, 8, k, None) == wq.WQ_ERR_K
+        assert L.wq_gemm_q4_0(A, B, C, 2, 8, k, None) == wq.WQ_ERR_K
+        assert L.wq_matmul(A, B, C, 2, 8, k, wq.WQ_FMT_Q4_0, None) == wq.WQ_ERR_K
     assert L.wq_quantize_q8_0(A, B, 33, None) == wq.WQ_ERR_K
 
 
@@ -78,7 +81,7 @@ def test_shape_format_null_align_alias():
     assert L.wq_matmul(A, B, C, 1, -8, 64, 0, None) == wq.WQ_ERR_SHAPE
     assert L.wq_matmul(A, B, C, 1, 8, -64, 0, None) == wq.WQ_ERR_SHAPE
     assert L.wq_matmul(A, B, C, 1 << 40, 1 << 40, 64, 0, None) == wq.WQ_ERR_SHAPE  # overflow
-    assert L.wq_matmul(A, B, C, 1, 8, 64, 2, None) == wq.WQ_ERR_FORMAT
+    assert L.wq_matmul(A, B, C, 1, 8, 64, 3, None) == wq.WQ_ERR_FORMAT
     assert L.wq_matmul(A, B, C, 1, 8, 64, -1, None) == wq.WQ_ERR_FORMAT
     assert L.wq_gemv_f16(None, B, C, 8, 64, None) == wq.WQ_ERR_NULL
     assert L.wq_gemv_f16(A, None, C, 8, 64, None) == wq.WQ_ERR_NULL
@@ -90,6 +93,9 @@ def test_shape_format_null_align_alias():
     # c overlapping a or b
     assert L.wq_gemv_f16(A, B, A + 64, 8, 64, None) == wq.WQ_ERR_ALIAS
     assert L.wq_gemm_q8_0(A, B, B + 4, 2, 8, 64, None) == wq.WQ_ERR_ALIAS
+    assert L.wq_gemv_q4_0(A, B + 1, C, 8, 64, None) == wq.WQ_ERR_ALIGN
+    # Q4_0 b spans n*(k/32)*18 = 288 bytes here: c starting inside it overlaps
+    assert L.wq_gemv_q4_0(A, B, B + 8 * 2 * 18 - 4, 8, 64, None) == wq.WQ_ERR_ALIAS
     assert L.wq_pack_f16(A, A + 8, 64, None) == wq.WQ_ERR_ALIAS
     assert L.wq_pack_f16(A, B, -1, None) == wq.WQ_ERR_SHAPE
     assert L.wq_pack_f16(A, B, 0, None) == wq.WQ_OK
@@ -98,7 +104,7 @@ def test_shape_format_null_align_alias():
 
 
 def test_routing_rule():
-    for fmt in (wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0):
+    for fmt in (wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0):
         assert wq.wq_route_for(1, 4096, 4096, fmt) == wq.WQ_ROUTE_GEMV
         top = 8 if fmt == wq.WQ_FMT_F16 else 4
         for m in range(2, top + 1):
@@ -106,6 +112,7 @@ def test_routing_rule():
         for m in (top + 1, 16, 17, 64, 512):
             assert wq.wq_route_for(m, 4096, 4096, fmt) == wq.WQ_ROUTE_GEMM
     assert wq.wq_route_for(2, 8, 33, wq.WQ_FMT_Q8_0) == -wq.WQ_ERR_K
+    assert wq.wq_route_for(2, 8, 48, wq.WQ_FMT_Q4_0) == -wq.WQ_ERR_K
     assert wq.wq_route_for(2, 8, 32, 5) == -wq.WQ_ERR_FORMAT
     assert wq.wq_route_for(-2, 8, 32, 0) == -wq.WQ_ERR_SHAPE
 

@@ -27,7 +27,8 @@ import wqgen
 
 pytestmark = pytest.mark.gpu
 
-F16, Q8 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0
+F16, Q8, Q4 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0
+ALL = [F16, Q8, Q4]
 DECODE_SHAPES = [(6144, 2048), (2048, 6144), (2048, 2048), (151936, 2048)]
 SWEEP_SHAPES = [(11008, 4096), (4096, 11008)]
 SWEEP_M = [1, 2, 4, 8, 16, 64, 512]
@@ -59,7 +60,13 @@ def acts(m, k, seed=0):
 
 @functools.lru_cache(maxsize=6)
 def encoded(n, k, fmt, seed=0):
-    """(oracle bytes, library bytes on the GPU) for the same f32 weights."""
+    """(oracle bytes, library bytes on the GPU) for the same f32 weights; for
+    Q4_0 (no encoder on the pages) the same synthetic bytes on both sides."""
+    if fmt == Q4:
+        raw = wqgen.q4_0_bytes(n, k, seed)
+        dev = torch.from_numpy(raw).cuda()
+        torch.cuda.synchronize()
+        return raw, dev
     w = weights_f32(n, k, seed)
     ref = oracle.encode(w, fmt)
     wd = torch.from_numpy(w).cuda()
@@ -71,10 +78,10 @@ def encoded(n, k, fmt, seed=0):
 
 def _entry(name, fmt):
     if name == "gemv":
-        f = wq.wq_gemv_f16 if fmt == F16 else wq.wq_gemv_q8_0
+        f = {F16: wq.wq_gemv_f16, Q8: wq.wq_gemv_q8_0, Q4: wq.wq_gemv_q4_0}[fmt]
         return lambda a, b, c, m, n, k: f(a, b, c, n, k)
     if name == "gemm":
-        f = wq.wq_gemm_f16 if fmt == F16 else wq.wq_gemm_q8_0
+        f = {F16: wq.wq_gemm_f16, Q8: wq.wq_gemm_q8_0, Q4: wq.wq_gemm_q4_0}[fmt]
         return lambda a, b, c, m, n, k: f(a, b, c, m, n, k)
     return lambda a, b, c, m, n, k: wq.wq_matmul(a, b, c, m, n, k, fmt)
 
@@ -183,7 +190,7 @@ def test_gemv_f16_1024():
     full_case("gemv", F16, 1, 1024, 1024)
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("nk", DECODE_SHAPES)
 def test_decode_suite(fmt, nk):
     """Decode GEMV at hidden 2048: gate/up, down, o_proj, LM head."""
@@ -197,14 +204,15 @@ def test_prefill_f16_m512(nk):
     sampled_case("matmul", F16, 512, n, k)
 
 
+@pytest.mark.parametrize("fmt", [Q8, Q4])
 @pytest.mark.parametrize("nk", SWEEP_SHAPES)
 @pytest.mark.parametrize("m", SWEEP_M)
-def test_q8_sweep(nk, m):
+def test_quant_sweep(fmt, nk, m):
     n, k = nk
     if m <= 16:
-        full_case("matmul", Q8, m, n, k)
+        full_case("matmul", fmt, m, n, k)
     else:
-        sampled_case("matmul", Q8, m, n, k)
+        sampled_case("matmul", fmt, m, n, k)
 
 
 # ---------------------------------------------------------- ragged / edges --
@@ -213,7 +221,7 @@ RAGGED = [(1, 1, 32), (1, 7, 96), (1, 129, 1056), (1, 1000, 4128), (1, 33, 256),
           (1, 300, 20480), (5, 4099, 256)]
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("mnk", RAGGED, ids=[f"{m}x{n}x{k}" for m, n, k in RAGGED])
 def test_ragged(fmt, mnk):
     m, n, k = mnk
@@ -230,7 +238,7 @@ def test_f16_any_k(mnk):
     full_case("gemm", F16, m, n, k, seed=2)
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("entry", ["gemv", "gemm", "matmul"])
 def test_misaligned_pointers(fmt, entry):
     """a offset by 4 bytes and b by 2 bytes from 16-byte alignment (wq_matmul
@@ -250,12 +258,12 @@ def test_misaligned_pointers(fmt, entry):
     s = torch.cuda.current_stream().cuda_stream
     bp = b_buf.data_ptr() + 2
     if entry == "gemv":
-        fn = L.wq_gemv_f16 if fmt == F16 else L.wq_gemv_q8_0
+        fn = {F16: L.wq_gemv_f16, Q8: L.wq_gemv_q8_0, Q4: L.wq_gemv_q4_0}[fmt]
         st = fn(a_buf.data_ptr() + 4, bp, c.data_ptr(), n, k, s)
     elif entry == "matmul":
         st = L.wq_matmul(a_buf.data_ptr() + 4, bp, c.data_ptr(), m, n, k, fmt, s)
     else:
-        fn = L.wq_gemm_f16 if fmt == F16 else L.wq_gemm_q8_0
+        fn = {F16: L.wq_gemm_f16, Q8: L.wq_gemm_q8_0, Q4: L.wq_gemm_q4_0}[fmt]
         st = fn(a_buf.data_ptr() + 4, bp, c.data_ptr(), m, n, k, s)
     assert st == wq.WQ_OK
     torch.cuda.synchronize()
@@ -263,7 +271,7 @@ def test_misaligned_pointers(fmt, entry):
     assert_close(c.cpu().numpy(), c_ref, bound, "misaligned")
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", ALL)
 def test_onehot_a_dequant_bit_exact(fmt):
     """a = e_j gives c[n] = w[n, j] exactly: the decode is bit-exact, through the
     GEMV and through the GEMM."""
@@ -283,7 +291,7 @@ def test_onehot_a_dequant_bit_exact(fmt):
         assert np.array_equal(c[i].astype(np.float64), w[:, j]), f"gemm column {j}"
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", ALL)
 def test_identity_a_gives_transposed_weights(fmt):
     """A = I (M = K) gives C = W^T exactly: checks the matrix-core lane layout
     and every tile edge of the GEMM."""
@@ -295,7 +303,7 @@ def test_identity_a_gives_transposed_weights(fmt):
         assert np.array_equal(c.astype(np.float64), w.T)
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", ALL)
 def test_empty_and_k0(fmt):
     say(f"empty outputs fmt={fmt}")
     c = torch.full((4, 8), float("nan"), device="cuda")
@@ -312,10 +320,10 @@ def test_empty_and_k0(fmt):
         assert (c == 0).all()
     else:
         with pytest.raises(wq.WQError):
-            wq.wq_matmul(a, b, c, 4, 8, 0, Q8)
+            wq.wq_matmul(a, b, c, 4, 8, 0, fmt)
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("m", [1, 7, 512])
 def test_deterministic_and_linear(fmt, m):
     """Repeated calls are bitwise identical; C(2A) = 2 C(A) and C(-A) = -C(A)."""
@@ -330,7 +338,7 @@ def test_deterministic_and_linear(fmt, m):
     assert np.array_equal(run_gpu("matmul", fmt, -a, dev_b, m, n, k), -c1)
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", ALL)
 def test_routes_agree_and_are_counted(fmt):
     """Every route gives the oracle's product for any M, and the path-proof
     counters show which kernels ran: the GEMV once per row of A, the GEMM once,
@@ -372,10 +380,11 @@ def test_nondefault_stream():
 
 
 SKINNY_SHAPES = {F16: [(1, 8), (37, 1000), (300, 2048), (4099, 136), (19, 33), (64, 1001)],
-                 Q8: [(1, 32), (37, 992), (300, 2080), (4099, 160), (64, 4096)]}
+                 Q8: [(1, 32), (37, 992), (300, 2080), (4099, 160), (64, 4096)],
+                 Q4: [(1, 32), (37, 992), (300, 2080), (4099, 160), (64, 4096)]}
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("m", [1, 2, 4, 5, 8, 9, 12, 13, 16])
 def test_small_m_kernel_every_row_group(fmt, m):
     """The small-M kernel (forced route) for every group count of A rows
@@ -390,7 +399,7 @@ def test_small_m_kernel_every_row_group(fmt, m):
 
 
 PLAN_CASES = [(F16, 37, 300, 640), (Q8, 37, 300, 640), (F16, 130, 97, 1000), (F16, 5, 77, 1003),
-              (Q8, 300, 129, 2080)]
+              (Q8, 300, 129, 2080), (Q4, 37, 300, 640), (Q4, 300, 129, 2080)]
 
 
 @pytest.mark.parametrize("case", PLAN_CASES, ids=[f"fmt{f}-{m}x{n}x{k}" for f, m, n, k in PLAN_CASES])

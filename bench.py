@@ -14,9 +14,11 @@ rather than from the 256 MB Infinity Cache.
 bytes (N*K*2 weight bytes) over its average launch duration, measured with
 HIP events around each launch on the stream it runs on, inside the timed
 region.  ``cpu_baseline`` times the CPU oracle (all host cores it uses) on the
-same suite.  ``secondary`` reports the other configurations: the Q8_0 decode
-suite, the f16 prefill GEMM at M = 512, the Q8_0 M sweep, and a plain device
-copy as the achievable-bandwidth reference.
+same suite.  ``secondary`` reports the other configurations: the Q8_0 and
+Q4_0 decode suites, the f16 prefill GEMM at M = 512, the Q8_0 and Q4_0 M
+sweeps, and a plain device copy as the achievable-bandwidth reference.  Q4_0
+weights are synthetic bytes (random codes and scales) since no Q4_0 encoder is
+given.
 """
 from __future__ import annotations
 
@@ -84,7 +86,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-secondary", action="store_true", help="headline suite only")
-    p.add_argument("--only", choices=["f16", "q8", "prefill", "sweep"], default=None,
+    p.add_argument("--only", choices=["f16", "q8", "q4", "prefill", "sweep"], default=None,
                    help="run one workload only (for profiling); prints no headline line")
     return p.parse_args()
 
@@ -96,10 +98,12 @@ class Suite:
         self.fmt = fmt
         self.items = []
         for name, n, k in DECODE:
-            w = host_weights[(n, k)]
-            wd = torch.from_numpy(w).cuda()
-            b0 = wq.pack_f16(wd) if fmt == wq.WQ_FMT_F16 else wq.quantize_q8_0(wd)
-            del wd
+            if fmt == wq.WQ_FMT_Q4_0:
+                b0 = torch.from_numpy(wqgen.q4_0_bytes(n, k, seed)).cuda()
+            else:
+                wd = torch.from_numpy(host_weights[(n, k)]).cuda()
+                b0 = wq.pack_f16(wd) if fmt == wq.WQ_FMT_F16 else wq.quantize_q8_0(wd)
+                del wd
             nbytes = wq.weight_bytes(n, k, fmt)
             copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
             bs = [b0] + [b0.clone() for _ in range(copies - 1)]
@@ -145,15 +149,25 @@ def time_suite(torch, wq, suite, steps, warmup, bracket):
 
 
 def time_launches(torch, fn, iters, warmup):
+    """GPU seconds per launch of fn.  A spin kernel (a few ms) holds the stream
+    while the host enqueues the timed launches, so that per-call host overhead
+    (Python binding and launch, about 10 us) does not leak into the GPU time of
+    kernels shorter than that."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, s, e = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    torch.cuda._sleep(10_000_000)
     s.record()
+    t0 = time.perf_counter()
     for i in range(iters):
         fn(warmup + i)
+    host = time.perf_counter() - t0
     e.record()
     torch.cuda.synchronize()
+    if host > 0.9 * e0.elapsed_time(s) / 1e3:
+        log(f"warning: host enqueue ({host * 1e3:.2f} ms) outlasted the stream hold; GPU time may include gaps")
     return s.elapsed_time(e) / 1e3 / iters
 
 
@@ -197,7 +211,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
-    F16, Q8 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0
+    F16, Q8, Q4 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0
 
     log("drawing inputs")
     host_weights = {(n, k): wqgen.weights(n, k, args.seed) for _, n, k in DECODE}
@@ -259,23 +273,25 @@ def main():
         del s16
         torch.cuda.empty_cache()
 
-    if not args.no_secondary and only in (None, "q8"):
-        log("Q8_0 decode suite")
-        s8 = Suite(wq, wqgen, torch, Q8, args.seed, host_weights)
-        lm8 = [i for i, it in enumerate(s8.items) if it["name"] == "lm_head"][0]
-        total, _, per = time_suite(torch, wq, s8, args.steps, args.warmup, bracket=[lm8])
-        _, _, per_all = time_suite(torch, wq, s8, max(10, args.steps // 2), 2, bracket=range(len(s8.items)))
-        secondary["q8_decode_suite"] = {
-            "GB/s": round(s8.bytes_per_step * args.steps / total / 1e9, 2),
-            "frac_hbm": round(s8.bytes_per_step * args.steps / total / 1e9 / HBM_PEAK_GBS, 4),
+    for fmt, key in ((Q8, "q8"), (Q4, "q4")):
+        if args.no_secondary or only not in (None, key):
+            continue
+        log(f"{key} decode suite")
+        sq = Suite(wq, wqgen, torch, fmt, args.seed, host_weights)
+        lmq = [i for i, it in enumerate(sq.items) if it["name"] == "lm_head"][0]
+        total, _, per = time_suite(torch, wq, sq, args.steps, args.warmup, bracket=[lmq])
+        _, _, per_all = time_suite(torch, wq, sq, max(10, args.steps // 2), 2, bracket=range(len(sq.items)))
+        secondary[f"{key}_decode_suite"] = {
+            "GB/s": round(sq.bytes_per_step * args.steps / total / 1e9, 2),
+            "frac_hbm": round(sq.bytes_per_step * args.steps / total / 1e9 / HBM_PEAK_GBS, 4),
             "ms_per_step": round(total / args.steps * 1e3, 5),
-            "lm_head_us": round(per[lm8] * 1e6, 3),
-            "lm_head_GB/s": round(s8.items[lm8]["bytes"] / per[lm8] / 1e9, 1),
+            "lm_head_us": round(per[lmq] * 1e6, 3),
+            "lm_head_GB/s": round(sq.items[lmq]["bytes"] / per[lmq] / 1e9, 1),
             "per_kernel_event_timed": {it["name"]: {"us": round(per_all[j] * 1e6, 3),
                                                     "GB/s": round(it["bytes"] / per_all[j] / 1e9, 1)}
-                                       for j, it in enumerate(s8.items)},
+                                       for j, it in enumerate(sq.items)},
         }
-        del s8
+        del sq
         torch.cuda.empty_cache()
 
     if not args.no_secondary and only in (None, "prefill"):
@@ -294,25 +310,28 @@ def main():
         secondary["f16_prefill_m512"] = out
 
     if not args.no_secondary and only in (None, "sweep"):
-        log("Q8_0 M sweep")
-        out = {}
-        for n, k in SWEEP_SHAPES:
-            w = wqgen.weights(n, k, args.seed)
-            b0 = wq.quantize_q8_0(torch.from_numpy(w).cuda())
-            nbytes = wq.weight_bytes(n, k, Q8)
-            bs = [b0] + [b0.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / nbytes)) - 1)]
-            a_all = torch.from_numpy(wqgen.activations(max(SWEEP_M), k, args.seed)).cuda()
-            for m in SWEEP_M:
-                a = a_all[:m].contiguous()
-                c = torch.empty((m, n), device="cuda")
-                t = time_launches(torch, lambda i: wq.wq_matmul(a, bs[i % len(bs)], c, m, n, k, Q8),
-                                  max(10, args.steps // 2), args.warmup)
-                out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(nbytes / t / 1e9, 1),
-                                       "TFLOP/s": round(2.0 * m * n * k / t / 1e12, 2),
-                                       "route": ROUTE_NAMES[wq.wq_route_for(m, n, k, Q8)]}
-            del bs, b0
-            torch.cuda.empty_cache()
-        secondary["q8_sweep"] = out
+        for fmt, key in ((Q8, "q8"), (Q4, "q4")):
+            log(f"{key} M sweep")
+            out = {}
+            for n, k in SWEEP_SHAPES:
+                if fmt == Q4:
+                    b0 = torch.from_numpy(wqgen.q4_0_bytes(n, k, args.seed)).cuda()
+                else:
+                    b0 = wq.quantize_q8_0(torch.from_numpy(wqgen.weights(n, k, args.seed)).cuda())
+                nbytes = wq.weight_bytes(n, k, fmt)
+                bs = [b0] + [b0.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / nbytes)) - 1)]
+                a_all = torch.from_numpy(wqgen.activations(max(SWEEP_M), k, args.seed)).cuda()
+                for m in SWEEP_M:
+                    a = a_all[:m].contiguous()
+                    c = torch.empty((m, n), device="cuda")
+                    t = time_launches(torch, lambda i: wq.wq_matmul(a, bs[i % len(bs)], c, m, n, k, fmt),
+                                      max(10, args.steps // 2), args.warmup)
+                    out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(nbytes / t / 1e9, 1),
+                                           "TFLOP/s": round(2.0 * m * n * k / t / 1e12, 2),
+                                           "route": ROUTE_NAMES[wq.wq_route_for(m, n, k, fmt)]}
+                del bs, b0
+                torch.cuda.empty_cache()
+            secondary[f"{key}_sweep"] = out
 
     if (not args.no_secondary and only is None) or only == "f16":
         log("device copy reference")

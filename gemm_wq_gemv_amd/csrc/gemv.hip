@@ -172,9 +172,22 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 // 16 * (u - 8) for codes in bits 4..7 (HI): the code is placed in the
 // mantissa of the f16 1024 (0x6400), which reads as 1024 + u (1024 + 16 u),
 // and one packed subtraction removes 1032 (1152).  Every step is exact.
+// The mask (in a VGPR) and 0x64006400 (in an SGPR) are register operands so
+// that the and-or is one v_and_or_b32: a gfx9 VOP3 instruction takes no
+// literal and at most one scalar operand.
+struct Q4Consts {
+    uint32_t lo, hi, magic;
+};
+__device__ __forceinline__ Q4Consts q4_consts() {
+    Q4Consts k;
+    asm("v_mov_b32 %0, 0x000f000f" : "=v"(k.lo));
+    asm("v_mov_b32 %0, 0x00f000f0" : "=v"(k.hi));
+    asm("s_mov_b32 %0, 0x64006400" : "=s"(k.magic));
+    return k;
+}
 template <bool HI>
-__device__ __forceinline__ h2 q4_pair(uint32_t x) {
-    const uint32_t m = (x & (HI ? 0x00F000F0u : 0x000F000Fu)) | 0x64006400u;
+__device__ __forceinline__ h2 q4_pair(uint32_t x, const Q4Consts &k) {
+    const uint32_t m = (x & (HI ? k.hi : k.lo)) | k.magic;
     const _Float16 bias = HI ? static_cast<_Float16>(1152.0f) : static_cast<_Float16>(1032.0f);
     return __builtin_bit_cast(h2, m) - h2{bias, bias};
 }
@@ -190,15 +203,16 @@ __device__ __forceinline__ float q4_block_dot(const uint8_t *stage, int pb, cons
     u32x4 q;
     __builtin_memcpy(&q, __builtin_assume_aligned(stage + pb + 2, 2), 16);
     const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    const Q4Consts kc = q4_consts();
     float lo[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         // dword i = code bytes 4i .. 4i+3 = weights 8i .. 8i+7
         const uint32_t w = wd[i], w8 = wd[i] >> 8;
-        const h2 p0 = q4_pair<false>(w);   // weights 8i+0, 8i+4
-        const h2 p1 = q4_pair<true>(w);    // 8i+1, 8i+5 (x16)
-        const h2 p2 = q4_pair<false>(w8);  // 8i+2, 8i+6
-        const h2 p3 = q4_pair<true>(w8);   // 8i+3, 8i+7 (x16)
+        const h2 p0 = q4_pair<false>(w, kc);   // weights 8i+0, 8i+4
+        const h2 p1 = q4_pair<true>(w, kc);    // 8i+1, 8i+5 (x16)
+        const h2 p2 = q4_pair<false>(w8, kc);  // 8i+2, 8i+6
+        const h2 p3 = q4_pair<true>(w8, kc);   // 8i+3, 8i+7 (x16)
         const float *x = av + 8 * i;
         lo[0] = fmaf(static_cast<float>(p0.x), x[0], lo[0]);
         lo[1] = fmaf(static_cast<float>(p0.y), x[4], lo[1]);
@@ -391,8 +405,8 @@ hipError_t run_q_staged_sl(const float *a, const uint8_t *b, float *c, int64_t n
     constexpr int S = SL * (kWave / LPR);
     const int row_bytes = static_cast<int>((k >> 5) * QB<FMT>::kBytes);
     const int64_t passes = (n + S - 1) / S;
-    // 8 waves per CU (LDS stages of 9 fill a CU): measured best on MI355X.
-    const int64_t blocks = balanced_workers(passes, static_cast<int64_t>(cus) * 8);
+    // 12 single-wave workgroups per CU: measured best on MI355X (N = 151936).
+    const int64_t blocks = balanced_workers(passes, static_cast<int64_t>(cus) * 12);
     const size_t lds = (static_cast<size_t>(S) * row_bytes + 1023) / 1024 * 1024;  // whole 1 KiB writes
     if (trace_enabled())
         fprintf(stderr,
@@ -412,11 +426,9 @@ hipError_t run_q_staged(const float *a, const uint8_t *b, float *c, int64_t n, i
     const int row_bytes = static_cast<int>((k >> 5) * QB<FMT>::kBytes);
     const int64_t s_fit = QB<FMT>::kStage / row_bytes;
     const int64_t s_fill = std::max<int64_t>(1, n / (4LL * cus));
-    const int64_t sl_max = std::max<int64_t>(1, std::min(s_fit, s_fill) / RPL);
-    if constexpr (FMT == QFMT_Q4_0 && J <= 1)
-        if (sl_max >= 16 && 16 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 16>(a, b, c, n, k, s, cus);
-    if constexpr (J <= 1)
-        if (sl_max >= 8 && 8 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 8>(a, b, c, n, k, s, cus);
+    // At most 4 rows per lane group and pass: with 12 waves per CU that was
+    // measured faster than 8 or 16 rows for both formats at K = 2048.
+    const int64_t sl_max = std::max<int64_t>(1, std::min<int64_t>(4, std::min(s_fit, s_fill) / RPL));
     if constexpr (J <= 2)
         if (sl_max >= 4 && 4 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 4>(a, b, c, n, k, s, cus);
     if constexpr (J <= 4)

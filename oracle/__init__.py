@@ -1,4 +1,5 @@
-"""CPU oracle for C[M,N] = A[M,K] · B[N,K]^T with f16 or Q8_0 weights.
+"""CPU oracle for C[M,N] = A[M,K] · B[N,K]^T with f16, Q8_0 or Q4_0 weights,
+and for the residual and SwiGLU epilogues on that product.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this package.  The GPU
@@ -15,6 +16,11 @@ Parity status of each function (what pins it, see ``tests/test_oracle.py``):
   decode         hand-built blocks, one-hot / identity products
   matmul         exact rational brute force, identity, one-hot, linearity,
                  permutation, numpy float64 matmul on the decoded weights
+  silu           closed forms: silu(0) = 0, silu(ln 3) = (3/4) ln 3,
+                 silu(x) - silu(-x) = x, limits at +-inf, sign
+  matmul_epilogue  residual: exact hand sums on the worked example, linearity;
+                 SwiGLU: hand-derived values (gate ln 3 / 0 / +-40), which half
+                 is gate, the identity out(g) - out(-g) = g * u
 """
 from __future__ import annotations
 
@@ -31,6 +37,9 @@ _LIB = os.path.join(_HERE, "libwqref.so")
 FMT_F16 = 0
 FMT_Q8_0 = 1
 FMT_Q4_0 = 2
+EPI_NONE = 0
+EPI_RESIDUAL = 1
+EPI_SWIGLU = 2
 QK = 32
 BLOCK_BYTES = 34
 
@@ -82,6 +91,12 @@ class Oracle:
         lib.wqref_matmul.argtypes = [P, P, I, I64, I64, I64, P, P, I]
         lib.wqref_matmul_entries.restype = I
         lib.wqref_matmul_entries.argtypes = [P, P, I, I64, I64, I64, P, P, I64, P, P, I]
+        lib.wqref_silu.restype = ctypes.c_double
+        lib.wqref_silu.argtypes = [ctypes.c_double]
+        lib.wqref_silu_array.restype = None
+        lib.wqref_silu_array.argtypes = [P, P, I64]
+        lib.wqref_epilogue.restype = I
+        lib.wqref_epilogue.argtypes = [I, P, P, I64, I64, P, P, P]
         self.lib = lib
         self.path = path
 
@@ -163,6 +178,65 @@ class Oracle:
             raise ValueError("matmul_entries: bad arguments")
         return c, bound
 
+    # -- epilogues (silu_mul / residual GEMM statements, see wqref.c) ---------
+    def silu(self, x) -> np.ndarray:
+        """silu(x) = x / (1 + exp(-x)) in float64."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.empty(x.shape, dtype=np.float64)
+        self.lib.wqref_silu_array(x.ctypes.data, out.ctypes.data, x.size)
+        return out
+
+    def epilogue(self, epi: int, acc, acc_bound, m: int, n: int, resid=None):
+        """(out, bound) of epilogue epi (1 residual, 2 SwiGLU) on product sums
+        acc [m, n] (residual) or [m, 2n] (SwiGLU: gate sums, then up sums)."""
+        acc = np.ascontiguousarray(acc, dtype=np.float64)
+        acc_bound = np.ascontiguousarray(acc_bound, dtype=np.float64)
+        if acc.size != (2 if epi == EPI_SWIGLU else 1) * m * n or acc_bound.size != acc.size:
+            raise ValueError("epilogue: acc has the wrong size")
+        r = None
+        if epi == EPI_RESIDUAL:
+            r = np.ascontiguousarray(resid, dtype=np.float32)
+            if r.size != m * n:
+                raise ValueError("epilogue: residual has the wrong size")
+        out = np.empty((m, n), dtype=np.float64)
+        bound = np.empty((m, n), dtype=np.float64)
+        rc = self.lib.wqref_epilogue(epi, acc.ctypes.data, acc_bound.ctypes.data, m, n,
+                                     None if r is None else r.ctypes.data,
+                                     out.ctypes.data, bound.ctypes.data)
+        if rc != 0:
+            raise ValueError("epilogue: bad arguments")
+        return out, bound
+
+    def matmul_epilogue(self, a, b, fmt: int, m: int, n: int, k: int, epi: int, resid=None,
+                        threads: int | None = None):
+        """(out, bound) of the product with an epilogue: EPI_NONE as matmul;
+        EPI_RESIDUAL resid + A.B^T (resid f32 [m, n]); EPI_SWIGLU with b holding
+        2n rows (gate rows, then up rows) and out = silu(A.gate^T) * (A.up^T)."""
+        if epi == EPI_NONE:
+            return self.matmul(a, b, fmt, m, n, k, threads)
+        rows = 2 * n if epi == EPI_SWIGLU else n
+        acc, bnd = self.matmul(a, b, fmt, m, rows, k, threads)
+        return self.epilogue(epi, acc, bnd, m, n, resid)
+
+    def epilogue_entries(self, a, b, fmt: int, m: int, n: int, k: int, epi: int, rows, cols,
+                         resid=None, threads: int | None = None):
+        """(out, bound) of the epilogue product at the entries (rows[i], cols[i]);
+        resid, when given, is the full f32 [m, n] residual."""
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        cols = np.ascontiguousarray(cols, dtype=np.int64)
+        if epi == EPI_NONE:
+            return self.matmul_entries(a, b, fmt, m, n, k, rows, cols, threads)
+        if epi == EPI_RESIDUAL:
+            s, bs = self.matmul_entries(a, b, fmt, m, n, k, rows, cols, threads)
+            r = np.asarray(resid, dtype=np.float32).reshape(m, n)[rows, cols]
+            out, bound = self.epilogue(EPI_RESIDUAL, s, bs, rows.size, 1, r)
+            return out.reshape(-1), bound.reshape(-1)
+        both_rows = np.stack([rows, rows], axis=1).reshape(-1)
+        both_cols = np.stack([cols, cols + n], axis=1).reshape(-1)  # (gate, up) per entry
+        s, bs = self.matmul_entries(a, b, fmt, m, 2 * n, k, both_rows, both_cols, threads)
+        out, bound = self.epilogue(EPI_SWIGLU, s, bs, rows.size, 1)
+        return out.reshape(-1), bound.reshape(-1)
+
 
 _default: Oracle | None = None
 
@@ -201,3 +275,15 @@ def matmul_entries(a, b, fmt, m, n, k, rows, cols, threads=None):
 def encode(w, fmt: int) -> np.ndarray:
     """Weight bytes of float32 w [n, k] in the given format, by the oracle's own encoders."""
     return get().encode(w, fmt)
+
+
+def silu(x):
+    return get().silu(x)
+
+
+def matmul_epilogue(a, b, fmt, m, n, k, epi, resid=None, threads=None):
+    return get().matmul_epilogue(a, b, fmt, m, n, k, epi, resid, threads)
+
+
+def epilogue_entries(a, b, fmt, m, n, k, epi, rows, cols, resid=None, threads=None):
+    return get().epilogue_entries(a, b, fmt, m, n, k, epi, rows, cols, resid, threads)

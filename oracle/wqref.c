@@ -308,3 +308,56 @@ int wqref_matmul_entries(const float *a, const void *b, int fmt, int64_t M, int6
     job_t base = {a, b, fmt, M, N, K, c, bound, 0, 0, rows, cols};
     return run_jobs(&base, count, nthreads, entries_worker);
 }
+
+/* ------------------------------------------------------------ epilogues -- */
+
+/* SiLU of the pages' silu_mul kernel (lattice-inference 0.1.2 page): the gate
+ * value divided by one plus e to the minus gate value, here in double. */
+double wqref_silu(double x) { return x / (1.0 + exp(-x)); }
+
+void wqref_silu_array(const double *x, double *out, int64_t count) {
+    for (int64_t i = 0; i < count; ++i) out[i] = wqref_silu(x[i]);
+}
+
+/* Epilogue on finished product sums, element by element.
+ *
+ * epi 1, residual: out[i,j] = r[i,j] + s[i,j], with acc = s [M, N] and r the
+ *   f32 residual the product is added into (gemm_q1_v7_residual in the
+ *   oxibonsai-kernels 0.1.4 page's encode_layer_prefill; add_buf on the
+ *   lattice-inference 0.1.2 page).  Tolerance: the product's own bound plus
+ *   one f32 rounding of the addition, 2^-23 * (|r| + |s|).
+ * epi 2, SwiGLU: acc is [M, 2N], columns 0..N-1 the gate sums g and N..2N-1
+ *   the up sums u of the same output (gate rows first in the fused gate||up
+ *   weight: dispatch_gemm_at on the lattice-inference 0.9.0 page binds gate at
+ *   offset 0 and up at the gate's byte size; dispatch_silu_mul_fused computes
+ *   silu(first half) * second half); out[i,j] = silu(g) * u.  Tolerance:
+ *   silu' lies in (-0.1, 1.1), so a gate error of at most Bg moves silu(g) by
+ *   at most 1.1 Bg; with an up error of at most Bu the stored value is within
+ *   1.1 Bg (|u| + Bu) + |silu(g)| Bu of the exact one, plus 2^-20 |out| for the
+ *   f32 evaluation of silu and of the product.
+ * Returns 0, or -1 on bad arguments. */
+int wqref_epilogue(int epi, const double *acc, const double *acc_bound, int64_t M, int64_t N,
+                   const float *resid, double *out, double *bound) {
+    if (M < 0 || N < 0 || !acc || !acc_bound || !out || !bound) return -1;
+    if (epi == 1) {
+        if (!resid) return -1;
+        for (int64_t i = 0; i < M * N; ++i) {
+            const double r = (double)resid[i], s = acc[i];
+            out[i] = r + s;
+            bound[i] = acc_bound[i] + ldexp(fabs(r) + fabs(s), -23);
+        }
+        return 0;
+    }
+    if (epi == 2) {
+        for (int64_t i = 0; i < M; ++i)
+            for (int64_t j = 0; j < N; ++j) {
+                const int64_t gi = i * 2 * N + j, ui = gi + N;
+                const double g = acc[gi], u = acc[ui], bg = acc_bound[gi], bu = acc_bound[ui];
+                const double sg = wqref_silu(g);
+                out[i * N + j] = sg * u;
+                bound[i * N + j] = 1.1 * bg * (fabs(u) + bu) + fabs(sg) * bu + ldexp(fabs(sg * u), -20);
+            }
+        return 0;
+    }
+    return -1;
+}

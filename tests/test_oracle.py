@@ -401,6 +401,99 @@ def pin_numpy_matmul(orc):
     assert np.array_equal(c, np.zeros((2, 3))) and np.allclose(bound, 1e-6)
 
 
+# ------------------------------------------------------------- epilogues --
+LN3 = float(np.log(3.0))
+
+
+def pin_silu_closed_forms(orc):
+    """silu(x) = x * sigma(x) with sigma(x) = 1 / (1 + e^-x) (silu_mul, lattice-inference
+    0.1.2 page).  Closed forms: sigma(0) = 1/2 so silu(0) = 0; sigma(ln 3) = 1/(1 + 1/3) = 3/4;
+    sigma(1) = e / (1 + e); sigma(x) + sigma(-x) = 1 gives silu(x) - silu(-x) = x; silu(x) / x
+    tends to 1 at +inf and silu(x) to 0- at -inf; 0 < silu(x) < x and silu(x) > x / 2 for x > 0."""
+    assert orc.silu([0.0])[0] == 0.0
+    assert abs(orc.silu([LN3])[0] - 0.75 * LN3) <= 1e-15
+    assert abs(orc.silu([1.0])[0] - np.e / (1.0 + np.e)) <= 1e-15
+    x = np.concatenate([np.geomspace(1e-6, 30.0, 200), [0.5, 2.0, 7.25]])
+    assert np.all(np.abs(orc.silu(x) - orc.silu(-x) - x) <= 4e-16 * x + 1e-300)
+    pos = orc.silu(x)
+    assert np.all((pos > x / 2) & (pos < x))
+    assert orc.silu([40.0])[0] == 40.0                      # 40 / (1 + e^-40), e^-40 < 2^-53
+    v = orc.silu([-40.0])[0]
+    assert -40.0 * np.exp(-40.0) <= v < -0.99 * 40.0 * np.exp(-40.0)
+    assert orc.silu([-1000.0])[0] == 0.0 and orc.silu([1000.0])[0] == 1000.0
+
+
+def pin_residual_golden(orc):
+    """The worked 2x3x32 example (tests/golden/matmul_tiny.txt) added into a residual
+    (gemm_q1_v7_residual, oxibonsai-kernels 0.1.4 page): out = r + C, each sum below
+    exact and done by hand; the tolerance adds one f32 rounding, 2^-23 (|r| + |C|)."""
+    M, N, K, A, B16, B8, B4, C = _golden_matmul()
+    r = np.array([[0.25, -1.0, 1e6], [0.5, -4.5, 7.0]], np.float32)
+    want = np.array([[3.25, -1.0, 1000002.0], [0.0, 0.0, 2.0]])
+    for fmt, b in ((FMT_F16, B16), (FMT_Q8_0, B8), (FMT_Q4_0, B4)):
+        out, bound = orc.matmul_epilogue(A, b, fmt, M, N, K, oracle.EPI_RESIDUAL, r)
+        assert np.array_equal(out, want), (fmt, out)
+        _, pb = orc.matmul(A, b, fmt, M, N, K)
+        assert np.allclose(bound, pb + (np.abs(r) + np.abs(C)) * 2.0 ** -23, rtol=1e-15, atol=0)
+        rows, cols = np.array([1, 0, 1]), np.array([2, 2, 0])
+        oe, be = orc.epilogue_entries(A, b, fmt, M, N, K, oracle.EPI_RESIDUAL, rows, cols, r)
+        assert np.array_equal(oe, want[rows, cols]) and np.array_equal(be, bound[rows, cols])
+
+
+def _swiglu_tiny():
+    """A hand-built SwiGLU case, K = 32, n = 2: gate rows 0, 1 then up rows 2, 3 (f16
+    one-hots) of the fused gate||up weight (gate at offset 0, up after it:
+    dispatch_gemm_at, lattice-inference 0.9.0 page)."""
+    K, n = 32, 2
+    w = np.zeros((2 * n, K), np.uint16)
+    w[0, 0] = 0x3C00   # gate 0 = a[0]
+    w[1, 1] = 0xBC00   # gate 1 = -a[1]
+    w[2, 0] = 0x4000   # up 0 = 2 a[0]
+    w[3, 2] = 0x3800   # up 1 = a[2] / 2
+    g = np.float32(LN3)  # the f32 nearest ln 3, |g - ln 3| < 2^-23
+    a = np.zeros((3, K), np.float32)
+    a[0, 0], a[0, 2] = g, 4.0            # gate (g, 0), up (2g, 2)
+    a[1, 1], a[1, 2] = -g, 8.0           # gate (0, g), up (0, 4)
+    a[2, 0], a[2, 1], a[2, 2] = -40.0, 40.0, -6.0  # gate (-40, -40), up (-80, -3)
+    # out = silu(gate) * up:  row 0: (3/4 g * 2g, 0) = (1.5 g^2, 0); row 1: (0, 3/4 g * 4) = (0, 3g);
+    # row 2: silu(-40) * (-80) and silu(-40) * (-3), both within 100 e^-40 of 0.
+    want = np.array([[1.5 * LN3 * LN3, 0.0], [0.0, 3.0 * LN3], [0.0, 0.0]])
+    return a, w, K, n, want
+
+
+def pin_swiglu_golden(orc):
+    """Hand values of _swiglu_tiny (sigma(ln 3) = 3/4; silu(0) = 0; silu(-40) ~ 0): which
+    half is the gate, its pairing with the up row of the same index, and the sign of the
+    exponent; the relative 1e-7 covers g being the f32 nearest ln 3."""
+    a, w, K, n, want = _swiglu_tiny()
+    out, bound = orc.matmul_epilogue(a, w, FMT_F16, 3, n, K, oracle.EPI_SWIGLU)
+    assert out.shape == (3, n)
+    assert np.all(np.abs(out - want) <= 1e-7 * np.abs(want) + 1e-13), out
+    assert np.all(bound >= 2.0 ** -20 * np.abs(out))
+    oe, be = orc.epilogue_entries(a, w, FMT_F16, 3, n, K, oracle.EPI_SWIGLU, [1, 0, 2], [1, 0, 1])
+    assert np.array_equal(oe, out[[1, 0, 2], [1, 0, 1]]) and np.array_equal(be, bound[[1, 0, 2], [1, 0, 1]])
+
+
+def pin_swiglu_identity(orc):
+    """silu(g) u - silu(-g) u = g u (sigma(x) + sigma(-x) = 1): negating the gate rows
+    (flipping their f16 sign bits) and subtracting must give g * u, with g and u from
+    numpy on numpy-decoded weights, for random activations and weights."""
+    M, n, K = 5, 37, 96
+    a = wqgen.normal((M, K), seed=3, stream=0)
+    w = _weights(orc, FMT_F16, 2 * n, K, seed=11)
+    wneg = w.copy()
+    wneg[:n] ^= np.uint16(0x8000)
+    out, _ = orc.matmul_epilogue(a, w, FMT_F16, M, n, K, oracle.EPI_SWIGLU)
+    outn, _ = orc.matmul_epilogue(a, wneg, FMT_F16, M, n, K, oracle.EPI_SWIGLU)
+    wd = _numpy_decode(w, FMT_F16, 2 * n, K)
+    a64 = a.astype(np.float64)
+    g, u = a64 @ wd[:n].T, a64 @ wd[n:].T
+    assert np.all(np.abs((out - outn) - g * u) <= 1e-12 * (np.abs(g) + 1) * (np.abs(u) + 1))
+    # silu(g) u itself lies between 0 and g u for g > 0 and between g u and 0 for g < 0.
+    gu = g * u
+    assert np.all(np.minimum(0, gu) - 1e-12 <= out) and np.all(out <= np.maximum(0, gu) + 1e-12)
+
+
 PINS = [
     pin_f16_decode_exhaustive,
     pin_f16_encode_golden,
@@ -414,6 +507,10 @@ PINS = [
     pin_identity_and_onehot,
     pin_invariants,
     pin_numpy_matmul,
+    pin_silu_closed_forms,
+    pin_residual_golden,
+    pin_swiglu_golden,
+    pin_swiglu_identity,
 ]
 
 
@@ -464,6 +561,14 @@ MUTANTS = {
     "q4_split_halves_layout": ("blk[2 + i / 2];\n    const int u = (i % 2 == 0) ? (byte & 0x0F) : (byte >> 4);",
                                "blk[2 + i % 16];\n    const int u = (i < 16) ? (byte & 0x0F) : (byte >> 4);"),
     "q4_signed_nibble": ("(byte & 0x0F) : (byte >> 4);", "((byte & 0x0F) ^ 8) : ((byte >> 4) ^ 8);"),
+    "silu_exp_sign": ("x / (1.0 + exp(-x))", "x / (1.0 + exp(x))"),
+    "silu_is_sigmoid": ("x / (1.0 + exp(-x))", "1.0 / (1.0 + exp(-x))"),
+    "silu_no_gate_product": ("out[i * N + j] = sg * u;", "out[i * N + j] = sg;"),
+    "glu_halves_swapped": ("gi = i * 2 * N + j, ui = gi + N;", "ui = i * 2 * N + j, gi = ui + N;"),
+    "glu_interleaved": ("gi = i * 2 * N + j, ui = gi + N;", "gi = i * 2 * N + 2 * j, ui = gi + 1;"),
+    "residual_dropped": ("out[i] = r + s;", "out[i] = s;"),
+    "residual_subtracted": ("out[i] = r + s;", "out[i] = s - r;"),
+    "residual_bound_no_rounding": ("acc_bound[i] + ldexp(fabs(r) + fabs(s), -23)", "acc_bound[i]"),
 }
 
 

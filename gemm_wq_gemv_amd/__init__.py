@@ -34,11 +34,16 @@ WQ_ERR_ALIGN = 5
 WQ_ERR_LAUNCH = 6
 WQ_ERR_ALIAS = 7
 WQ_ERR_ROUTE = 8
+WQ_ERR_EPILOGUE = 9
 
 WQ_ROUTE_AUTO = 0
 WQ_ROUTE_GEMV = 1
 WQ_ROUTE_GEMM = 2
 WQ_ROUTE_SKINNY = 3
+
+WQ_EPI_NONE = 0
+WQ_EPI_RESIDUAL = 1
+WQ_EPI_SWIGLU = 2
 
 Q8_0_BLOCK_BYTES = 34
 Q8_0_BLOCK_WEIGHTS = 32
@@ -65,6 +70,7 @@ def _load() -> ctypes.CDLL:
         "wq_gemm_q8_0": (I, [P, P, P, I64, I64, I64, P]),
         "wq_gemm_q4_0": (I, [P, P, P, I64, I64, I64, P]),
         "wq_matmul": (I, [P, P, P, I64, I64, I64, I, P]),
+        "wq_matmul_ex": (I, [P, P, P, I64, I64, I64, I, I, P]),
         "wq_pack_f16": (I, [P, P, I64, P]),
         "wq_quantize_q8_0": (I, [P, P, I64, P]),
         "wq_route_for": (I, [I64, I64, I64, I]),
@@ -142,7 +148,7 @@ def _check(status: int, what: str):
         raise WQError(status, what)
 
 
-def _sizes(a, b, c, m, n, k, fmt):
+def _sizes(a, b, c, m, n, k, fmt, weight_rows=None):
     if m > 0 and n > 0:
         _dtype(a, _F32, "a")
         _dtype(c, _F32, "c")
@@ -150,7 +156,7 @@ def _sizes(a, b, c, m, n, k, fmt):
         _need(a, 4 * m * k, "a")
         _need(c, 4 * m * n, "c")
         if k >= 0 and (fmt == WQ_FMT_F16 or k % 32 == 0):
-            _need(b, weight_bytes(n, k, fmt), "b")
+            _need(b, weight_bytes(n if weight_rows is None else weight_rows, k, fmt), "b")
 
 
 # ------------------------------------------------------------ entry points --
@@ -188,6 +194,14 @@ def wq_matmul(a, b, c, m: int, n: int, k: int, fmt: int, stream=None) -> None:
     if fmt in (WQ_FMT_F16, WQ_FMT_Q8_0, WQ_FMT_Q4_0):
         _sizes(a, b, c, m, n, k, fmt)
     _check(_lib.wq_matmul(_ptr(a), _ptr(b), _ptr(c), m, n, k, fmt, _stream(stream, c)), "wq_matmul")
+
+
+def wq_matmul_ex(a, b, c, m: int, n: int, k: int, fmt: int, epi: int, stream=None) -> None:
+    """wq_matmul with a fused epilogue: WQ_EPI_RESIDUAL (c += a.b^T) or
+    WQ_EPI_SWIGLU (b holds 2n rows, gate then up; c = silu(gate) * up)."""
+    if fmt in (WQ_FMT_F16, WQ_FMT_Q8_0, WQ_FMT_Q4_0) and epi in (WQ_EPI_NONE, WQ_EPI_RESIDUAL, WQ_EPI_SWIGLU):
+        _sizes(a, b, c, m, n, k, fmt, 2 * n if epi == WQ_EPI_SWIGLU else n)
+    _check(_lib.wq_matmul_ex(_ptr(a), _ptr(b), _ptr(c), m, n, k, fmt, epi, _stream(stream, c)), "wq_matmul_ex")
 
 
 def wq_pack_f16(w, out, count: int, stream=None) -> None:

@@ -77,6 +77,19 @@ struct Gemm {
         uint32_t q8[QUANT ? B8_ITERS : 1][QW];
     };
 
+    // Weight row feeding row `row` of the LDS weight tile.  Plain: n0 + row
+    // (clamped: rows past N only feed outputs that are never stored).  GLU
+    // (gate/up pairs for the SwiGLU epilogue; N = 2*NO weight rows, n0 = the
+    // tile's first output column): each wave's WTN tile rows are WTN/2 gate
+    // rows followed by the up rows of the same output columns, so fragment fj
+    // and fj + FN/2 of a wave hold a gate and its up at the same lane.
+    static __device__ __forceinline__ int64_t brow(int64_t n0, int row, int64_t N, int64_t NO, bool glu) {
+        if (!glu) return min<int64_t>(n0 + row, N - 1);
+        const int wn = row / WTN, within = row % WTN;
+        const int64_t oc = min<int64_t>(n0 + wn * (WTN / 2) + within % (WTN / 2), NO - 1);
+        return within < WTN / 2 ? oc : NO + oc;
+    }
+
     // Global -> registers for the k-tile starting at k0.  On the vector path
     // every thread issues the same number of loads on every call (addresses
     // are clamped into the matrices and out-of-range values zeroed after the
@@ -86,7 +99,7 @@ struct Gemm {
     static __device__ __forceinline__ void load(Regs &r, const float *__restrict__ a,
                                                 const void *__restrict__ bw, int64_t M, int64_t N,
                                                 int64_t K, int64_t m0, int64_t n0, int64_t k0,
-                                                int tid) {
+                                                int tid, int64_t NO, bool glu) {
 #pragma unroll
         for (int i = 0; i < A_ITERS; ++i) {
             const int row = (tid >> 3) + 32 * i;
@@ -113,12 +126,12 @@ struct Gemm {
             for (int i = 0; i < B16_ITERS; ++i) {
                 const int row = (tid >> 2) + 64 * i;
                 const int c8 = tid & 3;
-                const int64_t gn = n0 + row, gk = k0 + 8 * c8;
+                const int64_t gn = brow(n0, row, N, NO, glu), gk = k0 + 8 * c8;
                 uint4 v = make_uint4(0u, 0u, 0u, 0u);
                 if (VEC) {
-                    const int64_t gnc = min<int64_t>(gn, N - 1), gkc = min<int64_t>(gk, K - 8);
-                    v = *reinterpret_cast<const uint4 *>(b + gnc * K + gkc);
-                } else if (row < BN && gn < N) {
+                    const int64_t gkc = min<int64_t>(gk, K - 8);
+                    v = *reinterpret_cast<const uint4 *>(b + gn * K + gkc);
+                } else if (row < BN) {
                     const uint16_t *p = b + gn * K + gk;
                     uint32_t h[8];
 #pragma unroll
@@ -139,7 +152,7 @@ struct Gemm {
                 const int row = (tid >> 1) + 128 * i;
                 const int h = tid & 1;
                 // Rows past N only feed outputs that are never stored.
-                const int64_t gnc = min<int64_t>(n0 + row, N - 1);
+                const int64_t gnc = brow(n0, row, N, NO, glu);
                 const uint16_t *blk = reinterpret_cast<const uint16_t *>(b + gnc * row_bytes + kb * QBB);
                 r.d8[i] = blk[0];
 #pragma unroll
@@ -261,12 +274,15 @@ struct Gemm {
 };
 
 // Grid: tiles * splits workgroups.  Split s covers k-tiles [s*kts, min(kt, (s+1)*kts)).
-// With one split the tile goes straight to C; otherwise to out = partial + s*M*N
-// (same layout), summed in split order by reduce_splits.
+// N = weight rows; NO = output columns (N, or N / 2 for the GLU epilogue).
+// With one split the tile goes to C [M, NO] through the epilogue; otherwise the
+// raw sums go to out = partial + s*M*N, column = weight row, and
+// reduce_splits sums them in split order and applies the epilogue.
 template <int BM, int BN, int WM, int WN, int FMT, bool VEC>
 __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, const void *__restrict__ bw,
                                                  float *__restrict__ c, int64_t M, int64_t N, int64_t K,
-                                                 int mtiles, int tiles, int splits, int kts) {
+                                                 int mtiles, int tiles, int splits, int kts, int64_t NO,
+                                                 int epi) {
     using G = Gemm<BM, BN, WM, WN, FMT, VEC>;
     __shared__ float As[2][BM][LDP];
     __shared__ float Bs[2][BN][LDP];
@@ -276,8 +292,9 @@ __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, co
     const int wm = wave / WN, wn = wave % WN;
     const int idx = xcd_tile(blockIdx.x, tiles * splits);
     const int tile = idx % tiles, split = idx / tiles;
+    const bool glu = epi == kEpiGlu;
     const int64_t m0 = static_cast<int64_t>(tile % mtiles) * BM;
-    const int64_t n0 = static_cast<int64_t>(tile / mtiles) * BN;
+    const int64_t n0 = static_cast<int64_t>(tile / mtiles) * (glu ? BN / 2 : BN);  // first output column
     const int64_t ktiles = (K + BK - 1) / BK;
     const int64_t kt0 = static_cast<int64_t>(split) * kts;
     const int64_t nkt = min<int64_t>(ktiles, kt0 + kts) - kt0;  // >= 1 by construction
@@ -293,14 +310,14 @@ __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, co
     // registers and is written to the other buffer between the two MFMA
     // halves of step i; tile i+2 is being loaded from global memory.
     typename G::Regs r0, r1;
-    G::load(r0, a, bw, M, N, K, m0, n0, kt0 * BK, tid);
+    G::load(r0, a, bw, M, N, K, m0, n0, kt0 * BK, tid, NO, glu);
     G::store(r0, As[0], Bs[0], tid, kt0 * BK, K);
-    G::load(r1, a, bw, M, N, K, m0, n0, (kt0 + min<int64_t>(1, nkt - 1)) * BK, tid);
+    G::load(r1, a, bw, M, N, K, m0, n0, (kt0 + min<int64_t>(1, nkt - 1)) * BK, tid, NO, glu);
     __syncthreads();
 
     auto step = [&](int64_t i, typename G::Regs &rnext, typename G::Regs &rfut) {
         // Always load (the last tile again near the end): a fixed load count.
-        G::load(rfut, a, bw, M, N, K, m0, n0, (kt0 + min<int64_t>(i + 2, nkt - 1)) * BK, tid);
+        G::load(rfut, a, bw, M, N, K, m0, n0, (kt0 + min<int64_t>(i + 2, nkt - 1)) * BK, tid, NO, glu);
         const int cur = static_cast<int>(i & 1);
         typename G::Frags fr;
         G::read_frags(fr, As[cur], Bs[cur], wm, wn, lane);
@@ -318,28 +335,71 @@ __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, co
 
     // D[i][j] of a 16x16 block: lane l, register v holds row 4*(l/16) + v, column l%16.
     const int li = lane & 15, lg = lane >> 4;
+    if (splits == 1 && glu) {
+        // SwiGLU: gate fragment fj pairs with up fragment fj + FN/2.
+        if constexpr (G::FN % 2 == 0) {
+#pragma unroll
+            for (int fi = 0; fi < G::FM; ++fi) {
+                const int64_t rbase = m0 + wm * G::WTM + 16 * fi + 4 * lg;
+#pragma unroll
+                for (int fj = 0; fj < G::FN / 2; ++fj) {
+                    const int64_t col = n0 + wn * (G::WTN / 2) + 16 * fj + li;
+                    if (col >= NO) continue;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (rbase + v < M)
+                            c[(rbase + v) * NO + col] = silu(acc[fi][fj][v]) * acc[fi][fj + G::FN / 2][v];
+                }
+            }
+        }
+        return;
+    }
+    const bool resid = splits == 1 && epi == kEpiResidual;
 #pragma unroll
     for (int fi = 0; fi < G::FM; ++fi) {
         const int64_t rbase = m0 + wm * G::WTM + 16 * fi + 4 * lg;
 #pragma unroll
         for (int fj = 0; fj < G::FN; ++fj) {
-            const int64_t col = n0 + wn * G::WTN + 16 * fj + li;
-            if (col >= N) continue;
+            // Column of C (one split) or of the partial buffer (weight row).
+            int64_t col = n0 + wn * G::WTN + 16 * fj + li;
+            bool ok = col < N;
+            if (glu) {
+                const int within = 16 * fj + li;
+                const int64_t oc = n0 + wn * (G::WTN / 2) + within % (G::WTN / 2);
+                ok = oc < NO;
+                col = within < G::WTN / 2 ? oc : NO + oc;
+            }
+            if (!ok) continue;
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                if (rbase + v < M) out[(rbase + v) * N + col] = acc[fi][fj][v];
+                if (rbase + v < M) {
+                    float *dst = out + (rbase + v) * N + col;
+                    *dst = resid ? *dst + acc[fi][fj][v] : acc[fi][fj][v];
+                }
         }
     }
 }
 
-// C[i] = sum over s < splits of partial[s][i], in split order (deterministic).
+// C[r, j] (r < m, j < no) from the split partial sums partial[s][r][.] (row
+// length nw), summed in split order (deterministic): plain, added to C
+// (residual), or silu(gate) * up with gate at column j and up at no + j (GLU,
+// nw = 2 * no).  With splits == 1 it is the GLU epilogue alone.
 __global__ __launch_bounds__(256) void reduce_splits(const float *__restrict__ partial, float *__restrict__ c,
-                                                     int64_t count, int splits) {
+                                                     int64_t m, int64_t no, int64_t nw, int splits, int epi) {
+    const int64_t count = m * no, plane = m * nw;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < count; e += stride) {
-        float v = partial[e];
-        for (int s = 1; s < splits; ++s) v += partial[static_cast<int64_t>(s) * count + e];
-        c[e] = v;
+        const int64_t r = e / no, j = e - r * no;
+        const int64_t base = r * nw + j;
+        float v = partial[base];
+        for (int s = 1; s < splits; ++s) v += partial[static_cast<int64_t>(s) * plane + base];
+        if (epi == kEpiGlu) {
+            float u = partial[base + no];
+            for (int s = 1; s < splits; ++s) u += partial[static_cast<int64_t>(s) * plane + base + no];
+            c[e] = silu(v) * u;
+        } else {
+            c[e] = epi == kEpiResidual ? c[e] + v : v;
+        }
     }
 }
 
@@ -358,23 +418,24 @@ struct Plan {
 
 template <int BM, int BN, int WM, int WN, int FMT>
 hipError_t run(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, bool vec, int splits,
-               int kts, hipStream_t s) {
-    const int64_t mt = (m + BM - 1) / BM, nt = (n + BN - 1) / BN;
+               int kts, hipStream_t s, int64_t no, int epi) {
+    const bool glu = epi == kEpiGlu;
+    const int64_t mt = (m + BM - 1) / BM, nt = glu ? (no + BN / 2 - 1) / (BN / 2) : (n + BN - 1) / BN;
     const int64_t tiles = mt * nt;
     if (tiles * splits > 0x7fffffffLL) return hipErrorInvalidValue;
     const int64_t grid = tiles * splits;
     if (trace_enabled())
         fprintf(stderr,
                 "[wqmm] gemm_mfma<BM=%d,BN=%d,WM=%d,WN=%d,fmt=%d,vec=%d> m=%lld n=%lld k=%lld splits=%d kts=%d "
-                "grid=%lld\n",
-                BM, BN, WM, WN, FMT, vec ? 1 : 0, (long long)m, (long long)n, (long long)k, splits, kts,
+                "epi=%d grid=%lld\n",
+                BM, BN, WM, WN, FMT, vec ? 1 : 0, (long long)m, (long long)n, (long long)k, splits, kts, epi,
                 (long long)grid);
     if (vec)
         hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, true>), dim3(grid), dim3(256), 0, s, a, b, c, m, n, k,
-                           static_cast<int>(mt), static_cast<int>(tiles), splits, kts);
+                           static_cast<int>(mt), static_cast<int>(tiles), splits, kts, no, epi);
     else
         hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, false>), dim3(grid), dim3(256), 0, s, a, b, c, m, n, k,
-                           static_cast<int>(mt), static_cast<int>(tiles), splits, kts);
+                           static_cast<int>(mt), static_cast<int>(tiles), splits, kts, no, epi);
     return hipGetLastError();
 }
 
@@ -392,7 +453,11 @@ constexpr TileCfg kCfgs[] = {
 // a single workgroup (one wave per SIMD) loses latency hiding (factor 0.6),
 // two recover most of it (0.92).  Weight streaming bounds the time from
 // below; a split adds the partial-sum pass.
-Plan choose_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus) {
+// The GLU epilogue pairs fragment fj with fj + FN/2 inside a wave: it needs an
+// even number of 16-column fragments per wave (WN = 4 for BM = 16, else 2).
+bool glu_ok(const TileCfg &t) { return (t.bn / (t.bm == 16 ? 4 : 2) / 16) % 2 == 0; }
+
+Plan choose_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, bool glu = false) {
     const int64_t ktiles = (k + BK - 1) / BK;
     const double wbytes = fmt == FMT_F16 ? 2.0 * n * k
                           : static_cast<double>(n) * (k / 32) * (fmt == FMT_Q4_0 ? kQ4BlockBytes : kQ8BlockBytes);
@@ -401,6 +466,7 @@ Plan choose_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus) {
     double best_t = 1e300;
     for (const TileCfg &t : kCfgs) {
         if (t.bm > 16 && t.bm >= 2 * m) continue;  // mostly padding rows
+        if (glu && !glu_ok(t)) continue;
         const int64_t tiles = ((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn);
         for (int sp : {1, 2, 3, 4, 6, 8, 12, 16}) {
             const int64_t kts = (ktiles + sp - 1) / sp;
@@ -426,19 +492,20 @@ Plan choose_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus) {
     return best;
 }
 
+// n = weight rows, no = output columns.
 template <int FMT>
 hipError_t dispatch_tile(const Plan &p, const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k,
-                         bool vec, hipStream_t s) {
+                         bool vec, hipStream_t s, int64_t no, int epi) {
     const int sp = p.splits, kts = p.kts;
     const TileCfg t = p.t;
-    if (t.bm == 128 && t.bn == 128) return run<128, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
-    if (t.bm == 128 && t.bn == 96) return run<128, 96, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
-    if (t.bm == 128 && t.bn == 64) return run<128, 64, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
-    if (t.bm == 64 && t.bn == 128) return run<64, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
-    if (t.bm == 64 && t.bn == 64) return run<64, 64, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
-    if (t.bm == 32 && t.bn == 128) return run<32, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
-    if (t.bm == 16 && t.bn == 128) return run<16, 128, 1, 4, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
-    return run<16, 64, 1, 4, FMT>(a, b, c, m, n, k, vec, sp, kts, s);
+    if (t.bm == 128 && t.bn == 128) return run<128, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s, no, epi);
+    if (t.bm == 128 && t.bn == 96) return run<128, 96, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s, no, epi);
+    if (t.bm == 128 && t.bn == 64) return run<128, 64, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s, no, epi);
+    if (t.bm == 64 && t.bn == 128) return run<64, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s, no, epi);
+    if (t.bm == 64 && t.bn == 64) return run<64, 64, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s, no, epi);
+    if (t.bm == 32 && t.bn == 128) return run<32, 128, 2, 2, FMT>(a, b, c, m, n, k, vec, sp, kts, s, no, epi);
+    if (t.bm == 16 && t.bn == 128) return run<16, 128, 1, 4, FMT>(a, b, c, m, n, k, vec, sp, kts, s, no, epi);
+    return run<16, 64, 1, 4, FMT>(a, b, c, m, n, k, vec, sp, kts, s, no, epi);
 }
 
 std::atomic<uint64_t> g_plan_override{0};  // bm | bn << 16 | splits << 32; 0 = none
@@ -449,10 +516,12 @@ bool known_tile(int bm, int bn) {
     return false;
 }
 
-Plan planned(int64_t m, int64_t n, int64_t k, int fmt, int cus) {
+// A forced tile that cannot take the GLU epilogue falls back to the model.
+Plan planned(int64_t m, int64_t n, int64_t k, int fmt, int cus, bool glu = false) {
     const uint64_t o = g_plan_override.load(std::memory_order_relaxed);
-    if (o == 0) return choose_plan(m, n, k, fmt, cus);
+    if (o == 0) return choose_plan(m, n, k, fmt, cus, glu);
     const int bm = static_cast<int>(o & 0xffff), bn = static_cast<int>((o >> 16) & 0xffff);
+    if (glu && !glu_ok(TileCfg{bm, bn, 1, 1.0})) return choose_plan(m, n, k, fmt, cus, glu);
     const int64_t ktiles = (k + BK - 1) / BK;
     const int64_t want = std::max<int64_t>(1, std::min<int64_t>(static_cast<int64_t>(o >> 32), ktiles));
     const int64_t kts = (ktiles + want - 1) / want;
@@ -462,30 +531,33 @@ Plan planned(int64_t m, int64_t n, int64_t k, int fmt, int cus) {
     return Plan{t, static_cast<int>((ktiles + kts - 1) / kts), static_cast<int>(kts)};
 }
 
+// n = output columns; the weights have nw = n (or 2n for the GLU epilogue) rows.
 template <int FMT>
 hipError_t dispatch(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, bool vec,
-                    hipStream_t s, int cus) {
-    Plan p = planned(m, n, k, FMT, cus);
-    if (p.splits == 1) return dispatch_tile<FMT>(p, a, b, c, m, n, k, vec, s);
+                    hipStream_t s, int cus, int epi) {
+    const int64_t nw = epi == kEpiGlu ? 2 * n : n;
+    Plan p = planned(m, nw, k, FMT, cus, epi == kEpiGlu);
+    if (p.splits == 1) return dispatch_tile<FMT>(p, a, b, c, m, nw, k, vec, s, n, epi);
     // Split K: partial tiles go to the device's scratch buffer, then one pass
-    // sums them in split order.
+    // sums them in split order and applies the epilogue.
     ScratchLease lease;
     void *scratch = nullptr;
-    const size_t bytes = static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(n) * 4;
+    const size_t bytes = static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(nw) * 4;
     hipError_t e = lease.acquire(bytes, s, &scratch);
     if (e != hipSuccess) return e;
     float *partial = static_cast<float *>(scratch);
-    e = dispatch_tile<FMT>(p, a, b, partial, m, n, k, vec, s);
-    if (e == hipSuccess) e = launch_reduce_splits(partial, c, m * n, p.splits, s);
+    e = dispatch_tile<FMT>(p, a, b, partial, m, nw, k, vec, s, n, epi);
+    if (e == hipSuccess) e = launch_reduce_splits(partial, c, m, n, nw, p.splits, epi, s);
     const hipError_t er = lease.release();
     return e != hipSuccess ? e : er;
 }
 
 }  // namespace
 
-hipError_t launch_reduce_splits(const float *partial, float *c, int64_t count, int splits, hipStream_t s) {
-    const int64_t grid = std::min<int64_t>((count + 255) / 256, 65536);
-    hipLaunchKernelGGL(reduce_splits, dim3(grid), dim3(256), 0, s, partial, c, count, splits);
+hipError_t launch_reduce_splits(const float *partial, float *c, int64_t m, int64_t no, int64_t nw, int splits,
+                                int epi, hipStream_t s) {
+    const int64_t grid = std::min<int64_t>((m * no + 255) / 256, 65536);
+    hipLaunchKernelGGL(reduce_splits, dim3(grid), dim3(256), 0, s, partial, c, m, no, nw, splits, epi);
     return hipGetLastError();
 }
 
@@ -509,7 +581,7 @@ bool set_gemm_plan_override(int bm, int bn, int splits) {
 }
 
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
-                       hipStream_t s) {
+                       hipStream_t s, int epi) {
     DeviceInfo di;
     hipError_t e = device_info(&di);
     if (e != hipSuccess) return e;
@@ -517,11 +589,11 @@ hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t
     const bool b16 = (reinterpret_cast<uintptr_t>(b) & 15u) == 0;
     if (fmt == FMT_F16) {
         const bool vec = a16 && b16 && (k % 8 == 0);
-        return dispatch<FMT_F16>(a, b, c, m, n, k, vec, s, di.cus);
+        return dispatch<FMT_F16>(a, b, c, m, n, k, vec, s, di.cus, epi);
     }
     const bool vec = a16;  // K % 32 == 0 always holds for Q8_0 and Q4_0
-    if (fmt == FMT_Q4_0) return dispatch<FMT_Q4_0>(a, b, c, m, n, k, vec, s, di.cus);
-    return dispatch<FMT_Q8_0>(a, b, c, m, n, k, vec, s, di.cus);
+    if (fmt == FMT_Q4_0) return dispatch<FMT_Q4_0>(a, b, c, m, n, k, vec, s, di.cus, epi);
+    return dispatch<FMT_Q8_0>(a, b, c, m, n, k, vec, s, di.cus, epi);
 }
 
 }  // namespace wq

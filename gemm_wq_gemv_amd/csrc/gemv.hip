@@ -1,4 +1,5 @@
-// Decode GEMV (M = 1): c[n] = sum_k a[k] * w[n, k] for f16, Q8_0 and Q4_0 weights.
+// Decode GEMV (M = 1): c[n] = sum_k a[k] * w[n, k] for f16, Q8_0 and Q4_0 weights
+// (or c[n] += that sum when the launcher's resid flag is set).
 //
 // The operation is the M = 1 case of dispatch_matmul_half / dispatch_matmul_q8 /
 // dispatch_matmul_q4 (lattice-inference 0.9.0, dispatch.rs) and of the kernels
@@ -58,7 +59,7 @@ template <int T, int R, bool FULL>
 __global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
                                                     const uint16_t *__restrict__ b,
                                                     float *__restrict__ c, int64_t n, int64_t k,
-                                                    int64_t groups) {
+                                                    int64_t groups, int resid) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
     const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) / kWave;
@@ -107,14 +108,14 @@ __global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
             const float s = wave_sum(acc[r]);
             if (lane == r) mine = s;
         }
-        if (lane < R && r0 + lane < n) c[r0 + lane] = mine;
+        if (lane < R && r0 + lane < n) c[r0 + lane] = resid ? c[r0 + lane] + mine : mine;
     }
 }
 
 // Any K, any 2-byte alignment of b: one wave per row, lanes stride over K.
 __global__ __launch_bounds__(256) void gemv_f16_any(const float *__restrict__ a,
                                                     const uint16_t *__restrict__ b,
-                                                    float *__restrict__ c, int64_t n, int64_t k) {
+                                                    float *__restrict__ c, int64_t n, int64_t k, int resid) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
     const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) / kWave;
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256) void gemv_f16_any(const float *__restrict__ a,
         float acc = 0.f;
         for (int64_t kk = lane; kk < k; kk += kWave) acc = fmaf(half_bits_to_float(brow[kk]), a[kk], acc);
         acc = wave_sum(acc);
-        if (lane == 0) c[row] = acc;
+        if (lane == 0) c[row] = resid ? c[row] + acc : acc;
     }
 }
 
@@ -246,7 +247,7 @@ template <int FMT, int J, int LPR, int SL>
 __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
                                                     const uint8_t *__restrict__ b,
                                                     float *__restrict__ c, int64_t n, int64_t k,
-                                                    int64_t passes) {
+                                                    int64_t passes, int resid) {
     extern __shared__ uint4 stage4[];
     constexpr int BB = QB<FMT>::kBytes;
     constexpr int CH = QB<FMT>::kChunks;
@@ -323,7 +324,10 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
         const float sum = rows_sum<SL, LPR>(acc, jl);
         const int sl_mine = jl / (LPR / SL);
         const int srow_mine = sl_mine * RPL + rsub;
-        if (jl % (LPR / SL) == 0 && srow_mine < rows) c[row0 + srow_mine] = sum;
+        if (jl % (LPR / SL) == 0 && srow_mine < rows) {
+            float *dst = c + row0 + srow_mine;
+            *dst = resid ? *dst + sum : sum;
+        }
     }
 }
 
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
 // blocks, reading each block with 2-byte loads.
 template <int FMT>
 __global__ __launch_bounds__(256) void gemv_q_any(const float *__restrict__ a, const uint8_t *__restrict__ b,
-                                                  float *__restrict__ c, int64_t n, int64_t k) {
+                                                  float *__restrict__ c, int64_t n, int64_t k, int resid) {
     constexpr int BB = QB<FMT>::kBytes;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(256) void gemv_q_any(const float *__restrict__ a, c
             acc = fmaf(half_bits_to_float(blk[0]), sumq, acc);
         }
         acc = wave_sum(acc);
-        if (lane == 0) c[row] = acc;
+        if (lane == 0) c[row] = resid ? c[row] + acc : acc;
     }
 }
 
@@ -384,7 +388,7 @@ inline int64_t balanced_workers(int64_t items, int64_t cap) {
 
 template <int T, int R>
 hipError_t run_f16_vec(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
-                       hipStream_t s, int cus) {
+                       hipStream_t s, int cus, int resid) {
     const int64_t groups = (n + R - 1) / R;
     const int64_t waves = balanced_workers(groups, static_cast<int64_t>(cus) * 16);
     const int64_t blocks = (waves + 3) / 4;
@@ -393,15 +397,15 @@ hipError_t run_f16_vec(const float *a, const uint16_t *b, float *c, int64_t n, i
         fprintf(stderr, "[wqmm] gemv_f16_vec<T=%d,R=%d,full=%d> n=%lld k=%lld grid=%lld block=256\n", T, R,
                 full ? 1 : 0, (long long)n, (long long)k, (long long)blocks);
     if (full)
-        hipLaunchKernelGGL((gemv_f16_vec<T, R, true>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups);
+        hipLaunchKernelGGL((gemv_f16_vec<T, R, true>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups, resid);
     else
-        hipLaunchKernelGGL((gemv_f16_vec<T, R, false>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups);
+        hipLaunchKernelGGL((gemv_f16_vec<T, R, false>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups, resid);
     return hipGetLastError();
 }
 
 template <int FMT, int J, int LPR, int SL>
 hipError_t run_q_staged_sl(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
-                           int cus) {
+                           int cus, int resid) {
     constexpr int S = SL * (kWave / LPR);
     const int row_bytes = static_cast<int>((k >> 5) * QB<FMT>::kBytes);
     const int64_t passes = (n + S - 1) / S;
@@ -412,7 +416,7 @@ hipError_t run_q_staged_sl(const float *a, const uint8_t *b, float *c, int64_t n
         fprintf(stderr,
                 "[wqmm] gemv_q_staged<fmt=%d,J=%d,LPR=%d,SL=%d> n=%lld k=%lld S=%d grid=%lld block=64 lds=%zu\n",
                 FMT, J, LPR, SL, (long long)n, (long long)k, S, (long long)blocks, lds);
-    hipLaunchKernelGGL((gemv_q_staged<FMT, J, LPR, SL>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k, passes);
+    hipLaunchKernelGGL((gemv_q_staged<FMT, J, LPR, SL>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k, passes, resid);
     return hipGetLastError();
 }
 
@@ -421,7 +425,7 @@ hipError_t run_q_staged_sl(const float *a, const uint8_t *b, float *c, int64_t n
 // decodes its rows after its loads land); SL is a power of two.
 template <int FMT, int J, int LPR>
 hipError_t run_q_staged(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
-                        int cus) {
+                        int cus, int resid) {
     constexpr int RPL = kWave / LPR;
     const int row_bytes = static_cast<int>((k >> 5) * QB<FMT>::kBytes);
     const int64_t s_fit = QB<FMT>::kStage / row_bytes;
@@ -430,16 +434,17 @@ hipError_t run_q_staged(const float *a, const uint8_t *b, float *c, int64_t n, i
     // measured faster than 8 or 16 rows for both formats at K = 2048.
     const int64_t sl_max = std::max<int64_t>(1, std::min<int64_t>(4, std::min(s_fit, s_fill) / RPL));
     if constexpr (J <= 2)
-        if (sl_max >= 4 && 4 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 4>(a, b, c, n, k, s, cus);
+        if (sl_max >= 4 && 4 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 4>(a, b, c, n, k, s, cus, resid);
     if constexpr (J <= 4)
-        if (sl_max >= 2 && 2 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 2>(a, b, c, n, k, s, cus);
-    return run_q_staged_sl<FMT, J, LPR, 1>(a, b, c, n, k, s, cus);
+        if (sl_max >= 2 && 2 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 2>(a, b, c, n, k, s, cus, resid);
+    return run_q_staged_sl<FMT, J, LPR, 1>(a, b, c, n, k, s, cus, resid);
 }
 
 // Staged kernel when K % 256 == 0, a and b are 16-byte aligned and a row fits
 // the stage with at most 8 blocks per lane; otherwise the plain kernel.
 template <int FMT>
-hipError_t launch_gemv_q(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s) {
+hipError_t launch_gemv_q(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
+                         int resid) {
     DeviceInfo di;
     hipError_t e = device_info(&di);
     if (e != hipSuccess) return e;
@@ -448,21 +453,21 @@ hipError_t launch_gemv_q(const float *a, const uint8_t *b, float *c, int64_t n, 
     if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= QB<FMT>::kStage && nb <= 512) {
         if (nb >= 64) {
             switch ((nb + 63) / 64) {
-                case 1: return run_q_staged<FMT, 1, 64>(a, b, c, n, k, s, di.cus);
-                case 2: return run_q_staged<FMT, 2, 64>(a, b, c, n, k, s, di.cus);
-                case 3: return run_q_staged<FMT, 3, 64>(a, b, c, n, k, s, di.cus);
-                case 4: return run_q_staged<FMT, 4, 64>(a, b, c, n, k, s, di.cus);
-                case 5: return run_q_staged<FMT, 5, 64>(a, b, c, n, k, s, di.cus);
-                case 6: return run_q_staged<FMT, 6, 64>(a, b, c, n, k, s, di.cus);
-                case 7: return run_q_staged<FMT, 7, 64>(a, b, c, n, k, s, di.cus);
-                default: return run_q_staged<FMT, 8, 64>(a, b, c, n, k, s, di.cus);
+                case 1: return run_q_staged<FMT, 1, 64>(a, b, c, n, k, s, di.cus, resid);
+                case 2: return run_q_staged<FMT, 2, 64>(a, b, c, n, k, s, di.cus, resid);
+                case 3: return run_q_staged<FMT, 3, 64>(a, b, c, n, k, s, di.cus, resid);
+                case 4: return run_q_staged<FMT, 4, 64>(a, b, c, n, k, s, di.cus, resid);
+                case 5: return run_q_staged<FMT, 5, 64>(a, b, c, n, k, s, di.cus, resid);
+                case 6: return run_q_staged<FMT, 6, 64>(a, b, c, n, k, s, di.cus, resid);
+                case 7: return run_q_staged<FMT, 7, 64>(a, b, c, n, k, s, di.cus, resid);
+                default: return run_q_staged<FMT, 8, 64>(a, b, c, n, k, s, di.cus, resid);
             }
         } else if (nb >= 32) {
-            if (nb == 32) return run_q_staged<FMT, 1, 32>(a, b, c, n, k, s, di.cus);
-            return run_q_staged<FMT, 2, 32>(a, b, c, n, k, s, di.cus);
+            if (nb == 32) return run_q_staged<FMT, 1, 32>(a, b, c, n, k, s, di.cus, resid);
+            return run_q_staged<FMT, 2, 32>(a, b, c, n, k, s, di.cus, resid);
         } else {
-            if (nb <= 16) return run_q_staged<FMT, 1, 16>(a, b, c, n, k, s, di.cus);
-            return run_q_staged<FMT, 2, 16>(a, b, c, n, k, s, di.cus);
+            if (nb <= 16) return run_q_staged<FMT, 1, 16>(a, b, c, n, k, s, di.cus, resid);
+            return run_q_staged<FMT, 2, 16>(a, b, c, n, k, s, di.cus, resid);
         }
     }
     const int64_t waves = balanced_workers(n, static_cast<int64_t>(di.cus) * 16);
@@ -470,46 +475,46 @@ hipError_t launch_gemv_q(const float *a, const uint8_t *b, float *c, int64_t n, 
     if (trace_enabled())
         fprintf(stderr, "[wqmm] gemv_q_any<fmt=%d> n=%lld k=%lld grid=%lld block=256\n", FMT, (long long)n,
                 (long long)k, (long long)blocks);
-    hipLaunchKernelGGL((gemv_q_any<FMT>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k);
+    hipLaunchKernelGGL((gemv_q_any<FMT>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, resid);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
-                           hipStream_t s) {
+                           hipStream_t s, bool resid) {
     DeviceInfo di;
     hipError_t e = device_info(&di);
     if (e != hipSuccess) return e;
     const int64_t nch = k / 8;
     const int64_t T = (nch + 63) / 64;
     if (k % 8 == 0 && aligned16(a) && aligned16(b) && T >= 1 && T <= 32) {
-        if (T <= 1) return run_f16_vec<1, 8>(a, b, c, n, k, s, di.cus);
-        if (T <= 2) return run_f16_vec<2, 8>(a, b, c, n, k, s, di.cus);
-        if (T <= 4) return run_f16_vec<4, 4>(a, b, c, n, k, s, di.cus);
-        if (T <= 8) return run_f16_vec<8, 2>(a, b, c, n, k, s, di.cus);
-        if (T <= 12) return run_f16_vec<12, 1>(a, b, c, n, k, s, di.cus);
-        if (T <= 16) return run_f16_vec<16, 1>(a, b, c, n, k, s, di.cus);
-        if (T <= 24) return run_f16_vec<24, 1>(a, b, c, n, k, s, di.cus);
-        return run_f16_vec<32, 1>(a, b, c, n, k, s, di.cus);
+        if (T <= 1) return run_f16_vec<1, 8>(a, b, c, n, k, s, di.cus, resid);
+        if (T <= 2) return run_f16_vec<2, 8>(a, b, c, n, k, s, di.cus, resid);
+        if (T <= 4) return run_f16_vec<4, 4>(a, b, c, n, k, s, di.cus, resid);
+        if (T <= 8) return run_f16_vec<8, 2>(a, b, c, n, k, s, di.cus, resid);
+        if (T <= 12) return run_f16_vec<12, 1>(a, b, c, n, k, s, di.cus, resid);
+        if (T <= 16) return run_f16_vec<16, 1>(a, b, c, n, k, s, di.cus, resid);
+        if (T <= 24) return run_f16_vec<24, 1>(a, b, c, n, k, s, di.cus, resid);
+        return run_f16_vec<32, 1>(a, b, c, n, k, s, di.cus, resid);
     }
     const int64_t waves = balanced_workers(n, static_cast<int64_t>(di.cus) * 16);
     const int64_t blocks = (waves + 3) / 4;
     if (trace_enabled())
         fprintf(stderr, "[wqmm] gemv_f16_any n=%lld k=%lld grid=%lld block=256\n", (long long)n, (long long)k,
                 (long long)blocks);
-    hipLaunchKernelGGL(gemv_f16_any, dim3(blocks), dim3(256), 0, s, a, b, c, n, k);
+    hipLaunchKernelGGL(gemv_f16_any, dim3(blocks), dim3(256), 0, s, a, b, c, n, k, resid);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
-                            hipStream_t s) {
-    return launch_gemv_q<QFMT_Q8_0>(a, b, c, n, k, s);
+                            hipStream_t s, bool resid) {
+    return launch_gemv_q<QFMT_Q8_0>(a, b, c, n, k, s, resid);
 }
 
 hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
-                            hipStream_t s) {
-    return launch_gemv_q<QFMT_Q4_0>(a, b, c, n, k, s);
+                            hipStream_t s, bool resid) {
+    return launch_gemv_q<QFMT_Q4_0>(a, b, c, n, k, s, resid);
 }
 
 }  // namespace wq

@@ -101,7 +101,9 @@ struct Skinny {
         int b, c;
     };
 
-    static __device__ __forceinline__ Lane lane_offsets(int lane, int64_t M, int64_t K) {
+    // glu: tiles t < NT/2 are gate rows and t >= NT/2 the matching up rows,
+    // each half addressed from its own base (row 4 * (t % (NT/2)) + c).
+    static __device__ __forceinline__ Lane lane_offsets(int lane, int64_t M, int64_t K, bool glu) {
         Lane L;
         L.b = lane >> 2;
         L.c = lane & 3;
@@ -111,7 +113,8 @@ struct Skinny {
         const uint64_t row_bytes = FMT == FMT_F16 ? 2ull * K : static_cast<uint64_t>(K >> 5) * QBB;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const uint64_t rb = static_cast<uint64_t>(4 * t + L.c) * row_bytes;
+            const int tt = glu ? t % (NT / 2) : t;
+            const uint64_t rb = static_cast<uint64_t>(4 * tt + L.c) * row_bytes;
             if constexpr (FMT == FMT_F16) {
                 L.w[t] = static_cast<uint32_t>(rb + 2 * E * L.b);
                 L.d[t] = 0;
@@ -126,13 +129,15 @@ struct Skinny {
         return L;
     }
 
-    // Loads one step.  ra / rw: resources whose base is the step's first
-    // column in A / in the workgroup's first weight row.  For the scalar
-    // variant: k0 = the lane's first column, a the matrix, wrows the
-    // workgroup's first f16 weight row and rows_left = N - (its index).
+    // Loads one step.  ra / rw / ru: resources whose base is the step's first
+    // column in A / in the workgroup's first weight row / in its first up row
+    // (ru serves tiles t >= NT/2 when glu).  For the scalar variant: k0 = the
+    // lane's first column, a the matrix, wrows / urows the f16 rows at those
+    // bases and rows_left the rows from a base to the end of its half.
     static __device__ __forceinline__ void load(Regs &r, const Lane &L, __amdgpu_buffer_rsrc_t ra,
-                                                __amdgpu_buffer_rsrc_t rw, const float *__restrict__ a,
-                                                const uint16_t *__restrict__ wrows, int64_t M, int64_t K,
+                                                __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t ru, bool glu,
+                                                const float *__restrict__ a, const uint16_t *__restrict__ wrows,
+                                                const uint16_t *__restrict__ urows, int64_t M, int64_t K,
                                                 int64_t rows_left, int64_t k0) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -157,16 +162,19 @@ struct Skinny {
         if constexpr (FMT == FMT_F16) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
+                const bool up = glu && t >= NT / 2;
                 if constexpr (VEC) {
+                    const __amdgpu_buffer_rsrc_t rt = up ? ru : rw;
 #pragma unroll
                     for (int q = 0; q < E / 8; ++q) {
-                        const u32x4 v = bload16(rw, L.w[t] + 16 * q);
+                        const u32x4 v = bload16(rt, L.w[t] + 16 * q);
 #pragma unroll
                         for (int u = 0; u < 4; ++u) r.w[t][4 * q + u] = v[u];
                     }
                 } else {
-                    // Rows past N repeat the last row (outputs never stored).
-                    const uint16_t *row = wrows + min<int64_t>(4 * t + L.c, rows_left - 1) * K;
+                    // Rows past the end repeat the last row (outputs never stored).
+                    const int tt = glu ? t % (NT / 2) : t;
+                    const uint16_t *row = (up ? urows : wrows) + min<int64_t>(4 * tt + L.c, rows_left - 1) * K;
 #pragma unroll
                     for (int e = 0; e < E; e += 2) {
                         const uint32_t lo = (k0 + e < K) ? row[k0 + e] : 0u;
@@ -179,16 +187,17 @@ struct Skinny {
             // WD dwords of codes: 4 (Q8_0) or 8 (Q4_0) weights per dword.
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                r.d[t] = bload2(rw, L.d[t]);
+                const __amdgpu_buffer_rsrc_t rt = (glu && t >= NT / 2) ? ru : rw;
+                r.d[t] = bload2(rt, L.d[t]);
                 if constexpr (WD == 1) {
-                    r.w[t][0] = bload4(rw, L.w[t]);
+                    r.w[t][0] = bload4(rt, L.w[t]);
                 } else if constexpr (WD == 2) {
-                    const u32x2 v = bload8(rw, L.w[t]);
+                    const u32x2 v = bload8(rt, L.w[t]);
                     r.w[t][0] = v[0], r.w[t][1] = v[1];
                 } else {
 #pragma unroll
                     for (int q = 0; q < WD / 4; ++q) {
-                        const u32x4 v = bload16(rw, L.w[t] + 16 * q);
+                        const u32x4 v = bload16(rt, L.w[t] + 16 * q);
 #pragma unroll
                         for (int u = 0; u < 4; ++u) r.w[t][4 * q + u] = v[u];
                     }
@@ -250,13 +259,16 @@ __device__ __forceinline__ float block_sum(float v) {
 }
 
 // Workgroup (grp, split) = (blockIdx.x % groups, blockIdx.x / groups) owns
-// weight rows [4*NT*grp, 4*NT*(grp+1)) and steps [split*sps,
-// min(nsteps, (split+1)*sps)); wave w takes steps w, w+W, ... of that range.
-// With one split the sums go to C, otherwise to out + split*M*N.
+// weight rows [4*NT*grp, 4*NT*(grp+1)) -- with the GLU epilogue, output
+// columns [2*NT*grp, 2*NT*(grp+1)): their gate rows and (NO later) their up
+// rows -- and steps [split*sps, min(nsteps, (split+1)*sps)); wave w takes
+// steps w, w+W, ... of that range.  N = weight rows, NO = output columns.
+// With one split the sums go to C [M, NO] through the epilogue, otherwise the
+// raw sums go to out + split*M*N with column = weight row.
 template <int FMT, int MB, int NT, int E, int P, int W, bool VEC>
 __global__ __launch_bounds__(W * 64) void gemm_skinny(const float *__restrict__ a, const void *__restrict__ bw,
                                                       float *__restrict__ out, int64_t M, int64_t N, int64_t K,
-                                                      int groups, int sps) {
+                                                      int groups, int sps, int splits, int64_t NO, int epi) {
     using S = Skinny<FMT, MB, NT, E, VEC>;
     constexpr int KS = S::KS;
     constexpr int NV = MB * NT * 4;  // accumulator values per lane
@@ -264,17 +276,25 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const float *__restrict__ 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int grp = static_cast<int>(blockIdx.x % groups), sp = static_cast<int>(blockIdx.x / groups);
-    const int64_t n0 = static_cast<int64_t>(grp) * 4 * NT;
+    const bool glu = epi == kEpiGlu;
+    // n0: first weight row (plain) or first output column (glu) of the group;
+    // g0 / u0: first gate / up weight row; rows_left: rows from g0 (or u0) to
+    // the end of its half of the matrix.
+    const int64_t n0 = static_cast<int64_t>(grp) * (glu ? 2 : 4) * NT;
+    const int64_t g0 = n0, u0 = glu ? NO + n0 : n0;
+    const int64_t rows_left = (glu ? NO : N) - n0;
     const int nsteps = static_cast<int>((K + KS - 1) / KS);
     const int nfull = static_cast<int>(K / KS);
     const int s0 = sp * sps, s1 = min(nsteps, s0 + sps);
 
-    const typename S::Lane L = S::lane_offsets(lane, M, K);
+    const typename S::Lane L = S::lane_offsets(lane, M, K, glu);
     const uint64_t row_bytes = FMT == FMT_F16 ? 2ull * K : static_cast<uint64_t>(K >> 5) * S::QBB;
-    const uint8_t *wbase = static_cast<const uint8_t *>(bw) + n0 * row_bytes;
-    const uint64_t wbytes = (N - n0) * row_bytes;  // from the workgroup's first row to the end
+    const uint8_t *wbase = static_cast<const uint8_t *>(bw) + g0 * row_bytes;
+    const uint8_t *ubase = static_cast<const uint8_t *>(bw) + u0 * row_bytes;
+    const uint64_t wbytes = (N - g0) * row_bytes, ubytes = (N - u0) * row_bytes;  // to the matrix end
     const uint64_t abytes = static_cast<uint64_t>(M) * K * 4;
-    const uint16_t *wrows = static_cast<const uint16_t *>(bw) + n0 * K;  // scalar f16 path
+    const uint16_t *wrows = static_cast<const uint16_t *>(bw) + g0 * K;  // scalar f16 path
+    const uint16_t *urows = static_cast<const uint16_t *>(bw) + u0 * K;
 
     v4f acc[MB][NT];
 #pragma unroll
@@ -286,7 +306,8 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const float *__restrict__ 
     auto load_step = [&](typename S::Regs &dst, int st) {
         const uint64_t wo = static_cast<uint64_t>(st) * S::kWStep, ao = static_cast<uint64_t>(st) * S::kAStep;
         S::load(dst, L, make_rsrc(reinterpret_cast<const uint8_t *>(a) + ao, abytes - ao),
-                make_rsrc(wbase + wo, wbytes - wo), a, wrows, M, K, N - n0, static_cast<int64_t>(st) * KS + E * L.b);
+                make_rsrc(wbase + wo, wbytes - wo), make_rsrc(ubase + wo, ubytes - wo), glu, a, wrows, urows, M, K,
+                rows_left, static_cast<int64_t>(st) * KS + E * L.b);
     };
 
     // Full steps of this wave: first, first + W, ... below min(s1, nfull).
@@ -333,16 +354,41 @@ __global__ __launch_bounds__(W * 64) void gemm_skinny(const float *__restrict__ 
                 if ((v & 15) == L.b) red[wv][v][L.c] = s;
             }
     __syncthreads();
+    if (splits == 1 && glu) {
+        // SwiGLU: gate tile t pairs with up tile t + NT/2 of the same columns.
+        for (int e = threadIdx.x; e < NV * 2; e += W * kWave) {
+            const int vg = e >> 2, j = e & 3;  // vg over (mb, t < NT/2, i)
+            const int mb = vg / (NT * 2), t = (vg >> 2) % (NT / 2), i = vg & 3;
+            const int v = (mb * NT + t) * 4 + i, vu = v + 2 * NT;
+            const int64_t row = 4 * mb + i, col = n0 + 4 * t + j;
+            if (row >= M || col >= NO) continue;
+            float g = red[0][v][j], u = red[0][vu][j];
+#pragma unroll
+            for (int w = 1; w < W; ++w) g += red[w][v][j], u += red[w][vu][j];
+            out[row * NO + col] = silu(g) * u;
+        }
+        return;
+    }
+    const bool resid = splits == 1 && epi == kEpiResidual;
     float *dst = out + static_cast<int64_t>(sp) * M * N;
     for (int e = threadIdx.x; e < NV * 4; e += W * kWave) {
         const int v = e >> 2, j = e & 3;
         const int mb = v / (NT * 4), t = (v >> 2) % NT, i = v & 3;
-        const int64_t row = 4 * mb + i, col = n0 + 4 * t + j;
-        if (row >= M || col >= N) continue;
+        const int64_t row = 4 * mb + i;
+        // Column of C (plain) or weight row (glu partial sums).
+        int64_t col = n0 + 4 * t + j;
+        bool ok = col < N;
+        if (glu) {
+            const int64_t oc = n0 + 4 * (t % (NT / 2)) + j;
+            ok = oc < NO;
+            col = t < NT / 2 ? oc : NO + oc;
+        }
+        if (row >= M || !ok) continue;
         float sum = red[0][v][j];
 #pragma unroll
         for (int w = 1; w < W; ++w) sum += red[w][v][j];
-        dst[row * N + col] = sum;
+        float *p = dst + row * N + col;
+        *p = resid ? *p + sum : sum;
     }
 }
 
@@ -370,48 +416,53 @@ struct SkPlan {
 
 // Workgroups for about kSkWavesPerCU waves per CU; K is split across
 // workgroups only as far as that needs, and every split keeps at least P+1
-// steps per wave.
+// steps per wave.  n = output columns (glu: 2*NT per group, else 4*NT).
 template <int FMT, int MB>
-SkPlan plan_for(int64_t n, int64_t k, int cus) {
+SkPlan plan_for(int64_t n, int64_t k, int cus, bool glu) {
     using C = SkCfg<FMT, MB>;
     const int64_t nsteps = (k + 16LL * C::E - 1) / (16LL * C::E);
-    const int64_t groups = (n + 4LL * C::NT - 1) / (4LL * C::NT);
+    const int64_t per = (glu ? 2LL : 4LL) * C::NT;
+    const int64_t groups = (n + per - 1) / per;
     int64_t want = (static_cast<int64_t>(kSkWavesPerCU) * cus + groups * kSkW - 1) / (groups * kSkW);
     want = std::max<int64_t>(1, std::min<int64_t>(want, nsteps / (static_cast<int64_t>(kSkW) * (C::P + 1))));
     const int64_t sps = (nsteps + want - 1) / want;
     return SkPlan{static_cast<int>(groups), static_cast<int>((nsteps + sps - 1) / sps), static_cast<int>(sps)};
 }
 
+// n = output columns; the weights have nw = n (or 2n with the GLU epilogue) rows.
 template <int FMT, int MB>
 hipError_t run_skinny(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, bool vec, int cus,
-                      hipStream_t s) {
+                      hipStream_t s, int epi) {
     using C = SkCfg<FMT, MB>;
-    const SkPlan p = plan_for<FMT, MB>(n, k, cus);
+    static_assert(C::NT % 2 == 0, "the GLU epilogue pairs tile halves");
+    const bool glu = epi == kEpiGlu;
+    const int64_t nw = glu ? 2 * n : n;
+    const SkPlan p = plan_for<FMT, MB>(n, k, cus, glu);
     ScratchLease lease;
     float *out = c;
     if (p.splits > 1) {
         void *scratch = nullptr;
         hipError_t e = lease.acquire(
-            static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(n) * 4, s, &scratch);
+            static_cast<size_t>(p.splits) * static_cast<size_t>(m) * static_cast<size_t>(nw) * 4, s, &scratch);
         if (e != hipSuccess) return e;
         out = static_cast<float *>(scratch);
     }
     if (trace_enabled())
         fprintf(stderr,
                 "[wqmm] gemm_skinny<fmt=%d,MB=%d,NT=%d,E=%d,P=%d,W=%d,vec=%d> m=%lld n=%lld k=%lld groups=%d "
-                "splits=%d sps=%d\n",
+                "splits=%d sps=%d epi=%d\n",
                 FMT, MB, C::NT, C::E, C::P, kSkW, vec, (long long)m, (long long)n, (long long)k, p.groups,
-                p.splits, p.sps);
+                p.splits, p.sps, epi);
     const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(p.groups) * p.splits));
     if (vec)
         hipLaunchKernelGGL((gemm_skinny<FMT, MB, C::NT, C::E, C::P, kSkW, true>), grid, dim3(kSkW * 64), 0, s, a,
-                           b, out, m, n, k, p.groups, p.sps);
+                           b, out, m, nw, k, p.groups, p.sps, p.splits, n, epi);
     else
         hipLaunchKernelGGL((gemm_skinny<FMT, MB, C::NT, C::E, C::P, kSkW, false>), grid, dim3(kSkW * 64), 0, s, a,
-                           b, out, m, n, k, p.groups, p.sps);
+                           b, out, m, nw, k, p.groups, p.sps, p.splits, n, epi);
     hipError_t e = hipGetLastError();
     if (p.splits > 1) {
-        if (e == hipSuccess) e = launch_reduce_splits(out, c, m * n, p.splits, s);
+        if (e == hipSuccess) e = launch_reduce_splits(out, c, m, n, nw, p.splits, epi, s);
         const hipError_t er = lease.release();
         if (e == hipSuccess) e = er;
     }
@@ -420,19 +471,19 @@ hipError_t run_skinny(const float *a, const void *b, float *c, int64_t m, int64_
 
 template <int FMT>
 hipError_t run_fmt(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, bool vec, int cus,
-                   hipStream_t s) {
+                   hipStream_t s, int epi) {
     switch ((m + 3) / 4) {
-        case 1: return run_skinny<FMT, 1>(a, b, c, m, n, k, vec, cus, s);
-        case 2: return run_skinny<FMT, 2>(a, b, c, m, n, k, vec, cus, s);
-        case 3: return run_skinny<FMT, 3>(a, b, c, m, n, k, vec, cus, s);
-        default: return run_skinny<FMT, 4>(a, b, c, m, n, k, vec, cus, s);
+        case 1: return run_skinny<FMT, 1>(a, b, c, m, n, k, vec, cus, s, epi);
+        case 2: return run_skinny<FMT, 2>(a, b, c, m, n, k, vec, cus, s, epi);
+        case 3: return run_skinny<FMT, 3>(a, b, c, m, n, k, vec, cus, s, epi);
+        default: return run_skinny<FMT, 4>(a, b, c, m, n, k, vec, cus, s, epi);
     }
 }
 
 }  // namespace
 
 hipError_t launch_skinny(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
-                         hipStream_t s) {
+                         hipStream_t s, int epi) {
     if (m < 1 || m > 16) return hipErrorInvalidValue;
     DeviceInfo di;
     hipError_t e = device_info(&di);
@@ -440,10 +491,10 @@ hipError_t launch_skinny(const float *a, const void *b, int fmt, float *c, int64
     const bool a16 = (reinterpret_cast<uintptr_t>(a) & 15) == 0;
     if (fmt == FMT_F16) {
         const bool vec = a16 && (reinterpret_cast<uintptr_t>(b) & 15) == 0 && k % 8 == 0;
-        return run_fmt<FMT_F16>(a, b, c, m, n, k, vec, di.cus, s);
+        return run_fmt<FMT_F16>(a, b, c, m, n, k, vec, di.cus, s, epi);
     }
-    if (fmt == FMT_Q4_0) return run_fmt<FMT_Q4_0>(a, b, c, m, n, k, a16, di.cus, s);
-    return run_fmt<FMT_Q8_0>(a, b, c, m, n, k, a16, di.cus, s);
+    if (fmt == FMT_Q4_0) return run_fmt<FMT_Q4_0>(a, b, c, m, n, k, a16, di.cus, s, epi);
+    return run_fmt<FMT_Q8_0>(a, b, c, m, n, k, a16, di.cus, s, epi);
 }
 
 }  // namespace wq

@@ -87,6 +87,14 @@ __device__ __forceinline__ float rows_sum(const float (&v)[N], int g) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
+// SiLU as on the pages' silu_mul kernel: x / (1 + e^-x), in f32.
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// Epilogues (the values of wq_epilogue in wqmm.h).  Residual: C += A.B^T.
+// GLU: the weights hold 2*NO rows (gate rows, then up rows) and
+// C[m, j] = silu(g) * u for the gate sum g (row j) and up sum u (row NO + j).
+constexpr int kEpiNone = 0, kEpiResidual = 1, kEpiGlu = 2;
+
 // ------------------------------------------------------------------- host --
 struct DeviceInfo {
     int cus;  // compute units of the current device
@@ -96,19 +104,23 @@ hipError_t device_info(DeviceInfo *out);
 
 // Launchers.  Arguments are already validated by the C-ABI layer; these only
 // pick a kernel variant and grid and enqueue it on `s`.
+// resid: c[n] += the dot product instead of c[n] = it.
 hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
-                           hipStream_t s);
+                           hipStream_t s, bool resid = false);
 hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
-                            hipStream_t s);
+                            hipStream_t s, bool resid = false);
 hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
-                            hipStream_t s);
+                            hipStream_t s, bool resid = false);
+// n = output columns; with kEpiGlu the weights have 2n rows.
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,
-                       int64_t k, hipStream_t s);
+                       int64_t k, hipStream_t s, int epi = kEpiNone);
 // Small-M weight-streaming product (M <= 16 rows of A per launch).
 hipError_t launch_skinny(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
-                         hipStream_t s);
-// C[i] = sum of partial[s * count + i] over s < splits, in split order.
-hipError_t launch_reduce_splits(const float *partial, float *c, int64_t count, int splits, hipStream_t s);
+                         hipStream_t s, int epi = kEpiNone);
+// C [m, no] from split partial sums [splits][m][nw] summed in split order,
+// then the epilogue (nw = no, or 2 * no for kEpiGlu: gate then up columns).
+hipError_t launch_reduce_splits(const float *partial, float *c, int64_t m, int64_t no, int64_t nw, int splits,
+                                int epi, hipStream_t s);
 // Tile shape and K-split count the GEMM picks for a problem on `cus` CUs.
 void gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits);
 // Test hook: force the GEMM tiling (bm, bn from the compiled set; splits >= 1,

@@ -142,12 +142,15 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 bool known_format(int fmt) { return fmt == WQ_FMT_F16 || fmt == WQ_FMT_Q8_0 || fmt == WQ_FMT_Q4_0; }
 
+bool known_epilogue(int epi) { return epi == WQ_EPI_NONE || epi == WQ_EPI_RESIDUAL || epi == WQ_EPI_SWIGLU; }
+
 // Validates a product call.  Returns WQ_OK with *noop = true when nothing is
 // to be done (m == 0 or n == 0), WQ_OK with *noop = false when a launch
-// follows, or an error status.
+// follows, or an error status.  The weights have n rows, or 2n for SWIGLU.
 int validate(const float *a, const void *b, const float *c, int64_t m, int64_t n, int64_t k, int fmt,
-             bool *noop) {
+             bool *noop, int epi = WQ_EPI_NONE) {
     *noop = false;
+    if (!known_epilogue(epi)) return WQ_ERR_EPILOGUE;
     if (!known_format(fmt)) return WQ_ERR_FORMAT;
     if (m < 0 || n < 0 || k < 0) return WQ_ERR_SHAPE;
     if (m == 0 || n == 0) {
@@ -155,14 +158,17 @@ int validate(const float *a, const void *b, const float *c, int64_t m, int64_t n
         return WQ_OK;
     }
     if (fmt != WQ_FMT_F16 && (k == 0 || k % 32 != 0)) return WQ_ERR_K;
-    int64_t a_elems, c_elems, b_bytes, a_bytes, c_bytes;
+    int64_t a_elems, c_elems, b_bytes, a_bytes, c_bytes, nw;
+    if (!mul_ok(n, epi == WQ_EPI_SWIGLU ? 2 : 1, &nw)) return WQ_ERR_SHAPE;
     if (!mul_ok(m, k, &a_elems) || !mul_ok(a_elems, 4, &a_bytes)) return WQ_ERR_SHAPE;
     if (!mul_ok(m, n, &c_elems) || !mul_ok(c_elems, 4, &c_bytes)) return WQ_ERR_SHAPE;
+    int64_t glu_bytes;  // the M == 1 route's scratch: [m, 2n] f32 sums
+    if (epi == WQ_EPI_SWIGLU && !mul_ok(c_bytes, 2, &glu_bytes)) return WQ_ERR_SHAPE;
     if (fmt == WQ_FMT_F16) {
         int64_t nk;
-        if (!mul_ok(n, k, &nk) || !mul_ok(nk, 2, &b_bytes)) return WQ_ERR_SHAPE;
+        if (!mul_ok(nw, k, &nk) || !mul_ok(nk, 2, &b_bytes)) return WQ_ERR_SHAPE;
     } else {
-        if (!mul_ok(n, (k / 32) * (fmt == WQ_FMT_Q8_0 ? 34 : 18), &b_bytes)) return WQ_ERR_SHAPE;
+        if (!mul_ok(nw, (k / 32) * (fmt == WQ_FMT_Q8_0 ? 34 : 18), &b_bytes)) return WQ_ERR_SHAPE;
     }
     if (!c) return WQ_ERR_NULL;
     if (k > 0 && (!a || !b)) return WQ_ERR_NULL;
@@ -183,32 +189,61 @@ int auto_route(int64_t m, int fmt) {
 }
 bool known_route(int r) { return r == WQ_ROUTE_GEMV || r == WQ_ROUTE_GEMM || r == WQ_ROUTE_SKINNY; }
 
-int run_gemv(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s) {
-    // One GEMV launch per row of A (the route for M == 1; forced otherwise).
+// Kernel-side epilogue code of a wq_epilogue value.
+int kernel_epi(int epi) {
+    return epi == WQ_EPI_RESIDUAL ? wq::kEpiResidual : epi == WQ_EPI_SWIGLU ? wq::kEpiGlu : wq::kEpiNone;
+}
+
+// One GEMV launch per row of A over n weight rows into c [m, n] (ldc = n),
+// adding into c when resid is set.
+int gemv_rows(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
+              bool resid) {
     for (int64_t i = 0; i < m; ++i) {
         const float *ai = a + i * k;
         float *ci = c + i * n;
-        hipError_t e = (fmt == WQ_FMT_F16)    ? wq::launch_gemv_f16(ai, static_cast<const uint16_t *>(b), ci, n, k, s)
-                       : (fmt == WQ_FMT_Q8_0) ? wq::launch_gemv_q8_0(ai, static_cast<const uint8_t *>(b), ci, n, k, s)
-                                              : wq::launch_gemv_q4_0(ai, static_cast<const uint8_t *>(b), ci, n, k, s);
+        const auto *b8 = static_cast<const uint8_t *>(b);
+        hipError_t e = (fmt == WQ_FMT_F16)
+                           ? wq::launch_gemv_f16(ai, static_cast<const uint16_t *>(b), ci, n, k, s, resid)
+                       : (fmt == WQ_FMT_Q8_0) ? wq::launch_gemv_q8_0(ai, b8, ci, n, k, s, resid)
+                                              : wq::launch_gemv_q4_0(ai, b8, ci, n, k, s, resid);
         if (e != hipSuccess) return WQ_ERR_LAUNCH;
         wq::g_route_count[WQ_ROUTE_GEMV].fetch_add(1, std::memory_order_relaxed);
     }
     return WQ_OK;
 }
 
-int run_gemm(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s) {
-    hipError_t e = wq::launch_gemm(a, b, fmt, c, m, n, k, s);
+// The GEMV route (M == 1; forced otherwise).  SWIGLU: gate and up rows are
+// contiguous, so one GEMV per row of A covers all 2n rows into a [m, 2n]
+// scratch, and one element-wise pass writes silu(gate) * up into c.
+int run_gemv(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
+             int epi) {
+    if (epi != WQ_EPI_SWIGLU) return gemv_rows(a, b, c, m, n, k, fmt, s, epi == WQ_EPI_RESIDUAL);
+    wq::ScratchLease lease;
+    void *scratch = nullptr;
+    if (lease.acquire(static_cast<size_t>(m) * static_cast<size_t>(2 * n) * 4, s, &scratch) != hipSuccess)
+        return WQ_ERR_LAUNCH;
+    float *gu = static_cast<float *>(scratch);
+    int st = gemv_rows(a, b, gu, m, 2 * n, k, fmt, s, false);
+    if (st == WQ_OK && wq::launch_reduce_splits(gu, c, m, n, 2 * n, 1, wq::kEpiGlu, s) != hipSuccess)
+        st = WQ_ERR_LAUNCH;
+    if (lease.release() != hipSuccess && st == WQ_OK) st = WQ_ERR_LAUNCH;
+    return st;
+}
+
+int run_gemm(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
+             int epi) {
+    hipError_t e = wq::launch_gemm(a, b, fmt, c, m, n, k, s, kernel_epi(epi));
     if (e != hipSuccess) return WQ_ERR_LAUNCH;
     wq::g_route_count[WQ_ROUTE_GEMM].fetch_add(1, std::memory_order_relaxed);
     return WQ_OK;
 }
 
 // One small-M launch per block of up to kSkinnyRows rows of A.
-int run_skinny(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s) {
+int run_skinny(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
+               int epi) {
     for (int64_t i = 0; i < m; i += kSkinnyRows) {
         const int64_t rows = m - i < kSkinnyRows ? m - i : kSkinnyRows;
-        hipError_t e = wq::launch_skinny(a + i * k, b, fmt, c + i * n, rows, n, k, s);
+        hipError_t e = wq::launch_skinny(a + i * k, b, fmt, c + i * n, rows, n, k, s, kernel_epi(epi));
         if (e != hipSuccess) return WQ_ERR_LAUNCH;
         wq::g_route_count[WQ_ROUTE_SKINNY].fetch_add(1, std::memory_order_relaxed);
     }
@@ -220,11 +255,23 @@ int run_zero(float *c, int64_t m, int64_t n, hipStream_t s) {
     return status_of(wq::launch_fill_zero(c, m * n, s));
 }
 
+// Validated product with an epilogue on the route the M rule (or the forced
+// route) picks.
+int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, int epi,
+               hipStream_t s) {
+    if (k == 0) return epi == WQ_EPI_RESIDUAL ? WQ_OK : run_zero(c, m, n, s);  // silu(0) * 0 = 0
+    int route = wq::g_forced_route.load(std::memory_order_relaxed);
+    if (route == WQ_ROUTE_AUTO) route = auto_route(m, fmt);
+    if (route == WQ_ROUTE_GEMV) return run_gemv(a, b, c, m, n, k, fmt, s, epi);
+    if (route == WQ_ROUTE_SKINNY) return run_skinny(a, b, c, m, n, k, fmt, s, epi);
+    return run_gemm(a, b, c, m, n, k, fmt, s, epi);
+}
+
 }  // namespace
 
 extern "C" {
 
-int wq_abi_version(void) { return 101; }
+int wq_abi_version(void) { return 102; }
 
 const char *wq_status_str(int status) {
     switch (status) {
@@ -237,6 +284,7 @@ const char *wq_status_str(int status) {
         case WQ_ERR_LAUNCH: return "HIP kernel launch failed";
         case WQ_ERR_ALIAS: return "output overlaps an input";
         case WQ_ERR_ROUTE: return "unknown route";
+        case WQ_ERR_EPILOGUE: return "unknown epilogue";
         default: return "unknown status";
     }
 }
@@ -247,21 +295,21 @@ int wq_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t 
     if (st != WQ_OK || noop) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (k == 0) return run_zero(c, 1, n, s);
-    return run_gemv(a, b, c, 1, n, k, WQ_FMT_F16, s);
+    return run_gemv(a, b, c, 1, n, k, WQ_FMT_F16, s, WQ_EPI_NONE);
 }
 
 int wq_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, void *stream) {
     bool noop;
     int st = validate(a, b, c, 1, n, k, WQ_FMT_Q8_0, &noop);
     if (st != WQ_OK || noop) return st;
-    return run_gemv(a, b, c, 1, n, k, WQ_FMT_Q8_0, static_cast<hipStream_t>(stream));
+    return run_gemv(a, b, c, 1, n, k, WQ_FMT_Q8_0, static_cast<hipStream_t>(stream), WQ_EPI_NONE);
 }
 
 int wq_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, void *stream) {
     bool noop;
     int st = validate(a, b, c, 1, n, k, WQ_FMT_Q4_0, &noop);
     if (st != WQ_OK || noop) return st;
-    return run_gemv(a, b, c, 1, n, k, WQ_FMT_Q4_0, static_cast<hipStream_t>(stream));
+    return run_gemv(a, b, c, 1, n, k, WQ_FMT_Q4_0, static_cast<hipStream_t>(stream), WQ_EPI_NONE);
 }
 
 int wq_gemm_f16(const float *a, const uint16_t *b, float *c, int64_t m, int64_t n, int64_t k, void *stream) {
@@ -270,34 +318,33 @@ int wq_gemm_f16(const float *a, const uint16_t *b, float *c, int64_t m, int64_t 
     if (st != WQ_OK || noop) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (k == 0) return run_zero(c, m, n, s);
-    return run_gemm(a, b, c, m, n, k, WQ_FMT_F16, s);
+    return run_gemm(a, b, c, m, n, k, WQ_FMT_F16, s, WQ_EPI_NONE);
 }
 
 int wq_gemm_q8_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t n, int64_t k, void *stream) {
     bool noop;
     int st = validate(a, b, c, m, n, k, WQ_FMT_Q8_0, &noop);
     if (st != WQ_OK || noop) return st;
-    return run_gemm(a, b, c, m, n, k, WQ_FMT_Q8_0, static_cast<hipStream_t>(stream));
+    return run_gemm(a, b, c, m, n, k, WQ_FMT_Q8_0, static_cast<hipStream_t>(stream), WQ_EPI_NONE);
 }
 
 int wq_gemm_q4_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t n, int64_t k, void *stream) {
     bool noop;
     int st = validate(a, b, c, m, n, k, WQ_FMT_Q4_0, &noop);
     if (st != WQ_OK || noop) return st;
-    return run_gemm(a, b, c, m, n, k, WQ_FMT_Q4_0, static_cast<hipStream_t>(stream));
+    return run_gemm(a, b, c, m, n, k, WQ_FMT_Q4_0, static_cast<hipStream_t>(stream), WQ_EPI_NONE);
 }
 
 int wq_matmul(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, void *stream) {
+    return wq_matmul_ex(a, b, c, m, n, k, fmt, WQ_EPI_NONE, stream);
+}
+
+int wq_matmul_ex(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, int epi,
+                 void *stream) {
     bool noop;
-    int st = validate(a, b, c, m, n, k, fmt, &noop);
+    int st = validate(a, b, c, m, n, k, fmt, &noop, epi);
     if (st != WQ_OK || noop) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (k == 0) return run_zero(c, m, n, s);
-    int route = wq::g_forced_route.load(std::memory_order_relaxed);
-    if (route == WQ_ROUTE_AUTO) route = auto_route(m, fmt);
-    if (route == WQ_ROUTE_GEMV) return run_gemv(a, b, c, m, n, k, fmt, s);
-    if (route == WQ_ROUTE_SKINNY) return run_skinny(a, b, c, m, n, k, fmt, s);
-    return run_gemm(a, b, c, m, n, k, fmt, s);
+    return run_routed(a, b, c, m, n, k, fmt, epi, static_cast<hipStream_t>(stream));
 }
 
 int wq_pack_f16(const float *w, uint16_t *out, int64_t count, void *stream) {

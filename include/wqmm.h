@@ -77,7 +77,8 @@ typedef enum wq_status {
     WQ_ERR_ALIGN = 5,   /* a or c not 4-byte aligned, or b not 2-byte aligned */
     WQ_ERR_LAUNCH = 6,  /* the HIP runtime failed to enqueue a kernel or scratch */
     WQ_ERR_ALIAS = 7,   /* c overlaps a or b */
-    WQ_ERR_ROUTE = 8    /* not a wq_route value */
+    WQ_ERR_ROUTE = 8,   /* not a wq_route value */
+    WQ_ERR_EPILOGUE = 9 /* not a wq_epilogue value */
 } wq_status;
 
 /* Kernel families wq_matmul can route to. */
@@ -121,6 +122,49 @@ int wq_gemm_q4_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t 
  * M > 1 batched product). */
 int wq_matmul(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt,
               void *stream);
+
+/* Epilogues fused into the product (wq_matmul_ex). */
+typedef enum wq_epilogue {
+    WQ_EPI_NONE = 0,     /* c = a . b^T, as wq_matmul */
+    WQ_EPI_RESIDUAL = 1, /* c += a . b^T: c holds the residual stream on entry */
+    WQ_EPI_SWIGLU = 2    /* b has 2n rows, gate rows 0..n-1 then up rows n..2n-1;
+                            c = silu(a . gate^T) * (a . up^T), silu(x) = x / (1 + e^-x) */
+} wq_epilogue;
+
+/* wq_matmul with an epilogue applied to each output before it is stored, so
+ * that the extra pass over C (or over a [M, 2n] gate||up buffer) that the
+ * pages spend on a separate element-wise kernel is not needed.
+ *
+ * WQ_EPI_RESIDUAL -- c[i,j] = c[i,j] + sum_k a[i,k] w[j,k].  Passage:
+ *   encode_layer_prefill on the oxibonsai-kernels 0.1.4 page,
+ *   gpu_backend/metal_prefill/functions.rs, which adds the attention output
+ *   and down projections into the hidden state inside the GEMM
+ *   (gemm_q1_v7_residual), and whose ternary twin spells the same step as a
+ *   GEMM plus residual_add; add_buf on the lattice-inference 0.1.2 page.
+ *   The residual is read from c itself (in place, as those calls do).
+ * WQ_EPI_SWIGLU -- b is the fused gate||up weight, [2n, K] in the format's
+ *   layout (gate rows first, then up rows; the up half starts at row n, byte
+ *   n * row_bytes), and c is [m, n]:
+ *   c[i,j] = silu(g) * u, g = sum_k a[i,k] gate[j,k], u = sum_k a[i,k] up[j,k].
+ *   Passage: same page, fused_gate_up_swiglu_gemm, and the ternary twin's
+ *   GEMM over n_rows = 2 * inter followed by batched_swiglu;
+ *   dispatch_silu_mul_fused on the lattice-inference 0.9.0 page (first half
+ *   of a gate||up buffer = silu(first half) * second half) and kernel
+ *   silu_mul on the 0.1.2 page (silu(g) = g / (1 + exp(-g)), times up).
+ *   Tiled-GEMM and small-M routes apply the epilogue in the kernel when K is
+ *   not split, else in the pass that sums the splits; the M == 1 route runs
+ *   the GEMV over all 2n rows into scratch (2*M*n*4 bytes, stream-ordered as
+ *   for split-K) and then one element-wise pass.
+ * Sub-matrices of fused weight buffers (gate or up alone, q||k||v) need no
+ * offset argument: pass b advanced by whole rows (row r starts at byte
+ * r * row_bytes, always 2-byte aligned).
+ * Routing and K rules are those of wq_matmul.  K == 0 (f16): NONE writes
+ * zeros, RESIDUAL leaves c as it is, SWIGLU writes silu(0) * 0 = 0.
+ * Returns WQ_ERR_EPILOGUE for an unknown epi (before any other check);
+ * otherwise as wq_matmul, with the weight bounds (overlap, size) taken over
+ * the 2n rows for SWIGLU. */
+int wq_matmul_ex(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt,
+                 int epi, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Weight preparation (done once, at load time).

@@ -28,7 +28,7 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("wq_gemv_f16", "wq_gemv_q8_0", "wq_gemv_q4_0", "wq_gemm_f16", "wq_gemm_q8_0",
-                 "wq_gemm_q4_0", "wq_matmul", "wq_pack_f16", "wq_quantize_q8_0"):
+                 "wq_gemm_q4_0", "wq_matmul", "wq_matmul_ex", "wq_pack_f16", "wq_quantize_q8_0"):
         assert want in names
 
 
@@ -50,8 +50,8 @@ def test_single_hip_runtime_in_process():
 
 
 def test_abi_and_status_strings():
-    assert wq.wq_abi_version() == 101
-    for st in range(0, 9):
+    assert wq.wq_abi_version() == 102
+    for st in range(0, 10):
         assert wq.status_str(st)
     assert wq.status_str(99) == "unknown status"
 
@@ -101,6 +101,34 @@ def test_shape_format_null_align_alias():
     assert L.wq_pack_f16(A, B, 0, None) == wq.WQ_OK
     assert L.wq_pack_f16(None, B, 5, None) == wq.WQ_ERR_NULL
     assert L.wq_quantize_q8_0(A, B + 1, 64, None) == wq.WQ_ERR_ALIGN
+
+
+def test_epilogue_validation():
+    EX = L.wq_matmul_ex
+    # An unknown epilogue is reported before anything else is looked at.
+    for epi in (-1, 3, 99):
+        assert EX(A, B, C, 2, 8, 64, wq.WQ_FMT_F16, epi, None) == wq.WQ_ERR_EPILOGUE
+        assert EX(None, None, None, -1, 8, 64, 7, epi, None) == wq.WQ_ERR_EPILOGUE
+    for epi in (wq.WQ_EPI_NONE, wq.WQ_EPI_RESIDUAL, wq.WQ_EPI_SWIGLU):
+        assert EX(None, None, None, 0, 8, 64, wq.WQ_FMT_Q8_0, epi, None) == wq.WQ_OK  # m == 0
+        assert EX(None, None, None, 4, 0, 64, wq.WQ_FMT_Q4_0, epi, None) == wq.WQ_OK  # n == 0
+        assert EX(A, B, C, 2, 8, 48, wq.WQ_FMT_Q8_0, epi, None) == wq.WQ_ERR_K
+        assert EX(A, B, C, 2, 8, 64, 5, epi, None) == wq.WQ_ERR_FORMAT
+        assert EX(A, B, None, 2, 8, 64, wq.WQ_FMT_F16, epi, None) == wq.WQ_ERR_NULL
+        assert EX(A, B, C + 2, 2, 8, 64, wq.WQ_FMT_F16, epi, None) == wq.WQ_ERR_ALIGN
+        assert EX(A, B, A + 8, 2, 8, 64, wq.WQ_FMT_F16, epi, None) == wq.WQ_ERR_ALIAS
+    # SwiGLU weights span 2n rows: for f16 n = 8, K = 64 that is 2048 bytes, so a
+    # c starting 1536 bytes into b overlaps the up half.
+    assert EX(A, B, B + 1536, 1, 8, 64, wq.WQ_FMT_F16, wq.WQ_EPI_SWIGLU, None) == wq.WQ_ERR_ALIAS
+    assert EX(A, B, B + 1020, 1, 8, 64, wq.WQ_FMT_F16, wq.WQ_EPI_NONE, None) == wq.WQ_ERR_ALIAS
+    # Q4_0 up half: b spans 2 * 8 * 2 * 18 = 576 bytes.
+    assert EX(A, B, B + 500, 1, 8, 64, wq.WQ_FMT_Q4_0, wq.WQ_EPI_SWIGLU, None) == wq.WQ_ERR_ALIAS
+    # 2n rows overflow int64.
+    assert EX(A, B, C, 1, 1 << 62, 64, wq.WQ_FMT_F16, wq.WQ_EPI_SWIGLU, None) == wq.WQ_ERR_SHAPE
+    import torch
+    with pytest.raises(ValueError):  # the binding checks b against 2n rows for SwiGLU
+        wq.wq_matmul_ex(torch.zeros(64), torch.zeros(8 * 64, dtype=torch.uint16), torch.zeros(8), 1, 8, 64,
+                        wq.WQ_FMT_F16, wq.WQ_EPI_SWIGLU)
 
 
 def test_routing_rule():

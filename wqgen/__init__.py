@@ -7,7 +7,8 @@ and never multiplies, so it holds none of the matmul's arithmetic.
 Stream convention: activations A come from stream 0 and weights B from
 stream 1 of the same seed, so a workload is fixed by (seed, shapes).  Q4_0
 weight bytes (no Q4_0 encoder is on the pages) come straight from stream 2 as
-random codes and scale bit patterns.
+random codes and scale bit patterns.  Residual-stream values (the C that a
+residual epilogue adds into) come from stream 3.
 """
 from __future__ import annotations
 
@@ -24,6 +25,7 @@ _LIB = os.path.join(_HERE, "libwqgen.so")
 STREAM_A = 0
 STREAM_B = 1
 STREAM_Q4 = 2
+STREAM_R = 3
 WEIGHT_STD = 0.02  # B ~ N(0, 0.02): 0.02 is the standard deviation
 
 
@@ -89,6 +91,11 @@ def normal(shape, seed: int = 0, stream: int = 0, mean: float = 0.0,
 def activations(m: int, k: int, seed: int = 0) -> np.ndarray:
     """A ~ N(0, 1), float32 [m, k], row-major; row i is the same for every m > i."""
     return normal((m, k), seed=seed, stream=STREAM_A)
+
+
+def residual(m: int, n: int, seed: int = 0) -> np.ndarray:
+    """Residual stream R ~ N(0, 1), float32 [m, n]."""
+    return normal((m, n), seed=seed, stream=STREAM_R)
 
 
 def weights(n: int, k: int, seed: int = 0, std: float = WEIGHT_STD) -> np.ndarray:

@@ -16,7 +16,9 @@ HIP events around each launch on the stream it runs on, inside the timed
 region.  ``cpu_baseline`` times the CPU oracle (all host cores it uses) on the
 same suite.  ``secondary`` reports the other configurations: the Q8_0 and
 Q4_0 decode suites, the f16 prefill GEMM at M = 512, the Q8_0 and Q4_0 M
-sweeps, and a plain device copy as the achievable-bandwidth reference.  Q4_0
+sweeps, the fused residual and SwiGLU epilogues against the same product
+followed by separate element-wise kernels, and a plain device copy as the
+achievable-bandwidth reference.  Q4_0
 weights are synthetic bytes (random codes and scales) since no Q4_0 encoder is
 given.
 """
@@ -86,7 +88,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-secondary", action="store_true", help="headline suite only")
-    p.add_argument("--only", choices=["f16", "q8", "q4", "prefill", "sweep"], default=None,
+    p.add_argument("--only", choices=["f16", "q8", "q4", "prefill", "sweep", "epi"], default=None,
                    help="run one workload only (for profiling); prints no headline line")
     return p.parse_args()
 
@@ -169,6 +171,55 @@ def time_launches(torch, fn, iters, warmup):
     if host > 0.9 * e0.elapsed_time(s) / 1e3:
         log(f"warning: host enqueue ({host * 1e3:.2f} ms) outlasted the stream hold; GPU time may include gaps")
     return s.elapsed_time(e) / 1e3 / iters
+
+
+def epilogue_bench(torch, wq, wqgen, seed, iters, warmup):
+    """Fused epilogues on the suite's FFN shapes (hidden 2048, intermediate 3072):
+    gate||up [6144, 2048] with SwiGLU into [m, 3072], and down [2048, 6144] added
+    into the residual stream, at M = 1 (decode) and M = 512 (prefill), for every
+    format.  `unfused` is the same product through wq_matmul into a buffer
+    followed by torch's element-wise silu * up or add (the extra pass over C
+    that the fused call saves)."""
+    import torch.nn.functional as F
+    out = {}
+    fmts = ((wq.WQ_FMT_F16, "f16"), (wq.WQ_FMT_Q8_0, "q8"), (wq.WQ_FMT_Q4_0, "q4"))
+    for fmt, key in fmts:
+        for name, rows, k, epi in (("swiglu_gate_up", 6144, 2048, wq.WQ_EPI_SWIGLU),
+                                   ("residual_down", 2048, 6144, wq.WQ_EPI_RESIDUAL)):
+            if fmt == wq.WQ_FMT_Q4_0:
+                b0 = torch.from_numpy(wqgen.q4_0_bytes(rows, k, seed)).cuda()
+            else:
+                wd = torch.from_numpy(wqgen.weights(rows, k, seed)).cuda()
+                b0 = wq.pack_f16(wd) if fmt == wq.WQ_FMT_F16 else wq.quantize_q8_0(wd)
+                del wd
+            nbytes = wq.weight_bytes(rows, k, fmt)
+            bs = [b0] + [b0.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / nbytes)) - 1)]
+            n = rows // 2 if epi == wq.WQ_EPI_SWIGLU else rows
+            for m in (1, 512):
+                a = torch.from_numpy(wqgen.activations(m, k, seed)).cuda()
+                c = torch.from_numpy(wqgen.residual(m, n, seed)).cuda()
+                tmp = torch.empty((m, rows), device="cuda")
+
+                def fused(i):
+                    wq.wq_matmul_ex(a, bs[i % len(bs)], c, m, n, k, fmt, epi)
+
+                def unfused(i):
+                    wq.wq_matmul(a, bs[i % len(bs)], tmp, m, rows, k, fmt)
+                    if epi == wq.WQ_EPI_SWIGLU:
+                        torch.mul(F.silu(tmp[:, :n]), tmp[:, n:], out=c)
+                    else:
+                        c.add_(tmp)
+
+                tf = time_launches(torch, fused, iters, warmup)
+                tu = time_launches(torch, unfused, iters, warmup)
+                out[f"{key}_{name}_m{m}_{rows}x{k}"] = {
+                    "fused_us": round(tf * 1e6, 2), "unfused_us": round(tu * 1e6, 2),
+                    "speedup": round(tu / tf, 3), "fused_weight_GB/s": round(nbytes / tf / 1e9, 1),
+                    "route": ROUTE_NAMES[wq.wq_route_for(m, n, k, fmt)]}
+                del a, c, tmp
+            del bs, b0
+            torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(host_weights, seed, budget_s=12.0):
@@ -332,6 +383,10 @@ def main():
                 del bs, b0
                 torch.cuda.empty_cache()
             secondary[f"{key}_sweep"] = out
+
+    if not args.no_secondary and only in (None, "epi"):
+        log("fused epilogues")
+        secondary["epilogues"] = epilogue_bench(torch, wq, wqgen, args.seed, max(10, args.steps // 2), args.warmup)
 
     if (not args.no_secondary and only is None) or only == "f16":
         log("device copy reference")

@@ -1,5 +1,6 @@
-// Decode GEMV (M = 1): c[n] = sum_k a[k] * w[n, k] for f16, Q8_0 and Q4_0 weights
-// (or c[n] += that sum when the launcher's resid flag is set).
+// Decode GEMV (M = 1): c[n] = sum_k a[k] * w[n, k] for f16, Q8_0 and Q4_0 weights,
+// with the epilogues: c[n] += that sum (residual), or c[j] = silu(g_j) * u_j
+// for a fused gate||up weight of 2n rows (SwiGLU; gate row j and up row n + j).
 //
 // The operation is the M = 1 case of dispatch_matmul_half / dispatch_matmul_q8 /
 // dispatch_matmul_q4 (lattice-inference 0.9.0, dispatch.rs) and of the kernels
@@ -31,6 +32,13 @@
 //  * Reductions: DPP within 16-lane rows, lane-xor across rows (64 lanes).
 //  * Persistent waves: the grid is sized to fill the chip once and every wave
 //    walks row groups with a stride, balanced so all waves do equal work.
+//  * SwiGLU: a wave's row group (f16) or pass (Q8_0, Q4_0) holds gate rows
+//    and the up rows of the same outputs, so after the reduction the gate and
+//    up sums sit in two lanes of the same wave; one lane shuffle brings them
+//    together and silu(g) * u is stored directly (no [2n] intermediate, no
+//    second kernel).  Shapes those kernels cannot pair (K > 8192, unaligned
+//    or odd K) take one GEMV over all 2n rows into scratch and one
+//    element-wise pass.
 #include "wq_internal.h"
 
 #include <algorithm>
@@ -54,12 +62,16 @@ __device__ __forceinline__ float dot8_f16(uint4 w, float4 lo, float4 hi, float a
 
 // T 16-byte chunk slots per lane cover K = 512*T weights; R rows per step.
 // FULL: K == 512*T exactly, so no slot needs a bounds check.
+// GLU: n is the output count and b has 2n rows; a group is R/2 gate rows and
+// the R/2 up rows of the same outputs.  Otherwise a group is R rows of b.
 // Requires K % 8 == 0 and 16-byte aligned a and b.
-template <int T, int R, bool FULL>
+template <int T, int R, bool FULL, bool GLU>
 __global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
                                                     const uint16_t *__restrict__ b,
                                                     float *__restrict__ c, int64_t n, int64_t k,
                                                     int64_t groups, int resid) {
+    static_assert(!GLU || R % 2 == 0, "a GLU group pairs gate and up rows");
+    constexpr int OC = GLU ? R / 2 : R;  // outputs per group
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
     const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) / kWave;
@@ -80,16 +92,17 @@ __global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
     }
 
     for (int64_t g = wave; g < groups; g += nwaves) {
-        const int64_t r0 = g * R;
+        const int64_t r0 = g * OC;  // first output of the group
         uint4 w[R][T];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int64_t row = r0 + r;
+            const int64_t oc = r0 + r % OC;
+            const int64_t row = GLU && r >= OC ? n + oc : oc;
             const uint4 *brow = reinterpret_cast<const uint4 *>(b + row * k);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const int idx = t * kWave + lane;
-                if ((FULL || idx < nch) && row < n)
+                if ((FULL || idx < nch) && oc < n)
                     w[r][t] = load_nt16(brow + idx);
                 else
                     w[r][t] = make_uint4(0u, 0u, 0u, 0u);
@@ -108,7 +121,12 @@ __global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
             const float s = wave_sum(acc[r]);
             if (lane == r) mine = s;
         }
-        if (lane < R && r0 + lane < n) c[r0 + lane] = resid ? c[r0 + lane] + mine : mine;
+        if constexpr (GLU) {
+            const float up = __shfl_down(mine, OC, kWave);  // lane r + OC holds the up sum
+            if (lane < OC && r0 + lane < n) c[r0 + lane] = silu(mine) * up;
+        } else {
+            if (lane < R && r0 + lane < n) c[r0 + lane] = resid ? c[r0 + lane] + mine : mine;
+        }
     }
 }
 
@@ -243,7 +261,10 @@ __device__ __forceinline__ float block_dot(const uint8_t *stage, int pb, const f
 // current pass, already copied to LDS, is decoded; the SL rows a lane group
 // decodes are unrolled so their LDS reads and reductions interleave.
 // Requires K % 256 == 0 (rows are whole 16-byte chunks), 16-byte aligned a, b.
-template <int FMT, int J, int LPR, int SL>
+// GLU: n is the output count and b has 2n rows; a pass stages HS = S/2 gate
+// rows (stage rows 0 .. HS-1) and the up rows of the same outputs (stage rows
+// HS .. S-1), two contiguous byte ranges.
+template <int FMT, int J, int LPR, int SL, bool GLU>
 __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
                                                     const uint8_t *__restrict__ b,
                                                     float *__restrict__ c, int64_t n, int64_t k,
@@ -253,6 +274,8 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
     constexpr int CH = QB<FMT>::kChunks;
     constexpr int RPL = kWave / LPR;
     constexpr int S = SL * RPL;
+    static_assert(!GLU || S % 2 == 0, "a GLU pass pairs gate and up rows");
+    constexpr int HS = GLU ? S / 2 : S;  // outputs per pass
     const int lane = threadIdx.x;
     const int nb = static_cast<int>(k >> 5);
     const int row_bytes = nb * BB;
@@ -280,21 +303,35 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
     // the end re-read the pass's last chunk (in bounds) and write it to LDS
     // slots nobody reads.  No per-lane exec masking in the streaming loop.
     uint4 next[CH];
+    const int hc = HS * row_bytes / 16;  // stage chunks of one GLU half
     auto fetch = [&](int64_t p) {
-        const int nch = static_cast<int>(min<int64_t>(S, n - p * S)) * row_bytes / 16;
-        const uint4 *src = reinterpret_cast<const uint4 *>(b + p * S * row_bytes);
+        const int nch = static_cast<int>(min<int64_t>(HS, n - p * HS)) * row_bytes / 16;
+        const uint4 *src = reinterpret_cast<const uint4 *>(b + p * HS * row_bytes);
+        if constexpr (GLU) {
+            // Stage chunk ci < hc: gate chunk ci; else up chunk ci - hc.  Chunks
+            // past a half's end (last pass) re-read its last chunk, in bounds.
+            const uint4 *usrc = reinterpret_cast<const uint4 *>(b + (n + p * HS) * row_bytes);
 #pragma unroll
-        for (int u = 0; u < CH; ++u)
-            if (u * kWave < nch) next[u] = load_nt16(src + min(u * kWave + lane, nch - 1));
+            for (int u = 0; u < CH; ++u)
+                if (u * kWave < 2 * hc) {
+                    const int ci = u * kWave + lane;
+                    const bool up = ci >= hc;
+                    next[u] = load_nt16((up ? usrc : src) + min(up ? ci - hc : ci, nch - 1));
+                }
+        } else {
+#pragma unroll
+            for (int u = 0; u < CH; ++u)
+                if (u * kWave < nch) next[u] = load_nt16(src + min(u * kWave + lane, nch - 1));
+        }
     };
 
     const uint8_t *stage = reinterpret_cast<const uint8_t *>(stage4);
     int64_t p = blockIdx.x;
     if (p < passes) fetch(p);
     for (; p < passes; p += gridDim.x) {
-        const int64_t row0 = p * S;
-        const int rows = static_cast<int>(min<int64_t>(S, n - row0));
-        const int nch = rows * row_bytes / 16;
+        const int64_t row0 = p * HS;  // first output of the pass
+        const int rows = static_cast<int>(min<int64_t>(HS, n - row0));
+        const int nch = GLU ? 2 * hc : rows * row_bytes / 16;
         __syncthreads();  // the previous pass is fully read from LDS
 #pragma unroll
         for (int u = 0; u < CH; ++u)
@@ -316,7 +353,7 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
                 const float d = block_dot<FMT>(stage, srow * row_bytes + BB * min(j, nb - 1), av[t]);
                 acc[sl] += (j < nb) ? d : 0.f;
             }
-            if (srow >= rows) acc[sl] = 0.f;
+            if ((GLU ? srow % HS : srow) >= rows) acc[sl] = 0.f;
         }
         // One butterfly reduction for all SL rows of the lane group; lane
         // jl then holds the sum of row sl = jl / (LPR / SL), stored by the
@@ -324,9 +361,18 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
         const float sum = rows_sum<SL, LPR>(acc, jl);
         const int sl_mine = jl / (LPR / SL);
         const int srow_mine = sl_mine * RPL + rsub;
-        if (jl % (LPR / SL) == 0 && srow_mine < rows) {
-            float *dst = c + row0 + srow_mine;
-            *dst = resid ? *dst + sum : sum;
+        if constexpr (GLU) {
+            // Up row srow + HS is held D lanes up: by sl + SL/2 of the same
+            // lane group (SL >= 2), or by lane group rsub + RPL/2 (SL == 1).
+            constexpr int D = SL >= 2 ? LPR / 2 : kWave / 2;
+            const float up = __shfl_down(sum, D, kWave);
+            if (jl % (LPR / SL) == 0 && srow_mine < HS && srow_mine < rows)
+                c[row0 + srow_mine] = silu(sum) * up;
+        } else {
+            if (jl % (LPR / SL) == 0 && srow_mine < rows) {
+                float *dst = c + row0 + srow_mine;
+                *dst = resid ? *dst + sum : sum;
+            }
         }
     }
 }
@@ -386,37 +432,56 @@ inline int64_t balanced_workers(int64_t items, int64_t cap) {
     return (items + rounds - 1) / rounds;
 }
 
-template <int T, int R>
+// SwiGLU as one GEMV over all 2n rows into scratch and one element-wise pass.
+template <typename Gemv2n>
+hipError_t glu_two_pass(float *c, int64_t n, hipStream_t s, Gemv2n &&gemv2n) {
+    ScratchLease lease;
+    void *scratch = nullptr;
+    hipError_t e = lease.acquire(static_cast<size_t>(2 * n) * 4, s, &scratch);
+    if (e != hipSuccess) return e;
+    float *gu = static_cast<float *>(scratch);
+    e = gemv2n(gu);
+    if (e == hipSuccess) e = launch_reduce_splits(gu, c, 1, n, 2 * n, 1, kEpiGlu, s);
+    const hipError_t er = lease.release();
+    return e != hipSuccess ? e : er;
+}
+
+template <int T, int R, bool GLU = false>
 hipError_t run_f16_vec(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
                        hipStream_t s, int cus, int resid) {
-    const int64_t groups = (n + R - 1) / R;
+    const int64_t groups = (n + (GLU ? R / 2 : R) - 1) / (GLU ? R / 2 : R);
     const int64_t waves = balanced_workers(groups, static_cast<int64_t>(cus) * 16);
     const int64_t blocks = (waves + 3) / 4;
     const bool full = (k == 512LL * T);
     if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_f16_vec<T=%d,R=%d,full=%d> n=%lld k=%lld grid=%lld block=256\n", T, R,
-                full ? 1 : 0, (long long)n, (long long)k, (long long)blocks);
+        fprintf(stderr, "[wqmm] gemv_f16_vec<T=%d,R=%d,full=%d,glu=%d> n=%lld k=%lld grid=%lld block=256\n", T,
+                R, full ? 1 : 0, GLU ? 1 : 0, (long long)n, (long long)k, (long long)blocks);
     if (full)
-        hipLaunchKernelGGL((gemv_f16_vec<T, R, true>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups, resid);
+        hipLaunchKernelGGL((gemv_f16_vec<T, R, true, GLU>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups,
+                           resid);
     else
-        hipLaunchKernelGGL((gemv_f16_vec<T, R, false>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups, resid);
+        hipLaunchKernelGGL((gemv_f16_vec<T, R, false, GLU>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups,
+                           resid);
     return hipGetLastError();
 }
 
-template <int FMT, int J, int LPR, int SL>
+template <int FMT, int J, int LPR, int SL, bool GLU = false>
 hipError_t run_q_staged_sl(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
                            int cus, int resid) {
     constexpr int S = SL * (kWave / LPR);
+    constexpr int HS = GLU ? S / 2 : S;
     const int row_bytes = static_cast<int>((k >> 5) * QB<FMT>::kBytes);
-    const int64_t passes = (n + S - 1) / S;
+    const int64_t passes = (n + HS - 1) / HS;
     // 12 single-wave workgroups per CU: measured best on MI355X (N = 151936).
     const int64_t blocks = balanced_workers(passes, static_cast<int64_t>(cus) * 12);
     const size_t lds = (static_cast<size_t>(S) * row_bytes + 1023) / 1024 * 1024;  // whole 1 KiB writes
     if (trace_enabled())
         fprintf(stderr,
-                "[wqmm] gemv_q_staged<fmt=%d,J=%d,LPR=%d,SL=%d> n=%lld k=%lld S=%d grid=%lld block=64 lds=%zu\n",
-                FMT, J, LPR, SL, (long long)n, (long long)k, S, (long long)blocks, lds);
-    hipLaunchKernelGGL((gemv_q_staged<FMT, J, LPR, SL>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k, passes, resid);
+                "[wqmm] gemv_q_staged<fmt=%d,J=%d,LPR=%d,SL=%d,glu=%d> n=%lld k=%lld S=%d grid=%lld block=64 "
+                "lds=%zu\n",
+                FMT, J, LPR, SL, GLU ? 1 : 0, (long long)n, (long long)k, S, (long long)blocks, lds);
+    hipLaunchKernelGGL((gemv_q_staged<FMT, J, LPR, SL, GLU>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k, passes,
+                       resid);
     return hipGetLastError();
 }
 
@@ -440,17 +505,70 @@ hipError_t run_q_staged(const float *a, const uint8_t *b, float *c, int64_t n, i
     return run_q_staged_sl<FMT, J, LPR, 1>(a, b, c, n, k, s, cus, resid);
 }
 
+// The fused SwiGLU variant (n outputs, 2n rows): as run_q_staged over the 2n
+// rows, but a pass needs at least two rows (one gate, one up), so with 64
+// lanes per row SL >= 2.  Returns false (nothing launched) when no variant
+// fits the stage.
+template <int FMT, int J, int LPR>
+bool run_q_staged_glu(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int cus,
+                      hipError_t *e) {
+    constexpr int RPL = kWave / LPR;
+    const int row_bytes = static_cast<int>((k >> 5) * QB<FMT>::kBytes);
+    const int64_t s_fit = QB<FMT>::kStage / row_bytes;
+    const int64_t s_fill = std::max<int64_t>(1, 2 * n / (4LL * cus));
+    const int64_t sl_max = std::max<int64_t>(1, std::min<int64_t>(4, std::min(s_fit, s_fill) / RPL));
+    if constexpr (J <= 2)
+        if (sl_max >= 4 && 4 * RPL <= s_fit) {
+            *e = run_q_staged_sl<FMT, J, LPR, 4, true>(a, b, c, n, k, s, cus, 0);
+            return true;
+        }
+    if constexpr (J <= 4)
+        if ((sl_max >= 2 || RPL == 1) && 2 * RPL <= s_fit) {
+            *e = run_q_staged_sl<FMT, J, LPR, 2, true>(a, b, c, n, k, s, cus, 0);
+            return true;
+        }
+    if constexpr (RPL >= 2) {
+        *e = run_q_staged_sl<FMT, J, LPR, 1, true>(a, b, c, n, k, s, cus, 0);
+        return true;
+    }
+    return false;
+}
+
 // Staged kernel when K % 256 == 0, a and b are 16-byte aligned and a row fits
 // the stage with at most 8 blocks per lane; otherwise the plain kernel.
 template <int FMT>
 hipError_t launch_gemv_q(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
-                         int resid) {
+                         int epi) {
     DeviceInfo di;
     hipError_t e = device_info(&di);
     if (e != hipSuccess) return e;
+    const int resid = epi == kEpiResidual;
     const int64_t nb = k / 32;
     const int64_t row_bytes = nb * QB<FMT>::kBytes;
-    if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= QB<FMT>::kStage && nb <= 512) {
+    const bool staged = nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= QB<FMT>::kStage && nb <= 512;
+    if (epi == kEpiGlu) {
+        if (staged) {
+            bool done = false;
+            if (nb >= 64) {
+                switch ((nb + 63) / 64) {
+                    case 1: done = run_q_staged_glu<FMT, 1, 64>(a, b, c, n, k, s, di.cus, &e); break;
+                    case 2: done = run_q_staged_glu<FMT, 2, 64>(a, b, c, n, k, s, di.cus, &e); break;
+                    case 3: done = run_q_staged_glu<FMT, 3, 64>(a, b, c, n, k, s, di.cus, &e); break;
+                    case 4: done = run_q_staged_glu<FMT, 4, 64>(a, b, c, n, k, s, di.cus, &e); break;
+                    default: break;
+                }
+            } else if (nb >= 32) {
+                done = nb == 32 ? run_q_staged_glu<FMT, 1, 32>(a, b, c, n, k, s, di.cus, &e)
+                                : run_q_staged_glu<FMT, 2, 32>(a, b, c, n, k, s, di.cus, &e);
+            } else {
+                done = nb <= 16 ? run_q_staged_glu<FMT, 1, 16>(a, b, c, n, k, s, di.cus, &e)
+                                : run_q_staged_glu<FMT, 2, 16>(a, b, c, n, k, s, di.cus, &e);
+            }
+            if (done) return e;
+        }
+        return glu_two_pass(c, n, s, [&](float *gu) { return launch_gemv_q<FMT>(a, b, gu, 2 * n, k, s, kEpiNone); });
+    }
+    if (staged) {
         if (nb >= 64) {
             switch ((nb + 63) / 64) {
                 case 1: return run_q_staged<FMT, 1, 64>(a, b, c, n, k, s, di.cus, resid);
@@ -482,13 +600,26 @@ hipError_t launch_gemv_q(const float *a, const uint8_t *b, float *c, int64_t n, 
 }  // namespace
 
 hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
-                           hipStream_t s, bool resid) {
+                           hipStream_t s, int epi) {
     DeviceInfo di;
     hipError_t e = device_info(&di);
     if (e != hipSuccess) return e;
+    const int resid = epi == kEpiResidual;
     const int64_t nch = k / 8;
     const int64_t T = (nch + 63) / 64;
-    if (k % 8 == 0 && aligned16(a) && aligned16(b) && T >= 1 && T <= 32) {
+    const bool vec = k % 8 == 0 && aligned16(a) && aligned16(b) && T >= 1 && T <= 32;
+    if (epi == kEpiGlu) {
+        // R rows per group as below, at least one gate and one up row.
+        if (vec && T <= 16) {
+            if (T <= 1) return run_f16_vec<1, 8, true>(a, b, c, n, k, s, di.cus, 0);
+            if (T <= 2) return run_f16_vec<2, 8, true>(a, b, c, n, k, s, di.cus, 0);
+            if (T <= 4) return run_f16_vec<4, 4, true>(a, b, c, n, k, s, di.cus, 0);
+            if (T <= 8) return run_f16_vec<8, 2, true>(a, b, c, n, k, s, di.cus, 0);
+            return run_f16_vec<16, 2, true>(a, b, c, n, k, s, di.cus, 0);
+        }
+        return glu_two_pass(c, n, s, [&](float *gu) { return launch_gemv_f16(a, b, gu, 2 * n, k, s, kEpiNone); });
+    }
+    if (vec) {
         if (T <= 1) return run_f16_vec<1, 8>(a, b, c, n, k, s, di.cus, resid);
         if (T <= 2) return run_f16_vec<2, 8>(a, b, c, n, k, s, di.cus, resid);
         if (T <= 4) return run_f16_vec<4, 4>(a, b, c, n, k, s, di.cus, resid);
@@ -508,13 +639,13 @@ hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t 
 }
 
 hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
-                            hipStream_t s, bool resid) {
-    return launch_gemv_q<QFMT_Q8_0>(a, b, c, n, k, s, resid);
+                            hipStream_t s, int epi) {
+    return launch_gemv_q<QFMT_Q8_0>(a, b, c, n, k, s, epi);
 }
 
 hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
-                            hipStream_t s, bool resid) {
-    return launch_gemv_q<QFMT_Q4_0>(a, b, c, n, k, s, resid);
+                            hipStream_t s, int epi) {
+    return launch_gemv_q<QFMT_Q4_0>(a, b, c, n, k, s, epi);
 }
 
 }  // namespace wq

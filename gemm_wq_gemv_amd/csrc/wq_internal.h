@@ -104,13 +104,14 @@ hipError_t device_info(DeviceInfo *out);
 
 // Launchers.  Arguments are already validated by the C-ABI layer; these only
 // pick a kernel variant and grid and enqueue it on `s`.
-// resid: c[n] += the dot product instead of c[n] = it.
+// GEMV epilogue epi: kEpiNone, kEpiResidual (c[n] += the dot product) or
+// kEpiGlu (n outputs from 2n weight rows: c[j] = silu(row j) * row n + j).
 hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
-                           hipStream_t s, bool resid = false);
+                           hipStream_t s, int epi = kEpiNone);
 hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
-                            hipStream_t s, bool resid = false);
+                            hipStream_t s, int epi = kEpiNone);
 hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
-                            hipStream_t s, bool resid = false);
+                            hipStream_t s, int epi = kEpiNone);
 // n = output columns; with kEpiGlu the weights have 2n rows.
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,
                        int64_t k, hipStream_t s, int epi = kEpiNone);

@@ -194,40 +194,22 @@ int kernel_epi(int epi) {
     return epi == WQ_EPI_RESIDUAL ? wq::kEpiResidual : epi == WQ_EPI_SWIGLU ? wq::kEpiGlu : wq::kEpiNone;
 }
 
-// One GEMV launch per row of A over n weight rows into c [m, n] (ldc = n),
-// adding into c when resid is set.
-int gemv_rows(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
-              bool resid) {
+// The GEMV route (M == 1; forced otherwise): one GEMV launch per row of A,
+// each applying the epilogue itself.
+int run_gemv(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
+             int epi) {
+    const int ke = kernel_epi(epi);
+    const auto *b8 = static_cast<const uint8_t *>(b);
     for (int64_t i = 0; i < m; ++i) {
         const float *ai = a + i * k;
         float *ci = c + i * n;
-        const auto *b8 = static_cast<const uint8_t *>(b);
-        hipError_t e = (fmt == WQ_FMT_F16)
-                           ? wq::launch_gemv_f16(ai, static_cast<const uint16_t *>(b), ci, n, k, s, resid)
-                       : (fmt == WQ_FMT_Q8_0) ? wq::launch_gemv_q8_0(ai, b8, ci, n, k, s, resid)
-                                              : wq::launch_gemv_q4_0(ai, b8, ci, n, k, s, resid);
+        hipError_t e = (fmt == WQ_FMT_F16)    ? wq::launch_gemv_f16(ai, static_cast<const uint16_t *>(b), ci, n, k, s, ke)
+                       : (fmt == WQ_FMT_Q8_0) ? wq::launch_gemv_q8_0(ai, b8, ci, n, k, s, ke)
+                                              : wq::launch_gemv_q4_0(ai, b8, ci, n, k, s, ke);
         if (e != hipSuccess) return WQ_ERR_LAUNCH;
         wq::g_route_count[WQ_ROUTE_GEMV].fetch_add(1, std::memory_order_relaxed);
     }
     return WQ_OK;
-}
-
-// The GEMV route (M == 1; forced otherwise).  SWIGLU: gate and up rows are
-// contiguous, so one GEMV per row of A covers all 2n rows into a [m, 2n]
-// scratch, and one element-wise pass writes silu(gate) * up into c.
-int run_gemv(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
-             int epi) {
-    if (epi != WQ_EPI_SWIGLU) return gemv_rows(a, b, c, m, n, k, fmt, s, epi == WQ_EPI_RESIDUAL);
-    wq::ScratchLease lease;
-    void *scratch = nullptr;
-    if (lease.acquire(static_cast<size_t>(m) * static_cast<size_t>(2 * n) * 4, s, &scratch) != hipSuccess)
-        return WQ_ERR_LAUNCH;
-    float *gu = static_cast<float *>(scratch);
-    int st = gemv_rows(a, b, gu, m, 2 * n, k, fmt, s, false);
-    if (st == WQ_OK && wq::launch_reduce_splits(gu, c, m, n, 2 * n, 1, wq::kEpiGlu, s) != hipSuccess)
-        st = WQ_ERR_LAUNCH;
-    if (lease.release() != hipSuccess && st == WQ_OK) st = WQ_ERR_LAUNCH;
-    return st;
 }
 
 int run_gemm(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,

@@ -156,6 +156,23 @@ def test_decode_ffn_shapes(fmt):
     case(fmt, RES, 1, 2048, 6144, seed=43)
 
 
+GEMV_K = {F16: [64, 1000, 2048, 4096, 8192, 16384, 1001, 12],
+          Q8: [256, 768, 1024, 1536, 2048, 4096, 6144, 8192, 10240, 992],
+          Q4: [256, 768, 1024, 1536, 2048, 4096, 6144, 8192, 10240, 992]}
+
+
+@pytest.mark.parametrize("epi", [RES, GLU], ids=["residual", "swiglu"])
+@pytest.mark.parametrize("fmt", ALL)
+def test_decode_every_gemv_variant(fmt, epi):
+    """M = 1 over every GEMV kernel family: f16 rows of 1..32 chunk slots per
+    lane (full and partial), 16/32/64 lanes per quantized row with 1..4 blocks
+    per lane (SwiGLU fused in the GEMV), and the shapes that take one GEMV over
+    all 2n rows plus an element-wise pass (K > 8192, K % 256 != 0, K % 8 != 0)."""
+    for k in GEMV_K[fmt]:
+        for n in (37, 1000):
+            case(fmt, epi, 1, n, k, seed=k + n, route="gemv")
+
+
 @pytest.mark.parametrize("epi", [RES, GLU], ids=["residual", "swiglu"])
 @pytest.mark.parametrize("fmt", ALL)
 def test_prefill_sampled(fmt, epi):

@@ -18,6 +18,8 @@ Parity status of each function (what pins it, see ``tests/test_oracle.py``):
                  permutation, numpy float64 matmul on the decoded weights
   silu           closed forms: silu(0) = 0, silu(ln 3) = (3/4) ln 3,
                  silu(x) - silu(-x) = x, limits at +-inf, sign
+  topk           numpy lexsort on random and tie-heavy logits, hand cases with
+                 ties, NaN, +-inf, k > n (sentinel padding)
   matmul_epilogue  residual: exact hand sums on the worked example, linearity;
                  SwiGLU: hand-derived values (gate ln 3 / 0 / +-40), which half
                  is gate, the identity out(g) - out(-g) = g * u
@@ -97,6 +99,8 @@ class Oracle:
         lib.wqref_silu_array.argtypes = [P, P, I64]
         lib.wqref_epilogue.restype = I
         lib.wqref_epilogue.argtypes = [I, P, P, I64, I64, P, P, P]
+        lib.wqref_topk.restype = I
+        lib.wqref_topk.argtypes = [P, I64, I64, P, P]
         self.lib = lib
         self.path = path
 
@@ -237,6 +241,25 @@ class Oracle:
         out, bound = self.epilogue(EPI_SWIGLU, s, bs, rows.size, 1)
         return out.reshape(-1), bound.reshape(-1)
 
+    # -- top-k (TopKCandidate / topk_better, lattice-inference 0.1.2 page) ----
+    def topk(self, logits, topk: int):
+        """(vals float64 [topk], ids int64 [topk]): the topk best logits, higher first,
+        equal logits by lower id, NaN left out, padded with (-inf, 4294967295)."""
+        x = np.ascontiguousarray(logits, dtype=np.float64).reshape(-1)
+        vals = np.empty(topk, dtype=np.float64)
+        ids = np.empty(topk, dtype=np.int64)
+        if self.lib.wqref_topk(x.ctypes.data, x.size, topk, vals.ctypes.data, ids.ctypes.data) != 0:
+            raise ValueError("topk: bad arguments")
+        return vals, ids
+
+    def lm_head_topk(self, a, b, fmt: int, n: int, k: int, topk: int, threads: int | None = None):
+        """The LM-head product for one token, logits[j] = sum_k a[k] w[j, k], then
+        its top-k: (vals, ids, logits, bound) with the full float64 logits and their
+        per-row tolerance 1e-5 * sum_k |a_k w_jk| + 1e-6."""
+        logits, bound = self.matmul(np.asarray(a, np.float32).reshape(1, -1), b, fmt, 1, n, k, threads)
+        vals, ids = self.topk(logits[0], topk)
+        return vals, ids, logits[0], bound[0]
+
 
 _default: Oracle | None = None
 
@@ -287,3 +310,11 @@ def matmul_epilogue(a, b, fmt, m, n, k, epi, resid=None, threads=None):
 
 def epilogue_entries(a, b, fmt, m, n, k, epi, rows, cols, resid=None, threads=None):
     return get().epilogue_entries(a, b, fmt, m, n, k, epi, rows, cols, resid, threads)
+
+
+def topk(logits, k):
+    return get().topk(logits, k)
+
+
+def lm_head_topk(a, b, fmt, n, k, topk_, threads=None):
+    return get().lm_head_topk(a, b, fmt, n, k, topk_, threads)

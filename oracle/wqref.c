@@ -361,3 +361,46 @@ int wqref_epilogue(int epi, const double *acc, const double *acc_bound, int64_t 
     }
     return -1;
 }
+
+/* ---------------------------------------------------------------- top-k -- */
+
+/* Ranking of (logit, token id) candidates, from the TopKCandidate /
+ * topk_better definitions on the lattice-inference 0.1.2 page: a higher logit
+ * ranks first, equal logits rank by the lower id, and a NaN logit never ranks
+ * before anything (the first passes there replace a NaN logit by the sentinel
+ * (-inf, UINT_MAX), so it is never selected).  Returns <0 when a ranks first. */
+typedef struct {
+    double v;
+    int64_t id;
+} wqref_cand;
+
+static int cand_cmp(const void *pa, const void *pb) {
+    const wqref_cand *a = (const wqref_cand *)pa, *b = (const wqref_cand *)pb;
+    if (a->v > b->v) return -1;
+    if (a->v < b->v) return 1;
+    return (a->id < b->id) ? -1 : (a->id > b->id) ? 1 : 0;
+}
+
+/* The topk best of logits[0..n-1] in rank order: vals[r], ids[r].  NaN logits
+ * are left out; when fewer than topk remain, the rest is the sentinel
+ * (-inf, 4294967295).  A plain sort of every candidate.  Returns 0, or -1 on
+ * bad arguments or memory. */
+int wqref_topk(const double *logits, int64_t n, int64_t topk, double *vals, int64_t *ids) {
+    if (n < 0 || topk < 0 || (n > 0 && !logits) || (topk > 0 && (!vals || !ids))) return -1;
+    wqref_cand *c = (wqref_cand *)malloc(sizeof(wqref_cand) * (size_t)(n > 0 ? n : 1));
+    if (!c) return -1;
+    int64_t cnt = 0;
+    for (int64_t i = 0; i < n; ++i)
+        if (!isnan(logits[i])) {
+            c[cnt].v = logits[i];
+            c[cnt].id = i;
+            ++cnt;
+        }
+    qsort(c, (size_t)cnt, sizeof(wqref_cand), cand_cmp);
+    for (int64_t r = 0; r < topk; ++r) {
+        vals[r] = r < cnt ? c[r].v : -INFINITY;
+        ids[r] = r < cnt ? c[r].id : (int64_t)4294967295LL;
+    }
+    free(c);
+    return 0;
+}

@@ -494,6 +494,67 @@ def pin_swiglu_identity(orc):
     assert np.all(np.minimum(0, gu) - 1e-12 <= out) and np.all(out <= np.maximum(0, gu) + 1e-12)
 
 
+# ----------------------------------------------------------------- top-k --
+UMAX = 4294967295
+
+
+def pin_topk_hand(orc):
+    """The ranking of the pages' TopKCandidate / topk_better (lattice-inference 0.1.2):
+    higher logit first, equal logits by lower id, NaN never selected, sentinel
+    (-inf, UINT_MAX) padding; -inf logits rank above the sentinel by their id.
+    Every expected list below is worked out by hand."""
+    x = [1.0, 3.0, float("nan"), 3.0, float("-inf"), 2.0]
+    v, i = orc.topk(x, 7)
+    assert list(i) == [1, 3, 5, 0, 4, UMAX, UMAX]
+    assert list(v[:4]) == [3.0, 3.0, 2.0, 1.0] and np.all(np.isneginf(v[4:]))
+    v, i = orc.topk(x, 1)
+    assert list(i) == [1] and v[0] == 3.0
+    v, i = orc.topk([float("nan")] * 3, 2)
+    assert list(i) == [UMAX, UMAX] and np.all(np.isneginf(v))
+    v, i = orc.topk([-1.0, float("inf"), 5.0, float("inf")], 3)
+    assert list(i) == [1, 3, 2] and v[2] == 5.0
+    v, i = orc.topk([0.0, -0.0, 0.0], 3)  # -0.0 == 0.0: ties by id
+    assert list(i) == [0, 1, 2]
+    v, i = orc.topk([], 2)
+    assert list(i) == [UMAX, UMAX]
+
+
+def pin_topk_vs_lexsort(orc):
+    """Against numpy's lexsort (descending logit, then ascending id) with NaNs
+    dropped, on tie-heavy integer logits and on N(0,1) logits, for k below, at and
+    above the number of candidates."""
+    rng = np.random.default_rng(12)
+    for n in (1, 7, 63, 64, 65, 1000, 5000):
+        for kind in ("ties", "normal"):
+            x = rng.integers(-3, 4, n).astype(np.float64) if kind == "ties" else rng.standard_normal(n)
+            if n > 10:
+                x[rng.integers(0, n, n // 10)] = np.nan
+            keep = np.flatnonzero(~np.isnan(x))
+            order = keep[np.lexsort((keep, -x[keep]))]
+            for k in (1, 5, 50, 64, n + 3):
+                v, i = orc.topk(x, k)
+                m = min(k, order.size)
+                assert np.array_equal(i[:m], order[:m]), (n, kind, k)
+                assert np.array_equal(v[:m], x[order[:m]])
+                assert np.all(i[m:] == UMAX) and np.all(np.isneginf(v[m:]))
+
+
+def pin_lm_head_topk(orc):
+    """One-hot LM head: row j of the f16 weights holds w_j at column 0 and a = e_0, so
+    logit j = w_j exactly; the top-k of chosen w_j (with ties and a NaN row) is known by
+    hand.  Also the logits and bounds it returns are those of the product."""
+    K = 32
+    w = np.array([0.5, -2.0, 3.0, 3.0, float("nan"), 1.0, 3.0, -0.25], np.float32)
+    b = np.zeros((w.size, K), np.uint16)
+    b[:, 0] = w.astype(np.float16).view(np.uint16)
+    a = np.zeros(K, np.float32)
+    a[0] = 1.0
+    v, i, logits, bound = orc.lm_head_topk(a, b, FMT_F16, w.size, K, 5)
+    assert list(i) == [2, 3, 6, 5, 0] and list(v) == [3.0, 3.0, 3.0, 1.0, 0.5]
+    c, bd = orc.matmul(a.reshape(1, K), b, FMT_F16, 1, w.size, K)
+    assert np.array_equal(logits, c[0], equal_nan=True) and np.array_equal(bound, bd[0], equal_nan=True)
+
+
 PINS = [
     pin_f16_decode_exhaustive,
     pin_f16_encode_golden,
@@ -511,6 +572,9 @@ PINS = [
     pin_residual_golden,
     pin_swiglu_golden,
     pin_swiglu_identity,
+    pin_topk_hand,
+    pin_topk_vs_lexsort,
+    pin_lm_head_topk,
 ]
 
 
@@ -569,6 +633,15 @@ MUTANTS = {
     "residual_dropped": ("out[i] = r + s;", "out[i] = s;"),
     "residual_subtracted": ("out[i] = r + s;", "out[i] = s - r;"),
     "residual_bound_no_rounding": ("acc_bound[i] + ldexp(fabs(r) + fabs(s), -23)", "acc_bound[i]"),
+    "topk_ties_higher_id": ("return (a->id < b->id) ? -1 : (a->id > b->id) ? 1 : 0;",
+                            "return (a->id > b->id) ? -1 : (a->id < b->id) ? 1 : 0;"),
+    "topk_ascending": ("if (a->v > b->v) return -1;\n    if (a->v < b->v) return 1;",
+                       "if (a->v < b->v) return -1;\n    if (a->v > b->v) return 1;"),
+    "topk_keeps_nan": ("if (!isnan(logits[i])) {", "if (1) {"),
+    "topk_sentinel_zero": ("vals[r] = r < cnt ? c[r].v : -INFINITY;", "vals[r] = r < cnt ? c[r].v : 0.0;"),
+    "topk_sentinel_id": ("(int64_t)4294967295LL", "(int64_t)-1"),
+    "topk_drops_last": ("for (int64_t r = 0; r < topk; ++r) {\n        vals[r]",
+                        "for (int64_t r = 0; r < topk; ++r) {\n        if (r == topk - 1 && r > 0) { vals[r] = -INFINITY; ids[r] = 4294967295LL; continue; }\n        vals[r]"),
 }
 
 

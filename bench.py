@@ -17,8 +17,9 @@ region.  ``cpu_baseline`` times the CPU oracle (all host cores it uses) on the
 same suite.  ``secondary`` reports the other configurations: the Q8_0 and
 Q4_0 decode suites, the f16 prefill GEMM at M = 512, the Q8_0 and Q4_0 M
 sweeps, the fused residual and SwiGLU epilogues against the same product
-followed by separate element-wise kernels, and a plain device copy as the
-achievable-bandwidth reference.  Q4_0
+followed by separate element-wise kernels, the fused LM-head GEMV + top-k
+against the GEMV alone and the GEMV followed by a top-k pass, and a plain
+device copy as the achievable-bandwidth reference.  Q4_0
 weights are synthetic bytes (random codes and scales) since no Q4_0 encoder is
 given.
 """
@@ -88,7 +89,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-secondary", action="store_true", help="headline suite only")
-    p.add_argument("--only", choices=["f16", "q8", "q4", "prefill", "sweep", "epi"], default=None,
+    p.add_argument("--only", choices=["f16", "q8", "q4", "prefill", "sweep", "epi", "topk"], default=None,
                    help="run one workload only (for profiling); prints no headline line")
     return p.parse_args()
 
@@ -219,6 +220,44 @@ def epilogue_bench(torch, wq, wqgen, seed, iters, warmup):
                 del a, c, tmp
             del bs, b0
             torch.cuda.empty_cache()
+    return out
+
+
+def topk_bench(torch, wq, wqgen, seed, iters, warmup):
+    """LM-head top-k at vocab 151936, hidden 2048, for every format and k in
+    {1, 50}: the fused GEMV + top-k (wq_lm_head_topk) against the GEMV alone
+    (wq_matmul writing the logits) and against the GEMV followed by wq_topk."""
+    n, k = 151936, 2048
+    out = {}
+    for fmt, key in ((wq.WQ_FMT_F16, "f16"), (wq.WQ_FMT_Q8_0, "q8"), (wq.WQ_FMT_Q4_0, "q4")):
+        if fmt == wq.WQ_FMT_Q4_0:
+            b0 = torch.from_numpy(wqgen.q4_0_bytes(n, k, seed)).cuda()
+        else:
+            wd = torch.from_numpy(wqgen.weights(n, k, seed)).cuda()
+            b0 = wq.pack_f16(wd) if fmt == wq.WQ_FMT_F16 else wq.quantize_q8_0(wd)
+            del wd
+        nbytes = wq.weight_bytes(n, k, fmt)
+        bs = [b0] + [b0.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / nbytes)) - 1)]
+        a = torch.from_numpy(wqgen.activations(1, k, seed)).cuda()
+        logits = torch.empty((1, n), device="cuda")
+        t_gemv = time_launches(torch, lambda i: wq.wq_matmul(a, bs[i % len(bs)], logits, 1, n, k, fmt), iters,
+                               warmup)
+        for topk in (1, 50):
+            vals = torch.empty(topk, device="cuda")
+            ids = torch.empty(topk, dtype=torch.int32, device="cuda")
+            t_fused = time_launches(
+                torch, lambda i: wq.wq_lm_head_topk(a, bs[i % len(bs)], n, k, fmt, topk, vals, ids), iters, warmup)
+
+            def unfused(i):
+                wq.wq_matmul(a, bs[i % len(bs)], logits, 1, n, k, fmt)
+                wq.wq_topk(logits, n, topk, vals, ids)
+
+            t_unf = time_launches(torch, unfused, iters, warmup)
+            out[f"{key}_k{topk}"] = {"fused_us": round(t_fused * 1e6, 2), "gemv_then_topk_us": round(t_unf * 1e6, 2),
+                                     "gemv_only_us": round(t_gemv * 1e6, 2),
+                                     "fused_weight_GB/s": round(nbytes / t_fused / 1e9, 1)}
+        del bs, b0
+        torch.cuda.empty_cache()
     return out
 
 
@@ -387,6 +426,11 @@ def main():
     if not args.no_secondary and only in (None, "epi"):
         log("fused epilogues")
         secondary["epilogues"] = epilogue_bench(torch, wq, wqgen, args.seed, max(10, args.steps // 2), args.warmup)
+
+    if not args.no_secondary and only in (None, "topk"):
+        log("LM-head top-k")
+        secondary["lm_head_topk_151936x2048"] = topk_bench(torch, wq, wqgen, args.seed, max(10, args.steps // 2),
+                                                          args.warmup)
 
     if (not args.no_secondary and only is None) or only == "f16":
         log("device copy reference")

@@ -35,6 +35,9 @@ WQ_ERR_LAUNCH = 6
 WQ_ERR_ALIAS = 7
 WQ_ERR_ROUTE = 8
 WQ_ERR_EPILOGUE = 9
+WQ_ERR_TOPK = 10
+WQ_TOPK_MAX = 64
+WQ_TOPK_NO_ID = 0xFFFFFFFF
 
 WQ_ROUTE_AUTO = 0
 WQ_ROUTE_GEMV = 1
@@ -71,6 +74,8 @@ def _load() -> ctypes.CDLL:
         "wq_gemm_q4_0": (I, [P, P, P, I64, I64, I64, P]),
         "wq_matmul": (I, [P, P, P, I64, I64, I64, I, P]),
         "wq_matmul_ex": (I, [P, P, P, I64, I64, I64, I, I, P]),
+        "wq_lm_head_topk": (I, [P, P, I64, I64, I, I, P, P, P]),
+        "wq_topk": (I, [P, I64, I, P, P, P]),
         "wq_pack_f16": (I, [P, P, I64, P]),
         "wq_quantize_q8_0": (I, [P, P, I64, P]),
         "wq_route_for": (I, [I64, I64, I64, I]),
@@ -204,6 +209,37 @@ def wq_matmul_ex(a, b, c, m: int, n: int, k: int, fmt: int, epi: int, stream=Non
     _check(_lib.wq_matmul_ex(_ptr(a), _ptr(b), _ptr(c), m, n, k, fmt, epi, _stream(stream, c)), "wq_matmul_ex")
 
 
+def _topk_out(vals, ids, topk):
+    if 1 <= topk <= WQ_TOPK_MAX:
+        _dtype(vals, _F32, "vals")
+        _dtype(ids, (torch.uint32, torch.int32), "ids")
+        _need(vals, 4 * topk, "vals")
+        _need(ids, 4 * topk, "ids")
+
+
+def wq_lm_head_topk(a, b, n: int, k: int, fmt: int, topk: int, vals, ids, stream=None) -> None:
+    """Fused LM-head GEMV + top-k for one token: vals / ids (topk entries, rank
+    order) of logits[j] = sum_k a[k] w[j, k]."""
+    if fmt in (WQ_FMT_F16, WQ_FMT_Q8_0, WQ_FMT_Q4_0) and n > 0:
+        _dtype(a, _F32, "a")
+        _dtype(b, _H if fmt == WQ_FMT_F16 else _U8, "b")
+        _need(a, 4 * k, "a")
+        if k >= 0 and (fmt == WQ_FMT_F16 or k % 32 == 0):
+            _need(b, weight_bytes(n, k, fmt), "b")
+    _topk_out(vals, ids, topk)
+    _check(_lib.wq_lm_head_topk(_ptr(a), _ptr(b), n, k, fmt, topk, _ptr(vals), _ptr(ids), _stream(stream, vals)),
+           "wq_lm_head_topk")
+
+
+def wq_topk(logits, n: int, topk: int, vals, ids, stream=None) -> None:
+    """Top-k of an f32 logits vector [n] (device)."""
+    if n > 0:
+        _dtype(logits, _F32, "logits")
+        _need(logits, 4 * n, "logits")
+    _topk_out(vals, ids, topk)
+    _check(_lib.wq_topk(_ptr(logits), n, topk, _ptr(vals), _ptr(ids), _stream(stream, vals)), "wq_topk")
+
+
 def wq_pack_f16(w, out, count: int, stream=None) -> None:
     if count > 0:
         _dtype(w, _F32, "w")
@@ -286,3 +322,12 @@ def matmul(a: torch.Tensor, b: torch.Tensor, n: int, k: int, fmt: int, out=None,
     c = out if out is not None else torch.empty((m, n), dtype=torch.float32, device=a.device)
     wq_matmul(a, b, c, m, n, k, fmt, stream)
     return c
+
+
+def lm_head_topk(a: torch.Tensor, b: torch.Tensor, n: int, k: int, fmt: int, topk: int, stream=None):
+    """(vals f32 [topk], ids int32 [topk]) via wq_lm_head_topk; ids hold the uint32
+    token ids as int32 bit patterns (the sentinel WQ_TOPK_NO_ID reads as -1)."""
+    vals = torch.empty(topk, dtype=torch.float32, device=a.device)
+    ids = torch.empty(topk, dtype=torch.int32, device=a.device)
+    wq_lm_head_topk(a, b, n, k, fmt, topk, vals, ids, stream)
+    return vals, ids

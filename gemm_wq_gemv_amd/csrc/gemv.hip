@@ -46,6 +46,12 @@
 namespace wq {
 namespace {
 
+// What a GEMV kernel does with its row sums: store them (or add them: the
+// residual flag), store silu(gate) * up (GLU), or keep a per-wave top-k list
+// of (sum, row) and write it out at the end (TOPK: c is then a TopkCand array
+// of one list of `aux` entries per wave, and the flag argument is that k).
+enum { kModeStore = 0, kModeGlu = 1, kModeTopk = 2 };
+
 // ------------------------------------------------------------------ f16 ----
 
 __device__ __forceinline__ float dot8_f16(uint4 w, float4 lo, float4 hi, float acc) {
@@ -65,11 +71,12 @@ __device__ __forceinline__ float dot8_f16(uint4 w, float4 lo, float4 hi, float a
 // GLU: n is the output count and b has 2n rows; a group is R/2 gate rows and
 // the R/2 up rows of the same outputs.  Otherwise a group is R rows of b.
 // Requires K % 8 == 0 and 16-byte aligned a and b.
-template <int T, int R, bool FULL, bool GLU>
+template <int T, int R, bool FULL, int MODE>
 __global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
                                                     const uint16_t *__restrict__ b,
                                                     float *__restrict__ c, int64_t n, int64_t k,
                                                     int64_t groups, int resid) {
+    constexpr bool GLU = MODE == kModeGlu;
     static_assert(!GLU || R % 2 == 0, "a GLU group pairs gate and up rows");
     constexpr int OC = GLU ? R / 2 : R;  // outputs per group
     const int lane = threadIdx.x & (kWave - 1);
@@ -91,6 +98,8 @@ __global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
         }
     }
 
+    WaveTopk top;
+    if constexpr (MODE == kModeTopk) top.init();
     for (int64_t g = wave; g < groups; g += nwaves) {
         const int64_t r0 = g * OC;  // first output of the group
         uint4 w[R][T];
@@ -124,26 +133,36 @@ __global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
         if constexpr (GLU) {
             const float up = __shfl_down(mine, OC, kWave);  // lane r + OC holds the up sum
             if (lane < OC && r0 + lane < n) c[r0 + lane] = silu(mine) * up;
+        } else if constexpr (MODE == kModeTopk) {
+            top.offer(resid, mine, static_cast<uint32_t>(r0 + lane), lane < R && r0 + lane < n);
         } else {
             if (lane < R && r0 + lane < n) c[r0 + lane] = resid ? c[r0 + lane] + mine : mine;
         }
     }
+    if constexpr (MODE == kModeTopk) top.store(reinterpret_cast<TopkCand *>(c) + wave * resid, resid);
 }
 
 // Any K, any 2-byte alignment of b: one wave per row, lanes stride over K.
+template <bool TOPK>
 __global__ __launch_bounds__(256) void gemv_f16_any(const float *__restrict__ a,
                                                     const uint16_t *__restrict__ b,
                                                     float *__restrict__ c, int64_t n, int64_t k, int resid) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
     const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) / kWave;
+    WaveTopk top;
+    if constexpr (TOPK) top.init();
     for (int64_t row = wave; row < n; row += nwaves) {
         const uint16_t *brow = b + row * k;
         float acc = 0.f;
         for (int64_t kk = lane; kk < k; kk += kWave) acc = fmaf(half_bits_to_float(brow[kk]), a[kk], acc);
         acc = wave_sum(acc);
-        if (lane == 0) c[row] = resid ? c[row] + acc : acc;
+        if constexpr (TOPK)
+            top.offer(resid, acc, static_cast<uint32_t>(row), lane == 0);
+        else if (lane == 0)
+            c[row] = resid ? c[row] + acc : acc;
     }
+    if constexpr (TOPK) top.store(reinterpret_cast<TopkCand *>(c) + wave * resid, resid);
 }
 
 // ------------------------------------------------------- Q8_0 and Q4_0 ----
@@ -264,11 +283,12 @@ __device__ __forceinline__ float block_dot(const uint8_t *stage, int pb, const f
 // GLU: n is the output count and b has 2n rows; a pass stages HS = S/2 gate
 // rows (stage rows 0 .. HS-1) and the up rows of the same outputs (stage rows
 // HS .. S-1), two contiguous byte ranges.
-template <int FMT, int J, int LPR, int SL, bool GLU>
+template <int FMT, int J, int LPR, int SL, int MODE>
 __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
                                                     const uint8_t *__restrict__ b,
                                                     float *__restrict__ c, int64_t n, int64_t k,
                                                     int64_t passes, int resid) {
+    constexpr bool GLU = MODE == kModeGlu;
     extern __shared__ uint4 stage4[];
     constexpr int BB = QB<FMT>::kBytes;
     constexpr int CH = QB<FMT>::kChunks;
@@ -326,6 +346,8 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
     };
 
     const uint8_t *stage = reinterpret_cast<const uint8_t *>(stage4);
+    WaveTopk top;
+    if constexpr (MODE == kModeTopk) top.init();
     int64_t p = blockIdx.x;
     if (p < passes) fetch(p);
     for (; p < passes; p += gridDim.x) {
@@ -368,6 +390,9 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
             const float up = __shfl_down(sum, D, kWave);
             if (jl % (LPR / SL) == 0 && srow_mine < HS && srow_mine < rows)
                 c[row0 + srow_mine] = silu(sum) * up;
+        } else if constexpr (MODE == kModeTopk) {
+            top.offer(resid, sum, static_cast<uint32_t>(row0 + srow_mine),
+                      jl % (LPR / SL) == 0 && srow_mine < rows);
         } else {
             if (jl % (LPR / SL) == 0 && srow_mine < rows) {
                 float *dst = c + row0 + srow_mine;
@@ -375,11 +400,13 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
             }
         }
     }
+    if constexpr (MODE == kModeTopk)
+        top.store(reinterpret_cast<TopkCand *>(c) + static_cast<int64_t>(blockIdx.x) * resid, resid);
 }
 
 // Any K % 32 == 0 and 2-byte aligned b: one wave per row, lanes stride over
 // blocks, reading each block with 2-byte loads.
-template <int FMT>
+template <int FMT, bool TOPK>
 __global__ __launch_bounds__(256) void gemv_q_any(const float *__restrict__ a, const uint8_t *__restrict__ b,
                                                   float *__restrict__ c, int64_t n, int64_t k, int resid) {
     constexpr int BB = QB<FMT>::kBytes;
@@ -387,6 +414,8 @@ __global__ __launch_bounds__(256) void gemv_q_any(const float *__restrict__ a, c
     const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
     const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) / kWave;
     const int64_t nb = k >> 5;
+    WaveTopk top;
+    if constexpr (TOPK) top.init();
     for (int64_t row = wave; row < n; row += nwaves) {
         const uint8_t *brow = b + row * nb * BB;
         float acc = 0.f;
@@ -415,8 +444,12 @@ __global__ __launch_bounds__(256) void gemv_q_any(const float *__restrict__ a, c
             acc = fmaf(half_bits_to_float(blk[0]), sumq, acc);
         }
         acc = wave_sum(acc);
-        if (lane == 0) c[row] = resid ? c[row] + acc : acc;
+        if constexpr (TOPK)
+            top.offer(resid, acc, static_cast<uint32_t>(row), lane == 0);
+        else if (lane == 0)
+            c[row] = resid ? c[row] + acc : acc;
     }
+    if constexpr (TOPK) top.store(reinterpret_cast<TopkCand *>(c) + wave * resid, resid);
 }
 
 // ---------------------------------------------------------------- helpers --
@@ -446,51 +479,56 @@ hipError_t glu_two_pass(float *c, int64_t n, hipStream_t s, Gemv2n &&gemv2n) {
     return e != hipSuccess ? e : er;
 }
 
-template <int T, int R, bool GLU = false>
+// Launch helpers.  aux: the residual flag (kModeStore) or k (kModeTopk);
+// *lists (kModeTopk): the number of per-wave lists the launch writes.
+template <int T, int R, int MODE = kModeStore>
 hipError_t run_f16_vec(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
-                       hipStream_t s, int cus, int resid) {
-    const int64_t groups = (n + (GLU ? R / 2 : R) - 1) / (GLU ? R / 2 : R);
+                       hipStream_t s, int cus, int aux, int64_t *lists = nullptr) {
+    constexpr int OC = MODE == kModeGlu ? R / 2 : R;
+    const int64_t groups = (n + OC - 1) / OC;
     const int64_t waves = balanced_workers(groups, static_cast<int64_t>(cus) * 16);
     const int64_t blocks = (waves + 3) / 4;
     const bool full = (k == 512LL * T);
+    if (lists) *lists = blocks * 4;
     if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_f16_vec<T=%d,R=%d,full=%d,glu=%d> n=%lld k=%lld grid=%lld block=256\n", T,
-                R, full ? 1 : 0, GLU ? 1 : 0, (long long)n, (long long)k, (long long)blocks);
+        fprintf(stderr, "[wqmm] gemv_f16_vec<T=%d,R=%d,full=%d,mode=%d> n=%lld k=%lld grid=%lld block=256\n", T,
+                R, full ? 1 : 0, MODE, (long long)n, (long long)k, (long long)blocks);
     if (full)
-        hipLaunchKernelGGL((gemv_f16_vec<T, R, true, GLU>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups,
-                           resid);
+        hipLaunchKernelGGL((gemv_f16_vec<T, R, true, MODE>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups,
+                           aux);
     else
-        hipLaunchKernelGGL((gemv_f16_vec<T, R, false, GLU>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups,
-                           resid);
+        hipLaunchKernelGGL((gemv_f16_vec<T, R, false, MODE>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups,
+                           aux);
     return hipGetLastError();
 }
 
-template <int FMT, int J, int LPR, int SL, bool GLU = false>
+template <int FMT, int J, int LPR, int SL, int MODE = kModeStore>
 hipError_t run_q_staged_sl(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
-                           int cus, int resid) {
+                           int cus, int aux, int64_t *lists = nullptr) {
     constexpr int S = SL * (kWave / LPR);
-    constexpr int HS = GLU ? S / 2 : S;
+    constexpr int HS = MODE == kModeGlu ? S / 2 : S;
     const int row_bytes = static_cast<int>((k >> 5) * QB<FMT>::kBytes);
     const int64_t passes = (n + HS - 1) / HS;
     // 12 single-wave workgroups per CU: measured best on MI355X (N = 151936).
     const int64_t blocks = balanced_workers(passes, static_cast<int64_t>(cus) * 12);
     const size_t lds = (static_cast<size_t>(S) * row_bytes + 1023) / 1024 * 1024;  // whole 1 KiB writes
+    if (lists) *lists = blocks;
     if (trace_enabled())
         fprintf(stderr,
-                "[wqmm] gemv_q_staged<fmt=%d,J=%d,LPR=%d,SL=%d,glu=%d> n=%lld k=%lld S=%d grid=%lld block=64 "
+                "[wqmm] gemv_q_staged<fmt=%d,J=%d,LPR=%d,SL=%d,mode=%d> n=%lld k=%lld S=%d grid=%lld block=64 "
                 "lds=%zu\n",
-                FMT, J, LPR, SL, GLU ? 1 : 0, (long long)n, (long long)k, S, (long long)blocks, lds);
-    hipLaunchKernelGGL((gemv_q_staged<FMT, J, LPR, SL, GLU>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k, passes,
-                       resid);
+                FMT, J, LPR, SL, MODE, (long long)n, (long long)k, S, (long long)blocks, lds);
+    hipLaunchKernelGGL((gemv_q_staged<FMT, J, LPR, SL, MODE>), dim3(blocks), dim3(64), lds, s, a, b, c, n, k,
+                       passes, aux);
     return hipGetLastError();
 }
 
 // Rows per pass: as many as fit the stage (S * row_bytes <= kStage), but few
 // enough that a small matrix still gives every CU about four waves (a wave
 // decodes its rows after its loads land); SL is a power of two.
-template <int FMT, int J, int LPR>
+template <int FMT, int J, int LPR, int MODE = kModeStore>
 hipError_t run_q_staged(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
-                        int cus, int resid) {
+                        int cus, int aux, int64_t *lists = nullptr) {
     constexpr int RPL = kWave / LPR;
     const int row_bytes = static_cast<int>((k >> 5) * QB<FMT>::kBytes);
     const int64_t s_fit = QB<FMT>::kStage / row_bytes;
@@ -499,10 +537,12 @@ hipError_t run_q_staged(const float *a, const uint8_t *b, float *c, int64_t n, i
     // measured faster than 8 or 16 rows for both formats at K = 2048.
     const int64_t sl_max = std::max<int64_t>(1, std::min<int64_t>(4, std::min(s_fit, s_fill) / RPL));
     if constexpr (J <= 2)
-        if (sl_max >= 4 && 4 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 4>(a, b, c, n, k, s, cus, resid);
+        if (sl_max >= 4 && 4 * RPL <= s_fit)
+            return run_q_staged_sl<FMT, J, LPR, 4, MODE>(a, b, c, n, k, s, cus, aux, lists);
     if constexpr (J <= 4)
-        if (sl_max >= 2 && 2 * RPL <= s_fit) return run_q_staged_sl<FMT, J, LPR, 2>(a, b, c, n, k, s, cus, resid);
-    return run_q_staged_sl<FMT, J, LPR, 1>(a, b, c, n, k, s, cus, resid);
+        if (sl_max >= 2 && 2 * RPL <= s_fit)
+            return run_q_staged_sl<FMT, J, LPR, 2, MODE>(a, b, c, n, k, s, cus, aux, lists);
+    return run_q_staged_sl<FMT, J, LPR, 1, MODE>(a, b, c, n, k, s, cus, aux, lists);
 }
 
 // The fused SwiGLU variant (n outputs, 2n rows): as run_q_staged over the 2n
@@ -519,30 +559,70 @@ bool run_q_staged_glu(const float *a, const uint8_t *b, float *c, int64_t n, int
     const int64_t sl_max = std::max<int64_t>(1, std::min<int64_t>(4, std::min(s_fit, s_fill) / RPL));
     if constexpr (J <= 2)
         if (sl_max >= 4 && 4 * RPL <= s_fit) {
-            *e = run_q_staged_sl<FMT, J, LPR, 4, true>(a, b, c, n, k, s, cus, 0);
+            *e = run_q_staged_sl<FMT, J, LPR, 4, kModeGlu>(a, b, c, n, k, s, cus, 0);
             return true;
         }
     if constexpr (J <= 4)
         if ((sl_max >= 2 || RPL == 1) && 2 * RPL <= s_fit) {
-            *e = run_q_staged_sl<FMT, J, LPR, 2, true>(a, b, c, n, k, s, cus, 0);
+            *e = run_q_staged_sl<FMT, J, LPR, 2, kModeGlu>(a, b, c, n, k, s, cus, 0);
             return true;
         }
     if constexpr (RPL >= 2) {
-        *e = run_q_staged_sl<FMT, J, LPR, 1, true>(a, b, c, n, k, s, cus, 0);
+        *e = run_q_staged_sl<FMT, J, LPR, 1, kModeGlu>(a, b, c, n, k, s, cus, 0);
         return true;
     }
     return false;
 }
 
+// Upper bound of the per-wave lists any top-k GEMV launch writes: f16 and the
+// plain kernels use at most 16 waves per CU (plus a partial workgroup), the
+// staged kernel 12.
+int64_t max_topk_lists(int cus) { return static_cast<int64_t>(cus) * 16 + 4; }
+
 // Staged kernel when K % 256 == 0, a and b are 16-byte aligned and a row fits
 // the stage with at most 8 blocks per lane; otherwise the plain kernel.
+// MODE kModeStore (aux = residual flag) or kModeTopk (aux = k).
+template <int FMT, int MODE>
+hipError_t gemv_q_rows(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int cus,
+                       int aux, int64_t *lists) {
+    const int64_t nb = k / 32;
+    const int64_t row_bytes = nb * QB<FMT>::kBytes;
+    if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= QB<FMT>::kStage && nb <= 512) {
+        if (nb >= 64) {
+            switch ((nb + 63) / 64) {
+                case 1: return run_q_staged<FMT, 1, 64, MODE>(a, b, c, n, k, s, cus, aux, lists);
+                case 2: return run_q_staged<FMT, 2, 64, MODE>(a, b, c, n, k, s, cus, aux, lists);
+                case 3: return run_q_staged<FMT, 3, 64, MODE>(a, b, c, n, k, s, cus, aux, lists);
+                case 4: return run_q_staged<FMT, 4, 64, MODE>(a, b, c, n, k, s, cus, aux, lists);
+                case 5: return run_q_staged<FMT, 5, 64, MODE>(a, b, c, n, k, s, cus, aux, lists);
+                case 6: return run_q_staged<FMT, 6, 64, MODE>(a, b, c, n, k, s, cus, aux, lists);
+                case 7: return run_q_staged<FMT, 7, 64, MODE>(a, b, c, n, k, s, cus, aux, lists);
+                default: return run_q_staged<FMT, 8, 64, MODE>(a, b, c, n, k, s, cus, aux, lists);
+            }
+        } else if (nb >= 32) {
+            if (nb == 32) return run_q_staged<FMT, 1, 32, MODE>(a, b, c, n, k, s, cus, aux, lists);
+            return run_q_staged<FMT, 2, 32, MODE>(a, b, c, n, k, s, cus, aux, lists);
+        } else {
+            if (nb <= 16) return run_q_staged<FMT, 1, 16, MODE>(a, b, c, n, k, s, cus, aux, lists);
+            return run_q_staged<FMT, 2, 16, MODE>(a, b, c, n, k, s, cus, aux, lists);
+        }
+    }
+    const int64_t waves = balanced_workers(n, static_cast<int64_t>(cus) * 16);
+    const int64_t blocks = (waves + 3) / 4;
+    if (lists) *lists = blocks * 4;
+    if (trace_enabled())
+        fprintf(stderr, "[wqmm] gemv_q_any<fmt=%d,topk=%d> n=%lld k=%lld grid=%lld block=256\n", FMT,
+                MODE == kModeTopk, (long long)n, (long long)k, (long long)blocks);
+    hipLaunchKernelGGL((gemv_q_any<FMT, MODE == kModeTopk>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, aux);
+    return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t launch_gemv_q(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
                          int epi) {
     DeviceInfo di;
     hipError_t e = device_info(&di);
     if (e != hipSuccess) return e;
-    const int resid = epi == kEpiResidual;
     const int64_t nb = k / 32;
     const int64_t row_bytes = nb * QB<FMT>::kBytes;
     const bool staged = nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= QB<FMT>::kStage && nb <= 512;
@@ -568,32 +648,32 @@ hipError_t launch_gemv_q(const float *a, const uint8_t *b, float *c, int64_t n, 
         }
         return glu_two_pass(c, n, s, [&](float *gu) { return launch_gemv_q<FMT>(a, b, gu, 2 * n, k, s, kEpiNone); });
     }
-    if (staged) {
-        if (nb >= 64) {
-            switch ((nb + 63) / 64) {
-                case 1: return run_q_staged<FMT, 1, 64>(a, b, c, n, k, s, di.cus, resid);
-                case 2: return run_q_staged<FMT, 2, 64>(a, b, c, n, k, s, di.cus, resid);
-                case 3: return run_q_staged<FMT, 3, 64>(a, b, c, n, k, s, di.cus, resid);
-                case 4: return run_q_staged<FMT, 4, 64>(a, b, c, n, k, s, di.cus, resid);
-                case 5: return run_q_staged<FMT, 5, 64>(a, b, c, n, k, s, di.cus, resid);
-                case 6: return run_q_staged<FMT, 6, 64>(a, b, c, n, k, s, di.cus, resid);
-                case 7: return run_q_staged<FMT, 7, 64>(a, b, c, n, k, s, di.cus, resid);
-                default: return run_q_staged<FMT, 8, 64>(a, b, c, n, k, s, di.cus, resid);
-            }
-        } else if (nb >= 32) {
-            if (nb == 32) return run_q_staged<FMT, 1, 32>(a, b, c, n, k, s, di.cus, resid);
-            return run_q_staged<FMT, 2, 32>(a, b, c, n, k, s, di.cus, resid);
-        } else {
-            if (nb <= 16) return run_q_staged<FMT, 1, 16>(a, b, c, n, k, s, di.cus, resid);
-            return run_q_staged<FMT, 2, 16>(a, b, c, n, k, s, di.cus, resid);
-        }
+    return gemv_q_rows<FMT, kModeStore>(a, b, c, n, k, s, di.cus, epi == kEpiResidual, nullptr);
+}
+
+// f16 rows: the vector kernel when K % 8 == 0, a and b are 16-byte aligned and
+// K <= 16384, else the plain kernel.  MODE kModeStore or kModeTopk.
+template <int MODE>
+hipError_t gemv_f16_rows(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
+                         int cus, int aux, int64_t *lists) {
+    const int64_t T = (k / 8 + 63) / 64;
+    if (k % 8 == 0 && aligned16(a) && aligned16(b) && T >= 1 && T <= 32) {
+        if (T <= 1) return run_f16_vec<1, 8, MODE>(a, b, c, n, k, s, cus, aux, lists);
+        if (T <= 2) return run_f16_vec<2, 8, MODE>(a, b, c, n, k, s, cus, aux, lists);
+        if (T <= 4) return run_f16_vec<4, 4, MODE>(a, b, c, n, k, s, cus, aux, lists);
+        if (T <= 8) return run_f16_vec<8, 2, MODE>(a, b, c, n, k, s, cus, aux, lists);
+        if (T <= 12) return run_f16_vec<12, 1, MODE>(a, b, c, n, k, s, cus, aux, lists);
+        if (T <= 16) return run_f16_vec<16, 1, MODE>(a, b, c, n, k, s, cus, aux, lists);
+        if (T <= 24) return run_f16_vec<24, 1, MODE>(a, b, c, n, k, s, cus, aux, lists);
+        return run_f16_vec<32, 1, MODE>(a, b, c, n, k, s, cus, aux, lists);
     }
-    const int64_t waves = balanced_workers(n, static_cast<int64_t>(di.cus) * 16);
+    const int64_t waves = balanced_workers(n, static_cast<int64_t>(cus) * 16);
     const int64_t blocks = (waves + 3) / 4;
+    if (lists) *lists = blocks * 4;
     if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_q_any<fmt=%d> n=%lld k=%lld grid=%lld block=256\n", FMT, (long long)n,
-                (long long)k, (long long)blocks);
-    hipLaunchKernelGGL((gemv_q_any<FMT>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, resid);
+        fprintf(stderr, "[wqmm] gemv_f16_any<topk=%d> n=%lld k=%lld grid=%lld block=256\n", MODE == kModeTopk,
+                (long long)n, (long long)k, (long long)blocks);
+    hipLaunchKernelGGL((gemv_f16_any<MODE == kModeTopk>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, aux);
     return hipGetLastError();
 }
 
@@ -604,38 +684,19 @@ hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t 
     DeviceInfo di;
     hipError_t e = device_info(&di);
     if (e != hipSuccess) return e;
-    const int resid = epi == kEpiResidual;
-    const int64_t nch = k / 8;
-    const int64_t T = (nch + 63) / 64;
-    const bool vec = k % 8 == 0 && aligned16(a) && aligned16(b) && T >= 1 && T <= 32;
+    const int64_t T = (k / 8 + 63) / 64;
     if (epi == kEpiGlu) {
-        // R rows per group as below, at least one gate and one up row.
-        if (vec && T <= 16) {
-            if (T <= 1) return run_f16_vec<1, 8, true>(a, b, c, n, k, s, di.cus, 0);
-            if (T <= 2) return run_f16_vec<2, 8, true>(a, b, c, n, k, s, di.cus, 0);
-            if (T <= 4) return run_f16_vec<4, 4, true>(a, b, c, n, k, s, di.cus, 0);
-            if (T <= 8) return run_f16_vec<8, 2, true>(a, b, c, n, k, s, di.cus, 0);
-            return run_f16_vec<16, 2, true>(a, b, c, n, k, s, di.cus, 0);
+        // R rows per group as for the plain rows, at least one gate and one up row.
+        if (k % 8 == 0 && aligned16(a) && aligned16(b) && T >= 1 && T <= 16) {
+            if (T <= 1) return run_f16_vec<1, 8, kModeGlu>(a, b, c, n, k, s, di.cus, 0);
+            if (T <= 2) return run_f16_vec<2, 8, kModeGlu>(a, b, c, n, k, s, di.cus, 0);
+            if (T <= 4) return run_f16_vec<4, 4, kModeGlu>(a, b, c, n, k, s, di.cus, 0);
+            if (T <= 8) return run_f16_vec<8, 2, kModeGlu>(a, b, c, n, k, s, di.cus, 0);
+            return run_f16_vec<16, 2, kModeGlu>(a, b, c, n, k, s, di.cus, 0);
         }
         return glu_two_pass(c, n, s, [&](float *gu) { return launch_gemv_f16(a, b, gu, 2 * n, k, s, kEpiNone); });
     }
-    if (vec) {
-        if (T <= 1) return run_f16_vec<1, 8>(a, b, c, n, k, s, di.cus, resid);
-        if (T <= 2) return run_f16_vec<2, 8>(a, b, c, n, k, s, di.cus, resid);
-        if (T <= 4) return run_f16_vec<4, 4>(a, b, c, n, k, s, di.cus, resid);
-        if (T <= 8) return run_f16_vec<8, 2>(a, b, c, n, k, s, di.cus, resid);
-        if (T <= 12) return run_f16_vec<12, 1>(a, b, c, n, k, s, di.cus, resid);
-        if (T <= 16) return run_f16_vec<16, 1>(a, b, c, n, k, s, di.cus, resid);
-        if (T <= 24) return run_f16_vec<24, 1>(a, b, c, n, k, s, di.cus, resid);
-        return run_f16_vec<32, 1>(a, b, c, n, k, s, di.cus, resid);
-    }
-    const int64_t waves = balanced_workers(n, static_cast<int64_t>(di.cus) * 16);
-    const int64_t blocks = (waves + 3) / 4;
-    if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_f16_any n=%lld k=%lld grid=%lld block=256\n", (long long)n, (long long)k,
-                (long long)blocks);
-    hipLaunchKernelGGL(gemv_f16_any, dim3(blocks), dim3(256), 0, s, a, b, c, n, k, resid);
-    return hipGetLastError();
+    return gemv_f16_rows<kModeStore>(a, b, c, n, k, s, di.cus, epi == kEpiResidual, nullptr);
 }
 
 hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
@@ -646,6 +707,38 @@ hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t 
 hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
                             hipStream_t s, int epi) {
     return launch_gemv_q<QFMT_Q4_0>(a, b, c, n, k, s, epi);
+}
+
+hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk,
+                               float *vals, uint32_t *ids, hipStream_t s) {
+    if (topk < 1 || topk > kTopkMax) return hipErrorInvalidValue;
+    DeviceInfo di;
+    hipError_t e = device_info(&di);
+    if (e != hipSuccess) return e;
+    const int64_t cap = max_topk_lists(di.cus);
+    ScratchLease lease;
+    void *scratch = nullptr;
+    e = lease.acquire(static_cast<size_t>(cap + kTopkGroups) * topk * sizeof(TopkCand), s, &scratch);
+    if (e != hipSuccess) return e;
+    TopkCand *cand = static_cast<TopkCand *>(scratch);
+    TopkCand *partial = cand + cap * topk;
+    float *out = reinterpret_cast<float *>(cand);
+    // Every top-k launch below writes at most `cap` lists: balanced_workers never
+    // exceeds its cap (16 waves per CU, rounded up to whole workgroups of 4, or
+    // 12 single-wave workgroups per CU for the staged kernel).
+    // n == 0: no GEMV, and the merge of zero lists writes sentinels.
+    int64_t lists = 0;
+    if (n == 0)
+        e = hipSuccess;
+    else if (fmt == QFMT_Q8_0)
+        e = gemv_q_rows<QFMT_Q8_0, kModeTopk>(a, static_cast<const uint8_t *>(b), out, n, k, s, di.cus, topk, &lists);
+    else if (fmt == QFMT_Q4_0)
+        e = gemv_q_rows<QFMT_Q4_0, kModeTopk>(a, static_cast<const uint8_t *>(b), out, n, k, s, di.cus, topk, &lists);
+    else
+        e = gemv_f16_rows<kModeTopk>(a, static_cast<const uint16_t *>(b), out, n, k, s, di.cus, topk, &lists);
+    if (e == hipSuccess) e = launch_topk_merge(cand, lists, nullptr, 0, topk, partial, vals, ids, s);
+    const hipError_t er = lease.release();
+    return e != hipSuccess ? e : er;
 }
 
 }  // namespace wq

@@ -90,6 +90,173 @@ __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 // SiLU as on the pages' silu_mul kernel: x / (1 + e^-x), in f32.
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
+// ----------------------------------------------------------------- top-k --
+// A (logit, token id) candidate.  Ranking (the pages' TopKCandidate rule): a
+// higher value first, equal values by the lower id; NaN values are never
+// taken, and empty slots hold the sentinel (-inf, kTopkNoId).
+struct TopkCand {
+    float v;
+    uint32_t id;
+};
+constexpr int kTopkMax = 64;  // one list entry per lane of a wave
+constexpr uint32_t kTopkNoId = 0xffffffffu;
+
+// Branch-free (bitwise) so that it compiles to compares and mask logic.
+__device__ __forceinline__ bool cand_better(float av, uint32_t aid, float bv, uint32_t bid) {
+    return (av > bv) | ((av == bv) & (aid < bid));
+}
+
+// A wave's running top-k list (k <= 64), sorted across lanes: lane r holds
+// rank r (lanes >= k hold scratch).  kv / kid: the entry of rank k - 1, the
+// bar a new candidate must beat (wave-uniform).
+// Value of lane (lane ^ D) for D = 1, 2, 4, 8 (DPP within a row of 16:
+// quad permutes and the row / half-row mirrors, xor 15 and xor 7), 16
+// (ds_swizzle bit mode within 32 lanes) and 32 (ds_bpermute).
+template <int D>
+__device__ __forceinline__ int xor_lane(int x) {
+    if constexpr (D == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+    if constexpr (D == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+    if constexpr (D == 4)  // row_half_mirror (xor 7), then quad_perm [3,2,1,0] (xor 3)
+        return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false), 0x1B, 0xf, 0xf, false);
+    if constexpr (D == 8)  // row_mirror (xor 15), then row_half_mirror (xor 7)
+        return __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false), 0x141, 0xf, 0xf, false);
+    if constexpr (D == 16) return __builtin_amdgcn_ds_swizzle(x, 0x401f);  // and 0x1f, xor 0x10
+    if constexpr (D == 32)
+        return __builtin_amdgcn_ds_bpermute(((static_cast<int>(threadIdx.x) & (kWave - 1)) ^ 32) * 4, x);
+    return x;
+}
+
+struct WaveTopk {
+    float v, kv;
+    uint32_t id, kid;
+
+    // Compare-exchange with lane ^ D: the lower lane of the pair keeps the
+    // better entry when `desc`, the worse otherwise.
+    template <int D>
+    __device__ __forceinline__ void bitonic_step(int lane, bool desc) {
+        const float pv = __builtin_bit_cast(float, xor_lane<D>(__builtin_bit_cast(int, v)));
+        const uint32_t pid = static_cast<uint32_t>(xor_lane<D>(static_cast<int>(id)));
+        const bool lower = (lane & D) == 0;
+        const bool keep_better = lower == desc;
+        const bool partner_better = cand_better(pv, pid, v, id);
+        const bool take = keep_better == partner_better;
+        v = take ? pv : v;
+        id = take ? pid : id;
+    }
+
+    // One block-size stage of the bitonic sort (blocks of S lanes sorted
+    // best first when lane & S == 0, worst first otherwise; S == 64: best first).
+    template <int S>
+    __device__ __forceinline__ void sort_block(int lane) {
+        const bool desc = S == kWave || (lane & S) == 0;
+        if constexpr (S >= 64) bitonic_step<32>(lane, desc);
+        if constexpr (S >= 32) bitonic_step<16>(lane, desc);
+        if constexpr (S >= 16) bitonic_step<8>(lane, desc);
+        if constexpr (S >= 8) bitonic_step<4>(lane, desc);
+        if constexpr (S >= 4) bitonic_step<2>(lane, desc);
+        bitonic_step<1>(lane, desc);
+    }
+
+    __device__ __forceinline__ void init() {
+        v = kv = -__builtin_huge_valf();
+        id = kid = kTopkNoId;
+    }
+
+    // Every lane may offer one candidate (pv, pid) (valid, not NaN).  Offers
+    // that beat the bar are inserted one at a time, lowest lane first: the
+    // insert position is the number of entries that rank before the
+    // candidate (a prefix of the lanes), and the entries from there on move
+    // up one lane (DPP wave_shr:1, a gfx9 whole-wave shift).  The loop runs
+    // once per accepted candidate and is wave-uniform; every cross-lane step
+    // is a readlane, a ballot or a DPP move, no LDS permute.
+    __device__ __forceinline__ void offer(int k, float pv, uint32_t pid, bool valid) {
+        const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+        valid = valid && !__builtin_isnan(pv);
+        uint64_t m = __builtin_amdgcn_ballot_w64(valid & cand_better(pv, pid, kv, kid));
+        while (m) {
+            const int j = static_cast<int>(__builtin_ctzll(m));
+            const float cv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pv), j));
+            const uint32_t cid = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(pid), j));
+            const int pos =
+                static_cast<int>(__builtin_popcountll(__builtin_amdgcn_ballot_w64((lane < k) & cand_better(v, id, cv, cid))));
+            const int uv = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x138, 0xf, 0xf, false);
+            const int uid = __builtin_amdgcn_update_dpp(0, static_cast<int>(id), 0x138, 0xf, 0xf, false);
+            v = lane == pos ? cv : lane > pos ? __builtin_bit_cast(float, uv) : v;
+            id = lane == pos ? cid : lane > pos ? static_cast<uint32_t>(uid) : id;
+            kv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k - 1));
+            kid = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(id), k - 1));
+            valid &= lane != j;
+            m = __builtin_amdgcn_ballot_w64(valid & cand_better(pv, pid, kv, kid));
+        }
+    }
+
+    // Merge of a list (bv, bid) sorted across the 64 lanes (best first,
+    // sentinels last) into this one: the top 64 of the union are
+    // better(mine[i], theirs[63 - i]) lane by lane, a bitonic sequence, which
+    // a 6-step bitonic merge sorts.  Entries of rank >= k are dropped first.
+    __device__ __forceinline__ void merge_sorted(int k, float bv, uint32_t bid) {
+        const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+        if (k == 1) {  // the better of the two first entries
+            const float fv = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, bv)));
+            const uint32_t fid = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bid)));
+            if (cand_better(fv, fid, kv, kid)) kv = fv, kid = fid;
+            v = kv;
+            id = kid;
+            return;
+        }
+        if (lane >= k) v = -__builtin_huge_valf(), id = kTopkNoId;
+        const int rev = (kWave - 1 - lane) * 4;
+        const float rv = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(rev, __builtin_bit_cast(int, bv)));
+        const uint32_t rid = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(rev, static_cast<int>(bid)));
+        const bool take = cand_better(rv, rid, v, id);
+        v = take ? rv : v;
+        id = take ? rid : id;
+        bitonic_step<32>(lane, true);
+        bitonic_step<16>(lane, true);
+        bitonic_step<8>(lane, true);
+        bitonic_step<4>(lane, true);
+        bitonic_step<2>(lane, true);
+        bitonic_step<1>(lane, true);
+        kv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k - 1));
+        kid = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(id), k - 1));
+    }
+
+    // The best of the 64 lanes' (v, id) in every lane (xor butterfly).
+    __device__ __forceinline__ void best_all() {
+        best_step<32>();
+        best_step<16>();
+        best_step<8>();
+        best_step<4>();
+        best_step<2>();
+        best_step<1>();
+    }
+    template <int D>
+    __device__ __forceinline__ void best_step() {
+        const float pv = __builtin_bit_cast(float, xor_lane<D>(__builtin_bit_cast(int, v)));
+        const uint32_t pid = static_cast<uint32_t>(xor_lane<D>(static_cast<int>(id)));
+        const bool take = cand_better(pv, pid, v, id);
+        v = take ? pv : v;
+        id = take ? pid : id;
+    }
+
+    // Sorts the 64 lanes' (v, id) best first (a full bitonic sort).
+    __device__ __forceinline__ void sort64() {
+        const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+        sort_block<2>(lane);
+        sort_block<4>(lane);
+        sort_block<8>(lane);
+        sort_block<16>(lane);
+        sort_block<32>(lane);
+        sort_block<64>(lane);
+    }
+
+    // Entries of rank < k as they stand (lane r writes rank r).
+    __device__ __forceinline__ void store(TopkCand *out, int k) const {
+        const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+        if (lane < k) out[lane] = TopkCand{v, id};
+    }
+};
+
 // Epilogues (the values of wq_epilogue in wqmm.h).  Residual: C += A.B^T.
 // GLU: the weights hold 2*NO rows (gate rows, then up rows) and
 // C[m, j] = silu(g) * u for the gate sum g (row j) and up sum u (row NO + j).
@@ -112,6 +279,20 @@ hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t 
                             hipStream_t s, int epi = kEpiNone);
 hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
                             hipStream_t s, int epi = kEpiNone);
+// Top-k of the LM-head logits w . a (w [n, k] in format fmt, one token):
+// the GEMV keeps a top-k list per wave, then launch_topk_merge reduces the
+// lists.  vals / ids: topk entries in rank order (1 <= topk <= kTopkMax).
+hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk,
+                               float *vals, uint32_t *ids, hipStream_t s);
+// Merge of candidate lists into the final top-k.  Lists are either `lists`
+// arrays of topk TopkCand (cand) or, with cand == nullptr, a logits vector
+// of n values cut into lists of 64 consecutive ids.  Two kernels: up to
+// kTopkGroups workgroups each reduce a share of the lists into `partial`
+// (kTopkGroups * topk entries), then one workgroup reduces those.
+constexpr int kTopkGroups = 64;
+hipError_t launch_topk_merge(const TopkCand *cand, int64_t lists, const float *logits, int64_t n, int topk,
+                             TopkCand *partial, float *vals, uint32_t *ids, hipStream_t s);
+
 // n = output columns; with kEpiGlu the weights have 2n rows.
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,
                        int64_t k, hipStream_t s, int epi = kEpiNone);
@@ -131,12 +312,13 @@ hipError_t launch_fill_zero(float *c, int64_t count, hipStream_t s);
 hipError_t launch_pack_f16(const float *w, uint16_t *out, int64_t count, hipStream_t s);
 hipError_t launch_quantize_q8_0(const float *w, uint8_t *out, int64_t count, hipStream_t s);
 
-// Split-K scratch.  One buffer per device, grown on demand from the device's
-// default memory pool (stream-ordered) and kept for reuse; a lease holds the
+// Scratch for split-K partial sums and the like.  One buffer per (device,
+// stream), grown on demand from the device's default memory pool
+// (stream-ordered) and kept for reuse: uses on one stream are ordered by the
+// stream, uses on different streams never share a buffer.  A lease holds the
 // device's lock from acquire() until the kernels that use the buffer are
-// enqueued, then records an event on the stream, and the next lease waits on
-// that event from its own stream, so uses on different streams never overlap.
-// Requests above kScratchCacheBytes take a private stream-ordered allocation.
+// enqueued.  Requests above kScratchCacheBytes, and streams beyond the first
+// eight seen on a device, take a private stream-ordered allocation.
 constexpr size_t kScratchCacheBytes = size_t(256) << 20;
 class ScratchLease {
   public:

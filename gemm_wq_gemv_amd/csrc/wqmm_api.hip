@@ -46,12 +46,19 @@ hipError_t device_info(DeviceInfo *out) {
 }
 
 namespace {
-struct DevScratch {
-    std::mutex mu;
+// One cached buffer per (device, stream): work on one stream is ordered by the
+// stream itself, so a reuse needs no event (an event record costs about 3 us
+// of GPU time on MI355X).  Up to kStreamSlots streams per device are cached.
+constexpr int kStreamSlots = 8;
+struct StreamScratch {
+    bool live = false;
+    hipStream_t stream = nullptr;
     void *ptr = nullptr;
     size_t bytes = 0;
-    hipEvent_t done = nullptr;  // recorded after the last use
-    bool used = false;
+};
+struct DevScratch {
+    std::mutex mu;
+    StreamScratch slot[kStreamSlots];
 };
 DevScratch g_scratch[kMaxDevices];
 }  // namespace
@@ -62,46 +69,50 @@ hipError_t ScratchLease::acquire(size_t bytes, hipStream_t s, void **ptr) {
     hipError_t e = hipGetDevice(&dev_);
     if (e != hipSuccess) return e;
     if (dev_ < 0 || dev_ >= kMaxDevices) return hipErrorInvalidDevice;
-    if (bytes > kScratchCacheBytes) {
+    DevScratch &d = g_scratch[dev_];
+    StreamScratch *slot = nullptr;
+    if (bytes <= kScratchCacheBytes) {
+        d.mu.lock();
+        held_ = true;
+        for (StreamScratch &x : d.slot)
+            if (x.live && x.stream == s) slot = &x;
+        if (!slot)
+            for (StreamScratch &x : d.slot)
+                if (!x.live) {
+                    slot = &x;
+                    slot->live = true;
+                    slot->stream = s;
+                    break;
+                }
+        if (!slot) {  // every slot taken by another stream
+            d.mu.unlock();
+            held_ = false;
+        }
+    }
+    if (!slot) {
         e = hipMallocAsync(&priv_, bytes, s);
         if (e == hipSuccess) *ptr = priv_;
         return e;
     }
-    DevScratch &d = g_scratch[dev_];
-    d.mu.lock();
-    held_ = true;
-    if (!d.done) {
-        e = hipEventCreateWithFlags(&d.done, hipEventDisableTiming);
-        if (e != hipSuccess) {
-            d.done = nullptr;
-            return e;
-        }
-    }
-    // Order this use after the previous one, whichever stream it was on.
-    if (d.used) {
-        e = hipStreamWaitEvent(s, d.done, 0);
-        if (e != hipSuccess) return e;
-    }
-    if (bytes > d.bytes) {
-        // Grow (at least double): free the old buffer and allocate the new one
-        // on this stream, both ordered after the wait above.
-        size_t want = d.bytes * 2 > bytes ? d.bytes * 2 : bytes;
+    if (bytes > slot->bytes) {
+        // Grow (at least double) on this stream, after its earlier uses.
+        size_t want = slot->bytes * 2 > bytes ? slot->bytes * 2 : bytes;
         if (want > kScratchCacheBytes) want = kScratchCacheBytes;
         want = (want + 4095) & ~size_t(4095);
-        if (d.ptr) {
-            e = hipFreeAsync(d.ptr, s);
-            d.ptr = nullptr;
-            d.bytes = 0;
+        if (slot->ptr) {
+            e = hipFreeAsync(slot->ptr, s);
+            slot->ptr = nullptr;
+            slot->bytes = 0;
             if (e != hipSuccess) return e;
         }
-        e = hipMallocAsync(&d.ptr, want, s);
+        e = hipMallocAsync(&slot->ptr, want, s);
         if (e != hipSuccess) {
-            d.ptr = nullptr;
+            slot->ptr = nullptr;
             return e;
         }
-        d.bytes = want;
+        slot->bytes = want;
     }
-    *ptr = d.ptr;
+    *ptr = slot->ptr;
     return hipSuccess;
 }
 
@@ -112,14 +123,8 @@ hipError_t ScratchLease::release() {
         priv_ = nullptr;
     }
     if (held_) {
-        DevScratch &d = g_scratch[dev_];
-        if (d.done) {
-            const hipError_t er = hipEventRecord(d.done, s_);
-            d.used = er == hipSuccess;
-            if (e == hipSuccess) e = er;
-        }
         held_ = false;
-        d.mu.unlock();
+        g_scratch[dev_].mu.unlock();
     }
     return e;
 }
@@ -253,7 +258,7 @@ int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, in
 
 extern "C" {
 
-int wq_abi_version(void) { return 102; }
+int wq_abi_version(void) { return 103; }
 
 const char *wq_status_str(int status) {
     switch (status) {
@@ -267,6 +272,7 @@ const char *wq_status_str(int status) {
         case WQ_ERR_ALIAS: return "output overlaps an input";
         case WQ_ERR_ROUTE: return "unknown route";
         case WQ_ERR_EPILOGUE: return "unknown epilogue";
+        case WQ_ERR_TOPK: return "top-k count outside 1 .. WQ_TOPK_MAX";
         default: return "unknown status";
     }
 }
@@ -327,6 +333,54 @@ int wq_matmul_ex(const float *a, const void *b, float *c, int64_t m, int64_t n, 
     int st = validate(a, b, c, m, n, k, fmt, &noop, epi);
     if (st != WQ_OK || noop) return st;
     return run_routed(a, b, c, m, n, k, fmt, epi, static_cast<hipStream_t>(stream));
+}
+
+int wq_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt, int topk, float *vals,
+                    uint32_t *ids, void *stream) {
+    if (!known_format(fmt)) return WQ_ERR_FORMAT;
+    if (n < 0 || k < 0) return WQ_ERR_SHAPE;
+    if (topk < 1 || topk > WQ_TOPK_MAX) return WQ_ERR_TOPK;
+    if (n >= static_cast<int64_t>(WQ_TOPK_NO_ID)) return WQ_ERR_SHAPE;  // ids must stay below the sentinel
+    if (fmt != WQ_FMT_F16 && (k == 0 || k % 32 != 0)) return WQ_ERR_K;
+    int64_t nk, b_bytes;
+    if (fmt == WQ_FMT_F16) {
+        if (!mul_ok(n, k, &nk) || !mul_ok(nk, 2, &b_bytes)) return WQ_ERR_SHAPE;
+    } else if (!mul_ok(n, (k / 32) * (fmt == WQ_FMT_Q8_0 ? 34 : 18), &b_bytes)) {
+        return WQ_ERR_SHAPE;
+    }
+    if (!vals || !ids) return WQ_ERR_NULL;
+    if (n > 0 && k > 0 && (!a || !b)) return WQ_ERR_NULL;
+    if (!aligned(vals, 4) || !aligned(ids, 4) || (a && !aligned(a, 4)) || (b && !aligned(b, 2))) return WQ_ERR_ALIGN;
+    const int64_t a_bytes = 4 * k, o_bytes = 4LL * topk;
+    if (overlaps(vals, o_bytes, ids, o_bytes)) return WQ_ERR_ALIAS;
+    for (const void *o : {static_cast<const void *>(vals), static_cast<const void *>(ids)})
+        if (overlaps(o, o_bytes, a, a_bytes) || overlaps(o, o_bytes, b, b_bytes)) return WQ_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // n == 0 or K == 0 still go through the kernels: the lists are then all
+    // sentinels (n == 0) or all logits are 0 (K == 0, f16).
+    return status_of(wq::launch_lm_head_topk(a, b, fmt, n, k, topk, vals, ids, s));
+}
+
+int wq_topk(const float *logits, int64_t n, int topk, float *vals, uint32_t *ids, void *stream) {
+    if (n < 0) return WQ_ERR_SHAPE;
+    if (topk < 1 || topk > WQ_TOPK_MAX) return WQ_ERR_TOPK;
+    if (n >= static_cast<int64_t>(WQ_TOPK_NO_ID)) return WQ_ERR_SHAPE;
+    if (!vals || !ids || (n > 0 && !logits)) return WQ_ERR_NULL;
+    if (!aligned(vals, 4) || !aligned(ids, 4) || (logits && !aligned(logits, 4))) return WQ_ERR_ALIGN;
+    const int64_t o_bytes = 4LL * topk;
+    if (overlaps(vals, o_bytes, ids, o_bytes) || overlaps(vals, o_bytes, logits, 4 * n) ||
+        overlaps(ids, o_bytes, logits, 4 * n))
+        return WQ_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    wq::ScratchLease lease;
+    void *scratch = nullptr;
+    if (lease.acquire(static_cast<size_t>(wq::kTopkGroups) * topk * sizeof(wq::TopkCand), s, &scratch) !=
+        hipSuccess)
+        return WQ_ERR_LAUNCH;
+    int st = status_of(wq::launch_topk_merge(nullptr, 0, logits, n, topk, static_cast<wq::TopkCand *>(scratch),
+                                             vals, ids, s));
+    if (lease.release() != hipSuccess && st == WQ_OK) st = WQ_ERR_LAUNCH;
+    return st;
 }
 
 int wq_pack_f16(const float *w, uint16_t *out, int64_t count, void *stream) {

@@ -37,8 +37,13 @@
  * the current HIP device.  The caller owns all memory; the library never
  * allocates, frees or keeps caller buffers.  Buffers must stay alive until the
  * enqueued work has run.  A GEMM that splits K takes a scratch buffer of
- * splits*M*N*4 bytes from the device's default memory pool, stream-ordered on
- * the call's stream (hipMallocAsync / hipFreeAsync); wq_gemm_plan tells when.
+ * splits*M*N*4 bytes (the other users of scratch say so below) from the
+ * device's default memory pool, stream-ordered on the call's stream
+ * (hipMallocAsync / hipFreeAsync); wq_gemm_plan tells when.  The library keeps
+ * one such buffer per stream it has seen (up to 256 MiB each, for the first
+ * eight streams of a device) and reuses it on that stream without further
+ * synchronisation; a stream must therefore have finished its libwqmm work
+ * before it is destroyed.
  *
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Every call only enqueues work and returns without synchronising;
@@ -78,7 +83,8 @@ typedef enum wq_status {
     WQ_ERR_LAUNCH = 6,  /* the HIP runtime failed to enqueue a kernel or scratch */
     WQ_ERR_ALIAS = 7,   /* c overlaps a or b */
     WQ_ERR_ROUTE = 8,   /* not a wq_route value */
-    WQ_ERR_EPILOGUE = 9 /* not a wq_epilogue value */
+    WQ_ERR_EPILOGUE = 9, /* not a wq_epilogue value */
+    WQ_ERR_TOPK = 10     /* top-k count outside 1 .. WQ_TOPK_MAX */
 } wq_status;
 
 /* Kernel families wq_matmul can route to. */
@@ -165,6 +171,41 @@ typedef enum wq_epilogue {
  * the 2n rows for SWIGLU. */
 int wq_matmul_ex(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt,
                  int epi, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* LM-head top-k (greedy and top-k sampling front end).
+ *
+ * Candidates are (logit, token id) pairs ranked as the pages' TopKCandidate
+ * (topk_better, lattice-inference 0.1.2 metal_qwen35.rs): a higher logit
+ * first, equal logits by the lower id; a NaN logit is never selected.  The
+ * result is the exact top-k under that ranking of the f32 logits the kernels
+ * compute, written in rank order to vals[0..topk-1] (f32) and ids[0..topk-1]
+ * (u32); when fewer than topk candidates exist the rest is (-inf,
+ * WQ_TOPK_NO_ID), the pages' sentinel (-INFINITY, UINT_MAX).  1 <= topk <=
+ * WQ_TOPK_MAX (the pages' block-local k values go up to 64) else
+ * WQ_ERR_TOPK; n < WQ_TOPK_NO_ID.  vals and ids are device pointers
+ * (4-byte aligned, not overlapping each other or the inputs).  Scratch:
+ * about (16 * CUs + 64) * topk * 8 bytes per call, stream-ordered as above. */
+#define WQ_TOPK_MAX 64
+#define WQ_TOPK_NO_ID 0xffffffffu
+
+/* Fused LM-head GEMV + top-k for one token: logits[j] = sum_k a[k] w[j, k]
+ * for the [n, K] weights b in format fmt (layouts as for the GEMV), and their
+ * top-k, without writing the n logits: every wave of the GEMV keeps a sorted
+ * top-k list of the rows it computed, and two small passes merge the lists.
+ * Passage: dispatch_lm_head_block_stage1_enc (fused LM-head GEMV with a
+ * block-local exact top-k writing compact (logit, token_id) candidates) and
+ * dispatch_block_topk_merge_enc (merge of those candidates), lattice-inference
+ * 0.9.0 dispatch.rs; k == 1 is the argmax of logits_argmax_first / _merge.
+ * n == 0 gives sentinels only; K == 0 (f16) makes every logit 0. */
+int wq_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt, int topk, float *vals,
+                    uint32_t *ids, void *stream);
+
+/* Top-k of an existing f32 logits vector [n] (device): the same selection
+ * over logits a caller already has.  Passage: dispatch_topk_enc,
+ * lattice-inference 0.9.0 dispatch.rs (argmax for k == 1, tournament merge
+ * passes for k > 1). */
+int wq_topk(const float *logits, int64_t n, int topk, float *vals, uint32_t *ids, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Weight preparation (done once, at load time).

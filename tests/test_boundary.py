@@ -28,7 +28,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("wq_gemv_f16", "wq_gemv_q8_0", "wq_gemv_q4_0", "wq_gemm_f16", "wq_gemm_q8_0",
-                 "wq_gemm_q4_0", "wq_matmul", "wq_matmul_ex", "wq_pack_f16", "wq_quantize_q8_0"):
+                 "wq_gemm_q4_0", "wq_matmul", "wq_matmul_ex", "wq_lm_head_topk", "wq_topk", "wq_pack_f16",
+                 "wq_quantize_q8_0"):
         assert want in names
 
 
@@ -50,8 +51,8 @@ def test_single_hip_runtime_in_process():
 
 
 def test_abi_and_status_strings():
-    assert wq.wq_abi_version() == 102
-    for st in range(0, 10):
+    assert wq.wq_abi_version() == 103
+    for st in range(0, 11):
         assert wq.status_str(st)
     assert wq.status_str(99) == "unknown status"
 
@@ -129,6 +130,36 @@ def test_epilogue_validation():
     with pytest.raises(ValueError):  # the binding checks b against 2n rows for SwiGLU
         wq.wq_matmul_ex(torch.zeros(64), torch.zeros(8 * 64, dtype=torch.uint16), torch.zeros(8), 1, 8, 64,
                         wq.WQ_FMT_F16, wq.WQ_EPI_SWIGLU)
+
+
+def test_topk_validation():
+    LM, TK = L.wq_lm_head_topk, L.wq_topk
+    V, I = 0x1900000, 0x1A00000  # output pointers
+    for topk in (0, -1, 65, 1000):
+        assert LM(A, B, 100, 64, wq.WQ_FMT_F16, topk, V, I, None) == wq.WQ_ERR_TOPK
+        assert TK(A, 100, topk, V, I, None) == wq.WQ_ERR_TOPK
+    assert LM(A, B, 100, 64, 3, 1, V, I, None) == wq.WQ_ERR_FORMAT
+    assert LM(A, B, -1, 64, wq.WQ_FMT_F16, 1, V, I, None) == wq.WQ_ERR_SHAPE
+    assert LM(A, B, 100, -64, wq.WQ_FMT_F16, 1, V, I, None) == wq.WQ_ERR_SHAPE
+    assert LM(A, B, 1 << 32, 64, wq.WQ_FMT_F16, 1, V, I, None) == wq.WQ_ERR_SHAPE  # ids would reach the sentinel
+    assert TK(A, (1 << 32) - 1, 1, V, I, None) == wq.WQ_ERR_SHAPE
+    assert TK(A, -5, 1, V, I, None) == wq.WQ_ERR_SHAPE
+    for k in (0, 48):
+        assert LM(A, B, 100, k, wq.WQ_FMT_Q8_0, 1, V, I, None) == wq.WQ_ERR_K
+        assert LM(A, B, 100, k, wq.WQ_FMT_Q4_0, 1, V, I, None) == wq.WQ_ERR_K
+    assert LM(A, B, 100, 64, wq.WQ_FMT_F16, 1, None, I, None) == wq.WQ_ERR_NULL
+    assert LM(A, B, 100, 64, wq.WQ_FMT_F16, 1, V, None, None) == wq.WQ_ERR_NULL
+    assert LM(None, B, 100, 64, wq.WQ_FMT_F16, 1, V, I, None) == wq.WQ_ERR_NULL
+    assert LM(A, None, 100, 64, wq.WQ_FMT_F16, 1, V, I, None) == wq.WQ_ERR_NULL
+    assert TK(None, 100, 1, V, I, None) == wq.WQ_ERR_NULL
+    assert LM(A, B, 100, 64, wq.WQ_FMT_F16, 1, V + 2, I, None) == wq.WQ_ERR_ALIGN
+    assert LM(A, B, 100, 64, wq.WQ_FMT_F16, 1, V, I + 1, None) == wq.WQ_ERR_ALIGN
+    assert LM(A + 2, B, 100, 64, wq.WQ_FMT_F16, 1, V, I, None) == wq.WQ_ERR_ALIGN
+    assert TK(A + 1, 100, 1, V, I, None) == wq.WQ_ERR_ALIGN
+    assert LM(A, B, 100, 64, wq.WQ_FMT_F16, 8, V, V + 16, None) == wq.WQ_ERR_ALIAS   # vals / ids overlap
+    assert LM(A, B, 100, 64, wq.WQ_FMT_F16, 8, A + 64, I, None) == wq.WQ_ERR_ALIAS   # vals inside a
+    assert LM(A, B, 100, 64, wq.WQ_FMT_F16, 8, V, B + 1000, None) == wq.WQ_ERR_ALIAS  # ids inside b
+    assert TK(A, 100, 8, A + 396, I, None) == wq.WQ_ERR_ALIAS                       # vals inside logits
 
 
 def test_routing_rule():

@@ -18,6 +18,10 @@ Parity status of each function (what pins it, see ``tests/test_oracle.py``):
                  permutation, numpy float64 matmul on the decoded weights
   silu           closed forms: silu(0) = 0, silu(ln 3) = (3/4) ln 3,
                  silu(x) - silu(-x) = x, limits at +-inf, sign
+  decode_attention  L = 1 gives v of the mapped KV head exactly; equal keys or
+                 scale 0 give the mean of v; a dominant key gives its v (also
+                 at scores of 1e4, which overflow without the max shift); numpy
+                 float64 softmax attention; joint token permutation; L = 0
   topk           numpy lexsort on random and tie-heavy logits, hand cases with
                  ties, NaN, +-inf, k > n (sentinel padding)
   matmul_epilogue  residual: exact hand sums on the worked example, linearity;
@@ -42,6 +46,8 @@ FMT_Q4_0 = 2
 EPI_NONE = 0
 EPI_RESIDUAL = 1
 EPI_SWIGLU = 2
+KV_F32 = 0
+KV_F16 = 1
 QK = 32
 BLOCK_BYTES = 34
 
@@ -101,6 +107,8 @@ class Oracle:
         lib.wqref_epilogue.argtypes = [I, P, P, I64, I64, P, P, P]
         lib.wqref_topk.restype = I
         lib.wqref_topk.argtypes = [P, I64, I64, P, P]
+        lib.wqref_decode_attention.restype = I
+        lib.wqref_decode_attention.argtypes = [P, P, P, I, I64, I64, I64, I64, ctypes.c_float, P, P]
         self.lib = lib
         self.path = path
 
@@ -260,6 +268,25 @@ class Oracle:
         vals, ids = self.topk(logits[0], topk)
         return vals, ids, logits[0], bound[0]
 
+    # -- decode attention (decode_attention / flash partial + reduce, engine page)
+    def decode_attention(self, q, k, v, kvfmt: int, L: int, D: int, Hq: int, Hkv: int, scale: float):
+        """(out, bound), float64 [Hq, D]: one query token's grouped-query attention over
+        an L-token K/V cache [L, Hkv*D] (kvfmt 0 f32, 1 f16 bits); head h reads KV head
+        h // (Hq // Hkv)."""
+        q = np.ascontiguousarray(q, dtype=np.float32)
+        dt = np.float32 if kvfmt == KV_F32 else np.uint16
+        k = np.ascontiguousarray(k, dtype=dt)
+        v = np.ascontiguousarray(v, dtype=dt)
+        if q.size < Hq * D or k.size < L * Hkv * D or v.size < L * Hkv * D:
+            raise ValueError("decode_attention: input too small")
+        out = np.empty((Hq, D), dtype=np.float64)
+        bound = np.empty((Hq, D), dtype=np.float64)
+        rc = self.lib.wqref_decode_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data, kvfmt, L, D, Hq, Hkv,
+                                             scale, out.ctypes.data, bound.ctypes.data)
+        if rc != 0:
+            raise ValueError("decode_attention: bad arguments")
+        return out, bound
+
 
 _default: Oracle | None = None
 
@@ -318,3 +345,7 @@ def topk(logits, k):
 
 def lm_head_topk(a, b, fmt, n, k, topk_, threads=None):
     return get().lm_head_topk(a, b, fmt, n, k, topk_, threads)
+
+
+def decode_attention(q, k, v, kvfmt, L, D, Hq, Hkv, scale):
+    return get().decode_attention(q, k, v, kvfmt, L, D, Hq, Hkv, scale)

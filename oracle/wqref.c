@@ -404,3 +404,72 @@ int wqref_topk(const double *logits, int64_t n, int64_t topk, double *vals, int6
     free(c);
     return 0;
 }
+
+/* ------------------------------------------------------ decode attention -- */
+
+/* Decode (one query token) grouped-query attention, as the lattice-inference
+ * 0.1.2 page's decode_attention / decode_attention_flash_partial +
+ * decode_attention_flash_reduce compute it: q is [Hq, D] f32; the K and V
+ * caches are [L, Hkv * D] (token-major, head h of token t at t * Hkv * D +
+ * h * D), f32 (kvfmt 0) or f16 bit patterns (kvfmt 1, the page's f16-KV
+ * variant); query head h reads KV head h / G with G = Hq / Hkv.  For each h:
+ * s_t = scale * sum_d q[h, d] k[t, d], p = softmax over t < L of s (written
+ * here as exp(s_t - max s) / sum, the same value), out[h, d] = sum_t p_t
+ * v[t, d].  L = 0 gives 0 (the reduce pass's l > 0 ? acc / l : 0).
+ *
+ * Tolerance per output: with B_t = |scale| (1e-5 sum_d |q_d k_td| + 1e-6)
+ * the product tolerance of each score, every p_t moves by at most a factor
+ * exp(+-2 max_t B_t); so |out - out_ref| <= (expm1(2 max_t B_t) + 1e-5)
+ * sum_t p_t |v_td| + 1e-6, the 1e-5 term covering the f32 exponentials and
+ * sums.  Returns 0, or -1 on bad arguments or memory. */
+static double kv_value(const void *c, int kvfmt, int64_t i) {
+    return kvfmt == 1 ? wqref_f16_value(((const uint16_t *)c)[i]) : (double)((const float *)c)[i];
+}
+
+int wqref_decode_attention(const float *q, const void *k, const void *v, int kvfmt, int64_t L, int64_t D,
+                           int64_t Hq, int64_t Hkv, float scale, double *out, double *bound) {
+    if (L < 0 || D <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || (kvfmt != 0 && kvfmt != 1)) return -1;
+    if (!q || !out || !bound || (L > 0 && (!k || !v))) return -1;
+    const int64_t G = Hq / Hkv, kv_dim = Hkv * D;
+    double *s = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    double *b = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    if (!s || !b) {
+        free(s);
+        free(b);
+        return -1;
+    }
+    for (int64_t h = 0; h < Hq; ++h) {
+        const int64_t kvh = h / G;
+        double smax = -INFINITY, bmax = 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            double dot = 0.0, mag = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                const double p = (double)q[h * D + d] * kv_value(k, kvfmt, t * kv_dim + kvh * D + d);
+                dot += p;
+                mag += fabs(p);
+            }
+            s[t] = (double)scale * dot;
+            b[t] = fabs((double)scale) * (1e-5 * mag + 1e-6);
+            if (s[t] > smax) smax = s[t];
+            if (b[t] > bmax) bmax = b[t];
+        }
+        double z = 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            s[t] = exp(s[t] - smax); /* unnormalised weight */
+            z += s[t];
+        }
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const double vv = kv_value(v, kvfmt, t * kv_dim + kvh * D + d);
+                acc += s[t] * vv;
+                mag += s[t] * fabs(vv);
+            }
+            out[h * D + d] = L > 0 ? acc / z : 0.0;
+            bound[h * D + d] = (L > 0 ? (expm1(2.0 * bmax) + 1e-5) * (mag / z) : 0.0) + 1e-6;
+        }
+    }
+    free(s);
+    free(b);
+    return 0;
+}

@@ -555,6 +555,96 @@ def pin_lm_head_topk(orc):
     assert np.array_equal(logits, c[0], equal_nan=True) and np.array_equal(bound, bd[0], equal_nan=True)
 
 
+# ------------------------------------------------------ decode attention --
+def _attn_inputs(L, D, Hq, Hkv, seed, kvfmt=oracle.KV_F32):
+    q = wqgen.normal((Hq, D), seed=seed, stream=11)
+    k = wqgen.normal((L, Hkv * D), seed=seed, stream=12)
+    v = wqgen.normal((L, Hkv * D), seed=seed, stream=13)
+    if kvfmt == oracle.KV_F16:
+        k, v = k.astype(np.float16).view(np.uint16), v.astype(np.float16).view(np.uint16)
+    return q, k, v
+
+
+def _kv_numpy(c, kvfmt):
+    return (c.view(np.float16) if kvfmt == oracle.KV_F16 else c).astype(np.float64)
+
+
+def pin_attention_single_token(orc):
+    """L = 1: softmax of one score is 1, so out[h] is the V row of the KV head that
+    query head h reads (h // G, the page's qh_base = kvh * group_size) exactly, for f32
+    and f16 caches (f16 decoded by numpy)."""
+    for kvfmt in (oracle.KV_F32, oracle.KV_F16):
+        for (D, Hq, Hkv) in ((256, 8, 2), (64, 6, 3), (128, 4, 4)):
+            q, k, v = _attn_inputs(1, D, Hq, Hkv, 5, kvfmt)
+            out, _ = orc.decode_attention(q, k, v, kvfmt, 1, D, Hq, Hkv, 0.0625)
+            vn = _kv_numpy(v, kvfmt).reshape(Hkv, D)
+            G = Hq // Hkv
+            for h in range(Hq):
+                assert np.array_equal(out[h], vn[h // G]), (kvfmt, D, Hq, Hkv, h)
+
+
+def pin_attention_uniform(orc):
+    """Equal keys, or scale 0, make every score equal, so p is uniform and out is the
+    mean of the V rows (numpy mean)."""
+    L, D, Hq, Hkv = 37, 64, 4, 2
+    q, k, v = _attn_inputs(L, D, Hq, Hkv, 6)
+    kk = np.repeat(k[:1], L, axis=0)
+    G = Hq // Hkv
+    for kc, scale in ((kk, 0.7), (k, 0.0)):
+        out, _ = orc.decode_attention(q, kc, v, oracle.KV_F32, L, D, Hq, Hkv, scale)
+        mean = v.astype(np.float64).reshape(L, Hkv, D).mean(axis=0)
+        for h in range(Hq):
+            assert np.allclose(out[h], mean[h // G], rtol=0, atol=1e-12)
+
+
+def pin_attention_dominant_key(orc):
+    """One key aligned with q and 60 (then 1e4) score units above the rest: its weight
+    is 1 within e^-60, so out is its V row; at 1e4 the scores overflow exp unless the
+    maximum is taken out first."""
+    L, D, Hq, Hkv = 50, 64, 2, 1
+    q, k, v = _attn_inputs(L, D, Hq, Hkv, 7)
+    q[1] = q[0]
+    k = np.zeros_like(k)
+    t0 = 17
+    for big in (60.0, 1e4):
+        kk = k.copy()
+        kk[t0] = q[0] * np.float32(big / float(np.dot(q[0].astype(np.float64), q[0])))
+        out, _ = orc.decode_attention(q, kk, v, oracle.KV_F32, L, D, Hq, Hkv, 1.0)
+        assert np.all(np.isfinite(out))
+        assert np.allclose(out[0], v[t0].astype(np.float64), rtol=0, atol=1e-20 + 10 * np.exp(-59.0) * 10)
+
+
+def pin_attention_numpy(orc):
+    """Against float64 numpy softmax attention (matmul, exp, sum) on random inputs,
+    f32 and f16 caches, ragged L; and the bound covers a 2e-5 relative perturbation."""
+    for kvfmt in (oracle.KV_F32, oracle.KV_F16):
+        for (L, D, Hq, Hkv) in ((1, 256, 8, 2), (100, 256, 8, 2), (513, 128, 8, 1), (77, 64, 3, 3)):
+            q, k, v = _attn_inputs(L, D, Hq, Hkv, L + D, kvfmt)
+            scale = 1.0 / np.sqrt(D)
+            out, bound = orc.decode_attention(q, k, v, kvfmt, L, D, Hq, Hkv, scale)
+            kn = _kv_numpy(k, kvfmt).reshape(L, Hkv, D)
+            vn = _kv_numpy(v, kvfmt).reshape(L, Hkv, D)
+            G = Hq // Hkv
+            for h in range(Hq):
+                s_ = np.float64(np.float32(scale)) * (kn[:, h // G, :] @ q[h].astype(np.float64))
+                w = np.exp(s_ - s_.max())
+                ref = (w / w.sum()) @ vn[:, h // G, :]
+                assert np.allclose(out[h], ref, rtol=1e-12, atol=1e-14), (kvfmt, L, D, h)
+            assert np.all(bound > 1e-6) and np.all(bound < 1e-2)
+
+
+def pin_attention_permutation_and_empty(orc):
+    """Permuting the cache tokens (K and V together) leaves out unchanged; L = 0 gives 0."""
+    L, D, Hq, Hkv = 64, 128, 4, 2
+    q, k, v = _attn_inputs(L, D, Hq, Hkv, 8)
+    perm = np.random.default_rng(1).permutation(L)
+    a, _ = orc.decode_attention(q, k, v, oracle.KV_F32, L, D, Hq, Hkv, 0.1)
+    b, _ = orc.decode_attention(q, k[perm], v[perm], oracle.KV_F32, L, D, Hq, Hkv, 0.1)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
+    z, bz = orc.decode_attention(q, k[:0], v[:0], oracle.KV_F32, 0, D, Hq, Hkv, 0.1)
+    assert np.array_equal(z, np.zeros((Hq, D)))
+
+
 PINS = [
     pin_f16_decode_exhaustive,
     pin_f16_encode_golden,
@@ -575,6 +665,11 @@ PINS = [
     pin_topk_hand,
     pin_topk_vs_lexsort,
     pin_lm_head_topk,
+    pin_attention_single_token,
+    pin_attention_uniform,
+    pin_attention_dominant_key,
+    pin_attention_numpy,
+    pin_attention_permutation_and_empty,
 ]
 
 
@@ -640,6 +735,14 @@ MUTANTS = {
     "topk_keeps_nan": ("if (!isnan(logits[i])) {", "if (1) {"),
     "topk_sentinel_zero": ("vals[r] = r < cnt ? c[r].v : -INFINITY;", "vals[r] = r < cnt ? c[r].v : 0.0;"),
     "topk_sentinel_id": ("(int64_t)4294967295LL", "(int64_t)-1"),
+    "attn_head_mod": ("const int64_t kvh = h / G;", "const int64_t kvh = h % Hkv;"),
+    "attn_no_scale": ("s[t] = (double)scale * dot;", "s[t] = dot;"),
+    "attn_no_max_shift": ("s[t] = exp(s[t] - smax);", "s[t] = exp(s[t]);"),
+    "attn_k_for_v": ("const double vv = kv_value(v, kvfmt,", "const double vv = kv_value(k, kvfmt,"),
+    "attn_last_token_dropped": ("for (int64_t t = 0; t < L; ++t) {\n            double dot",
+                                "for (int64_t t = 0; t + 1 < L; ++t) {\n            double dot"),
+    "attn_unnormalised": ("out[h * D + d] = L > 0 ? acc / z : 0.0;", "out[h * D + d] = L > 0 ? acc : 0.0;"),
+    "attn_head_stride_kvdim": ("kv_value(k, kvfmt, t * kv_dim + kvh * D + d)", "kv_value(k, kvfmt, t * D + kvh * D + d)"),
     "topk_drops_last": ("for (int64_t r = 0; r < topk; ++r) {\n        vals[r]",
                         "for (int64_t r = 0; r < topk; ++r) {\n        if (r == topk - 1 && r > 0) { vals[r] = -INFINITY; ids[r] = 4294967295LL; continue; }\n        vals[r]"),
 }

@@ -18,8 +18,9 @@ same suite.  ``secondary`` reports the other configurations: the Q8_0 and
 Q4_0 decode suites, the f16 prefill GEMM at M = 512, the Q8_0 and Q4_0 M
 sweeps, the fused residual and SwiGLU epilogues against the same product
 followed by separate element-wise kernels, the fused LM-head GEMV + top-k
-against the GEMV alone and the GEMV followed by a top-k pass, and a plain
-device copy as the achievable-bandwidth reference.  Q4_0
+against the GEMV alone and the GEMV followed by a top-k pass, the split-KV decode
+attention (KV bytes GB/s at 4K-128K tokens), and a plain device copy as the
+achievable-bandwidth reference.  Q4_0
 weights are synthetic bytes (random codes and scales) since no Q4_0 encoder is
 given.
 """
@@ -89,7 +90,7 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-secondary", action="store_true", help="headline suite only")
-    p.add_argument("--only", choices=["f16", "q8", "q4", "prefill", "sweep", "epi", "topk"], default=None,
+    p.add_argument("--only", choices=["f16", "q8", "q4", "prefill", "sweep", "epi", "topk", "attn"], default=None,
                    help="run one workload only (for profiling); prints no headline line")
     return p.parse_args()
 
@@ -259,6 +260,39 @@ def topk_bench(torch, wq, wqgen, seed, iters, warmup):
         del bs, b0
         torch.cuda.empty_cache()
     return out
+
+
+ATTN_LENS = [4096, 32768, 131072]
+
+
+def attention_bench(torch, wq, seed, iters, warmup):
+    """Split-KV decode attention at head_dim 256, 8 query heads over 2 KV heads
+    (q_dim 2048 = the o_proj input of the decode suite), f32 and f16 caches of
+    4096 / 32768 / 131072 tokens; K and V ~ N(0,1) drawn on the device (seeded),
+    rotated over copies of >= 1 GiB.  Bytes = the K and V rows read once."""
+    D, hq, hkv = 256, 8, 2
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    q = torch.randn((hq, D), device="cuda", generator=gen)
+    out = torch.empty((hq, D), device="cuda")
+    res = {}
+    for kvfmt, key in ((wq.WQ_KV_F32, "f32"), (wq.WQ_KV_F16, "f16")):
+        for L in ATTN_LENS:
+            dt = torch.float32 if kvfmt == wq.WQ_KV_F32 else torch.float16
+            nbytes = 2 * L * hkv * D * (4 if kvfmt == wq.WQ_KV_F32 else 2)
+            copies = max(2, math.ceil(ROTATE_BYTES / nbytes))
+            ks = [torch.randn((L, hkv * D), device="cuda", generator=gen).to(dt) for _ in range(copies)]
+            vs = [torch.randn((L, hkv * D), device="cuda", generator=gen).to(dt) for _ in range(copies)]
+            if kvfmt == wq.WQ_KV_F16:
+                ks = [x.view(torch.int16) for x in ks]
+                vs = [x.view(torch.int16) for x in vs]
+            t = time_launches(torch, lambda i: wq.wq_decode_attention(q, ks[i % copies], vs[i % copies], out, L, D,
+                                                                      hq, hkv, kvfmt, 0.0625), iters, warmup)
+            res[f"{key}_L{L}"] = {"us": round(t * 1e6, 2), "kv_GB/s": round(nbytes / t / 1e9, 1),
+                                  "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "kv_bytes": nbytes}
+            del ks, vs
+            torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(host_weights, seed, budget_s=12.0):
@@ -431,6 +465,11 @@ def main():
         log("LM-head top-k")
         secondary["lm_head_topk_151936x2048"] = topk_bench(torch, wq, wqgen, args.seed, max(10, args.steps // 2),
                                                           args.warmup)
+
+    if not args.no_secondary and only in (None, "attn"):
+        log("decode attention")
+        secondary["decode_attention_h256_q8_kv2"] = attention_bench(torch, wq, args.seed, max(10, args.steps // 2),
+                                                                   args.warmup)
 
     if (not args.no_secondary and only is None) or only == "f16":
         log("device copy reference")

@@ -37,6 +37,9 @@ WQ_ERR_ROUTE = 8
 WQ_ERR_EPILOGUE = 9
 WQ_ERR_TOPK = 10
 WQ_TOPK_MAX = 64
+WQ_ATTN_MAX_GROUP = 8
+WQ_KV_F32 = 0
+WQ_KV_F16 = 1
 WQ_TOPK_NO_ID = 0xFFFFFFFF
 
 WQ_ROUTE_AUTO = 0
@@ -76,6 +79,7 @@ def _load() -> ctypes.CDLL:
         "wq_matmul_ex": (I, [P, P, P, I64, I64, I64, I, I, P]),
         "wq_lm_head_topk": (I, [P, P, I64, I64, I, I, P, P, P]),
         "wq_topk": (I, [P, I64, I, P, P, P]),
+        "wq_decode_attention": (I, [P, P, P, P, I64, I, I, I, I, ctypes.c_float, P]),
         "wq_pack_f16": (I, [P, P, I64, P]),
         "wq_quantize_q8_0": (I, [P, P, I64, P]),
         "wq_route_for": (I, [I64, I64, I64, I]),
@@ -238,6 +242,27 @@ def wq_topk(logits, n: int, topk: int, vals, ids, stream=None) -> None:
         _need(logits, 4 * n, "logits")
     _topk_out(vals, ids, topk)
     _check(_lib.wq_topk(_ptr(logits), n, topk, _ptr(vals), _ptr(ids), _stream(stream, vals)), "wq_topk")
+
+
+def wq_decode_attention(q, k_cache, v_cache, out, cache_len: int, head_dim: int, num_q_heads: int,
+                        num_kv_heads: int, kv_fmt: int, scale: float, stream=None) -> None:
+    """One query token's grouped-query attention over a [cache_len, num_kv_heads*head_dim]
+    K/V cache (f32 or f16 bits): out [num_q_heads, head_dim]."""
+    if num_q_heads > 0 and head_dim > 0:
+        _dtype(q, _F32, "q")
+        _dtype(out, _F32, "out")
+        _need(q, 4 * num_q_heads * head_dim, "q")
+        _need(out, 4 * num_q_heads * head_dim, "out")
+        if cache_len > 0 and num_kv_heads > 0 and kv_fmt in (WQ_KV_F32, WQ_KV_F16):
+            kv = (_F32 if kv_fmt == WQ_KV_F32 else _H)
+            nbytes = cache_len * num_kv_heads * head_dim * (4 if kv_fmt == WQ_KV_F32 else 2)
+            _dtype(k_cache, kv, "k_cache")
+            _dtype(v_cache, kv, "v_cache")
+            _need(k_cache, nbytes, "k_cache")
+            _need(v_cache, nbytes, "v_cache")
+    _check(_lib.wq_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), cache_len, head_dim,
+                                    num_q_heads, num_kv_heads, kv_fmt, scale, _stream(stream, out)),
+           "wq_decode_attention")
 
 
 def wq_pack_f16(w, out, count: int, stream=None) -> None:

@@ -50,6 +50,20 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Maximum over aligned groups of G lanes, every lane of a group receiving it
+// (the same lane pairings as group_sum).
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "group size");
+    if constexpr (G >= 2) v = fmaxf(v, dpp_f32<0xb1>(v));
+    if constexpr (G >= 4) v = fmaxf(v, dpp_f32<0x4e>(v));
+    if constexpr (G >= 8) v = fmaxf(v, dpp_f32<0x141>(v));
+    if constexpr (G >= 16) v = fmaxf(v, dpp_f32<0x140>(v));
+    if constexpr (G >= 32) v = fmaxf(v, __shfl_xor(v, 16, kWave));
+    if constexpr (G >= 64) v = fmaxf(v, __shfl_xor(v, 32, kWave));
+    return v;
+}
+
 // The value of a partner lane that differs from this one in bit log2(H) and is
 // a perfect matching of the lanes with that bit clear to those with it set
 // (lane xor H for H >= 8; the DPP mirrors pair lanes inside a row).
@@ -292,6 +306,12 @@ hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n
 constexpr int kTopkGroups = 64;
 hipError_t launch_topk_merge(const TopkCand *cand, int64_t lists, const float *logits, int64_t n, int topk,
                              TopkCand *partial, float *vals, uint32_t *ids, hipStream_t s);
+
+// Decode attention for one query token (q [hq, d], K/V caches [len, hkv * d]
+// in f32 (kvf 0) or f16 (kvf 1), out [hq, d]); d in {64, 128, 256}, hq / hkv
+// in 1..8.  Split over the cache in partitions, then a merge pass.
+hipError_t launch_decode_attention(const float *q, const void *k, const void *v, int kvf, float *out, int64_t len,
+                                   int d, int hq, int hkv, float scale, hipStream_t s);
 
 // n = output columns; with kEpiGlu the weights have 2n rows.
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,

@@ -258,7 +258,7 @@ int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, in
 
 extern "C" {
 
-int wq_abi_version(void) { return 103; }
+int wq_abi_version(void) { return 104; }
 
 const char *wq_status_str(int status) {
     switch (status) {
@@ -381,6 +381,29 @@ int wq_topk(const float *logits, int64_t n, int topk, float *vals, uint32_t *ids
                                              vals, ids, s));
     if (lease.release() != hipSuccess && st == WQ_OK) st = WQ_ERR_LAUNCH;
     return st;
+}
+
+int wq_decode_attention(const float *q, const void *k_cache, const void *v_cache, float *out, int64_t cache_len,
+                        int head_dim, int num_q_heads, int num_kv_heads, int kv_fmt, float scale, void *stream) {
+    if (kv_fmt != WQ_KV_F32 && kv_fmt != WQ_KV_F16) return WQ_ERR_FORMAT;
+    if (cache_len < 0 || num_q_heads < 1 || num_kv_heads < 1) return WQ_ERR_SHAPE;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256) return WQ_ERR_SHAPE;
+    if (num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > WQ_ATTN_MAX_GROUP) return WQ_ERR_SHAPE;
+    const int64_t elem = kv_fmt == WQ_KV_F32 ? 4 : 2;
+    int64_t cache_elems, cache_bytes;
+    if (!mul_ok(cache_len, static_cast<int64_t>(num_kv_heads) * head_dim, &cache_elems) ||
+        !mul_ok(cache_elems, elem, &cache_bytes))
+        return WQ_ERR_SHAPE;
+    if (!q || !out || (cache_len > 0 && (!k_cache || !v_cache))) return WQ_ERR_NULL;
+    if (!aligned(q, 4) || !aligned(out, 4) || (k_cache && !aligned(k_cache, 16)) ||
+        (v_cache && !aligned(v_cache, 16)))
+        return WQ_ERR_ALIGN;
+    const int64_t qo_bytes = static_cast<int64_t>(num_q_heads) * head_dim * 4;
+    if (overlaps(out, qo_bytes, q, qo_bytes) || overlaps(out, qo_bytes, k_cache, cache_bytes) ||
+        overlaps(out, qo_bytes, v_cache, cache_bytes))
+        return WQ_ERR_ALIAS;
+    return status_of(wq::launch_decode_attention(q, k_cache, v_cache, kv_fmt, out, cache_len, head_dim, num_q_heads,
+                                                 num_kv_heads, scale, static_cast<hipStream_t>(stream)));
 }
 
 int wq_pack_f16(const float *w, uint16_t *out, int64_t count, void *stream) {

@@ -208,6 +208,36 @@ int wq_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt
 int wq_topk(const float *logits, int64_t n, int topk, float *vals, uint32_t *ids, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Decode attention for one query token over a KV cache (grouped-query,
+ * split over the cache).
+ *
+ * out[h, d] = sum_t p_t v[t, kvh * head_dim + d] with p = softmax over
+ * t < cache_len of s_t = scale * sum_d q[h, d] k[t, kvh * head_dim + d] and
+ * kvh = h / (num_q_heads / num_kv_heads).  Passage: kernels decode_attention,
+ * decode_attention_flash_partial and decode_attention_flash_reduce (online
+ * softmax over the cache, per-partition (m, l, acc) partials merged by the
+ * same recurrence), lattice-inference 0.1.2 metal_qwen35.rs;
+ * dispatch_decode_attention (direct or partitioned, f32 or f16 cache) and
+ * validate_flash_decode_shape (GQA group 1..8, q_dim = num_q_heads *
+ * head_dim, kv_dim = num_kv_heads * head_dim), lattice-inference 0.9.0
+ * dispatch.rs.
+ *
+ * Layouts (device pointers, row-major): q f32 [num_q_heads, head_dim]; k_cache
+ * and v_cache [cache_len, num_kv_heads * head_dim], f32 (kv_fmt WQ_KV_F32) or
+ * binary16 bit patterns (WQ_KV_F16), token-major as the pages' flat
+ * [max_cache_len * kv_dim] caches, 16-byte aligned; out f32 [num_q_heads,
+ * head_dim], 4-byte aligned, not overlapping the inputs.  head_dim is 64, 128
+ * or 256 (the pages support 256), num_q_heads a multiple of num_kv_heads with
+ * a group of at most WQ_ATTN_MAX_GROUP, else WQ_ERR_SHAPE; an unknown kv_fmt
+ * is WQ_ERR_FORMAT.  cache_len == 0 writes zeros (the reduce pass's empty
+ * result).  Accumulation in f32; scratch for the partitions' partial states
+ * ((num_q_heads * (head_dim + 2) * 4 bytes per partition) as above. */
+#define WQ_ATTN_MAX_GROUP 8
+enum { WQ_KV_F32 = 0, WQ_KV_F16 = 1 };
+int wq_decode_attention(const float *q, const void *k_cache, const void *v_cache, float *out, int64_t cache_len,
+                        int head_dim, int num_q_heads, int num_kv_heads, int kv_fmt, float scale, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Weight preparation (done once, at load time).
  * wq_pack_f16: out[i] = binary16 bits of w[i], round to nearest even, with
  *   subnormals; overflow gives infinity.  Passage: f32_to_f16 and

@@ -28,8 +28,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("wq_gemv_f16", "wq_gemv_q8_0", "wq_gemv_q4_0", "wq_gemm_f16", "wq_gemm_q8_0",
-                 "wq_gemm_q4_0", "wq_matmul", "wq_matmul_ex", "wq_lm_head_topk", "wq_topk", "wq_pack_f16",
-                 "wq_quantize_q8_0"):
+                 "wq_gemm_q4_0", "wq_matmul", "wq_matmul_ex", "wq_lm_head_topk", "wq_topk",
+                 "wq_decode_attention", "wq_pack_f16", "wq_quantize_q8_0"):
         assert want in names
 
 
@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process():
 
 
 def test_abi_and_status_strings():
-    assert wq.wq_abi_version() == 103
+    assert wq.wq_abi_version() == 104
     for st in range(0, 11):
         assert wq.status_str(st)
     assert wq.status_str(99) == "unknown status"
@@ -160,6 +160,30 @@ def test_topk_validation():
     assert LM(A, B, 100, 64, wq.WQ_FMT_F16, 8, A + 64, I, None) == wq.WQ_ERR_ALIAS   # vals inside a
     assert LM(A, B, 100, 64, wq.WQ_FMT_F16, 8, V, B + 1000, None) == wq.WQ_ERR_ALIAS  # ids inside b
     assert TK(A, 100, 8, A + 396, I, None) == wq.WQ_ERR_ALIAS                       # vals inside logits
+
+
+def test_decode_attention_validation():
+    AT = L.wq_decode_attention
+    Q, K, V, O = 0x100000, 0x2000000, 0x4000000, 0x6000000
+
+    def call(q=Q, k=K, v=V, o=O, L_=4096, D=256, hq=8, hkv=2, fmt=wq.WQ_KV_F32):
+        return AT(q, k, v, o, L_, D, hq, hkv, fmt, 0.0625, None)
+    assert call(fmt=2) == wq.WQ_ERR_FORMAT
+    assert call(fmt=-1) == wq.WQ_ERR_FORMAT
+    for bad in (dict(L_=-1), dict(D=96), dict(D=512), dict(D=0), dict(hq=0), dict(hkv=0), dict(hq=6, hkv=4),
+                dict(hq=18, hkv=2), dict(hq=2, hkv=4), dict(L_=1 << 60)):
+        assert call(**bad) == wq.WQ_ERR_SHAPE, bad
+    assert call(q=None) == wq.WQ_ERR_NULL
+    assert call(o=None) == wq.WQ_ERR_NULL
+    assert call(k=None) == wq.WQ_ERR_NULL
+    assert call(v=None) == wq.WQ_ERR_NULL
+    assert call(q=Q + 2) == wq.WQ_ERR_ALIGN
+    assert call(o=O + 1) == wq.WQ_ERR_ALIGN
+    assert call(k=K + 8) == wq.WQ_ERR_ALIGN      # caches need 16 bytes
+    assert call(v=V + 4, fmt=wq.WQ_KV_F16) == wq.WQ_ERR_ALIGN
+    assert call(o=Q + 64) == wq.WQ_ERR_ALIAS
+    assert call(o=K + 4096 * 512 * 4 - 16) == wq.WQ_ERR_ALIAS   # inside the f32 K cache
+    assert call(o=V + 100 * 16) == wq.WQ_ERR_ALIAS
 
 
 def test_routing_rule():

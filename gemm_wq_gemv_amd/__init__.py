@@ -80,6 +80,7 @@ def _load() -> ctypes.CDLL:
         "wq_lm_head_topk": (I, [P, P, I64, I64, I, I, P, P, P]),
         "wq_topk": (I, [P, I64, I, P, P, P]),
         "wq_decode_attention": (I, [P, P, P, P, I64, I, I, I, I, ctypes.c_float, P]),
+        "wq_set_attn_partition": (I, [I64]),
         "wq_pack_f16": (I, [P, P, I64, P]),
         "wq_quantize_q8_0": (I, [P, P, I64, P]),
         "wq_route_for": (I, [I64, I64, I64, I]),
@@ -263,6 +264,11 @@ def wq_decode_attention(q, k_cache, v_cache, out, cache_len: int, head_dim: int,
     _check(_lib.wq_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), cache_len, head_dim,
                                     num_q_heads, num_kv_heads, kv_fmt, scale, _stream(stream, out)),
            "wq_decode_attention")
+
+
+def wq_set_attn_partition(tokens: int) -> None:
+    """Force the attention partition size (tokens); 0 = automatic."""
+    _check(_lib.wq_set_attn_partition(tokens), "wq_set_attn_partition")
 
 
 def wq_pack_f16(w, out, count: int, stream=None) -> None:

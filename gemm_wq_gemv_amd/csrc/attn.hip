@@ -27,18 +27,20 @@
 //  * the workgroup's 4 waves take the partition's tiles round-robin and merge
 //    their (m, l, acc) states through LDS at the end; with more than one
 //    partition the states go to scratch and attn_reduce merges them (16 waves
-//    per workgroup, 8 partitions loaded at a time per wave).
+//    per workgroup, 16 partitions loaded at a time per wave).
 // Partitions are sized so that about two workgroups per CU exist (>= 64
 // tokens each); one partition writes the output directly.
 #include "wq_internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 namespace wq {
 namespace {
 
 constexpr int kAttnWaves = 4;
+std::atomic<int64_t> g_attn_ptok{0};  // forced partition size in tokens; 0 = automatic
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial(const float *
 }
 
 constexpr int kReduceWaves = 16;
-constexpr int kReduceLoads = 8;  // partitions a wave loads before it merges them
+constexpr int kReduceLoads = 16;  // partitions a wave loads before it merges them
 
 // Workgroup (h, chunk) = (blockIdx.x / (D / 64), blockIdx.x % (D / 64)):
 // lane = dimension chunk * 64 + lane of query head h; wave w merges
@@ -283,15 +285,21 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void attn_reduce(const float 
                 mp[u] = base[0], lp[u] = base[1], ap[u] = base[2 + d];
             }
         }
+        // New maximum first, then independent weights (no serial exp chain).
+        float mn = m;
+#pragma unroll
+        for (int u = 0; u < U; ++u) mn = fmaxf(mn, mp[u]);
+        if (mn == -__builtin_huge_valf()) continue;  // nothing but empty partitions so far
+        const float ca = m == -__builtin_huge_valf() ? 0.f : expf(m - mn);
+        l *= ca;
+        a *= ca;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float mn = fmaxf(m, mp[u]);
-            const float ca = m == -__builtin_huge_valf() ? 0.f : expf(m - mn);
             const float cp = mp[u] == -__builtin_huge_valf() ? 0.f : expf(mp[u] - mn);
-            l = ca * l + cp * lp[u];
-            a = ca * a + cp * ap[u];
-            m = mn;
+            l = fmaf(cp, lp[u], l);
+            a = fmaf(cp, ap[u], a);
         }
+        m = mn;
     }
     if (lane == 0) sm[w] = m, sl[w] = l;
     sa[w][lane] = a;
@@ -313,10 +321,13 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void attn_reduce(const float 
 template <int D, int GP, int KVF>
 hipError_t run_attn(const float *q, const void *k, const void *v, float *out, int64_t len, int hq, int hkv,
                     float scale, hipStream_t s, int cus) {
-    // About two workgroups per CU, at least 64 tokens per partition.
+    // About two workgroups per CU, at least 64 tokens per partition (or the
+    // size set through set_attn_partition_override).
     const int64_t want = std::max<int64_t>(1, (2LL * cus + hkv - 1) / hkv);
     int64_t ptok = (len + want - 1) / want;
     ptok = std::max<int64_t>(64, (ptok + 63) / 64 * 64);
+    const int64_t forced = g_attn_ptok.load(std::memory_order_relaxed);
+    if (forced > 0) ptok = forced;
     const int64_t parts = (len + ptok - 1) / ptok;
     if (parts * hkv > 0x7fffffffLL || parts > 0x7fffffffLL) return hipErrorInvalidValue;
     const int g_real = hq / hkv;
@@ -355,6 +366,8 @@ hipError_t run_group(const float *q, const void *k, const void *v, float *out, i
 }
 
 }  // namespace
+
+void set_attn_partition_override(int64_t tokens) { g_attn_ptok.store(tokens, std::memory_order_relaxed); }
 
 hipError_t launch_decode_attention(const float *q, const void *k, const void *v, int kvf, float *out, int64_t len,
                                    int d, int hq, int hkv, float scale, hipStream_t s) {

@@ -312,6 +312,8 @@ hipError_t launch_topk_merge(const TopkCand *cand, int64_t lists, const float *l
 // in 1..8.  Split over the cache in partitions, then a merge pass.
 hipError_t launch_decode_attention(const float *q, const void *k, const void *v, int kvf, float *out, int64_t len,
                                    int d, int hq, int hkv, float scale, hipStream_t s);
+// Partition size (tokens) every later attention call uses; 0 = automatic.
+void set_attn_partition_override(int64_t tokens);
 
 // n = output columns; with kEpiGlu the weights have 2n rows.
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,

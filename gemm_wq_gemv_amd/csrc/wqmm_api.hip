@@ -447,6 +447,12 @@ int wq_set_gemm_plan(int bm, int bn, int splits) {
     return wq::set_gemm_plan_override(bm, bn, splits) ? WQ_OK : WQ_ERR_SHAPE;
 }
 
+int wq_set_attn_partition(int64_t tokens) {
+    if (tokens < 0) return WQ_ERR_SHAPE;
+    wq::set_attn_partition_override(tokens);
+    return WQ_OK;
+}
+
 int wq_set_forced_route(int route) {
     if (route != WQ_ROUTE_AUTO && !known_route(route)) return -WQ_ERR_ROUTE;
     return wq::g_forced_route.exchange(route);

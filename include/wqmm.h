@@ -237,6 +237,13 @@ enum { WQ_KV_F32 = 0, WQ_KV_F16 = 1 };
 int wq_decode_attention(const float *q, const void *k_cache, const void *v_cache, float *out, int64_t cache_len,
                         int head_dim, int num_q_heads, int num_kv_heads, int kv_fmt, float scale, void *stream);
 
+/* Test/tuning hook (host only): every later wq_decode_attention call in the
+ * process splits the cache into partitions of `tokens` tokens (0 restores
+ * the automatic size, about two workgroups per compute unit).  Returns
+ * WQ_ERR_SHAPE for tokens < 0.  Not thread-safe with respect to concurrent
+ * attention calls that expect the automatic size. */
+int wq_set_attn_partition(int64_t tokens);
+
 /* ---------------------------------------------------------------------- */
 /* Weight preparation (done once, at load time).
  * wq_pack_f16: out[i] = binary16 bits of w[i], round to nearest even, with

@@ -184,6 +184,8 @@ def test_decode_attention_validation():
     assert call(o=Q + 64) == wq.WQ_ERR_ALIAS
     assert call(o=K + 4096 * 512 * 4 - 16) == wq.WQ_ERR_ALIAS   # inside the f32 K cache
     assert call(o=V + 100 * 16) == wq.WQ_ERR_ALIAS
+    assert L.wq_set_attn_partition(-1) == wq.WQ_ERR_SHAPE
+    assert L.wq_set_attn_partition(0) == wq.WQ_OK
 
 
 def test_routing_rule():

@@ -109,3 +109,17 @@ def test_deterministic_and_stream():
     with torch.cuda.stream(s):
         c = run(q, k, v, L, D, Hq, Hkv, F16, 0.0625, stream=s)
     assert np.array_equal(a, b) and np.array_equal(a, c)
+
+
+def test_forced_partition_sizes():
+    """The merge pass over many partitions (ptok 64 at 20K tokens: 313 partitions,
+    more than one load round per wave), partitions that end inside a tile
+    (ptok 100, 8 and 1), and one partition for a long cache."""
+    try:
+        for ptok, L in ((64, 20000), (100, 3001), (8, 1000), (1, 300), (1 << 20, 50000)):
+            wq.wq_set_attn_partition(ptok)
+            say(f"forced partition {ptok} tokens, L={L}")
+            check(L, 256, 8, 2, F32, seed=ptok)
+            check(L, 128, 4, 4, F16, seed=ptok + 1)
+    finally:
+        wq.wq_set_attn_partition(0)

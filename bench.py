@@ -314,10 +314,33 @@ def cpu_baseline(host_weights, seed, budget_s=12.0):
             t_total += time.perf_counter() - t0
             bytes_done += 2 * n * k
         passes += 1
+    # The other hot-path rows, one oracle call each (the same shapes as their GPU tables).
+    rows = {}
+    a = wqgen.activations(1, 2048, seed)
+    gu = enc[(6144, 2048)]
+    t0 = time.perf_counter()
+    oracle.matmul_epilogue(a, gu, oracle.FMT_F16, 1, 3072, 2048, oracle.EPI_SWIGLU, threads=threads)
+    dt = time.perf_counter() - t0
+    rows["swiglu_gate_up_m1_6144x2048"] = {"ms": round(dt * 1e3, 2), "weight_GB/s": round(2 * 6144 * 2048 / dt / 1e9, 3)}
+    lm = enc[(151936, 2048)]
+    t0 = time.perf_counter()
+    oracle.lm_head_topk(a, lm, oracle.FMT_F16, 151936, 2048, 50, threads=threads)
+    dt = time.perf_counter() - t0
+    rows["lm_head_topk50_151936x2048"] = {"ms": round(dt * 1e3, 2), "weight_GB/s": round(lm.nbytes / dt / 1e9, 3)}
+    L, D, hq, hkv = 4096, 256, 8, 2
+    q = wqgen.normal((hq, D), seed=seed, stream=11)
+    kc = wqgen.normal((L, hkv * D), seed=seed, stream=12)
+    vc = wqgen.normal((L, hkv * D), seed=seed, stream=13)
+    t0 = time.perf_counter()
+    oracle.decode_attention(q, kc, vc, oracle.KV_F32, L, D, hq, hkv, 0.0625)
+    dt = time.perf_counter() - t0
+    rows["decode_attention_f32_L4096"] = {"ms": round(dt * 1e3, 2), "kv_GB/s": round(2 * kc.nbytes / dt / 1e9, 3),
+                                          "threads": 1}
     del np
     return {"value": round(bytes_done / t_total / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} full pass(es) of the f16 decode suite (4 GEMVs, M=1, {bytes_done // passes} "
-                      f"weight bytes per pass), f64 accumulation, {t_total:.1f} s"}
+                      f"weight bytes per pass), f64 accumulation, {t_total:.1f} s",
+            "other_rows": rows}
 
 
 def main():

@@ -43,6 +43,7 @@ METRIC = "decode GEMV weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA pea
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 ROTATE_BYTES = 1 << 30
+WARM_GPU_S = 0.05  # sustained GPU time before a timed burst
 DECODE = [("gate_up", 6144, 2048), ("down", 2048, 6144), ("o_proj", 2048, 2048), ("lm_head", 151936, 2048)]
 PREFILL = [(512, 6144, 2048), (512, 2048, 6144)]
 SWEEP_SHAPES = [(11008, 4096), (4096, 11008)]
@@ -131,40 +132,89 @@ class Suite:
                 ev[1].record()
 
 
+_SLEEP_CYCLES_PER_S = None
+
+
+def hold_stream(torch, seconds):
+    """Enqueue a spin kernel that keeps the stream busy for about `seconds`
+    (torch.cuda._sleep counts GPU clock cycles; the rate is measured once)."""
+    global _SLEEP_CYCLES_PER_S
+    if _SLEEP_CYCLES_PER_S is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(100_000)
+        a.record()
+        torch.cuda._sleep(4_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_S = 4_000_000 / max(a.elapsed_time(b) / 1e3, 1e-4)
+    torch.cuda._sleep(int(min(seconds, 0.5) * _SLEEP_CYCLES_PER_S))
+
+
 def time_suite(torch, wq, suite, steps, warmup, bracket):
-    """Times `steps` suite passes.  HIP events bracket the launches of the items
-    listed in `bracket` only (events between kernels cost a few microseconds of
-    GPU time each, so the other launches run back to back).  Returns (timed
-    seconds, host wall seconds, {item: mean launch seconds})."""
+    """Times `steps` suite passes back to back on the GPU.  HIP events bracket
+    the launches of the items listed in `bracket` only (events between kernels
+    cost a few microseconds of GPU time each, so the other launches run back
+    to back).  The Python binding validates its arguments on every call (tens
+    of microseconds of host time per step), so a spin kernel sized from the
+    warmup's host rate holds the stream while all timed steps are enqueued:
+    the GPU then runs them without waiting for the host, as a compiled decode
+    loop or a captured graph would.  Returns (timed seconds, host wall seconds
+    including the hold, {item: mean launch seconds})."""
+    t0 = time.perf_counter()
     for i in range(warmup):
         suite.step(wq, i)
+    host_step = (time.perf_counter() - t0) / max(warmup, 1)
     torch.cuda.synchronize()
     ev = {j: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
           for j in bracket}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    hold.record()
+    hold_stream(torch, 1.5 * host_step * steps * (1 + len(bracket)) + 1e-3)
     start.record()
+    t1 = time.perf_counter()
     for i in range(steps):
         suite.step(wq, warmup + i, {j: e[i] for j, e in ev.items()})
+    host = time.perf_counter() - t1
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if host > 0.9 * hold.elapsed_time(start) / 1e3:
+        log(f"warning: host enqueue ({host * 1e3:.2f} ms) outlasted the stream hold; GPU time may include gaps")
     total = start.elapsed_time(end) / 1e3
     per = {j: sum(a.elapsed_time(b) for a, b in e) / steps / 1e3 for j, e in ev.items()}
     return total, wall, per
 
 
 def time_launches(torch, fn, iters, warmup):
-    """GPU seconds per launch of fn.  A spin kernel (a few ms) holds the stream
-    while the host enqueues the timed launches, so that per-call host overhead
-    (Python binding and launch, about 10 us) does not leak into the GPU time of
-    kernels shorter than that."""
+    """GPU seconds per launch of fn, at the clock the chip holds under
+    sustained load.  The compute clock ramps up over about 20 ms of load and
+    drops again after a few milliseconds of idle (the 512x6144x2048 f16 GEMM
+    takes about 136 us just after idle and 119 us sustained; HBM-bound kernels
+    do not move), so the warmup is W launches and then as many more as make
+    about WARM_GPU_S of GPU time.  A spin kernel then holds the stream while
+    the host enqueues the timed launches, so that per-call host overhead
+    (Python binding and launch, about 10 us) does not leak into the GPU time
+    of kernels shorter than that; it is sized from the warmup's host rate,
+    so the GPU idles no longer than the enqueue takes."""
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    w0.record()
     for i in range(warmup):
         fn(i)
+    w1.record()
+    host_call = (time.perf_counter() - t0) / max(warmup, 1)
     torch.cuda.synchronize()
+    per = max(w0.elapsed_time(w1) / 1e3 / max(warmup, 1), 1e-6)
+    extra = min(math.ceil(WARM_GPU_S / per), 20000)
+    t0 = time.perf_counter()
+    for i in range(extra):
+        fn(i)
+    backlog = max(0.0, extra * per - (time.perf_counter() - t0))  # GPU work still queued, at most
     e0, s, e = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     e0.record()
-    torch.cuda._sleep(10_000_000)
+    hold_stream(torch, 2e-4 + 1.5 * host_call * iters)
     s.record()
     t0 = time.perf_counter()
     for i in range(iters):
@@ -172,7 +222,7 @@ def time_launches(torch, fn, iters, warmup):
     host = time.perf_counter() - t0
     e.record()
     torch.cuda.synchronize()
-    if host > 0.9 * e0.elapsed_time(s) / 1e3:
+    if host > 0.9 * (e0.elapsed_time(s) / 1e3 + backlog):
         log(f"warning: host enqueue ({host * 1e3:.2f} ms) outlasted the stream hold; GPU time may include gaps")
     return s.elapsed_time(e) / 1e3 / iters
 
@@ -374,9 +424,10 @@ def main():
         s16 = Suite(wq, wqgen, torch, F16, args.seed, host_weights)
         log("f16 decode suite: timing")
         lm = [i for i, it in enumerate(s16.items) if it["name"] == "lm_head"][0]
-        total, wall, per = time_suite(torch, wq, s16, args.steps, args.warmup, bracket=[lm])
+        # The timed steps carry no event markers (each costs GPU time between
+        # kernels); per-launch event pairs are taken in a separate pass below.
+        total, wall, _ = time_suite(torch, wq, s16, args.steps, args.warmup, bracket=[])
         lm_bytes = s16.items[lm]["bytes"]
-        lm_pairs_s = per[lm]
         # Average LM-head launch duration: a burst of back-to-back launches of
         # the same kernel on the same stream (the suite's rotated weight copies),
         # bracketed by one event pair while a spin kernel holds the stream, so
@@ -386,6 +437,10 @@ def main():
                                                            it["k"], F16), max(20, args.steps), 3)
         achieved = lm_bytes / lm_s / 1e9
         value = s16.bytes_per_step * args.steps / total / 1e9
+        # Per-kernel times in a separate, untimed pass with every launch bracketed
+        # (includes the events' own cost, about 3 us for the small kernels).
+        _, _, per_all = time_suite(torch, wq, s16, max(10, args.steps // 2), 2, bracket=range(len(s16.items)))
+        lm_pairs_s = per_all[lm]
         result = {
             "metric": METRIC,
             "value": round(value, 2),
@@ -409,7 +464,7 @@ def main():
                 "wall_s": round(wall, 4),
             },
             "roofline": {
-                "kernel": "gemv_f16_vec (LM head, N=151936, K=2048)",
+                "kernel": "gemv_f16_ksplit (LM head, N=151936, K=2048)",
                 "bound": "hbm",
                 "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS,
@@ -421,9 +476,6 @@ def main():
                 "algorithmic_bytes_per_launch": lm_bytes,
             },
         }
-        # Per-kernel times in a separate, untimed pass with every launch bracketed
-        # (includes the events' own cost, about 3 us for the small kernels).
-        _, _, per_all = time_suite(torch, wq, s16, max(10, args.steps // 2), 2, bracket=range(len(s16.items)))
         secondary["f16_decode_per_kernel_event_timed"] = {
             it["name"]: {"us": round(per_all[j] * 1e6, 3), "GB/s": round(it["bytes"] / per_all[j] / 1e9, 1)}
             for j, it in enumerate(s16.items)}
@@ -436,14 +488,17 @@ def main():
         log(f"{key} decode suite")
         sq = Suite(wq, wqgen, torch, fmt, args.seed, host_weights)
         lmq = [i for i, it in enumerate(sq.items) if it["name"] == "lm_head"][0]
-        total, _, per = time_suite(torch, wq, sq, args.steps, args.warmup, bracket=[lmq])
+        total, _, _ = time_suite(torch, wq, sq, args.steps, args.warmup, bracket=[])
         _, _, per_all = time_suite(torch, wq, sq, max(10, args.steps // 2), 2, bracket=range(len(sq.items)))
+        it = sq.items[lmq]
+        lmq_s = time_launches(torch, lambda i: wq.wq_matmul(it["a"], it["bs"][i % len(it["bs"])], it["c"], 1, it["n"],
+                                                            it["k"], fmt), max(20, args.steps), 3)
         secondary[f"{key}_decode_suite"] = {
             "GB/s": round(sq.bytes_per_step * args.steps / total / 1e9, 2),
             "frac_hbm": round(sq.bytes_per_step * args.steps / total / 1e9 / HBM_PEAK_GBS, 4),
             "ms_per_step": round(total / args.steps * 1e3, 5),
-            "lm_head_us": round(per[lmq] * 1e6, 3),
-            "lm_head_GB/s": round(sq.items[lmq]["bytes"] / per[lmq] / 1e9, 1),
+            "lm_head_us": round(lmq_s * 1e6, 3),
+            "lm_head_GB/s": round(it["bytes"] / lmq_s / 1e9, 1),
             "per_kernel_event_timed": {it["name"]: {"us": round(per_all[j] * 1e6, 3),
                                                     "GB/s": round(it["bytes"] / per_all[j] / 1e9, 1)}
                                        for j, it in enumerate(sq.items)},
@@ -455,15 +510,18 @@ def main():
         log("f16 prefill GEMM, M=512")
         out = {}
         for m, n, k in PREFILL:
-            w = wqgen.weights(n, k, args.seed)
-            b = wq.pack_f16(torch.from_numpy(w).cuda())
+            b0 = wq.pack_f16(torch.from_numpy(wqgen.weights(n, k, args.seed)).cuda())
+            nbytes = wq.weight_bytes(n, k, F16)
+            bs = [b0] + [b0.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / nbytes)) - 1)]
             a = torch.from_numpy(wqgen.activations(m, k, args.seed)).cuda()
             c = torch.empty((m, n), device="cuda")
-            t = time_launches(torch, lambda i: wq.wq_matmul(a, b, c, m, n, k, F16), max(10, args.steps // 2),
-                              args.warmup)
+            t = time_launches(torch, lambda i: wq.wq_matmul(a, bs[i % len(bs)], c, m, n, k, F16),
+                              max(10, args.steps // 2), args.warmup)
             tf = 2.0 * m * n * k / t / 1e12
             out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(tf, 2),
                                    "frac_mfma_fp32": round(tf / FP32_MFMA_PEAK_TFLOPS, 4)}
+            del bs, b0
+            torch.cuda.empty_cache()
         secondary["f16_prefill_m512"] = out
 
     if not args.no_secondary and only in (None, "sweep"):

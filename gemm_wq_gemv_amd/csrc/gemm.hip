@@ -383,22 +383,32 @@ __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, co
 // C[r, j] (r < m, j < no) from the split partial sums partial[s][r][.] (row
 // length nw), summed in split order (deterministic): plain, added to C
 // (residual), or silu(gate) * up with gate at column j and up at no + j (GLU,
-// nw = 2 * no).  With splits == 1 it is the GLU epilogue alone.
+// nw = 2 * no).  With splits == 1 it is the GLU epilogue alone.  A thread
+// takes W adjacent columns of one row (W = 4: 16-byte loads and stores, when
+// no is a multiple of 4 and C is 16-byte aligned); blockIdx.y strides rows.
+template <int W>
 __global__ __launch_bounds__(256) void reduce_splits(const float *__restrict__ partial, float *__restrict__ c,
                                                      int64_t m, int64_t no, int64_t nw, int splits, int epi) {
-    const int64_t count = m * no, plane = m * nw;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < count; e += stride) {
-        const int64_t r = e / no, j = e - r * no;
-        const int64_t base = r * nw + j;
-        float v = partial[base];
-        for (int s = 1; s < splits; ++s) v += partial[static_cast<int64_t>(s) * plane + base];
+    typedef float vec __attribute__((ext_vector_type(W)));
+    const int64_t j = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * W;
+    if (j >= no) return;
+    const int64_t plane = m * nw;
+    for (int64_t r = blockIdx.y; r < m; r += gridDim.y) {
+        const float *p = partial + r * nw + j;
+        vec v = *reinterpret_cast<const vec *>(p);
+#pragma unroll 4
+        for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const vec *>(p + s * plane);
+        vec *out = reinterpret_cast<vec *>(c + r * no + j);
         if (epi == kEpiGlu) {
-            float u = partial[base + no];
-            for (int s = 1; s < splits; ++s) u += partial[static_cast<int64_t>(s) * plane + base + no];
-            c[e] = silu(v) * u;
+            vec u = *reinterpret_cast<const vec *>(p + no);
+#pragma unroll 4
+            for (int s = 1; s < splits; ++s) u += *reinterpret_cast<const vec *>(p + s * plane + no);
+            vec o;
+#pragma unroll
+            for (int i = 0; i < W; ++i) o[i] = silu(v[i]) * u[i];
+            *out = o;
         } else {
-            c[e] = epi == kEpiResidual ? c[e] + v : v;
+            *out = epi == kEpiResidual ? *out + v : v;
         }
     }
 }
@@ -556,8 +566,19 @@ hipError_t dispatch(const float *a, const void *b, float *c, int64_t m, int64_t 
 
 hipError_t launch_reduce_splits(const float *partial, float *c, int64_t m, int64_t no, int64_t nw, int splits,
                                 int epi, hipStream_t s) {
-    const int64_t grid = std::min<int64_t>((m * no + 255) / 256, 65536);
-    hipLaunchKernelGGL(reduce_splits, dim3(grid), dim3(256), 0, s, partial, c, m, no, nw, splits, epi);
+    if (m <= 0 || no <= 0) return hipSuccess;
+    const bool vec = no % 4 == 0 && reinterpret_cast<uintptr_t>(c) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(partial) % 16 == 0;
+    const int w = vec ? 4 : 1;
+    const int64_t gx = (no + 256 * w - 1) / (256 * w);
+    if (gx > 0x7fffffffLL) return hipErrorInvalidValue;
+    // Enough rows per launch for about 2048 workgroups; the rest are strided.
+    const int64_t gy = std::max<int64_t>(1, std::min<int64_t>({m, 65535, (2048 + gx - 1) / gx}));
+    const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
+    if (vec)
+        hipLaunchKernelGGL(reduce_splits<4>, grid, dim3(256), 0, s, partial, c, m, no, nw, splits, epi);
+    else
+        hipLaunchKernelGGL(reduce_splits<1>, grid, dim3(256), 0, s, partial, c, m, no, nw, splits, epi);
     return hipGetLastError();
 }
 

@@ -10,14 +10,17 @@
 // for f16, two rows per threadgroup for Q8_0).  On CDNA4 the work is bound by
 // HBM bandwidth, so the design here is about the byte stream:
 //
-//  * A wave (64 lanes) owns whole weight rows.  The activation vector is held
-//    in VGPRs for the wave's lifetime (each lane keeps the slice of `a` that
-//    matches the weight bytes it reads), so `a` is read from L2 once per wave
-//    instead of once per row.
-//  * f16: each lane reads 16-byte chunks (8 weights) of R rows at once with
-//    128-bit non-temporal loads; a row of K = 2048 is four such loads per lane,
-//    fully coalesced.  f16 -> f32 widening happens in registers.
-//  * Q8_0: a 34-byte block is only 2-byte aligned, so the wave first copies S
+//  * f16: a workgroup of KW waves owns a block of 4 rows and splits K among
+//    its waves (KW = K / 512 for K <= 8192): each lane reads one 16-byte
+//    chunk (8 weights) of each of the 4 rows with 128-bit non-temporal loads,
+//    fully coalesced, plus the matching 8 activations; f16 -> f32 widening
+//    happens in registers; the waves' partial sums meet in LDS.  One block
+//    per workgroup: the hardware dispatcher starts a fresh workgroup as each
+//    one retires, which streams HBM faster on MI355X than persistent waves
+//    walking the rows (85 us against 93-97 us at N = 151936, K = 2048).
+//  * Q8_0: a wave owns whole rows and holds the activation vector in VGPRs
+//    (each lane keeps the slice of `a` that matches the blocks it decodes).
+//    A 34-byte block is only 2-byte aligned, so the wave first copies S
 //    whole rows (a contiguous, 16-byte aligned byte range when K % 256 == 0)
 //    into its LDS slice with coalesced 128-bit loads, then each lane decodes
 //    whole blocks from LDS (scale, 32 int8 codes, read with unaligned 16-byte
@@ -29,15 +32,15 @@
 //    The decode of a pass is branch-free so the rows' dependency
 //    chains overlap, and the rows of a pass are reduced together by one
 //    butterfly (each cross-lane step halves the values a lane carries).
+//    The Q8_0 / Q4_0 grid is persistent: sized to fill the chip once, every
+//    wave walks passes with a stride, balanced so all waves do equal work.
 //  * Reductions: DPP within 16-lane rows, lane-xor across rows (64 lanes).
-//  * Persistent waves: the grid is sized to fill the chip once and every wave
-//    walks row groups with a stride, balanced so all waves do equal work.
-//  * SwiGLU: a wave's row group (f16) or pass (Q8_0, Q4_0) holds gate rows
-//    and the up rows of the same outputs, so after the reduction the gate and
-//    up sums sit in two lanes of the same wave; one lane shuffle brings them
+//  * SwiGLU: an f16 row block or a Q8_0 / Q4_0 pass holds gate rows and the
+//    up rows of the same outputs, so after the reduction the gate and up
+//    sums sit in two lanes of the same wave; one lane shuffle brings them
 //    together and silu(g) * u is stored directly (no [2n] intermediate, no
-//    second kernel).  Shapes those kernels cannot pair (K > 8192, unaligned
-//    or odd K) take one GEMV over all 2n rows into scratch and one
+//    second kernel).  Shapes those kernels cannot pair (unaligned or odd K,
+//    very long K) take one GEMV over all 2n rows into scratch and one
 //    element-wise pass.
 #include "wq_internal.h"
 
@@ -66,29 +69,52 @@ __device__ __forceinline__ float dot8_f16(uint4 w, float4 lo, float4 hi, float a
     return acc;
 }
 
-// T 16-byte chunk slots per lane cover K = 512*T weights; R rows per step.
-// FULL: K == 512*T exactly, so no slot needs a bounds check.
-// GLU: n is the output count and b has 2n rows; a group is R/2 gate rows and
-// the R/2 up rows of the same outputs.  Otherwise a group is R rows of b.
-// Requires K % 8 == 0 and 16-byte aligned a and b.
-template <int T, int R, bool FULL, int MODE>
-__global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
-                                                    const uint16_t *__restrict__ b,
-                                                    float *__restrict__ c, int64_t n, int64_t k,
-                                                    int64_t groups, int resid) {
+// K-split f16 GEMV (store and GLU modes): workgroup g (KW waves, KW =
+// blockDim.x / 64) owns the g-th block of RB consecutive weight rows (GLU:
+// RB/2 gate rows and the up rows of the same outputs) and wave w reads the
+// w-th K slice of each row, T2 16-byte chunks per lane (chunk (w*T2 + t)*64 +
+// lane of the row), against the matching activations.  Every wave has RB*T2
+// loads in flight at once and the activations are read once per workgroup;
+// the RB partial sums of a wave are reduced by one butterfly, then summed
+// over the waves in wave order through LDS.  One block per workgroup and no
+// grid stride: fresh workgroups from the hardware dispatcher keep every CU
+// supplied until the last block (measured on MI355X, any per-workgroup loop
+// over blocks, prefetched or not, costs 5-12 % at N = 151936).
+// FULL: K == KW*T2*512 exactly.  Requires K % 8 == 0, 16-byte aligned a and b.
+constexpr int kSplitMaxWaves = 16;
+
+template <int T2, int RB, bool FULL, int MODE>
+__global__ __launch_bounds__(kSplitMaxWaves * kWave) void gemv_f16_ksplit(const float *__restrict__ a,
+                                                                          const uint16_t *__restrict__ b,
+                                                                          float *__restrict__ c, int64_t n,
+                                                                          int64_t k, int resid) {
     constexpr bool GLU = MODE == kModeGlu;
-    static_assert(!GLU || R % 2 == 0, "a GLU group pairs gate and up rows");
-    constexpr int OC = GLU ? R / 2 : R;  // outputs per group
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
-    const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * blockDim.x) / kWave;
+    static_assert(MODE == kModeStore || GLU, "store or GLU");
+    static_assert(!GLU || RB % 2 == 0, "a GLU block pairs gate and up rows");
+    constexpr int OC = GLU ? RB / 2 : RB;  // outputs per block
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int kw = blockDim.x / kWave;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * OC;  // first output of the block
     const int nch = static_cast<int>(k >> 3);
 
-    float4 alo[T], ahi[T];
+    uint4 wv[RB][T2];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        // Rows past the end are read clamped; their sums are never stored.
+        const int64_t oc = min<int64_t>(r0 + r % OC, n - 1);
+        const int64_t row = GLU && r >= OC ? n + oc : oc;
+        const uint4 *brow = reinterpret_cast<const uint4 *>(b + row * k);
+#pragma unroll
+        for (int t = 0; t < T2; ++t) {
+            const int idx = (w * T2 + t) * kWave + lane;
+            wv[r][t] = (FULL || idx < nch) ? load_nt16(brow + idx) : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    float4 alo[T2], ahi[T2];
     const float4 *a4 = reinterpret_cast<const float4 *>(a);
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int idx = t * kWave + lane;
+    for (int t = 0; t < T2; ++t) {
+        const int idx = (w * T2 + t) * kWave + lane;
         if (FULL || idx < nch) {
             alo[t] = a4[2 * idx];
             ahi[t] = a4[2 * idx + 1];
@@ -97,49 +123,29 @@ __global__ __launch_bounds__(256) void gemv_f16_vec(const float *__restrict__ a,
             ahi[t] = alo[t];
         }
     }
-
-    WaveTopk top;
-    if constexpr (MODE == kModeTopk) top.init();
-    for (int64_t g = wave; g < groups; g += nwaves) {
-        const int64_t r0 = g * OC;  // first output of the group
-        uint4 w[R][T];
+    float acc[RB];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int64_t oc = r0 + r % OC;
-            const int64_t row = GLU && r >= OC ? n + oc : oc;
-            const uint4 *brow = reinterpret_cast<const uint4 *>(b + row * k);
+    for (int r = 0; r < RB; ++r) {
+        acc[r] = 0.f;
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int idx = t * kWave + lane;
-                if ((FULL || idx < nch) && oc < n)
-                    w[r][t] = load_nt16(brow + idx);
-                else
-                    w[r][t] = make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-        float acc[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            acc[r] = 0.f;
-#pragma unroll
-            for (int t = 0; t < T; ++t) acc[r] = dot8_f16(w[r][t], alo[t], ahi[t], acc[r]);
-        }
-        float mine = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float s = wave_sum(acc[r]);
-            if (lane == r) mine = s;
-        }
-        if constexpr (GLU) {
-            const float up = __shfl_down(mine, OC, kWave);  // lane r + OC holds the up sum
-            if (lane < OC && r0 + lane < n) c[r0 + lane] = silu(mine) * up;
-        } else if constexpr (MODE == kModeTopk) {
-            top.offer(resid, mine, static_cast<uint32_t>(r0 + lane), lane < R && r0 + lane < n);
-        } else {
-            if (lane < R && r0 + lane < n) c[r0 + lane] = resid ? c[r0 + lane] + mine : mine;
-        }
+        for (int t = 0; t < T2; ++t) acc[r] = dot8_f16(wv[r][t], alo[t], ahi[t], acc[r]);
     }
-    if constexpr (MODE == kModeTopk) top.store(reinterpret_cast<TopkCand *>(c) + wave * resid, resid);
+    // rows_sum leaves row j's sum in lanes j*(64/RB) ..; lane j (< RB) takes it.
+    float v = __shfl(rows_sum<RB, kWave>(acc, lane), (lane % RB) * (kWave / RB), kWave);
+    if (kw > 1) {
+        __shared__ float part[kSplitMaxWaves][RB];
+        if (lane < RB) part[w][lane] = v;
+        __syncthreads();
+        if (w != 0) return;
+        v = part[0][lane % RB];
+        for (int q = 1; q < kw; ++q) v += part[q][lane % RB];
+    }
+    if constexpr (GLU) {
+        const float up = __shfl_down(v, OC, kWave);  // lane j + OC holds the up sum of output j
+        if (lane < OC && r0 + lane < n) c[r0 + lane] = silu(v) * up;
+    } else {
+        if (lane < RB && r0 + lane < n) c[r0 + lane] = resid ? c[r0 + lane] + v : v;
+    }
 }
 
 // Any K, any 2-byte alignment of b: one wave per row, lanes stride over K.
@@ -481,25 +487,48 @@ hipError_t glu_two_pass(float *c, int64_t n, hipStream_t s, Gemv2n &&gemv2n) {
 
 // Launch helpers.  aux: the residual flag (kModeStore) or k (kModeTopk);
 // *lists (kModeTopk): the number of per-wave lists the launch writes.
-template <int T, int R, int MODE = kModeStore>
-hipError_t run_f16_vec(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k,
-                       hipStream_t s, int cus, int aux, int64_t *lists = nullptr) {
-    constexpr int OC = MODE == kModeGlu ? R / 2 : R;
-    const int64_t groups = (n + OC - 1) / OC;
-    const int64_t waves = balanced_workers(groups, static_cast<int64_t>(cus) * 16);
-    const int64_t blocks = (waves + 3) / 4;
-    const bool full = (k == 512LL * T);
-    if (lists) *lists = blocks * 4;
+
+// K-split launch: T = 16-byte chunk slots per lane for the whole row
+// (ceil(K / 512)); T2 of them per wave and KW = ceil(T / T2) waves; one
+// workgroup per row block.
+template <int T2, int RB, int MODE>
+hipError_t run_f16_ksplit(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
+                          int resid) {
+    constexpr int OC = MODE == kModeGlu ? RB / 2 : RB;
+    const int64_t T = (k / 8 + kWave - 1) / kWave;
+    const int kw = static_cast<int>((T + T2 - 1) / T2);
+    const int64_t blocks = (n + OC - 1) / OC;
+    if (kw < 1 || kw > kSplitMaxWaves || blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (blocks == 0) return hipSuccess;
+    const bool full = k == 512LL * T2 * kw;
     if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_f16_vec<T=%d,R=%d,full=%d,mode=%d> n=%lld k=%lld grid=%lld block=256\n", T,
-                R, full ? 1 : 0, MODE, (long long)n, (long long)k, (long long)blocks);
+        fprintf(stderr, "[wqmm] gemv_f16_ksplit<T2=%d,RB=%d,full=%d,mode=%d> n=%lld k=%lld grid=%lld block=%d\n",
+                T2, RB, full ? 1 : 0, MODE, (long long)n, (long long)k, (long long)blocks, kw * kWave);
     if (full)
-        hipLaunchKernelGGL((gemv_f16_vec<T, R, true, MODE>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups,
-                           aux);
+        hipLaunchKernelGGL((gemv_f16_ksplit<T2, RB, true, MODE>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kw * kWave), 0, s, a, b, c, n, k, resid);
     else
-        hipLaunchKernelGGL((gemv_f16_vec<T, R, false, MODE>), dim3(blocks), dim3(256), 0, s, a, b, c, n, k, groups,
-                           aux);
+        hipLaunchKernelGGL((gemv_f16_ksplit<T2, RB, false, MODE>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kw * kWave), 0, s, a, b, c, n, k, resid);
     return hipGetLastError();
+}
+
+// Shapes the K-split kernel takes: K % 8 == 0, 16-byte aligned a and b, and
+// K <= 32768 (at most 16 waves of at most four chunk slots per lane).
+inline bool f16_ksplit_ok(const float *a, const uint16_t *b, int64_t k) {
+    const int64_t T = (k / 8 + kWave - 1) / kWave;
+    return k % 8 == 0 && aligned16(a) && aligned16(b) && T >= 1 && T <= 4 * kSplitMaxWaves;
+}
+
+// Chunk slots per wave by K: one up to K = 8192, two up to 16384, four up to
+// 32768.  Requires f16_ksplit_ok.
+template <int MODE>
+hipError_t f16_ksplit(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
+                      int resid) {
+    const int64_t T = (k / 8 + kWave - 1) / kWave;
+    if (T <= kSplitMaxWaves) return run_f16_ksplit<1, 4, MODE>(a, b, c, n, k, s, resid);
+    if (T <= 2 * kSplitMaxWaves) return run_f16_ksplit<2, 4, MODE>(a, b, c, n, k, s, resid);
+    return run_f16_ksplit<4, 4, MODE>(a, b, c, n, k, s, resid);
 }
 
 template <int FMT, int J, int LPR, int SL, int MODE = kModeStore>
@@ -651,25 +680,11 @@ hipError_t launch_gemv_q(const float *a, const uint8_t *b, float *c, int64_t n, 
     return gemv_q_rows<FMT, kModeStore>(a, b, c, n, k, s, di.cus, epi == kEpiResidual, nullptr);
 }
 
-// f16 rows: the vector kernel when K % 8 == 0, a and b are 16-byte aligned and
-// K <= 16384, else the plain kernel.  MODE kModeStore or kModeTopk.
+// f16 rows of any K and alignment (shapes the K-split kernel does not take):
+// one wave per row.  MODE kModeStore or kModeTopk.
 template <int MODE>
 hipError_t gemv_f16_rows(const float *a, const uint16_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
                          int cus, int aux, int64_t *lists) {
-    const int64_t T = (k / 8 + 63) / 64;
-    if (k % 8 == 0 && aligned16(a) && aligned16(b) && T >= 1 && T <= 32) {
-        // Rows per group measured on MI355X: one row at K <= 2048 (the LM
-        // head: 93 us against 95.5 us with 4 rows; finer groups balance the
-        // waves' last round), four at K <= 1024.
-        if (T <= 1) return run_f16_vec<1, 4, MODE>(a, b, c, n, k, s, cus, aux, lists);
-        if (T <= 2) return run_f16_vec<2, 4, MODE>(a, b, c, n, k, s, cus, aux, lists);
-        if (T <= 4) return run_f16_vec<4, 1, MODE>(a, b, c, n, k, s, cus, aux, lists);
-        if (T <= 8) return run_f16_vec<8, 2, MODE>(a, b, c, n, k, s, cus, aux, lists);
-        if (T <= 12) return run_f16_vec<12, 1, MODE>(a, b, c, n, k, s, cus, aux, lists);
-        if (T <= 16) return run_f16_vec<16, 1, MODE>(a, b, c, n, k, s, cus, aux, lists);
-        if (T <= 24) return run_f16_vec<24, 1, MODE>(a, b, c, n, k, s, cus, aux, lists);
-        return run_f16_vec<32, 1, MODE>(a, b, c, n, k, s, cus, aux, lists);
-    }
     const int64_t waves = balanced_workers(n, static_cast<int64_t>(cus) * 16);
     const int64_t blocks = (waves + 3) / 4;
     if (lists) *lists = blocks * 4;
@@ -687,18 +702,11 @@ hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t 
     DeviceInfo di;
     hipError_t e = device_info(&di);
     if (e != hipSuccess) return e;
-    const int64_t T = (k / 8 + 63) / 64;
     if (epi == kEpiGlu) {
-        // R rows per group as for the plain rows, at least one gate and one up row.
-        if (k % 8 == 0 && aligned16(a) && aligned16(b) && T >= 1 && T <= 16) {
-            if (T <= 1) return run_f16_vec<1, 8, kModeGlu>(a, b, c, n, k, s, di.cus, 0);
-            if (T <= 2) return run_f16_vec<2, 8, kModeGlu>(a, b, c, n, k, s, di.cus, 0);
-            if (T <= 4) return run_f16_vec<4, 4, kModeGlu>(a, b, c, n, k, s, di.cus, 0);
-            if (T <= 8) return run_f16_vec<8, 2, kModeGlu>(a, b, c, n, k, s, di.cus, 0);
-            return run_f16_vec<16, 2, kModeGlu>(a, b, c, n, k, s, di.cus, 0);
-        }
+        if (f16_ksplit_ok(a, b, k)) return f16_ksplit<kModeGlu>(a, b, c, n, k, s, 0);
         return glu_two_pass(c, n, s, [&](float *gu) { return launch_gemv_f16(a, b, gu, 2 * n, k, s, kEpiNone); });
     }
+    if (f16_ksplit_ok(a, b, k)) return f16_ksplit<kModeStore>(a, b, c, n, k, s, epi == kEpiResidual);
     return gemv_f16_rows<kModeStore>(a, b, c, n, k, s, di.cus, epi == kEpiResidual, nullptr);
 }
 
@@ -718,6 +726,25 @@ hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n
     DeviceInfo di;
     hipError_t e = device_info(&di);
     if (e != hipSuccess) return e;
+    const uint16_t *b16 = static_cast<const uint16_t *>(b);
+    // f16 rows the K-split kernel takes: its logits go to scratch and the
+    // merge reads them 64 at a time.  A per-workgroup top-k list inside that
+    // kernel would need a loop over row blocks, which costs more than the
+    // logits round trip (608 KB at N = 151936).
+    if (fmt != QFMT_Q8_0 && fmt != QFMT_Q4_0 && n > 0 && f16_ksplit_ok(a, b16, k)) {
+        ScratchLease lease;
+        void *scratch = nullptr;
+        const int64_t lbytes = (n * 4 + 255) / 256 * 256;
+        e = lease.acquire(static_cast<size_t>(lbytes) + static_cast<size_t>(kTopkGroups) * topk * sizeof(TopkCand),
+                          s, &scratch);
+        if (e != hipSuccess) return e;
+        float *logits = static_cast<float *>(scratch);
+        TopkCand *partial = reinterpret_cast<TopkCand *>(static_cast<char *>(scratch) + lbytes);
+        e = f16_ksplit<kModeStore>(a, b16, logits, n, k, s, 0);
+        if (e == hipSuccess) e = launch_topk_merge(nullptr, 0, logits, n, topk, partial, vals, ids, s);
+        const hipError_t er = lease.release();
+        return e != hipSuccess ? e : er;
+    }
     const int64_t cap = max_topk_lists(di.cus);
     ScratchLease lease;
     void *scratch = nullptr;
@@ -738,7 +765,7 @@ hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n
     else if (fmt == QFMT_Q4_0)
         e = gemv_q_rows<QFMT_Q4_0, kModeTopk>(a, static_cast<const uint8_t *>(b), out, n, k, s, di.cus, topk, &lists);
     else
-        e = gemv_f16_rows<kModeTopk>(a, static_cast<const uint16_t *>(b), out, n, k, s, di.cus, topk, &lists);
+        e = gemv_f16_rows<kModeTopk>(a, b16, out, n, k, s, di.cus, topk, &lists);
     if (e == hipSuccess) e = launch_topk_merge(cand, lists, nullptr, 0, topk, partial, vals, ids, s);
     const hipError_t er = lease.release();
     return e != hipSuccess ? e : er;

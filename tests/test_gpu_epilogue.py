@@ -156,7 +156,7 @@ def test_decode_ffn_shapes(fmt):
     case(fmt, RES, 1, 2048, 6144, seed=43)
 
 
-GEMV_K = {F16: [64, 1000, 2048, 4096, 8192, 16384, 1001, 12],
+GEMV_K = {F16: [64, 1000, 2048, 4096, 8192, 10000, 16384, 24584, 32768, 32776, 1001, 12],
           Q8: [256, 768, 1024, 1536, 2048, 4096, 6144, 8192, 10240, 992],
           Q4: [256, 768, 1024, 1536, 2048, 4096, 6144, 8192, 10240, 992]}
 
@@ -164,10 +164,12 @@ GEMV_K = {F16: [64, 1000, 2048, 4096, 8192, 16384, 1001, 12],
 @pytest.mark.parametrize("epi", [RES, GLU], ids=["residual", "swiglu"])
 @pytest.mark.parametrize("fmt", ALL)
 def test_decode_every_gemv_variant(fmt, epi):
-    """M = 1 over every GEMV kernel family: f16 rows of 1..32 chunk slots per
-    lane (full and partial), 16/32/64 lanes per quantized row with 1..4 blocks
-    per lane (SwiGLU fused in the GEMV), and the shapes that take one GEMV over
-    all 2n rows plus an element-wise pass (K > 8192, K % 256 != 0, K % 8 != 0)."""
+    """M = 1 over every GEMV kernel family: f16 K-split blocks of 1..16 waves
+    with 1, 2 or 4 chunk slots per lane (K a multiple of the split or not, up
+    to K = 32768; 32776 takes the plain kernel), 16/32/64 lanes per quantized
+    row with 1..4 blocks per lane (SwiGLU fused in the GEMV), and the shapes
+    that take one GEMV over all 2n rows plus an element-wise pass (quantized
+    K > 8192 or K % 256 != 0, f16 K % 8 != 0 or K > 32768)."""
     for k in GEMV_K[fmt]:
         for n in (37, 1000):
             case(fmt, epi, 1, n, k, seed=k + n, route="gemv")

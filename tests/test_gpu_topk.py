@@ -125,16 +125,18 @@ def test_lm_head_full_vocab(fmt, topk):
     lm_case(fmt, 151936, 2048, topk, seed=1)
 
 
-GEMV_K = {F16: [64, 1000, 2048, 4096, 8192, 16384, 1001],
+GEMV_K = {F16: [64, 1000, 2048, 4096, 8192, 16384, 24584, 1001, 12],
           Q8: [256, 768, 1024, 1536, 2048, 4096, 8192, 10240, 992],
           Q4: [256, 768, 1024, 1536, 2048, 4096, 8192, 10240, 992]}
 
 
 @pytest.mark.parametrize("fmt", ALL)
 def test_every_gemv_family(fmt):
-    """Every GEMV kernel family keeps its per-wave lists right: f16 rows of 1..32
-    chunk slots per lane, 16/32/64 lanes per quantized row, the plain kernels;
-    ragged vocab sizes, fewer rows than k, fewer rows than waves."""
+    """Every GEMV kernel family feeds the merge right: f16 K-split logits
+    (1..16 waves, 1, 2 or 4 chunk slots per lane) read 64 at a time, the
+    quantized kernels' per-wave lists (16/32/64 lanes per row), the plain
+    kernels' lists (odd or short K); ragged vocab sizes, fewer rows than k,
+    fewer rows than waves."""
     for k in GEMV_K[fmt]:
         for n, topk in ((1, 1), (37, 50), (1000, 1), (5000, 64), (4099, 7)):
             lm_case(fmt, n, k, topk, seed=k + n)

@@ -23,8 +23,9 @@
 //    A 34-byte block is only 2-byte aligned, so the wave first copies S
 //    whole rows (a contiguous, 16-byte aligned byte range when K % 256 == 0)
 //    into its LDS slice with coalesced 128-bit loads, then each lane decodes
-//    whole blocks from LDS (scale, 32 int8 codes, read with unaligned 16-byte
-//    LDS loads) against its register slice of `a`: sum_q = sum_i q_i a_i,
+//    whole blocks from LDS (the block's dword-aligned 36-byte window, read
+//    with 32-bit LDS loads and realigned by a byte permute) against its
+//    register slice of `a`: sum_q = sum_i q_i a_i,
 //    acc += d * sum_q, as the pages apply d after the block's int8 dot
 //    product.  Q4_0 (18-byte blocks, 4-bit codes) is staged the same way; its
 //    codes are turned into exact f16 values (u - 8) with one packed f16
@@ -186,16 +187,33 @@ struct QB {
 constexpr int kQ8BlockBytes = QB<QFMT_Q8_0>::kBytes;
 constexpr int kQ4BlockBytes = QB<QFMT_Q4_0>::kBytes;
 
+// A block starts at an even LDS byte offset pb (rows are whole 16-byte chunks
+// and blocks are 34 or 18 bytes long), so it lies in the dword-aligned window
+// starting at pb & ~3.  The window is read with aligned 32-bit LDS loads
+// (ds_read2_b32), which measured faster on MI355X than 16-byte reads at
+// 2-byte aligned addresses; for a block at pb = 2 (mod 4) everything sits two
+// bytes higher, and one v_perm_b32 per code dword, with a per-lane selector,
+// realigns it.  Returns the scale bits and fills codes[0..NW).
+template <int NW>
+__device__ __forceinline__ uint32_t block_window(const uint8_t *stage, int pb, uint32_t (&codes)[NW]) {
+    const uint32_t *w32 = reinterpret_cast<const uint32_t *>(stage + (pb & ~3));
+    uint32_t w[NW + 1];
+#pragma unroll
+    for (int i = 0; i <= NW; ++i) w[i] = w32[i];
+    const bool hi = (pb & 2) != 0;
+    // v_perm_b32(x, y, sel): byte b of the result is byte sel.b of the pair
+    // (y = bytes 0-3, x = bytes 4-7).  Codes start at window byte 2 (hi: 4).
+    const uint32_t sel = hi ? 0x07060504u : 0x05040302u;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) codes[i] = __builtin_amdgcn_perm(w[i + 1], w[i], sel);
+    return hi ? w[0] >> 16 : w[0] & 0xffffu;
+}
+
 // Dot product of one Q8_0 block held in LDS at byte offset pb with the 32
-// activations av[0..31]: returns d * sum_i q_i * av[i].  The codes are read as
-// two 16-byte LDS loads at block bytes 2 and 18, which are only 2-byte aligned
-// for half of the blocks; gfx950 LDS accepts such unaligned reads.
+// activations av[0..31]: returns d * sum_i q_i * av[i].
 __device__ __forceinline__ float q8_block_dot(const uint8_t *stage, int pb, const float *av) {
-    const uint32_t hb = *reinterpret_cast<const uint16_t *>(stage + pb);
-    u32x4 q0, q1;
-    __builtin_memcpy(&q0, __builtin_assume_aligned(stage + pb + 2, 2), 16);
-    __builtin_memcpy(&q1, __builtin_assume_aligned(stage + pb + 18, 2), 16);
-    const uint32_t wd[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    uint32_t wd[8];
+    const uint32_t hb = block_window<8>(stage, pb, wd);
     // Four independent partial sums (one per byte lane) keep four FMA chains
     // in flight instead of one 32-long dependent chain.
     float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -237,16 +255,14 @@ __device__ __forceinline__ h2 q4_pair(uint32_t x, const Q4Consts &k) {
 }
 
 // Dot product of one Q4_0 block in LDS at byte offset pb with av[0..31]:
-// d * sum_i (u_i - 8) * av[i].  Byte j of the 16 code bytes (one unaligned
-// 16-byte LDS read at block byte 2) holds weight 2j in its low nibble and
+// d * sum_i (u_i - 8) * av[i].  Byte j of the 16 code bytes (block bytes
+// 2..17, read through block_window) holds weight 2j in its low nibble and
 // 2j + 1 in its high nibble.  Codes from high nibbles come out scaled by 16
 // and are summed apart; the exact power-of-two 1/16 is applied at the end.
 // The f16 code values feed mixed-precision FMAs (f32 activation, f32 sum).
 __device__ __forceinline__ float q4_block_dot(const uint8_t *stage, int pb, const float *av) {
-    const uint32_t hb = *reinterpret_cast<const uint16_t *>(stage + pb);
-    u32x4 q;
-    __builtin_memcpy(&q, __builtin_assume_aligned(stage + pb + 2, 2), 16);
-    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    uint32_t wd[4];
+    const uint32_t hb = block_window<4>(stage, pb, wd);
     const Q4Consts kc = q4_consts();
     float lo[2] = {0.f, 0.f}, hi[2] = {0.f, 0.f};
 #pragma unroll

@@ -426,6 +426,85 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
         top.store(reinterpret_cast<TopkCand *>(c) + static_cast<int64_t>(blockIdx.x) * resid, resid);
 }
 
+// K-split quantized GEMV for long rows (store mode, optional residual).
+// Workgroup g (KW = ceil(nb / 64) waves) owns rows [g S, g S + S) and wave w
+// the 64-block slice w of every row: lane l decodes block 64 w + l against
+// a[32 (64 w + l) ..] held in 32 VGPRs, however long K is.  Each wave copies
+// the S slices of its rows (S byte ranges of up to 64 blocks, each a whole
+// number of 16-byte chunks because K % 256 == 0) into its own LDS region with
+// coalesced 128-bit loads, decodes them, reduces its S row partials with one
+// butterfly, and the KW wave partials are summed in wave order through LDS.
+// One pass per workgroup: as for the f16 GEMV, fresh workgroups from the
+// hardware dispatcher stream HBM better than persistent waves, and with `a`
+// spread over the waves no wave re-reads a long activation vector per row.
+template <int FMT, int S>
+__global__ __launch_bounds__(kSplitMaxWaves * kWave) void gemv_q_ksplit(const float *__restrict__ a,
+                                                                        const uint8_t *__restrict__ b,
+                                                                        float *__restrict__ c, int64_t n,
+                                                                        int64_t k, int resid) {
+    extern __shared__ uint4 stage4[];
+    constexpr int BB = QB<FMT>::kBytes;
+    constexpr int SLICE = kWave * BB;       // bytes of a full 64-block slice of a row
+    constexpr int SCH = SLICE / 16;         // its 16-byte chunks (136 for Q8_0, 72 for Q4_0)
+    constexpr int LPS = (SCH + kWave - 1) / kWave;  // chunk loads per lane and row
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int kw = blockDim.x / kWave;
+    const int nb = static_cast<int>(k >> 5);
+    const int64_t row_bytes = static_cast<int64_t>(nb) * BB;
+    const int nbw = min(kWave, nb - kWave * w);  // blocks in this wave's slice, a multiple of 8
+    const int sch = nbw * BB / 16;               // chunks of the slice
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * S;
+    const int rows = static_cast<int>(min<int64_t>(S, n - r0));
+
+    uint4 v[S][LPS];
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+        // Rows past the end are read clamped; their sums are never stored.
+        const int64_t row = min<int64_t>(r0 + r, n - 1);
+        const uint4 *src = reinterpret_cast<const uint4 *>(b + row * row_bytes + static_cast<int64_t>(w) * SLICE);
+#pragma unroll
+        for (int u = 0; u < LPS; ++u)
+            if (u * kWave < sch) v[r][u] = load_nt16(src + min(u * kWave + lane, sch - 1));
+    }
+    const int j = kWave * w + lane;
+    float av[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < nb) x = reinterpret_cast<const float4 *>(a + 32 * j)[i];
+        av[4 * i + 0] = x.x;
+        av[4 * i + 1] = x.y;
+        av[4 * i + 2] = x.z;
+        av[4 * i + 3] = x.w;
+    }
+    uint4 *stage = stage4 + w * S * SCH;  // this wave's region: S slices at a stride of SCH chunks
+#pragma unroll
+    for (int r = 0; r < S; ++r)
+#pragma unroll
+        for (int u = 0; u < LPS; ++u)
+            if (u * kWave < sch && u * kWave + lane < sch) stage[r * SCH + u * kWave + lane] = v[r][u];
+    __syncthreads();
+    const uint8_t *st = reinterpret_cast<const uint8_t *>(stage);
+    const int pb = BB * min(lane, nbw - 1);  // lanes past the slice decode its last block, masked
+    float acc[S];
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+        acc[r] = block_dot<FMT>(st, r * SLICE + pb, av);
+        if (lane >= nbw || r >= rows) acc[r] = 0.f;
+    }
+    // rows_sum leaves row r's partial in lanes r * (64 / S) ..; one lane per row keeps it.
+    const float sum = rows_sum<S, kWave>(acc, lane);
+    __shared__ float part[kSplitMaxWaves][S];
+    if (lane % (kWave / S) == 0) part[w][lane / (kWave / S)] = sum;
+    __syncthreads();
+    if (w == 0 && lane < rows) {
+        float t = part[0][lane];
+        for (int q = 1; q < kw; ++q) t += part[q][lane];
+        float *dst = c + r0 + lane;
+        *dst = resid ? *dst + t : t;
+    }
+}
+
 // Any K % 32 == 0 and 2-byte aligned b: one wave per row, lanes stride over
 // blocks, reading each block with 2-byte loads.
 template <int FMT, bool TOPK>
@@ -627,11 +706,39 @@ int64_t max_topk_lists(int cus) { return static_cast<int64_t>(cus) * 16 + 4; }
 // Staged kernel when K % 256 == 0, a and b are 16-byte aligned and a row fits
 // the stage with at most 8 blocks per lane; otherwise the plain kernel.
 // MODE kModeStore (aux = residual flag) or kModeTopk (aux = k).
+// The K-split kernel: 4 rows per workgroup while the workgroup's stage fits
+// 64 KiB, else 2 or 1.  Measured on MI355X (Q8_0 and Q4_0, N = 1024 .. 8192,
+// K = 4352 .. 11008): 4 rows beat 1 and 2 at every N (the activation slice a
+// wave loads is amortised over more rows) and 8 (more staging registers).
+template <int FMT>
+hipError_t run_q_ksplit(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s,
+                        int resid) {
+    const int kw = static_cast<int>((k / 32 + 63) / 64);
+    const size_t slice = static_cast<size_t>(kWave) * QB<FMT>::kBytes;
+    int srows = 4;
+    while (srows > 1 && static_cast<size_t>(kw) * srows * slice > 65536) srows /= 2;
+    const int64_t blocks = (n + srows - 1) / srows;
+    const size_t lds = static_cast<size_t>(kw) * srows * slice;
+    if (trace_enabled())
+        fprintf(stderr, "[wqmm] gemv_q_ksplit<fmt=%d,S=%d> n=%lld k=%lld grid=%lld block=%d lds=%zu\n", FMT, srows,
+                (long long)n, (long long)k, (long long)blocks, kw * kWave, lds);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kw * kWave);
+    switch (srows) {
+        case 4: hipLaunchKernelGGL((gemv_q_ksplit<FMT, 4>), grid, block, lds, s, a, b, c, n, k, resid); break;
+        case 2: hipLaunchKernelGGL((gemv_q_ksplit<FMT, 2>), grid, block, lds, s, a, b, c, n, k, resid); break;
+        default: hipLaunchKernelGGL((gemv_q_ksplit<FMT, 1>), grid, block, lds, s, a, b, c, n, k, resid); break;
+    }
+    return hipGetLastError();
+}
+
 template <int FMT, int MODE>
 hipError_t gemv_q_rows(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int cus,
                        int aux, int64_t *lists) {
     const int64_t nb = k / 32;
     const int64_t row_bytes = nb * QB<FMT>::kBytes;
+    // Long rows (more than 128 blocks, up to 16 waves of 64): K split over the waves of a workgroup.
+    if (MODE == kModeStore && nb % 8 == 0 && nb > 128 && nb <= 64 * kSplitMaxWaves && aligned16(a) && aligned16(b))
+        return run_q_ksplit<FMT>(a, b, c, n, k, s, aux);
     if (nb % 8 == 0 && aligned16(a) && aligned16(b) && row_bytes <= QB<FMT>::kStage && nb <= 512) {
         if (nb >= 64) {
             switch ((nb + 63) / 64) {

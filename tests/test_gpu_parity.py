@@ -230,6 +230,36 @@ def test_ragged(fmt, mnk):
         full_case("gemm", fmt, m, n, k, seed=1)
 
 
+# Quantized GEMV rows of more than 128 blocks split K over the waves of a
+# workgroup (one 64-block slice per wave): slices of 8 blocks at the end
+# (K = 4352), 16 waves with one row per workgroup (K = 32768), row counts
+# that leave the last workgroup partial, and the down / sweep shapes.
+LONG_K = [(1, 4352), (3, 4352), (5, 6144), (513, 6144), (2048, 6144), (77, 11008), (4096, 11008), (9, 32768),
+          (130, 16640)]
+
+
+@pytest.mark.parametrize("fmt", [Q8, Q4])
+@pytest.mark.parametrize("nk", LONG_K, ids=[f"{n}x{k}" for n, k in LONG_K])
+def test_gemv_long_k_split(fmt, nk):
+    n, k = nk
+    full_case("gemv", fmt, 1, n, k, seed=11)
+
+
+@pytest.mark.parametrize("fmt", [Q8, Q4])
+def test_gemv_long_k_onehot_bit_exact(fmt):
+    """a = e_j through the K-split GEMV returns column j of the decoded weights
+    exactly, for a block in every wave's slice and at slice edges."""
+    n, k = 515, 6144
+    ref_b, dev_b = encoded(n, k, fmt, 12)
+    w = oracle.decode(ref_b, fmt, n, k)
+    for j in (0, 31, 32, 2047, 2048, 2080, 4095, 4096, 6143):
+        say(f"long-K one-hot fmt={fmt} j={j}")
+        a = np.zeros((1, k), np.float32)
+        a[0, j] = 1.0
+        c = run_gpu("gemv", fmt, a, dev_b, 1, n, k)
+        assert np.array_equal(c[0].astype(np.float64), w[:, j]), f"gemv column {j}"
+
+
 @pytest.mark.parametrize("mnk", [(1, 37, 1), (1, 50, 7), (2, 19, 33), (1, 64, 1001), (9, 40, 999), (1, 8, 4100)])
 def test_f16_any_k(mnk):
     """K not a multiple of 8 (or of 32): the general code paths."""

@@ -9,8 +9,12 @@
 //
 // CDNA4 design:
 //  * A workgroup of 4 waves computes a BM x BN tile of C; waves are arranged
-//    WM x WN and each owns a (BM/WM) x (BN/WN) sub-tile made of 16x16 blocks,
-//    each block accumulated by v_mfma_f32_16x16x4_f32 in four AGPRs.
+//    WM x WN and each owns a (BM/WM) x (BN/WN) sub-tile made of 32x32 blocks,
+//    each accumulated by v_mfma_f32_32x32x2_f32 in 16 AGPRs, where the
+//    sub-tile is a multiple of 32 both ways; otherwise of 16x16 blocks,
+//    accumulated by v_mfma_f32_16x16x4_f32 in four AGPRs.  The 32x32 block
+//    needs fewer independent accumulator chains to keep the matrix core busy
+//    (measured on MI355X: 2-6 % faster on every 64/128-row tile and split).
 //  * The K loop steps by BK = 32, exactly one Q8_0 block per weight row.  Each
 //    step stages the A tile (f32) and the weight tile, widened (f16) or
 //    dequantised (d*q, exact in f32), in LDS.  Three-stage pipeline with one
@@ -18,9 +22,10 @@
 //    tile i+1 (already in registers) is written to the other buffer between
 //    the two halves of step i's MFMAs, and tile i+2 is loading from memory.
 //  * The reduction index inside a 32-wide step is permuted so that every lane
-//    reads 8 consecutive k (two 128-bit LDS reads) per 16-row fragment: in MFMA
-//    step t the lane group g = lane/16 supplies k = 8g + t.  The sum over k is
-//    unchanged; only its order differs.
+//    reads consecutive k with 128-bit LDS reads: with 16x16 blocks, in MFMA
+//    step t the lane group g = lane/16 supplies k = 8g + t (8 k per lane);
+//    with 32x32 blocks g = lane/32 supplies k = 16g + t (16 k per lane).  The
+//    sum over k is unchanged; only its order differs.
 //  * Rows of the LDS tiles are padded by 16 bytes to spread LDS banks.
 //  * Split K: when the (M, N) tiles alone cannot fill 256 CUs (small M, long
 //    K), the K range is cut into equal splits whose partial tiles go to a
@@ -34,6 +39,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 namespace wq {
 namespace {
@@ -57,12 +63,22 @@ __device__ __forceinline__ int xcd_tile(int bid, int tiles) {
     return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
 }
 
-template <int BM, int BN, int WM, int WN, int FMT, bool VEC>
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// MF: the matrix-core block, 16 (v_mfma_f32_16x16x4_f32, 4 accumulators per
+// lane) or 32 (v_mfma_f32_32x32x2_f32, 16 accumulators per lane).
+template <int BM, int BN, int WM, int WN, int FMT, bool VEC, int MF>
 struct Gemm {
     static_assert(WM * WN == 4, "four waves");
+    static_assert(MF == 16 || MF == 32, "matrix block");
     static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int FM = WTM / 16, FN = WTN / 16;
-    static_assert(FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+    static constexpr int FM = WTM / MF, FN = WTN / MF;
+    static_assert(FM >= 1 && FN >= 1 && WTM % MF == 0 && WTN % MF == 0, "wave tile");
+    // Per lane and k-tile: 64 / MF lane groups share the BK = 32 reduction
+    // indices, KQ float4 (KQ * 4 consecutive k) each.
+    static constexpr int LG = 64 / MF, KQ = BK / LG / 4;
+    static constexpr int NV = MF == 16 ? 4 : 16;  // accumulators per lane and block
+    typedef typename std::conditional<MF == 16, v4f, v16f>::type acc_t;
     static constexpr int A_ITERS = (BM * 8 + 255) / 256;    // float4 chunks of A per thread
     static constexpr int B16_ITERS = (BN * 4 + 255) / 256;  // uint4 chunks of f16 B per thread
     static constexpr int B8_ITERS = (BN * 2 + 255) / 256;   // half blocks of Q8_0 / Q4_0 B per thread
@@ -230,46 +246,57 @@ struct Gemm {
         }
     }
 
-    // Fragments of one k-tile: lane (i = lane % 16, g = lane / 16) holds, for
-    // fragment f, the 8 consecutive k = 8g .. 8g+7 of its row: `lo` covers MFMA
-    // steps t = 0..3 and `hi` steps t = 4..7.
+    // Fragments of one k-tile: lane (i = lane % MF, g = lane / MF) holds, for
+    // fragment f, the 4 KQ consecutive k = 4 KQ g .. 4 KQ g + 4 KQ - 1 of its
+    // row (8 for MF = 16, 16 for MF = 32); MFMA step t takes component t.
     struct Frags {
-        float4 a_lo[FM], a_hi[FM], b_lo[FN], b_hi[FN];
+        float4 a[FM][KQ], b[FN][KQ];
     };
 
     static __device__ __forceinline__ void read_frags(Frags &fr, const float (*As)[LDP],
                                                       const float (*Bs)[LDP], int wm, int wn,
                                                       int lane) {
-        const int li = lane & 15, lg = lane >> 4;
+        const int li = lane % MF, lg = lane / MF;
 #pragma unroll
-        for (int f = 0; f < FM; ++f)
-            fr.a_lo[f] = *reinterpret_cast<const float4 *>(&As[wm * WTM + 16 * f + li][8 * lg]);
+        for (int q = 0; q < KQ; ++q) {
 #pragma unroll
-        for (int f = 0; f < FN; ++f)
-            fr.b_lo[f] = *reinterpret_cast<const float4 *>(&Bs[wn * WTN + 16 * f + li][8 * lg]);
+            for (int f = 0; f < FM; ++f)
+                fr.a[f][q] = *reinterpret_cast<const float4 *>(&As[wm * WTM + MF * f + li][4 * KQ * lg + 4 * q]);
 #pragma unroll
-        for (int f = 0; f < FM; ++f)
-            fr.a_hi[f] = *reinterpret_cast<const float4 *>(&As[wm * WTM + 16 * f + li][8 * lg + 4]);
-#pragma unroll
-        for (int f = 0; f < FN; ++f)
-            fr.b_hi[f] = *reinterpret_cast<const float4 *>(&Bs[wn * WTN + 16 * f + li][8 * lg + 4]);
+            for (int f = 0; f < FN; ++f)
+                fr.b[f][q] = *reinterpret_cast<const float4 *>(&Bs[wn * WTN + MF * f + li][4 * KQ * lg + 4 * q]);
+        }
     }
 
     static __device__ __forceinline__ float comp(const float4 &v, int t) {
         return t == 0 ? v.x : t == 1 ? v.y : t == 2 ? v.z : v.w;
     }
 
-    // Four MFMA steps (k = 8g + t0 .. 8g + t0 + 3) on every 16x16 block.
-    static __device__ __forceinline__ void mfma_half(v4f (&acc)[FM][FN], const float4 (&a)[FM],
-                                                     const float4 (&b)[FN]) {
+    // MFMA steps t = H * 4 KQ / 2 .. (H + 1) * 4 KQ / 2 - 1 on every block
+    // (k = 4 KQ g + t in lane group g): half of the k-tile.
+    template <int H>
+    static __device__ __forceinline__ void mfma_half(acc_t (&acc)[FM][FN], const Frags &fr) {
+        constexpr int T = 4 * KQ / 2;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = H * T; t < (H + 1) * T; ++t)
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(a[i], t), comp(b[j], t), acc[i][j],
-                                                                     0, 0, 0);
+                for (int j = 0; j < FN; ++j) {
+                    if constexpr (MF == 16)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(comp(fr.a[i][t / 4], t % 4),
+                                                                         comp(fr.b[j][t / 4], t % 4), acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(fr.a[i][t / 4], t % 4),
+                                                                         comp(fr.b[j][t / 4], t % 4), acc[i][j], 0, 0, 0);
+                }
+    }
+
+    // Row (within the block) of accumulator v of a lane: 16x16 blocks hold
+    // row 4 (lane / 16) + v, 32x32 blocks row 8 (v / 4) + 4 (lane / 32) + v % 4;
+    // the column is lane % MF.
+    static __device__ __forceinline__ int acc_row(int lane, int v) {
+        return MF == 16 ? 4 * (lane / 16) + v : 8 * (v / 4) + 4 * (lane / 32) + v % 4;
     }
 };
 
@@ -278,12 +305,12 @@ struct Gemm {
 // With one split the tile goes to C [M, NO] through the epilogue; otherwise the
 // raw sums go to out = partial + s*M*N, column = weight row, and
 // reduce_splits sums them in split order and applies the epilogue.
-template <int BM, int BN, int WM, int WN, int FMT, bool VEC>
+template <int BM, int BN, int WM, int WN, int FMT, bool VEC, int MF>
 __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, const void *__restrict__ bw,
                                                  float *__restrict__ c, int64_t M, int64_t N, int64_t K,
                                                  int mtiles, int tiles, int splits, int kts, int64_t NO,
                                                  int epi) {
-    using G = Gemm<BM, BN, WM, WN, FMT, VEC>;
+    using G = Gemm<BM, BN, WM, WN, FMT, VEC, MF>;
     __shared__ float As[2][BM][LDP];
     __shared__ float Bs[2][BN][LDP];
 
@@ -300,11 +327,13 @@ __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, co
     const int64_t nkt = min<int64_t>(ktiles, kt0 + kts) - kt0;  // >= 1 by construction
     float *out = c + static_cast<int64_t>(split) * M * N;
 
-    v4f acc[G::FM][G::FN];
+    typename G::acc_t acc[G::FM][G::FN];
 #pragma unroll
     for (int i = 0; i < G::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < G::FN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < G::FN; ++j)
+#pragma unroll
+            for (int v = 0; v < G::NV; ++v) acc[i][j][v] = 0.f;
 
     // Software pipeline: tile i is in LDS buffer i & 1; tile i+1 sits in
     // registers and is written to the other buffer between the two MFMA
@@ -321,9 +350,9 @@ __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, co
         const int cur = static_cast<int>(i & 1);
         typename G::Frags fr;
         G::read_frags(fr, As[cur], Bs[cur], wm, wn, lane);
-        G::mfma_half(acc, fr.a_lo, fr.b_lo);
+        G::template mfma_half<0>(acc, fr);
         if (i + 1 < nkt) G::store(rnext, As[cur ^ 1], Bs[cur ^ 1], tid, (kt0 + i + 1) * BK, K);
-        G::mfma_half(acc, fr.a_hi, fr.b_hi);
+        G::template mfma_half<1>(acc, fr);
         __syncthreads();
     };
     int64_t i = 0;
@@ -333,22 +362,23 @@ __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, co
     }
     if (i < nkt) step(i, r1, r0);
 
-    // D[i][j] of a 16x16 block: lane l, register v holds row 4*(l/16) + v, column l%16.
-    const int li = lane & 15, lg = lane >> 4;
+    // Accumulator v of block (fi, fj): row G::acc_row(lane, v), column lane % MF.
+    const int li = lane % MF;
+    const int64_t rwave = m0 + wm * G::WTM;
     if (splits == 1 && glu) {
         // SwiGLU: gate fragment fj pairs with up fragment fj + FN/2.
         if constexpr (G::FN % 2 == 0) {
 #pragma unroll
             for (int fi = 0; fi < G::FM; ++fi) {
-                const int64_t rbase = m0 + wm * G::WTM + 16 * fi + 4 * lg;
 #pragma unroll
                 for (int fj = 0; fj < G::FN / 2; ++fj) {
-                    const int64_t col = n0 + wn * (G::WTN / 2) + 16 * fj + li;
+                    const int64_t col = n0 + wn * (G::WTN / 2) + MF * fj + li;
                     if (col >= NO) continue;
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (rbase + v < M)
-                            c[(rbase + v) * NO + col] = silu(acc[fi][fj][v]) * acc[fi][fj + G::FN / 2][v];
+                    for (int v = 0; v < G::NV; ++v) {
+                        const int64_t row = rwave + MF * fi + G::acc_row(lane, v);
+                        if (row < M) c[row * NO + col] = silu(acc[fi][fj][v]) * acc[fi][fj + G::FN / 2][v];
+                    }
                 }
             }
         }
@@ -357,25 +387,26 @@ __global__ __launch_bounds__(256) void gemm_mfma(const float *__restrict__ a, co
     const bool resid = splits == 1 && epi == kEpiResidual;
 #pragma unroll
     for (int fi = 0; fi < G::FM; ++fi) {
-        const int64_t rbase = m0 + wm * G::WTM + 16 * fi + 4 * lg;
 #pragma unroll
         for (int fj = 0; fj < G::FN; ++fj) {
             // Column of C (one split) or of the partial buffer (weight row).
-            int64_t col = n0 + wn * G::WTN + 16 * fj + li;
+            int64_t col = n0 + wn * G::WTN + MF * fj + li;
             bool ok = col < N;
             if (glu) {
-                const int within = 16 * fj + li;
+                const int within = MF * fj + li;
                 const int64_t oc = n0 + wn * (G::WTN / 2) + within % (G::WTN / 2);
                 ok = oc < NO;
                 col = within < G::WTN / 2 ? oc : NO + oc;
             }
             if (!ok) continue;
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                if (rbase + v < M) {
-                    float *dst = out + (rbase + v) * N + col;
+            for (int v = 0; v < G::NV; ++v) {
+                const int64_t row = rwave + MF * fi + G::acc_row(lane, v);
+                if (row < M) {
+                    float *dst = out + row * N + col;
                     *dst = resid ? *dst + acc[fi][fj][v] : acc[fi][fj][v];
                 }
+            }
         }
     }
 }
@@ -440,12 +471,22 @@ hipError_t run(const float *a, const void *b, float *c, int64_t m, int64_t n, in
                 "epi=%d grid=%lld\n",
                 BM, BN, WM, WN, FMT, vec ? 1 : 0, (long long)m, (long long)n, (long long)k, splits, kts, epi,
                 (long long)grid);
-    if (vec)
-        hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, true>), dim3(grid), dim3(256), 0, s, a, b, c, m, n, k,
+    // 32x32 blocks where the wave tile is a multiple of 32 both ways (and, for
+    // the fused SwiGLU, has an even number of 32-column fragments); else 16x16.
+    constexpr bool mf32_tile = (BM / WM) % 32 == 0 && (BN / WN) % 32 == 0;
+    constexpr bool mf32_glu = mf32_tile && ((BN / WN) / 32) % 2 == 0;
+    const bool mf32 = vec && mf32_tile && (!glu || splits > 1 || mf32_glu);
+    if (mf32) {
+        if constexpr (mf32_tile)
+            hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, true, 32>), dim3(grid), dim3(256), 0, s, a, b, c, m, n,
+                               k, static_cast<int>(mt), static_cast<int>(tiles), splits, kts, no, epi);
+    } else if (vec) {
+        hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, true, 16>), dim3(grid), dim3(256), 0, s, a, b, c, m, n, k,
                            static_cast<int>(mt), static_cast<int>(tiles), splits, kts, no, epi);
-    else
-        hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, false>), dim3(grid), dim3(256), 0, s, a, b, c, m, n, k,
-                           static_cast<int>(mt), static_cast<int>(tiles), splits, kts, no, epi);
+    } else {
+        hipLaunchKernelGGL((gemm_mfma<BM, BN, WM, WN, FMT, false, 16>), dim3(grid), dim3(256), 0, s, a, b, c, m, n,
+                           k, static_cast<int>(mt), static_cast<int>(tiles), splits, kts, no, epi);
+    }
     return hipGetLastError();
 }
 

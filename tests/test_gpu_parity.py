@@ -260,6 +260,20 @@ def test_gemv_long_k_onehot_bit_exact(fmt):
         assert np.array_equal(c[0].astype(np.float64), w[:, j]), f"gemv column {j}"
 
 
+@pytest.mark.parametrize("fmt", [Q8, Q4])
+def test_gemv_long_k_deterministic_and_linear(fmt):
+    """The K-split GEMV sums its wave partials in a fixed order: repeated calls
+    are bitwise identical, C(2a) = 2 C(a) and C(-a) = -C(a)."""
+    n, k = 515, 11008
+    say(f"long-K determinism fmt={fmt}")
+    _, dev_b = encoded(n, k, fmt, 13)
+    a = acts(1, k, 13)
+    c1 = run_gpu("gemv", fmt, a, dev_b, 1, n, k)
+    assert np.array_equal(c1, run_gpu("gemv", fmt, a, dev_b, 1, n, k))
+    assert np.array_equal(run_gpu("gemv", fmt, 2 * a, dev_b, 1, n, k), 2 * c1)
+    assert np.array_equal(run_gpu("gemv", fmt, -a, dev_b, 1, n, k), -c1)
+
+
 @pytest.mark.parametrize("mnk", [(1, 37, 1), (1, 50, 7), (2, 19, 33), (1, 64, 1001), (9, 40, 999), (1, 8, 4100)])
 def test_f16_any_k(mnk):
     """K not a multiple of 8 (or of 32): the general code paths."""

@@ -21,8 +21,12 @@ Q4_0 decode suites, the f16 prefill GEMM at M = 512, the Q8_0 and Q4_0 M
 sweeps, the fused residual and SwiGLU epilogues against the same product
 followed by separate element-wise kernels, the fused LM-head GEMV + top-k
 against the GEMV alone and the GEMV followed by a top-k pass, the split-KV decode
-attention (KV bytes GB/s at 4K-128K tokens), and a plain device copy as the
-achievable-bandwidth reference.  Q4_0
+attention (KV bytes GB/s at 4K-128K tokens), the 1024x1024 f16 GEMV, a plain
+device copy, and ``read_ceiling``: a read-only kernel (wq_read_probe, the
+GEMVs' 128-bit non-temporal loads and nothing else) timed on every byte size
+a bandwidth-bound row reads, rotated over >= 1 GiB of copies like the
+weights.  Every decode GEMV is reported against both the 8 TB/s peak and the
+plain read of its own byte count.  Q4_0
 weights are synthetic bytes (random codes and scales) since no Q4_0 encoder is
 given.
 """
@@ -227,6 +231,44 @@ def time_launches(torch, fn, iters, warmup):
     return s.elapsed_time(e) / 1e3 / iters
 
 
+def read_ceiling(torch, wq, sizes, iters, warmup):
+    """Plain-read time of each byte size in `sizes` (label -> bytes): the read
+    probe over rotated copies totalling >= 1 GiB, best of its 2, 4 and 8 chunks
+    per lane."""
+    res = {}
+    for label, nbytes in sizes.items():
+        nb = (nbytes + 15) // 16 * 16
+        copies = max(2, math.ceil(ROTATE_BYTES / nb))
+        bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        for b in bufs:
+            b.fill_(1)
+        out = torch.empty((nb + 1023) // 1024, dtype=torch.int32, device="cuda")
+        best = None
+        for variant in (1, 2, 3):
+            t = time_launches(torch, lambda i: wq.wq_read_probe(bufs[i % copies], nb, out, variant), iters, warmup)
+            if best is None or t < best[0]:
+                best = (t, variant)
+        res[label] = {"bytes": nbytes, "us": round(best[0] * 1e6, 2), "GB/s": round(nbytes / best[0] / 1e9, 1),
+                      "chunks_per_lane": 1 << best[1]}
+        del bufs, out
+        torch.cuda.empty_cache()
+    return res
+
+
+def gemv_table(torch, wq, suite, fmt, iters, warmup, ceiling):
+    """Each decode GEMV of a suite timed alone as a burst of back-to-back launches
+    (rotated weights), against the 8 TB/s peak and the plain read of its bytes."""
+    out = {}
+    for it in suite.items:
+        t = time_launches(torch, lambda i: wq.wq_matmul(it["a"], it["bs"][i % len(it["bs"])], it["c"], 1, it["n"],
+                                                        it["k"], fmt), iters, warmup)
+        gbs = it["bytes"] / t / 1e9
+        ceil_gbs = ceiling.get(it["bytes"])
+        out[it["name"]] = {"us": round(t * 1e6, 2), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                           "frac_read_ceiling": round(gbs / ceil_gbs, 4) if ceil_gbs else None}
+    return out
+
+
 def epilogue_bench(torch, wq, wqgen, seed, iters, warmup):
     """Fused epilogues on the suite's FFN shapes (hidden 2048, intermediate 3072):
     gate||up [6144, 2048] with SwiGLU into [m, 3072], and down [2048, 6144] added
@@ -347,15 +389,36 @@ def attention_bench(torch, wq, seed, iters, warmup):
     return res
 
 
-def cpu_baseline(host_weights, seed, budget_s=12.0):
-    """The CPU oracle on the f16 decode suite: whole suite repeated until the
-    time budget is used (at least one pass)."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(host_weights, seed, budget_s=8.0):
+    """The CPU oracle, timed on this host: the f16 decode suite repeated until the
+    time budget is used (the headline value), then one oracle call per other
+    configuration -- the 1024x1024 GEMV, the Q8_0 decode suite, the two M = 512 f16
+    prefill products and every M of the Q8_0 sweep at both shapes -- and one call
+    per fused row (SwiGLU, LM-head top-50, attention over 4096 tokens).  Threads:
+    every CPU in the process's affinity mask, unless OMP_NUM_THREADS asks for
+    fewer (the GPU machine sets it to the CPU share of one GPU)."""
     import numpy as np
 
     import oracle
     import wqgen
 
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    threads = affinity
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and 0 < int(omp) < threads:
+        threads = int(omp)
+    threads = max(1, min(128, threads))
     enc = {(n, k): oracle.encode(host_weights[(n, k)], oracle.FMT_F16) for _, n, k in DECODE}
     acts = {k: wqgen.activations(1, k, seed) for _, _, k in DECODE}
     bytes_done, t_total, passes = 0, 0.0, 0
@@ -366,33 +429,68 @@ def cpu_baseline(host_weights, seed, budget_s=12.0):
             t_total += time.perf_counter() - t0
             bytes_done += 2 * n * k
         passes += 1
-    # The other hot-path rows, one oracle call each (the same shapes as their GPU tables).
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    configs = {}
+    # C1: GEMV 1024 x 1024 f16.
+    w1 = oracle.encode(wqgen.weights(1024, 1024, seed), oracle.FMT_F16)
+    a1 = wqgen.activations(1, 1024, seed)
+    dt = timed(lambda: oracle.matmul(a1, w1, oracle.FMT_F16, 1, 1024, 1024, threads=threads))
+    configs["gemv_f16_1024x1024"] = {"ms": round(dt * 1e3, 3), "weight_GB/s": round(w1.nbytes / dt / 1e9, 3)}
+    # Q8_0 decode suite (same f32 weights, quantised by the oracle).
+    q8 = {(n, k): oracle.encode(host_weights[(n, k)], oracle.FMT_Q8_0) for _, n, k in DECODE}
+    tq, bq = 0.0, 0
+    for name, n, k in DECODE:
+        dt = timed(lambda: oracle.matmul(acts[k], q8[(n, k)], oracle.FMT_Q8_0, 1, n, k, threads=threads))
+        configs[f"q8_decode_{name}_{n}x{k}"] = {"ms": round(dt * 1e3, 3),
+                                                "weight_GB/s": round(q8[(n, k)].nbytes / dt / 1e9, 3)}
+        tq += dt
+        bq += q8[(n, k)].nbytes
+    configs["q8_decode_suite"] = {"ms": round(tq * 1e3, 3), "weight_GB/s": round(bq / tq / 1e9, 3)}
+    del q8
+    # f16 prefill at M = 512, both shapes, full products.
+    for m, n, k in PREFILL:
+        w = oracle.encode(wqgen.weights(n, k, seed), oracle.FMT_F16)
+        a = wqgen.activations(m, k, seed)
+        dt = timed(lambda: oracle.matmul(a, w, oracle.FMT_F16, m, n, k, threads=threads))
+        configs[f"f16_prefill_{m}x{n}x{k}"] = {"ms": round(dt * 1e3, 2), "GFLOP/s": round(2.0 * m * n * k / dt / 1e9, 2)}
+    # Q8_0 M sweep, every M at both shapes.
+    for n, k in SWEEP_SHAPES:
+        w = oracle.encode(wqgen.weights(n, k, seed), oracle.FMT_Q8_0)
+        a_all = wqgen.activations(max(SWEEP_M), k, seed)
+        for m in SWEEP_M:
+            a = np.ascontiguousarray(a_all[:m])
+            dt = timed(lambda: oracle.matmul(a, w, oracle.FMT_Q8_0, m, n, k, threads=threads))
+            configs[f"q8_sweep_{m}x{n}x{k}"] = {"ms": round(dt * 1e3, 2),
+                                                "GFLOP/s": round(2.0 * m * n * k / dt / 1e9, 2),
+                                                "weight_GB/s": round(w.nbytes / dt / 1e9, 3)}
+        del w, a_all
+    # The fused rows, one oracle call each (the same shapes as their GPU tables).
     rows = {}
     a = wqgen.activations(1, 2048, seed)
     gu = enc[(6144, 2048)]
-    t0 = time.perf_counter()
-    oracle.matmul_epilogue(a, gu, oracle.FMT_F16, 1, 3072, 2048, oracle.EPI_SWIGLU, threads=threads)
-    dt = time.perf_counter() - t0
+    dt = timed(lambda: oracle.matmul_epilogue(a, gu, oracle.FMT_F16, 1, 3072, 2048, oracle.EPI_SWIGLU,
+                                              threads=threads))
     rows["swiglu_gate_up_m1_6144x2048"] = {"ms": round(dt * 1e3, 2), "weight_GB/s": round(2 * 6144 * 2048 / dt / 1e9, 3)}
     lm = enc[(151936, 2048)]
-    t0 = time.perf_counter()
-    oracle.lm_head_topk(a, lm, oracle.FMT_F16, 151936, 2048, 50, threads=threads)
-    dt = time.perf_counter() - t0
+    dt = timed(lambda: oracle.lm_head_topk(a, lm, oracle.FMT_F16, 151936, 2048, 50, threads=threads))
     rows["lm_head_topk50_151936x2048"] = {"ms": round(dt * 1e3, 2), "weight_GB/s": round(lm.nbytes / dt / 1e9, 3)}
     L, D, hq, hkv = 4096, 256, 8, 2
     q = wqgen.normal((hq, D), seed=seed, stream=11)
     kc = wqgen.normal((L, hkv * D), seed=seed, stream=12)
     vc = wqgen.normal((L, hkv * D), seed=seed, stream=13)
-    t0 = time.perf_counter()
-    oracle.decode_attention(q, kc, vc, oracle.KV_F32, L, D, hq, hkv, 0.0625)
-    dt = time.perf_counter() - t0
+    dt = timed(lambda: oracle.decode_attention(q, kc, vc, oracle.KV_F32, L, D, hq, hkv, 0.0625))
     rows["decode_attention_f32_L4096"] = {"ms": round(dt * 1e3, 2), "kv_GB/s": round(2 * kc.nbytes / dt / 1e9, 3),
                                           "threads": 1}
-    del np
     return {"value": round(bytes_done / t_total / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} full pass(es) of the f16 decode suite (4 GEMVs, M=1, {bytes_done // passes} "
-                      f"weight bytes per pass), f64 accumulation, {t_total:.1f} s",
-            "other_rows": rows}
+                      f"weight bytes per pass), f64 accumulation, {t_total:.1f} s; then one oracle call per "
+                      f"other configuration (configs)",
+            "cpu_model": _cpu_model(), "affinity_cpus": affinity, "configs": configs, "other_rows": rows}
 
 
 def main():
@@ -418,6 +516,23 @@ def main():
     secondary = {}
     only = args.only
     result = None
+    iters = max(10, args.steps // 2)
+
+    # Plain-read ceilings at every byte size a bandwidth-bound row reads.
+    ceiling = {}
+    if only in (None, "f16", "q8", "q4", "sweep"):
+        log("read ceiling")
+        sizes = {"gemv_f16_1024x1024": wq.weight_bytes(1024, 1024, F16)}
+        for fmt, key in ((F16, "f16"), (Q8, "q8"), (Q4, "q4")):
+            for name, n, k in DECODE:
+                sizes[f"{key}_{name}_{n}x{k}"] = wq.weight_bytes(n, k, fmt)
+        for fmt, key in ((Q8, "q8"), (Q4, "q4")):
+            for n, k in SWEEP_SHAPES:
+                sizes[f"{key}_sweep_{n}x{k}"] = wq.weight_bytes(n, k, fmt)
+        sizes["1GiB"] = 1 << 30
+        rc = read_ceiling(torch, wq, sizes, iters, args.warmup)
+        secondary["read_ceiling"] = rc
+        ceiling = {v["bytes"]: v["GB/s"] for v in rc.values()}
 
     if only in (None, "f16"):
         log("f16 decode suite: encoding + rotation copies")
@@ -437,6 +552,7 @@ def main():
                                                            it["k"], F16), max(20, args.steps), 3)
         achieved = lm_bytes / lm_s / 1e9
         value = s16.bytes_per_step * args.steps / total / 1e9
+        per_burst = gemv_table(torch, wq, s16, F16, iters, args.warmup, ceiling)
         # Per-kernel times in a separate, untimed pass with every launch bracketed
         # (includes the events' own cost, about 3 us for the small kernels).
         _, _, per_all = time_suite(torch, wq, s16, max(10, args.steps // 2), 2, bracket=range(len(s16.items)))
@@ -474,12 +590,32 @@ def main():
                 "avg_launch_us": round(lm_s * 1e6, 3),
                 "avg_launch_us_per_launch_event_pairs_in_suite": round(lm_pairs_s * 1e6, 3),
                 "algorithmic_bytes_per_launch": lm_bytes,
+                "read_ceiling_GB/s": ceiling.get(lm_bytes),
+                "frac_of_read_ceiling": round(achieved / ceiling[lm_bytes], 4) if lm_bytes in ceiling else None,
             },
         }
+        secondary["f16_decode_per_kernel"] = per_burst
         secondary["f16_decode_per_kernel_event_timed"] = {
             it["name"]: {"us": round(per_all[j] * 1e6, 3), "GB/s": round(it["bytes"] / per_all[j] / 1e9, 1)}
             for j, it in enumerate(s16.items)}
         del s16
+        torch.cuda.empty_cache()
+
+    if not args.no_secondary and only in (None, "f16"):
+        log("GEMV f16 1024x1024")
+        n, k = 1024, 1024
+        b0 = wq.pack_f16(torch.from_numpy(wqgen.weights(n, k, args.seed)).cuda())
+        nbytes = wq.weight_bytes(n, k, F16)
+        bs = [b0] + [b0.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / nbytes)) - 1)]
+        a = torch.from_numpy(wqgen.activations(1, k, args.seed)).cuda()
+        c = torch.empty((1, n), device="cuda")
+        t = time_launches(torch, lambda i: wq.wq_matmul(a, bs[i % len(bs)], c, 1, n, k, F16), iters, args.warmup)
+        gbs = nbytes / t / 1e9
+        secondary["gemv_f16_1024x1024"] = {"us": round(t * 1e6, 2), "GB/s": round(gbs, 1),
+                                           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                           "frac_read_ceiling": round(gbs / ceiling[nbytes], 4) if nbytes in ceiling
+                                           else None}
+        del bs, b0
         torch.cuda.empty_cache()
 
     for fmt, key in ((Q8, "q8"), (Q4, "q4")):
@@ -494,6 +630,7 @@ def main():
         lmq_s = time_launches(torch, lambda i: wq.wq_matmul(it["a"], it["bs"][i % len(it["bs"])], it["c"], 1, it["n"],
                                                             it["k"], fmt), max(20, args.steps), 3)
         secondary[f"{key}_decode_suite"] = {
+            "per_kernel": gemv_table(torch, wq, sq, fmt, iters, args.warmup, ceiling),
             "GB/s": round(sq.bytes_per_step * args.steps / total / 1e9, 2),
             "frac_hbm": round(sq.bytes_per_step * args.steps / total / 1e9 / HBM_PEAK_GBS, 4),
             "ms_per_step": round(total / args.steps * 1e3, 5),
@@ -541,8 +678,16 @@ def main():
                     c = torch.empty((m, n), device="cuda")
                     t = time_launches(torch, lambda i: wq.wq_matmul(a, bs[i % len(bs)], c, m, n, k, fmt),
                                       max(10, args.steps // 2), args.warmup)
-                    out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(nbytes / t / 1e9, 1),
-                                           "TFLOP/s": round(2.0 * m * n * k / t / 1e12, 2),
+                    gbs, tf = nbytes / t / 1e9, 2.0 * m * n * k / t / 1e12
+                    # Binding roofline: HBM below the ridge (19.7 flop/B), fp32 MFMA above it.
+                    hbm_bound = 2.0 * m * n * k / nbytes < FP32_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+                    out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(gbs, 1),
+                                           "TFLOP/s": round(tf, 2),
+                                           "bound": "hbm" if hbm_bound else "mfma",
+                                           "frac_of_bound": round(gbs / HBM_PEAK_GBS if hbm_bound
+                                                                  else tf / FP32_MFMA_PEAK_TFLOPS, 4),
+                                           "frac_read_ceiling": round(gbs / ceiling[nbytes], 4)
+                                           if hbm_bound and nbytes in ceiling else None,
                                            "route": ROUTE_NAMES[wq.wq_route_for(m, n, k, fmt)]}
                 del bs, b0
                 torch.cuda.empty_cache()

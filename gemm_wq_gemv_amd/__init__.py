@@ -83,6 +83,7 @@ def _load() -> ctypes.CDLL:
         "wq_set_attn_partition": (I, [I64]),
         "wq_pack_f16": (I, [P, P, I64, P]),
         "wq_quantize_q8_0": (I, [P, P, I64, P]),
+        "wq_read_probe": (I, [P, I64, P, I, P]),
         "wq_route_for": (I, [I64, I64, I64, I]),
         "wq_gemm_plan": (I, [I64, I64, I64, I, I, P, P, P]),
         "wq_set_gemm_plan": (I, [I, I, I]),
@@ -287,6 +288,16 @@ def wq_quantize_q8_0(w, out, count: int, stream=None) -> None:
         _need(w, 4 * count, "w")
         _need(out, count // 32 * Q8_0_BLOCK_BYTES, "out")
     _check(_lib.wq_quantize_q8_0(_ptr(w), _ptr(out), count, _stream(stream, out)), "wq_quantize_q8_0")
+
+
+def wq_read_probe(p, nbytes: int, out, variant: int = 2, stream=None) -> None:
+    """Measurement hook: stream `nbytes` bytes of tensor p once (plain read);
+    out (uint32/int32, ceil(nbytes / 1024) elements) receives per-wave checksums."""
+    if nbytes > 0:
+        _need(p, nbytes, "p")
+        _dtype(out, (torch.uint32, torch.int32), "out")
+        _need(out, 4 * ((nbytes + 1023) // 1024), "out")
+    _check(_lib.wq_read_probe(_ptr(p), nbytes, _ptr(out), variant, _stream(stream, out)), "wq_read_probe")
 
 
 def wq_route_for(m: int, n: int, k: int, fmt: int) -> int:

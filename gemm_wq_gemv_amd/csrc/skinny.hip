@@ -225,14 +225,15 @@ struct Skinny {
 
     // One step's matrix ops.  TAIL (the partial step only): chunks of 8
     // columns at or past K are zeroed in both operands, so bytes read past a
-    // row's end cannot leak in.  The scalar f16 loads already return zeros
-    // past K (and K need not be a multiple of 8 there).
+    // row's end (the next row's blocks, whose scale may be anything) cannot
+    // leak in -- for every format and load variant except scalar f16, whose
+    // loads already return zeros past K (K need not be a multiple of 8 there).
     template <bool TAIL>
     static __device__ __forceinline__ void compute(v4f (&acc)[MB][NT], const Regs &r, int64_t k0, int64_t K) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             bool in = true;
-            if constexpr (TAIL && (VEC || FMT == FMT_Q8_0)) in = k0 + (e & ~7) + 8 <= K;
+            if constexpr (TAIL && (VEC || FMT != FMT_F16)) in = k0 + (e & ~7) + 8 <= K;
             float wv[NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) wv[t] = in ? weight(r, t, e) : 0.f;

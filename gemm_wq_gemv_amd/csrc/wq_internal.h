@@ -331,6 +331,9 @@ void gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *
 // capped at the number of k-tiles); (0, 0, 0) clears it.  False if unknown.
 bool set_gemm_plan_override(int bm, int bn, int splits);
 hipError_t launch_fill_zero(float *c, int64_t count, hipStream_t s);
+// Read-bandwidth probe (variant v: 2^v 16-byte chunks per lane); out gets one
+// dword per wave.
+hipError_t launch_read_probe(const void *p, int64_t bytes, uint32_t *out, int variant, hipStream_t s);
 hipError_t launch_pack_f16(const float *w, uint16_t *out, int64_t count, hipStream_t s);
 hipError_t launch_quantize_q8_0(const float *w, uint8_t *out, int64_t count, hipStream_t s);
 

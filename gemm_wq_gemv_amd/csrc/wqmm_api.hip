@@ -427,6 +427,15 @@ int wq_quantize_q8_0(const float *w, uint8_t *out, int64_t count, void *stream) 
     return status_of(wq::launch_quantize_q8_0(w, out, count, static_cast<hipStream_t>(stream)));
 }
 
+int wq_read_probe(const void *p, int64_t bytes, uint32_t *out, int variant, void *stream) {
+    if (bytes < 0 || bytes % 16 != 0 || variant < 0 || variant > 3) return WQ_ERR_SHAPE;
+    if (bytes == 0) return WQ_OK;
+    if (!p || !out) return WQ_ERR_NULL;
+    if (!aligned(p, 16) || !aligned(out, 4)) return WQ_ERR_ALIGN;
+    if (overlaps(out, (bytes + 1023) / 1024 * 4, p, bytes)) return WQ_ERR_ALIAS;
+    return status_of(wq::launch_read_probe(p, bytes, out, variant, static_cast<hipStream_t>(stream)));
+}
+
 int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt) {
     if (!known_format(fmt)) return -WQ_ERR_FORMAT;
     if (m < 0 || n < 0 || k < 0) return -WQ_ERR_SHAPE;

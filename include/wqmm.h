@@ -262,6 +262,17 @@ int wq_pack_f16(const float *w, uint16_t *out, int64_t count, void *stream);
 int wq_quantize_q8_0(const float *w, uint8_t *out, int64_t count, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Measurement hook: the achievable-read ceiling.  Reads `bytes` bytes at p
+ * (device, 16-byte aligned, bytes % 16 == 0, else WQ_ERR_ALIGN / WQ_ERR_SHAPE)
+ * once with 128-bit non-temporal loads -- the loads the GEMVs stream weights
+ * with -- and writes an XOR checksum per wave to out (device, 4-byte aligned,
+ * room for ceil(bytes / 1024) uint32).  variant 0..3: 1, 2, 4 or 8 chunks of
+ * 16 bytes per lane and workgroup of 256 lanes.  It computes nothing of the
+ * product; the benchmark times it to report each bandwidth-bound kernel against
+ * a plain read of the same bytes as well as against the HBM peak. */
+int wq_read_probe(const void *p, int64_t bytes, uint32_t *out, int variant, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Routing and introspection (host only; these never touch the GPU). */
 
 /* The route wq_matmul takes for these arguments when nothing is forced

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import attn_cases
 import gemm_wq_gemv_amd as wq
 import oracle
 import wqgen
@@ -54,6 +55,10 @@ def check(L, D, Hq, Hkv, kvfmt, seed=0, scale=None, kscale=1.0):
     scale = float(np.float32(1.0 / np.sqrt(D))) if scale is None else scale
     say(f"attention L={L} D={D} Hq={Hq} Hkv={Hkv} kv={kvfmt} scale={scale} kscale={kscale}")
     q, k, v = inputs(L, D, Hq, Hkv, kvfmt, seed, kscale)
+    return check_inputs(q, k, v, L, D, Hq, Hkv, kvfmt, scale)
+
+
+def check_inputs(q, k, v, L, D, Hq, Hkv, kvfmt, scale):
     out = run(q, k, v, L, D, Hq, Hkv, kvfmt, scale)
     ref, bound = oracle.decode_attention(q, k, v, kvfmt, L, D, Hq, Hkv, scale)
     err = np.abs(out.astype(np.float64) - ref)
@@ -123,3 +128,41 @@ def test_forced_partition_sizes():
             check(L, 128, 4, 4, F16, seed=ptok + 1)
     finally:
         wq.wq_set_attn_partition(0)
+
+
+@pytest.mark.parametrize("kvfmt", [F32, F16], ids=["f32", "f16"])
+@pytest.mark.parametrize("L", [32768, 131072])
+def test_long_cache_every_token_counts(L, kvfmt):
+    """Scale 0 and one-hot V rows (tests/attn_cases.py): every token weighs 1/L and
+    feeds one output alone, so a skipped token -- the first, the last, one at a
+    partition or tile edge -- puts that output 7x (L = 131072) to 29x (L = 32768)
+    outside the tolerance (tests/test_case_design.py checks this on the CPU)."""
+    say(f"one-hot V, scale 0, L={L} kv={kvfmt}")
+    q, k, v, scale = attn_cases.onehot_v(L, 256, 8, 2, kvfmt)
+    check_inputs(q, k, v, L, 256, 8, 2, kvfmt, scale)
+
+
+def test_dominant_keys_at_partition_edges():
+    """Keys that each carry ~1/9 of the weight placed at the first and last token and
+    at the first and last token of the second and the last partition, for forced
+    partition sizes (ragged last partitions, partitions ending inside a tile) and the
+    automatic size; also the one-hot V case under a forced partition size."""
+    try:
+        for part, L in ((1000, 32768), (64, 4096), (37, 3001), (8, 1000)):
+            wq.wq_set_attn_partition(part)
+            for kvfmt in (F32, F16):
+                pos = attn_cases.edge_positions(L, part)
+                say(f"dominant keys at {pos}, partition {part}, L={L} kv={kvfmt}")
+                q, k, v, scale = attn_cases.dominant(L, 256, 8, 2, kvfmt, pos, seed=part)
+                check_inputs(q, k, v, L, 256, 8, 2, kvfmt, scale)
+        wq.wq_set_attn_partition(1000)
+        say("one-hot V, scale 0, partition 1000, L=32768")
+        q, k, v, scale = attn_cases.onehot_v(32768, 256, 8, 2, F16, seed=1)
+        check_inputs(q, k, v, 32768, 256, 8, 2, F16, scale)
+    finally:
+        wq.wq_set_attn_partition(0)
+    for L in (777, 4096, 32768):
+        pos = sorted({0, L // 4, L // 2, L - 2, L - 1})
+        say(f"dominant keys at {pos}, automatic partitions, L={L}")
+        q, k, v, scale = attn_cases.dominant(L, 256, 8, 2, F32, pos, seed=L)
+        check_inputs(q, k, v, L, 256, 8, 2, F32, scale)

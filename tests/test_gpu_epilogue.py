@@ -177,9 +177,9 @@ def test_decode_every_gemv_variant(fmt, epi):
 
 @pytest.mark.parametrize("epi", [RES, GLU], ids=["residual", "swiglu"])
 @pytest.mark.parametrize("fmt", ALL)
-def test_prefill_sampled(fmt, epi):
-    """M = 512 prefill at the FFN shapes, checked on sampled outputs (first and
-    last rows and columns, tile edges, random picks) and finite elsewhere."""
+def test_prefill_full(fmt, epi):
+    """M = 512 prefill at the FFN shapes (gate||up 2 x 11008 rows with SwiGLU, down
+    11008 -> 4096 into the residual): every output against the oracle."""
     m, k = 512, 4096
     n = 11008 if epi == GLU else 4096
     kk = k if epi == GLU else 11008
@@ -189,12 +189,8 @@ def test_prefill_sampled(fmt, epi):
     a = wqgen.activations(m, kk, 51)
     r = wqgen.residual(m, n, 51) if epi == RES else None
     c = run_ex(a, dev_b, m, n, kk, fmt, epi, r)
-    assert np.isfinite(c).all()
-    rng = np.random.default_rng(5)
-    rr = np.concatenate([[0, 0, m - 1, m - 1, 63, 64, 127, 128], rng.integers(0, m, 500)])
-    cc = np.concatenate([[0, n - 1, 0, n - 1, 63, 64, 95, 96], rng.integers(0, n, 500)])
-    c_ref, bound = oracle.epilogue_entries(a, ref_b, fmt, m, n, kk, epi, rr, cc, r)
-    assert_close(c[rr, cc], c_ref, bound, f"prefill epi={epi} fmt={fmt}")
+    c_ref, bound = oracle.matmul_epilogue(a, ref_b, fmt, m, n, kk, epi, r)
+    assert_close(c, c_ref, bound, f"prefill epi={epi} fmt={fmt}")
 
 
 @pytest.mark.parametrize("fmt", ALL)

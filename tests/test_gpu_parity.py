@@ -8,10 +8,11 @@ bit for bit.  Products must satisfy, per element,
 with c_ref the oracle's float64 result.  Outputs are poisoned with NaN before
 every launch, so an element that is never written fails.
 
-Sizes: the oracle computes every output of the small and ragged cases and of
-the decode configurations; at M = 64 and 512 it computes a sample of outputs
-(first/last rows and columns, tile edges, random picks), and the rest of the
-GPU output is checked to be finite.
+Sizes: the oracle computes every output of every case, the M = 512 prefill and
+the M = 512 sweep (5.6 M outputs) included.  Hand-built Q8_0 / Q4_0 blocks the
+quantiser never writes (zero, subnormal, negative and largest scales, code
+-128) go through every route with one-hot rows of A and must come back bit for
+bit.
 """
 from __future__ import annotations
 
@@ -118,26 +119,6 @@ def full_case(entry, fmt, m, n, k, seed=0):
     return assert_close(c, c_ref, bound, f"{entry} fmt={fmt} {m}x{n}x{k}")
 
 
-def sample_indices(m, n, rng, count=2048):
-    rows = sorted({0, 1, m - 1, m // 2, min(m - 1, 63), min(m - 1, 64), min(m - 1, 127), min(m - 1, 128)}
-                  | set(rng.integers(0, m, 8).tolist()))
-    cols = sorted({0, 1, n - 1, n // 2, min(n - 1, 95), min(n - 1, 96), min(n - 1, 127), min(n - 1, 128)}
-                  | set(rng.integers(0, n, max(8, count // len(rows) - 8)).tolist()))
-    rr, cc = np.meshgrid(rows, cols, indexing="ij")
-    return rr.ravel(), cc.ravel()
-
-
-def sampled_case(entry, fmt, m, n, k, seed=0):
-    say(f"{entry} fmt={fmt} m={m} n={n} k={k} seed={seed} (sampled)")
-    ref_b, dev_b = encoded(n, k, fmt, seed)
-    a = acts(m, k, seed)
-    c = run_gpu(entry, fmt, a, dev_b, m, n, k)
-    assert np.isfinite(c).all(), "unwritten (NaN) or non-finite outputs"
-    rows, cols = sample_indices(m, n, np.random.default_rng(seed + m))
-    c_ref, bound = oracle.matmul_entries(a, ref_b, fmt, m, n, k, rows, cols)
-    return assert_close(c[rows, cols], c_ref, bound, f"{entry} fmt={fmt} {m}x{n}x{k} sampled")
-
-
 # ------------------------------------------------------- weight encoding --
 @pytest.mark.parametrize("fmt", [F16, Q8])
 @pytest.mark.parametrize("nk", [(1024, 1024), (6144, 2048), (2048, 6144), (151936, 2048), (4096, 11008), (3, 96)])
@@ -200,19 +181,18 @@ def test_decode_suite(fmt, nk):
 
 @pytest.mark.parametrize("nk", [(6144, 2048), (2048, 6144)])
 def test_prefill_f16_m512(nk):
+    """The f16 prefill at M = 512: every one of the 3.1 M outputs against the oracle."""
     n, k = nk
-    sampled_case("matmul", F16, 512, n, k)
+    full_case("matmul", F16, 512, n, k)
 
 
 @pytest.mark.parametrize("fmt", [Q8, Q4])
 @pytest.mark.parametrize("nk", SWEEP_SHAPES)
 @pytest.mark.parametrize("m", SWEEP_M)
 def test_quant_sweep(fmt, nk, m):
+    """The M sweep, every output against the oracle (up to 5.6 M at M = 512)."""
     n, k = nk
-    if m <= 16:
-        full_case("matmul", fmt, m, n, k)
-    else:
-        sampled_case("matmul", fmt, m, n, k)
+    full_case("matmul", fmt, m, n, k)
 
 
 # ---------------------------------------------------------- ragged / edges --
@@ -465,3 +445,135 @@ def test_every_gemm_tiling_and_split(case):
                 assert_close(c, c_ref, bound, f"plan {bm}x{bn}/{sp}")
     finally:
         wq.wq_set_gemm_plan(0, 0, 0)
+
+
+# ------------------------------------------------------------ edge blocks --
+# Hand-built blocks the quantiser never writes: zero, subnormal, negative,
+# largest-magnitude and negative-zero scales, and every int8 code -128 .. 127
+# (Q4_0: every nibble 0 .. 15).  The pages' kernels read the scale as a raw
+# half, so any finite f16 is a valid scale.  One-hot rows of A make each output
+# a single decoded weight, which every route must return bit for bit.
+Q8_EDGE_SCALES = [0x0000, 0x0001, 0x03FF, 0xC000, 0x8000, 0x3C00, 0x7BFF, 0x0400, 0x8001, 0x2E66, 0xFBFF, 0x0200]
+Q4_EDGE_SCALES = [0x0000, 0x0001, 0x03FF, 0x8400, 0xBC00, 0x3C00, 0x7BFF, 0x8001, 0xFBFF, 0x8000]
+
+
+def edge_weights(fmt, n, k, seed=0):
+    """Weight bytes [n, k/32 * bytes] of hand-built blocks: block j of row r takes
+    scale list[(r + 3j) % len] and codes that run through every value."""
+    nb = k // 32
+    r = np.arange(n)[:, None, None]
+    j = np.arange(nb)[None, :, None]
+    scales = np.array(Q8_EDGE_SCALES if fmt == Q8 else Q4_EDGE_SCALES, np.uint16)
+    sc = scales[(r[:, :, 0] + 3 * j[:, :, 0]) % len(scales)]                    # [n, nb]
+    if fmt == Q8:
+        raw = np.empty((n, nb, 34), np.uint8)
+        i = np.arange(32)[None, None, :]
+        raw[:, :, 2:] = ((7 * r + 13 * j + i + seed) % 256).astype(np.uint8)     # every code value
+    else:
+        raw = np.empty((n, nb, 18), np.uint8)
+        i = np.arange(16)[None, None, :]
+        lo, hi = (3 * r + 5 * j + i + seed) % 16, (11 * r + 7 * j + 2 * i + seed + 1) % 16
+        raw[:, :, 2:] = (lo | (hi << 4)).astype(np.uint8)
+    raw[:, :, 0] = (sc & 0xFF).astype(np.uint8)
+    raw[:, :, 1] = (sc >> 8).astype(np.uint8)
+    return raw.reshape(n, -1)
+
+
+def onehot_positions(k, rng):
+    """Columns hitting the first, second, a middle and the last block at code
+    positions 0, 1, 15, 16 and 31, and a few random columns."""
+    nb = k // 32
+    blocks = sorted({0, min(1, nb - 1), nb // 2, nb - 1})
+    pos = sorted({32 * b + i for b in blocks for i in (0, 1, 15, 16, 31)} | set(rng.integers(0, k, 6).tolist()))
+    return pos
+
+
+@pytest.mark.parametrize("fmt", [Q8, Q4])
+@pytest.mark.parametrize("k", [96, 256, 1024, 2048, 2080, 8448])
+def test_edge_blocks_every_route_bit_exact(fmt, k):
+    """Hand-built edge blocks through the GEMV (staged: K = 256, 1024, 2048; K split
+    over waves: K = 8448; plain: K = 96, 2080), the small-M kernel and the GEMM, with
+    one-hot rows of A: each output equals the oracle's decoded weight exactly."""
+    n = 37
+    raw = edge_weights(fmt, n, k)
+    w = oracle.decode(raw, fmt, n, k)
+    pos = onehot_positions(k, np.random.default_rng(k))
+    a = np.zeros((len(pos), k), np.float32)
+    a[np.arange(len(pos)), pos] = 1.0
+    want = w[:, pos].T                                        # [rows of A, n]
+    dev_b = torch.from_numpy(raw).cuda()
+    routes = ((wq.WQ_ROUTE_GEMV, "gemv"), (wq.WQ_ROUTE_SKINNY, "small-M"), (wq.WQ_ROUTE_GEMM, "gemm"))
+    try:
+        for route, name in routes:
+            wq.wq_set_forced_route(route)
+            for m0 in range(0, len(pos), 16):                 # the small-M kernel takes up to 16 rows
+                rows = slice(m0, min(len(pos), m0 + 16))
+                say(f"edge blocks fmt={fmt} k={k} route={name} rows {rows.start}..{rows.stop - 1}")
+                c = run_gpu("matmul", fmt, a[rows], dev_b, rows.stop - rows.start, n, k)
+                assert np.array_equal(c.astype(np.float64), want[rows]), f"{name} rows {rows}"
+    finally:
+        wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
+    if k in (256, 2080):
+        try:
+            for bm, bn in wq.GEMM_TILES:
+                for sp in (1, 3):
+                    say(f"edge blocks fmt={fmt} k={k} plan {bm}x{bn}/{sp}")
+                    wq.wq_set_gemm_plan(bm, bn, sp)
+                    c = run_gpu("gemm", fmt, a, dev_b, len(pos), n, k)
+                    assert np.array_equal(c.astype(np.float64), want), f"plan {bm}x{bn}/{sp}"
+        finally:
+            wq.wq_set_gemm_plan(0, 0, 0)
+
+
+@pytest.mark.parametrize("fmt", [Q8, Q4])
+def test_identity_a_edge_blocks(fmt):
+    """A = I (M = K = 256) on the edge blocks: C = W^T exactly through the GEMM and the
+    small-M kernel (16 launches of 16 rows)."""
+    n, k = 45, 256
+    raw = edge_weights(fmt, n, k, seed=5)
+    w = oracle.decode(raw, fmt, n, k)
+    dev_b = torch.from_numpy(raw).cuda()
+    try:
+        for route in (wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY):
+            wq.wq_set_forced_route(route)
+            say(f"identity a, edge blocks fmt={fmt} route={route}")
+            c = run_gpu("matmul", fmt, np.eye(k, dtype=np.float32), dev_b, k, n, k)
+            assert np.array_equal(c.astype(np.float64), w.T)
+    finally:
+        wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
+
+
+@pytest.mark.parametrize("fmt", [Q8, Q4])
+@pytest.mark.parametrize("m", [1, 3, 16])
+def test_partial_step_does_not_read_the_next_row(fmt, m):
+    """K = 2080 (one 32-column block past the last full 256-column step) with a
+    misaligned a (the small-M kernel's scalar-load variant) and b: the first eight
+    blocks of every odd row have an infinite scale, so a kernel whose partial step
+    let the next row's blocks into a row's sum would turn the even rows' outputs
+    into inf or NaN.  Even rows must match the oracle."""
+    n, k = 300, 2080
+    raw = (wqgen.q4_0_bytes(n, k, 14) if fmt == Q4 else oracle.encode(weights_f32(n, k, 14), Q8)).copy()
+    blk = 18 if fmt == Q4 else 34
+    for j in range(8):
+        raw[1::2, j * blk] = 0x00
+        raw[1::2, j * blk + 1] = 0x7C                                  # +inf scale
+    a = acts(m, k, 14)
+    c_ref, bound = oracle.matmul(a, raw, fmt, m, n, k)
+    dev = torch.from_numpy(raw.ravel()).cuda()
+    b_buf = torch.empty(dev.numel() + 2, dtype=torch.uint8, device="cuda")
+    b_buf[2:].copy_(dev)
+    a_buf = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+    a_buf[1:].copy_(torch.from_numpy(a.ravel()))
+    L = wq._lib
+    s = torch.cuda.current_stream().cuda_stream
+    for route in (wq.WQ_ROUTE_AUTO, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_GEMM):
+        say(f"partial step, next row inf, fmt={fmt} m={m} route={route}")
+        c = torch.full((m, n), float("nan"), device="cuda")
+        prev = wq.wq_set_forced_route(route)
+        try:
+            assert L.wq_matmul(a_buf.data_ptr() + 4, b_buf.data_ptr() + 2, c.data_ptr(), m, n, k, fmt, s) == wq.WQ_OK
+            torch.cuda.synchronize()
+        finally:
+            wq.wq_set_forced_route(prev)
+        got = c.cpu().numpy()
+        assert_close(got[:, 0::2], c_ref[:, 0::2], bound[:, 0::2], f"route {route} even rows")

@@ -36,6 +36,7 @@ WQ_ERR_ALIAS = 7
 WQ_ERR_ROUTE = 8
 WQ_ERR_EPILOGUE = 9
 WQ_ERR_TOPK = 10
+WQ_ERR_WORKSPACE = 11
 WQ_TOPK_MAX = 64
 WQ_ATTN_MAX_GROUP = 8
 WQ_KV_F32 = 0
@@ -78,6 +79,8 @@ def _load() -> ctypes.CDLL:
         "wq_matmul": (I, [P, P, P, I64, I64, I64, I, P]),
         "wq_matmul_ex": (I, [P, P, P, I64, I64, I64, I, I, P]),
         "wq_lm_head_topk": (I, [P, P, I64, I64, I, I, P, P, P]),
+        "wq_lm_head_topk_noalloc": (I, [P, P, I64, I64, I, I, P, P, P]),
+        "wq_noalloc_workspace_bytes": (ctypes.c_size_t, []),
         "wq_topk": (I, [P, I64, I, P, P, P]),
         "wq_decode_attention": (I, [P, P, P, P, I64, I, I, I, I, ctypes.c_float, P]),
         "wq_set_attn_partition": (I, [I64]),
@@ -235,6 +238,23 @@ def wq_lm_head_topk(a, b, n: int, k: int, fmt: int, topk: int, vals, ids, stream
     _topk_out(vals, ids, topk)
     _check(_lib.wq_lm_head_topk(_ptr(a), _ptr(b), n, k, fmt, topk, _ptr(vals), _ptr(ids), _stream(stream, vals)),
            "wq_lm_head_topk")
+
+
+def wq_lm_head_topk_noalloc(a, b, n: int, k: int, fmt: int, topk: int, vals, ids, stream=None) -> None:
+    """wq_lm_head_topk without any allocation (fixed per-GPU workspace)."""
+    if fmt in (WQ_FMT_F16, WQ_FMT_Q8_0, WQ_FMT_Q4_0) and n > 0:
+        _dtype(a, _F32, "a")
+        _dtype(b, _H if fmt == WQ_FMT_F16 else _U8, "b")
+        _need(a, 4 * k, "a")
+        if k >= 0 and (fmt == WQ_FMT_F16 or k % 32 == 0):
+            _need(b, weight_bytes(n, k, fmt), "b")
+    _topk_out(vals, ids, topk)
+    _check(_lib.wq_lm_head_topk_noalloc(_ptr(a), _ptr(b), n, k, fmt, topk, _ptr(vals), _ptr(ids),
+                                        _stream(stream, vals)), "wq_lm_head_topk_noalloc")
+
+
+def wq_noalloc_workspace_bytes() -> int:
+    return int(_lib.wq_noalloc_workspace_bytes())
 
 
 def wq_topk(logits, n: int, topk: int, vals, ids, stream=None) -> None:

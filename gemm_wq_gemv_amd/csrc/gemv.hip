@@ -843,53 +843,68 @@ hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t 
     return launch_gemv_q<QFMT_Q4_0>(a, b, c, n, k, s, epi);
 }
 
+// Scratch layout of an LM-head top-k call: the f16 K-split route keeps the n
+// logits (rounded up to 256 bytes) and kTopkGroups partial lists; the other
+// routes keep up to max_topk_lists(cus) per-wave lists and the partial lists.
+static bool lm_head_f16_logits_route(const float *a, const void *b, int fmt, int64_t n, int64_t k) {
+    return fmt != QFMT_Q8_0 && fmt != QFMT_Q4_0 && n > 0 && f16_ksplit_ok(a, static_cast<const uint16_t *>(b), k);
+}
+
+size_t lm_head_topk_scratch_bytes(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk, int cus) {
+    const size_t part = static_cast<size_t>(kTopkGroups) * topk * sizeof(TopkCand);
+    if (lm_head_f16_logits_route(a, b, fmt, n, k)) return static_cast<size_t>((n * 4 + 255) / 256 * 256) + part;
+    return static_cast<size_t>(max_topk_lists(cus)) * topk * sizeof(TopkCand) + part;
+}
+
 hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk,
-                               float *vals, uint32_t *ids, hipStream_t s) {
+                               float *vals, uint32_t *ids, hipStream_t s, void *workspace, size_t workspace_bytes) {
     if (topk < 1 || topk > kTopkMax) return hipErrorInvalidValue;
     DeviceInfo di;
     hipError_t e = device_info(&di);
     if (e != hipSuccess) return e;
-    const uint16_t *b16 = static_cast<const uint16_t *>(b);
-    // f16 rows the K-split kernel takes: its logits go to scratch and the
-    // merge reads them 64 at a time.  A per-workgroup top-k list inside that
-    // kernel would need a loop over row blocks, which costs more than the
-    // logits round trip (608 KB at N = 151936).
-    if (fmt != QFMT_Q8_0 && fmt != QFMT_Q4_0 && n > 0 && f16_ksplit_ok(a, b16, k)) {
-        ScratchLease lease;
-        void *scratch = nullptr;
-        const int64_t lbytes = (n * 4 + 255) / 256 * 256;
-        e = lease.acquire(static_cast<size_t>(lbytes) + static_cast<size_t>(kTopkGroups) * topk * sizeof(TopkCand),
-                          s, &scratch);
+    const size_t need = lm_head_topk_scratch_bytes(a, b, fmt, n, k, topk, di.cus);
+    ScratchLease lease;
+    void *scratch = workspace;
+    if (scratch) {
+        if (workspace_bytes < need) return hipErrorInvalidValue;
+    } else {
+        e = lease.acquire(need, s, &scratch);
         if (e != hipSuccess) return e;
+    }
+    const uint16_t *b16 = static_cast<const uint16_t *>(b);
+    if (lm_head_f16_logits_route(a, b, fmt, n, k)) {
+        // f16 rows the K-split kernel takes: its logits go to scratch and the
+        // merge reads them 64 at a time.  A per-workgroup top-k list inside that
+        // kernel would need a loop over row blocks, which costs more than the
+        // logits round trip (608 KB at N = 151936).
+        const int64_t lbytes = (n * 4 + 255) / 256 * 256;
         float *logits = static_cast<float *>(scratch);
         TopkCand *partial = reinterpret_cast<TopkCand *>(static_cast<char *>(scratch) + lbytes);
         e = f16_ksplit<kModeStore>(a, b16, logits, n, k, s, 0);
         if (e == hipSuccess) e = launch_topk_merge(nullptr, 0, logits, n, topk, partial, vals, ids, s);
-        const hipError_t er = lease.release();
-        return e != hipSuccess ? e : er;
+    } else {
+        const int64_t cap = max_topk_lists(di.cus);
+        TopkCand *cand = static_cast<TopkCand *>(scratch);
+        TopkCand *partial = cand + cap * topk;
+        float *out = reinterpret_cast<float *>(cand);
+        // Every top-k launch below writes at most `cap` lists: balanced_workers never
+        // exceeds its cap (16 waves per CU, rounded up to whole workgroups of 4, or
+        // 12 single-wave workgroups per CU for the staged kernel).  Every list the
+        // merge reads is written first by the same call, so the buffer needs no
+        // clearing.  n == 0: no GEMV, and the merge of zero lists writes sentinels.
+        int64_t lists = 0;
+        if (n == 0)
+            e = hipSuccess;
+        else if (fmt == QFMT_Q8_0)
+            e = gemv_q_rows<QFMT_Q8_0, kModeTopk>(a, static_cast<const uint8_t *>(b), out, n, k, s, di.cus, topk,
+                                                  &lists);
+        else if (fmt == QFMT_Q4_0)
+            e = gemv_q_rows<QFMT_Q4_0, kModeTopk>(a, static_cast<const uint8_t *>(b), out, n, k, s, di.cus, topk,
+                                                  &lists);
+        else
+            e = gemv_f16_rows<kModeTopk>(a, b16, out, n, k, s, di.cus, topk, &lists);
+        if (e == hipSuccess) e = launch_topk_merge(cand, lists, nullptr, 0, topk, partial, vals, ids, s);
     }
-    const int64_t cap = max_topk_lists(di.cus);
-    ScratchLease lease;
-    void *scratch = nullptr;
-    e = lease.acquire(static_cast<size_t>(cap + kTopkGroups) * topk * sizeof(TopkCand), s, &scratch);
-    if (e != hipSuccess) return e;
-    TopkCand *cand = static_cast<TopkCand *>(scratch);
-    TopkCand *partial = cand + cap * topk;
-    float *out = reinterpret_cast<float *>(cand);
-    // Every top-k launch below writes at most `cap` lists: balanced_workers never
-    // exceeds its cap (16 waves per CU, rounded up to whole workgroups of 4, or
-    // 12 single-wave workgroups per CU for the staged kernel).
-    // n == 0: no GEMV, and the merge of zero lists writes sentinels.
-    int64_t lists = 0;
-    if (n == 0)
-        e = hipSuccess;
-    else if (fmt == QFMT_Q8_0)
-        e = gemv_q_rows<QFMT_Q8_0, kModeTopk>(a, static_cast<const uint8_t *>(b), out, n, k, s, di.cus, topk, &lists);
-    else if (fmt == QFMT_Q4_0)
-        e = gemv_q_rows<QFMT_Q4_0, kModeTopk>(a, static_cast<const uint8_t *>(b), out, n, k, s, di.cus, topk, &lists);
-    else
-        e = gemv_f16_rows<kModeTopk>(a, b16, out, n, k, s, di.cus, topk, &lists);
-    if (e == hipSuccess) e = launch_topk_merge(cand, lists, nullptr, 0, topk, partial, vals, ids, s);
     const hipError_t er = lease.release();
     return e != hipSuccess ? e : er;
 }

@@ -296,8 +296,17 @@ hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t 
 // Top-k of the LM-head logits w . a (w [n, k] in format fmt, one token):
 // the GEMV keeps a top-k list per wave, then launch_topk_merge reduces the
 // lists.  vals / ids: topk entries in rank order (1 <= topk <= kTopkMax).
+// workspace: nullptr (scratch from the per-stream cache) or a device buffer of
+// at least lm_head_topk_scratch_bytes(...) bytes that the call uses instead.
 hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk,
-                               float *vals, uint32_t *ids, hipStream_t s);
+                               float *vals, uint32_t *ids, hipStream_t s, void *workspace = nullptr,
+                               size_t workspace_bytes = 0);
+// The fixed workspace of the allocation-free entry point (wqmm_api.hip): its
+// size, and its device address on the current device.
+constexpr size_t kNoAllocBytes = size_t(4) << 20;
+hipError_t noalloc_workspace(void **ptr);
+// Scratch bytes launch_lm_head_topk needs for these arguments on `cus` CUs.
+size_t lm_head_topk_scratch_bytes(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk, int cus);
 // Merge of candidate lists into the final top-k.  Lists are either `lists`
 // arrays of topk TopkCand (cand) or, with cand == nullptr, a logits vector
 // of n values cut into lists of 64 consecutive ids.  Two kernels: up to

@@ -131,6 +131,35 @@ hipError_t ScratchLease::release() {
 
 ScratchLease::~ScratchLease() { (void)release(); }
 
+// The allocation-free workspace: one fixed array per GPU, in device memory the
+// code object brings along when the library is loaded on that GPU.  Host code
+// never uses the array's name as an address: it takes the device address with
+// hipGetSymbolAddress once per device (that device current) and passes that.
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+namespace {
+std::once_flag g_noalloc_once[kMaxDevices];
+void *g_noalloc_ptr[kMaxDevices];
+hipError_t g_noalloc_err[kMaxDevices];
+}  // namespace
+
+// Device address of the current device's workspace (looked up on its first use).
+hipError_t noalloc_workspace(void **ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_noalloc_once[dev], [dev] {
+        void *p = nullptr;
+        g_noalloc_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_noalloc_ptr[dev] = g_noalloc_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_noalloc_err[dev] != hipSuccess) return g_noalloc_err[dev];
+    *ptr = g_noalloc_ptr[dev];
+    return *ptr ? hipSuccess : hipErrorInvalidSymbol;
+}
+
 }  // namespace wq
 
 namespace {
@@ -273,6 +302,7 @@ const char *wq_status_str(int status) {
         case WQ_ERR_ROUTE: return "unknown route";
         case WQ_ERR_EPILOGUE: return "unknown epilogue";
         case WQ_ERR_TOPK: return "top-k count outside 1 .. WQ_TOPK_MAX";
+        case WQ_ERR_WORKSPACE: return "request needs more than the fixed no-allocation workspace";
         default: return "unknown status";
     }
 }
@@ -335,8 +365,11 @@ int wq_matmul_ex(const float *a, const void *b, float *c, int64_t m, int64_t n, 
     return run_routed(a, b, c, m, n, k, fmt, epi, static_cast<hipStream_t>(stream));
 }
 
-int wq_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt, int topk, float *vals,
-                    uint32_t *ids, void *stream) {
+}  // extern "C"
+
+namespace {
+int validate_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt, int topk,
+                          const float *vals, const uint32_t *ids) {
     if (!known_format(fmt)) return WQ_ERR_FORMAT;
     if (n < 0 || k < 0) return WQ_ERR_SHAPE;
     if (topk < 1 || topk > WQ_TOPK_MAX) return WQ_ERR_TOPK;
@@ -355,11 +388,36 @@ int wq_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt
     if (overlaps(vals, o_bytes, ids, o_bytes)) return WQ_ERR_ALIAS;
     for (const void *o : {static_cast<const void *>(vals), static_cast<const void *>(ids)})
         if (overlaps(o, o_bytes, a, a_bytes) || overlaps(o, o_bytes, b, b_bytes)) return WQ_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    return WQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int wq_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt, int topk, float *vals,
+                    uint32_t *ids, void *stream) {
+    const int st = validate_lm_head_topk(a, b, n, k, fmt, topk, vals, ids);
+    if (st != WQ_OK) return st;
     // n == 0 or K == 0 still go through the kernels: the lists are then all
     // sentinels (n == 0) or all logits are 0 (K == 0, f16).
-    return status_of(wq::launch_lm_head_topk(a, b, fmt, n, k, topk, vals, ids, s));
+    return status_of(wq::launch_lm_head_topk(a, b, fmt, n, k, topk, vals, ids, static_cast<hipStream_t>(stream)));
 }
+
+int wq_lm_head_topk_noalloc(const float *a, const void *b, int64_t n, int64_t k, int fmt, int topk, float *vals,
+                            uint32_t *ids, void *stream) {
+    const int st = validate_lm_head_topk(a, b, n, k, fmt, topk, vals, ids);
+    if (st != WQ_OK) return st;
+    wq::DeviceInfo di;
+    if (wq::device_info(&di) != hipSuccess) return WQ_ERR_LAUNCH;
+    const size_t need = wq::lm_head_topk_scratch_bytes(a, b, fmt, n, k, topk, di.cus);
+    if (need > wq::kNoAllocBytes) return WQ_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (wq::noalloc_workspace(&ws) != hipSuccess) return WQ_ERR_LAUNCH;
+    return status_of(wq::launch_lm_head_topk(a, b, fmt, n, k, topk, vals, ids, static_cast<hipStream_t>(stream), ws,
+                                             wq::kNoAllocBytes));
+}
+
+size_t wq_noalloc_workspace_bytes(void) { return wq::kNoAllocBytes; }
 
 int wq_topk(const float *logits, int64_t n, int topk, float *vals, uint32_t *ids, void *stream) {
     if (n < 0) return WQ_ERR_SHAPE;

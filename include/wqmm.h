@@ -59,6 +59,7 @@
 #ifndef WQMM_H
 #define WQMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -84,7 +85,8 @@ typedef enum wq_status {
     WQ_ERR_ALIAS = 7,   /* c overlaps a or b */
     WQ_ERR_ROUTE = 8,   /* not a wq_route value */
     WQ_ERR_EPILOGUE = 9, /* not a wq_epilogue value */
-    WQ_ERR_TOPK = 10     /* top-k count outside 1 .. WQ_TOPK_MAX */
+    WQ_ERR_TOPK = 10,    /* top-k count outside 1 .. WQ_TOPK_MAX */
+    WQ_ERR_WORKSPACE = 11 /* needs more scratch than the fixed no-allocation workspace */
 } wq_status;
 
 /* Kernel families wq_matmul can route to. */
@@ -200,6 +202,24 @@ int wq_matmul_ex(const float *a, const void *b, float *c, int64_t m, int64_t n, 
  * n == 0 gives sentinels only; K == 0 (f16) makes every logit 0. */
 int wq_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt, int topk, float *vals,
                     uint32_t *ids, void *stream);
+
+/* wq_lm_head_topk for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and the same result, bit for bit, but the scratch lives in a fixed
+ * array of wq_noalloc_workspace_bytes() (4 MiB) that the library's code object
+ * holds in every GPU's memory from load until the process ends; the call itself
+ * allocates and frees nothing.  It returns WQ_ERR_WORKSPACE (before anything is
+ * enqueued) when the call needs more than that: (n * 4 rounded up to 256) +
+ * 64 * topk * 8 bytes for f16 weights on the K-split route, else (16 * CUs + 68)
+ * * topk * 8 bytes -- at most 2.2 MB on MI355X, and 0.6 MB for the f16 LM head
+ * at vocab 151936.  Every list the merge reads is written earlier in the same
+ * call, so the array needs no clearing.  All calls on one GPU share its array:
+ * calls that may overlap in time on one GPU (different streams, or several host
+ * threads without ordering) race; calls on one stream are ordered and safe. */
+int wq_lm_head_topk_noalloc(const float *a, const void *b, int64_t n, int64_t k, int fmt, int topk, float *vals,
+                            uint32_t *ids, void *stream);
+/* Size of the fixed workspace of the allocation-free entry point (bytes). */
+size_t wq_noalloc_workspace_bytes(void);
 
 /* Top-k of an existing f32 logits vector [n] (device): the same selection
  * over logits a caller already has.  Passage: dispatch_topk_enc,

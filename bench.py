@@ -233,8 +233,8 @@ def time_launches(torch, fn, iters, warmup):
 
 def read_ceiling(torch, wq, sizes, iters, warmup):
     """Plain-read time of each byte size in `sizes` (label -> bytes): the read
-    probe over rotated copies totalling >= 1 GiB, best of its 2, 4 and 8 chunks
-    per lane."""
+    probe over rotated copies totalling >= 1 GiB, best of 1, 2, 4 and 8 slabs of
+    4 KiB per workgroup."""
     res = {}
     for label, nbytes in sizes.items():
         nb = (nbytes + 15) // 16 * 16
@@ -244,12 +244,12 @@ def read_ceiling(torch, wq, sizes, iters, warmup):
             b.fill_(1)
         out = torch.empty((nb + 1023) // 1024, dtype=torch.int32, device="cuda")
         best = None
-        for variant in (1, 2, 3):
+        for variant in (0, 1, 2, 3):
             t = time_launches(torch, lambda i: wq.wq_read_probe(bufs[i % copies], nb, out, variant), iters, warmup)
             if best is None or t < best[0]:
                 best = (t, variant)
         res[label] = {"bytes": nbytes, "us": round(best[0] * 1e6, 2), "GB/s": round(nbytes / best[0] / 1e9, 1),
-                      "chunks_per_lane": 1 << best[1]}
+                      "slabs_per_workgroup": 1 << best[1]}
         del bufs, out
         torch.cuda.empty_cache()
     return res

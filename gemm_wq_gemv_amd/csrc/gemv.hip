@@ -46,6 +46,7 @@
 #include "wq_internal.h"
 
 #include <algorithm>
+#include <cstdlib>
 
 namespace wq {
 namespace {
@@ -187,28 +188,6 @@ struct QB {
 constexpr int kQ8BlockBytes = QB<QFMT_Q8_0>::kBytes;
 constexpr int kQ4BlockBytes = QB<QFMT_Q4_0>::kBytes;
 
-// A block starts at an even LDS byte offset pb (rows are whole 16-byte chunks
-// and blocks are 34 or 18 bytes long), so it lies in the dword-aligned window
-// starting at pb & ~3.  The window is read with aligned 32-bit LDS loads
-// (ds_read2_b32), which measured faster on MI355X than 16-byte reads at
-// 2-byte aligned addresses; for a block at pb = 2 (mod 4) everything sits two
-// bytes higher, and one v_perm_b32 per code dword, with a per-lane selector,
-// realigns it.  Returns the scale bits and fills codes[0..NW).
-template <int NW>
-__device__ __forceinline__ uint32_t block_window(const uint8_t *stage, int pb, uint32_t (&codes)[NW]) {
-    const uint32_t *w32 = reinterpret_cast<const uint32_t *>(stage + (pb & ~3));
-    uint32_t w[NW + 1];
-#pragma unroll
-    for (int i = 0; i <= NW; ++i) w[i] = w32[i];
-    const bool hi = (pb & 2) != 0;
-    // v_perm_b32(x, y, sel): byte b of the result is byte sel.b of the pair
-    // (y = bytes 0-3, x = bytes 4-7).  Codes start at window byte 2 (hi: 4).
-    const uint32_t sel = hi ? 0x07060504u : 0x05040302u;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) codes[i] = __builtin_amdgcn_perm(w[i + 1], w[i], sel);
-    return hi ? w[0] >> 16 : w[0] & 0xffffu;
-}
-
 // Dot product of one Q8_0 block held in LDS at byte offset pb with the 32
 // activations av[0..31]: returns d * sum_i q_i * av[i].
 __device__ __forceinline__ float q8_block_dot(const uint8_t *stage, int pb, const float *av) {
@@ -324,21 +303,6 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
     const int jl = lane % LPR;
     const int rsub = lane / LPR;
 
-    float av[J][32];
-#pragma unroll
-    for (int t = 0; t < J; ++t) {
-        const int j = jl + LPR * t;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j < nb) v = reinterpret_cast<const float4 *>(a + 32 * j)[i];
-            av[t][4 * i + 0] = v.x;
-            av[t][4 * i + 1] = v.y;
-            av[t][4 * i + 2] = v.z;
-            av[t][4 * i + 3] = v.w;
-        }
-    }
-    wait_vmem_all();
 
     // Staging guards are wave-uniform: a whole 1 KiB load (or LDS write) is
     // skipped when the pass ends before it; inside the last one, lanes past
@@ -371,7 +335,31 @@ __global__ __launch_bounds__(64) void gemv_q_staged(const float *__restrict__ a,
     WaveTopk top;
     if constexpr (MODE == kModeTopk) top.init();
     int64_t p = blockIdx.x;
-    if (p < passes) fetch(p);
+    // Waves that walk several passes issue their first pass's weights before
+    // the activation slices (measured on MI355X: Q8_0 LM head 58.3 -> 56.9 us);
+    // single-pass waves (small matrices) load the activations first (gate/up
+    // 6144 x 2048: 6.7 -> 5.9 us).
+    const bool weights_first = passes > static_cast<int64_t>(gridDim.x);
+    if (weights_first && p < passes) fetch(p);
+    float av[J][32];
+#pragma unroll
+    for (int t = 0; t < J; ++t) {
+        const int j = jl + LPR * t;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j < nb) v = reinterpret_cast<const float4 *>(a + 32 * j)[i];
+            av[t][4 * i + 0] = v.x;
+            av[t][4 * i + 1] = v.y;
+            av[t][4 * i + 2] = v.z;
+            av[t][4 * i + 3] = v.w;
+        }
+    }
+    if (!weights_first) {
+        wait_vmem_all();
+        if (p < passes) fetch(p);
+    }
+    wait_vmem_all();
     for (; p < passes; p += gridDim.x) {
         const int64_t row0 = p * HS;  // first output of the pass
         const int rows = static_cast<int>(min<int64_t>(HS, n - row0));
@@ -580,6 +568,22 @@ hipError_t glu_two_pass(float *c, int64_t n, hipStream_t s, Gemv2n &&gemv2n) {
     return e != hipSuccess ? e : er;
 }
 
+// Tuning hooks (unset or 0 = automatic): WQ_GEMV_SL forces the rows per lane
+// group and pass of the staged quantized GEMV (1, 2 or 4), WQ_GEMV_SROWS the rows
+// per workgroup of the K-split quantized GEMV (1, 2 or 4).
+int env_int(const char *name) {
+    const char *e = std::getenv(name);
+    return e ? std::atoi(e) : 0;
+}
+int forced_sl() {
+    static const int v = env_int("WQ_GEMV_SL");
+    return v;
+}
+int forced_srows() {
+    static const int v = env_int("WQ_GEMV_SROWS");
+    return v;
+}
+
 // Launch helpers.  aux: the residual flag (kModeStore) or k (kModeTopk);
 // *lists (kModeTopk): the number of per-wave lists the launch writes.
 
@@ -659,7 +663,14 @@ hipError_t run_q_staged(const float *a, const uint8_t *b, float *c, int64_t n, i
     const int64_t s_fill = std::max<int64_t>(1, n / (4LL * cus));
     // At most 4 rows per lane group and pass: with 12 waves per CU that was
     // measured faster than 8 or 16 rows for both formats at K = 2048.
-    const int64_t sl_max = std::max<int64_t>(1, std::min<int64_t>(4, std::min(s_fit, s_fill) / RPL));
+    int64_t sl_max = std::max<int64_t>(1, std::min<int64_t>(4, std::min(s_fit, s_fill) / RPL));
+    // Rows of 128 or more blocks (K >= 4096) with whole rows per lane group: one
+    // row per pass, so a wave walks several passes with the next one in flight
+    // (measured on MI355X at 11008 x 4096: Q8_0 16.4 -> 14.1 us, Q4_0 14.1 ->
+    // 12.9 us; four rows per pass need 17 KiB of LDS per wave, so only 9 waves
+    // fit on a CU and the 2752 passes take two rounds).
+    if (MODE == kModeStore && LPR == kWave && k >= 4096) sl_max = 1;
+    if (forced_sl() > 0) sl_max = forced_sl();
     if constexpr (J <= 2)
         if (sl_max >= 4 && 4 * RPL <= s_fit)
             return run_q_staged_sl<FMT, J, LPR, 4, MODE>(a, b, c, n, k, s, cus, aux, lists);
@@ -717,6 +728,7 @@ hipError_t run_q_ksplit(const float *a, const uint8_t *b, float *c, int64_t n, i
     const size_t slice = static_cast<size_t>(kWave) * QB<FMT>::kBytes;
     int srows = 4;
     while (srows > 1 && static_cast<size_t>(kw) * srows * slice > 65536) srows /= 2;
+    if (forced_srows() > 0) srows = forced_srows();
     const int64_t blocks = (n + srows - 1) / srows;
     const size_t lds = static_cast<size_t>(kw) * srows * slice;
     if (trace_enabled())

@@ -101,6 +101,28 @@ __device__ __forceinline__ float rows_sum(const float (&v)[N], int g) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
+// A block starts at an even LDS byte offset pb (rows are whole 16-byte chunks
+// and blocks are 34 or 18 bytes long), so it lies in the dword-aligned window
+// starting at pb & ~3.  The window is read with aligned 32-bit LDS loads
+// (ds_read2_b32), which measured faster on MI355X than 16-byte reads at
+// 2-byte aligned addresses; for a block at pb = 2 (mod 4) everything sits two
+// bytes higher, and one v_perm_b32 per code dword, with a per-lane selector,
+// realigns it.  Returns the scale bits and fills codes[0..NW).
+template <int NW>
+__device__ __forceinline__ uint32_t block_window(const uint8_t *stage, int pb, uint32_t (&codes)[NW]) {
+    const uint32_t *w32 = reinterpret_cast<const uint32_t *>(stage + (pb & ~3));
+    uint32_t w[NW + 1];
+#pragma unroll
+    for (int i = 0; i <= NW; ++i) w[i] = w32[i];
+    const bool hi = (pb & 2) != 0;
+    // v_perm_b32(x, y, sel): byte b of the result is byte sel.b of the pair
+    // (y = bytes 0-3, x = bytes 4-7).  Codes start at window byte 2 (hi: 4).
+    const uint32_t sel = hi ? 0x07060504u : 0x05040302u;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) codes[i] = __builtin_amdgcn_perm(w[i + 1], w[i], sel);
+    return hi ? w[0] >> 16 : w[0] & 0xffffu;
+}
+
 // SiLU as on the pages' silu_mul kernel: x / (1 + e^-x), in f32.
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
@@ -327,6 +349,12 @@ void set_attn_partition_override(int64_t tokens);
 // n = output columns; with kEpiGlu the weights have 2n rows.
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,
                        int64_t k, hipStream_t s, int epi = kEpiNone);
+// Small-M product for Q8_0 / Q4_0 weights with K % 256 == 0 and 16-byte
+// aligned a and b (smallm_ok), 1 <= M <= 16; n = output columns (2n weight
+// rows with kEpiGlu).
+bool smallm_ok(const float *a, const void *b, int fmt, int64_t m, int64_t k);
+hipError_t launch_smallm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
+                         hipStream_t s, int epi = kEpiNone);
 // Small-M weight-streaming product (M <= 16 rows of A per launch).
 hipError_t launch_skinny(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
                          hipStream_t s, int epi = kEpiNone);

@@ -213,13 +213,20 @@ int validate(const float *a, const void *b, const float *c, int64_t m, int64_t n
 
 int status_of(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_LAUNCH; }
 
-// M == 1: the decode GEMV; 2 <= M <= 8 (f16) or 4 (Q8_0): the weight-streaming
-// small-M kernel, which is faster than the tiled GEMM there (measured on
-// MI355X at N, K in {4096, 11008}); larger M: the LDS-tiled GEMM.
+// M == 1: the decode GEMV; 2 <= M <= 8: the weight-streaming small-M kernels
+// (quantized weights with K % 256 == 0 and 16-byte aligned operands take the
+// staged one); larger M: the LDS-tiled GEMM.  The crossovers are measured on
+// MI355X at (N, K) = (11008, 4096) and (4096, 11008): for Q8_0 the staged
+// small-M kernel takes 18-20 us at M = 2, 20-22 us at M = 4 and 25-29 us at
+// M = 8 against 30-31 us for the GEMM at M = 8..16; the general small-M kernel
+// beats the GEMM up to M = 4 for quantized rows it has to take (other K), and
+// up to M = 8 for f16.
 constexpr int64_t kSkinnyRows = 16;  // rows of A per small-M launch
-int auto_route(int64_t m, int fmt) {
+int auto_route(int64_t m, int64_t k, int fmt) {
     if (m <= 1) return WQ_ROUTE_GEMV;
-    return m <= (fmt == WQ_FMT_F16 ? 8 : 4) ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;  // Q4_0 as Q8_0
+    if (fmt == WQ_FMT_F16) return m <= 8 ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;
+    const bool staged = k % 256 == 0;  // alignment is checked at launch; the route only depends on shapes
+    return m <= (staged ? 8 : 4) ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;  // Q4_0 as Q8_0
 }
 bool known_route(int r) { return r == WQ_ROUTE_GEMV || r == WQ_ROUTE_GEMM || r == WQ_ROUTE_SKINNY; }
 
@@ -254,12 +261,17 @@ int run_gemm(const float *a, const void *b, float *c, int64_t m, int64_t n, int6
     return WQ_OK;
 }
 
-// One small-M launch per block of up to kSkinnyRows rows of A.
+// One small-M launch per block of up to kSkinnyRows rows of A: the staged
+// quantized kernel where it applies (K % 256 == 0, 16-byte aligned operands),
+// else the general one.
 int run_skinny(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
                int epi) {
     for (int64_t i = 0; i < m; i += kSkinnyRows) {
         const int64_t rows = m - i < kSkinnyRows ? m - i : kSkinnyRows;
-        hipError_t e = wq::launch_skinny(a + i * k, b, fmt, c + i * n, rows, n, k, s, kernel_epi(epi));
+        const float *ai = a + i * k;
+        hipError_t e = wq::smallm_ok(ai, b, fmt, rows, k)
+                           ? wq::launch_smallm(ai, b, fmt, c + i * n, rows, n, k, s, kernel_epi(epi))
+                           : wq::launch_skinny(ai, b, fmt, c + i * n, rows, n, k, s, kernel_epi(epi));
         if (e != hipSuccess) return WQ_ERR_LAUNCH;
         wq::g_route_count[WQ_ROUTE_SKINNY].fetch_add(1, std::memory_order_relaxed);
     }
@@ -277,7 +289,7 @@ int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, in
                hipStream_t s) {
     if (k == 0) return epi == WQ_EPI_RESIDUAL ? WQ_OK : run_zero(c, m, n, s);  // silu(0) * 0 = 0
     int route = wq::g_forced_route.load(std::memory_order_relaxed);
-    if (route == WQ_ROUTE_AUTO) route = auto_route(m, fmt);
+    if (route == WQ_ROUTE_AUTO) route = auto_route(m, k, fmt);
     if (route == WQ_ROUTE_GEMV) return run_gemv(a, b, c, m, n, k, fmt, s, epi);
     if (route == WQ_ROUTE_SKINNY) return run_skinny(a, b, c, m, n, k, fmt, s, epi);
     return run_gemm(a, b, c, m, n, k, fmt, s, epi);
@@ -498,7 +510,7 @@ int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt) {
     if (!known_format(fmt)) return -WQ_ERR_FORMAT;
     if (m < 0 || n < 0 || k < 0) return -WQ_ERR_SHAPE;
     if (fmt != WQ_FMT_F16 && m > 0 && n > 0 && (k == 0 || k % 32 != 0)) return -WQ_ERR_K;
-    return auto_route(m, fmt);
+    return auto_route(m, k, fmt);
 }
 
 int wq_gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits) {

@@ -121,11 +121,12 @@ int wq_gemm_q4_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t 
                  void *stream);
 
 /* M-routed product for either format (fmt is a wq_format).  M == 1 takes the
- * GEMV; 2 <= M <= 8 (f16) or 2 <= M <= 4 (Q8_0, Q4_0) the small-M weight-streaming
- * kernel; larger M the tiled GEMM, unless a route is forced
- * (wq_set_forced_route).  The small-M kernel reads every weight once per 16
- * rows of A with fp32 matrix-core accumulation; when it splits K it uses the
- * same scratch as the GEMM (splits*M*N*4 bytes).  Passage: dispatch_gemm_q8
+ * GEMV; 2 <= M <= 8 the small-M weight-streaming kernels (for Q8_0 / Q4_0 with
+ * K % 256 != 0 only up to M == 4); larger M the tiled GEMM, unless a route is
+ * forced (wq_set_forced_route).  The small-M kernels read every weight once per
+ * 16 rows of A with fp32 matrix-core accumulation; when they split K (and for
+ * the SwiGLU epilogue on the quantized one) they use the same scratch as the
+ * GEMM (splits*M*N*4 bytes, 2n columns for SwiGLU).  Passage: dispatch_gemm_q8
  * and dispatch_gemm, lattice-inference 0.9.0 dispatch.rs (M == 1 decode,
  * M > 1 batched product). */
 int wq_matmul(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt,
@@ -285,9 +286,10 @@ int wq_quantize_q8_0(const float *w, uint8_t *out, int64_t count, void *stream);
 /* Measurement hook: the achievable-read ceiling.  Reads `bytes` bytes at p
  * (device, 16-byte aligned, bytes % 16 == 0, else WQ_ERR_ALIGN / WQ_ERR_SHAPE)
  * once with 128-bit non-temporal loads -- the loads the GEMVs stream weights
- * with -- and writes an XOR checksum per wave to out (device, 4-byte aligned,
- * room for ceil(bytes / 1024) uint32).  variant 0..3: 1, 2, 4 or 8 chunks of
- * 16 bytes per lane and workgroup of 256 lanes.  It computes nothing of the
+ * with -- in workgroups of 256 lanes that each read 1, 2, 4 or 8 slabs of
+ * 4 KiB (variant 0..3).  out (device, 4-byte aligned, room for
+ * ceil(bytes / 1024) uint32) only receives a value when a workgroup's XOR
+ * checksum hits a fixed pattern, so the loads are kept.  It computes nothing of the
  * product; the benchmark times it to report each bandwidth-bound kernel against
  * a plain read of the same bytes as well as against the HBM peak. */
 int wq_read_probe(const void *p, int64_t bytes, uint32_t *out, int variant, void *stream);

@@ -189,13 +189,15 @@ def test_decode_attention_validation():
 
 
 def test_routing_rule():
+    """M = 1: GEMV; 2..8: small-M (quantized rows with K % 256 != 0: 2..4); more: GEMM."""
     for fmt in (wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0):
-        assert wq.wq_route_for(1, 4096, 4096, fmt) == wq.WQ_ROUTE_GEMV
-        top = 8 if fmt == wq.WQ_FMT_F16 else 4
-        for m in range(2, top + 1):
-            assert wq.wq_route_for(m, 4096, 4096, fmt) == wq.WQ_ROUTE_SKINNY
-        for m in (top + 1, 16, 17, 64, 512):
-            assert wq.wq_route_for(m, 4096, 4096, fmt) == wq.WQ_ROUTE_GEMM
+        for k in (4096, 4128):
+            assert wq.wq_route_for(1, 4096, k, fmt) == wq.WQ_ROUTE_GEMV
+            top = 8 if fmt == wq.WQ_FMT_F16 or k % 256 == 0 else 4
+            for m in range(2, top + 1):
+                assert wq.wq_route_for(m, 4096, k, fmt) == wq.WQ_ROUTE_SKINNY
+            for m in (top + 1, 16, 17, 64, 512):
+                assert wq.wq_route_for(m, 4096, k, fmt) == wq.WQ_ROUTE_GEMM
     assert wq.wq_route_for(2, 8, 33, wq.WQ_FMT_Q8_0) == -wq.WQ_ERR_K
     assert wq.wq_route_for(2, 8, 48, wq.WQ_FMT_Q4_0) == -wq.WQ_ERR_K
     assert wq.wq_route_for(2, 8, 32, 5) == -wq.WQ_ERR_FORMAT

@@ -403,9 +403,14 @@ def test_nondefault_stream():
         assert_close(c, c_ref, bound, f"stream m={m}")
 
 
+# Quantized shapes with K % 256 == 0 take the staged small-M kernel: one step
+# (K = 256, 512), a partial last step (K = 768: 16 + 8 blocks, K = 8448), ragged
+# row tiles (N = 37, 300, 4099) and K split across workgroups (small N).
 SKINNY_SHAPES = {F16: [(1, 8), (37, 1000), (300, 2048), (4099, 136), (19, 33), (64, 1001)],
-                 Q8: [(1, 32), (37, 992), (300, 2080), (4099, 160), (64, 4096)],
-                 Q4: [(1, 32), (37, 992), (300, 2080), (4099, 160), (64, 4096)]}
+                 Q8: [(1, 32), (37, 992), (300, 2080), (4099, 160), (64, 4096), (37, 512), (300, 768),
+                      (4099, 256), (70, 8448), (1000, 2048)],
+                 Q4: [(1, 32), (37, 992), (300, 2080), (4099, 160), (64, 4096), (37, 512), (300, 768),
+                      (4099, 256), (70, 8448), (1000, 2048)]}
 
 
 @pytest.mark.parametrize("fmt", ALL)

@@ -97,9 +97,136 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--no-secondary", action="store_true", help="headline suite only")
-    p.add_argument("--only", choices=["f16", "q8", "q4", "prefill", "sweep", "epi", "topk", "attn"], default=None,
-                   help="run one workload only (for profiling); prints no headline line")
+    p.add_argument("--only", choices=["f16", "q8", "q4", "prefill", "sweep", "epi", "topk", "attn", "counters"],
+                   default=None, help="run one workload only (for profiling); prints no headline line")
+    p.add_argument("--summarize", nargs="+", metavar="CSV", default=None,
+                   help="print per-kernel medians (a rocprofv3 kernel_trace.csv) or counter tables "
+                        "(counter_collection.csv files, with the kernel_trace.csv of the same runs) and exit")
     return p.parse_args()
+
+
+# ------------------------------------------------------------ profiling aids --
+# COUNTER_WORKLOAD: (label, launcher) pairs run by `--only counters`, a fixed
+# set of launches of every kernel family whose counters the profiles summarise,
+# each on weights rotated over >= 1 GiB, plus a 1 GiB device copy whose
+# FETCH_SIZE / WRITE_SIZE calibrate the byte counters.
+COUNTER_REPEAT = 12
+
+
+def counter_workload(torch, wq, wqgen, seed):
+    F16, Q8 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0
+
+    def rotated(n, k, fmt):
+        if fmt == F16:
+            b0 = wq.pack_f16(torch.from_numpy(wqgen.weights(n, k, seed)).cuda())
+        else:
+            b0 = wq.quantize_q8_0(torch.from_numpy(wqgen.weights(n, k, seed)).cuda())
+        nb = wq.weight_bytes(n, k, fmt)
+        return [b0] + [b0.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / nb)) - 1)]
+
+    def product(label, m, n, k, fmt, route=wq.WQ_ROUTE_AUTO):
+        bs = rotated(n, k, fmt)
+        a = torch.from_numpy(wqgen.activations(m, k, seed)).cuda()
+        c = torch.empty((m, n), device="cuda")
+        log(f"counters: {label}")
+        prev = wq.wq_set_forced_route(route)
+        for i in range(COUNTER_REPEAT):
+            wq.wq_matmul(a, bs[i % len(bs)], c, m, n, k, fmt)
+        torch.cuda.synchronize()
+        wq.wq_set_forced_route(prev)
+        del bs
+
+    nb = 1 << 30
+    src = torch.empty(nb // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    log("counters: 1 GiB device copy (byte-counter calibration)")
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    product("f16 LM head 151936x2048", 1, 151936, 2048, F16)
+    product("Q8_0 LM head 151936x2048", 1, 151936, 2048, Q8)
+    product("Q8_0 GEMV 4096x11008 (K split)", 1, 4096, 11008, Q8)
+    product("Q8_0 GEMV 11008x4096 (staged)", 1, 11008, 4096, Q8)
+    product("Q8_0 small-M 2x11008x4096", 2, 11008, 4096, Q8)
+    product("Q8_0 small-M 8x4096x11008", 8, 4096, 11008, Q8)
+    product("f16 small-M 4x11008x4096", 4, 11008, 4096, F16)
+    product("Q8_0 GEMM 16x11008x4096", 16, 11008, 4096, Q8)
+    product("f16 GEMM 512x6144x2048", 512, 6144, 2048, F16)
+    for fmt, key in ((F16, "f16"), (Q8, "Q8_0")):
+        bs = rotated(151936, 2048, fmt)
+        a = torch.from_numpy(wqgen.activations(1, 2048, seed)).cuda()
+        vals = torch.empty(50, device="cuda")
+        ids = torch.empty(50, dtype=torch.int32, device="cuda")
+        log(f"counters: {key} LM-head top-50")
+        for i in range(COUNTER_REPEAT):
+            wq.wq_lm_head_topk(a, bs[i % len(bs)], 151936, 2048, fmt, 50, vals, ids)
+        torch.cuda.synchronize()
+        del bs
+    D, hq, hkv, L = 256, 8, 2, 32768
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    q = torch.randn((hq, D), device="cuda", generator=gen)
+    out = torch.empty((hq, D), device="cuda")
+    copies = max(2, math.ceil(ROTATE_BYTES / (2 * L * hkv * D * 2)))
+    ks = [torch.randn((L, hkv * D), device="cuda", generator=gen).half().view(torch.int16) for _ in range(copies)]
+    vs = [torch.randn((L, hkv * D), device="cuda", generator=gen).half().view(torch.int16) for _ in range(copies)]
+    log("counters: decode attention f16 L=32768")
+    for i in range(COUNTER_REPEAT):
+        wq.wq_decode_attention(q, ks[i % copies], vs[i % copies], out, L, D, hq, hkv, wq.WQ_KV_F16, 0.0625)
+    torch.cuda.synchronize()
+
+
+def _kernel_short(name: str) -> str:
+    """`ns::(anonymous namespace)::kernel<args>(params)` -> `kernel<args>`."""
+    name = name.split("(")[0] if "(anonymous" not in name else name
+    for pre in ("void ", "wq::", "(anonymous namespace)::"):
+        name = name.replace(pre, "")
+    if "(" in name:
+        name = name[:name.index("(")]
+    return name.strip()
+
+
+def summarize(paths):
+    """Markdown tables from rocprofv3 CSV output: per-kernel duration statistics
+    (median first) from a kernel_trace.csv; from counter_collection.csv files, the
+    per-dispatch counter means per (kernel, grid) -- FETCH_SIZE / WRITE_SIZE in
+    bytes (KiB x 1024) -- next to the median duration of the same dispatches."""
+    import csv
+    import statistics
+    from collections import defaultdict
+    traces = [p for p in paths if p.endswith("kernel_trace.csv")]
+    counters = [p for p in paths if p.endswith("counter_collection.csv")]
+    for path in traces:
+        dur = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            key = (_kernel_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"])),
+                   int(r["Workgroup_Size_X"]))
+            dur[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print(f"Kernel durations from {os.path.basename(path)} (us; workgroups, lanes per workgroup)\n")
+        print("| kernel | workgroups | lanes | dispatches | median | mean | min | max |")
+        print("|---|---:|---:|---:|---:|---:|---:|---:|")
+        for (k, g, w), v in sorted(dur.items(), key=lambda x: -sum(x[1])):
+            print(f"| `{k}` | {g} | {w} | {len(v)} | {statistics.median(v):.2f} | {statistics.mean(v):.2f} | "
+                  f"{min(v):.2f} | {max(v):.2f} |")
+        print()
+    for path in counters:
+        vals = defaultdict(lambda: defaultdict(list))
+        for r in csv.DictReader(open(path)):
+            key = (_kernel_short(r["Kernel_Name"]), int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])))
+            vals[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        names = sorted({c for v in vals.values() for c in v})
+        print(f"Counters from {os.path.basename(path)} (mean per dispatch; *_SIZE in bytes)\n")
+        print("| kernel | workgroups | dispatches | " + " | ".join(names) + " |")
+        print("|---|---:|---:|" + "---:|" * len(names))
+        for (k, g), cs in sorted(vals.items()):
+            n = max(len(x) for x in cs.values())
+            cells = []
+            for c in names:
+                x = statistics.mean(cs[c]) if cs.get(c) else float("nan")
+                cells.append(f"{x * 1024:,.0f}" if c.endswith("_SIZE") else f"{x:,.0f}")
+            print(f"| `{k}` | {g} | {n} | " + " | ".join(cells) + " |")
+        print()
 
 
 class Suite:
@@ -495,6 +622,9 @@ def cpu_baseline(host_weights, seed, budget_s=8.0):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path (pass --gpus 1)",
               file=sys.stderr)
@@ -517,6 +647,9 @@ def main():
     only = args.only
     result = None
     iters = max(10, args.steps // 2)
+    if only == "counters":
+        counter_workload(torch, wq, wqgen, args.seed)
+        return
 
     # Plain-read ceilings at every byte size a bandwidth-bound row reads.
     ceiling = {}

@@ -62,6 +62,13 @@ __device__ __forceinline__ float code_value(const uint32_t (&cw)[SmFmt<FMT>::kCo
     }
 }
 
+// Raw, untyped buffer resource over [p, p + bytes) (bytes capped at 4 GiB - 1).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sm_rsrc(const void *p, uint64_t bytes) {
+    const uint32_t n = (bytes >> 32) != 0 ? 0xffffffffu : static_cast<uint32_t>(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, static_cast<int>(n), 0x00020000);
+}
+constexpr int kSmStream = 2;  // non-temporal: every weight is read once
+
 // Sum over the 16 blocks (lanes with equal lane % 4): rotations by 4 and 8
 // inside each 16-lane row, then across rows.
 __device__ __forceinline__ float block_sum16(float v) {
@@ -128,21 +135,28 @@ __global__ __launch_bounds__(W * 64) void gemm_smallm(const float *__restrict__ 
         soff[u] = static_cast<uint32_t>(r * SBY + 16 * cc);
         ccol[u] = cc;
     }
+    // Loads go through a buffer resource over the rest of the tile's rows from
+    // the step on; `real == false` gives a resource of size 0, so every load is
+    // out of range and returns zeros without touching memory (the last
+    // iteration's stand-in prefetch, see below).
     uint4 nxt[LPL];
-    auto fetch = [&](int s) {
+    const uint64_t tile_bytes = static_cast<uint64_t>(min<int64_t>(R, rows_left)) * row_bytes;
+    auto fetch = [&](int s, bool real) {
         const int cpr = min(16, nb - 16 * s) * F::kBytes / 16;  // chunks per row in this step
-        const uint8_t *base = wrows + static_cast<int64_t>(s) * SBY;
+        const uint64_t start = static_cast<uint64_t>(s) * SBY;
+        const __amdgpu_buffer_rsrc_t rs = sm_rsrc(wrows + start, real ? tile_bytes - start : 0);
 #pragma unroll
         for (int u = 0; u < LPL; ++u) {
             const uint32_t o = ccol[u] < cpr ? goff[u] : goff[u] - 16 * cpr;
-            nxt[u] = load_nt16(reinterpret_cast<const uint4 *>(base + o));
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(o), 0, kSmStream);
+            nxt[u] = make_uint4(v.x, v.y, v.z, v.w);
         }
     };
 
     const int first = s0 + w;
     const int cnt = first < s1 ? (s1 - 1 - first) / W + 1 : 0;
     const int last = first + (cnt - 1) * W;
-    if (cnt > 0) fetch(first);
+    if (cnt > 0) fetch(first, true);
     for (int i = 0; i < cnt; ++i) {
         const int s = first + i * W;
         const int nbs = min(16, nb - 16 * s);  // blocks in this step (a multiple of 8)
@@ -171,10 +185,10 @@ __global__ __launch_bounds__(W * 64) void gemm_smallm(const float *__restrict__ 
             }
         }
         // The next step's weights, in flight during the decode.  Issued on every
-        // iteration (the last one re-reads its own step, in bounds): a
-        // conditional prefetch makes the compiler's wait counts pessimistic at
-        // the join, which serialises the prefetch with the decode.
-        fetch(min(s + W, last));
+        // iteration (the last one through an empty resource): a conditional
+        // prefetch makes the compiler's wait counts pessimistic at the join,
+        // which serialises the prefetch with the decode.
+        fetch(min(s + W, last), i + 1 < cnt);
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int t = 0; t < NT; ++t) {

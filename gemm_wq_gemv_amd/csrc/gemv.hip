@@ -55,7 +55,28 @@ namespace {
 // residual flag), store silu(gate) * up (GLU), or keep a per-wave top-k list
 // of (sum, row) and write it out at the end (TOPK: c is then a TopkCand array
 // of one list of `aux` entries per wave, and the flag argument is that k).
-enum { kModeStore = 0, kModeGlu = 1, kModeTopk = 2 };
+enum { kModeStore = 0, kModeGlu = 1, kModeTopk = 2, kModeArgmax = 3 };
+
+// Fused argmax of the f16 LM head (top-1): every workgroup folds its best row
+// into one of kArgmaxSlots 64-bit slots with an atomic max of an order-keeping
+// key, and argmax_finish reads the slots, writes the result and clears them.
+// One set of slots per cached stream (kStreamSlots) plus one for the
+// allocation-free entry point; zero (no candidate) between calls.
+constexpr int kArgmaxSlots = 4096;  // about 9 workgroups per slot at N = 151936
+__device__ unsigned long long g_argmax_slots[kStreamSlots + 1][kArgmaxSlots];
+
+// Key of a candidate: the logit's bits made monotonic (negative values
+// complemented, positive ones with the sign bit set; -0 counts as +0; NaN maps
+// to the key 0, below every logit, so it is never taken) in the high word,
+// 0xffffffff minus the id in the low word (equal logits: the lower id wins).
+// Key 0: no candidate.
+__device__ __forceinline__ unsigned long long argmax_key(float x, uint32_t id) {
+    x = x + 0.0f;  // -0 -> +0
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const unsigned long long key = (static_cast<unsigned long long>(k) << 32) | (0xffffffffu - id);
+    return __builtin_isnan(x) ? 0ull : key;
+}
 
 // ------------------------------------------------------------------ f16 ----
 
@@ -91,7 +112,7 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void gemv_f16_ksplit(const 
                                                                           float *__restrict__ c, int64_t n,
                                                                           int64_t k, int resid) {
     constexpr bool GLU = MODE == kModeGlu;
-    static_assert(MODE == kModeStore || GLU, "store or GLU");
+    static_assert(MODE == kModeStore || GLU || MODE == kModeArgmax, "store, GLU or argmax");
     static_assert(!GLU || RB % 2 == 0, "a GLU block pairs gate and up rows");
     constexpr int OC = GLU ? RB / 2 : RB;  // outputs per block
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
@@ -145,6 +166,13 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void gemv_f16_ksplit(const 
     if constexpr (GLU) {
         const float up = __shfl_down(v, OC, kWave);  // lane j + OC holds the up sum of output j
         if (lane < OC && r0 + lane < n) c[r0 + lane] = silu(v) * up;
+    } else if constexpr (MODE == kModeArgmax) {
+        // resid is the slot set; the block's best row goes to one slot.
+        static_assert(RB <= 4, "the block's rows sit in one quad");
+        unsigned long long key = (lane < RB && r0 + lane < n) ? argmax_key(v, static_cast<uint32_t>(r0 + lane)) : 0ull;
+        key = max(key, static_cast<unsigned long long>(__shfl_xor(key, 1, kWave)));
+        key = max(key, static_cast<unsigned long long>(__shfl_xor(key, 2, kWave)));
+        if (lane == 0 && key != 0ull) atomicMax(&g_argmax_slots[resid][blockIdx.x % kArgmaxSlots], key);
     } else {
         if (lane < RB && r0 + lane < n) c[r0 + lane] = resid ? c[r0 + lane] + v : v;
     }
@@ -171,6 +199,34 @@ __global__ __launch_bounds__(256) void gemv_f16_any(const float *__restrict__ a,
             c[row] = resid ? c[row] + acc : acc;
     }
     if constexpr (TOPK) top.store(reinterpret_cast<TopkCand *>(c) + wave * resid, resid);
+}
+
+// The result of a fused argmax: the best slot of set `set` (the sentinel
+// (-inf, no id) when every slot is empty), then every slot cleared for the
+// next call.  One workgroup of 1024 lanes.
+__global__ __launch_bounds__(1024) void argmax_finish(int set, float *__restrict__ vals, uint32_t *__restrict__ ids) {
+    __shared__ unsigned long long wbest[16];
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int i = threadIdx.x; i < kArgmaxSlots; i += 1024) {
+        best = max(best, g_argmax_slots[set][i]);
+        g_argmax_slots[set][i] = 0ull;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) best = max(best, static_cast<unsigned long long>(__shfl_xor(best, d, kWave)));
+    if ((threadIdx.x & (kWave - 1)) == 0) wbest[threadIdx.x / kWave] = best;
+    __syncthreads();
+    if (threadIdx.x != 0) return;
+    for (int w = 1; w < 16; ++w) best = max(best, wbest[w]);
+    if (best == 0ull) {
+        vals[0] = -__builtin_huge_valf();
+        ids[0] = kTopkNoId;
+        return;
+    }
+    const uint32_t k = static_cast<uint32_t>(best >> 32);
+    const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    vals[0] = __builtin_bit_cast(float, u);
+    ids[0] = 0xffffffffu - static_cast<uint32_t>(best & 0xffffffffu);
 }
 
 // ------------------------------------------------------- Q8_0 and Q4_0 ----
@@ -884,7 +940,17 @@ hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n
         if (e != hipSuccess) return e;
     }
     const uint16_t *b16 = static_cast<const uint16_t *>(b);
-    if (lm_head_f16_logits_route(a, b, fmt, n, k)) {
+    // Top-1 of f16 rows on the K-split route: the argmax fused into the GEMV
+    // (slot set of this stream, or the allocation-free entry point's own).
+    const int set = workspace ? kStreamSlots : lease.slot();
+    if (topk == 1 && set >= 0 && lm_head_f16_logits_route(a, b, fmt, n, k)) {
+        e = f16_ksplit<kModeArgmax>(a, b16, nullptr, n, k, s, set);
+        if (e == hipSuccess) {
+            if (trace_enabled()) fprintf(stderr, "[wqmm] argmax_finish set=%d\n", set);
+            hipLaunchKernelGGL(argmax_finish, dim3(1), dim3(1024), 0, s, set, vals, ids);
+            e = hipGetLastError();
+        }
+    } else if (lm_head_f16_logits_route(a, b, fmt, n, k)) {
         // f16 rows the K-split kernel takes: its logits go to scratch and the
         // merge reads them 64 at a time.  A per-workgroup top-k list inside that
         // kernel would need a loop over row blocks, which costs more than the

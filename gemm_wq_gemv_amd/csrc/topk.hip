@@ -34,17 +34,30 @@ enum { kSrcSorted = 0, kSrcFlat = 1, kSrcLogits = 2 };
 // (lanes >= topk get the sentinel); kSrcFlat: candidates 64 l .. 64 l + 63 of
 // an array of n single entries (lists of one); kSrcLogits: ids 64 l ..
 // 64 l + 63 of a logits vector, NaN as the sentinel.  Ids past n: sentinel.
+// Every lane loads from an in-bounds index (clamped) and the sentinel is
+// selected by value afterwards: selecting between a load and a local sentinel
+// object made the compiler keep the sentinel on the stack and issue generic
+// (flat) loads through a selected pointer.
 template <int SRC>
 __device__ __forceinline__ TopkCand load_batch(const TopkCand *cand, const float *logits, int64_t n, int topk,
                                                int64_t l) {
     const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
-    const TopkCand none{-__builtin_huge_valf(), kTopkNoId};
-    if constexpr (SRC == kSrcSorted) return lane < topk ? cand[l * topk + lane] : none;
+    const float ninf = -__builtin_huge_valf();
+    if constexpr (SRC == kSrcSorted) {
+        const bool in = lane < topk;
+        const TopkCand x = cand[l * topk + (in ? lane : 0)];
+        return TopkCand{in ? x.v : ninf, in ? x.id : kTopkNoId};
+    }
     const int64_t i = l * kWave + lane;
-    if (i >= n) return none;
-    if constexpr (SRC == kSrcFlat) return cand[i];
-    const float x = logits[i];
-    return __builtin_isnan(x) ? none : TopkCand{x, static_cast<uint32_t>(i)};
+    const bool in = i < n;
+    const int64_t j = in ? i : n - 1;  // n >= 1 whenever a batch exists
+    if constexpr (SRC == kSrcFlat) {
+        const TopkCand x = cand[j];
+        return TopkCand{in ? x.v : ninf, in ? x.id : kTopkNoId};
+    }
+    const float x = logits[j];
+    const bool ok = in && !__builtin_isnan(x);
+    return TopkCand{ok ? x : ninf, ok ? static_cast<uint32_t>(i) : kTopkNoId};
 }
 
 // Folds one batch into the wave's list.  A sorted list whose best entry does
@@ -96,8 +109,8 @@ __device__ __forceinline__ void fold_waves(WaveTopk &t, int topk, TopkCand (*lds
 #pragma unroll
     for (int h = 1; h < kMergeWaves; h *= 2) {
         if (w % (2 * h) == h) {
-            if (lane >= topk) t.v = -__builtin_huge_valf(), t.id = kTopkNoId;
-            lds[w][lane] = TopkCand{t.v, t.id};
+            const bool in = lane < topk;
+            lds[w][lane] = TopkCand{in ? t.v : -__builtin_huge_valf(), in ? t.id : kTopkNoId};
         }
         __syncthreads();
         if (w % (2 * h) == 0) fold_batch(t, topk, lds[w + h][lane], true);

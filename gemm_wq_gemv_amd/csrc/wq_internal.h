@@ -232,29 +232,44 @@ struct WaveTopk {
     // a 6-step bitonic merge sorts.  Entries of rank >= k are dropped first.
     __device__ __forceinline__ void merge_sorted(int k, float bv, uint32_t bid) {
         const int lane = static_cast<int>(threadIdx.x) & (kWave - 1);
+        // Both branches produce values and the four fields are assigned once
+        // afterwards: assigning them inside the branches let the compiler merge
+        // the stores through a selected pointer and keep the list in scratch.
+        float nv, nkv;
+        uint32_t nid, nkid;
         if (k == 1) {  // the better of the two first entries
             const float fv = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, bv)));
             const uint32_t fid = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(bid)));
-            if (cand_better(fv, fid, kv, kid)) kv = fv, kid = fid;
-            v = kv;
-            id = kid;
-            return;
+            const bool take = cand_better(fv, fid, kv, kid);
+            nkv = take ? fv : kv;
+            nkid = take ? fid : kid;
+            nv = nkv;
+            nid = nkid;
+        } else {
+            WaveTopk m;
+            m.v = lane >= k ? -__builtin_huge_valf() : v;
+            m.id = lane >= k ? kTopkNoId : id;
+            const int rev = (kWave - 1 - lane) * 4;
+            const float rv = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(rev, __builtin_bit_cast(int, bv)));
+            const uint32_t rid = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(rev, static_cast<int>(bid)));
+            const bool take = cand_better(rv, rid, m.v, m.id);
+            m.v = take ? rv : m.v;
+            m.id = take ? rid : m.id;
+            m.bitonic_step<32>(lane, true);
+            m.bitonic_step<16>(lane, true);
+            m.bitonic_step<8>(lane, true);
+            m.bitonic_step<4>(lane, true);
+            m.bitonic_step<2>(lane, true);
+            m.bitonic_step<1>(lane, true);
+            nv = m.v;
+            nid = m.id;
+            nkv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m.v), k - 1));
+            nkid = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(m.id), k - 1));
         }
-        if (lane >= k) v = -__builtin_huge_valf(), id = kTopkNoId;
-        const int rev = (kWave - 1 - lane) * 4;
-        const float rv = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(rev, __builtin_bit_cast(int, bv)));
-        const uint32_t rid = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(rev, static_cast<int>(bid)));
-        const bool take = cand_better(rv, rid, v, id);
-        v = take ? rv : v;
-        id = take ? rid : id;
-        bitonic_step<32>(lane, true);
-        bitonic_step<16>(lane, true);
-        bitonic_step<8>(lane, true);
-        bitonic_step<4>(lane, true);
-        bitonic_step<2>(lane, true);
-        bitonic_step<1>(lane, true);
-        kv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k - 1));
-        kid = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(id), k - 1));
+        v = nv;
+        id = nid;
+        kv = nkv;
+        kid = nkid;
     }
 
     // The best of the 64 lanes' (v, id) in every lane (xor butterfly).
@@ -382,6 +397,7 @@ hipError_t launch_quantize_q8_0(const float *w, uint8_t *out, int64_t count, hip
 // enqueued.  Requests above kScratchCacheBytes, and streams beyond the first
 // eight seen on a device, take a private stream-ordered allocation.
 constexpr size_t kScratchCacheBytes = size_t(256) << 20;
+constexpr int kStreamSlots = 8;  // streams per device with a cached scratch buffer
 class ScratchLease {
   public:
     ScratchLease() = default;
@@ -392,8 +408,13 @@ class ScratchLease {
     hipError_t acquire(size_t bytes, hipStream_t s, void **ptr);
     // After the last kernel using the buffer is enqueued on `s`.
     hipError_t release();
+    // Index (0 .. kStreamSlots - 1) of the per-stream cache slot the lease
+    // holds, the same for every lease on this stream; -1 for a private
+    // allocation (a stream beyond the cached ones, or a large request).
+    int slot() const { return slot_; }
 
   private:
+    int slot_ = -1;
     int dev_ = -1;
     hipStream_t s_ = nullptr;
     void *priv_ = nullptr;  // private allocation (large requests)

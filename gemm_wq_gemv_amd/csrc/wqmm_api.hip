@@ -49,7 +49,6 @@ namespace {
 // One cached buffer per (device, stream): work on one stream is ordered by the
 // stream itself, so a reuse needs no event (an event record costs about 3 us
 // of GPU time on MI355X).  Up to kStreamSlots streams per device are cached.
-constexpr int kStreamSlots = 8;
 struct StreamScratch {
     bool live = false;
     hipStream_t stream = nullptr;
@@ -113,6 +112,7 @@ hipError_t ScratchLease::acquire(size_t bytes, hipStream_t s, void **ptr) {
         slot->bytes = want;
     }
     *ptr = slot->ptr;
+    slot_ = static_cast<int>(slot - d.slot);
     return hipSuccess;
 }
 

@@ -194,8 +194,16 @@ int wq_matmul_ex(const float *a, const void *b, float *c, int64_t m, int64_t n, 
 
 /* Fused LM-head GEMV + top-k for one token: logits[j] = sum_k a[k] w[j, k]
  * for the [n, K] weights b in format fmt (layouts as for the GEMV), and their
- * top-k, without writing the n logits: every wave of the GEMV keeps a sorted
- * top-k list of the rows it computed, and two small passes merge the lists.
+ * top-k.  Q8_0 and Q4_0 weights (and f16 rows the K-split GEMV does not take):
+ * every wave of the GEMV keeps a sorted top-k list of the rows it computed,
+ * without writing the n logits, and two small passes merge the lists.  f16
+ * rows on the K-split GEMV (K % 8 == 0, K <= 32768, 16-byte aligned a and b):
+ * for topk == 1 every workgroup folds its best (logit, id) into one of 4096
+ * device slots with a 64-bit atomic max of an order-keeping key, and a
+ * one-workgroup pass takes the best slot and clears the slots for the next
+ * call (one slot set per cached stream, one for the allocation-free entry
+ * point); for topk > 1 the GEMV writes the logits to scratch and the merge
+ * reads them 64 at a time.
  * Passage: dispatch_lm_head_block_stage1_enc (fused LM-head GEMV with a
  * block-local exact top-k writing compact (logit, token_id) candidates) and
  * dispatch_block_topk_merge_enc (merge of those candidates), lattice-inference
@@ -214,7 +222,9 @@ int wq_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt
  * 64 * topk * 8 bytes for f16 weights on the K-split route, else (16 * CUs + 68)
  * * topk * 8 bytes -- at most 2.2 MB on MI355X, and 0.6 MB for the f16 LM head
  * at vocab 151936.  Every list the merge reads is written earlier in the same
- * call, so the array needs no clearing.  All calls on one GPU share its array:
+ * call, so the array needs no clearing (the top-1 slots of the f16 K-split
+ * route are a separate fixed array, cleared by the call that fills them).
+ * All calls on one GPU share its array and slots:
  * calls that may overlap in time on one GPU (different streams, or several host
  * threads without ordering) race; calls on one stream are ordered and safe. */
 int wq_lm_head_topk_noalloc(const float *a, const void *b, int64_t n, int64_t k, int fmt, int topk, float *vals,

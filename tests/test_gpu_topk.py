@@ -186,6 +186,59 @@ def test_nan_and_inf_rows():
     check_topk(vals, ids, logits2, bound2, 4, "nan/inf")
 
 
+def test_top1_ties_nan_inf_and_back_to_back_calls():
+    """Top-1 of f16 rows on the K-split route, where the argmax is fused into the
+    GEMV: copies of the best row go to the lowest id; a NaN best row is skipped;
+    +inf rows win by id; all rows NaN gives the sentinel; all logits negative
+    still gives the best one; and a call after a call with a larger maximum
+    returns its own (nothing is left over from the previous call)."""
+    n, k = 20000, 2048
+    ref_b, dev_b = encoded(n, k, F16, 3)
+    a = wqgen.activations(1, k, 3)[0]
+    _, _, logits, _ = oracle.lm_head_topk(a, ref_b, F16, n, k, 1)
+    best = int(np.nanargmax(logits))
+
+    say("top1 ties")
+    b = np.array(ref_b, copy=True)
+    for c in (9000, 19999, 3):
+        b[c] = b[best]
+    vals, ids = gpu_lm_head_topk(a, torch.from_numpy(b).cuda(), n, k, F16, 1)
+    assert ids[0] == 3
+    _, _, logits2, bound2 = oracle.lm_head_topk(a, b, F16, n, k, 1)
+    check_topk(vals, ids, logits2, bound2, 1, "top1 ties")
+
+    say("top1 nan best row, then +inf rows")
+    b = np.array(ref_b, copy=True)
+    b[best, 7] = 0x7E00
+    vals, ids = gpu_lm_head_topk(a, torch.from_numpy(b).cuda(), n, k, F16, 1)
+    assert ids[0] != best
+    _, _, logits2, bound2 = oracle.lm_head_topk(a, b, F16, n, k, 1)
+    check_topk(vals, ids, logits2, bound2, 1, "top1 nan")
+    col = int(np.flatnonzero(a > 0)[0])
+    for r in (15001, 4321):
+        b[r, :] = 0
+        b[r, col] = 0x7C00
+    vals, ids = gpu_lm_head_topk(a, torch.from_numpy(b).cuda(), n, k, F16, 1)
+    assert ids[0] == 4321 and np.isposinf(vals[0])
+
+    say("top1 all nan")
+    b = np.full((n, k), 0x7E00, dtype=np.uint16)
+    vals, ids = gpu_lm_head_topk(a, torch.from_numpy(b).cuda(), n, k, F16, 1)
+    assert ids[0] == NO_ID and np.isneginf(vals[0])
+
+    say("top1 all negative, after a call with a larger maximum")
+    big = gpu_lm_head_topk(a, dev_b, n, k, F16, 1)
+    neg = np.array(ref_b, copy=True)
+    neg[:, :] = 0
+    neg[:, col] = np.float16(-1.0).view(np.uint16)   # every logit = -a[col] ...
+    neg[777, col] = np.float16(-0.5).view(np.uint16)  # ... but row 777's is -a[col] / 2
+    vals, ids = gpu_lm_head_topk(a, torch.from_numpy(neg).cuda(), n, k, F16, 1)
+    assert big[0][0] > 0 and ids[0] == 777 and vals[0] == np.float32(-0.5 * np.float32(a[col]))
+    say("top1 ragged row counts")
+    for nn in (1, 2, 3, 5, 4097):
+        lm_case(F16, nn, 4096, 1, seed=nn)
+
+
 def test_more_k_than_rows_and_empty():
     for fmt in ALL:
         lm_case(fmt, 5, 256, 8, seed=5)      # 3 sentinels

@@ -90,6 +90,7 @@ def _load() -> ctypes.CDLL:
         "wq_route_for": (I, [I64, I64, I64, I]),
         "wq_gemm_plan": (I, [I64, I64, I64, I, I, P, P, P]),
         "wq_set_gemm_plan": (I, [I, I, I]),
+        "wq_set_gemv_plan": (I, [I, I, I]),
         "wq_set_forced_route": (I, [I]),
         "wq_route_count": (ctypes.c_uint64, [I]),
         "wq_reset_route_counts": (None, []),
@@ -336,7 +337,12 @@ def wq_set_gemm_plan(bm: int, bn: int, splits: int) -> None:
     _check(_lib.wq_set_gemm_plan(bm, bn, splits), "wq_set_gemm_plan")
 
 
+def wq_set_gemv_plan(rb: int, nf: int, nr: int) -> None:
+    _check(_lib.wq_set_gemv_plan(rb, nf, nr), "wq_set_gemv_plan")
+
+
 GEMM_TILES = [(128, 128), (128, 96), (128, 64), (64, 128), (64, 64), (32, 128), (16, 128), (16, 64)]
+GEMV_PLANS = [(8, 2, 1), (4, 2, 1), (4, 3, 1), (4, 1, 1), (8, 1, 1), (16, 1, 1), (2, 2, 1)]
 
 
 def wq_set_forced_route(route: int) -> int:

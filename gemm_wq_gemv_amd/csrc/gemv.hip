@@ -46,6 +46,8 @@
 #include "wq_internal.h"
 
 #include <algorithm>
+#include <atomic>
+#include <cstdio>
 #include <cstdlib>
 
 namespace wq {
@@ -549,6 +551,246 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void gemv_q_ksplit(const fl
     }
 }
 
+// ------------------------------------------------ Q8_0 from row chunks ----
+// Q8_0 GEMV that decodes every weight byte in the register it was loaded into:
+// no LDS staging, one pass per workgroup (as the f16 K-split kernel).  With
+// K % 256 == 0 a row of nb blocks is C = 17 nb / 8 whole 16-byte chunks.
+// A workgroup owns RB rows.  "Full" unit U (< C / 64) gives lane L chunk
+// 64 U + L of every one of the RB rows (one activation window, RB rows); the
+// last rem = C % 64 chunks of the RB rows form rem * RB (row, chunk) pairs,
+// one per lane of the "remainder" units.  Wave w takes full units
+// w NF .. w NF + NF - 1 and remainder units w NR .. w NR + NR - 1.
+//
+// Chunk c (bytes 16c .. 16c + 15 of a row) holds codes of at most two blocks:
+// j0, the block in progress at byte 16c - 1, and j0 + 1 when that block's
+// scale starts inside the chunk, at the even byte p = 34 (j0 + 1) - 16 c <= 14.
+// Dwords 0 .. bd - 1 hold codes of j0 and dwords bd .. 3 codes of j0 + 1, with
+// bd = (p + 2) / 4 (bd = 4 when no block starts in the chunk); the two scale
+// bytes are paired with zero activations.  Code byte i takes activation
+// s0 + i before the scale and s0 + i - 2 after it, s0 = 16 c - 2 j0 - 2.  The
+// scale of j0 + 1 is read from the chunk itself; the scale of j0 lies in chunk
+// c - 1 or c - 2 of the same row, whose lane extracted it as its own start
+// scale and hands it over with ds_bpermute; lanes whose source chunk is in
+// another unit load those two bytes from memory instead (a buffer load that
+// every other lane turns into an out-of-range no-op).
+struct ChunkGeo {
+    int p;     // byte of the block start in the chunk, or >= 16 when none
+    int bd;    // dwords of block j0
+    int s0;    // activation index of byte 0
+    int j0;    // block in progress at the chunk start (-1 for chunk 0)
+    int dsrc;  // chunk c - dsrc holds the scale of j0 (1 or 2)
+};
+__device__ __forceinline__ ChunkGeo chunk_geo(int c) {
+    ChunkGeo g;
+    g.j0 = (16 * c + 33) / 34 - 1;
+    g.p = 34 * (g.j0 + 1) - 16 * c;
+    g.bd = g.p <= 14 ? (g.p + 2) >> 2 : 4;
+    g.s0 = 16 * c - 2 * g.j0 - 2;
+    g.dsrc = 34 * g.j0 >= 16 * (c - 1) ? 1 : 2;
+    return g;
+}
+
+// Byte offsets (into a) of the activation pairs of the chunk: pair t covers
+// code bytes 2t, 2t + 1; the pair of scale bytes gets an out-of-range offset
+// (the buffer load returns zeros), as do pairs past the end of a.
+__device__ __forceinline__ uint32_t act_pair_offset(const ChunkGeo &g, int t, bool valid) {
+    const int hp = g.p >> 1;  // the scale pair (>= 8: none)
+    const int idx = g.s0 + 2 * t - (t > hp ? 2 : 0);
+    return (valid && t != hp) ? static_cast<uint32_t>(idx) * 4u : 0x80000000u;
+}
+
+// The f16 bits at byte p (even, <= 14) of a 16-byte chunk: the dword pair
+// holding it picked with a bit mask (v_bfi_b32; written as selects of the
+// vector's fields, the compiler turned them into a dynamically indexed stack
+// copy), then bytes p % 8 and p % 8 + 1 of the pair moved to the low half by
+// one v_perm_b32 (selector 0x0c: a zero byte).  sel = half_selector(p).
+__device__ __forceinline__ uint32_t half_selector(int p) {
+    const uint32_t b = static_cast<uint32_t>(p) & 7u;
+    return 0x0c0c0000u | ((b + 1u) << 8) | b;
+}
+__device__ __forceinline__ uint32_t chunk_half(const uint4 &v, int p, uint32_t sel) {
+    const uint32_t m8 = 0u - ((static_cast<uint32_t>(p) >> 3) & 1u);
+    const uint32_t lo = (v.z & m8) | (v.x & ~m8);
+    const uint32_t hi = (v.w & m8) | (v.y & ~m8);
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+constexpr int kQcStream = 2;  // non-temporal buffer loads: every weight is read once
+
+// One (row, chunk): adds d_j0 * (codes of j0 . x) + d_j1 * (codes of j1 . x)
+// to acc.  own: the chunk's start scale (valid when p <= 14); from: the
+// scale handed over by the source lane (or loaded); d0, d1 chosen per dword.
+__device__ __forceinline__ float chunk_dot(const uint4 &v, const float (&x)[16], float d0, float d1, int bd,
+                                           float acc) {
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t q = wd[d];
+        float t = static_cast<float>(static_cast<int8_t>(q & 0xffu)) * x[4 * d + 0];
+        t = fmaf(static_cast<float>(static_cast<int8_t>((q >> 8) & 0xffu)), x[4 * d + 1], t);
+        t = fmaf(static_cast<float>(static_cast<int8_t>((q >> 16) & 0xffu)), x[4 * d + 2], t);
+        t = fmaf(static_cast<float>(static_cast<int8_t>(q >> 24)), x[4 * d + 3], t);
+        acc = fmaf(d < bd ? d0 : d1, t, acc);
+    }
+    return acc;
+}
+
+constexpr int kQcMaxWaves = 4;
+
+template <int RB, int NF, int NR>
+__global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q8_chunks(const float *__restrict__ a,
+                                                                      const uint8_t *__restrict__ b,
+                                                                      float *__restrict__ c, int64_t n, int64_t k,
+                                                                      int resid) {
+    constexpr int NU = NF + NR;
+    constexpr uint32_t kOut = 0x80000000u;  // an out-of-range buffer offset: the load returns zeros
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int kw = blockDim.x / kWave;
+    const int nb = static_cast<int>(k >> 5);
+    const int C = (17 * nb) >> 3;
+    const int q = C >> 6, rem = C & 63, P = rem * RB;
+    const int remd = rem > 0 ? rem : 1;  // divisor for lanes of empty remainder units
+    const uint32_t row_bytes = 34u * static_cast<uint32_t>(nb);
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * RB;
+    // The host checks n * row_bytes < 2^31 and 4 K < 2^31: every offset below
+    // fits 31 bits and kOut is out of range of both resources.
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(b), 0, static_cast<int>(static_cast<uint32_t>(n) * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a), 0, static_cast<int>(4 * k), 0x00020000);
+    const uint32_t sbase = static_cast<uint32_t>(r0) * row_bytes;  // soffset of the workgroup's first row
+
+    // Unit geometry.  Every load of a unit past the end (full units beyond
+    // C / 64, remainder lanes beyond rem * RB) is out of range: its data,
+    // scales and activations are zero, and bd = 0 makes both of its scales
+    // the chunk's own (zero) one, so it adds exactly 0 with no branch.
+    ChunkGeo geo[NU];
+    uint32_t voff[NU];  // byte offset of the unit's chunk (remainder: from row r0)
+    int rrow[NR > 0 ? NR : 1], co[NR > 0 ? NR : 1];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const int u = w * NF + f;
+        const bool ok = u < q;
+        geo[f] = chunk_geo(ok ? 64 * u + lane : 0);
+        if (!ok) geo[f].bd = 0;
+        voff[f] = ok ? 16u * static_cast<uint32_t>(64 * u + lane) : kOut;
+    }
+#pragma unroll
+    for (int g = 0; g < NR; ++g) {
+        const int e = 64 * (w * NR + g) + lane;
+        const bool ok = e < P;
+        co[g] = ok ? e % remd : 0;
+        rrow[g] = ok ? e / remd : 0;
+        geo[NF + g] = chunk_geo(64 * q + co[g]);
+        if (!ok) geo[NF + g].bd = 0;
+        const uint32_t roff = static_cast<uint32_t>(min<int64_t>(rrow[g], n - 1 - r0)) * row_bytes;
+        voff[NF + g] = ok ? roff + 16u * static_cast<uint32_t>(64 * q + co[g]) : kOut;
+    }
+
+    // Weight chunks first (rows past n read the last row; never stored).
+    uint32_t rowoff[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) rowoff[r] = sbase + static_cast<uint32_t>(min<int64_t>(r, n - 1 - r0)) * row_bytes;
+    uint4 wv[NF][RB];
+    uint4 wr[NR > 0 ? NR : 1];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rb, static_cast<int>(voff[f]),
+                                                                 static_cast<int>(rowoff[r]), kQcStream);
+            wv[f][r] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+#pragma unroll
+    for (int g = 0; g < NR; ++g) {
+        const u32x4 v =
+            __builtin_amdgcn_raw_buffer_load_b128(rb, static_cast<int>(voff[NF + g]), static_cast<int>(sbase), kQcStream);
+        wr[g] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+    // Scales of j0 whose source chunk is in another unit: full units, lanes
+    // 0 .. dsrc - 1; remainder units, those lanes and the first dsrc chunks of
+    // each row's remainder.  Every other lane's load is out of range.
+    uint32_t fb[NF][RB], fr[NR > 0 ? NR : 1];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const bool need = geo[f].bd > 0 && lane < geo[f].dsrc;
+        const uint32_t o = need ? 34u * static_cast<uint32_t>(geo[f].j0) : kOut;
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+            fb[f][r] = __builtin_amdgcn_raw_buffer_load_b16(rb, static_cast<int>(o), static_cast<int>(rowoff[r]), 0);
+    }
+#pragma unroll
+    for (int g = 0; g < NR; ++g) {
+        const ChunkGeo &ge = geo[NF + g];
+        const bool need = ge.bd > 0 && (co[g] < ge.dsrc || lane < ge.dsrc);
+        const uint32_t roff = static_cast<uint32_t>(min<int64_t>(rrow[g], n - 1 - r0)) * row_bytes;
+        const uint32_t o = need ? roff + 34u * static_cast<uint32_t>(ge.j0) : kOut;
+        fr[g] = __builtin_amdgcn_raw_buffer_load_b16(rb, static_cast<int>(o), static_cast<int>(sbase), 0);
+    }
+    // Activation windows (pairs; zeros at the scale bytes, past K and for
+    // units past the end).
+    float x[NU][16];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const bool ok = voff[u] != kOut;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const auto v =
+                __builtin_amdgcn_raw_buffer_load_b64(ra, static_cast<int>(act_pair_offset(geo[u], t, ok)), 0, 0);
+            const float2 f2 = __builtin_bit_cast(float2, v);
+            x[u][2 * t] = f2.x;
+            x[u][2 * t + 1] = f2.y;
+        }
+    }
+    // Every load above is issued before any decode (the scheduler otherwise
+    // sinks some weight loads below the first unit's decode).
+    __builtin_amdgcn_sched_barrier(0);
+
+    float acc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc[r] = 0.f;
+    // Scale of j0: a lane with bd == 0 (no code of j0) reads its own start
+    // scale through the permute (source = itself), fallback lanes their load.
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const ChunkGeo &g = geo[f];
+        const int src = (g.bd == 0 ? lane : lane - g.dsrc) * 4;
+        const bool fbl = g.bd > 0 && lane < g.dsrc;
+        const uint32_t sel = half_selector(g.p);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const uint32_t own = chunk_half(wv[f][r], g.p, sel);
+            const uint32_t got = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(own)));
+            const uint32_t b0 = fbl ? fb[f][r] : got;
+            const uint32_t b1 = g.p <= 14 ? own : b0;
+            acc[r] = chunk_dot(wv[f][r], x[f], half_bits_to_float(b0), half_bits_to_float(b1), g.bd, acc[r]);
+        }
+    }
+#pragma unroll
+    for (int gi = 0; gi < NR; ++gi) {
+        const ChunkGeo &g = geo[NF + gi];
+        const uint32_t own = chunk_half(wr[gi], g.p, half_selector(g.p));
+        const uint32_t got = static_cast<uint32_t>(
+            __builtin_amdgcn_ds_bpermute((g.bd == 0 ? lane : lane - g.dsrc) * 4, static_cast<int>(own)));
+        const uint32_t b0 = (g.bd > 0 && (co[gi] < g.dsrc || lane < g.dsrc)) ? fr[gi] : got;
+        const uint32_t b1 = g.p <= 14 ? own : b0;
+        const float part = chunk_dot(wr[gi], x[NF + gi], half_bits_to_float(b0), half_bits_to_float(b1), g.bd, 0.f);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) acc[r] += rrow[gi] == r ? part : 0.f;
+    }
+    // Row sums: one butterfly over the wave, then the waves in order through LDS.
+    const float sum = rows_sum<RB, kWave>(acc, lane);
+    __shared__ float part[kQcMaxWaves][RB];
+    if (lane % (kWave / RB) == 0) part[w][lane / (kWave / RB)] = sum;
+    __syncthreads();
+    if (w == 0 && lane < RB && r0 + lane < n) {
+        float t = part[0][lane];
+        for (int qq = 1; qq < kw; ++qq) t += part[qq][lane];
+        float *dst = c + r0 + lane;
+        *dst = resid ? *dst + t : t;
+    }
+}
+
 // Any K % 32 == 0 and 2-byte aligned b: one wave per row, lanes stride over
 // blocks, reading each block with 2-byte loads.
 template <int FMT, bool TOPK>
@@ -799,11 +1041,77 @@ hipError_t run_q_ksplit(const float *a, const uint8_t *b, float *c, int64_t n, i
     return hipGetLastError();
 }
 
+// Plan of the register-chunk Q8_0 GEMV: RB rows per workgroup, NF full and
+// NR remainder units per wave, KW <= 4 waves.  A forced plan that needs more
+// waves falls back to the other kernels.
+struct QcPlan {
+    int rb, nf, nr, kw;
+};
+bool q8c_fit(int64_t k, int rb, int nf, int nr, QcPlan *pl) {
+    const int64_t nb = k / 32, C = 17 * nb / 8, q = C / 64, P = (C % 64) * rb;
+    const int64_t kw = std::max<int64_t>(std::max<int64_t>((q + nf - 1) / nf, (P + 64 * nr - 1) / (64 * nr)), 1);
+    if (kw > kQcMaxWaves) return false;
+    *pl = QcPlan{rb, nf, nr, static_cast<int>(kw)};
+    return true;
+}
+// Forced plan (wq_set_gemv_plan): rb * 256 + nf * 16 + nr, 0 = automatic,
+// -1 = the kernel switched off.
+std::atomic<int> g_q8c_override{0};
+bool q8c_enabled() { return g_q8c_override.load(std::memory_order_relaxed) >= 0; }
+bool q8c_plan(const float *a, const uint8_t *b, int64_t n, int64_t k, QcPlan *pl) {
+    const int64_t nb = k / 32;
+    if (nb % 8 != 0 || nb == 0 || !aligned16(a) || !aligned16(b) || n < 1) return false;
+    if (n * 34 * nb >= (int64_t(1) << 31) || 4 * k >= (int64_t(1) << 31)) return false;
+    if (const int f = g_q8c_override.load(std::memory_order_relaxed); f > 0)
+        return q8c_fit(k, f >> 8, (f >> 4) & 15, f & 15, pl);
+    // Measured on MI355X against the staged and K-split kernels (Q8_0, M = 1):
+    // rows of 128 blocks or more (K >= 4096) and the LM head gain (151936 x 2048
+    // 56.8 -> 54.7 us, 11008 x 4096 14.2 -> 13.0, 4096 x 4096 8.9 -> 7.2,
+    // 2048 x 6144 7.2 -> 6.7, 4096 x 11008 19.2 -> 14.7); shorter rows with
+    // fewer than 65536 of them measured the same or slower (6144 x 2048 6.2 ->
+    // 6.3-6.7 us), so they keep the staged kernel.
+    if (nb < 128) return n >= 65536 && q8c_fit(k, 16, 1, 1, pl);
+    if (n >= 8192 && q8c_fit(k, 8, 1, 1, pl)) return true;
+    return q8c_fit(k, 4, 2, 1, pl) || q8c_fit(k, 4, 3, 1, pl);
+}
+
+template <int RB, int NF, int NR>
+hipError_t run_q8c(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int resid,
+                   int kw) {
+    const int64_t blocks = (n + RB - 1) / RB;
+    if (trace_enabled())
+        fprintf(stderr, "[wqmm] gemv_q8_chunks<RB=%d,NF=%d,NR=%d> n=%lld k=%lld grid=%lld block=%d\n", RB, NF, NR,
+                (long long)n, (long long)k, (long long)blocks, kw * kWave);
+    hipLaunchKernelGGL((gemv_q8_chunks<RB, NF, NR>), dim3(static_cast<unsigned>(blocks)), dim3(kw * kWave), 0, s, a,
+                       b, c, n, k, resid);
+    return hipGetLastError();
+}
+
+// Returns false (nothing launched) when no instantiated plan fits.
+bool launch_q8c(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int resid,
+                hipError_t *e) {
+    QcPlan pl;
+    if (!q8c_plan(a, b, n, k, &pl)) return false;
+    if (pl.rb == 8 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<8, 2, 1>(a, b, c, n, k, s, resid, pl.kw);
+    else if (pl.rb == 4 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<4, 2, 1>(a, b, c, n, k, s, resid, pl.kw);
+    else if (pl.rb == 4 && pl.nf == 3 && pl.nr == 1) *e = run_q8c<4, 3, 1>(a, b, c, n, k, s, resid, pl.kw);
+    else if (pl.rb == 4 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<4, 1, 1>(a, b, c, n, k, s, resid, pl.kw);
+    else if (pl.rb == 8 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<8, 1, 1>(a, b, c, n, k, s, resid, pl.kw);
+    else if (pl.rb == 16 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<16, 1, 1>(a, b, c, n, k, s, resid, pl.kw);
+    else if (pl.rb == 2 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<2, 2, 1>(a, b, c, n, k, s, resid, pl.kw);
+    else return false;
+    return true;
+}
+
 template <int FMT, int MODE>
 hipError_t gemv_q_rows(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int cus,
                        int aux, int64_t *lists) {
     const int64_t nb = k / 32;
     const int64_t row_bytes = nb * QB<FMT>::kBytes;
+    if constexpr (FMT == QFMT_Q8_0 && MODE == kModeStore) {
+        hipError_t e = hipSuccess;
+        if (q8c_enabled() && launch_q8c(a, b, c, n, k, s, aux, &e)) return e;
+    }
     // Long rows (more than 128 blocks, up to 16 waves of 64): K split over the waves of a workgroup.
     if (MODE == kModeStore && nb % 8 == 0 && nb > 128 && nb <= 64 * kSplitMaxWaves && aligned16(a) && aligned16(b))
         return run_q_ksplit<FMT>(a, b, c, n, k, s, aux);
@@ -899,6 +1207,24 @@ hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t 
     }
     if (f16_ksplit_ok(a, b, k)) return f16_ksplit<kModeStore>(a, b, c, n, k, s, epi == kEpiResidual);
     return gemv_f16_rows<kModeStore>(a, b, c, n, k, s, di.cus, epi == kEpiResidual, nullptr);
+}
+
+bool set_gemv_plan_override(int rb, int nf, int nr) {
+    if (rb == 0 && nf == 0 && nr == 0) {
+        g_q8c_override.store(0, std::memory_order_relaxed);
+        return true;
+    }
+    if (rb == -1 && nf == 0 && nr == 0) {
+        g_q8c_override.store(-1, std::memory_order_relaxed);
+        return true;
+    }
+    static const int kPlans[][3] = {{8, 2, 1}, {4, 2, 1}, {4, 3, 1}, {4, 1, 1}, {8, 1, 1}, {16, 1, 1}, {2, 2, 1}};
+    for (const auto &pl : kPlans)
+        if (pl[0] == rb && pl[1] == nf && pl[2] == nr) {
+            g_q8c_override.store(rb * 256 + nf * 16 + nr, std::memory_order_relaxed);
+            return true;
+        }
+    return false;
 }
 
 hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,

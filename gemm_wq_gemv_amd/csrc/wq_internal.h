@@ -382,6 +382,9 @@ void gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *
 // Test hook: force the GEMM tiling (bm, bn from the compiled set; splits >= 1,
 // capped at the number of k-tiles); (0, 0, 0) clears it.  False if unknown.
 bool set_gemm_plan_override(int bm, int bn, int splits);
+// Forces the register-chunk Q8_0 GEMV plan (rb, nf, nr); (0, 0, 0) automatic,
+// (-1, 0, 0) off.  False for a plan that is not instantiated.
+bool set_gemv_plan_override(int rb, int nf, int nr);
 hipError_t launch_fill_zero(float *c, int64_t count, hipStream_t s);
 // Read-bandwidth probe (variant v: 2^v 16-byte chunks per lane); out gets one
 // dword per wave.

@@ -526,6 +526,10 @@ int wq_set_gemm_plan(int bm, int bn, int splits) {
     return wq::set_gemm_plan_override(bm, bn, splits) ? WQ_OK : WQ_ERR_SHAPE;
 }
 
+int wq_set_gemv_plan(int rb, int nf, int nr) {
+    return wq::set_gemv_plan_override(rb, nf, nr) ? WQ_OK : WQ_ERR_SHAPE;
+}
+
 int wq_set_attn_partition(int64_t tokens) {
     if (tokens < 0) return WQ_ERR_SHAPE;
     wq::set_attn_partition_override(tokens);

@@ -326,6 +326,17 @@ int wq_gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int
  * do not depend on the tiling beyond f32 rounding. */
 int wq_set_gemm_plan(int bm, int bn, int splits);
 
+/* Test and tuning hook for the Q8_0 decode GEMV (M == 1, K % 256 == 0,
+ * 16-byte aligned operands, N * K * 34 / 32 < 2^31 bytes): force every later
+ * call whose shape fits onto the register-chunk kernel with rb rows per
+ * workgroup and nf full / nr remainder 64-chunk units per wave (the kernel
+ * takes at most 4 waves; shapes that would need more keep the other kernels);
+ * (0, 0, 0) restores the measured rule, (-1, 0, 0) switches the kernel off.
+ * Plans: (8,2,1) (4,2,1) (4,3,1) (4,1,1) (8,1,1) (16,1,1) (2,2,1); anything
+ * else returns WQ_ERR_SHAPE.  Results do not depend on the plan beyond f32
+ * rounding. */
+int wq_set_gemv_plan(int rb, int nf, int nr);
+
 /* Force every later wq_matmul call in the process onto one route
  * (WQ_ROUTE_AUTO restores the M rule).  Returns the previous setting, or
  * -WQ_ERR_ROUTE for an unknown value.  Meant for tests that check that all

@@ -266,6 +266,18 @@ def test_gemm_planner_invariants():
     assert wq.wq_gemm_plan(16, 11008, 4096, wq.WQ_FMT_Q8_0) == (16, 128, 8)
 
 
+def test_gemv_plan_override_hook():
+    try:
+        for pl in wq.GEMV_PLANS:
+            wq.wq_set_gemv_plan(*pl)
+        wq.wq_set_gemv_plan(-1, 0, 0)
+        for bad in ((3, 2, 1), (8, 2, 2), (16, 2, 1), (-1, 1, 0)):
+            with pytest.raises(wq.WQError):
+                wq.wq_set_gemv_plan(*bad)
+    finally:
+        wq.wq_set_gemv_plan(0, 0, 0)
+
+
 def test_gemm_plan_override_hook():
     try:
         wq.wq_set_gemm_plan(32, 128, 3)

@@ -52,7 +52,7 @@ DECODE = [("gate_up", 6144, 2048), ("down", 2048, 6144), ("o_proj", 2048, 2048),
 PREFILL = [(512, 6144, 2048), (512, 2048, 6144)]
 SWEEP_SHAPES = [(11008, 4096), (4096, 11008)]
 SWEEP_M = [1, 2, 4, 8, 16, 64, 512]
-ROUTE_NAMES = {1: "gemv", 2: "gemm", 3: "small_m"}
+ROUTE_NAMES = {1: "gemv", 2: "gemm", 3: "small_m", 4: "stream"}
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_f16_lm_head_151936x2048.md")

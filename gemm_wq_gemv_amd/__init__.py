@@ -47,6 +47,7 @@ WQ_ROUTE_AUTO = 0
 WQ_ROUTE_GEMV = 1
 WQ_ROUTE_GEMM = 2
 WQ_ROUTE_SKINNY = 3
+WQ_ROUTE_STREAM = 4
 
 WQ_EPI_NONE = 0
 WQ_EPI_RESIDUAL = 1
@@ -91,6 +92,7 @@ def _load() -> ctypes.CDLL:
         "wq_gemm_plan": (I, [I64, I64, I64, I, I, P, P, P]),
         "wq_set_gemm_plan": (I, [I, I, I]),
         "wq_set_gemv_plan": (I, [I, I, I]),
+        "wq_set_stream_plan": (I, [I, I]),
         "wq_set_forced_route": (I, [I]),
         "wq_route_count": (ctypes.c_uint64, [I]),
         "wq_reset_route_counts": (None, []),
@@ -339,6 +341,15 @@ def wq_set_gemm_plan(bm: int, bn: int, splits: int) -> None:
 
 def wq_set_gemv_plan(rb: int, nf: int, nr: int) -> None:
     _check(_lib.wq_set_gemv_plan(rb, nf, nr), "wq_set_gemv_plan")
+
+
+def wq_set_stream_plan(shape: int, splits: int) -> None:
+    _check(_lib.wq_set_stream_plan(shape, splits), "wq_set_stream_plan")
+
+
+# (tiles per wave, K sub-ranges per workgroup, tile groups, weights staged in LDS)
+STREAM_SHAPES = [(1, 4, 1, 0), (1, 8, 1, 0), (2, 4, 1, 0), (1, 2, 2, 0), (2, 1, 4, 0), (1, 1, 4, 0), (2, 8, 1, 0),
+                 (1, 4, 1, 1), (1, 1, 4, 1), (2, 1, 4, 1), (1, 8, 1, 1), (1, 2, 2, 1), (1, 1, 8, 1), (2, 1, 8, 1)]
 
 
 GEMM_TILES = [(128, 128), (128, 96), (128, 64), (64, 128), (64, 64), (32, 128), (16, 128), (16, 64)]

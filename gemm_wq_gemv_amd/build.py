@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwqmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["wqmm_api.hip", "gemv.hip", "gemm.hip", "skinny.hip", "pack.hip", "topk.hip", "attn.hip", "probe.hip", "smallm.hip"]
+SOURCES = ["wqmm_api.hip", "gemv.hip", "gemm.hip", "skinny.hip", "pack.hip", "topk.hip", "attn.hip", "probe.hip", "smallm.hip", "wstream.hip"]
 
 # gfx950 only.  Packed-FP32 VALU ops are disabled for all device code; the
 # host pass does not know that target feature and warns, which is harmless.

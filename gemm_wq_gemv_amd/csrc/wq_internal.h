@@ -370,6 +370,14 @@ hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t
 bool smallm_ok(const float *a, const void *b, int fmt, int64_t m, int64_t k);
 hipError_t launch_smallm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
                          hipStream_t s, int epi = kEpiNone);
+// Weight stream through the f16 matrix cores for Q8_0 / Q4_0 weights,
+// 1 <= M <= 16, K % 256 == 0, 16-byte aligned a and b (wstream_ok); epi
+// kEpiNone or kEpiResidual.
+bool wstream_ok(const float *a, const void *b, int fmt, int64_t m, int64_t n, int64_t k);
+hipError_t launch_wstream(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
+                          hipStream_t s, int epi = kEpiNone);
+// Test hook: workgroup shape 1..7 and K splits; 0 = automatic.
+bool set_wstream_plan_override(int shape, int splits);
 // Small-M weight-streaming product (M <= 16 rows of A per launch).
 hipError_t launch_skinny(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
                          hipStream_t s, int epi = kEpiNone);

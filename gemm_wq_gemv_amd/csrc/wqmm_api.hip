@@ -18,7 +18,7 @@ DeviceInfo g_dev[kMaxDevices];
 hipError_t g_dev_err[kMaxDevices];
 
 std::atomic<int> g_forced_route{WQ_ROUTE_AUTO};
-std::atomic<uint64_t> g_route_count[4];
+std::atomic<uint64_t> g_route_count[5];
 
 int trace_flag() {
     static const int v = [] {
@@ -213,22 +213,22 @@ int validate(const float *a, const void *b, const float *c, int64_t m, int64_t n
 
 int status_of(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_LAUNCH; }
 
-// M == 1: the decode GEMV; 2 <= M <= 8: the weight-streaming small-M kernels
-// (quantized weights with K % 256 == 0 and 16-byte aligned operands take the
-// staged one); larger M: the LDS-tiled GEMM.  The crossovers are measured on
-// MI355X at (N, K) = (11008, 4096) and (4096, 11008): for Q8_0 the staged
-// small-M kernel takes 18-20 us at M = 2, 20-22 us at M = 4 and 25-29 us at
-// M = 8 against 30-31 us for the GEMM at M = 8..16; the general small-M kernel
-// beats the GEMM up to M = 4 for quantized rows it has to take (other K), and
-// up to M = 8 for f16.
+// M == 1: the decode GEMV; small M: weight-streaming kernels; larger M: the
+// LDS-tiled GEMM.  Quantized weights with K % 256 == 0 take the f16
+// matrix-core stream for M <= 16 (its time hardly depends on M: measured on
+// MI355X at (N, K) = (11008, 4096) and (4096, 11008) it beats the tiled GEMM up
+// to M = 16); other quantized shapes take the fp32 small-M kernel up to M = 4,
+// f16 weights up to M = 8 (crossovers measured on the same shapes).
 constexpr int64_t kSkinnyRows = 16;  // rows of A per small-M launch
 int auto_route(int64_t m, int64_t k, int fmt) {
     if (m <= 1) return WQ_ROUTE_GEMV;
     if (fmt == WQ_FMT_F16) return m <= 8 ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;
-    const bool staged = k % 256 == 0;  // alignment is checked at launch; the route only depends on shapes
-    return m <= (staged ? 8 : 4) ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;  // Q4_0 as Q8_0
+    if (k % 256 == 0) return m <= 16 ? WQ_ROUTE_STREAM : WQ_ROUTE_GEMM;  // alignment is checked at launch
+    return m <= 4 ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;  // Q4_0 as Q8_0
 }
-bool known_route(int r) { return r == WQ_ROUTE_GEMV || r == WQ_ROUTE_GEMM || r == WQ_ROUTE_SKINNY; }
+bool known_route(int r) {
+    return r == WQ_ROUTE_GEMV || r == WQ_ROUTE_GEMM || r == WQ_ROUTE_SKINNY || r == WQ_ROUTE_STREAM;
+}
 
 // Kernel-side epilogue code of a wq_epilogue value.
 int kernel_epi(int epi) {
@@ -278,6 +278,24 @@ int run_skinny(const float *a, const void *b, float *c, int64_t m, int64_t n, in
     return WQ_OK;
 }
 
+// The f16 matrix-core weight stream, one launch per block of up to 16 rows of
+// A, where it applies (Q8_0 / Q4_0, K % 256 == 0, 16-byte aligned operands, no
+// SwiGLU); anything else takes the small-M route.
+int run_stream(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
+               int epi) {
+    const int ke = kernel_epi(epi);
+    bool ok = ke != wq::kEpiGlu;
+    for (int64_t i = 0; ok && i < m; i += kSkinnyRows)
+        ok = wq::wstream_ok(a + i * k, b, fmt, m - i < kSkinnyRows ? m - i : kSkinnyRows, n, k);
+    if (!ok) return run_skinny(a, b, c, m, n, k, fmt, s, epi);
+    for (int64_t i = 0; i < m; i += kSkinnyRows) {
+        const int64_t rows = m - i < kSkinnyRows ? m - i : kSkinnyRows;
+        if (wq::launch_wstream(a + i * k, b, fmt, c + i * n, rows, n, k, s, ke) != hipSuccess) return WQ_ERR_LAUNCH;
+        wq::g_route_count[WQ_ROUTE_STREAM].fetch_add(1, std::memory_order_relaxed);
+    }
+    return WQ_OK;
+}
+
 // K == 0 (f16 only): the empty sum, c = 0.
 int run_zero(float *c, int64_t m, int64_t n, hipStream_t s) {
     return status_of(wq::launch_fill_zero(c, m * n, s));
@@ -292,6 +310,7 @@ int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, in
     if (route == WQ_ROUTE_AUTO) route = auto_route(m, k, fmt);
     if (route == WQ_ROUTE_GEMV) return run_gemv(a, b, c, m, n, k, fmt, s, epi);
     if (route == WQ_ROUTE_SKINNY) return run_skinny(a, b, c, m, n, k, fmt, s, epi);
+    if (route == WQ_ROUTE_STREAM) return run_stream(a, b, c, m, n, k, fmt, s, epi);
     return run_gemm(a, b, c, m, n, k, fmt, s, epi);
 }
 
@@ -299,7 +318,7 @@ int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, in
 
 extern "C" {
 
-int wq_abi_version(void) { return 104; }
+int wq_abi_version(void) { return 105; }
 
 const char *wq_status_str(int status) {
     switch (status) {
@@ -528,6 +547,10 @@ int wq_set_gemm_plan(int bm, int bn, int splits) {
 
 int wq_set_gemv_plan(int rb, int nf, int nr) {
     return wq::set_gemv_plan_override(rb, nf, nr) ? WQ_OK : WQ_ERR_SHAPE;
+}
+
+int wq_set_stream_plan(int shape, int splits) {
+    return wq::set_wstream_plan_override(shape, splits) ? WQ_OK : WQ_ERR_SHAPE;
 }
 
 int wq_set_attn_partition(int64_t tokens) {

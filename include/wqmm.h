@@ -94,8 +94,14 @@ typedef enum wq_route {
     WQ_ROUTE_AUTO = 0,  /* choose by M (wq_route_for) */
     WQ_ROUTE_GEMV = 1,  /* decode GEMV: one launch per row of A */
     WQ_ROUTE_GEMM = 2,  /* LDS-tiled fp32-MFMA GEMM */
-    WQ_ROUTE_SKINNY = 3 /* small-M weight-streaming fp32-MFMA product: one
-                           launch per block of up to 16 rows of A */
+    WQ_ROUTE_SKINNY = 3, /* small-M weight-streaming fp32-MFMA product: one
+                            launch per block of up to 16 rows of A */
+    WQ_ROUTE_STREAM = 4  /* small-M weight stream through the f16 matrix cores
+                            with f32 results (Q8_0 / Q4_0, K % 256 == 0,
+                            M * K <= 196608 per block of rows, 16-byte aligned
+                            a and b, no SwiGLU; other calls on this route take
+                            WQ_ROUTE_SKINNY): one launch per block of up to 16
+                            rows of A */
 } wq_route;
 
 /* ---------------------------------------------------------------------- */
@@ -121,14 +127,17 @@ int wq_gemm_q4_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t 
                  void *stream);
 
 /* M-routed product for either format (fmt is a wq_format).  M == 1 takes the
- * GEMV; 2 <= M <= 8 the small-M weight-streaming kernels (for Q8_0 / Q4_0 with
- * K % 256 != 0 only up to M == 4); larger M the tiled GEMM, unless a route is
- * forced (wq_set_forced_route).  The small-M kernels read every weight once per
- * 16 rows of A with fp32 matrix-core accumulation; when they split K (and for
- * the SwiGLU epilogue on the quantized one) they use the same scratch as the
- * GEMM (splits*M*N*4 bytes, 2n columns for SwiGLU).  Passage: dispatch_gemm_q8
- * and dispatch_gemm, lattice-inference 0.9.0 dispatch.rs (M == 1 decode,
- * M > 1 batched product). */
+ * GEMV.  Q8_0 / Q4_0 with K % 256 == 0 take, for 2 <= M <= 16, the f16
+ * matrix-core weight stream (activations carried as two f16 parts, hi + lo,
+ * after a power-of-two scaling per row and K range, so the product keeps f32
+ * accuracy; f32 accumulation); other quantized shapes the fp32 small-M kernel
+ * up to M == 4, f16 weights up to M == 8; larger M the tiled GEMM, unless a
+ * route is forced (wq_set_forced_route).  The small-M kernels read every weight
+ * once per 16 rows of A; when they split K (and for the SwiGLU epilogue on the
+ * fp32 small-M kernel) they use the same scratch as the GEMM (splits*M*N*4
+ * bytes, 2n columns for SwiGLU).  Passage: dispatch_gemm_q8 and dispatch_gemm,
+ * lattice-inference 0.9.0 dispatch.rs (M == 1 decode, M > 1 batched
+ * product). */
 int wq_matmul(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt,
               void *stream);
 
@@ -308,7 +317,8 @@ int wq_read_probe(const void *p, int64_t bytes, uint32_t *out, int variant, void
 /* Routing and introspection (host only; these never touch the GPU). */
 
 /* The route wq_matmul takes for these arguments when nothing is forced
- * (WQ_ROUTE_GEMV, WQ_ROUTE_SKINNY or WQ_ROUTE_GEMM), or a negative wq_status
+ * (WQ_ROUTE_GEMV, WQ_ROUTE_STREAM, WQ_ROUTE_SKINNY or WQ_ROUTE_GEMM), or a
+ * negative wq_status
  * on bad arguments. */
 int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt);
 
@@ -337,13 +347,25 @@ int wq_set_gemm_plan(int bm, int bn, int splits);
  * rounding. */
 int wq_set_gemv_plan(int rb, int nf, int nr);
 
+/* Test and tuning hook for the f16 matrix-core weight stream
+ * (WQ_ROUTE_STREAM): workgroup shape 1..14 (index into the compiled set of
+ * (tiles of 16 weight rows per wave, K sub-ranges per workgroup, tile groups
+ * per workgroup, weights staged through LDS): (1,4,1,0) (1,8,1,0) (2,4,1,0)
+ * (1,2,2,0) (2,1,4,0) (1,1,4,0) (2,8,1,0) (1,4,1,1) (1,1,4,1) (2,1,4,1)
+ * (1,8,1,1) (1,2,2,1) (1,1,8,1) (2,1,8,1)) and the number of K splits across
+ * workgroups (at most min(K / 256, 16); raised where one split's activations
+ * would not fit the kernel's staging); 0 = automatic for either.  Returns
+ * WQ_ERR_SHAPE for a shape outside 0..14 or negative splits.  Results do not depend on the plan beyond
+ * f32 rounding. */
+int wq_set_stream_plan(int shape, int splits);
+
 /* Force every later wq_matmul call in the process onto one route
  * (WQ_ROUTE_AUTO restores the M rule).  Returns the previous setting, or
  * -WQ_ERR_ROUTE for an unknown value.  Meant for tests that check that all
  * routes agree (the pages' test hook forcing the fallback GEMM). */
 int wq_set_forced_route(int route);
 
-/* Kernel launches made so far per route (GEMV, GEMM or SKINNY) by
+/* Kernel launches made so far per route (GEMV, GEMM, SKINNY or STREAM) by
  * any entry point, and a reset.  The pages keep such "path proof" counters. */
 uint64_t wq_route_count(int route);
 void wq_reset_route_counts(void);

@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process():
 
 
 def test_abi_and_status_strings():
-    assert wq.wq_abi_version() == 104
+    assert wq.wq_abi_version() == 105
     for st in range(0, 11):
         assert wq.status_str(st)
     assert wq.status_str(99) == "unknown status"
@@ -189,14 +189,18 @@ def test_decode_attention_validation():
 
 
 def test_routing_rule():
-    """M = 1: GEMV; 2..8: small-M (quantized rows with K % 256 != 0: 2..4); more: GEMM."""
+    """M = 1: GEMV; quantized with K % 256 == 0: 2..16 the f16 matrix-core
+    stream; other quantized K: 2..4 small-M; f16: 2..8 small-M; more: GEMM."""
     for fmt in (wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0):
         for k in (4096, 4128):
             assert wq.wq_route_for(1, 4096, k, fmt) == wq.WQ_ROUTE_GEMV
-            top = 8 if fmt == wq.WQ_FMT_F16 or k % 256 == 0 else 4
+            if fmt != wq.WQ_FMT_F16 and k % 256 == 0:
+                small, top = wq.WQ_ROUTE_STREAM, 16
+            else:
+                small, top = wq.WQ_ROUTE_SKINNY, 8 if fmt == wq.WQ_FMT_F16 else 4
             for m in range(2, top + 1):
-                assert wq.wq_route_for(m, 4096, k, fmt) == wq.WQ_ROUTE_SKINNY
-            for m in (top + 1, 16, 17, 64, 512):
+                assert wq.wq_route_for(m, 4096, k, fmt) == small
+            for m in (top + 1, 17, 64, 512):
                 assert wq.wq_route_for(m, 4096, k, fmt) == wq.WQ_ROUTE_GEMM
     assert wq.wq_route_for(2, 8, 33, wq.WQ_FMT_Q8_0) == -wq.WQ_ERR_K
     assert wq.wq_route_for(2, 8, 48, wq.WQ_FMT_Q4_0) == -wq.WQ_ERR_K
@@ -210,12 +214,13 @@ def test_forced_route_setting():
         assert prev == wq.WQ_ROUTE_AUTO
         assert wq.wq_set_forced_route(wq.WQ_ROUTE_GEMV) == wq.WQ_ROUTE_GEMM
         assert wq.wq_set_forced_route(wq.WQ_ROUTE_SKINNY) == wq.WQ_ROUTE_GEMV
+        assert wq.wq_set_forced_route(wq.WQ_ROUTE_STREAM) == wq.WQ_ROUTE_SKINNY
         assert wq.wq_set_forced_route(7) == -wq.WQ_ERR_ROUTE
         assert wq.wq_set_forced_route(-1) == -wq.WQ_ERR_ROUTE
     finally:
         wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
     wq.wq_reset_route_counts()
-    for r in (wq.WQ_ROUTE_GEMV, wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY):
+    for r in (wq.WQ_ROUTE_GEMV, wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_STREAM):
         assert wq.wq_route_count(r) == 0
     assert wq.wq_route_count(99) == 0
 
@@ -276,6 +281,17 @@ def test_gemv_plan_override_hook():
                 wq.wq_set_gemv_plan(*bad)
     finally:
         wq.wq_set_gemv_plan(0, 0, 0)
+
+
+def test_stream_plan_override_hook():
+    try:
+        for p, sp in ((1, 0), (14, 0), (0, 3), (2, 43)):
+            wq.wq_set_stream_plan(p, sp)
+        for bad in ((15, 0), (-1, 0), (1, -2)):
+            with pytest.raises(wq.WQError):
+                wq.wq_set_stream_plan(*bad)
+    finally:
+        wq.wq_set_stream_plan(0, 0)
 
 
 def test_gemm_plan_override_hook():

@@ -27,7 +27,7 @@ F16, Q8, Q4 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0
 ALL = [F16, Q8, Q4]
 RES, GLU = wq.WQ_EPI_RESIDUAL, wq.WQ_EPI_SWIGLU
 ROUTES = {"gemv": wq.WQ_ROUTE_GEMV, "skinny": wq.WQ_ROUTE_SKINNY, "gemm": wq.WQ_ROUTE_GEMM,
-          "auto": wq.WQ_ROUTE_AUTO}
+          "stream": wq.WQ_ROUTE_STREAM, "auto": wq.WQ_ROUTE_AUTO}
 
 
 def say(msg: str):
@@ -99,14 +99,14 @@ SHAPES = {F16: [(1, 37, 1000), (3, 300, 2048), (13, 129, 96), (37, 97, 1003), (5
           Q4: [(1, 37, 992), (3, 300, 2048), (13, 129, 96), (37, 97, 1024), (5, 1000, 8192)]}
 
 
-@pytest.mark.parametrize("route", ["gemv", "skinny", "gemm", "auto"])
+@pytest.mark.parametrize("route", ["gemv", "skinny", "gemm", "stream", "auto"])
 @pytest.mark.parametrize("epi", [RES, GLU], ids=["residual", "swiglu"])
 @pytest.mark.parametrize("fmt", ALL)
 def test_epilogue_every_route(fmt, epi, route):
     """Ragged N (not a multiple of any tile), K tails (f16 K % 32 != 0), K split
     across workgroups (small N, large K), and every small-M row-group count."""
     for m, n, k in SHAPES[fmt]:
-        if route == "skinny" and m > 16:
+        if route in ("skinny", "stream") and m > 16:
             continue
         case(fmt, epi, m, n, k, seed=m + n, route=route)
 
@@ -116,6 +116,20 @@ def test_epilogue_every_route(fmt, epi, route):
 def test_epilogue_small_m_every_row_group(fmt, epi):
     for m in (2, 4, 5, 8, 9, 12, 16):
         case(fmt, epi, m, 200, 1024, seed=20 + m, route="skinny")
+        case(fmt, epi, m, 200, 1024, seed=20 + m, route="stream")
+
+
+@pytest.mark.parametrize("fmt", [Q8, Q4])
+def test_residual_stream_split_k(fmt):
+    """The f16 matrix-core stream adds the residual in the last arrival of a
+    split-K row group (forced splits) as well as in a single split."""
+    try:
+        for p, sp in ((1, 1), (5, 3), (2, 8)):
+            wq.wq_set_stream_plan(p, sp)
+            for m in (1, 5, 16):
+                case(fmt, RES, m, 333, 2048, seed=40 + m, route="stream")
+    finally:
+        wq.wq_set_stream_plan(0, 0)
 
 
 PLAN = [(F16, 37, 300, 640), (Q8, 130, 97, 1024), (Q4, 37, 300, 640), (F16, 5, 77, 1003)]

@@ -637,7 +637,7 @@ __device__ __forceinline__ float chunk_dot(const uint4 &v, const float (&x)[16],
 
 constexpr int kQcMaxWaves = 4;
 
-template <int RB, int NF, int NR>
+template <int RB, int NF, int NR, int MODE = kModeStore>
 __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q8_chunks(const float *__restrict__ a,
                                                                       const uint8_t *__restrict__ b,
                                                                       float *__restrict__ c, int64_t n, int64_t k,
@@ -783,7 +783,19 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q8_chunks(const floa
     __shared__ float part[kQcMaxWaves][RB];
     if (lane % (kWave / RB) == 0) part[w][lane / (kWave / RB)] = sum;
     __syncthreads();
-    if (w == 0 && lane < RB && r0 + lane < n) {
+    if constexpr (MODE == kModeArgmax) {
+        // resid is the slot set: the workgroup's best row goes to one slot.
+        if (w != 0) return;
+        unsigned long long key = 0ull;
+        if (lane < RB && r0 + lane < n) {
+            float t = part[0][lane];
+            for (int qq = 1; qq < kw; ++qq) t += part[qq][lane];
+            key = argmax_key(t, static_cast<uint32_t>(r0 + lane));
+        }
+#pragma unroll
+        for (int d = 1; d < RB; d *= 2) key = max(key, static_cast<unsigned long long>(__shfl_xor(key, d, kWave)));
+        if (lane == 0 && key != 0ull) atomicMax(&g_argmax_slots[resid][blockIdx.x % kArgmaxSlots], key);
+    } else if (w == 0 && lane < RB && r0 + lane < n) {
         float t = part[0][lane];
         for (int qq = 1; qq < kw; ++qq) t += part[qq][lane];
         float *dst = c + r0 + lane;
@@ -1075,30 +1087,32 @@ bool q8c_plan(const float *a, const uint8_t *b, int64_t n, int64_t k, QcPlan *pl
     return q8c_fit(k, 4, 2, 1, pl) || q8c_fit(k, 4, 3, 1, pl);
 }
 
-template <int RB, int NF, int NR>
+template <int RB, int NF, int NR, int MODE = kModeStore>
 hipError_t run_q8c(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int resid,
                    int kw) {
     const int64_t blocks = (n + RB - 1) / RB;
     if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_q8_chunks<RB=%d,NF=%d,NR=%d> n=%lld k=%lld grid=%lld block=%d\n", RB, NF, NR,
-                (long long)n, (long long)k, (long long)blocks, kw * kWave);
-    hipLaunchKernelGGL((gemv_q8_chunks<RB, NF, NR>), dim3(static_cast<unsigned>(blocks)), dim3(kw * kWave), 0, s, a,
-                       b, c, n, k, resid);
+        fprintf(stderr, "[wqmm] gemv_q8_chunks<RB=%d,NF=%d,NR=%d,mode=%d> n=%lld k=%lld grid=%lld block=%d\n", RB, NF,
+                NR, MODE, (long long)n, (long long)k, (long long)blocks, kw * kWave);
+    hipLaunchKernelGGL((gemv_q8_chunks<RB, NF, NR, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(kw * kWave), 0,
+                       s, a, b, c, n, k, resid);
     return hipGetLastError();
 }
 
-// Returns false (nothing launched) when no instantiated plan fits.
-bool launch_q8c(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int resid,
+// Returns false (nothing launched) when no instantiated plan fits.  MODE
+// kModeStore (aux: residual flag) or kModeArgmax (aux: the slot set).
+template <int MODE = kModeStore>
+bool launch_q8c(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int aux,
                 hipError_t *e) {
     QcPlan pl;
     if (!q8c_plan(a, b, n, k, &pl)) return false;
-    if (pl.rb == 8 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<8, 2, 1>(a, b, c, n, k, s, resid, pl.kw);
-    else if (pl.rb == 4 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<4, 2, 1>(a, b, c, n, k, s, resid, pl.kw);
-    else if (pl.rb == 4 && pl.nf == 3 && pl.nr == 1) *e = run_q8c<4, 3, 1>(a, b, c, n, k, s, resid, pl.kw);
-    else if (pl.rb == 4 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<4, 1, 1>(a, b, c, n, k, s, resid, pl.kw);
-    else if (pl.rb == 8 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<8, 1, 1>(a, b, c, n, k, s, resid, pl.kw);
-    else if (pl.rb == 16 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<16, 1, 1>(a, b, c, n, k, s, resid, pl.kw);
-    else if (pl.rb == 2 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<2, 2, 1>(a, b, c, n, k, s, resid, pl.kw);
+    if (pl.rb == 8 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<8, 2, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 4 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<4, 2, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 4 && pl.nf == 3 && pl.nr == 1) *e = run_q8c<4, 3, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 4 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<4, 1, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 8 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<8, 1, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 16 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<16, 1, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 2 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<2, 2, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
     else return false;
     return true;
 }
@@ -1237,16 +1251,33 @@ hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t 
     return launch_gemv_q<QFMT_Q4_0>(a, b, c, n, k, s, epi);
 }
 
-// Scratch layout of an LM-head top-k call: the f16 K-split route keeps the n
-// logits (rounded up to 256 bytes) and kTopkGroups partial lists; the other
-// routes keep up to max_topk_lists(cus) per-wave lists and the partial lists.
+// Routes of an LM-head top-k call.  The logits route runs the fastest store
+// GEMV into scratch and merges the logits 64 at a time: f16 rows the K-split
+// kernel takes, and quantized rows of whole 256-column groups for k > 1 (the
+// register-chunk / staged store kernels beat the per-wave lists once k is
+// large: measured at N = 151936, k = 50, Q8_0 71.3 against 73.7 us, Q4_0 56.6
+// against 59.3 us).  Top-1 of f16 (K-split) and Q8_0 (register-chunk) rows
+// takes the argmax fused into the GEMV.  Everything else keeps per-wave
+// top-k lists inside the GEMV and merges them.
 static bool lm_head_f16_logits_route(const float *a, const void *b, int fmt, int64_t n, int64_t k) {
     return fmt != QFMT_Q8_0 && fmt != QFMT_Q4_0 && n > 0 && f16_ksplit_ok(a, static_cast<const uint16_t *>(b), k);
+}
+static bool lm_head_q_logits_route(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk) {
+    return (fmt == QFMT_Q8_0 || fmt == QFMT_Q4_0) && topk > 1 && n > 0 && (k / 32) % 8 == 0 && aligned16(a) &&
+           aligned16(b);
+}
+static bool lm_head_logits_route(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk) {
+    return lm_head_f16_logits_route(a, b, fmt, n, k) || lm_head_q_logits_route(a, b, fmt, n, k, topk);
+}
+static bool lm_head_q8_argmax_route(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk) {
+    QcPlan pl;
+    return fmt == QFMT_Q8_0 && topk == 1 && n > 0 && q8c_enabled() &&
+           q8c_plan(a, static_cast<const uint8_t *>(b), n, k, &pl);
 }
 
 size_t lm_head_topk_scratch_bytes(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk, int cus) {
     const size_t part = static_cast<size_t>(kTopkGroups) * topk * sizeof(TopkCand);
-    if (lm_head_f16_logits_route(a, b, fmt, n, k)) return static_cast<size_t>((n * 4 + 255) / 256 * 256) + part;
+    if (lm_head_logits_route(a, b, fmt, n, k, topk)) return static_cast<size_t>((n * 4 + 255) / 256 * 256) + part;
     return static_cast<size_t>(max_topk_lists(cus)) * topk * sizeof(TopkCand) + part;
 }
 
@@ -1266,25 +1297,36 @@ hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n
         if (e != hipSuccess) return e;
     }
     const uint16_t *b16 = static_cast<const uint16_t *>(b);
-    // Top-1 of f16 rows on the K-split route: the argmax fused into the GEMV
-    // (slot set of this stream, or the allocation-free entry point's own).
+    const uint8_t *b8 = static_cast<const uint8_t *>(b);
+    // Fused argmax: slot set of this stream, or the allocation-free entry point's own.
     const int set = workspace ? kStreamSlots : lease.slot();
+    bool argmax_done = false;
     if (topk == 1 && set >= 0 && lm_head_f16_logits_route(a, b, fmt, n, k)) {
         e = f16_ksplit<kModeArgmax>(a, b16, nullptr, n, k, s, set);
+        argmax_done = true;
+    } else if (set >= 0 && lm_head_q8_argmax_route(a, b, fmt, n, k, topk)) {
+        argmax_done = launch_q8c<kModeArgmax>(a, b8, nullptr, n, k, s, set, &e);
+    }
+    if (argmax_done) {
         if (e == hipSuccess) {
             if (trace_enabled()) fprintf(stderr, "[wqmm] argmax_finish set=%d\n", set);
             hipLaunchKernelGGL(argmax_finish, dim3(1), dim3(1024), 0, s, set, vals, ids);
             e = hipGetLastError();
         }
-    } else if (lm_head_f16_logits_route(a, b, fmt, n, k)) {
-        // f16 rows the K-split kernel takes: its logits go to scratch and the
-        // merge reads them 64 at a time.  A per-workgroup top-k list inside that
+    } else if (lm_head_logits_route(a, b, fmt, n, k, topk)) {
+        // The logits go to scratch (608 KB at N = 151936) and the merge reads
+        // them 64 at a time.  A per-workgroup top-k list inside the f16 K-split
         // kernel would need a loop over row blocks, which costs more than the
-        // logits round trip (608 KB at N = 151936).
+        // logits round trip.
         const int64_t lbytes = (n * 4 + 255) / 256 * 256;
         float *logits = static_cast<float *>(scratch);
         TopkCand *partial = reinterpret_cast<TopkCand *>(static_cast<char *>(scratch) + lbytes);
-        e = f16_ksplit<kModeStore>(a, b16, logits, n, k, s, 0);
+        if (fmt == QFMT_Q8_0)
+            e = gemv_q_rows<QFMT_Q8_0, kModeStore>(a, b8, logits, n, k, s, di.cus, 0, nullptr);
+        else if (fmt == QFMT_Q4_0)
+            e = gemv_q_rows<QFMT_Q4_0, kModeStore>(a, b8, logits, n, k, s, di.cus, 0, nullptr);
+        else
+            e = f16_ksplit<kModeStore>(a, b16, logits, n, k, s, 0);
         if (e == hipSuccess) e = launch_topk_merge(nullptr, 0, logits, n, topk, partial, vals, ids, s);
     } else {
         const int64_t cap = max_topk_lists(di.cus);
@@ -1300,11 +1342,9 @@ hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n
         if (n == 0)
             e = hipSuccess;
         else if (fmt == QFMT_Q8_0)
-            e = gemv_q_rows<QFMT_Q8_0, kModeTopk>(a, static_cast<const uint8_t *>(b), out, n, k, s, di.cus, topk,
-                                                  &lists);
+            e = gemv_q_rows<QFMT_Q8_0, kModeTopk>(a, b8, out, n, k, s, di.cus, topk, &lists);
         else if (fmt == QFMT_Q4_0)
-            e = gemv_q_rows<QFMT_Q4_0, kModeTopk>(a, static_cast<const uint8_t *>(b), out, n, k, s, di.cus, topk,
-                                                  &lists);
+            e = gemv_q_rows<QFMT_Q4_0, kModeTopk>(a, b8, out, n, k, s, di.cus, topk, &lists);
         else
             e = gemv_f16_rows<kModeTopk>(a, b16, out, n, k, s, di.cus, topk, &lists);
         if (e == hipSuccess) e = launch_topk_merge(cand, lists, nullptr, 0, topk, partial, vals, ids, s);

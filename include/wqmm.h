@@ -203,16 +203,22 @@ int wq_matmul_ex(const float *a, const void *b, float *c, int64_t m, int64_t n, 
 
 /* Fused LM-head GEMV + top-k for one token: logits[j] = sum_k a[k] w[j, k]
  * for the [n, K] weights b in format fmt (layouts as for the GEMV), and their
- * top-k.  Q8_0 and Q4_0 weights (and f16 rows the K-split GEMV does not take):
- * every wave of the GEMV keeps a sorted top-k list of the rows it computed,
- * without writing the n logits, and two small passes merge the lists.  f16
- * rows on the K-split GEMV (K % 8 == 0, K <= 32768, 16-byte aligned a and b):
- * for topk == 1 every workgroup folds its best (logit, id) into one of 4096
- * device slots with a 64-bit atomic max of an order-keeping key, and a
- * one-workgroup pass takes the best slot and clears the slots for the next
- * call (one slot set per cached stream, one for the allocation-free entry
- * point); for topk > 1 the GEMV writes the logits to scratch and the merge
- * reads them 64 at a time.
+ * top-k.  Routes:
+ *  - topk == 1, f16 rows on the K-split GEMV (K % 8 == 0, K <= 32768, 16-byte
+ *    aligned a and b) or Q8_0 rows on the register-chunk GEMV (the shapes
+ *    wq_set_gemv_plan describes): every workgroup folds its best (logit, id)
+ *    into one of 4096 device slots with a 64-bit atomic max of an
+ *    order-keeping key, and a one-workgroup pass takes the best slot and
+ *    clears the slots for the next call (one slot set per cached stream, one
+ *    for the allocation-free entry point);
+ *  - topk > 1 on those f16 rows, and on Q8_0 / Q4_0 rows with K % 256 == 0 and
+ *    16-byte aligned a and b: the GEMV writes the logits to scratch and the
+ *    merge reads them 64 at a time;
+ *  - everything else (Q4_0 top-1 among them): every wave of the GEMV keeps a
+ *    sorted top-k list of the rows it computed, without writing the n logits,
+ *    and two small passes merge the lists.
+ * The logits are the ones wq_matmul computes for the same arguments, so the
+ * result equals wq_matmul followed by wq_topk.
  * Passage: dispatch_lm_head_block_stage1_enc (fused LM-head GEMV with a
  * block-local exact top-k writing compact (logit, token_id) candidates) and
  * dispatch_block_topk_merge_enc (merge of those candidates), lattice-inference
@@ -228,11 +234,11 @@ int wq_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt
  * holds in every GPU's memory from load until the process ends; the call itself
  * allocates and frees nothing.  It returns WQ_ERR_WORKSPACE (before anything is
  * enqueued) when the call needs more than that: (n * 4 rounded up to 256) +
- * 64 * topk * 8 bytes for f16 weights on the K-split route, else (16 * CUs + 68)
- * * topk * 8 bytes -- at most 2.2 MB on MI355X, and 0.6 MB for the f16 LM head
- * at vocab 151936.  Every list the merge reads is written earlier in the same
- * call, so the array needs no clearing (the top-1 slots of the f16 K-split
- * route are a separate fixed array, cleared by the call that fills them).
+ * 64 * topk * 8 bytes on the logits route, else (16 * CUs + 68) * topk * 8
+ * bytes -- at most 2.2 MB on MI355X, and 0.6 MB for an LM head at vocab
+ * 151936 on the logits route.  Every list or logit the merge reads is written
+ * earlier in the same call, so the array needs no clearing (the top-1 slots
+ * are a separate fixed array, cleared by the call that fills them).
  * All calls on one GPU share its array and slots:
  * calls that may overlap in time on one GPU (different streams, or several host
  * threads without ordering) race; calls on one stream are ordered and safe. */

@@ -285,21 +285,16 @@ def test_topk_of_given_logits_is_exact(n):
 
 @pytest.mark.parametrize("fmt", ALL)
 def test_fused_equals_logits_then_topk(fmt):
-    """The fused call selects on the same f32 logits as the GEMV kernel it fuses
-    (same arithmetic), so it equals that GEMV followed by wq_topk bit for bit.
-    For Q8_0 the fused lists come from the staged GEMV, while a plain Q8_0 LM-head
-    GEMV takes the register-chunk kernel (another summation order), which the
-    reference logits therefore switch off."""
+    """The fused call selects on the same f32 logits as wq_matmul computes (the
+    same GEMV kernel: the argmax and logits routes run the store kernel's
+    arithmetic, the list routes the same row sums), so it equals wq_matmul
+    followed by wq_topk bit for bit."""
     n, k = 151936, 2048
     _, dev_b = encoded(n, k, fmt, 1)
     a = torch.from_numpy(wqgen.activations(1, k, 1)).cuda()
     logits = torch.empty((1, n), device="cuda")
-    try:
-        wq.wq_set_gemv_plan(-1, 0, 0)
-        wq.wq_matmul(a, dev_b, logits, 1, n, k, fmt)
-        torch.cuda.synchronize()
-    finally:
-        wq.wq_set_gemv_plan(0, 0, 0)
+    wq.wq_matmul(a, dev_b, logits, 1, n, k, fmt)
+    torch.cuda.synchronize()
     for topk in (1, 50):
         say(f"fused vs unfused fmt={fmt} topk={topk}")
         v1, i1 = wq.lm_head_topk(a, dev_b, n, k, fmt, topk)

@@ -172,9 +172,13 @@ hipError_t launch_topk_merge(const TopkCand *cand, int64_t lists, const float *l
                     (long long)batches, topk);
         return first(std::max<int64_t>(batches, 1), 1, vals, ids);
     }
-    // About 4 batches per wave, at most kTopkGroups partial lists, then one
-    // workgroup over those (flat for k = 1: single entries).
-    const int64_t want = (batches + 4 * kMergeWaves - 1) / (4 * kMergeWaves);
+    // About one batch per wave, at most kTopkGroups partial lists, then one
+    // workgroup over those (flat for k = 1: single entries).  The first pass
+    // is bound by the instruction rate of the CUs it occupies (a batch that
+    // beats a wave's bar costs a 64-lane sort and merge), so it spreads the
+    // batches over as many CUs as there are groups of 16: measured at
+    // n = 151936, k = 50, 4 batches per wave on 38 CUs took 12.5 us.
+    const int64_t want = (batches + kMergeWaves - 1) / kMergeWaves;
     const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(kTopkGroups, want));
     const int64_t per = (batches + groups - 1) / groups;
     const int64_t used = (batches + per - 1) / per;  // no empty workgroup

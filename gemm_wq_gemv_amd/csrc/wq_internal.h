@@ -349,7 +349,7 @@ size_t lm_head_topk_scratch_bytes(const float *a, const void *b, int fmt, int64_
 // of n values cut into lists of 64 consecutive ids.  Two kernels: up to
 // kTopkGroups workgroups each reduce a share of the lists into `partial`
 // (kTopkGroups * topk entries), then one workgroup reduces those.
-constexpr int kTopkGroups = 64;
+constexpr int kTopkGroups = 256;
 hipError_t launch_topk_merge(const TopkCand *cand, int64_t lists, const float *logits, int64_t n, int topk,
                              TopkCand *partial, float *vals, uint32_t *ids, hipStream_t s);
 

@@ -197,7 +197,7 @@ int wq_matmul_ex(const float *a, const void *b, float *c, int64_t m, int64_t n, 
  * WQ_TOPK_MAX (the pages' block-local k values go up to 64) else
  * WQ_ERR_TOPK; n < WQ_TOPK_NO_ID.  vals and ids are device pointers
  * (4-byte aligned, not overlapping each other or the inputs).  Scratch:
- * about (16 * CUs + 64) * topk * 8 bytes per call, stream-ordered as above. */
+ * about (16 * CUs + 260) * topk * 8 bytes per call, stream-ordered as above. */
 #define WQ_TOPK_MAX 64
 #define WQ_TOPK_NO_ID 0xffffffffu
 
@@ -234,8 +234,8 @@ int wq_lm_head_topk(const float *a, const void *b, int64_t n, int64_t k, int fmt
  * holds in every GPU's memory from load until the process ends; the call itself
  * allocates and frees nothing.  It returns WQ_ERR_WORKSPACE (before anything is
  * enqueued) when the call needs more than that: (n * 4 rounded up to 256) +
- * 64 * topk * 8 bytes on the logits route, else (16 * CUs + 68) * topk * 8
- * bytes -- at most 2.2 MB on MI355X, and 0.6 MB for an LM head at vocab
+ * 256 * topk * 8 bytes on the logits route, else (16 * CUs + 260) * topk * 8
+ * bytes -- at most 2.3 MB on MI355X, and 0.7 MB for an LM head at vocab
  * 151936 on the logits route.  Every list or logit the merge reads is written
  * earlier in the same call, so the array needs no clearing (the top-1 slots
  * are a separate fixed array, cleared by the call that fills them).

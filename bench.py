@@ -145,13 +145,17 @@ def counter_workload(torch, wq, wqgen, seed):
     torch.cuda.synchronize()
     del src, dst
     product("f16 LM head 151936x2048", 1, 151936, 2048, F16)
-    product("Q8_0 LM head 151936x2048", 1, 151936, 2048, Q8)
-    product("Q8_0 GEMV 4096x11008 (K split)", 1, 4096, 11008, Q8)
-    product("Q8_0 GEMV 11008x4096 (staged)", 1, 11008, 4096, Q8)
-    product("Q8_0 small-M 2x11008x4096", 2, 11008, 4096, Q8)
-    product("Q8_0 small-M 8x4096x11008", 8, 4096, 11008, Q8)
+    product("Q8_0 LM head 151936x2048 (register chunks)", 1, 151936, 2048, Q8)
+    product("Q8_0 GEMV 4096x11008 (register chunks)", 1, 4096, 11008, Q8)
+    product("Q8_0 GEMV 11008x4096 (register chunks)", 1, 11008, 4096, Q8)
+    product("Q8_0 GEMV 6144x2048 (staged)", 1, 6144, 2048, Q8)
+    product("Q8_0 stream 2x11008x4096", 2, 11008, 4096, Q8)
+    product("Q8_0 stream 8x4096x11008", 8, 4096, 11008, Q8)
+    product("Q8_0 stream 16x4096x11008", 16, 4096, 11008, Q8)
+    product("Q8_0 stream 16x11008x4096", 16, 11008, 4096, Q8)
+    product("Q8_0 small-M (fp32) 8x4096x11008", 8, 4096, 11008, Q8, wq.WQ_ROUTE_SKINNY)
     product("f16 small-M 4x11008x4096", 4, 11008, 4096, F16)
-    product("Q8_0 GEMM 16x11008x4096", 16, 11008, 4096, Q8)
+    product("Q8_0 GEMM 16x11008x4096", 16, 11008, 4096, Q8, wq.WQ_ROUTE_GEMM)
     product("f16 GEMM 512x6144x2048", 512, 6144, 2048, F16)
     for fmt, key in ((F16, "f16"), (Q8, "Q8_0")):
         bs = rotated(151936, 2048, fmt)

@@ -46,13 +46,23 @@ if ROOT not in sys.path:
 METRIC = "decode GEMV weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
+# The f16 matrix-core routes (stream, f16 matrix-core GEMM) issue two f16
+# products (A's hi and lo halves) per product of the f32 problem: their compute
+# roofline is half the MI355X dense f16 matrix peak (2.5 PFLOP/s).
+F16_PAIR_PEAK_TFLOPS = 2500.0 / 2
 ROTATE_BYTES = 1 << 30
 WARM_GPU_S = 0.05  # sustained GPU time before a timed burst
 DECODE = [("gate_up", 6144, 2048), ("down", 2048, 6144), ("o_proj", 2048, 2048), ("lm_head", 151936, 2048)]
 PREFILL = [(512, 6144, 2048), (512, 2048, 6144)]
 SWEEP_SHAPES = [(11008, 4096), (4096, 11008)]
 SWEEP_M = [1, 2, 4, 8, 16, 64, 512]
-ROUTE_NAMES = {1: "gemv", 2: "gemm", 3: "small_m", 4: "stream"}
+ROUTE_NAMES = {1: "gemv", 2: "gemm", 3: "small_m", 4: "stream", 5: "gemm_f16_pair"}
+F16_PAIR_ROUTES = (4, 5)
+
+
+def compute_peak(route):
+    """Matrix peak (TFLOP/s) of the products a route issues."""
+    return F16_PAIR_PEAK_TFLOPS if route in F16_PAIR_ROUTES else FP32_MFMA_PEAK_TFLOPS
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_f16_lm_head_151936x2048.md")
@@ -798,8 +808,21 @@ def main():
             t = time_launches(torch, lambda i: wq.wq_matmul(a, bs[i % len(bs)], c, m, n, k, F16),
                               max(10, args.steps // 2), args.warmup)
             tf = 2.0 * m * n * k / t / 1e12
-            out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(tf, 2),
-                                   "frac_mfma_fp32": round(tf / FP32_MFMA_PEAK_TFLOPS, 4)}
+            route = wq.wq_route_for(m, n, k, F16)
+            # The same product on the fp32 matrix-core GEMM, for comparison.
+            prev = wq.wq_set_forced_route(wq.WQ_ROUTE_GEMM)
+            try:
+                t32 = time_launches(torch, lambda i: wq.wq_matmul(a, bs[i % len(bs)], c, m, n, k, F16),
+                                    max(10, args.steps // 2), args.warmup)
+            finally:
+                wq.wq_set_forced_route(prev)
+            out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "TFLOP/s": round(tf, 2), "route": ROUTE_NAMES[route],
+                                   "plan": list(wq.wq_hgemm_plan(m, n, k, F16)),
+                                   "frac_mfma_fp32": round(tf / FP32_MFMA_PEAK_TFLOPS, 4),
+                                   "frac_route_peak": round(tf / compute_peak(route), 4),
+                                   "route_peak_TFLOP/s": compute_peak(route),
+                                   "fp32_gemm_us": round(t32 * 1e6, 2),
+                                   "fp32_gemm_TFLOP/s": round(2.0 * m * n * k / t32 / 1e12, 2)}
             del bs, b0
             torch.cuda.empty_cache()
         secondary["f16_prefill_m512"] = out
@@ -822,16 +845,20 @@ def main():
                     t = time_launches(torch, lambda i: wq.wq_matmul(a, bs[i % len(bs)], c, m, n, k, fmt),
                                       max(10, args.steps // 2), args.warmup)
                     gbs, tf = nbytes / t / 1e9, 2.0 * m * n * k / t / 1e12
-                    # Binding roofline: HBM below the ridge (19.7 flop/B), fp32 MFMA above it.
-                    hbm_bound = 2.0 * m * n * k / nbytes < FP32_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+                    # Binding roofline: HBM below the ridge, the route's matrix
+                    # peak above it (ridge 19.7 flop/B for fp32 MFMA, 156 for
+                    # the f16 pairs).
+                    route = wq.wq_route_for(m, n, k, fmt)
+                    peak = compute_peak(route)
+                    hbm_bound = 2.0 * m * n * k / nbytes < peak * 1e12 / (HBM_PEAK_GBS * 1e9)
                     out[f"{m}x{n}x{k}"] = {"us": round(t * 1e6, 2), "weight_GB/s": round(gbs, 1),
                                            "TFLOP/s": round(tf, 2),
                                            "bound": "hbm" if hbm_bound else "mfma",
-                                           "frac_of_bound": round(gbs / HBM_PEAK_GBS if hbm_bound
-                                                                  else tf / FP32_MFMA_PEAK_TFLOPS, 4),
+                                           "frac_of_bound": round(gbs / HBM_PEAK_GBS if hbm_bound else tf / peak, 4),
+                                           "frac_mfma_fp32": round(tf / FP32_MFMA_PEAK_TFLOPS, 4),
                                            "frac_read_ceiling": round(gbs / ceiling[nbytes], 4)
                                            if hbm_bound and nbytes in ceiling else None,
-                                           "route": ROUTE_NAMES[wq.wq_route_for(m, n, k, fmt)]}
+                                           "route": ROUTE_NAMES[route]}
                 del bs, b0
                 torch.cuda.empty_cache()
             secondary[f"{key}_sweep"] = out

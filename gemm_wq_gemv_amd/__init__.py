@@ -48,6 +48,7 @@ WQ_ROUTE_GEMV = 1
 WQ_ROUTE_GEMM = 2
 WQ_ROUTE_SKINNY = 3
 WQ_ROUTE_STREAM = 4
+WQ_ROUTE_GEMM_HL = 5
 
 WQ_EPI_NONE = 0
 WQ_EPI_RESIDUAL = 1
@@ -91,6 +92,8 @@ def _load() -> ctypes.CDLL:
         "wq_route_for": (I, [I64, I64, I64, I]),
         "wq_gemm_plan": (I, [I64, I64, I64, I, I, P, P, P]),
         "wq_set_gemm_plan": (I, [I, I, I]),
+        "wq_hgemm_plan": (I, [I64, I64, I64, I, I, P, P, P]),
+        "wq_set_hgemm_plan": (I, [I, I, I]),
         "wq_set_gemv_plan": (I, [I, I, I]),
         "wq_set_stream_plan": (I, [I, I]),
         "wq_set_forced_route": (I, [I]),
@@ -337,6 +340,21 @@ def wq_gemm_plan(m: int, n: int, k: int, fmt: int, cus: int = 256):
 
 def wq_set_gemm_plan(bm: int, bn: int, splits: int) -> None:
     _check(_lib.wq_set_gemm_plan(bm, bn, splits), "wq_set_gemm_plan")
+
+
+def wq_hgemm_plan(m: int, n: int, k: int, fmt: int, cus: int = 256):
+    """(bm, bn, splits) the f16 matrix-core GEMM uses for this problem."""
+    bm, bn, sp = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(_lib.wq_hgemm_plan(m, n, k, fmt, cus, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(sp)),
+           "wq_hgemm_plan")
+    return bm.value, bn.value, sp.value
+
+
+def wq_set_hgemm_plan(bm: int, bn: int, splits: int) -> None:
+    _check(_lib.wq_set_hgemm_plan(bm, bn, splits), "wq_set_hgemm_plan")
+
+
+HGEMM_TILES = [(128, 128), (128, 64), (64, 128), (64, 64)]
 
 
 def wq_set_gemv_plan(rb: int, nf: int, nr: int) -> None:

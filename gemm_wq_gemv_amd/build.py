@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libwqmm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["wqmm_api.hip", "gemv.hip", "gemm.hip", "skinny.hip", "pack.hip", "topk.hip", "attn.hip", "probe.hip", "smallm.hip", "wstream.hip"]
+SOURCES = ["wqmm_api.hip", "gemv.hip", "gemm.hip", "skinny.hip", "pack.hip", "topk.hip", "attn.hip", "probe.hip", "smallm.hip", "wstream.hip", "hgemm.hip"]
 
 # gfx950 only.  Packed-FP32 VALU ops are disabled for all device code; the
 # host pass does not know that target feature and warns, which is harmless.
@@ -40,10 +40,17 @@ def _run(cmd):
     return out
 
 
+# Per-file flags.  hgemm.hip: matrix-core results in ordinary VGPRs (the lane
+# scales and adds them; without this the compiler keeps them in AGPRs and
+# copies them back and forth every step).
+FILE_FLAGS = {"hgemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *HIPFLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    cmds = [[HIPCC, *HIPFLAGS, *FILE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():

@@ -49,19 +49,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int BK = 32;
 constexpr int PAD = 4;            // floats of padding per LDS row
 constexpr int LDP = BK + PAD;     // LDS row pitch in floats
-constexpr int kXcds = 8;
 constexpr int kQ8BlockBytes = 34;
 constexpr int kQ4BlockBytes = 18;
 
 enum { FMT_F16 = 0, FMT_Q8_0 = 1, FMT_Q4_0 = 2 };
-
-// Tile id for workgroup `bid` of `tiles`, so that XCD x (= bid % 8) receives a
-// contiguous range of tile ids.
-__device__ __forceinline__ int xcd_tile(int bid, int tiles) {
-    const int q = tiles / kXcds, r = tiles % kXcds;
-    const int x = bid % kXcds, local = bid / kXcds;
-    return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
-}
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -496,7 +487,7 @@ hipError_t run(const float *a, const void *b, float *c, int64_t m, int64_t n, in
 // M = 512 prefill shapes and the Q8_0 M sweep (M = 2 .. 64).
 constexpr TileCfg kCfgs[] = {
     {128, 128, 2, 0.90}, {128, 96, 2, 0.873}, {128, 64, 2, 0.837}, {64, 128, 2, 0.837},
-    {64, 64, 4, 0.80},   {32, 128, 3, 0.70},  {16, 128, 3, 0.35},  {16, 64, 6, 0.30},
+    {64, 64, 4, 0.76},   {32, 128, 3, 0.70},  {16, 128, 3, 0.35},  {16, 64, 6, 0.30},
 };
 
 // Cost model over tile shapes and K splits, in CU clock cycles.  The busiest

@@ -28,6 +28,17 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
+// Workgroups are dealt round-robin to the 8 XCDs of the chip (workgroup b runs
+// on XCD b % 8).  Tile id for workgroup `bid` of `tiles`, such that XCD x
+// receives a contiguous range of tile ids (neighbouring tiles share operand
+// rows and so hit the same L2).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile(int bid, int tiles) {
+    const int q = tiles / kXcds, r = tiles % kXcds;
+    const int x = bid % kXcds, local = bid / kXcds;
+    return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
     return __builtin_bit_cast(
@@ -364,6 +375,18 @@ void set_attn_partition_override(int64_t tokens);
 // n = output columns; with kEpiGlu the weights have 2n rows.
 hipError_t launch_gemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n,
                        int64_t k, hipStream_t s, int epi = kEpiNone);
+// Product through the f16 matrix cores with A split into hi / lo f16 halves
+// (hgemm_ok: K % 32 == 0, 16-byte aligned a and b, quantized weights under
+// 2 GiB); n = output columns (2n
+// weight rows with kEpiGlu).  Uses the stream's scratch for the split A.
+// nw: weight rows (2n with kEpiGlu).
+bool hgemm_ok(const float *a, const void *b, int fmt, int64_t m, int64_t nw, int64_t k);
+hipError_t launch_hgemm(const float *a, const void *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
+                        hipStream_t s, int epi = kEpiNone);
+// Tile shape and K splits of that product; test hook forcing them ((0, 0, 0)
+// clears; false for a tile that is not compiled in).
+void hgemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits);
+bool set_hgemm_plan_override(int bm, int bn, int splits);
 // Small-M product for Q8_0 / Q4_0 weights with K % 256 == 0 and 16-byte
 // aligned a and b (smallm_ok), 1 <= M <= 16; n = output columns (2n weight
 // rows with kEpiGlu).

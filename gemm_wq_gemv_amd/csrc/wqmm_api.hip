@@ -18,7 +18,7 @@ DeviceInfo g_dev[kMaxDevices];
 hipError_t g_dev_err[kMaxDevices];
 
 std::atomic<int> g_forced_route{WQ_ROUTE_AUTO};
-std::atomic<uint64_t> g_route_count[5];
+std::atomic<uint64_t> g_route_count[6];
 
 int trace_flag() {
     static const int v = [] {
@@ -214,20 +214,23 @@ int validate(const float *a, const void *b, const float *c, int64_t m, int64_t n
 int status_of(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_LAUNCH; }
 
 // M == 1: the decode GEMV; small M: weight-streaming kernels; larger M: the
-// LDS-tiled GEMM.  Quantized weights with K % 256 == 0 take the f16
-// matrix-core stream for M <= 16 (its time hardly depends on M: measured on
-// MI355X at (N, K) = (11008, 4096) and (4096, 11008) it beats the tiled GEMM up
-// to M = 16); other quantized shapes take the fp32 small-M kernel up to M = 4,
-// f16 weights up to M = 8 (crossovers measured on the same shapes).
+// LDS-tiled GEMM on the f16 matrix cores (A as hi / lo halves).  Quantized
+// weights with K % 256 == 0 take the f16 matrix-core stream for M <= 16 (its
+// time hardly depends on M: measured on MI355X at (N, K) = (11008, 4096) and
+// (4096, 11008) it beats the tiled products up to M = 16); other quantized
+// shapes take the fp32 small-M kernel up to M = 4, f16 weights up to M = 8
+// (crossovers measured on the same shapes).  Calls the tiled f16 product cannot
+// take (K % 32 != 0, misaligned a or b) go to the fp32 GEMM at launch.
 constexpr int64_t kSkinnyRows = 16;  // rows of A per small-M launch
 int auto_route(int64_t m, int64_t k, int fmt) {
     if (m <= 1) return WQ_ROUTE_GEMV;
-    if (fmt == WQ_FMT_F16) return m <= 8 ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;
-    if (k % 256 == 0) return m <= 16 ? WQ_ROUTE_STREAM : WQ_ROUTE_GEMM;  // alignment is checked at launch
-    return m <= 4 ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM;  // Q4_0 as Q8_0
+    if (fmt == WQ_FMT_F16) return m <= 8 ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM_HL;
+    if (k % 256 == 0) return m <= 16 ? WQ_ROUTE_STREAM : WQ_ROUTE_GEMM_HL;  // alignment is checked at launch
+    return m <= 4 ? WQ_ROUTE_SKINNY : WQ_ROUTE_GEMM_HL;  // Q4_0 as Q8_0
 }
 bool known_route(int r) {
-    return r == WQ_ROUTE_GEMV || r == WQ_ROUTE_GEMM || r == WQ_ROUTE_SKINNY || r == WQ_ROUTE_STREAM;
+    return r == WQ_ROUTE_GEMV || r == WQ_ROUTE_GEMM || r == WQ_ROUTE_SKINNY || r == WQ_ROUTE_STREAM ||
+           r == WQ_ROUTE_GEMM_HL;
 }
 
 // Kernel-side epilogue code of a wq_epilogue value.
@@ -258,6 +261,17 @@ int run_gemm(const float *a, const void *b, float *c, int64_t m, int64_t n, int6
     hipError_t e = wq::launch_gemm(a, b, fmt, c, m, n, k, s, kernel_epi(epi));
     if (e != hipSuccess) return WQ_ERR_LAUNCH;
     wq::g_route_count[WQ_ROUTE_GEMM].fetch_add(1, std::memory_order_relaxed);
+    return WQ_OK;
+}
+
+// The tiled product on the f16 matrix cores where it applies (K % 32 == 0,
+// 16-byte aligned a and b, quantized weights under 2 GiB); anything else takes
+// the fp32 GEMM.
+int run_gemm_hl(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
+                int epi) {
+    if (!wq::hgemm_ok(a, b, fmt, m, epi == WQ_EPI_SWIGLU ? 2 * n : n, k)) return run_gemm(a, b, c, m, n, k, fmt, s, epi);
+    if (wq::launch_hgemm(a, b, fmt, c, m, n, k, s, kernel_epi(epi)) != hipSuccess) return WQ_ERR_LAUNCH;
+    wq::g_route_count[WQ_ROUTE_GEMM_HL].fetch_add(1, std::memory_order_relaxed);
     return WQ_OK;
 }
 
@@ -311,6 +325,7 @@ int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, in
     if (route == WQ_ROUTE_GEMV) return run_gemv(a, b, c, m, n, k, fmt, s, epi);
     if (route == WQ_ROUTE_SKINNY) return run_skinny(a, b, c, m, n, k, fmt, s, epi);
     if (route == WQ_ROUTE_STREAM) return run_stream(a, b, c, m, n, k, fmt, s, epi);
+    if (route == WQ_ROUTE_GEMM_HL) return run_gemm_hl(a, b, c, m, n, k, fmt, s, epi);
     return run_gemm(a, b, c, m, n, k, fmt, s, epi);
 }
 
@@ -318,7 +333,7 @@ int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, in
 
 extern "C" {
 
-int wq_abi_version(void) { return 105; }
+int wq_abi_version(void) { return 106; }
 
 const char *wq_status_str(int status) {
     switch (status) {
@@ -543,6 +558,19 @@ int wq_gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int
 
 int wq_set_gemm_plan(int bm, int bn, int splits) {
     return wq::set_gemm_plan_override(bm, bn, splits) ? WQ_OK : WQ_ERR_SHAPE;
+}
+
+int wq_hgemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits) {
+    if (!known_format(fmt)) return WQ_ERR_FORMAT;
+    if (m <= 0 || n <= 0 || k <= 0 || cus <= 0) return WQ_ERR_SHAPE;
+    if (k % 32 != 0) return WQ_ERR_K;
+    if (!bm || !bn || !splits) return WQ_ERR_NULL;
+    wq::hgemm_plan(m, n, k, fmt, cus, bm, bn, splits);
+    return WQ_OK;
+}
+
+int wq_set_hgemm_plan(int bm, int bn, int splits) {
+    return wq::set_hgemm_plan_override(bm, bn, splits) ? WQ_OK : WQ_ERR_SHAPE;
 }
 
 int wq_set_gemv_plan(int rb, int nf, int nr) {

@@ -96,12 +96,20 @@ typedef enum wq_route {
     WQ_ROUTE_GEMM = 2,  /* LDS-tiled fp32-MFMA GEMM */
     WQ_ROUTE_SKINNY = 3, /* small-M weight-streaming fp32-MFMA product: one
                             launch per block of up to 16 rows of A */
-    WQ_ROUTE_STREAM = 4  /* small-M weight stream through the f16 matrix cores
+    WQ_ROUTE_STREAM = 4, /* small-M weight stream through the f16 matrix cores
                             with f32 results (Q8_0 / Q4_0, K % 256 == 0,
                             M * K <= 196608 per block of rows, 16-byte aligned
                             a and b, no SwiGLU; other calls on this route take
                             WQ_ROUTE_SKINNY): one launch per block of up to 16
                             rows of A */
+    WQ_ROUTE_GEMM_HL = 5 /* LDS-tiled GEMM on the f16 matrix cores with f32
+                            results: each row of A is scaled by a power of two
+                            and split into hi + lo f16 halves (22 significant
+                            bits), weights are exact in f16, products exact in
+                            f32 and summed in f32 (K % 32 == 0, 16-byte aligned
+                            a and b; other calls on this route take
+                            WQ_ROUTE_GEMM).  Scratch: M * K * 4 bytes for the
+                            split A, plus the split-K partial sums */
 } wq_route;
 
 /* ---------------------------------------------------------------------- */
@@ -131,7 +139,8 @@ int wq_gemm_q4_0(const float *a, const uint8_t *b, float *c, int64_t m, int64_t 
  * matrix-core weight stream (activations carried as two f16 parts, hi + lo,
  * after a power-of-two scaling per row and K range, so the product keeps f32
  * accuracy; f32 accumulation); other quantized shapes the fp32 small-M kernel
- * up to M == 4, f16 weights up to M == 8; larger M the tiled GEMM, unless a
+ * up to M == 4, f16 weights up to M == 8; larger M the tiled GEMM on the f16
+ * matrix cores (WQ_ROUTE_GEMM_HL, A split the same way per row), unless a
  * route is forced (wq_set_forced_route).  The small-M kernels read every weight
  * once per 16 rows of A; when they split K (and for the SwiGLU epilogue on the
  * fp32 small-M kernel) they use the same scratch as the GEMM (splits*M*N*4
@@ -323,7 +332,7 @@ int wq_read_probe(const void *p, int64_t bytes, uint32_t *out, int variant, void
 /* Routing and introspection (host only; these never touch the GPU). */
 
 /* The route wq_matmul takes for these arguments when nothing is forced
- * (WQ_ROUTE_GEMV, WQ_ROUTE_STREAM, WQ_ROUTE_SKINNY or WQ_ROUTE_GEMM), or a
+ * (WQ_ROUTE_GEMV, WQ_ROUTE_STREAM, WQ_ROUTE_SKINNY or WQ_ROUTE_GEMM_HL), or a
  * negative wq_status
  * on bad arguments. */
 int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt);
@@ -341,6 +350,15 @@ int wq_gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int
  * 32x128, 16x128, 16x64.  Returns WQ_ERR_SHAPE for anything else.  Results
  * do not depend on the tiling beyond f32 rounding. */
 int wq_set_gemm_plan(int bm, int bn, int splits);
+
+/* The tiling of the f16 matrix-core GEMM (WQ_ROUTE_GEMM_HL) for (m, n, k,
+ * fmt) on `cus` compute units, as wq_gemm_plan; k % 32 == 0. */
+int wq_hgemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits);
+
+/* Test and tuning hook: force every later WQ_ROUTE_GEMM_HL product onto tile
+ * (bm, bn) (128x128, 128x64, 64x128 or 64x64) with `splits` K splits (capped
+ * at K / 32); (0, 0, 0) restores the cost model.  WQ_ERR_SHAPE otherwise. */
+int wq_set_hgemm_plan(int bm, int bn, int splits);
 
 /* Test and tuning hook for the Q8_0 decode GEMV (M == 1, K % 256 == 0,
  * 16-byte aligned operands, N * K * 34 / 32 < 2^31 bytes): force every later
@@ -371,7 +389,7 @@ int wq_set_stream_plan(int shape, int splits);
  * routes agree (the pages' test hook forcing the fallback GEMM). */
 int wq_set_forced_route(int route);
 
-/* Kernel launches made so far per route (GEMV, GEMM, SKINNY or STREAM) by
+/* Kernel launches made so far per route (GEMV, GEMM, SKINNY, STREAM or GEMM_HL) by
  * any entry point, and a reset.  The pages keep such "path proof" counters. */
 uint64_t wq_route_count(int route);
 void wq_reset_route_counts(void);

@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process():
 
 
 def test_abi_and_status_strings():
-    assert wq.wq_abi_version() == 105
+    assert wq.wq_abi_version() == 106
     for st in range(0, 11):
         assert wq.status_str(st)
     assert wq.status_str(99) == "unknown status"
@@ -190,7 +190,9 @@ def test_decode_attention_validation():
 
 def test_routing_rule():
     """M = 1: GEMV; quantized with K % 256 == 0: 2..16 the f16 matrix-core
-    stream; other quantized K: 2..4 small-M; f16: 2..8 small-M; more: GEMM."""
+    stream; other quantized K: 2..4 small-M; f16: 2..8 small-M; more: the
+    tiled f16 matrix-core GEMM (which hands calls it cannot take to the fp32
+    GEMM at launch)."""
     for fmt in (wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0):
         for k in (4096, 4128):
             assert wq.wq_route_for(1, 4096, k, fmt) == wq.WQ_ROUTE_GEMV
@@ -201,7 +203,7 @@ def test_routing_rule():
             for m in range(2, top + 1):
                 assert wq.wq_route_for(m, 4096, k, fmt) == small
             for m in (top + 1, 17, 64, 512):
-                assert wq.wq_route_for(m, 4096, k, fmt) == wq.WQ_ROUTE_GEMM
+                assert wq.wq_route_for(m, 4096, k, fmt) == wq.WQ_ROUTE_GEMM_HL
     assert wq.wq_route_for(2, 8, 33, wq.WQ_FMT_Q8_0) == -wq.WQ_ERR_K
     assert wq.wq_route_for(2, 8, 48, wq.WQ_FMT_Q4_0) == -wq.WQ_ERR_K
     assert wq.wq_route_for(2, 8, 32, 5) == -wq.WQ_ERR_FORMAT
@@ -215,12 +217,13 @@ def test_forced_route_setting():
         assert wq.wq_set_forced_route(wq.WQ_ROUTE_GEMV) == wq.WQ_ROUTE_GEMM
         assert wq.wq_set_forced_route(wq.WQ_ROUTE_SKINNY) == wq.WQ_ROUTE_GEMV
         assert wq.wq_set_forced_route(wq.WQ_ROUTE_STREAM) == wq.WQ_ROUTE_SKINNY
+        assert wq.wq_set_forced_route(wq.WQ_ROUTE_GEMM_HL) == wq.WQ_ROUTE_STREAM
         assert wq.wq_set_forced_route(7) == -wq.WQ_ERR_ROUTE
         assert wq.wq_set_forced_route(-1) == -wq.WQ_ERR_ROUTE
     finally:
         wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
     wq.wq_reset_route_counts()
-    for r in (wq.WQ_ROUTE_GEMV, wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_STREAM):
+    for r in (wq.WQ_ROUTE_GEMV, wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_STREAM, wq.WQ_ROUTE_GEMM_HL):
         assert wq.wq_route_count(r) == 0
     assert wq.wq_route_count(99) == 0
 
@@ -307,3 +310,38 @@ def test_gemm_plan_override_hook():
         wq.wq_set_gemm_plan(0, 0, 0)
     assert wq.wq_gemm_plan(512, 6144, 2048, wq.WQ_FMT_F16) == (64, 64, 1)
     assert L.wq_gemm_plan(0, 1, 1, 0, 256, None, None, None) == wq.WQ_ERR_SHAPE
+
+
+def test_hgemm_planner_invariants():
+    """The f16 matrix-core GEMM's plans: a compiled tile, no empty split, no
+    128-row tile for M <= 64, and the measured-fastest tilings of the M = 512
+    prefill shapes."""
+    for m in (2, 17, 33, 64, 130, 512, 4096):
+        for n in (1, 97, 2048, 11008):
+            for k in (32, 1024, 2048, 11008):
+                for fmt in (wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0):
+                    bm, bn, sp = wq.wq_hgemm_plan(m, n, k, fmt)
+                    assert (bm, bn) in wq.HGEMM_TILES
+                    kt = k // 32
+                    assert 1 <= sp <= kt
+                    assert (sp - 1) * (-(-kt // sp)) < kt
+                    if m <= 64:
+                        assert bm == 64
+    assert wq.wq_hgemm_plan(512, 6144, 2048, wq.WQ_FMT_F16) == (64, 128, 2)
+    assert wq.wq_hgemm_plan(512, 2048, 6144, wq.WQ_FMT_F16) == (64, 128, 4)
+    assert wq.wq_hgemm_plan(512, 4096, 11008, wq.WQ_FMT_Q8_0) == (64, 128, 2)
+
+
+def test_hgemm_plan_override_hook():
+    try:
+        wq.wq_set_hgemm_plan(128, 64, 3)
+        assert wq.wq_hgemm_plan(512, 6144, 2048, wq.WQ_FMT_F16) == (128, 64, 3)
+        assert wq.wq_hgemm_plan(5, 10, 64, wq.WQ_FMT_F16) == (128, 64, 2)   # capped at 2 k-steps
+        for bad in ((32, 128, 1), (96, 64, 1), (64, 64, 0), (64, 64, 65)):
+            with pytest.raises(wq.WQError):
+                wq.wq_set_hgemm_plan(*bad)
+    finally:
+        wq.wq_set_hgemm_plan(0, 0, 0)
+    assert wq.wq_hgemm_plan(512, 6144, 2048, wq.WQ_FMT_F16) == (64, 128, 2)
+    assert L.wq_hgemm_plan(0, 1, 1, 0, 256, None, None, None) == wq.WQ_ERR_SHAPE
+    assert L.wq_hgemm_plan(4, 1, 48, 0, 256, None, None, None) == wq.WQ_ERR_K

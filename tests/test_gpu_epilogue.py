@@ -27,7 +27,7 @@ F16, Q8, Q4 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0
 ALL = [F16, Q8, Q4]
 RES, GLU = wq.WQ_EPI_RESIDUAL, wq.WQ_EPI_SWIGLU
 ROUTES = {"gemv": wq.WQ_ROUTE_GEMV, "skinny": wq.WQ_ROUTE_SKINNY, "gemm": wq.WQ_ROUTE_GEMM,
-          "stream": wq.WQ_ROUTE_STREAM, "auto": wq.WQ_ROUTE_AUTO}
+          "stream": wq.WQ_ROUTE_STREAM, "gemm_hl": wq.WQ_ROUTE_GEMM_HL, "auto": wq.WQ_ROUTE_AUTO}
 
 
 def say(msg: str):
@@ -99,7 +99,7 @@ SHAPES = {F16: [(1, 37, 1000), (3, 300, 2048), (13, 129, 96), (37, 97, 1003), (5
           Q4: [(1, 37, 992), (3, 300, 2048), (13, 129, 96), (37, 97, 1024), (5, 1000, 8192)]}
 
 
-@pytest.mark.parametrize("route", ["gemv", "skinny", "gemm", "stream", "auto"])
+@pytest.mark.parametrize("route", ["gemv", "skinny", "gemm", "stream", "gemm_hl", "auto"])
 @pytest.mark.parametrize("epi", [RES, GLU], ids=["residual", "swiglu"])
 @pytest.mark.parametrize("fmt", ALL)
 def test_epilogue_every_route(fmt, epi, route):

@@ -361,7 +361,7 @@ def test_deterministic_and_linear(fmt, m):
     assert np.array_equal(c1, c2)
     assert np.array_equal(run_gpu("matmul", fmt, 2 * a, dev_b, m, n, k), 2 * c1)
     cneg = run_gpu("matmul", fmt, -a, dev_b, m, n, k)
-    if wq.wq_route_for(m, n, k, fmt) == wq.WQ_ROUTE_STREAM:
+    if wq.wq_route_for(m, n, k, fmt) in (wq.WQ_ROUTE_STREAM, wq.WQ_ROUTE_GEMM_HL):
         # The f16 matrix core's internal sums do not round symmetrically
         # (negating the operands can move a result by an ulp); the result is
         # still within the oracle's bound of the negated product.
@@ -376,21 +376,22 @@ def test_deterministic_and_linear(fmt, m):
 @pytest.mark.parametrize("fmt", ALL)
 def test_routes_agree_and_are_counted(fmt):
     """Every route gives the oracle's product for any M, and the path-proof
-    counters show which kernels ran: the GEMV once per row of A, the GEMM once,
-    the small-M kernel once per 16 rows of A."""
+    counters show which kernels ran: the GEMV once per row of A, either GEMM
+    once, the small-M kernels once per 16 rows of A."""
     n, k = 1000, 1024
     ref_b, dev_b = encoded(n, k, fmt, 7)
     ms = (1, 3, 20)
     c_ref = {m: oracle.matmul(acts(m, k, 7), ref_b, fmt, m, n, k) for m in ms}
-    routes = (wq.WQ_ROUTE_GEMV, wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_STREAM)
-    skinny = {1: (0, 0, 1, 0), 3: (0, 0, 1, 0), 20: (0, 0, 2, 0)}
-    stream = skinny if fmt == F16 else {1: (0, 0, 0, 1), 3: (0, 0, 0, 1), 20: (0, 0, 0, 2)}
+    routes = (wq.WQ_ROUTE_GEMV, wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_STREAM, wq.WQ_ROUTE_GEMM_HL)
+    skinny = {1: (0, 0, 1, 0, 0), 3: (0, 0, 1, 0, 0), 20: (0, 0, 2, 0, 0)}
+    stream = skinny if fmt == F16 else {1: (0, 0, 0, 1, 0), 3: (0, 0, 0, 1, 0), 20: (0, 0, 0, 2, 0)}
     expect = {
-        wq.WQ_ROUTE_GEMV: {1: (1, 0, 0, 0), 3: (3, 0, 0, 0), 20: (20, 0, 0, 0)},
-        wq.WQ_ROUTE_GEMM: {1: (0, 1, 0, 0), 3: (0, 1, 0, 0), 20: (0, 1, 0, 0)},
+        wq.WQ_ROUTE_GEMV: {1: (1, 0, 0, 0, 0), 3: (3, 0, 0, 0, 0), 20: (20, 0, 0, 0, 0)},
+        wq.WQ_ROUTE_GEMM: {1: (0, 1, 0, 0, 0), 3: (0, 1, 0, 0, 0), 20: (0, 1, 0, 0, 0)},
         wq.WQ_ROUTE_SKINNY: skinny,
         wq.WQ_ROUTE_STREAM: stream,
-        wq.WQ_ROUTE_AUTO: {1: (1, 0, 0, 0), 3: skinny[3] if fmt == F16 else stream[3], 20: (0, 1, 0, 0)},
+        wq.WQ_ROUTE_GEMM_HL: {1: (0, 0, 0, 0, 1), 3: (0, 0, 0, 0, 1), 20: (0, 0, 0, 0, 1)},
+        wq.WQ_ROUTE_AUTO: {1: (1, 0, 0, 0, 0), 3: skinny[3] if fmt == F16 else stream[3], 20: (0, 0, 0, 0, 1)},
     }
     try:
         for route, per_call in expect.items():
@@ -587,7 +588,7 @@ def test_edge_blocks_every_route_bit_exact(fmt, k):
     want = w[:, pos].T                                        # [rows of A, n]
     dev_b = torch.from_numpy(raw).cuda()
     routes = ((wq.WQ_ROUTE_GEMV, "gemv"), (wq.WQ_ROUTE_SKINNY, "small-M"), (wq.WQ_ROUTE_STREAM, "stream"),
-              (wq.WQ_ROUTE_GEMM, "gemm"))
+              (wq.WQ_ROUTE_GEMM, "gemm"), (wq.WQ_ROUTE_GEMM_HL, "f16 matrix-core gemm"))
     try:
         for route, name in routes:
             wq.wq_set_forced_route(route)
@@ -608,6 +609,17 @@ def test_edge_blocks_every_route_bit_exact(fmt, k):
                     assert np.array_equal(c.astype(np.float64), want), f"plan {bm}x{bn}/{sp}"
         finally:
             wq.wq_set_gemm_plan(0, 0, 0)
+        try:
+            wq.wq_set_forced_route(wq.WQ_ROUTE_GEMM_HL)
+            for bm, bn in wq.HGEMM_TILES:
+                for sp in (1, 3):
+                    say(f"edge blocks fmt={fmt} k={k} f16 matrix-core plan {bm}x{bn}/{sp}")
+                    wq.wq_set_hgemm_plan(bm, bn, sp)
+                    c = run_gpu("matmul", fmt, a, dev_b, len(pos), n, k)
+                    assert np.array_equal(c.astype(np.float64), want), f"hl plan {bm}x{bn}/{sp}"
+        finally:
+            wq.wq_set_hgemm_plan(0, 0, 0)
+            wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
 
 
 def q8_chunk_plan_fits(k, rb, nf, nr):
@@ -678,7 +690,7 @@ def test_identity_a_edge_blocks(fmt):
     w = oracle.decode(raw, fmt, n, k)
     dev_b = torch.from_numpy(raw).cuda()
     try:
-        for route in (wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_STREAM):
+        for route in (wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_STREAM, wq.WQ_ROUTE_GEMM_HL):
             wq.wq_set_forced_route(route)
             say(f"identity a, edge blocks fmt={fmt} route={route}")
             c = run_gpu("matmul", fmt, np.eye(k, dtype=np.float32), dev_b, k, n, k)
@@ -710,7 +722,7 @@ def test_partial_step_does_not_read_the_next_row(fmt, m):
     a_buf[1:].copy_(torch.from_numpy(a.ravel()))
     L = wq._lib
     s = torch.cuda.current_stream().cuda_stream
-    for route in (wq.WQ_ROUTE_AUTO, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_GEMM):
+    for route in (wq.WQ_ROUTE_AUTO, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_GEMM_HL):
         say(f"partial step, next row inf, fmt={fmt} m={m} route={route}")
         c = torch.full((m, n), float("nan"), device="cuda")
         prev = wq.wq_set_forced_route(route)

@@ -166,7 +166,9 @@ def counter_workload(torch, wq, wqgen, seed):
     product("Q8_0 small-M (fp32) 8x4096x11008", 8, 4096, 11008, Q8, wq.WQ_ROUTE_SKINNY)
     product("f16 small-M 4x11008x4096", 4, 11008, 4096, F16)
     product("Q8_0 GEMM 16x11008x4096", 16, 11008, 4096, Q8, wq.WQ_ROUTE_GEMM)
-    product("f16 GEMM 512x6144x2048", 512, 6144, 2048, F16)
+    product("f16 GEMM 512x6144x2048 (f16 matrix cores)", 512, 6144, 2048, F16)
+    product("Q8_0 GEMM 512x4096x11008 (f16 matrix cores)", 512, 4096, 11008, Q8)
+    product("f16 GEMM 512x6144x2048 (fp32 MFMA)", 512, 6144, 2048, F16, wq.WQ_ROUTE_GEMM)
     for fmt, key in ((F16, "f16"), (Q8, "Q8_0")):
         bs = rotated(151936, 2048, fmt)
         a = torch.from_numpy(wqgen.activations(1, 2048, seed)).cuda()

@@ -55,7 +55,7 @@ def run(a_np, b_dev, m, n, k, fmt, epi=wq.WQ_EPI_NONE, c_init=None):
 # The last K is past the split pass's one-read limit (16384 columns): that row
 # is read twice.
 SHAPES = [(17, 100, 96), (64, 128, 256), (65, 300, 1056), (130, 257, 2080), (200, 520, 512), (512, 640, 384),
-          (20, 70, 16448)]
+          (33, 90, 4128), (20, 70, 16448)]
 
 
 @pytest.mark.parametrize("fmt", ALL)

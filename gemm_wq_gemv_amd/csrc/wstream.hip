@@ -503,16 +503,42 @@ int ws_min_splits(int64_t m, int nsb) {
 // has about two workgroups per CU: fewer, longer workgroups (or a count just
 // above the CU count) left the last round of the grid underused (e.g. 3 splits
 // of 16 superblocks at (11008, 4096): 21-22 us against 18-19 us for 4 or 8).
+// Workgroup shape and K splits by M and the weight size, the rule that came
+// closest to the best of every (shape, split) choice measured on MI355X for
+// Q8_0 and Q4_0 at M = 2, 4, 8, 16 over (N, K) = (6144, 2048), (2048, 6144),
+// (2048, 2048), (11008, 4096), (4096, 11008), (151936, 2048): within 2 % on
+// average and 16 % at worst (the previous fixed choice: 11 % and 46 %).
+// Shapes (0-based): 8 = one 16-row tile per wave, 4 tile groups per
+// workgroup; 10 = 8 K sub-ranges per workgroup; 12 / 13 = 8 tile groups of
+// one or two tiles.  splits = 0: about two workgroups per CU.
+struct WsRule {
+    int shape, splits;
+};
+WsRule ws_rule(int64_t m, int64_t n, int64_t k) {
+    const int64_t nk = n * k;
+    if (nk > (64LL << 20)) return WsRule{m >= 16 ? 13 : 12, 0};
+    if (nk > (16LL << 20)) {
+        if (m <= 4) return WsRule{8, 0};
+        if (m <= 8) return WsRule{12, 8};
+        return WsRule{n <= 6144 ? 13 : 12, 8};
+    }
+    if (m <= 2) return k > 4096 ? WsRule{8, 0} : WsRule{10, 1};
+    if (m <= 4) return WsRule{8, 8};
+    return WsRule{8, 0};
+}
+
 WsPlan ws_plan(int64_t m, int64_t n, int64_t k, int cus) {
     const int nsb = static_cast<int>(k / 256);
     const int smin = ws_min_splits(m, nsb);
-    int shape = m > 8 && n <= 6144 ? 13 : 12;
+    const WsRule rule = ws_rule(m, n, k);
+    int shape = rule.shape;
     if (const int fs = g_ws_shape.load(std::memory_order_relaxed); fs > 0) shape = fs - 1;
     const WsShape &sh = kWsShapes[shape];
     const int64_t rows = 16LL * sh.p * sh.tw;
     const int64_t groups = (n + rows - 1) / rows;
     int64_t splits = 1;
     while (splits < 8 && splits * groups < 2LL * cus) splits *= 2;
+    if (rule.splits > 0) splits = rule.splits;
     if (const int fsp = g_ws_splits.load(std::memory_order_relaxed); fsp > 0) splits = fsp;
     splits = std::min<int64_t>(std::min<int64_t>(std::max<int64_t>(splits, smin), nsb), kWsMaxSplits);
     return WsPlan{shape, static_cast<int>(groups), static_cast<int>(splits)};

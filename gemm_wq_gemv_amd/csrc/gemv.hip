@@ -243,8 +243,6 @@ struct QB {
     static constexpr int kChunks = FMT == QFMT_Q8_0 ? 17 : 18;
     static constexpr int kStage = kChunks * 64 * 16;
 };
-constexpr int kQ8BlockBytes = QB<QFMT_Q8_0>::kBytes;
-constexpr int kQ4BlockBytes = QB<QFMT_Q4_0>::kBytes;
 
 // Dot product of one Q8_0 block held in LDS at byte offset pb with the 32
 // activations av[0..31]: returns d * sum_i q_i * av[i].
@@ -551,28 +549,43 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void gemv_q_ksplit(const fl
     }
 }
 
-// ------------------------------------------------ Q8_0 from row chunks ----
-// Q8_0 GEMV that decodes every weight byte in the register it was loaded into:
-// no LDS staging, one pass per workgroup (as the f16 K-split kernel).  With
-// K % 256 == 0 a row of nb blocks is C = 17 nb / 8 whole 16-byte chunks.
-// A workgroup owns RB rows.  "Full" unit U (< C / 64) gives lane L chunk
-// 64 U + L of every one of the RB rows (one activation window, RB rows); the
-// last rem = C % 64 chunks of the RB rows form rem * RB (row, chunk) pairs,
-// one per lane of the "remainder" units.  Wave w takes full units
-// w NF .. w NF + NF - 1 and remainder units w NR .. w NR + NR - 1.
+// ------------------------------------ Q8_0 and Q4_0 from row chunks ----
+// Quantized GEMV that decodes every weight byte in the register it was loaded
+// into: no LDS staging, one pass per workgroup (as the f16 K-split kernel).
+// A block is B bytes (Q8_0: 34, Q4_0: 18) and each code byte carries W
+// weights (1 or 2).  With K % 256 == 0 a row of nb blocks is C = B nb / 16
+// whole 16-byte chunks.  A workgroup owns RB rows.  "Full" unit U (< C / 64)
+// gives lane L chunk 64 U + L of every one of the RB rows (one activation
+// window, RB rows); the last rem = C % 64 chunks of the RB rows form rem * RB
+// (row, chunk) pairs.  With R2 = rem rounded up to a power of two, pair
+// e = R2 r + co (remainder chunk co < rem of row r) sits on lane e % 64 of the
+// "remainder" unit e / 64: a row's remainder chunks are consecutive lanes of
+// one aligned group of R2 lanes (coalesced), summed by a butterfly inside the
+// group.  Wave w takes full units w NF .. w NF + NF - 1 and remainder units
+// w NR .. w NR + NR - 1.  A row's sum is its full-unit sum (the same lanes and
+// the same waves for every row) plus its remainder sum, added once at the
+// end, so equal rows give equal f32 results wherever they sit.
 //
-// Chunk c (bytes 16c .. 16c + 15 of a row) holds codes of at most two blocks:
-// j0, the block in progress at byte 16c - 1, and j0 + 1 when that block's
-// scale starts inside the chunk, at the even byte p = 34 (j0 + 1) - 16 c <= 14.
+// Chunk c (bytes 16c .. 16c + 15 of a row) holds codes of at most two blocks
+// (a block is longer than a chunk and at most one starts inside it): j0, the
+// block in progress at byte 16c - 1, and j0 + 1 when that block's scale
+// starts inside the chunk, at the even byte p = B (j0 + 1) - 16 c <= 14.
 // Dwords 0 .. bd - 1 hold codes of j0 and dwords bd .. 3 codes of j0 + 1, with
 // bd = (p + 2) / 4 (bd = 4 when no block starts in the chunk); the two scale
-// bytes are paired with zero activations.  Code byte i takes activation
-// s0 + i before the scale and s0 + i - 2 after it, s0 = 16 c - 2 j0 - 2.  The
-// scale of j0 + 1 is read from the chunk itself; the scale of j0 lies in chunk
-// c - 1 or c - 2 of the same row, whose lane extracted it as its own start
-// scale and hands it over with ds_bpermute; lanes whose source chunk is in
-// another unit load those two bytes from memory instead (a buffer load that
-// every other lane turns into an out-of-range no-op).
+// bytes are paired with zero activations.  Code byte i takes the W
+// activations from s0 + W i before the scale and s0 + W (i - 2) after it,
+// s0 = 32 j0 + W (16 c - B j0 - 2).  The scale of j0 + 1 is read from the
+// chunk itself; the scale of j0 lies in chunk c - 1 or c - 2 of the same row
+// (dsrc lanes back), whose lane extracted it as its own start scale and hands
+// it over with ds_bpermute; lanes whose source chunk is in another unit load
+// those two bytes from memory instead (a buffer load that every other lane
+// turns into an out-of-range no-op).
+template <int FMT>
+struct QC {
+    static constexpr int kB = QB<FMT>::kBytes;
+    static constexpr int kW = FMT == QFMT_Q8_0 ? 1 : 2;  // weights per code byte
+    static constexpr int kX = 16 * kW;                   // activations per chunk
+};
 struct ChunkGeo {
     int p;     // byte of the block start in the chunk, or >= 16 when none
     int bd;    // dwords of block j0
@@ -580,22 +593,27 @@ struct ChunkGeo {
     int j0;    // block in progress at the chunk start (-1 for chunk 0)
     int dsrc;  // chunk c - dsrc holds the scale of j0 (1 or 2)
 };
+template <int FMT>
 __device__ __forceinline__ ChunkGeo chunk_geo(int c) {
+    constexpr int B = QC<FMT>::kB, W = QC<FMT>::kW;
     ChunkGeo g;
-    g.j0 = (16 * c + 33) / 34 - 1;
-    g.p = 34 * (g.j0 + 1) - 16 * c;
+    g.j0 = (16 * c + B - 1) / B - 1;
+    g.p = B * (g.j0 + 1) - 16 * c;
     g.bd = g.p <= 14 ? (g.p + 2) >> 2 : 4;
-    g.s0 = 16 * c - 2 * g.j0 - 2;
-    g.dsrc = 34 * g.j0 >= 16 * (c - 1) ? 1 : 2;
+    g.s0 = 32 * g.j0 + W * (16 * c - B * g.j0 - 2);
+    g.dsrc = B * g.j0 >= 16 * (c - 1) ? 1 : 2;
     return g;
 }
 
-// Byte offsets (into a) of the activation pairs of the chunk: pair t covers
-// code bytes 2t, 2t + 1; the pair of scale bytes gets an out-of-range offset
-// (the buffer load returns zeros), as do pairs past the end of a.
-__device__ __forceinline__ uint32_t act_pair_offset(const ChunkGeo &g, int t, bool valid) {
-    const int hp = g.p >> 1;  // the scale pair (>= 8: none)
-    const int idx = g.s0 + 2 * t - (t > hp ? 2 : 0);
+// Byte offsets (into a) of the activation groups of the chunk: group t covers
+// code bytes 2t, 2t + 1 (2 W activations); the scale's group gets an
+// out-of-range offset (the buffer load returns zeros), as do groups of units
+// past the end.
+template <int FMT>
+__device__ __forceinline__ uint32_t act_group_offset(const ChunkGeo &g, int t, bool valid) {
+    constexpr int W = QC<FMT>::kW;
+    const int hp = g.p >> 1;  // the scale's group (>= 8: none)
+    const int idx = g.s0 + 2 * W * t - (t > hp ? 2 * W : 0);
     return (valid && t != hp) ? static_cast<uint32_t>(idx) * 4u : 0x80000000u;
 }
 
@@ -618,39 +636,106 @@ __device__ __forceinline__ uint32_t chunk_half(const uint4 &v, int p, uint32_t s
 constexpr int kQcStream = 2;  // non-temporal buffer loads: every weight is read once
 
 // One (row, chunk): adds d_j0 * (codes of j0 . x) + d_j1 * (codes of j1 . x)
-// to acc.  own: the chunk's start scale (valid when p <= 14); from: the
-// scale handed over by the source lane (or loaded); d0, d1 chosen per dword.
-__device__ __forceinline__ float chunk_dot(const uint4 &v, const float (&x)[16], float d0, float d1, int bd,
-                                           float acc) {
+// to acc; h0, h1 hold the f16 bits of d_j0, d_j1 (low half), picked per dword
+// and fed to the FMA as an f16 operand.  Q8_0: byte i of the chunk is one int8
+// code against x[i].  Q4_0: byte i holds codes for x[2i] (low nibble) and
+// x[2i + 1] (high nibble); the high-nibble codes come out of q4_pair scaled by
+// 16, and the caller has scaled the odd activations by the exact 1/16.  Each
+// dword's products form one chain started from +0 (an FMA, so that f16 codes
+// stay mixed-precision FMA operands).
+template <int FMT>
+__device__ __forceinline__ float chunk_dot(const uint4 &v, const float (&x)[QC<FMT>::kX], uint32_t h0,
+                                           uint32_t h1, int bd, float acc) {
     const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (FMT == QFMT_Q8_0) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const uint32_t q = wd[d];
-        float t = static_cast<float>(static_cast<int8_t>(q & 0xffu)) * x[4 * d + 0];
-        t = fmaf(static_cast<float>(static_cast<int8_t>((q >> 8) & 0xffu)), x[4 * d + 1], t);
-        t = fmaf(static_cast<float>(static_cast<int8_t>((q >> 16) & 0xffu)), x[4 * d + 2], t);
-        t = fmaf(static_cast<float>(static_cast<int8_t>(q >> 24)), x[4 * d + 3], t);
-        acc = fmaf(d < bd ? d0 : d1, t, acc);
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t q = wd[d];
+            float t = static_cast<float>(static_cast<int8_t>(q & 0xffu)) * x[4 * d + 0];
+            t = fmaf(static_cast<float>(static_cast<int8_t>((q >> 8) & 0xffu)), x[4 * d + 1], t);
+            t = fmaf(static_cast<float>(static_cast<int8_t>((q >> 16) & 0xffu)), x[4 * d + 2], t);
+            t = fmaf(static_cast<float>(static_cast<int8_t>(q >> 24)), x[4 * d + 3], t);
+            acc = fmaf(half_bits_to_float(d < bd ? h0 : h1), t, acc);
+        }
+    } else {
+        // Codes of all four dwords first, then the four dword chains advanced
+        // together (dependent mixed-precision FMAs back to back stall).
+        const Q4Consts kc = q4_consts();
+        h2 pc[4][4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t q = wd[d], q8 = wd[d] >> 8;
+            pc[d][0] = q4_pair<false>(q, kc);   // bytes 0, 2 low nibbles: x[8d], x[8d + 4]
+            pc[d][1] = q4_pair<true>(q, kc);    // bytes 0, 2 high nibbles: x[8d + 1], x[8d + 5]
+            pc[d][2] = q4_pair<false>(q8, kc);  // bytes 1, 3 low nibbles: x[8d + 2], x[8d + 6]
+            pc[d][3] = q4_pair<true>(q8, kc);   // bytes 1, 3 high nibbles: x[8d + 3], x[8d + 7]
+        }
+        float t[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) t[d] = fmaf(static_cast<float>(pc[d][0].x), x[8 * d], 0.f);
+#pragma unroll
+        for (int i = 1; i < 4; ++i)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) t[d] = fmaf(static_cast<float>(pc[d][i].x), x[8 * d + i], t[d]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) t[d] = fmaf(static_cast<float>(pc[d][i].y), x[8 * d + 4 + i], t[d]);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) acc = fmaf(half_bits_to_float(d < bd ? h0 : h1), t[d], acc);
     }
     return acc;
 }
 
+// The activation window of a chunk: 8 groups of 2 W floats (zeros at the
+// scale's group and for units past the end); Q4_0 odd (high-nibble)
+// activations are scaled by 1/16 (a power of two: exact unless the product
+// underflows f32's normal range, where it is rounded as a subnormal).
+template <int FMT>
+__device__ __forceinline__ void load_window(__amdgpu_buffer_rsrc_t ra, const ChunkGeo &g, bool ok,
+                                            float (&x)[QC<FMT>::kX]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int off = static_cast<int>(act_group_offset<FMT>(g, t, ok));
+        if constexpr (FMT == QFMT_Q8_0) {
+            const float2 f2 = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ra, off, 0, 0));
+            x[2 * t] = f2.x;
+            x[2 * t + 1] = f2.y;
+        } else {
+            // Whole-vector cast: a bit cast of one ext-vector element reads
+            // element 0 in this compiler.
+            const float4 f4 = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+            x[4 * t] = f4.x;
+            x[4 * t + 1] = f4.y;
+            x[4 * t + 2] = f4.z;
+            x[4 * t + 3] = f4.w;
+        }
+    }
+}
+
 constexpr int kQcMaxWaves = 4;
 
-template <int RB, int NF, int NR, int MODE = kModeStore>
-__global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q8_chunks(const float *__restrict__ a,
-                                                                      const uint8_t *__restrict__ b,
-                                                                      float *__restrict__ c, int64_t n, int64_t k,
-                                                                      int resid) {
+// v when keep, else +0 (through the bits, so that no branch is formed).
+__device__ __forceinline__ float masked(float v, bool keep) {
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & (0u - static_cast<uint32_t>(keep)));
+}
+
+template <int FMT, int RB, int NF, int NR, int MODE = kModeStore>
+__global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q_chunks(const float *__restrict__ a,
+                                                                     const uint8_t *__restrict__ b,
+                                                                     float *__restrict__ c, int64_t n, int64_t k,
+                                                                     int resid) {
     constexpr int NU = NF + NR;
+    constexpr int B = QC<FMT>::kB, X = QC<FMT>::kX;
     constexpr uint32_t kOut = 0x80000000u;  // an out-of-range buffer offset: the load returns zeros
     const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
     const int kw = blockDim.x / kWave;
     const int nb = static_cast<int>(k >> 5);
-    const int C = (17 * nb) >> 3;
-    const int q = C >> 6, rem = C & 63, P = rem * RB;
-    const int remd = rem > 0 ? rem : 1;  // divisor for lanes of empty remainder units
-    const uint32_t row_bytes = 34u * static_cast<uint32_t>(nb);
+    const int C = (B * nb) >> 4;
+    const int q = C >> 6, rem = C & 63;
+    const int lr = rem > 0 ? 32 - __clz(rem - 1) : 0;  // R2 = 1 << lr
+    const int P = rem > 0 ? RB << lr : 0;              // remainder pairs, padding included
+    const uint32_t row_bytes = static_cast<uint32_t>(B) * static_cast<uint32_t>(nb);
     const int64_t r0 = static_cast<int64_t>(blockIdx.x) * RB;
     // The host checks n * row_bytes < 2^31 and 4 K < 2^31: every offset below
     // fits 31 bits and kOut is out of range of both resources.
@@ -666,31 +751,58 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q8_chunks(const floa
     // the chunk's own (zero) one, so it adds exactly 0 with no branch.
     ChunkGeo geo[NU];
     uint32_t voff[NU];  // byte offset of the unit's chunk (remainder: from row r0)
-    int rrow[NR > 0 ? NR : 1], co[NR > 0 ? NR : 1];
+    int co[NR > 0 ? NR : 1], rrow[NR > 0 ? NR : 1];
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         const int u = w * NF + f;
         const bool ok = u < q;
-        geo[f] = chunk_geo(ok ? 64 * u + lane : 0);
+        geo[f] = chunk_geo<FMT>(ok ? 64 * u + lane : 0);
         if (!ok) geo[f].bd = 0;
         voff[f] = ok ? 16u * static_cast<uint32_t>(64 * u + lane) : kOut;
     }
 #pragma unroll
     for (int g = 0; g < NR; ++g) {
         const int e = 64 * (w * NR + g) + lane;
-        const bool ok = e < P;
-        co[g] = ok ? e % remd : 0;
-        rrow[g] = ok ? e / remd : 0;
-        geo[NF + g] = chunk_geo(64 * q + co[g]);
+        const bool ok = e < P && (e & ((1 << lr) - 1)) < rem;
+        co[g] = ok ? e & ((1 << lr) - 1) : 0;
+        rrow[g] = e < P ? e >> lr : 0;
+        geo[NF + g] = chunk_geo<FMT>(64 * q + co[g]);
         if (!ok) geo[NF + g].bd = 0;
         const uint32_t roff = static_cast<uint32_t>(min<int64_t>(rrow[g], n - 1 - r0)) * row_bytes;
         voff[NF + g] = ok ? roff + 16u * static_cast<uint32_t>(64 * q + co[g]) : kOut;
     }
 
-    // Weight chunks first (rows past n read the last row; never stored).
+    // Loads in the order the decode consumes them: the activation windows
+    // (Q4_0 scales half of them before any decode), the scale fallbacks, then
+    // the weights.
     uint32_t rowoff[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) rowoff[r] = sbase + static_cast<uint32_t>(min<int64_t>(r, n - 1 - r0)) * row_bytes;
+    float x[NU][X];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) load_window<FMT>(ra, geo[u], voff[u] != kOut, x[u]);
+    // Scales of j0 whose source chunk is in another unit: full units, lanes
+    // 0 .. dsrc - 1; remainder units, the first dsrc chunks of each row's
+    // remainder.  Every other lane's load is out of range.
+    uint32_t fb[NF][RB], fr[NR > 0 ? NR : 1];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const bool need = geo[f].bd > 0 && lane < geo[f].dsrc;
+        const uint32_t o = need ? static_cast<uint32_t>(B) * static_cast<uint32_t>(geo[f].j0) : kOut;
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+            fb[f][r] = __builtin_amdgcn_raw_buffer_load_b16(rb, static_cast<int>(o), static_cast<int>(rowoff[r]), 0);
+    }
+#pragma unroll
+    for (int g = 0; g < NR; ++g) {
+        const ChunkGeo &ge = geo[NF + g];
+        const bool need = ge.bd > 0 && co[g] < ge.dsrc;
+        const uint32_t roff = static_cast<uint32_t>(min<int64_t>(rrow[g], n - 1 - r0)) * row_bytes;
+        const uint32_t o = need ? roff + static_cast<uint32_t>(B) * static_cast<uint32_t>(ge.j0) : kOut;
+        fr[g] = __builtin_amdgcn_raw_buffer_load_b16(rb, static_cast<int>(o), static_cast<int>(sbase), 0);
+    }
+    // Then the weight chunks, row by row (rows past n read the last row; never
+    // stored), so that the decode of each row waits only for its own loads.
     uint4 wv[NF][RB];
     uint4 wr[NR > 0 ? NR : 1];
 #pragma unroll
@@ -707,44 +819,15 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q8_chunks(const floa
             __builtin_amdgcn_raw_buffer_load_b128(rb, static_cast<int>(voff[NF + g]), static_cast<int>(sbase), kQcStream);
         wr[g] = make_uint4(v.x, v.y, v.z, v.w);
     }
-    // Scales of j0 whose source chunk is in another unit: full units, lanes
-    // 0 .. dsrc - 1; remainder units, those lanes and the first dsrc chunks of
-    // each row's remainder.  Every other lane's load is out of range.
-    uint32_t fb[NF][RB], fr[NR > 0 ? NR : 1];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        const bool need = geo[f].bd > 0 && lane < geo[f].dsrc;
-        const uint32_t o = need ? 34u * static_cast<uint32_t>(geo[f].j0) : kOut;
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-            fb[f][r] = __builtin_amdgcn_raw_buffer_load_b16(rb, static_cast<int>(o), static_cast<int>(rowoff[r]), 0);
-    }
-#pragma unroll
-    for (int g = 0; g < NR; ++g) {
-        const ChunkGeo &ge = geo[NF + g];
-        const bool need = ge.bd > 0 && (co[g] < ge.dsrc || lane < ge.dsrc);
-        const uint32_t roff = static_cast<uint32_t>(min<int64_t>(rrow[g], n - 1 - r0)) * row_bytes;
-        const uint32_t o = need ? roff + 34u * static_cast<uint32_t>(ge.j0) : kOut;
-        fr[g] = __builtin_amdgcn_raw_buffer_load_b16(rb, static_cast<int>(o), static_cast<int>(sbase), 0);
-    }
-    // Activation windows (pairs; zeros at the scale bytes, past K and for
-    // units past the end).
-    float x[NU][16];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const bool ok = voff[u] != kOut;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const auto v =
-                __builtin_amdgcn_raw_buffer_load_b64(ra, static_cast<int>(act_pair_offset(geo[u], t, ok)), 0, 0);
-            const float2 f2 = __builtin_bit_cast(float2, v);
-            x[u][2 * t] = f2.x;
-            x[u][2 * t + 1] = f2.y;
-        }
-    }
     // Every load above is issued before any decode (the scheduler otherwise
     // sinks some weight loads below the first unit's decode).
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FMT == QFMT_Q4_0) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int i = 1; i < X; i += 2) x[u][i] *= 0.0625f;
+    }
 
     float acc[RB];
 #pragma unroll
@@ -763,22 +846,36 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q8_chunks(const floa
             const uint32_t got = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(own)));
             const uint32_t b0 = fbl ? fb[f][r] : got;
             const uint32_t b1 = g.p <= 14 ? own : b0;
-            acc[r] = chunk_dot(wv[f][r], x[f], half_bits_to_float(b0), half_bits_to_float(b1), g.bd, acc[r]);
+            acc[r] = chunk_dot<FMT>(wv[f][r], x[f], b0, b1, g.bd, acc[r]);
         }
     }
+    // Remainder sums: each row's group of R2 lanes reduced by a butterfly;
+    // every lane files its value (unconditional stores: no branch), and row r
+    // later reads the one of its group's first lane, pair R2 r.
+    __shared__ float rpart[kQcMaxWaves * (NR > 0 ? NR : 1)][kWave];
 #pragma unroll
     for (int gi = 0; gi < NR; ++gi) {
         const ChunkGeo &g = geo[NF + gi];
         const uint32_t own = chunk_half(wr[gi], g.p, half_selector(g.p));
         const uint32_t got = static_cast<uint32_t>(
             __builtin_amdgcn_ds_bpermute((g.bd == 0 ? lane : lane - g.dsrc) * 4, static_cast<int>(own)));
-        const uint32_t b0 = (g.bd > 0 && (co[gi] < g.dsrc || lane < g.dsrc)) ? fr[gi] : got;
+        const uint32_t b0 = (g.bd > 0 && co[gi] < g.dsrc) ? fr[gi] : got;
         const uint32_t b1 = g.p <= 14 ? own : b0;
-        const float part = chunk_dot(wr[gi], x[NF + gi], half_bits_to_float(b0), half_bits_to_float(b1), g.bd, 0.f);
-#pragma unroll
-        for (int r = 0; r < RB; ++r) acc[r] += rrow[gi] == r ? part : 0.f;
+        float rs = chunk_dot<FMT>(wr[gi], x[NF + gi], b0, b1, g.bd, 0.f);
+        // The steps of group_sum<64>, the partner's value kept (bit mask) only
+        // while the group is that large: no branch and no select for the
+        // compiler to turn into one (a branch here splits the kernel, and the
+        // compiler then waits on every load before decoding the full units).
+        rs += masked(dpp_f32<0xb1>(rs), lr >= 1);
+        rs += masked(dpp_f32<0x4e>(rs), lr >= 2);
+        rs += masked(dpp_f32<0x141>(rs), lr >= 3);
+        rs += masked(dpp_f32<0x140>(rs), lr >= 4);
+        rs += masked(__shfl_xor(rs, 16, kWave), lr >= 5);
+        rs += masked(__shfl_xor(rs, 32, kWave), lr >= 6);
+        rpart[w * NR + gi][lane] = rs;
     }
-    // Row sums: one butterfly over the wave, then the waves in order through LDS.
+    // Full-unit sums: one butterfly over the wave (lane j 64 / RB ends with
+    // row j), then the waves in order through LDS, then the remainder.
     const float sum = rows_sum<RB, kWave>(acc, lane);
     __shared__ float part[kQcMaxWaves][RB];
     if (lane % (kWave / RB) == 0) part[w][lane / (kWave / RB)] = sum;
@@ -790,6 +887,7 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q8_chunks(const floa
         if (lane < RB && r0 + lane < n) {
             float t = part[0][lane];
             for (int qq = 1; qq < kw; ++qq) t += part[qq][lane];
+            if (rem > 0) t += rpart[(lane << lr) >> 6][(lane << lr) & 63];
             key = argmax_key(t, static_cast<uint32_t>(r0 + lane));
         }
 #pragma unroll
@@ -798,6 +896,7 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q8_chunks(const floa
     } else if (w == 0 && lane < RB && r0 + lane < n) {
         float t = part[0][lane];
         for (int qq = 1; qq < kw; ++qq) t += part[qq][lane];
+        if (rem > 0) t += rpart[(lane << lr) >> 6][(lane << lr) & 63];
         float *dst = c + r0 + lane;
         *dst = resid ? *dst + t : t;
     }
@@ -1053,66 +1152,82 @@ hipError_t run_q_ksplit(const float *a, const uint8_t *b, float *c, int64_t n, i
     return hipGetLastError();
 }
 
-// Plan of the register-chunk Q8_0 GEMV: RB rows per workgroup, NF full and
-// NR remainder units per wave, KW <= 4 waves.  A forced plan that needs more
+// Plan of the register-chunk GEMV: RB rows per workgroup, NF full and NR
+// remainder units per wave, KW <= 4 waves.  A forced plan that needs more
 // waves falls back to the other kernels.
 struct QcPlan {
     int rb, nf, nr, kw;
 };
-bool q8c_fit(int64_t k, int rb, int nf, int nr, QcPlan *pl) {
-    const int64_t nb = k / 32, C = 17 * nb / 8, q = C / 64, P = (C % 64) * rb;
+template <int FMT>
+bool qc_fit(int64_t k, int rb, int nf, int nr, QcPlan *pl) {
+    const int64_t nb = k / 32, C = QC<FMT>::kB * nb / 16, q = C / 64, rem = C % 64;
+    int64_t r2 = rem > 0 ? 1 : 0;  // rem rounded up to a power of two
+    while (r2 < rem) r2 *= 2;
+    const int64_t P = r2 * rb;
     const int64_t kw = std::max<int64_t>(std::max<int64_t>((q + nf - 1) / nf, (P + 64 * nr - 1) / (64 * nr)), 1);
     if (kw > kQcMaxWaves) return false;
     *pl = QcPlan{rb, nf, nr, static_cast<int>(kw)};
     return true;
 }
-// Forced plan (wq_set_gemv_plan): rb * 256 + nf * 16 + nr, 0 = automatic,
-// -1 = the kernel switched off.
-std::atomic<int> g_q8c_override{0};
-bool q8c_enabled() { return g_q8c_override.load(std::memory_order_relaxed) >= 0; }
-bool q8c_plan(const float *a, const uint8_t *b, int64_t n, int64_t k, QcPlan *pl) {
+// Forced plan (wq_set_gemv_plan, both formats): rb * 256 + nf * 16 + nr,
+// 0 = automatic, -1 = the kernel switched off.
+std::atomic<int> g_qc_override{0};
+bool qc_enabled() { return g_qc_override.load(std::memory_order_relaxed) >= 0; }
+template <int FMT>
+bool qc_plan(const float *a, const uint8_t *b, int64_t n, int64_t k, QcPlan *pl) {
     const int64_t nb = k / 32;
     if (nb % 8 != 0 || nb == 0 || !aligned16(a) || !aligned16(b) || n < 1) return false;
-    if (n * 34 * nb >= (int64_t(1) << 31) || 4 * k >= (int64_t(1) << 31)) return false;
-    if (const int f = g_q8c_override.load(std::memory_order_relaxed); f > 0)
-        return q8c_fit(k, f >> 8, (f >> 4) & 15, f & 15, pl);
-    // Measured on MI355X against the staged and K-split kernels (Q8_0, M = 1):
-    // rows of 128 blocks or more (K >= 4096) and the LM head gain (151936 x 2048
-    // 56.8 -> 54.7 us, 11008 x 4096 14.2 -> 13.0, 4096 x 4096 8.9 -> 7.2,
-    // 2048 x 6144 7.2 -> 6.7, 4096 x 11008 19.2 -> 14.7); shorter rows with
-    // fewer than 65536 of them measured the same or slower (6144 x 2048 6.2 ->
-    // 6.3-6.7 us), so they keep the staged kernel.
-    if (nb < 128) return n >= 65536 && q8c_fit(k, 16, 1, 1, pl);
-    if (n >= 8192 && q8c_fit(k, 8, 1, 1, pl)) return true;
-    return q8c_fit(k, 4, 2, 1, pl) || q8c_fit(k, 4, 3, 1, pl);
+    if (n * QC<FMT>::kB * nb >= (int64_t(1) << 31) || 4 * k >= (int64_t(1) << 31)) return false;
+    if (const int f = g_qc_override.load(std::memory_order_relaxed); f > 0)
+        return qc_fit<FMT>(k, f >> 8, (f >> 4) & 15, f & 15, pl);
+    // Measured on MI355X (M = 1, every plan against the staged / K-split
+    // kernels, same box, us):
+    //   Q8_0 151936x2048 (16,1,1) 54.3, staged 57.5; 11008x4096 (16,1,1) 12.6,
+    //   (8,1,1) 13.2, K-split 14.1; 4096x11008 (4,3,1) 14.9, K-split 19.5;
+    //   4096x4096 (8,1,1) 7.1, (4,2,1) 7.4; 2048x6144 (4,2,1) 6.3, K-split 7.3;
+    //   6144x2048 and 2048x2048 staged 6.1 and 4.3, no plan faster.
+    //   Q4_0 11008x4096 (8,1,1) 9.8, staged 13.1; 4096x11008 (4,3,1) 11.2,
+    //   K-split 15.2; 4096x4096 (4,1,1) 5.9, staged 8.3; 2048x6144 (4,1,1) 5.5,
+    //   K-split 6.2; rows of 64 blocks (K = 2048, the LM head 40.9 against
+    //   41.3) keep the staged kernel.
+    if constexpr (FMT == QFMT_Q8_0) {
+        if (nb < 128) return n >= 65536 && qc_fit<FMT>(k, 16, 1, 1, pl);
+        if (n >= 8192 && qc_fit<FMT>(k, 16, 1, 1, pl)) return true;
+        if (n >= 4096 && qc_fit<FMT>(k, 8, 1, 1, pl)) return true;
+        return qc_fit<FMT>(k, 4, 2, 1, pl) || qc_fit<FMT>(k, 4, 3, 1, pl);
+    } else {
+        if (nb < 128) return false;
+        if (n >= 8192 && qc_fit<FMT>(k, 8, 1, 1, pl)) return true;
+        return qc_fit<FMT>(k, 4, 1, 1, pl) || qc_fit<FMT>(k, 4, 3, 1, pl);
+    }
 }
 
-template <int RB, int NF, int NR, int MODE = kModeStore>
-hipError_t run_q8c(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int resid,
-                   int kw) {
+template <int FMT, int RB, int NF, int NR, int MODE = kModeStore>
+hipError_t run_qc(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int resid,
+                  int kw) {
     const int64_t blocks = (n + RB - 1) / RB;
     if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_q8_chunks<RB=%d,NF=%d,NR=%d,mode=%d> n=%lld k=%lld grid=%lld block=%d\n", RB, NF,
-                NR, MODE, (long long)n, (long long)k, (long long)blocks, kw * kWave);
-    hipLaunchKernelGGL((gemv_q8_chunks<RB, NF, NR, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(kw * kWave), 0,
-                       s, a, b, c, n, k, resid);
+        fprintf(stderr, "[wqmm] gemv_q_chunks<fmt=%d,RB=%d,NF=%d,NR=%d,mode=%d> n=%lld k=%lld grid=%lld block=%d\n",
+                FMT, RB, NF, NR, MODE, (long long)n, (long long)k, (long long)blocks, kw * kWave);
+    hipLaunchKernelGGL((gemv_q_chunks<FMT, RB, NF, NR, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(kw * kWave),
+                       0, s, a, b, c, n, k, resid);
     return hipGetLastError();
 }
 
 // Returns false (nothing launched) when no instantiated plan fits.  MODE
 // kModeStore (aux: residual flag) or kModeArgmax (aux: the slot set).
-template <int MODE = kModeStore>
-bool launch_q8c(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int aux,
-                hipError_t *e) {
+template <int FMT, int MODE = kModeStore>
+bool launch_qc(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int aux,
+               hipError_t *e) {
     QcPlan pl;
-    if (!q8c_plan(a, b, n, k, &pl)) return false;
-    if (pl.rb == 8 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<8, 2, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
-    else if (pl.rb == 4 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<4, 2, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
-    else if (pl.rb == 4 && pl.nf == 3 && pl.nr == 1) *e = run_q8c<4, 3, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
-    else if (pl.rb == 4 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<4, 1, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
-    else if (pl.rb == 8 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<8, 1, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
-    else if (pl.rb == 16 && pl.nf == 1 && pl.nr == 1) *e = run_q8c<16, 1, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
-    else if (pl.rb == 2 && pl.nf == 2 && pl.nr == 1) *e = run_q8c<2, 2, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    if (!qc_plan<FMT>(a, b, n, k, &pl)) return false;
+    if (pl.rb == 8 && pl.nf == 2 && pl.nr == 1) *e = run_qc<FMT, 8, 2, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 4 && pl.nf == 2 && pl.nr == 1) *e = run_qc<FMT, 4, 2, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 4 && pl.nf == 3 && pl.nr == 1) *e = run_qc<FMT, 4, 3, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 4 && pl.nf == 1 && pl.nr == 1) *e = run_qc<FMT, 4, 1, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 8 && pl.nf == 1 && pl.nr == 1) *e = run_qc<FMT, 8, 1, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 16 && pl.nf == 1 && pl.nr == 1) *e = run_qc<FMT, 16, 1, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
+    else if (pl.rb == 2 && pl.nf == 2 && pl.nr == 1) *e = run_qc<FMT, 2, 2, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
     else return false;
     return true;
 }
@@ -1122,9 +1237,9 @@ hipError_t gemv_q_rows(const float *a, const uint8_t *b, float *c, int64_t n, in
                        int aux, int64_t *lists) {
     const int64_t nb = k / 32;
     const int64_t row_bytes = nb * QB<FMT>::kBytes;
-    if constexpr (FMT == QFMT_Q8_0 && MODE == kModeStore) {
+    if constexpr (MODE == kModeStore) {
         hipError_t e = hipSuccess;
-        if (q8c_enabled() && launch_q8c(a, b, c, n, k, s, aux, &e)) return e;
+        if (qc_enabled() && launch_qc<FMT>(a, b, c, n, k, s, aux, &e)) return e;
     }
     // Long rows (more than 128 blocks, up to 16 waves of 64): K split over the waves of a workgroup.
     if (MODE == kModeStore && nb % 8 == 0 && nb > 128 && nb <= 64 * kSplitMaxWaves && aligned16(a) && aligned16(b))
@@ -1225,17 +1340,17 @@ hipError_t launch_gemv_f16(const float *a, const uint16_t *b, float *c, int64_t 
 
 bool set_gemv_plan_override(int rb, int nf, int nr) {
     if (rb == 0 && nf == 0 && nr == 0) {
-        g_q8c_override.store(0, std::memory_order_relaxed);
+        g_qc_override.store(0, std::memory_order_relaxed);
         return true;
     }
     if (rb == -1 && nf == 0 && nr == 0) {
-        g_q8c_override.store(-1, std::memory_order_relaxed);
+        g_qc_override.store(-1, std::memory_order_relaxed);
         return true;
     }
     static const int kPlans[][3] = {{8, 2, 1}, {4, 2, 1}, {4, 3, 1}, {4, 1, 1}, {8, 1, 1}, {16, 1, 1}, {2, 2, 1}};
     for (const auto &pl : kPlans)
         if (pl[0] == rb && pl[1] == nf && pl[2] == nr) {
-            g_q8c_override.store(rb * 256 + nf * 16 + nr, std::memory_order_relaxed);
+            g_qc_override.store(rb * 256 + nf * 16 + nr, std::memory_order_relaxed);
             return true;
         }
     return false;
@@ -1256,8 +1371,8 @@ hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t 
 // kernel takes, and quantized rows of whole 256-column groups for k > 1 (the
 // register-chunk / staged store kernels beat the per-wave lists once k is
 // large: measured at N = 151936, k = 50, Q8_0 71.3 against 73.7 us, Q4_0 56.6
-// against 59.3 us).  Top-1 of f16 (K-split) and Q8_0 (register-chunk) rows
-// takes the argmax fused into the GEMV.  Everything else keeps per-wave
+// against 59.3 us).  Top-1 of f16 (K-split) and Q8_0 / Q4_0 (register-chunk)
+// rows takes the argmax fused into the GEMV.  Everything else keeps per-wave
 // top-k lists inside the GEMV and merges them.
 static bool lm_head_f16_logits_route(const float *a, const void *b, int fmt, int64_t n, int64_t k) {
     return fmt != QFMT_Q8_0 && fmt != QFMT_Q4_0 && n > 0 && f16_ksplit_ok(a, static_cast<const uint16_t *>(b), k);
@@ -1269,10 +1384,12 @@ static bool lm_head_q_logits_route(const float *a, const void *b, int fmt, int64
 static bool lm_head_logits_route(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk) {
     return lm_head_f16_logits_route(a, b, fmt, n, k) || lm_head_q_logits_route(a, b, fmt, n, k, topk);
 }
-static bool lm_head_q8_argmax_route(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk) {
+static bool lm_head_q_argmax_route(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk) {
     QcPlan pl;
-    return fmt == QFMT_Q8_0 && topk == 1 && n > 0 && q8c_enabled() &&
-           q8c_plan(a, static_cast<const uint8_t *>(b), n, k, &pl);
+    const uint8_t *b8 = static_cast<const uint8_t *>(b);
+    if (topk != 1 || n < 1 || !qc_enabled()) return false;
+    if (fmt == QFMT_Q8_0) return qc_plan<QFMT_Q8_0>(a, b8, n, k, &pl);
+    return fmt == QFMT_Q4_0 && qc_plan<QFMT_Q4_0>(a, b8, n, k, &pl);
 }
 
 size_t lm_head_topk_scratch_bytes(const float *a, const void *b, int fmt, int64_t n, int64_t k, int topk, int cus) {
@@ -1304,8 +1421,9 @@ hipError_t launch_lm_head_topk(const float *a, const void *b, int fmt, int64_t n
     if (topk == 1 && set >= 0 && lm_head_f16_logits_route(a, b, fmt, n, k)) {
         e = f16_ksplit<kModeArgmax>(a, b16, nullptr, n, k, s, set);
         argmax_done = true;
-    } else if (set >= 0 && lm_head_q8_argmax_route(a, b, fmt, n, k, topk)) {
-        argmax_done = launch_q8c<kModeArgmax>(a, b8, nullptr, n, k, s, set, &e);
+    } else if (set >= 0 && lm_head_q_argmax_route(a, b, fmt, n, k, topk)) {
+        argmax_done = fmt == QFMT_Q8_0 ? launch_qc<QFMT_Q8_0, kModeArgmax>(a, b8, nullptr, n, k, s, set, &e)
+                                       : launch_qc<QFMT_Q4_0, kModeArgmax>(a, b8, nullptr, n, k, s, set, &e);
     }
     if (argmax_done) {
         if (e == hipSuccess) {

@@ -333,7 +333,7 @@ int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, in
 
 extern "C" {
 
-int wq_abi_version(void) { return 106; }
+int wq_abi_version(void) { return 107; }
 
 const char *wq_status_str(int status) {
     switch (status) {

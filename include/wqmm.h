@@ -360,15 +360,15 @@ int wq_hgemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, in
  * at K / 32); (0, 0, 0) restores the cost model.  WQ_ERR_SHAPE otherwise. */
 int wq_set_hgemm_plan(int bm, int bn, int splits);
 
-/* Test and tuning hook for the Q8_0 decode GEMV (M == 1, K % 256 == 0,
- * 16-byte aligned operands, N * K * 34 / 32 < 2^31 bytes): force every later
- * call whose shape fits onto the register-chunk kernel with rb rows per
- * workgroup and nf full / nr remainder 64-chunk units per wave (the kernel
- * takes at most 4 waves; shapes that would need more keep the other kernels);
- * (0, 0, 0) restores the measured rule, (-1, 0, 0) switches the kernel off.
- * Plans: (8,2,1) (4,2,1) (4,3,1) (4,1,1) (8,1,1) (16,1,1) (2,2,1); anything
- * else returns WQ_ERR_SHAPE.  Results do not depend on the plan beyond f32
- * rounding. */
+/* Test and tuning hook for the Q8_0 and Q4_0 decode GEMV (M == 1,
+ * K % 256 == 0, 16-byte aligned operands, N * row bytes < 2^31): force every
+ * later call of either format whose shape fits onto the register-chunk kernel
+ * with rb rows per workgroup and nf full / nr remainder 64-chunk units per wave
+ * (the kernel takes at most 4 waves; shapes that would need more keep the
+ * other kernels); (0, 0, 0) restores the measured rule, (-1, 0, 0) switches
+ * the kernel off.  Plans: (8,2,1) (4,2,1) (4,3,1) (4,1,1) (8,1,1) (16,1,1)
+ * (2,2,1); anything else returns WQ_ERR_SHAPE.  Results do not depend on the
+ * plan beyond f32 rounding. */
 int wq_set_gemv_plan(int rb, int nf, int nr);
 
 /* Test and tuning hook for the f16 matrix-core weight stream

@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process():
 
 
 def test_abi_and_status_strings():
-    assert wq.wq_abi_version() == 106
+    assert wq.wq_abi_version() == 107
     for st in range(0, 11):
         assert wq.status_str(st)
     assert wq.status_str(99) == "unknown status"

@@ -622,62 +622,73 @@ def test_edge_blocks_every_route_bit_exact(fmt, k):
             wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
 
 
-def q8_chunk_plan_fits(k, rb, nf, nr):
-    """Whether the register-chunk Q8_0 GEMV takes K with plan (rb, nf, nr): rows of
-    C = 17 K / 256 16-byte chunks, C // 64 full units and (C % 64) * rb remainder
-    (row, chunk) pairs over at most four waves."""
+def chunk_plan_fits(fmt, k, rb, nf, nr):
+    """Whether the register-chunk GEMV takes K with plan (rb, nf, nr): rows of
+    C = B K / 512 16-byte chunks (B = 34 bytes per Q8_0 block, 18 per Q4_0
+    block), C // 64 full units and rb groups of remainder lanes (C % 64
+    rounded up to a power of two each) over at most four waves."""
     if k % 256:
         return False
-    c = 17 * (k // 32) // 8
-    q, pairs = c // 64, (c % 64) * rb
-    return max(-(-q // nf), -(-pairs // (64 * nr)), 1) <= 4
+    c = (34 if fmt == Q8 else 18) * (k // 32) // 16
+    q, rem = c // 64, c % 64
+    r2 = 1 << (rem - 1).bit_length() if rem else 0
+    return max(-(-q // nf), -(-(r2 * rb) // (64 * nr)), 1) <= 4
 
 
 CHUNK_K = [256, 1024, 2048, 2304, 3328, 4096, 6144, 11008]
 
 
+@pytest.mark.parametrize("fmt", [Q8, Q4])
 @pytest.mark.parametrize("plan", wq.GEMV_PLANS, ids=[f"{r}x{f}x{g}" for r, f, g in wq.GEMV_PLANS])
-def test_q8_chunk_gemv_every_plan(plan):
-    """The register-chunk Q8_0 GEMV under every plan it instantiates, at every K of
-    CHUNK_K the plan takes (rows whose last chunks fill a whole unit or part of
-    one, one to three remainder units, invalid full units in the last wave) and
-    row counts that leave the last workgroup partial: full compares against the
-    oracle, then one-hot rows of A over hand-built edge blocks, bit for bit."""
-    ks = [k for k in CHUNK_K if q8_chunk_plan_fits(k, *plan)]
+def test_chunk_gemv_every_plan(plan, fmt):
+    """The register-chunk Q8_0 / Q4_0 GEMV under every plan it instantiates, at
+    every K of CHUNK_K the plan takes (rows whose last chunks fill a whole unit
+    or part of one, one to three remainder units, invalid full units in the
+    last wave) and row counts that leave the last workgroup partial: full
+    compares against the oracle, then one-hot rows of A over hand-built edge
+    blocks, bit for bit."""
+    ks = [k for k in CHUNK_K if chunk_plan_fits(fmt, k, *plan)]
     assert len(ks) >= 3, ks
     try:
         wq.wq_set_gemv_plan(*plan)
         for k in ks:
             for n in (1, 5, 37, 133):
-                full_case("gemv", Q8, 1, n, k, seed=n + k)
+                full_case("gemv", fmt, 1, n, k, seed=n + k)
+            # Equal rows give equal f32 sums wherever they sit in a workgroup.
+            raw1 = encoded(1, k, fmt, k)[0]
+            same = np.ascontiguousarray(np.repeat(raw1, 37, axis=0))
+            a1 = acts(1, k, k + 1)
+            c = run_gpu("gemv", fmt, a1, torch.from_numpy(same).cuda(), 1, 37, k)
+            assert np.all(c[0] == c[0, 0]), f"plan {plan} k={k}: equal rows differ {np.unique(c[0])}"
             n = 21
-            raw = edge_weights(Q8, n, k, seed=2)
-            w = oracle.decode(raw, Q8, n, k)
+            raw = edge_weights(fmt, n, k, seed=2)
+            w = oracle.decode(raw, fmt, n, k)
             dev_b = torch.from_numpy(raw).cuda()
             for col in onehot_positions(k, np.random.default_rng(k)):
                 a = np.zeros((1, k), np.float32)
                 a[0, col] = 1.0
-                c = run_gpu("gemv", Q8, a, dev_b, 1, n, k)
+                c = run_gpu("gemv", fmt, a, dev_b, 1, n, k)
                 assert np.array_equal(c[0].astype(np.float64), w[:, col]), f"plan {plan} k={k} column {col}"
-            say(f"chunk plan {plan} k={k} edge blocks")
+            say(f"chunk plan {plan} fmt={fmt} k={k} edge blocks")
     finally:
         wq.wq_set_gemv_plan(0, 0, 0)
 
 
-def test_q8_chunk_gemv_residual_and_large_n():
+@pytest.mark.parametrize("fmt", [Q8, Q4])
+def test_chunk_gemv_residual_and_large_n(fmt):
     """Residual epilogue through the chunk kernel, and the automatic plans at the
-    shapes they are chosen for (the LM head's 16-row plan on a 70000-row matrix)."""
-    for n, k in ((70000, 2048), (9000, 4096), (300, 6144)):
-        say(f"chunk auto plan n={n} k={k}")
-        full_case("gemv", Q8, 1, n, k, seed=3)
+    shapes they are chosen for (the LM head's plan on a 70000-row matrix)."""
+    for n, k in ((70000, 2048), (9000, 4096), (300, 6144), (4096, 11008)):
+        say(f"chunk auto plan fmt={fmt} n={n} k={k}")
+        full_case("gemv", fmt, 1, n, k, seed=3)
     n, k = 133, 4096
-    ref_b, dev_b = encoded(n, k, Q8, 4)
+    ref_b, dev_b = encoded(n, k, fmt, 4)
     a = acts(1, k, 4)
     c0 = np.random.default_rng(4).standard_normal((1, n)).astype(np.float32)
     c = torch.from_numpy(c0).cuda()
-    wq.wq_matmul_ex(torch.from_numpy(a).cuda(), dev_b, c, 1, n, k, Q8, wq.WQ_EPI_RESIDUAL)
+    wq.wq_matmul_ex(torch.from_numpy(a).cuda(), dev_b, c, 1, n, k, fmt, wq.WQ_EPI_RESIDUAL)
     torch.cuda.synchronize()
-    c_ref, bound = oracle.matmul(a, ref_b, Q8, 1, n, k)
+    c_ref, bound = oracle.matmul(a, ref_b, fmt, 1, n, k)
     assert_close(c.cpu().numpy() - c0, c_ref, bound + 1e-6 * np.abs(c0), "residual")
 
 

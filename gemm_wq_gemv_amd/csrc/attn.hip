@@ -19,7 +19,9 @@
 //    one butterfly (rows_sum): afterwards each (head, token) score sits in its
 //    own lane(s), the TT tokens of a head in one aligned lane group;
 //  * the online-softmax update (tile max, rescale, exponentials, tile sum)
-//    runs inside that lane group with DPP reductions;
+//    runs inside that lane group with DPP reductions, on scores kept in log2
+//    units (scale * log2(e) folded into the query), so that each weight is
+//    one v_exp_f32;
 //  * P.V broadcasts each weight with a readlane and accumulates
 //    acc[g][e] += p[g][t] * v_t[e] per lane;
 //  * a wave's K and V rows for a tile load together, into one of two
@@ -90,6 +92,10 @@ __device__ __forceinline__ float elem(const uint32_t *x, int e) {
     return half_bits_to_float((e & 1) ? x[e >> 1] >> 16 : x[e >> 1] & 0xffffu);
 }
 
+// 2^x (v_exp_f32).  Scores are kept in log2 units (scaled by scale * log2 e
+// once, in the query), so every softmax weight is one exponential.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float lane_value(float v, int l) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
 }
@@ -119,14 +125,15 @@ struct TileBuf {
 // Workgroup (kvh, part) = (blockIdx.x % hkv, blockIdx.x / hkv) covers cache
 // tokens [part * ptok, min(len, (part + 1) * ptok)) for the G query heads of
 // KV head kvh.  parts == 1: out gets the result; else partials gets
-// (m, l, acc[D]) per query head at ((part * hq + h) * (D + 2)).
+// (m, l, acc[D]) per query head at ((part * hq + h) * (D + 2)), m in log2
+// units (the running maximum of scale * log2(e) * q . k).
 template <int D, int GP, int KVF>
 __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial(const float *__restrict__ q,
                                                                    const void *__restrict__ kc,
                                                                    const void *__restrict__ vc,
                                                                    float *__restrict__ out,
                                                                    float *__restrict__ partials, int64_t len,
-                                                                   int hq, int hkv, int g_real, float scale,
+                                                                   int hq, int hkv, int g_real, float scale2,
                                                                    int64_t ptok, int parts) {
     using S = AttnShape<D, GP, KVF>;
     using B = TileBuf<D, GP, KVF>;
@@ -147,9 +154,10 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial(const float *
 #pragma unroll
     for (int g = 0; g < GP; ++g)
 #pragma unroll
-        for (int e = 0; e < E; ++e) qv[g][e] = g < g_real ? q[static_cast<int64_t>(h0 + g) * D + lane * E + e] : 0.f;
+        for (int e = 0; e < E; ++e)
+            qv[g][e] = g < g_real ? q[static_cast<int64_t>(h0 + g) * D + lane * E + e] * scale2 : 0.f;
 
-    // Running state: m_run / l_run of this lane's head (lane / HL), the same
+    // Running state (log2 units): m_run / l_run of this lane's head (lane / HL), the same
     // in every lane of that head's group; acc[g][e] for every head.
     float m_run = -__builtin_huge_valf(), l_run = 0.f;
     float acc[GP][E];
@@ -182,10 +190,10 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial(const float *
         // Cross-lane steps run in every lane; only then are invalid tokens masked.
         const float dot = rows_sum<N, kWave>(pd, lane);
         const bool valid = rt < cnt;
-        const float s = valid ? dot * scale : -__builtin_huge_valf();
+        const float s = valid ? dot : -__builtin_huge_valf();
         const float m_new = fmaxf(m_run, group_max<HL>(s));
-        const float alpha = m_run == -__builtin_huge_valf() ? 0.f : expf(m_run - m_new);
-        const float p = valid ? expf(s - m_new) : 0.f;
+        const float alpha = m_run == -__builtin_huge_valf() ? 0.f : ex2(m_run - m_new);
+        const float p = valid ? ex2(s - m_new) : 0.f;
         l_run = alpha * l_run + group_sum<HL>(leader ? p : 0.f);
         m_run = m_new;
 #pragma unroll
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial(const float *
         float l = 0.f, a = 0.f;
 #pragma unroll
         for (int o = 0; o < kAttnWaves; ++o) {
-            const float c = sm[o][g] == -__builtin_huge_valf() ? 0.f : expf(sm[o][g] - mx);
+            const float c = sm[o][g] == -__builtin_huge_valf() ? 0.f : ex2(sm[o][g] - mx);
             l = fmaf(c, sl[o][g], l);
             a = fmaf(c, sacc[o][g][d], a);
         }
@@ -290,12 +298,12 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void attn_reduce(const float 
 #pragma unroll
         for (int u = 0; u < U; ++u) mn = fmaxf(mn, mp[u]);
         if (mn == -__builtin_huge_valf()) continue;  // nothing but empty partitions so far
-        const float ca = m == -__builtin_huge_valf() ? 0.f : expf(m - mn);
+        const float ca = m == -__builtin_huge_valf() ? 0.f : ex2(m - mn);
         l *= ca;
         a *= ca;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float cp = mp[u] == -__builtin_huge_valf() ? 0.f : expf(mp[u] - mn);
+            const float cp = mp[u] == -__builtin_huge_valf() ? 0.f : ex2(mp[u] - mn);
             l = fmaf(cp, lp[u], l);
             a = fmaf(cp, ap[u], a);
         }
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void attn_reduce(const float 
     float lt = 0.f, at = 0.f;
 #pragma unroll
     for (int o = 0; o < kReduceWaves; ++o) {
-        const float c = sm[o] == -__builtin_huge_valf() ? 0.f : expf(sm[o] - mx);
+        const float c = sm[o] == -__builtin_huge_valf() ? 0.f : ex2(sm[o] - mx);
         lt = fmaf(c, sl[o], lt);
         at = fmaf(c, sa[o][lane], at);
     }
@@ -331,6 +339,8 @@ hipError_t run_attn(const float *q, const void *k, const void *v, float *out, in
     const int64_t parts = (len + ptok - 1) / ptok;
     if (parts * hkv > 0x7fffffffLL || parts > 0x7fffffffLL) return hipErrorInvalidValue;
     const int g_real = hq / hkv;
+    // Scores in log2 units: scale * log2(e) folded into the query.
+    const float scale2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
     ScratchLease lease;
     float *partials = nullptr;
     if (parts > 1) {
@@ -343,7 +353,7 @@ hipError_t run_attn(const float *q, const void *k, const void *v, float *out, in
         fprintf(stderr, "[wqmm] attn_partial<D=%d,GP=%d,kvf=%d> len=%lld hq=%d hkv=%d ptok=%lld parts=%lld grid=%lld\n",
                 D, GP, KVF, (long long)len, hq, hkv, (long long)ptok, (long long)parts, (long long)(parts * hkv));
     hipLaunchKernelGGL((attn_partial<D, GP, KVF>), dim3(static_cast<unsigned>(parts * hkv)),
-                       dim3(kAttnWaves * kWave), 0, s, q, k, v, out, partials, len, hq, hkv, g_real, scale, ptok,
+                       dim3(kAttnWaves * kWave), 0, s, q, k, v, out, partials, len, hq, hkv, g_real, scale2, ptok,
                        static_cast<int>(parts));
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && parts > 1) {

@@ -124,11 +124,13 @@ COUNTER_REPEAT = 12
 
 
 def counter_workload(torch, wq, wqgen, seed):
-    F16, Q8 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0
+    F16, Q8, Q4 = wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0
 
     def rotated(n, k, fmt):
         if fmt == F16:
             b0 = wq.pack_f16(torch.from_numpy(wqgen.weights(n, k, seed)).cuda())
+        elif fmt == Q4:
+            b0 = torch.from_numpy(wqgen.q4_0_bytes(n, k, seed)).cuda()
         else:
             b0 = wq.quantize_q8_0(torch.from_numpy(wqgen.weights(n, k, seed)).cuda())
         nb = wq.weight_bytes(n, k, fmt)
@@ -159,6 +161,9 @@ def counter_workload(torch, wq, wqgen, seed):
     product("Q8_0 GEMV 4096x11008 (register chunks)", 1, 4096, 11008, Q8)
     product("Q8_0 GEMV 11008x4096 (register chunks)", 1, 11008, 4096, Q8)
     product("Q8_0 GEMV 6144x2048 (staged)", 1, 6144, 2048, Q8)
+    product("Q4_0 LM head 151936x2048 (staged)", 1, 151936, 2048, Q4)
+    product("Q4_0 GEMV 11008x4096 (register chunks)", 1, 11008, 4096, Q4)
+    product("Q4_0 GEMV 4096x11008 (register chunks)", 1, 4096, 11008, Q4)
     product("Q8_0 stream 2x11008x4096", 2, 11008, 4096, Q8)
     product("Q8_0 stream 8x4096x11008", 8, 4096, 11008, Q8)
     product("Q8_0 stream 16x4096x11008", 16, 4096, 11008, Q8)
@@ -243,6 +248,19 @@ def summarize(paths):
                 cells.append(f"{x * 1024:,.0f}" if c.endswith("_SIZE") else f"{x:,.0f}")
             print(f"| `{k}` | {g} | {n} | " + " | ".join(cells) + " |")
         print()
+        # Byte-counter calibration: the workload's first four 256-workgroup copy
+        # dispatches, the 1 GiB device copies it makes before anything else.
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        for c in names:
+            if not c.endswith("_SIZE"):
+                continue
+            big = [float(r["Counter_Value"]) for r in rows
+                   if r["Counter_Name"] == c and "copyBuffer" in r["Kernel_Name"]
+                   and int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"])) == 256][:4]
+            if big:
+                print(f"1 GiB copy calibration: {c} = {statistics.mean(big):,.1f} KiB per dispatch over "
+                      f"{len(big)} dispatches (1,048,576 KiB moved; scale factor "
+                      f"{1_048_576 / statistics.mean(big):.4f})\n")
 
 
 class Suite:

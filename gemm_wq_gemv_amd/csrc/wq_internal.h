@@ -45,10 +45,36 @@ __device__ __forceinline__ float dpp_f32(float v) {
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 
+// Cross-row exchange of a pair of values on gfx950 (v_permlane16_swap_b32 /
+// v_permlane32_swap_b32, one VALU instruction): with H = 16, the odd 16-lane
+// rows of a trade places with the even rows of b; with H = 32, the upper 32
+// lanes of a with the lower 32 lanes of b.  Afterwards, in every lane,
+// x = a and y = b of the lower (bit H clear) side of a lane pair, or of the
+// upper side, so x + y is a_l + a_partner(l) in lanes with bit H clear and
+// b_partner(l) + b_l in the others: one step of a butterfly over lane xor H
+// for two values at once, with no select and no LDS permute.
+struct SwapPair {
+    float x, y;
+};
+template <int H>
+__device__ __forceinline__ SwapPair lane_swap(float a, float b) {
+    static_assert(H == 16 || H == 32, "swap distance");
+    const unsigned ua = __builtin_bit_cast(unsigned, a), ub = __builtin_bit_cast(unsigned, b);
+    unsigned r0, r1;
+    if constexpr (H == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
+        r0 = r[0], r1 = r[1];  // elements copied to scalars before any bit cast
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(ua, ub, false, false);
+        r0 = r[0], r1 = r[1];
+    }
+    return SwapPair{__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1)};
+}
+
 // Sum over aligned groups of G lanes (G a power of two up to 64); every lane
 // of a group receives the group's sum.  Within a 16-lane DPP row:
 // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror;
-// across rows: lane xor 16 and 32.
+// across rows: lane xor 16 and 32 (a value swapped with itself).
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
     static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "group size");
@@ -56,8 +82,14 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (G >= 4) v += dpp_f32<0x4e>(v);
     if constexpr (G >= 8) v += dpp_f32<0x141>(v);
     if constexpr (G >= 16) v += dpp_f32<0x140>(v);
-    if constexpr (G >= 32) v += __shfl_xor(v, 16, kWave);
-    if constexpr (G >= 64) v += __shfl_xor(v, 32, kWave);
+    if constexpr (G >= 32) {
+        const SwapPair p = lane_swap<16>(v, v);
+        v = p.x + p.y;
+    }
+    if constexpr (G >= 64) {
+        const SwapPair p = lane_swap<32>(v, v);
+        v = p.x + p.y;
+    }
     return v;
 }
 
@@ -70,8 +102,14 @@ __device__ __forceinline__ float group_max(float v) {
     if constexpr (G >= 4) v = fmaxf(v, dpp_f32<0x4e>(v));
     if constexpr (G >= 8) v = fmaxf(v, dpp_f32<0x141>(v));
     if constexpr (G >= 16) v = fmaxf(v, dpp_f32<0x140>(v));
-    if constexpr (G >= 32) v = fmaxf(v, __shfl_xor(v, 16, kWave));
-    if constexpr (G >= 64) v = fmaxf(v, __shfl_xor(v, 32, kWave));
+    if constexpr (G >= 32) {
+        const SwapPair p = lane_swap<16>(v, v);
+        v = fmaxf(p.x, p.y);
+    }
+    if constexpr (G >= 64) {
+        const SwapPair p = lane_swap<32>(v, v);
+        v = fmaxf(p.x, p.y);
+    }
     return v;
 }
 
@@ -98,13 +136,22 @@ __device__ __forceinline__ float rows_sum(const float (&v)[N], int g) {
         return group_sum<G>(v[0]);
     } else {
         constexpr int H = G / 2;
-        const bool hi = (g & H) != 0;
         float w[N / 2];
+        if constexpr (H == 32 || H == 16) {
+            // Lanes with bit H clear keep rows 0 .. N/2 - 1, the others the rest.
 #pragma unroll
-        for (int i = 0; i < N / 2; ++i) {
-            const float send = hi ? v[i] : v[N / 2 + i];
-            const float keep = hi ? v[N / 2 + i] : v[i];
-            w[i] = keep + bit_partner<H>(send);
+            for (int i = 0; i < N / 2; ++i) {
+                const SwapPair p = lane_swap<H>(v[i], v[N / 2 + i]);
+                w[i] = p.x + p.y;
+            }
+        } else {
+            const bool hi = (g & H) != 0;
+#pragma unroll
+            for (int i = 0; i < N / 2; ++i) {
+                const float send = hi ? v[i] : v[N / 2 + i];
+                const float keep = hi ? v[N / 2 + i] : v[i];
+                w[i] = keep + bit_partner<H>(send);
+            }
         }
         return rows_sum<N / 2, H>(w, g);
     }

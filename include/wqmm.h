@@ -294,9 +294,9 @@ int wq_decode_attention(const float *q, const void *k_cache, const void *v_cache
 
 /* Test/tuning hook (host only): every later wq_decode_attention call in the
  * process splits the cache into partitions of `tokens` tokens (0 restores
- * the automatic size, about two workgroups per compute unit).  Returns
- * WQ_ERR_SHAPE for tokens < 0.  Not thread-safe with respect to concurrent
- * attention calls that expect the automatic size. */
+ * the automatic size, about one workgroup per compute unit and at least 32
+ * tokens).  Returns WQ_ERR_SHAPE for tokens < 0.  Not thread-safe with
+ * respect to concurrent attention calls that expect the automatic size. */
 int wq_set_attn_partition(int64_t tokens);
 
 /* ---------------------------------------------------------------------- */

@@ -207,12 +207,15 @@ __global__ __launch_bounds__(kAttnWaves * kWave) void attn_partial(const float *
             float vf[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) vf[e] = elem<KVF>(b.v[t], e);
+            // The token's weights for every head first: a readlane result used
+            // by the next instruction costs a wait state.
+            float pg[GP];
 #pragma unroll
-            for (int g = 0; g < GP; ++g) {
-                const float pg = lane_value(p, (g * TT + t) * R);
+            for (int g = 0; g < GP; ++g) pg[g] = lane_value(p, (g * TT + t) * R);
 #pragma unroll
-                for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pg, vf[e], acc[g][e]);
-            }
+            for (int g = 0; g < GP; ++g)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[g][e] = fmaf(pg[g], vf[e], acc[g][e]);
         }
     };
 

@@ -82,16 +82,19 @@ __device__ __forceinline__ unsigned long long argmax_key(float x, uint32_t id) {
 
 // ------------------------------------------------------------------ f16 ----
 
-__device__ __forceinline__ float dot8_f16(uint4 w, float4 lo, float4 hi, float acc) {
-    acc = fmaf(half_bits_to_float(w.x & 0xffffu), lo.x, acc);
-    acc = fmaf(half_bits_to_float(w.x >> 16), lo.y, acc);
-    acc = fmaf(half_bits_to_float(w.y & 0xffffu), lo.z, acc);
-    acc = fmaf(half_bits_to_float(w.y >> 16), lo.w, acc);
-    acc = fmaf(half_bits_to_float(w.z & 0xffffu), hi.x, acc);
-    acc = fmaf(half_bits_to_float(w.z >> 16), hi.y, acc);
-    acc = fmaf(half_bits_to_float(w.w & 0xffffu), hi.z, acc);
-    acc = fmaf(half_bits_to_float(w.w >> 16), hi.w, acc);
-    return acc;
+// acc[r] += sum_e w[r] . (lo, hi) over the 8 f16 weights of each row's chunk,
+// the rows' FMA chains advanced together (a mixed-precision FMA that depends
+// on the one just before it costs a wait state).
+template <int RB>
+__device__ __forceinline__ void dot8_f16_rows(const uint4 (&w)[RB], float4 lo, float4 hi, float (&acc)[RB]) {
+    const float x[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const uint32_t d = e < 2 ? w[r].x : e < 4 ? w[r].y : e < 6 ? w[r].z : w[r].w;
+            acc[r] = fmaf(half_bits_to_float((e & 1) ? d >> 16 : d & 0xffffu), x[e], acc[r]);
+        }
 }
 
 // K-split f16 GEMV (store and GLU modes): workgroup g (KW waves, KW =
@@ -150,10 +153,13 @@ __global__ __launch_bounds__(kSplitMaxWaves * kWave) void gemv_f16_ksplit(const 
     }
     float acc[RB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        acc[r] = 0.f;
+    for (int r = 0; r < RB; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int t = 0; t < T2; ++t) acc[r] = dot8_f16(wv[r][t], alo[t], ahi[t], acc[r]);
+    for (int t = 0; t < T2; ++t) {
+        uint4 wt[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) wt[r] = wv[r][t];
+        dot8_f16_rows<RB>(wt, alo[t], ahi[t], acc);
     }
     // rows_sum leaves row j's sum in lanes j*(64/RB) ..; lane j (< RB) takes it.
     float v = __shfl(rows_sum<RB, kWave>(acc, lane), (lane % RB) * (kWave / RB), kWave);

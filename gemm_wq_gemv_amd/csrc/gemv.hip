@@ -641,30 +641,39 @@ __device__ __forceinline__ uint32_t chunk_half(const uint4 &v, int p, uint32_t s
 
 constexpr int kQcStream = 2;  // non-temporal buffer loads: every weight is read once
 
-// One (row, chunk): adds d_j0 * (codes of j0 . x) + d_j1 * (codes of j1 . x)
-// to acc; h0, h1 hold the f16 bits of d_j0, d_j1 (low half), picked per dword
-// and fed to the FMA as an f16 operand.  Q8_0: byte i of the chunk is one int8
-// code against x[i].  Q4_0: byte i holds codes for x[2i] (low nibble) and
-// x[2i + 1] (high nibble); the high-nibble codes come out of q4_pair scaled by
-// 16, and the caller has scaled the odd activations by the exact 1/16.  Each
-// dword's products form one chain started from +0 (an FMA, so that f16 codes
-// stay mixed-precision FMA operands).
-template <int FMT>
-__device__ __forceinline__ float chunk_dot(const uint4 &v, const float (&x)[QC<FMT>::kX], uint32_t h0,
-                                           uint32_t h1, int bd, float acc) {
+// One (weight row, chunk) against MR rows of activations: adds d_j0 * (codes
+// of j0 . x_m) + d_j1 * (codes of j1 . x_m) to acc[m] for each m, the codes
+// decoded once; h0, h1 hold the f16 bits of d_j0, d_j1 (low half), picked
+// per dword and fed to the FMA as an f16 operand.  Q8_0: byte i of the chunk
+// is one int8 code against x_m[i].  Q4_0: byte i holds codes for x_m[2i]
+// (low nibble) and x_m[2i + 1] (high nibble); the high-nibble codes come out
+// of q4_pair scaled by 16, and the caller has scaled the odd activations by
+// the exact 1/16.  Each dword's products form one chain per row of A started
+// from +0 (an FMA, so that f16 codes stay mixed-precision FMA operands).
+template <int FMT, int MR>
+__device__ __forceinline__ void chunk_dot(const uint4 &v, const float (&x)[MR][QC<FMT>::kX], uint32_t h0,
+                                          uint32_t h1, int bd, float (&acc)[MR]) {
     const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
     if constexpr (FMT == QFMT_Q8_0) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const uint32_t q = wd[d];
-            float t = static_cast<float>(static_cast<int8_t>(q & 0xffu)) * x[4 * d + 0];
-            t = fmaf(static_cast<float>(static_cast<int8_t>((q >> 8) & 0xffu)), x[4 * d + 1], t);
-            t = fmaf(static_cast<float>(static_cast<int8_t>((q >> 16) & 0xffu)), x[4 * d + 2], t);
-            t = fmaf(static_cast<float>(static_cast<int8_t>(q >> 24)), x[4 * d + 3], t);
-            acc = fmaf(half_bits_to_float(d < bd ? h0 : h1), t, acc);
+            const float c0 = static_cast<float>(static_cast<int8_t>(q & 0xffu));
+            const float c1 = static_cast<float>(static_cast<int8_t>((q >> 8) & 0xffu));
+            const float c2 = static_cast<float>(static_cast<int8_t>((q >> 16) & 0xffu));
+            const float c3 = static_cast<float>(static_cast<int8_t>(q >> 24));
+            const uint32_t hs = d < bd ? h0 : h1;
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                float t = c0 * x[m][4 * d + 0];
+                t = fmaf(c1, x[m][4 * d + 1], t);
+                t = fmaf(c2, x[m][4 * d + 2], t);
+                t = fmaf(c3, x[m][4 * d + 3], t);
+                acc[m] = fmaf(half_bits_to_float(hs), t, acc[m]);
+            }
         }
     } else {
-        // Codes of all four dwords first, then the four dword chains advanced
+        // Codes of all four dwords first, then the dword chains advanced
         // together (dependent mixed-precision FMAs back to back stall).
         const Q4Consts kc = q4_consts();
         h2 pc[4][4];
@@ -676,33 +685,39 @@ __device__ __forceinline__ float chunk_dot(const uint4 &v, const float (&x)[QC<F
             pc[d][2] = q4_pair<false>(q8, kc);  // bytes 1, 3 low nibbles: x[8d + 2], x[8d + 6]
             pc[d][3] = q4_pair<true>(q8, kc);   // bytes 1, 3 high nibbles: x[8d + 3], x[8d + 7]
         }
-        float t[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) t[d] = fmaf(static_cast<float>(pc[d][0].x), x[8 * d], 0.f);
+        for (int m = 0; m < MR; ++m) {
+            float t[4];
 #pragma unroll
-        for (int i = 1; i < 4; ++i)
+            for (int d = 0; d < 4; ++d) t[d] = fmaf(static_cast<float>(pc[d][0].x), x[m][8 * d], 0.f);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) t[d] = fmaf(static_cast<float>(pc[d][i].x), x[8 * d + i], t[d]);
+            for (int i = 1; i < 4; ++i)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+                for (int d = 0; d < 4; ++d) t[d] = fmaf(static_cast<float>(pc[d][i].x), x[m][8 * d + i], t[d]);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) t[d] = fmaf(static_cast<float>(pc[d][i].y), x[8 * d + 4 + i], t[d]);
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) acc = fmaf(half_bits_to_float(d < bd ? h0 : h1), t[d], acc);
+                for (int d = 0; d < 4; ++d) t[d] = fmaf(static_cast<float>(pc[d][i].y), x[m][8 * d + 4 + i], t[d]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) acc[m] = fmaf(half_bits_to_float(d < bd ? h0 : h1), t[d], acc[m]);
+        }
     }
-    return acc;
 }
 
-// The activation window of a chunk: 8 groups of 2 W floats (zeros at the
-// scale's group and for units past the end); Q4_0 odd (high-nibble)
+// The activation window of a chunk in row row_off / (4 K) of A: 8 groups of
+// 2 W floats (zeros at the scale's group, for units past the end and for rows
+// past the end of A); Q4_0 odd (high-nibble)
 // activations are scaled by 1/16 (a power of two: exact unless the product
 // underflows f32's normal range, where it is rounded as a subnormal).
 template <int FMT>
 __device__ __forceinline__ void load_window(__amdgpu_buffer_rsrc_t ra, const ChunkGeo &g, bool ok,
-                                            float (&x)[QC<FMT>::kX]) {
+                                            float (&x)[QC<FMT>::kX], uint32_t row_off) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const int off = static_cast<int>(act_group_offset<FMT>(g, t, ok));
+        // The row offset goes into the range-checked (vector) offset, so a
+        // row past the end of A reads zeros.
+        const uint32_t o = act_group_offset<FMT>(g, t, ok);
+        const int off = static_cast<int>(o == 0x80000000u ? o : o + row_off);
         if constexpr (FMT == QFMT_Q8_0) {
             const float2 f2 = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ra, off, 0, 0));
             x[2 * t] = f2.x;
@@ -726,11 +741,15 @@ __device__ __forceinline__ float masked(float v, bool keep) {
     return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & (0u - static_cast<uint32_t>(keep)));
 }
 
-template <int FMT, int RB, int NF, int NR, int MODE = kModeStore>
+// MR rows of A (m_rows <= MR of them real, row-major [m_rows, K]; c is
+// [m_rows, n]): every chunk is decoded once and applied to each row of A.
+template <int FMT, int RB, int NF, int NR, int MODE = kModeStore, int MR = 1>
 __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q_chunks(const float *__restrict__ a,
                                                                      const uint8_t *__restrict__ b,
                                                                      float *__restrict__ c, int64_t n, int64_t k,
-                                                                     int resid) {
+                                                                     int resid, int m_rows) {
+    static_assert(MODE != kModeArgmax || MR == 1, "the fused argmax is for one row of A");
+    static_assert(RB * MR <= kWave, "one butterfly reduces every (row, row of A) sum");
     constexpr int NU = NF + NR;
     constexpr int B = QC<FMT>::kB, X = QC<FMT>::kX;
     constexpr uint32_t kOut = 0x80000000u;  // an out-of-range buffer offset: the load returns zeros
@@ -743,12 +762,13 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q_chunks(const float
     const int P = rem > 0 ? RB << lr : 0;              // remainder pairs, padding included
     const uint32_t row_bytes = static_cast<uint32_t>(B) * static_cast<uint32_t>(nb);
     const int64_t r0 = static_cast<int64_t>(blockIdx.x) * RB;
-    // The host checks n * row_bytes < 2^31 and 4 K < 2^31: every offset below
-    // fits 31 bits and kOut is out of range of both resources.
+    // The host checks n * row_bytes < 2^31 and 4 K MR < 2^31: every offset
+    // below fits 31 bits and kOut (plus a row offset of A) is out of range of
+    // both resources.  Rows of A past m_rows read as zeros.
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(b), 0, static_cast<int>(static_cast<uint32_t>(n) * row_bytes), 0x00020000);
-    const __amdgpu_buffer_rsrc_t ra =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(a), 0, static_cast<int>(4 * k), 0x00020000);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a), 0, static_cast<int>(4 * k * m_rows), 0x00020000);
     const uint32_t sbase = static_cast<uint32_t>(r0) * row_bytes;  // soffset of the workgroup's first row
 
     // Unit geometry.  Every load of a unit past the end (full units beyond
@@ -784,9 +804,12 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q_chunks(const float
     uint32_t rowoff[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) rowoff[r] = sbase + static_cast<uint32_t>(min<int64_t>(r, n - 1 - r0)) * row_bytes;
-    float x[NU][X];
+    float x[NU][MR][X];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) load_window<FMT>(ra, geo[u], voff[u] != kOut, x[u]);
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+            load_window<FMT>(ra, geo[u], voff[u] != kOut, x[u][m], static_cast<uint32_t>(4 * k * m));
     // Scales of j0 whose source chunk is in another unit: full units, lanes
     // 0 .. dsrc - 1; remainder units, the first dsrc chunks of each row's
     // remainder.  Every other lane's load is out of range.
@@ -832,12 +855,16 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q_chunks(const float
 #pragma unroll
         for (int u = 0; u < NU; ++u)
 #pragma unroll
-            for (int i = 1; i < X; i += 2) x[u][i] *= 0.0625f;
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+                for (int i = 1; i < X; i += 2) x[u][m][i] *= 0.0625f;
     }
 
-    float acc[RB];
+    float acc[RB][MR];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) acc[r] = 0.f;
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[r][m] = 0.f;
     // Scale of j0: a lane with bd == 0 (no code of j0) reads its own start
     // scale through the permute (source = itself), fallback lanes their load.
 #pragma unroll
@@ -852,13 +879,13 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q_chunks(const float
             const uint32_t got = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src, static_cast<int>(own)));
             const uint32_t b0 = fbl ? fb[f][r] : got;
             const uint32_t b1 = g.p <= 14 ? own : b0;
-            acc[r] = chunk_dot<FMT>(wv[f][r], x[f], b0, b1, g.bd, acc[r]);
+            chunk_dot<FMT, MR>(wv[f][r], x[f], b0, b1, g.bd, acc[r]);
         }
     }
     // Remainder sums: each row's group of R2 lanes reduced by a butterfly;
     // every lane files its value (unconditional stores: no branch), and row r
     // later reads the one of its group's first lane, pair R2 r.
-    __shared__ float rpart[kQcMaxWaves * (NR > 0 ? NR : 1)][kWave];
+    __shared__ float rpart[MR][kQcMaxWaves * (NR > 0 ? NR : 1) * kWave];
 #pragma unroll
     for (int gi = 0; gi < NR; ++gi) {
         const ChunkGeo &g = geo[NF + gi];
@@ -867,24 +894,38 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q_chunks(const float
             __builtin_amdgcn_ds_bpermute((g.bd == 0 ? lane : lane - g.dsrc) * 4, static_cast<int>(own)));
         const uint32_t b0 = (g.bd > 0 && co[gi] < g.dsrc) ? fr[gi] : got;
         const uint32_t b1 = g.p <= 14 ? own : b0;
-        float rs = chunk_dot<FMT>(wr[gi], x[NF + gi], b0, b1, g.bd, 0.f);
+        float rsm[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) rsm[m] = 0.f;
+        chunk_dot<FMT, MR>(wr[gi], x[NF + gi], b0, b1, g.bd, rsm);
         // The steps of group_sum<64>, the partner's value kept (bit mask) only
         // while the group is that large: no branch and no select for the
         // compiler to turn into one (a branch here splits the kernel, and the
         // compiler then waits on every load before decoding the full units).
-        rs += masked(dpp_f32<0xb1>(rs), lr >= 1);
-        rs += masked(dpp_f32<0x4e>(rs), lr >= 2);
-        rs += masked(dpp_f32<0x141>(rs), lr >= 3);
-        rs += masked(dpp_f32<0x140>(rs), lr >= 4);
-        rs += masked(__shfl_xor(rs, 16, kWave), lr >= 5);
-        rs += masked(__shfl_xor(rs, 32, kWave), lr >= 6);
-        rpart[w * NR + gi][lane] = rs;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            float rs = rsm[m];
+            rs += masked(dpp_f32<0xb1>(rs), lr >= 1);
+            rs += masked(dpp_f32<0x4e>(rs), lr >= 2);
+            rs += masked(dpp_f32<0x141>(rs), lr >= 3);
+            rs += masked(dpp_f32<0x140>(rs), lr >= 4);
+            rs += masked(__shfl_xor(rs, 16, kWave), lr >= 5);
+            rs += masked(__shfl_xor(rs, 32, kWave), lr >= 6);
+            rpart[m][(w * NR + gi) * kWave + lane] = rs;
+        }
     }
-    // Full-unit sums: one butterfly over the wave (lane j 64 / RB ends with
-    // row j), then the waves in order through LDS, then the remainder.
-    const float sum = rows_sum<RB, kWave>(acc, lane);
-    __shared__ float part[kQcMaxWaves][RB];
-    if (lane % (kWave / RB) == 0) part[w][lane / (kWave / RB)] = sum;
+    // Full-unit sums: value j = r MR + m (weight row r, row m of A) of every
+    // lane, reduced by one butterfly (lane j 64 / (RB MR) ends with sum j),
+    // then the waves in order through LDS, then the remainder.
+    constexpr int RM = RB * MR;
+    float accf[RM];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) accf[r * MR + m] = acc[r][m];
+    const float sum = rows_sum<RM, kWave>(accf, lane);
+    __shared__ float part[kQcMaxWaves][RM];
+    if (lane % (kWave / RM) == 0) part[w][lane / (kWave / RM)] = sum;
     __syncthreads();
     if constexpr (MODE == kModeArgmax) {
         // resid is the slot set: the workgroup's best row goes to one slot.
@@ -893,17 +934,18 @@ __global__ __launch_bounds__(kQcMaxWaves * kWave) void gemv_q_chunks(const float
         if (lane < RB && r0 + lane < n) {
             float t = part[0][lane];
             for (int qq = 1; qq < kw; ++qq) t += part[qq][lane];
-            if (rem > 0) t += rpart[(lane << lr) >> 6][(lane << lr) & 63];
+            if (rem > 0) t += rpart[0][lane << lr];
             key = argmax_key(t, static_cast<uint32_t>(r0 + lane));
         }
 #pragma unroll
         for (int d = 1; d < RB; d *= 2) key = max(key, static_cast<unsigned long long>(__shfl_xor(key, d, kWave)));
         if (lane == 0 && key != 0ull) atomicMax(&g_argmax_slots[resid][blockIdx.x % kArgmaxSlots], key);
-    } else if (w == 0 && lane < RB && r0 + lane < n) {
+    } else if (w == 0 && lane < RM && r0 + lane / MR < n && lane % MR < m_rows) {
+        const int r = lane / MR, m = lane % MR;
         float t = part[0][lane];
         for (int qq = 1; qq < kw; ++qq) t += part[qq][lane];
-        if (rem > 0) t += rpart[(lane << lr) >> 6][(lane << lr) & 63];
-        float *dst = c + r0 + lane;
+        if (rem > 0) t += rpart[m][r << lr];
+        float *dst = c + static_cast<int64_t>(m) * n + r0 + r;
         *dst = resid ? *dst + t : t;
     }
 }
@@ -1208,15 +1250,17 @@ bool qc_plan(const float *a, const uint8_t *b, int64_t n, int64_t k, QcPlan *pl)
     }
 }
 
-template <int FMT, int RB, int NF, int NR, int MODE = kModeStore>
+template <int FMT, int RB, int NF, int NR, int MODE = kModeStore, int MR = 1>
 hipError_t run_qc(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k, hipStream_t s, int resid,
-                  int kw) {
+                  int kw, int m_rows = 1) {
     const int64_t blocks = (n + RB - 1) / RB;
     if (trace_enabled())
-        fprintf(stderr, "[wqmm] gemv_q_chunks<fmt=%d,RB=%d,NF=%d,NR=%d,mode=%d> n=%lld k=%lld grid=%lld block=%d\n",
-                FMT, RB, NF, NR, MODE, (long long)n, (long long)k, (long long)blocks, kw * kWave);
-    hipLaunchKernelGGL((gemv_q_chunks<FMT, RB, NF, NR, MODE>), dim3(static_cast<unsigned>(blocks)), dim3(kw * kWave),
-                       0, s, a, b, c, n, k, resid);
+        fprintf(stderr,
+                "[wqmm] gemv_q_chunks<fmt=%d,RB=%d,NF=%d,NR=%d,mode=%d,MR=%d> m=%d n=%lld k=%lld grid=%lld "
+                "block=%d\n",
+                FMT, RB, NF, NR, MODE, MR, m_rows, (long long)n, (long long)k, (long long)blocks, kw * kWave);
+    hipLaunchKernelGGL((gemv_q_chunks<FMT, RB, NF, NR, MODE, MR>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kw * kWave), 0, s, a, b, c, n, k, resid, m_rows);
     return hipGetLastError();
 }
 
@@ -1235,6 +1279,69 @@ bool launch_qc(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
     else if (pl.rb == 16 && pl.nf == 1 && pl.nr == 1) *e = run_qc<FMT, 16, 1, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
     else if (pl.rb == 2 && pl.nf == 2 && pl.nr == 1) *e = run_qc<FMT, 2, 2, 1, MODE>(a, b, c, n, k, s, aux, pl.kw);
     else return false;
+    return true;
+}
+
+// Several rows of A (2 <= m <= MR) through one register-chunk launch.  The
+// activation windows take NU * MR * (16 or 32) VGPRs, so fewer plans are
+// compiled: MR = 2 Q8_0 (16,1,1) (8,1,1) (4,2,1) (4,3,1), Q4_0 (8,1,1) (4,1,1)
+// (4,2,1); MR = 4 (Q8_0 only) (8,1,1) (4,1,1).
+template <int FMT, int MR>
+bool qc_compiled_rows(int rb, int nf, int nr) {
+    if (nr != 1) return false;
+    if constexpr (MR == 2 && FMT == QFMT_Q8_0)
+        return (rb == 16 && nf == 1) || (rb == 8 && nf == 1) || (rb == 4 && nf == 2) || (rb == 4 && nf == 3);
+    else if constexpr (MR == 2)
+        return (rb == 8 && nf == 1) || (rb == 4 && nf == 1) || (rb == 4 && nf == 2);
+    else if constexpr (MR == 4 && FMT == QFMT_Q8_0)
+        return (rb == 8 && nf == 1) || (rb == 4 && nf == 1);
+    return false;
+}
+template <int FMT, int MR>
+bool qc_plan_rows(const float *a, const uint8_t *b, int64_t n, int64_t k, QcPlan *pl) {
+    const int64_t nb = k / 32;
+    if (nb % 8 != 0 || nb == 0 || !aligned16(a) || !aligned16(b) || n < 1) return false;
+    if (n * QC<FMT>::kB * nb >= (int64_t(1) << 31) || 4 * k * MR >= (int64_t(1) << 31)) return false;
+    if (const int f = g_qc_override.load(std::memory_order_relaxed); f > 0) {
+        const int rb = f >> 8, nf = (f >> 4) & 15, nr = f & 15;
+        return qc_compiled_rows<FMT, MR>(rb, nf, nr) && qc_fit<FMT>(k, rb, nf, nr, pl);
+    }
+    if constexpr (MR == 2 && FMT == QFMT_Q8_0) {
+        if (n >= 8192 && qc_fit<FMT>(k, 16, 1, 1, pl)) return true;
+        if (n >= 4096 && qc_fit<FMT>(k, 8, 1, 1, pl)) return true;
+        return qc_fit<FMT>(k, 4, 2, 1, pl) || qc_fit<FMT>(k, 4, 3, 1, pl);
+    } else if constexpr (MR == 2) {
+        if (n >= 8192 && qc_fit<FMT>(k, 8, 1, 1, pl)) return true;
+        return qc_fit<FMT>(k, 4, 1, 1, pl) || qc_fit<FMT>(k, 4, 2, 1, pl);
+    } else if constexpr (MR == 4 && FMT == QFMT_Q8_0) {
+        return qc_fit<FMT>(k, 8, 1, 1, pl) || qc_fit<FMT>(k, 4, 1, 1, pl);
+    }
+    return false;
+}
+template <int FMT, int MR>
+bool launch_qc_rows(const float *a, const uint8_t *b, float *c, int64_t m, int64_t n, int64_t k, hipStream_t s,
+                    int resid, hipError_t *e) {
+    QcPlan pl;
+    if (!qc_plan_rows<FMT, MR>(a, b, n, k, &pl)) return false;
+    const int mr = static_cast<int>(m);
+    if constexpr (MR == 2 && FMT == QFMT_Q8_0) {
+        if (pl.rb == 16 && pl.nf == 1) *e = run_qc<FMT, 16, 1, 1, kModeStore, 2>(a, b, c, n, k, s, resid, pl.kw, mr);
+        else if (pl.rb == 8 && pl.nf == 1) *e = run_qc<FMT, 8, 1, 1, kModeStore, 2>(a, b, c, n, k, s, resid, pl.kw, mr);
+        else if (pl.rb == 4 && pl.nf == 2) *e = run_qc<FMT, 4, 2, 1, kModeStore, 2>(a, b, c, n, k, s, resid, pl.kw, mr);
+        else if (pl.rb == 4 && pl.nf == 3) *e = run_qc<FMT, 4, 3, 1, kModeStore, 2>(a, b, c, n, k, s, resid, pl.kw, mr);
+        else return false;
+    } else if constexpr (MR == 2) {
+        if (pl.rb == 8 && pl.nf == 1) *e = run_qc<FMT, 8, 1, 1, kModeStore, 2>(a, b, c, n, k, s, resid, pl.kw, mr);
+        else if (pl.rb == 4 && pl.nf == 1) *e = run_qc<FMT, 4, 1, 1, kModeStore, 2>(a, b, c, n, k, s, resid, pl.kw, mr);
+        else if (pl.rb == 4 && pl.nf == 2) *e = run_qc<FMT, 4, 2, 1, kModeStore, 2>(a, b, c, n, k, s, resid, pl.kw, mr);
+        else return false;
+    } else if constexpr (MR == 4 && FMT == QFMT_Q8_0) {
+        if (pl.rb == 8 && pl.nf == 1) *e = run_qc<FMT, 8, 1, 1, kModeStore, 4>(a, b, c, n, k, s, resid, pl.kw, mr);
+        else if (pl.rb == 4 && pl.nf == 1) *e = run_qc<FMT, 4, 1, 1, kModeStore, 4>(a, b, c, n, k, s, resid, pl.kw, mr);
+        else return false;
+    } else {
+        return false;
+    }
     return true;
 }
 
@@ -1370,6 +1477,29 @@ hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t 
 hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
                             hipStream_t s, int epi) {
     return launch_gemv_q<QFMT_Q4_0>(a, b, c, n, k, s, epi);
+}
+
+bool launch_gemv_q_rows(const float *a, const uint8_t *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
+                        hipStream_t s, int epi, hipError_t *e) {
+    if ((epi != kEpiNone && epi != kEpiResidual) || !qc_enabled() || m < 2 || m > 4) return false;
+    const int resid = epi == kEpiResidual;
+    if (fmt == QFMT_Q8_0)
+        return m <= 2 ? launch_qc_rows<QFMT_Q8_0, 2>(a, b, c, m, n, k, s, resid, e)
+                      : launch_qc_rows<QFMT_Q8_0, 4>(a, b, c, m, n, k, s, resid, e);
+    if (fmt == QFMT_Q4_0 && m == 2) return launch_qc_rows<QFMT_Q4_0, 2>(a, b, c, m, n, k, s, resid, e);
+    return false;
+}
+
+// Two rows of A cost the windows 32 registers per unit.  With at most three
+// units per wave the kernel beats the weight stream on MI355X (Q8_0, two rows:
+// 2048 x 2048 5.3 against 6.1 us, 6144 x 2048 7.4 against 8.3, 2048 x 6144 7.8
+// against 9.2, 11008 x 4096 14.8 against 16.2); with four it does not (4096 x
+// 11008, plan (4, 3, 1): 20.0 against 15.8 us), nor do Q4_0 or three and four
+// rows (Q8_0 4 x 11008 x 4096: 24.6 against 18.0 us).
+bool gemv_q_rows_auto(const float *a, const uint8_t *b, int fmt, int64_t m, int64_t n, int64_t k, int epi) {
+    if (fmt != QFMT_Q8_0 || m != 2 || (epi != kEpiNone && epi != kEpiResidual) || !qc_enabled()) return false;
+    QcPlan pl;
+    return qc_plan_rows<QFMT_Q8_0, 2>(a, b, n, k, &pl) && pl.nf + pl.nr <= 3;
 }
 
 // Routes of an LM-head top-k call.  The logits route runs the fastest store

@@ -388,6 +388,17 @@ hipError_t launch_gemv_q4_0(const float *a, const uint8_t *b, float *c, int64_t 
                             hipStream_t s, int epi = kEpiNone);
 hipError_t launch_gemv_q8_0(const float *a, const uint8_t *b, float *c, int64_t n, int64_t k,
                             hipStream_t s, int epi = kEpiNone);
+// m (2 .. 4) rows of A [m, k] against Q8_0 (fmt 1) or Q4_0 (fmt 2) weights in
+// one register-chunk GEMV launch, c [m, n], epilogue kEpiNone or kEpiResidual.
+// Returns false (nothing launched) when no compiled plan takes the call
+// (Q4_0 beyond 2 rows, K % 256 != 0, misaligned operands, ...); *e gets the
+// launch status otherwise.
+bool launch_gemv_q_rows(const float *a, const uint8_t *b, int fmt, float *c, int64_t m, int64_t n, int64_t k,
+                        hipStream_t s, int epi, hipError_t *e);
+// Whether the automatic route gives the call to launch_gemv_q_rows rather than
+// the weight stream: two Q8_0 rows of A under a plan of at most three units
+// per wave (the case measured faster).
+bool gemv_q_rows_auto(const float *a, const uint8_t *b, int fmt, int64_t m, int64_t n, int64_t k, int epi);
 // Top-k of the LM-head logits w . a (w [n, k] in format fmt, one token):
 // the GEMV keeps a top-k list per wave, then launch_topk_merge reduces the
 // lists.  vals / ids: topk entries in rank order (1 <= topk <= kTopkMax).

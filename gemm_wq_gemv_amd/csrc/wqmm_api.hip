@@ -238,12 +238,32 @@ int kernel_epi(int epi) {
     return epi == WQ_EPI_RESIDUAL ? wq::kEpiResidual : epi == WQ_EPI_SWIGLU ? wq::kEpiGlu : wq::kEpiNone;
 }
 
-// The GEMV route (M == 1; forced otherwise): one GEMV launch per row of A,
-// each applying the epilogue itself.
+// The M rule, except that two Q8_0 rows of A the register-chunk GEMV takes in
+// one launch with at most three units per wave go to the GEMV route (faster
+// than the weight stream there).  a and b may be NULL: the shape alone decides.
+int pick_route(const float *a, const void *b, int64_t m, int64_t n, int64_t k, int fmt, int epi) {
+    const int route = auto_route(m, k, fmt);
+    if (route == WQ_ROUTE_STREAM &&
+        wq::gemv_q_rows_auto(a, static_cast<const uint8_t *>(b), fmt, m, n, k, kernel_epi(epi)))
+        return WQ_ROUTE_GEMV;
+    return route;
+}
+
+// The GEMV route (M == 1; 2 <= M <= 4 quantized rows where the register-chunk
+// kernel takes them in one launch; forced otherwise): else one GEMV launch
+// per row of A, each applying the epilogue itself.
 int run_gemv(const float *a, const void *b, float *c, int64_t m, int64_t n, int64_t k, int fmt, hipStream_t s,
              int epi) {
     const int ke = kernel_epi(epi);
     const auto *b8 = static_cast<const uint8_t *>(b);
+    if (fmt != WQ_FMT_F16 && m >= 2) {
+        hipError_t e = hipSuccess;
+        if (wq::launch_gemv_q_rows(a, b8, fmt, c, m, n, k, s, ke, &e)) {
+            if (e != hipSuccess) return WQ_ERR_LAUNCH;
+            wq::g_route_count[WQ_ROUTE_GEMV].fetch_add(1, std::memory_order_relaxed);
+            return WQ_OK;
+        }
+    }
     for (int64_t i = 0; i < m; ++i) {
         const float *ai = a + i * k;
         float *ci = c + i * n;
@@ -321,7 +341,7 @@ int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, in
                hipStream_t s) {
     if (k == 0) return epi == WQ_EPI_RESIDUAL ? WQ_OK : run_zero(c, m, n, s);  // silu(0) * 0 = 0
     int route = wq::g_forced_route.load(std::memory_order_relaxed);
-    if (route == WQ_ROUTE_AUTO) route = auto_route(m, k, fmt);
+    if (route == WQ_ROUTE_AUTO) route = pick_route(a, b, m, n, k, fmt, epi);
     if (route == WQ_ROUTE_GEMV) return run_gemv(a, b, c, m, n, k, fmt, s, epi);
     if (route == WQ_ROUTE_SKINNY) return run_skinny(a, b, c, m, n, k, fmt, s, epi);
     if (route == WQ_ROUTE_STREAM) return run_stream(a, b, c, m, n, k, fmt, s, epi);
@@ -333,7 +353,7 @@ int run_routed(const float *a, const void *b, float *c, int64_t m, int64_t n, in
 
 extern "C" {
 
-int wq_abi_version(void) { return 107; }
+int wq_abi_version(void) { return 108; }
 
 const char *wq_status_str(int status) {
     switch (status) {
@@ -544,7 +564,7 @@ int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt) {
     if (!known_format(fmt)) return -WQ_ERR_FORMAT;
     if (m < 0 || n < 0 || k < 0) return -WQ_ERR_SHAPE;
     if (fmt != WQ_FMT_F16 && m > 0 && n > 0 && (k == 0 || k % 32 != 0)) return -WQ_ERR_K;
-    return auto_route(m, k, fmt);
+    return pick_route(nullptr, nullptr, m, n, k, fmt, WQ_EPI_NONE);
 }
 
 int wq_gemm_plan(int64_t m, int64_t n, int64_t k, int fmt, int cus, int *bm, int *bn, int *splits) {

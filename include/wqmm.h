@@ -92,7 +92,11 @@ typedef enum wq_status {
 /* Kernel families wq_matmul can route to. */
 typedef enum wq_route {
     WQ_ROUTE_AUTO = 0,  /* choose by M (wq_route_for) */
-    WQ_ROUTE_GEMV = 1,  /* decode GEMV: one launch per row of A */
+    WQ_ROUTE_GEMV = 1,  /* decode GEMV: one launch per row of A, except 2 to 4
+                           Q8_0 rows (2 Q4_0 rows) with K % 256 == 0 and
+                           16-byte aligned a and b, which the register-chunk
+                           kernel takes in one launch (each weight chunk read
+                           once and applied to every row) */
     WQ_ROUTE_GEMM = 2,  /* LDS-tiled fp32-MFMA GEMM */
     WQ_ROUTE_SKINNY = 3, /* small-M weight-streaming fp32-MFMA product: one
                             launch per block of up to 16 rows of A */
@@ -332,9 +336,12 @@ int wq_read_probe(const void *p, int64_t bytes, uint32_t *out, int variant, void
 /* Routing and introspection (host only; these never touch the GPU). */
 
 /* The route wq_matmul takes for these arguments when nothing is forced
- * (WQ_ROUTE_GEMV, WQ_ROUTE_STREAM, WQ_ROUTE_SKINNY or WQ_ROUTE_GEMM_HL), or a
- * negative wq_status
- * on bad arguments. */
+ * (WQ_ROUTE_GEMV, WQ_ROUTE_STREAM, WQ_ROUTE_SKINNY or WQ_ROUTE_GEMM_HL) with
+ * 16-byte aligned operands and no epilogue, or a negative wq_status on bad
+ * arguments.  M == 1 takes the GEMV; quantized M <= 16 with K % 256 == 0 the
+ * weight stream, except M == 2 Q8_0 rows whose register-chunk plan keeps at
+ * most three units per wave (K % 256 == 0 and K <= 8448), which take the GEMV
+ * route. */
 int wq_route_for(int64_t m, int64_t n, int64_t k, int fmt);
 
 /* The tiling the GEMM uses for (m, n, k, fmt) on a device with `cus` compute

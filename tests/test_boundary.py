@@ -51,7 +51,7 @@ def test_single_hip_runtime_in_process():
 
 
 def test_abi_and_status_strings():
-    assert wq.wq_abi_version() == 107
+    assert wq.wq_abi_version() == 108
     for st in range(0, 11):
         assert wq.status_str(st)
     assert wq.status_str(99) == "unknown status"
@@ -190,7 +190,7 @@ def test_decode_attention_validation():
 
 def test_routing_rule():
     """M = 1: GEMV; quantized with K % 256 == 0: 2..16 the f16 matrix-core
-    stream; other quantized K: 2..4 small-M; f16: 2..8 small-M; more: the
+    stream (two Q8_0 rows the register-chunk GEMV takes with few units: GEMV); other quantized K: 2..4 small-M; f16: 2..8 small-M; more: the
     tiled f16 matrix-core GEMM (which hands calls it cannot take to the fp32
     GEMM at launch)."""
     for fmt in (wq.WQ_FMT_F16, wq.WQ_FMT_Q8_0, wq.WQ_FMT_Q4_0):
@@ -201,9 +201,22 @@ def test_routing_rule():
             else:
                 small, top = wq.WQ_ROUTE_SKINNY, 8 if fmt == wq.WQ_FMT_F16 else 4
             for m in range(2, top + 1):
-                assert wq.wq_route_for(m, 4096, k, fmt) == small
+                # Two Q8_0 rows at N = K = 4096: the register-chunk plan (8, 1, 1)
+                # keeps two units per wave, so the GEMV route takes them.
+                two_rows = fmt == wq.WQ_FMT_Q8_0 and m == 2 and k % 256 == 0
+                assert wq.wq_route_for(m, 4096, k, fmt) == (wq.WQ_ROUTE_GEMV if two_rows else small)
             for m in (top + 1, 17, 64, 512):
                 assert wq.wq_route_for(m, 4096, k, fmt) == wq.WQ_ROUTE_GEMM_HL
+    # Two Q8_0 rows: GEMV where the register-chunk plan has at most three
+    # units per wave (K <= 8448 at Q8_0's 34 bytes per 32 columns), the stream
+    # otherwise (K = 11008: four units).
+    for (n, k), route in (((11008, 4096), wq.WQ_ROUTE_GEMV), ((151936, 2048), wq.WQ_ROUTE_GEMV),
+                          ((6144, 2048), wq.WQ_ROUTE_GEMV), ((2048, 6144), wq.WQ_ROUTE_GEMV),
+                          ((2048, 2048), wq.WQ_ROUTE_GEMV), ((1000, 8448), wq.WQ_ROUTE_GEMV),
+                          ((4096, 11008), wq.WQ_ROUTE_STREAM), ((11008, 8704), wq.WQ_ROUTE_STREAM)):
+        assert wq.wq_route_for(2, n, k, wq.WQ_FMT_Q8_0) == route, (n, k)
+        assert wq.wq_route_for(2, n, k, wq.WQ_FMT_Q4_0) == wq.WQ_ROUTE_STREAM, (n, k)
+        assert wq.wq_route_for(3, n, k, wq.WQ_FMT_Q8_0) == wq.WQ_ROUTE_STREAM, (n, k)
     assert wq.wq_route_for(2, 8, 33, wq.WQ_FMT_Q8_0) == -wq.WQ_ERR_K
     assert wq.wq_route_for(2, 8, 48, wq.WQ_FMT_Q4_0) == -wq.WQ_ERR_K
     assert wq.wq_route_for(2, 8, 32, 5) == -wq.WQ_ERR_FORMAT

@@ -376,22 +376,27 @@ def test_deterministic_and_linear(fmt, m):
 @pytest.mark.parametrize("fmt", ALL)
 def test_routes_agree_and_are_counted(fmt):
     """Every route gives the oracle's product for any M, and the path-proof
-    counters show which kernels ran: the GEMV once per row of A, either GEMM
-    once, the small-M kernels once per 16 rows of A."""
+    counters show which kernels ran: the GEMV once per row of A (once for 2
+    to 4 Q8_0 rows, which the register-chunk kernel takes together), either
+    GEMM once, the small-M kernels once per 16 rows of A."""
     n, k = 1000, 1024
     ref_b, dev_b = encoded(n, k, fmt, 7)
-    ms = (1, 3, 20)
+    ms = (1, 2, 3, 20)
     c_ref = {m: oracle.matmul(acts(m, k, 7), ref_b, fmt, m, n, k) for m in ms}
     routes = (wq.WQ_ROUTE_GEMV, wq.WQ_ROUTE_GEMM, wq.WQ_ROUTE_SKINNY, wq.WQ_ROUTE_STREAM, wq.WQ_ROUTE_GEMM_HL)
-    skinny = {1: (0, 0, 1, 0, 0), 3: (0, 0, 1, 0, 0), 20: (0, 0, 2, 0, 0)}
-    stream = skinny if fmt == F16 else {1: (0, 0, 0, 1, 0), 3: (0, 0, 0, 1, 0), 20: (0, 0, 0, 2, 0)}
+    skinny = {1: (0, 0, 1, 0, 0), 2: (0, 0, 1, 0, 0), 3: (0, 0, 1, 0, 0), 20: (0, 0, 2, 0, 0)}
+    stream = skinny if fmt == F16 else {m: (0, 0, 0, 1 if m <= 16 else 2, 0) for m in ms}
+    gemm, hl = {m: (0, 1, 0, 0, 0) for m in ms}, {m: (0, 0, 0, 0, 1) for m in ms}
     expect = {
-        wq.WQ_ROUTE_GEMV: {1: (1, 0, 0, 0, 0), 3: (3, 0, 0, 0, 0), 20: (20, 0, 0, 0, 0)},
-        wq.WQ_ROUTE_GEMM: {1: (0, 1, 0, 0, 0), 3: (0, 1, 0, 0, 0), 20: (0, 1, 0, 0, 0)},
+        wq.WQ_ROUTE_GEMV: {1: (1, 0, 0, 0, 0), 2: (2 if fmt == F16 else 1, 0, 0, 0, 0),
+                           3: (1 if fmt == Q8 else 3, 0, 0, 0, 0), 20: (20, 0, 0, 0, 0)},
+        wq.WQ_ROUTE_GEMM: gemm,
         wq.WQ_ROUTE_SKINNY: skinny,
         wq.WQ_ROUTE_STREAM: stream,
-        wq.WQ_ROUTE_GEMM_HL: {1: (0, 0, 0, 0, 1), 3: (0, 0, 0, 0, 1), 20: (0, 0, 0, 0, 1)},
-        wq.WQ_ROUTE_AUTO: {1: (1, 0, 0, 0, 0), 3: skinny[3] if fmt == F16 else stream[3], 20: (0, 0, 0, 0, 1)},
+        wq.WQ_ROUTE_GEMM_HL: hl,
+        # Two Q8_0 rows at K = 1024: the register-chunk GEMV (plan 4 x 2 x 1).
+        wq.WQ_ROUTE_AUTO: {1: (1, 0, 0, 0, 0), 2: (1, 0, 0, 0, 0) if fmt == Q8 else stream[2],
+                           3: stream[3], 20: hl[20]},
     }
     try:
         for route, per_call in expect.items():
@@ -672,6 +677,65 @@ def test_chunk_gemv_every_plan(plan, fmt):
             say(f"chunk plan {plan} fmt={fmt} k={k} edge blocks")
     finally:
         wq.wq_set_gemv_plan(0, 0, 0)
+
+
+# Plans the register-chunk GEMV compiles for 2 and 4 rows of A (its activation
+# windows take NU * rows * 16 or 32 registers): (format, rows of A, plan).
+ROW_PLANS = ([(Q8, 2, p) for p in ((16, 1, 1), (8, 1, 1), (4, 2, 1), (4, 3, 1))]
+             + [(Q4, 2, p) for p in ((8, 1, 1), (4, 1, 1), (4, 2, 1))]
+             + [(Q8, 4, p) for p in ((8, 1, 1), (4, 1, 1))])
+
+
+@pytest.mark.parametrize("case", ROW_PLANS, ids=[f"fmt{f}-mr{r}-{p[0]}x{p[1]}x{p[2]}" for f, r, p in ROW_PLANS])
+def test_chunk_gemv_several_rows_every_plan(case):
+    """2 <= M <= 4 rows of A through one register-chunk launch (the GEMV route),
+    under every plan compiled for that many rows, at every K of CHUNK_K the
+    plan takes and row counts that leave the last workgroup partial: full
+    compares against the oracle at every row count the kernel serves (3 rows
+    on the 4-row kernel leave one padding row), equal weight rows giving equal sums,
+    the residual epilogue, and hand-built edge blocks bit for bit through one
+    one-hot row of A per row."""
+    fmt, mr, plan = case
+    ks = [k for k in CHUNK_K if chunk_plan_fits(fmt, k, *plan)]
+    assert len(ks) >= 2, ks
+    try:
+        wq.wq_set_forced_route(wq.WQ_ROUTE_GEMV)
+        wq.wq_set_gemv_plan(*plan)
+        for k in ks:
+            for m in range(mr // 2 + 1, mr + 1):
+                for n in (5, 37, 133):
+                    full_case("matmul", fmt, m, n, k, seed=n + k + m)
+            say(f"rows fmt={fmt} mr={mr} plan {plan} k={k}")
+            raw1 = encoded(1, k, fmt, k)[0]
+            same = np.ascontiguousarray(np.repeat(raw1, 37, axis=0))
+            a2 = acts(mr, k, k + 1)
+            c = run_gpu("matmul", fmt, a2, torch.from_numpy(same).cuda(), mr, 37, k)
+            for i in range(mr):
+                assert np.all(c[i] == c[i, 0]), f"plan {plan} k={k} row {i}: equal rows differ"
+            n = 21
+            raw = edge_weights(fmt, n, k, seed=2)
+            w = oracle.decode(raw, fmt, n, k)
+            dev_b = torch.from_numpy(raw).cuda()
+            cols = onehot_positions(k, np.random.default_rng(k))
+            for j in range(0, len(cols) - mr + 1, mr):
+                a = np.zeros((mr, k), np.float32)
+                for i in range(mr):
+                    a[i, cols[j + i]] = 1.0
+                c = run_gpu("matmul", fmt, a, dev_b, mr, n, k)
+                for i in range(mr):
+                    assert np.array_equal(c[i].astype(np.float64), w[:, cols[j + i]]), (plan, k, cols[j + i])
+        m, n, k = mr, 133, ks[-1]
+        ref_b, dev_b = encoded(n, k, fmt, 4)
+        a = acts(m, k, 4)
+        c0 = np.random.default_rng(4).standard_normal((m, n)).astype(np.float32)
+        c = torch.from_numpy(c0).cuda()
+        wq.wq_matmul_ex(torch.from_numpy(a).cuda(), dev_b, c, m, n, k, fmt, wq.WQ_EPI_RESIDUAL)
+        torch.cuda.synchronize()
+        c_ref, bound = oracle.matmul(a, ref_b, fmt, m, n, k)
+        assert_close(c.cpu().numpy() - c0, c_ref, bound + 1e-6 * np.abs(c0), "residual, several rows")
+    finally:
+        wq.wq_set_gemv_plan(0, 0, 0)
+        wq.wq_set_forced_route(wq.WQ_ROUTE_AUTO)
 
 
 @pytest.mark.parametrize("fmt", [Q8, Q4])
